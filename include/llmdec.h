@@ -1,0 +1,277 @@
+/*
+ * libllmdec: the KV-cached forward step of a LLaMA-style decoder over a paged
+ * KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * Pages the operations follow (cited by tag):
+ *   [W] "企业官网建设流程全解析" (www.dpshk.com/news/4990443), the weights
+ *       article: §1.1 forward skeleton, §1.2 where parameters live, §2.x
+ *       weight layout [out][in].
+ *   [F] "大模型推理全流程解析：从权重加载到文本生成的工程实践"
+ *       (www.stapisi.com/news/4049481): §2.2.1 embedding, §2.2.2 attention
+ *       and KV cache, §2.2.3 lm_head and greedy choice, §4 cached greedy loop.
+ *   [E] "为什么要自己动手写一个LLM推理引擎" (www.wzjinhao.cn/news/61427):
+ *       §3.4 KV cache sizing and paging, §4.2 RMSNorm, §4.3 attention forward
+ *       with the cache, §4.4 generate loop, §5.3 preallocated cache pool and
+ *       sampling on the device.
+ *
+ * Conventions for every function below.
+ *  - Pointers marked "dev" are device pointers; "host" are host pointers.
+ *  - The caller owns all memory (weights, packed weights, hidden states, the
+ *    KV pool's device buffer, workspaces, ids, tables).  The library never
+ *    allocates device memory; it only keeps the host-side pool handle.
+ *  - Device work is enqueued on the caller's stream (a hipStream_t passed as
+ *    llmdec_stream; NULL is the default stream) and the call returns after
+ *    enqueueing, without synchronising.  Buffers must stay alive until the
+ *    work completes.
+ *  - Every call checks what the host can check before it launches anything,
+ *    so a rejected call has done no work.  Status codes are returned; a
+ *    thread-local message is available from llmdec_last_error().  Nothing
+ *    prints, throws or aborts across this interface.
+ *  - Values that only the device knows (token ids, positions, block-table
+ *    entries) are range-checked inside the kernels: an out-of-range page id
+ *    or position makes the kernel skip that access and set a sticky error
+ *    word in the workspace, read back by llmdec_workspace_error().
+ *  - bf16 means IEEE-754 binary32 truncated to its top 16 bits; rounding into
+ *    bf16 is to nearest, ties to even.
+ *  - Not thread-safe per pool handle; distinct handles are independent.
+ */
+#ifndef LLMDEC_H
+#define LLMDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LLMDEC_OK = 0,
+  LLMDEC_E_INVALID = -1,     /* bad argument: null pointer, inconsistent sizes, out of range */
+  LLMDEC_E_UNSUPPORTED = -2, /* valid but not built: head_dim not 64/128, n_kv_heads != n_heads */
+  LLMDEC_E_NO_PAGES = -3,    /* the pool cannot cover a request; nothing was changed */
+  LLMDEC_E_WORKSPACE = -4,   /* workspace pointer missing or smaller than required */
+  LLMDEC_E_HIP = -5          /* a HIP runtime call or kernel launch failed */
+} llmdec_status;
+
+typedef void *llmdec_stream; /* hipStream_t */
+
+/* Model shape.  [W] §1.2 gives the 7B values: hidden 4096, 32 layers,
+ * intermediate 11008, vocab 32000; [E] §3.4 gives 32 heads of 128.
+ * page_size must be 16 ([E] §3.4 recommends 16 or 32 tokens per page).
+ * head_dim must be 64 or 128; hidden == n_heads * head_dim; n_kv_heads must
+ * equal n_heads; hidden and intermediate must be multiples of 16. */
+typedef struct {
+  int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, intermediate, vocab, page_size;
+  float rms_eps;    /* added to the mean square inside the root ([E] §4.2) */
+  float rope_theta; /* rotary base: pair i turns by pos * theta^(-2i/head_dim) */
+} llmdec_config;
+
+/* One layer's parameters as loaded: bf16, each matrix [out][in] row-major
+ * (the nn.Linear layout of [W] §1.2).  attn_norm, mlp_norm: [hidden];
+ * wq, wo: [hidden][hidden]; wk, wv: [n_kv_heads*head_dim][hidden];
+ * w_gate, w_up: [intermediate][hidden]; w_down: [hidden][intermediate]. */
+typedef struct {
+  const void *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+} llmdec_layer_weights;
+
+/* One layer re-laid out for the kernels by llmdec_pack_layer (pointers into
+ * the caller's packed buffer).  Matrices are stored as 16-row x 32-column
+ * tiles in the order the matrix-core operands are fed; q/k/v are fused into
+ * one [3*hidden][hidden] matrix and gate/up into one matrix whose 16-row
+ * blocks alternate gate and up.  The contents are the same bf16 values. */
+typedef struct {
+  const void *attn_norm, *mlp_norm; /* bf16 [hidden], copied */
+  const void *w_qkv, *w_o, *w_gu, *w_down;
+} llmdec_packed_layer;
+
+/* Whole model for llmdec_model_step_greedy.  embed: dev bf16 [vocab][hidden]
+ * as loaded; layers: host array [n_layers] of packed layers; final_norm: dev
+ * bf16 [hidden]; lm_head: dev, packed with llmdec_pack_matrix from the
+ * [vocab][hidden] matrix (untied from embed). */
+typedef struct {
+  const void *embed;
+  const llmdec_packed_layer *layers;
+  const void *final_norm;
+  const void *lm_head;
+} llmdec_model_weights;
+
+/* ------------------------------------------------------------------ errors */
+/* Message for the last failing call on this thread ("" if none). */
+const char *llmdec_last_error(void);
+
+/* ------------------------------------------------------------------ weights */
+/* Bytes of a packed rows x cols bf16 matrix (rows a multiple of 16; cols padded
+ * up to a multiple of 32 with zeros). */
+size_t llmdec_packed_matrix_bytes(int32_t rows, int32_t cols);
+/* Re-lay a dev bf16 [rows][cols] matrix into dev dst (>= packed_matrix_bytes).
+ * Errors: E_INVALID for null pointers, rows % 16 != 0, dst_bytes too small. */
+llmdec_status llmdec_pack_matrix(int32_t rows, int32_t cols, const void *src, void *dst, size_t dst_bytes,
+                                 llmdec_stream stream);
+/* Bytes of one packed layer for cfg. */
+size_t llmdec_packed_layer_bytes(const llmdec_config *cfg);
+/* Pack one layer ([W] §2 keeps weights [out][in] and lets the operator side
+ * pick the layout its kernels want) into dev buffer dst; fills *out with
+ * pointers into dst.  The input weights may be freed once the stream has run. */
+llmdec_status llmdec_pack_layer(const llmdec_config *cfg, const llmdec_layer_weights *in, void *dst,
+                                size_t dst_bytes, llmdec_packed_layer *out, llmdec_stream stream);
+
+/* ------------------------------------------------------------------ KV pool */
+/* [E] §3.4: the cache is split into fixed-size pages handed out from a free
+ * list on demand and returned when a request ends; attention reaches a
+ * token's cache block through a per-sequence page index.  Each sequence owns a
+ * block-table row of page ids; position p lives in page row[p / 16] at in-page
+ * offset o = p % 16.  Device layout per layer (element = bf16):
+ *   K: [num_pages][n_kv_heads][16][head_dim]   (K[page][h][o][d])
+ *   V: [num_pages][n_kv_heads][head_dim][16]   (V[page][h][d][o], transposed
+ *      inside the page so both attention kernels read V in 16-byte runs),
+ * K block then V block, layer after layer; so pool_bytes = n_layers * 2 *
+ * num_pages * n_kv_heads * 16 * head_dim * 2 (for 7B and 128 pages: 1 GiB,
+ * the [E] §3.4 example). */
+typedef struct llmdec_kv_pool llmdec_kv_pool;
+
+size_t llmdec_kv_pool_bytes(const llmdec_config *cfg, int32_t num_pages);
+/* Create a host handle over the caller's dev buffer (>= kv_pool_bytes).
+ * free_order (host, may be NULL = 0,1,2,...) is a permutation of page ids:
+ * the order in which pages are handed out.  Errors: E_INVALID for a bad
+ * config, null pointers, short buffer, or a free_order that is not a
+ * permutation. */
+llmdec_status llmdec_kv_pool_create(const llmdec_config *cfg, void *dev_base, size_t bytes, int32_t num_pages,
+                                    const int32_t *free_order, llmdec_kv_pool **out);
+/* Grow a sequence so that it covers tokens_needed tokens: appends
+ * ceil(tokens_needed/16) - *n_pages_inout pages (popped from the free list) to
+ * the host row block_table_row[0..max_pages) and updates *n_pages_inout.
+ * Atomic: on E_NO_PAGES neither the row nor the pool changes.  E_INVALID if
+ * ceil(tokens_needed/16) > max_pages or *n_pages_inout is out of range. */
+llmdec_status llmdec_kv_pool_alloc(llmdec_kv_pool *pool, int32_t tokens_needed, int32_t *block_table_row,
+                                   int32_t *n_pages_inout, int32_t max_pages);
+/* Return pages (host array) to the free list, pushed in the given order (the
+ * last one returned is handed out first).  E_INVALID, with no change, for an
+ * id out of range, an id already free, or a repeated id. */
+llmdec_status llmdec_kv_pool_free(llmdec_kv_pool *pool, const int32_t *pages, int32_t n);
+int32_t llmdec_kv_pool_free_count(const llmdec_kv_pool *pool);
+void *llmdec_kv_pool_device_base(const llmdec_kv_pool *pool);
+void llmdec_kv_pool_destroy(llmdec_kv_pool *pool);
+
+/* Test support: copy positions 0..n_tokens-1 of one sequence's K and V for
+ * one layer into dev k_out, v_out ([n_tokens][n_kv_heads][head_dim] bf16),
+ * walking the dev block-table row. */
+llmdec_status llmdec_debug_gather_kv(const llmdec_kv_pool *pool, int32_t layer, const int32_t *block_table_row,
+                                    int32_t n_tokens, void *k_out, void *v_out, llmdec_stream stream);
+
+/* ------------------------------------------------------------------ workspace */
+/* Bytes of device scratch needed for steps of up to max_tokens new tokens over
+ * up to max_seqs sequences whose block-table rows are max_pages wide.  The
+ * first 256 bytes hold the sticky device error word. */
+size_t llmdec_workspace_bytes(const llmdec_config *cfg, int32_t max_tokens, int32_t max_seqs, int32_t max_pages);
+/* Clear the device error word (enqueued on stream). */
+llmdec_status llmdec_workspace_reset(void *ws, size_t ws_bytes, llmdec_stream stream);
+/* Synchronise stream and read the device error word: 0 = none; otherwise a
+ * bit mask (1: page id out of range, 2: position beyond the block-table row,
+ * 4: token id out of range). */
+llmdec_status llmdec_workspace_error(const void *ws, llmdec_stream stream, uint32_t *error_bits);
+
+/* ------------------------------------------------------------------ layer steps */
+/* Prefill (or chunked prefill) of one layer.  hidden: dev fp32 [n_tokens][hidden],
+ * the residual stream, updated in place.  Sequence s owns tokens
+ * cu_seqlens[s]..cu_seqlens[s+1]-1 (dev int32 [n_seqs+1]); its first new token
+ * sits at position start_pos[s] (dev int32 [n_seqs]).  block_tables: dev int32
+ * [n_seqs][max_pages], rows already covering start_pos+len tokens.  n_tokens
+ * (= cu_seqlens[n_seqs]) and max_q_len (>= every sequence's new-token count)
+ * are host copies used to size the launch.  Computes ([W] §1.1, [E] §4.2-4.3):
+ *   y = RMSNorm(x); q,k,v = y Wq^T, y Wk^T, y Wv^T; rotate q, k by position;
+ *   store bf16 k, v into the pool; causal attention over positions 0..p;
+ *   x += o Wo^T; y = RMSNorm(x); x += (silu(y Wg^T) * (y Wu^T)) Wd^T. */
+llmdec_status llmdec_layer_prefill(const llmdec_config *cfg, const llmdec_packed_layer *w, int32_t layer,
+                                   float *hidden, int32_t n_seqs, int32_t n_tokens, int32_t max_q_len,
+                                   const int32_t *cu_seqlens, const int32_t *start_pos, const int32_t *block_tables,
+                                   int32_t max_pages, llmdec_kv_pool *pool, void *ws, size_t ws_bytes,
+                                   llmdec_stream stream);
+
+/* One decode token per sequence for one layer ([F] §2.2.2: only the new
+ * token's q, k, v are computed; cached K/V are reused).  hidden: dev fp32
+ * [n_seqs][hidden], updated in place.  ctx_lens: dev int32 [n_seqs], the
+ * number of tokens already cached = the new token's position; its K/V go to
+ * that position and attention covers positions 0..ctx_lens[s]. */
+llmdec_status llmdec_layer_decode(const llmdec_config *cfg, const llmdec_packed_layer *w, int32_t layer,
+                                  float *hidden, int32_t n_seqs, const int32_t *ctx_lens, const int32_t *block_tables,
+                                  int32_t max_pages, llmdec_kv_pool *pool, void *ws, size_t ws_bytes,
+                                  llmdec_stream stream);
+
+/* One greedy step of the whole model ([F] §4, [E] §4.4): embed the new
+ * tokens, run every layer, take each sequence's last new token, final
+ * RMSNorm, lm_head, argmax with the lowest index winning ties, and write
+ * next_tokens (dev int32 [n_seqs]) without a host synchronisation ([E] §5.3).
+ * tokens: dev int32 [n_tokens].  cu_seqlens == NULL means one token per
+ * sequence (decode; n_tokens == n_seqs, max_q_len == 1) at position
+ * start_pos[s]; otherwise as in llmdec_layer_prefill.  logits: optional dev
+ * fp32 [n_seqs][vocab]. */
+llmdec_status llmdec_model_step_greedy(const llmdec_config *cfg, const llmdec_model_weights *w, int32_t n_seqs,
+                                       int32_t n_tokens, int32_t max_q_len, const int32_t *tokens,
+                                       const int32_t *cu_seqlens, const int32_t *start_pos,
+                                       const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool,
+                                       int32_t *next_tokens, float *logits, void *ws, size_t ws_bytes,
+                                       llmdec_stream stream);
+
+/* ------------------------------------------------------------------ single operations
+ * The kernels the layer steps are built from, exposed one by one so each can
+ * be checked on its own.  Same conventions as above. */
+
+/* y = x * (mean(x^2) + eps)^(-1/2) * gamma per row ([E] §4.2).  x: dev fp32
+ * [rows][n]; gamma: dev bf16 [n].  Any of out_f32 (fp32 [rows][n]) and the
+ * pair out_hi/out_lo (bf16 [rows][ld_split], hi = bf16(y), lo = bf16(y - hi),
+ * columns n..ld_split-1 zeroed) may be NULL but not all. */
+llmdec_status llmdec_op_rmsnorm(const float *x, const void *gamma, int32_t rows, int32_t n, float eps,
+                                float *out_f32, void *out_hi, void *out_lo, int32_t ld_split, llmdec_stream stream);
+
+/* out[m][n] (+)= sum_k a[m][k] * W[n][k] for a dev fp32 [rows][k_dim] and a
+ * packed W (llmdec_pack_matrix of [n_dim][k_dim]).  accumulate = 0 stores, 1
+ * adds into out (the residual add of [W] §1.1).  ws: scratch for the split
+ * operands and split-k partial sums (>= llmdec_op_linear_ws_bytes).
+ * rows == 1 takes the fp32 GEMV path; rows > 1 the matrix-core path. */
+size_t llmdec_op_linear_ws_bytes(int32_t rows, int32_t k_dim, int32_t n_dim);
+llmdec_status llmdec_op_linear(const float *a, int32_t rows, int32_t k_dim, const void *w_packed, int32_t n_dim,
+                               float *out, int32_t accumulate, void *ws, size_t ws_bytes, llmdec_stream stream);
+
+/* Rotate q and k of each new token by its position and store bf16 k, v into
+ * the pool ([E] §4.3: rotation first, then the cache update).  qkv: dev fp32
+ * [n_tokens][3*hidden] (q | k | v); q is rotated in place.  Token t belongs
+ * to sequence seq_of_token[t] (dev int32) at position pos_of_token[t]. */
+llmdec_status llmdec_op_rope_append(const llmdec_config *cfg, float *qkv, int32_t n_tokens,
+                                    const int32_t *seq_of_token, const int32_t *pos_of_token,
+                                    const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool,
+                                    int32_t layer, void *ws, size_t ws_bytes, llmdec_stream stream);
+
+/* Decode attention: for each sequence s and head h, o = softmax(q K^T /
+ * sqrt(head_dim)) V over positions 0..ctx_lens[s] read through the pages
+ * ([E] §4.3).  q: dev fp32 [n_seqs][hidden]; out: dev fp32 [n_seqs][hidden]. */
+llmdec_status llmdec_op_decode_attention(const llmdec_config *cfg, const float *q, int32_t n_seqs,
+                                         const int32_t *ctx_lens, const int32_t *block_tables, int32_t max_pages,
+                                         const llmdec_kv_pool *pool, int32_t layer, float *out, void *ws,
+                                         size_t ws_bytes, llmdec_stream stream);
+
+/* Causal prefill attention: new token i of sequence s (position start_pos[s]+i)
+ * attends positions 0..start_pos[s]+i read through the pages.  q: dev fp32
+ * [n_tokens][hidden] (already rotated); out: dev fp32 [n_tokens][hidden]. */
+llmdec_status llmdec_op_prefill_attention(const llmdec_config *cfg, const float *q, int32_t n_seqs,
+                                          int32_t n_tokens, int32_t max_q_len, const int32_t *cu_seqlens,
+                                          const int32_t *start_pos, const int32_t *block_tables, int32_t max_pages,
+                                          const llmdec_kv_pool *pool, int32_t layer, float *out, void *ws,
+                                          size_t ws_bytes, llmdec_stream stream);
+
+/* u = silu(gate) * up, silu(z) = z / (1 + e^-z) ([W] §1.2, [E] §4.2).  gate,
+ * up: dev fp32 [rows][n]; out: dev fp32 [rows][n]. */
+llmdec_status llmdec_op_silu_mul(const float *gate, const float *up, int32_t rows, int32_t n, float *out,
+                                 llmdec_stream stream);
+
+/* Greedy choice ([F] §2.2.3): logits = x lm_head^T for dev fp32 x [rows][hidden]
+ * (already normalised) and a packed lm_head [vocab][hidden]; next[r] = argmax,
+ * lowest index on ties.  logits_out: optional dev fp32 [rows][vocab]. */
+llmdec_status llmdec_op_lm_head_argmax(const float *x, int32_t rows, int32_t hidden, const void *lm_head_packed,
+                                       int32_t vocab, int32_t *next, float *logits_out, void *ws, size_t ws_bytes,
+                                       llmdec_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LLMDEC_H */

@@ -1,0 +1,604 @@
+// C ABI of libllmdec: argument checks, workspace layout and the order of the
+// kernels in a layer step and a model step.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace llmdec {
+
+static thread_local char g_err[512] = "";
+
+llmdec_status set_error(llmdec_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+llmdec_status clear_error() {
+  g_err[0] = 0;
+  return LLMDEC_OK;
+}
+
+llmdec_status check_launch(const char *who) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(LLMDEC_E_HIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
+  return clear_error();
+}
+
+llmdec_status check_config(const llmdec_config *c, const char *who) {
+  if (!c) return set_error(LLMDEC_E_INVALID, "%s: config is NULL", who);
+  if (c->n_layers <= 0 || c->hidden <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || c->intermediate <= 0 ||
+      c->vocab <= 0)
+    return set_error(LLMDEC_E_INVALID, "%s: config sizes must be positive", who);
+  if (c->page_size != kPage)
+    return set_error(LLMDEC_E_UNSUPPORTED, "%s: page_size must be %d, got %d", who, kPage, c->page_size);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return set_error(LLMDEC_E_UNSUPPORTED, "%s: head_dim must be 64 or 128, got %d", who, c->head_dim);
+  if (c->n_heads * c->head_dim != c->hidden)
+    return set_error(LLMDEC_E_INVALID, "%s: hidden (%d) != n_heads (%d) * head_dim (%d)", who, c->hidden, c->n_heads,
+                     c->head_dim);
+  if (c->n_kv_heads != c->n_heads)
+    return set_error(LLMDEC_E_UNSUPPORTED, "%s: n_kv_heads (%d) must equal n_heads (%d)", who, c->n_kv_heads,
+                     c->n_heads);
+  if (c->hidden % 32 || c->intermediate % 16 || c->vocab % 16)
+    return set_error(LLMDEC_E_INVALID, "%s: hidden must be a multiple of 32, intermediate and vocab of 16", who);
+  if (c->hidden > 8192 || c->intermediate > 16384)
+    return set_error(LLMDEC_E_UNSUPPORTED, "%s: hidden <= 8192 and intermediate <= 16384 are supported", who);
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f))
+    return set_error(LLMDEC_E_INVALID, "%s: rms_eps must be >= 0 and rope_theta > 0", who);
+  return LLMDEC_OK;
+}
+
+static size_t al(size_t x) { return round_up_sz(x, 256); }
+
+WsLayout ws_layout(const llmdec_config &c, int max_tokens, int max_seqs, int max_pages) {
+  WsLayout L{};
+  const int T = std::max(1, max_tokens), S = std::max(1, max_seqs), P = std::max(1, max_pages);
+  const int h = c.hidden, I = c.intermediate;
+  L.max_tokens = T;
+  L.max_seqs = S;
+  L.max_pages = P;
+  L.kpad_max = round_up(std::max(h, I), kTileK);
+  const int rows_pad = round_up(std::max(T, S), 16);
+  // decode-attention partial slots: the worst case over every batch size up to S
+  size_t slots = 0;
+  for (int n = 1; n <= S; ++n) {
+    int ppp, parts;
+    decode_partition(n, c.n_heads, P, &ppp, &parts);
+    slots = std::max(slots, (size_t)n * c.n_heads * parts);
+  }
+  L.attn_slots = (int)slots;
+  size_t part = 0;
+  const int rows_lin = std::max(T, S);
+  const int shapes[5][2] = {{3 * h, h}, {h, h}, {2 * I, h}, {h, I}, {c.vocab, h}};
+  for (auto &sh : shapes) part = std::max(part, linear_partial_floats(std::min(rows_lin, 64), sh[0], sh[1]));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += al(bytes);
+    return o;
+  };
+  L.err = take(kWsHeader);
+  L.tok_seq = take(sizeof(int32_t) * T);
+  L.tok_pos = take(sizeof(int32_t) * T);
+  L.x = take(sizeof(float) * (size_t)std::max(T, S) * h);
+  L.act_f32 = take(sizeof(float) * (size_t)std::max(T, S) * std::max(h, I));
+  L.act_hi = take(sizeof(uint16_t) * (size_t)rows_pad * L.kpad_max);
+  L.act_lo = take(sizeof(uint16_t) * (size_t)rows_pad * L.kpad_max);
+  L.qkv = take(sizeof(float) * (size_t)T * 3 * h);
+  L.attn = take(sizeof(float) * (size_t)T * h);
+  L.gu = take(sizeof(float) * (size_t)T * 2 * I);
+  L.part = take(sizeof(float) * part);
+  L.attn_part = take(sizeof(float) * slots * (c.head_dim + 2));
+  L.logits = take(sizeof(float) * (size_t)S * c.vocab);
+  L.amax = take(256);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+static T *at(void *ws, size_t off) {
+  return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
+}
+
+static size_t layer_stride_elems(const llmdec_config &c, int num_pages) {
+  return (size_t)2 * num_pages * c.n_kv_heads * kPage * c.head_dim;
+}
+
+static void pool_layer(const llmdec_kv_pool *p, int layer, uint16_t **k, uint16_t **v) {
+  uint16_t *base = reinterpret_cast<uint16_t *>(p->base) + (size_t)layer * layer_stride_elems(p->cfg, p->num_pages);
+  *k = base;
+  *v = base + (size_t)p->num_pages * p->cfg.n_kv_heads * kPage * p->cfg.head_dim;
+}
+
+static bool same_shape(const llmdec_config &a, const llmdec_config &b) {
+  return a.n_layers == b.n_layers && a.hidden == b.hidden && a.n_heads == b.n_heads && a.n_kv_heads == b.n_kv_heads &&
+         a.head_dim == b.head_dim;
+}
+
+static llmdec_status check_packed(const llmdec_packed_layer *w, const char *who) {
+  if (!w || !w->attn_norm || !w->mlp_norm || !w->w_qkv || !w->w_o || !w->w_gu || !w->w_down)
+    return set_error(LLMDEC_E_INVALID, "%s: packed layer weights missing", who);
+  return LLMDEC_OK;
+}
+
+static llmdec_status check_pool(const llmdec_kv_pool *pool, const llmdec_config &c, int layer, const char *who) {
+  if (!pool) return set_error(LLMDEC_E_INVALID, "%s: pool is NULL", who);
+  if (!same_shape(pool->cfg, c)) return set_error(LLMDEC_E_INVALID, "%s: pool was created for another shape", who);
+  if (layer < 0 || layer >= c.n_layers)
+    return set_error(LLMDEC_E_INVALID, "%s: layer %d out of range [0,%d)", who, layer, c.n_layers);
+  return LLMDEC_OK;
+}
+
+static llmdec_status check_ws(const void *ws, size_t ws_bytes, size_t need, const char *who) {
+  if (!ws) return set_error(LLMDEC_E_WORKSPACE, "%s: workspace is NULL", who);
+  if (ws_bytes < need)
+    return set_error(LLMDEC_E_WORKSPACE, "%s: workspace holds %zu bytes, %zu needed", who, ws_bytes, need);
+  return LLMDEC_OK;
+}
+
+// The body of one layer once every argument has been checked.  rows == number
+// of new tokens; decode passes tok_seq = NULL (token t is sequence t) and
+// positions = ctx_lens.
+struct LayerArgs {
+  const llmdec_config *cfg;
+  const llmdec_packed_layer *w;
+  int layer;
+  float *hidden;
+  int rows;
+  bool decode;
+  int n_seqs, max_q_len;
+  const int32_t *cu, *start, *ctx;
+  const int32_t *bt;
+  int max_pages;
+  const llmdec_kv_pool *pool;
+  void *ws;
+  WsLayout L;
+  hipStream_t s;
+};
+
+static void run_layer(const LayerArgs &a) {
+  const llmdec_config &c = *a.cfg;
+  const int h = c.hidden, I = c.intermediate, M = a.rows;
+  const WsLayout &L = a.L;
+  uint32_t *err = at<uint32_t>(a.ws, L.err);
+  float *act = at<float>(a.ws, L.act_f32);
+  uint16_t *hi = at<uint16_t>(a.ws, L.act_hi), *lo = at<uint16_t>(a.ws, L.act_lo);
+  float *qkv = at<float>(a.ws, L.qkv), *gu = at<float>(a.ws, L.gu), *part = at<float>(a.ws, L.part);
+  const size_t part_n = (L.attn_part - L.part) / sizeof(float);
+  const bool vec = M == 1;  // GEMV path: fp32 activations
+  const int kh = round_up(h, kTileK), ki = round_up(I, kTileK);
+  Act ah, ai;
+  if (vec) {
+    ah.f32 = act;
+    ai.f32 = act;
+  } else {
+    ah.hi = ai.hi = hi;
+    ah.lo = ai.lo = lo;
+    ah.kpad = kh;
+    ai.kpad = ki;
+  }
+  ah.rows = ai.rows = M;
+  uint16_t *pk, *pv;
+  pool_layer(a.pool, a.layer, &pk, &pv);
+  const uint16_t *W = nullptr;
+
+  // attention block: x += Wo . attn(rope(Wq y), rope(Wk y), Wv y),  y = RMSNorm(x)
+  launch_rmsnorm(a.hidden, h, nullptr, (const uint16_t *)a.w->attn_norm, M, h, c.rms_eps, vec ? act : nullptr,
+                 vec ? nullptr : hi, vec ? nullptr : lo, kh, a.s);
+  W = (const uint16_t *)a.w->w_qkv;
+  launch_linear(ah, W, 3 * h, h, qkv, 3 * h, kStore, part, part_n, a.s);
+  if (a.decode) {
+    launch_rope_append(c, qkv, 3 * h, M, nullptr, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages, err, a.s);
+    launch_decode_attention(c, qkv, 3 * h, M, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages,
+                            at<float>(a.ws, L.attn_part), vec ? act : nullptr, vec ? nullptr : hi, vec ? nullptr : lo,
+                            kh, err, a.s);
+  } else {
+    int32_t *ts = at<int32_t>(a.ws, L.tok_seq), *tp = at<int32_t>(a.ws, L.tok_pos);
+    launch_token_map(a.cu, a.start, a.n_seqs, ts, tp, a.s);
+    launch_rope_append(c, qkv, 3 * h, M, ts, tp, a.bt, a.max_pages, pk, pv, a.pool->num_pages, err, a.s);
+    launch_prefill_attention(c, qkv, 3 * h, a.n_seqs, a.max_q_len, a.cu, a.start, a.bt, a.max_pages, pk, pv,
+                             a.pool->num_pages, vec ? act : nullptr, vec ? nullptr : hi, vec ? nullptr : lo, kh, err,
+                             a.s);
+  }
+  launch_linear(ah, (const uint16_t *)a.w->w_o, h, h, a.hidden, h, kAccumulate, part, part_n, a.s);
+
+  // MLP block: x += Wd (silu(Wg y) * (Wu y)),  y = RMSNorm(x)
+  launch_rmsnorm(a.hidden, h, nullptr, (const uint16_t *)a.w->mlp_norm, M, h, c.rms_eps, vec ? act : nullptr,
+                 vec ? nullptr : hi, vec ? nullptr : lo, kh, a.s);
+  launch_linear(ah, (const uint16_t *)a.w->w_gu, 2 * I, h, gu, 2 * I, kStore, part, part_n, a.s);
+  // gate/up rows alternate in 16-row blocks: gate j at column 32(j/16) + j%16, up 16 further
+  launch_silu_mul(gu, gu + 16, 2 * I, 32, M, I, vec ? act : nullptr, vec ? nullptr : hi, vec ? nullptr : lo, ki, a.s);
+  launch_linear(ai, (const uint16_t *)a.w->w_down, h, I, a.hidden, h, kAccumulate, part, part_n, a.s);
+}
+
+}  // namespace llmdec
+
+using namespace llmdec;
+
+extern "C" const char *llmdec_last_error(void) { return g_err; }
+
+// ------------------------------------------------------------------ weights
+extern "C" size_t llmdec_packed_matrix_bytes(int32_t rows, int32_t cols) {
+  if (rows <= 0 || cols <= 0 || rows % 16) return 0;
+  return (size_t)rows * round_up(cols, kTileK) * sizeof(uint16_t);
+}
+
+extern "C" llmdec_status llmdec_pack_matrix(int32_t rows, int32_t cols, const void *src, void *dst, size_t dst_bytes,
+                                           llmdec_stream stream) {
+  if (!src || !dst) return set_error(LLMDEC_E_INVALID, "pack_matrix: NULL pointer");
+  if (rows <= 0 || cols <= 0 || rows % 16)
+    return set_error(LLMDEC_E_INVALID, "pack_matrix: rows (%d) must be a positive multiple of 16, cols (%d) > 0", rows,
+                     cols);
+  const size_t need = llmdec_packed_matrix_bytes(rows, cols);
+  if (dst_bytes < need) return set_error(LLMDEC_E_INVALID, "pack_matrix: dst holds %zu bytes, %zu needed", dst_bytes, need);
+  launch_pack_matrix(rows, cols, (const uint16_t *)src, (uint16_t *)dst, (hipStream_t)stream);
+  return check_launch("pack_matrix");
+}
+
+static size_t packed_layer_parts(const llmdec_config &c, size_t off[6]) {
+  const int h = c.hidden, I = c.intermediate;
+  size_t o = 0;
+  off[0] = o;  // attn_norm
+  o += al((size_t)h * 2);
+  off[1] = o;  // mlp_norm
+  o += al((size_t)h * 2);
+  off[2] = o;  // qkv
+  o += al(llmdec_packed_matrix_bytes(3 * h, h));
+  off[3] = o;  // o
+  o += al(llmdec_packed_matrix_bytes(h, h));
+  off[4] = o;  // gate/up
+  o += al(llmdec_packed_matrix_bytes(2 * I, h));
+  off[5] = o;  // down
+  o += al(llmdec_packed_matrix_bytes(h, I));
+  return o;
+}
+
+extern "C" size_t llmdec_packed_layer_bytes(const llmdec_config *cfg) {
+  if (check_config(cfg, "packed_layer_bytes") != LLMDEC_OK) return 0;
+  size_t off[6];
+  return packed_layer_parts(*cfg, off);
+}
+
+extern "C" llmdec_status llmdec_pack_layer(const llmdec_config *cfg, const llmdec_layer_weights *in, void *dst,
+                                          size_t dst_bytes, llmdec_packed_layer *out, llmdec_stream stream) {
+  llmdec_status st = check_config(cfg, "pack_layer");
+  if (st != LLMDEC_OK) return st;
+  if (!in || !dst || !out || !in->attn_norm || !in->wq || !in->wk || !in->wv || !in->wo || !in->mlp_norm ||
+      !in->w_gate || !in->w_up || !in->w_down)
+    return set_error(LLMDEC_E_INVALID, "pack_layer: NULL pointer");
+  size_t off[6];
+  const size_t need = packed_layer_parts(*cfg, off);
+  if (dst_bytes < need) return set_error(LLMDEC_E_INVALID, "pack_layer: dst holds %zu bytes, %zu needed", dst_bytes, need);
+  const int h = cfg->hidden, I = cfg->intermediate;
+  hipStream_t s = (hipStream_t)stream;
+  char *d = (char *)dst;
+  if (hipMemcpyAsync(d + off[0], in->attn_norm, (size_t)h * 2, hipMemcpyDeviceToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(d + off[1], in->mlp_norm, (size_t)h * 2, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return set_error(LLMDEC_E_HIP, "pack_layer: copy of the norm gains failed");
+  // Fused q|k|v: row blocks of wq, then wk, then wv (each a whole number of 16-row blocks).
+  const int ktc = round_up(h, kTileK);
+  const size_t mat_hh = (size_t)h * ktc;  // packed elements of one [h][h] matrix
+  uint16_t *qkv = (uint16_t *)(d + off[2]);
+  launch_pack_matrix(h, h, (const uint16_t *)in->wq, qkv, s);
+  launch_pack_matrix(h, h, (const uint16_t *)in->wk, qkv + mat_hh, s);
+  launch_pack_matrix(h, h, (const uint16_t *)in->wv, qkv + 2 * mat_hh, s);
+  launch_pack_matrix(h, h, (const uint16_t *)in->wo, (uint16_t *)(d + off[3]), s);
+  // Gate/up interleaved by 16-row block: block 2j = gate rows 16j.., block 2j+1 = up rows 16j..
+  {
+    uint16_t *gu = (uint16_t *)(d + off[4]);
+    launch_pack_matrix(I, h, (const uint16_t *)in->w_gate, gu, s, 2);
+    launch_pack_matrix(I, h, (const uint16_t *)in->w_up, gu + (size_t)16 * ktc, s, 2);
+  }
+  launch_pack_matrix(h, I, (const uint16_t *)in->w_down, (uint16_t *)(d + off[5]), s);
+  st = check_launch("pack_layer");
+  if (st != LLMDEC_OK) return st;
+  out->attn_norm = d + off[0];
+  out->mlp_norm = d + off[1];
+  out->w_qkv = d + off[2];
+  out->w_o = d + off[3];
+  out->w_gu = d + off[4];
+  out->w_down = d + off[5];
+  return LLMDEC_OK;
+}
+
+// ------------------------------------------------------------------ workspace
+extern "C" size_t llmdec_workspace_bytes(const llmdec_config *cfg, int32_t max_tokens, int32_t max_seqs,
+                                         int32_t max_pages) {
+  if (check_config(cfg, "workspace_bytes") != LLMDEC_OK || max_tokens < 0 || max_seqs < 0 || max_pages < 0) return 0;
+  return ws_layout(*cfg, max_tokens, max_seqs, max_pages).total;
+}
+
+extern "C" llmdec_status llmdec_workspace_reset(void *ws, size_t ws_bytes, llmdec_stream stream) {
+  if (!ws || ws_bytes < kWsHeader) return set_error(LLMDEC_E_WORKSPACE, "workspace_reset: workspace missing or too small");
+  launch_fill_u32((uint32_t *)ws, 0u, kWsHeader / 4, (hipStream_t)stream);
+  return check_launch("workspace_reset");
+}
+
+extern "C" llmdec_status llmdec_workspace_error(const void *ws, llmdec_stream stream, uint32_t *bits) {
+  if (!ws || !bits) return set_error(LLMDEC_E_INVALID, "workspace_error: NULL pointer");
+  hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(bits, ws, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return set_error(LLMDEC_E_HIP, "workspace_error: read-back failed");
+  return clear_error();
+}
+
+extern "C" llmdec_status llmdec_debug_gather_kv(const llmdec_kv_pool *pool, int32_t layer, const int32_t *row,
+                                               int32_t n_tokens, void *k_out, void *v_out, llmdec_stream stream) {
+  if (!pool || !row || !k_out || !v_out) return set_error(LLMDEC_E_INVALID, "debug_gather_kv: NULL pointer");
+  if (layer < 0 || layer >= pool->cfg.n_layers || n_tokens < 0)
+    return set_error(LLMDEC_E_INVALID, "debug_gather_kv: layer %d / n_tokens %d out of range", layer, n_tokens);
+  uint16_t *pk, *pv;
+  pool_layer(pool, layer, &pk, &pv);
+  launch_gather_kv(pk, pv, pool->num_pages, pool->cfg.n_kv_heads, pool->cfg.head_dim, row, n_tokens,
+                   (uint16_t *)k_out, (uint16_t *)v_out, (hipStream_t)stream);
+  return check_launch("debug_gather_kv");
+}
+
+// ------------------------------------------------------------------ layer steps
+extern "C" llmdec_status llmdec_layer_prefill(const llmdec_config *cfg, const llmdec_packed_layer *w, int32_t layer,
+                                             float *hidden, int32_t n_seqs, int32_t n_tokens, int32_t max_q_len,
+                                             const int32_t *cu_seqlens, const int32_t *start_pos,
+                                             const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool,
+                                             void *ws, size_t ws_bytes, llmdec_stream stream) {
+  const char *who = "layer_prefill";
+  llmdec_status st = check_config(cfg, who);
+  if (st == LLMDEC_OK) st = check_packed(w, who);
+  if (st == LLMDEC_OK) st = check_pool(pool, *cfg, layer, who);
+  if (st != LLMDEC_OK) return st;
+  if (!hidden || !cu_seqlens || !start_pos || !block_tables)
+    return set_error(LLMDEC_E_INVALID, "%s: NULL device pointer", who);
+  if (n_seqs <= 0 || n_tokens <= 0 || max_q_len <= 0 || max_q_len > n_tokens || max_pages <= 0)
+    return set_error(LLMDEC_E_INVALID, "%s: n_seqs=%d n_tokens=%d max_q_len=%d max_pages=%d out of range", who, n_seqs,
+                     n_tokens, max_q_len, max_pages);
+  WsLayout L = ws_layout(*cfg, n_tokens, n_seqs, max_pages);
+  st = check_ws(ws, ws_bytes, L.total, who);
+  if (st != LLMDEC_OK) return st;
+  LayerArgs a{cfg, w, layer, hidden, n_tokens, false, n_seqs, max_q_len, cu_seqlens, start_pos, nullptr,
+              block_tables, max_pages, pool, ws, L, (hipStream_t)stream};
+  run_layer(a);
+  return check_launch(who);
+}
+
+extern "C" llmdec_status llmdec_layer_decode(const llmdec_config *cfg, const llmdec_packed_layer *w, int32_t layer,
+                                            float *hidden, int32_t n_seqs, const int32_t *ctx_lens,
+                                            const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool,
+                                            void *ws, size_t ws_bytes, llmdec_stream stream) {
+  const char *who = "layer_decode";
+  llmdec_status st = check_config(cfg, who);
+  if (st == LLMDEC_OK) st = check_packed(w, who);
+  if (st == LLMDEC_OK) st = check_pool(pool, *cfg, layer, who);
+  if (st != LLMDEC_OK) return st;
+  if (!hidden || !ctx_lens || !block_tables) return set_error(LLMDEC_E_INVALID, "%s: NULL device pointer", who);
+  if (n_seqs <= 0 || max_pages <= 0)
+    return set_error(LLMDEC_E_INVALID, "%s: n_seqs=%d max_pages=%d out of range", who, n_seqs, max_pages);
+  WsLayout L = ws_layout(*cfg, n_seqs, n_seqs, max_pages);
+  st = check_ws(ws, ws_bytes, L.total, who);
+  if (st != LLMDEC_OK) return st;
+  LayerArgs a{cfg, w, layer, hidden, n_seqs, true, n_seqs, 1, nullptr, nullptr, ctx_lens, block_tables, max_pages,
+              pool, ws, L, (hipStream_t)stream};
+  run_layer(a);
+  return check_launch(who);
+}
+
+extern "C" llmdec_status llmdec_model_step_greedy(const llmdec_config *cfg, const llmdec_model_weights *w,
+                                                 int32_t n_seqs, int32_t n_tokens, int32_t max_q_len,
+                                                 const int32_t *tokens, const int32_t *cu_seqlens,
+                                                 const int32_t *start_pos, const int32_t *block_tables,
+                                                 int32_t max_pages, llmdec_kv_pool *pool, int32_t *next_tokens,
+                                                 float *logits, void *ws, size_t ws_bytes, llmdec_stream stream) {
+  const char *who = "model_step_greedy";
+  llmdec_status st = check_config(cfg, who);
+  if (st != LLMDEC_OK) return st;
+  if (!w || !w->embed || !w->layers || !w->final_norm || !w->lm_head)
+    return set_error(LLMDEC_E_INVALID, "%s: model weights missing", who);
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    st = check_packed(&w->layers[l], who);
+    if (st != LLMDEC_OK) return st;
+  }
+  st = check_pool(pool, *cfg, 0, who);
+  if (st != LLMDEC_OK) return st;
+  if (!tokens || !start_pos || !block_tables || !next_tokens)
+    return set_error(LLMDEC_E_INVALID, "%s: NULL device pointer", who);
+  const bool decode = cu_seqlens == nullptr;
+  if (n_seqs <= 0 || max_pages <= 0 || n_tokens <= 0 || max_q_len <= 0 || max_q_len > n_tokens)
+    return set_error(LLMDEC_E_INVALID, "%s: n_seqs=%d n_tokens=%d max_q_len=%d max_pages=%d out of range", who, n_seqs,
+                     n_tokens, max_q_len, max_pages);
+  if (decode && (n_tokens != n_seqs || max_q_len != 1))
+    return set_error(LLMDEC_E_INVALID, "%s: without cu_seqlens each sequence takes one token (n_tokens=%d, n_seqs=%d)",
+                     who, n_tokens, n_seqs);
+  WsLayout L = ws_layout(*cfg, n_tokens, n_seqs, max_pages);
+  st = check_ws(ws, ws_bytes, L.total, who);
+  if (st != LLMDEC_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  float *x = at<float>(ws, L.x);
+  launch_embed((const uint16_t *)w->embed, tokens, n_tokens, cfg->hidden, cfg->vocab, x, at<uint32_t>(ws, L.err), s);
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    LayerArgs a{cfg, &w->layers[l], l, x, n_tokens, decode, n_seqs, max_q_len, cu_seqlens, start_pos,
+                decode ? start_pos : nullptr, block_tables, max_pages, pool, ws, L, s};
+    run_layer(a);
+  }
+  // final norm on each sequence's last new token, lm_head, argmax ([W] §1.1, [F] §2.2.3)
+  const int h = cfg->hidden;
+  const bool vec = n_seqs == 1;
+  float *act = at<float>(ws, L.act_f32);
+  uint16_t *hi = at<uint16_t>(ws, L.act_hi), *lo = at<uint16_t>(ws, L.act_lo);
+  const int kh = round_up(h, kTileK);
+  launch_rmsnorm(x, h, decode ? nullptr : cu_seqlens, (const uint16_t *)w->final_norm, n_seqs, h, cfg->rms_eps,
+                 vec ? act : nullptr, vec ? nullptr : hi, vec ? nullptr : lo, kh, s);
+  Act a;
+  a.rows = n_seqs;
+  if (vec) {
+    a.f32 = act;
+  } else {
+    a.hi = hi;
+    a.lo = lo;
+    a.kpad = kh;
+  }
+  float *lg = logits ? logits : at<float>(ws, L.logits);
+  launch_linear(a, (const uint16_t *)w->lm_head, cfg->vocab, h, lg, cfg->vocab, kStore, at<float>(ws, L.part),
+                (L.attn_part - L.part) / sizeof(float), s);
+  launch_argmax(lg, n_seqs, cfg->vocab, next_tokens, s);
+  return check_launch(who);
+}
+
+// ------------------------------------------------------------------ single operations
+extern "C" llmdec_status llmdec_op_rmsnorm(const float *x, const void *gamma, int32_t rows, int32_t n, float eps,
+                                          float *out_f32, void *out_hi, void *out_lo, int32_t ld_split,
+                                          llmdec_stream stream) {
+  if (!x || !gamma || (!out_f32 && !out_hi) || (!out_hi != !out_lo))
+    return set_error(LLMDEC_E_INVALID, "op_rmsnorm: NULL pointer");
+  if (rows <= 0 || n <= 0 || (out_hi && (ld_split < n || ld_split % 32)))
+    return set_error(LLMDEC_E_INVALID, "op_rmsnorm: rows=%d n=%d ld_split=%d out of range", rows, n, ld_split);
+  launch_rmsnorm(x, n, nullptr, (const uint16_t *)gamma, rows, n, eps, out_f32, (uint16_t *)out_hi,
+                 (uint16_t *)out_lo, ld_split, (hipStream_t)stream);
+  return check_launch("op_rmsnorm");
+}
+
+static size_t op_linear_parts(int rows, int k, int n, size_t *hi_off, size_t *lo_off, size_t *part_off) {
+  const int kp = round_up(k, kTileK);
+  const size_t split = rows > 1 ? al((size_t)round_up(rows, 16) * kp * 2) : 0;
+  *hi_off = kWsHeader;
+  *lo_off = *hi_off + split;
+  *part_off = *lo_off + split;
+  return *part_off + al(linear_partial_floats(rows, n, k) * sizeof(float));
+}
+
+extern "C" size_t llmdec_op_linear_ws_bytes(int32_t rows, int32_t k_dim, int32_t n_dim) {
+  size_t a, b, c;
+  if (rows <= 0 || k_dim <= 0 || n_dim <= 0) return 0;
+  return op_linear_parts(rows, k_dim, n_dim, &a, &b, &c);
+}
+
+extern "C" llmdec_status llmdec_op_linear(const float *a, int32_t rows, int32_t k_dim, const void *w_packed,
+                                         int32_t n_dim, float *out, int32_t accumulate, void *ws, size_t ws_bytes,
+                                         llmdec_stream stream) {
+  if (!a || !w_packed || !out) return set_error(LLMDEC_E_INVALID, "op_linear: NULL pointer");
+  if (rows <= 0 || k_dim <= 0 || k_dim > 16384 || n_dim <= 0 || n_dim % 16)
+    return set_error(LLMDEC_E_INVALID, "op_linear: rows=%d k=%d n=%d out of range (n a multiple of 16, k <= 16384)",
+                     rows, k_dim, n_dim);
+  size_t hi_off, lo_off, part_off;
+  const size_t need = op_linear_parts(rows, k_dim, n_dim, &hi_off, &lo_off, &part_off);
+  llmdec_status st = check_ws(ws, ws_bytes, need, "op_linear");
+  if (st != LLMDEC_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  Act act;
+  act.rows = rows;
+  if (rows == 1) {
+    act.f32 = a;
+  } else {
+    act.kpad = round_up(k_dim, kTileK);
+    act.hi = at<uint16_t>(ws, hi_off);
+    act.lo = at<uint16_t>(ws, lo_off);
+    launch_split(a, k_dim, rows, k_dim, (uint16_t *)act.hi, (uint16_t *)act.lo, act.kpad, s);
+  }
+  launch_linear(act, (const uint16_t *)w_packed, n_dim, k_dim, out, n_dim, accumulate ? kAccumulate : kStore,
+                at<float>(ws, part_off), linear_partial_floats(rows, n_dim, k_dim), s);
+  return check_launch("op_linear");
+}
+
+extern "C" llmdec_status llmdec_op_rope_append(const llmdec_config *cfg, float *qkv, int32_t n_tokens,
+                                              const int32_t *seq_of_token, const int32_t *pos_of_token,
+                                              const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool,
+                                              int32_t layer, void *ws, size_t ws_bytes, llmdec_stream stream) {
+  const char *who = "op_rope_append";
+  llmdec_status st = check_config(cfg, who);
+  if (st == LLMDEC_OK) st = check_pool(pool, *cfg, layer, who);
+  if (st == LLMDEC_OK) st = check_ws(ws, ws_bytes, kWsHeader, who);
+  if (st != LLMDEC_OK) return st;
+  if (!qkv || !seq_of_token || !pos_of_token || !block_tables) return set_error(LLMDEC_E_INVALID, "%s: NULL pointer", who);
+  if (n_tokens <= 0 || max_pages <= 0) return set_error(LLMDEC_E_INVALID, "%s: n_tokens/max_pages out of range", who);
+  uint16_t *pk, *pv;
+  pool_layer(pool, layer, &pk, &pv);
+  launch_rope_append(*cfg, qkv, 3 * cfg->hidden, n_tokens, seq_of_token, pos_of_token, block_tables, max_pages, pk, pv,
+                     pool->num_pages, (uint32_t *)ws, (hipStream_t)stream);
+  return check_launch(who);
+}
+
+extern "C" llmdec_status llmdec_op_decode_attention(const llmdec_config *cfg, const float *q, int32_t n_seqs,
+                                                   const int32_t *ctx_lens, const int32_t *block_tables,
+                                                   int32_t max_pages, const llmdec_kv_pool *pool, int32_t layer,
+                                                   float *out, void *ws, size_t ws_bytes, llmdec_stream stream) {
+  const char *who = "op_decode_attention";
+  llmdec_status st = check_config(cfg, who);
+  if (st == LLMDEC_OK) st = check_pool(pool, *cfg, layer, who);
+  if (st != LLMDEC_OK) return st;
+  if (!q || !ctx_lens || !block_tables || !out) return set_error(LLMDEC_E_INVALID, "%s: NULL pointer", who);
+  if (n_seqs <= 0 || max_pages <= 0) return set_error(LLMDEC_E_INVALID, "%s: n_seqs/max_pages out of range", who);
+  WsLayout L = ws_layout(*cfg, n_seqs, n_seqs, max_pages);
+  st = check_ws(ws, ws_bytes, L.total, who);
+  if (st != LLMDEC_OK) return st;
+  uint16_t *pk, *pv;
+  pool_layer(pool, layer, &pk, &pv);
+  launch_decode_attention(*cfg, q, cfg->hidden, n_seqs, ctx_lens, block_tables, max_pages, pk, pv, pool->num_pages,
+                          at<float>(ws, L.attn_part), out, nullptr, nullptr, 0, at<uint32_t>(ws, L.err),
+                          (hipStream_t)stream);
+  return check_launch(who);
+}
+
+extern "C" llmdec_status llmdec_op_prefill_attention(const llmdec_config *cfg, const float *q, int32_t n_seqs,
+                                                    int32_t n_tokens, int32_t max_q_len, const int32_t *cu_seqlens,
+                                                    const int32_t *start_pos, const int32_t *block_tables,
+                                                    int32_t max_pages, const llmdec_kv_pool *pool, int32_t layer,
+                                                    float *out, void *ws, size_t ws_bytes, llmdec_stream stream) {
+  const char *who = "op_prefill_attention";
+  llmdec_status st = check_config(cfg, who);
+  if (st == LLMDEC_OK) st = check_pool(pool, *cfg, layer, who);
+  if (st == LLMDEC_OK) st = check_ws(ws, ws_bytes, kWsHeader, who);
+  if (st != LLMDEC_OK) return st;
+  if (!q || !cu_seqlens || !start_pos || !block_tables || !out)
+    return set_error(LLMDEC_E_INVALID, "%s: NULL pointer", who);
+  if (n_seqs <= 0 || n_tokens <= 0 || max_q_len <= 0 || max_pages <= 0)
+    return set_error(LLMDEC_E_INVALID, "%s: sizes out of range", who);
+  uint16_t *pk, *pv;
+  pool_layer(pool, layer, &pk, &pv);
+  launch_prefill_attention(*cfg, q, cfg->hidden, n_seqs, max_q_len, cu_seqlens, start_pos, block_tables, max_pages,
+                           pk, pv, pool->num_pages, out, nullptr, nullptr, 0, (uint32_t *)ws, (hipStream_t)stream);
+  return check_launch(who);
+}
+
+extern "C" llmdec_status llmdec_op_silu_mul(const float *gate, const float *up, int32_t rows, int32_t n, float *out,
+                                           llmdec_stream stream) {
+  if (!gate || !up || !out) return set_error(LLMDEC_E_INVALID, "op_silu_mul: NULL pointer");
+  if (rows <= 0 || n <= 0) return set_error(LLMDEC_E_INVALID, "op_silu_mul: rows=%d n=%d out of range", rows, n);
+  launch_silu_mul(gate, up, n, 16, rows, n, out, nullptr, nullptr, 0, (hipStream_t)stream);
+  return check_launch("op_silu_mul");
+}
+
+extern "C" llmdec_status llmdec_op_lm_head_argmax(const float *x, int32_t rows, int32_t hidden,
+                                                 const void *lm_head_packed, int32_t vocab, int32_t *next,
+                                                 float *logits_out, void *ws, size_t ws_bytes, llmdec_stream stream) {
+  if (!x || !lm_head_packed || !next) return set_error(LLMDEC_E_INVALID, "op_lm_head_argmax: NULL pointer");
+  if (rows <= 0 || hidden <= 0 || vocab <= 0 || vocab % 16)
+    return set_error(LLMDEC_E_INVALID, "op_lm_head_argmax: rows=%d hidden=%d vocab=%d out of range", rows, hidden, vocab);
+  size_t hi_off, lo_off, part_off;
+  size_t need = op_linear_parts(rows, hidden, vocab, &hi_off, &lo_off, &part_off);
+  const size_t logit_off = need;
+  if (!logits_out) need += al((size_t)rows * vocab * sizeof(float));
+  llmdec_status st = check_ws(ws, ws_bytes, need, "op_lm_head_argmax");
+  if (st != LLMDEC_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  Act act;
+  act.rows = rows;
+  if (rows == 1) {
+    act.f32 = x;
+  } else {
+    act.kpad = round_up(hidden, kTileK);
+    act.hi = at<uint16_t>(ws, hi_off);
+    act.lo = at<uint16_t>(ws, lo_off);
+    launch_split(x, hidden, rows, hidden, (uint16_t *)act.hi, (uint16_t *)act.lo, act.kpad, s);
+  }
+  float *lg = logits_out ? logits_out : at<float>(ws, logit_off);
+  launch_linear(act, (const uint16_t *)lm_head_packed, vocab, hidden, lg, vocab, kStore, at<float>(ws, part_off),
+                linear_partial_floats(rows, vocab, hidden), s);
+  launch_argmax(lg, rows, vocab, next, s);
+  return check_launch("op_lm_head_argmax");
+}

@@ -1,0 +1,90 @@
+// Shared helpers for the libllmdec kernels and host code (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "llmdec.h"
+
+namespace llmdec {
+
+constexpr int kPage = 16;       // tokens per KV page
+constexpr int kTileRows = 16;   // packed-matrix tile: 16 rows ...
+constexpr int kTileK = 32;      // ... x 32 columns = one 16x16x32 MFMA operand
+constexpr int kTileElems = 512; // bf16 elements per tile (1 KiB)
+
+// Device error bits (sticky word at the start of every workspace).
+constexpr uint32_t kErrPage = 1u;   // block-table page id out of range
+constexpr uint32_t kErrPos = 2u;    // position beyond the block-table row
+constexpr uint32_t kErrToken = 4u;  // token id out of range
+constexpr size_t kWsHeader = 256;   // bytes reserved for the error word
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte load (weights and cache pages are read once per step).
+__device__ inline uint4 load_stream(const uint4 *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+__host__ __device__ inline size_t round_up_sz(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+// Element offset of (row, col) inside a packed matrix with kt_count tiles per
+// 16-row block.  Tile (nb, kt) holds rows 16nb..16nb+15 and columns
+// 32kt..32kt+31; inside it, lane l (0..63) owns 8 consecutive elements: row
+// l%16, columns 8*(l/16)..8*(l/16)+7.  That is exactly the operand a wave feeds
+// one 16x16x32 bf16 MFMA, so a wave loads a whole tile as one contiguous 1 KiB.
+__host__ __device__ inline size_t packed_offset(int row, int col, int kt_count) {
+  const int nb = row >> 4, kt = col >> 5;
+  const int lane = (row & 15) | (((col >> 3) & 3) << 4);
+  return ((((size_t)nb * kt_count + kt) << 6) + lane) * 8 + (col & 7);
+}
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ inline float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round to nearest bf16, ties to even (inputs are finite here).
+__device__ inline uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// hi = bf16(x), lo = bf16(x - hi): x == hi + lo to about 2^-17 relative.
+__device__ inline void split_bf16(float x, uint16_t &hi, uint16_t &lo) {
+  hi = f32_to_bf16(x);
+  lo = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ inline void raise_error(uint32_t *err, uint32_t bits) {
+  if (err) atomicOr(err, bits);
+}
+
+}  // namespace llmdec
+
+// The opaque pool handle (host side).
+struct llmdec_kv_pool {
+  llmdec_config cfg;
+  void *base;           // device base of the pool
+  size_t bytes;
+  int32_t num_pages;
+  int32_t *stack;       // free-page stack; top = stack[top-1]
+  int32_t top;
+  uint8_t *is_free;     // per page: 1 if on the free list
+};

@@ -1,0 +1,317 @@
+// Small bandwidth-bound kernels: weight packing, embedding lookup, RMSNorm,
+// activation splitting, rotary embedding + paged KV append, SwiGLU gate,
+// argmax, and the test-only cache gather.
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace llmdec {
+
+// ---------------------------------------------------------------- packing
+// One thread moves the 8 elements one lane owns in one tile.  Source 16-row
+// block nb lands at destination block nb * nb_stride (nb_stride 2 interleaves
+// two matrices block by block).
+__global__ void pack_matrix_kernel(int rows, int cols, int kt_count, int nb_stride, const uint16_t *__restrict__ src,
+                                   uint16_t *__restrict__ dst) {
+  const size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t n_slots = (size_t)(rows / 16) * kt_count * 64;
+  if (g >= n_slots) return;
+  const int lane = (int)(g & 63);
+  const size_t tile = g >> 6;
+  const int nb = (int)(tile / kt_count), kt = (int)(tile % kt_count);
+  const int r = nb * 16 + (lane & 15);
+  const int c0 = kt * 32 + (lane >> 4) * 8;
+  uint16_t v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (c0 + j < cols) ? src[(size_t)r * cols + c0 + j] : (uint16_t)0;
+  uint4 o;
+  o.x = v[0] | ((uint32_t)v[1] << 16);
+  o.y = v[2] | ((uint32_t)v[3] << 16);
+  o.z = v[4] | ((uint32_t)v[5] << 16);
+  o.w = v[6] | ((uint32_t)v[7] << 16);
+  const size_t dtile = (size_t)nb * nb_stride * kt_count + kt;
+  *reinterpret_cast<uint4 *>(dst + (dtile * 64 + lane) * 8) = o;
+}
+
+void launch_pack_matrix(int rows, int cols, const uint16_t *src, uint16_t *dst, hipStream_t s, int nb_stride) {
+  const int kt = round_up(cols, kTileK) / kTileK;
+  const size_t n = (size_t)(rows / 16) * kt * 64;
+  pack_matrix_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(rows, cols, kt, nb_stride, src, dst);
+}
+
+// ---------------------------------------------------------------- embedding ([F] §2.2.1: row lookup)
+__global__ void embed_kernel(const uint16_t *__restrict__ embed, const int32_t *__restrict__ tokens, int hidden,
+                             int vocab, float *__restrict__ x, uint32_t *err) {
+  const int t = blockIdx.x;
+  const int tok = tokens[t];
+  const bool ok = tok >= 0 && tok < vocab;
+  if (!ok && threadIdx.x == 0) raise_error(err, kErrToken);
+  const uint16_t *row = embed + (size_t)(ok ? tok : 0) * hidden;
+  for (int i = threadIdx.x; i < hidden; i += blockDim.x) x[(size_t)t * hidden + i] = ok ? bf16_to_f32(row[i]) : 0.f;
+}
+
+void launch_embed(const uint16_t *embed, const int32_t *tokens, int n_tokens, int hidden, int vocab, float *x,
+                  uint32_t *err, hipStream_t s) {
+  if (n_tokens > 0) embed_kernel<<<n_tokens, 256, 0, s>>>(embed, tokens, hidden, vocab, x, err);
+}
+
+// ---------------------------------------------------------------- split writer
+// Writes value v of activation (r, c) to the f32 and/or tiled hi/lo outputs.
+__device__ inline void store_act(float v, int r, int c, int n, float *out_f32, uint16_t *hi, uint16_t *lo, int kpad) {
+  if (out_f32) out_f32[(size_t)r * n + c] = v;
+  if (hi) {
+    uint16_t h, l;
+    split_bf16(v, h, l);
+    const size_t o = packed_offset(r, c, kpad >> 5);
+    hi[o] = h;
+    lo[o] = l;
+  }
+}
+
+// ---------------------------------------------------------------- RMSNorm ([E] §4.2)
+// y = x * (mean(x^2) + eps)^(-1/2) * gamma, eps inside the root.  One block per row.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ x, int ld_x,
+                                                      const int32_t *__restrict__ cu_last,
+                                                      const uint16_t *__restrict__ gamma, int n, float eps,
+                                                      float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad) {
+  const int r = blockIdx.x;
+  const int src_row = cu_last ? cu_last[r + 1] - 1 : r;
+  const float *xr = x + (size_t)src_row * ld_x;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const float v = xr[i];
+    ss = fmaf(v, v, ss);
+  }
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float total = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.0f / sqrtf(total / (float)n + eps);
+  for (int i = threadIdx.x; i < n; i += 256) store_act(xr[i] * inv * bf16_to_f32(gamma[i]), r, i, n, out_f32, out_hi, out_lo, kpad);
+  if (out_hi)
+    for (int i = n + threadIdx.x; i < kpad; i += 256) {
+      const size_t o = packed_offset(r, i, kpad >> 5);
+      out_hi[o] = 0;
+      out_lo[o] = 0;
+    }
+}
+
+void launch_rmsnorm(const float *x, int ld_x, const int32_t *cu_last, const uint16_t *gamma, int rows, int n,
+                    float eps, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad, hipStream_t s) {
+  if (rows > 0)
+    rmsnorm_kernel<<<rows, 256, 0, s>>>(x, ld_x, cu_last, gamma, n, eps, out_f32, out_hi, out_lo, kpad);
+}
+
+// ---------------------------------------------------------------- fp32 -> tiled hi/lo
+__global__ void split_kernel(const float *__restrict__ a, int ld, int rows, int cols, uint16_t *hi, uint16_t *lo,
+                             int kpad) {
+  const size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per_row = kpad / 8;
+  if (g >= (size_t)rows * per_row) return;
+  const int r = (int)(g / per_row), c0 = (int)(g % per_row) * 8;
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    uint16_t h0 = 0, l0 = 0, h1 = 0, l1 = 0;
+    if (c0 + j < cols) split_bf16(a[(size_t)r * ld + c0 + j], h0, l0);
+    if (c0 + j + 1 < cols) split_bf16(a[(size_t)r * ld + c0 + j + 1], h1, l1);
+    h[j / 2] = h0 | ((uint32_t)h1 << 16);
+    l[j / 2] = l0 | ((uint32_t)l1 << 16);
+  }
+  const size_t o = packed_offset(r, c0, kpad >> 5);
+  *reinterpret_cast<uint4 *>(hi + o) = make_uint4(h[0], h[1], h[2], h[3]);
+  *reinterpret_cast<uint4 *>(lo + o) = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+void launch_split(const float *a, int ld, int rows, int cols, uint16_t *hi, uint16_t *lo, int kpad, hipStream_t s) {
+  const size_t n = (size_t)rows * (kpad / 8);
+  if (n) split_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a, ld, rows, cols, hi, lo, kpad);
+}
+
+// ---------------------------------------------------------------- token -> (sequence, position)
+__global__ void token_map_kernel(const int32_t *__restrict__ cu, const int32_t *__restrict__ start, int32_t *tok_seq,
+                                 int32_t *tok_pos) {
+  const int s = blockIdx.x;
+  const int b = cu[s], e = cu[s + 1], p0 = start[s];
+  for (int i = b + threadIdx.x; i < e; i += blockDim.x) {
+    tok_seq[i] = s;
+    tok_pos[i] = p0 + (i - b);
+  }
+}
+
+void launch_token_map(const int32_t *cu, const int32_t *start, int n_seqs, int32_t *tok_seq, int32_t *tok_pos,
+                      hipStream_t s) {
+  if (n_seqs > 0) token_map_kernel<<<n_seqs, 256, 0, s>>>(cu, start, tok_seq, tok_pos);
+}
+
+// ---------------------------------------------------------------- RoPE + paged append ([E] §4.3)
+// One block per new token.  Pair i of every head turns by pos * theta^(-2i/D);
+// the angle and its sine/cosine are formed in double so that they do not
+// depend on fp32 range reduction at positions in the thousands.  q is rotated
+// in place; rotated k and plain v are rounded to bf16 and written to the page
+// slot bt[seq][pos/16], offset pos%16 (K as [h][o][d], V as [h][d][o]).
+__global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qkv, int ld_qkv, int n_heads,
+                                                          int head_dim, float theta,
+                                                          const int32_t *__restrict__ tok_seq,
+                                                          const int32_t *__restrict__ tok_pos,
+                                                          const int32_t *__restrict__ block_tables, int max_pages,
+                                                          uint16_t *__restrict__ pool_k, uint16_t *__restrict__ pool_v,
+                                                          int num_pages, uint32_t *err) {
+  const int t = blockIdx.x;
+  const int half = head_dim / 2;
+  const int hidden = n_heads * head_dim;
+  __shared__ float cs[64], sn[64];
+  const int seq = tok_seq ? tok_seq[t] : t;
+  const int pos = tok_pos[t];
+  if ((int)threadIdx.x < half) {
+    const int i = threadIdx.x;
+    const double inv_freq = pow((double)theta, -2.0 * (double)i / (double)head_dim);
+    double sd, cd;
+    sincos((double)pos * inv_freq, &sd, &cd);
+    cs[i] = (float)cd;
+    sn[i] = (float)sd;
+  }
+  __syncthreads();
+  int page = -1;
+  const int blk = pos >> 4, off = pos & 15;
+  if (pos < 0 || blk >= max_pages) {
+    if (threadIdx.x == 0) raise_error(err, kErrPos);
+  } else {
+    page = block_tables[(size_t)seq * max_pages + blk];
+    if (page < 0 || page >= num_pages) {
+      if (threadIdx.x == 0) raise_error(err, kErrPage);
+      page = -1;
+    }
+  }
+  float *q = qkv + (size_t)t * ld_qkv;
+  const float *k = q + hidden;
+  const float *v = q + 2 * hidden;
+  for (int g = threadIdx.x; g < n_heads * half; g += 256) {
+    const int h = g / half, i = g % half;
+    const float c = cs[i], s = sn[i];
+    const int d = h * head_dim + 2 * i;
+    const float q0 = q[d], q1 = q[d + 1];
+    q[d] = q0 * c - q1 * s;
+    q[d + 1] = q0 * s + q1 * c;
+    if (page >= 0) {
+      const float k0 = k[d], k1 = k[d + 1];
+      const uint32_t kb = f32_to_bf16(k0 * c - k1 * s) | ((uint32_t)f32_to_bf16(k0 * s + k1 * c) << 16);
+      const size_t kbase = (((size_t)page * n_heads + h) * 16 + off) * head_dim + 2 * i;
+      *reinterpret_cast<uint32_t *>(pool_k + kbase) = kb;
+      const size_t vbase = (((size_t)page * n_heads + h) * head_dim + 2 * i) * 16 + off;
+      pool_v[vbase] = f32_to_bf16(v[d]);
+      pool_v[vbase + 16] = f32_to_bf16(v[d + 1]);
+    }
+  }
+}
+
+void launch_rope_append(const llmdec_config &cfg, float *qkv, int ld_qkv, int n_tokens, const int32_t *tok_seq,
+                        const int32_t *tok_pos, const int32_t *block_tables, int max_pages, uint16_t *pool_k,
+                        uint16_t *pool_v, int num_pages, uint32_t *err, hipStream_t s) {
+  if (n_tokens > 0)
+    rope_append_kernel<<<n_tokens, 256, 0, s>>>(qkv, ld_qkv, cfg.n_heads, cfg.head_dim, cfg.rope_theta, tok_seq,
+                                                tok_pos, block_tables, max_pages, pool_k, pool_v, num_pages, err);
+}
+
+// ---------------------------------------------------------------- SwiGLU gate ([W] §1.2, [E] §4.2)
+__global__ void silu_mul_kernel(const float *__restrict__ g, const float *__restrict__ u, int ld_in, int blk, int n,
+                                int rows, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad) {
+  const int width = out_hi ? kpad : n;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)rows * width) return;
+  const int r = (int)(idx / width), j = (int)(idx % width);
+  if (j >= n) {  // zero the padding columns of the split output
+    const size_t o = packed_offset(r, j, kpad >> 5);
+    out_hi[o] = 0;
+    out_lo[o] = 0;
+    return;
+  }
+  const size_t off = (size_t)r * ld_in + (size_t)(j >> 4) * blk + (j & 15);
+  const float gv = g[off], uv = u[off];
+  store_act(gv / (1.0f + expf(-gv)) * uv, r, j, n, out_f32, out_hi, out_lo, kpad);
+}
+
+void launch_silu_mul(const float *g, const float *u, int ld_in, int blk, int rows, int n, float *out_f32,
+                     uint16_t *out_hi, uint16_t *out_lo, int kpad, hipStream_t s) {
+  const size_t total = (size_t)rows * (out_hi ? kpad : n);
+  if (total)
+    silu_mul_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(g, u, ld_in, blk, n, rows, out_f32, out_hi,
+                                                                     out_lo, kpad);
+}
+
+// ---------------------------------------------------------------- greedy argmax ([F] §2.2.3)
+// Largest logit per row; among equal values the lowest index wins.
+__global__ __launch_bounds__(256) void argmax_kernel(const float *__restrict__ logits, int vocab, int32_t *next) {
+  const int r = blockIdx.x;
+  const float *x = logits + (size_t)r * vocab;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < vocab; i += 256) {
+    const float v = x[i];
+    if (v > best) {  // ascending i per thread: strict > keeps the first
+      best = v;
+      bi = i;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ov > best || (ov == best && oi < bi)) {
+      best = ov;
+      bi = oi;
+    }
+  }
+  __shared__ float bv[4];
+  __shared__ int bix[4];
+  if ((threadIdx.x & 63) == 0) {
+    bv[threadIdx.x >> 6] = best;
+    bix[threadIdx.x >> 6] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (bv[w] > best || (bv[w] == best && bix[w] < bi)) {
+        best = bv[w];
+        bi = bix[w];
+      }
+    next[r] = (bi == 0x7fffffff) ? 0 : bi;
+  }
+}
+
+void launch_argmax(const float *logits, int rows, int vocab, int32_t *next, hipStream_t s) {
+  if (rows > 0) argmax_kernel<<<rows, 256, 0, s>>>(logits, vocab, next);
+}
+
+// ---------------------------------------------------------------- test-only gather
+__global__ void gather_kv_kernel(const uint16_t *__restrict__ pk, const uint16_t *__restrict__ pv, int num_pages,
+                                 int n_heads, int head_dim, const int32_t *__restrict__ row, uint16_t *k_out,
+                                 uint16_t *v_out) {
+  const int p = blockIdx.x;
+  const int page = row[p >> 4], off = p & 15;
+  const bool ok = page >= 0 && page < num_pages;
+  for (int e = threadIdx.x; e < n_heads * head_dim; e += blockDim.x) {
+    const int h = e / head_dim, d = e % head_dim;
+    const size_t o = (size_t)p * n_heads * head_dim + e;
+    k_out[o] = ok ? pk[(((size_t)page * n_heads + h) * 16 + off) * head_dim + d] : (uint16_t)0xffff;
+    v_out[o] = ok ? pv[(((size_t)page * n_heads + h) * head_dim + d) * 16 + off] : (uint16_t)0xffff;
+  }
+}
+
+void launch_gather_kv(const uint16_t *pk, const uint16_t *pv, int num_pages, int n_heads, int head_dim,
+                      const int32_t *row, int n_tokens, uint16_t *k_out, uint16_t *v_out, hipStream_t s) {
+  if (n_tokens > 0) gather_kv_kernel<<<n_tokens, 256, 0, s>>>(pk, pv, num_pages, n_heads, head_dim, row, k_out, v_out);
+}
+
+__global__ void fill_u32_kernel(uint32_t *p, uint32_t value, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = value;
+}
+
+void launch_fill_u32(uint32_t *p, uint32_t value, size_t n, hipStream_t s) {
+  if (n) fill_u32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p, value, n);
+}
+
+}  // namespace llmdec

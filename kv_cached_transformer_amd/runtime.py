@@ -1,0 +1,102 @@
+"""Device-memory plumbing around libllmdec for PyTorch callers.
+
+PyTorch only allocates device memory and supplies the stream; every step of
+the decoder runs in the library's kernels.  Weights and cache contents are
+passed as bf16 bit patterns (numpy uint16), held on the device as int16
+tensors.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import llmdec as L
+
+
+def stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def dev_u16(a: np.ndarray) -> torch.Tensor:
+    """Upload a uint16 bit-pattern array as an int16 device tensor."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda")
+
+
+def dev_i32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32))).to("cuda")
+
+
+def dev_f32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.float32))).to("cuda")
+
+
+def host_u16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+class PackedLayer:
+    """One layer packed for the kernels; owns its device buffer."""
+
+    def __init__(self, cfg, tensors: dict, keep_plain: bool = False):
+        nbytes = L.llmdec_packed_layer_bytes(cfg)
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        plain = {k: dev_u16(v) for k, v in tensors.items()}
+        w = L.llmdec_layer_weights(*(plain[k].data_ptr() for k in
+                                     ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")))
+        self.struct = L.llmdec_pack_layer(cfg, w, self.buf.data_ptr(), nbytes, stream())
+        torch.cuda.current_stream().synchronize()
+        self.plain = plain if keep_plain else None
+
+
+class PackedMatrix:
+    def __init__(self, rows: int, cols: int, bits: np.ndarray):
+        nbytes = L.llmdec_packed_matrix_bytes(rows, cols)
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        src = dev_u16(bits)
+        L.llmdec_pack_matrix(rows, cols, src.data_ptr(), self.buf.data_ptr(), nbytes, stream())
+        torch.cuda.current_stream().synchronize()
+        self.ptr = self.buf.data_ptr()
+
+
+class Pool:
+    """A device KV pool plus its host handle."""
+
+    def __init__(self, cfg, num_pages: int, free_order=None, fill_bits: int | None = None):
+        self.cfg = cfg
+        self.num_pages = num_pages
+        self.nbytes = L.llmdec_kv_pool_bytes(cfg, num_pages)
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device="cuda")
+        if fill_bits is not None:
+            self.buf.view(torch.int16).fill_(np.int16(np.uint16(fill_bits).view(np.int16)))
+        fo = None if free_order is None else np.ascontiguousarray(free_order, dtype=np.int32)
+        self.handle = L.llmdec_kv_pool_create(cfg, self.buf.data_ptr(), self.nbytes, num_pages, fo)
+
+    def alloc(self, tokens_needed, row: np.ndarray, n_pages: int, max_pages: int) -> int:
+        return L.llmdec_kv_pool_alloc(self.handle, tokens_needed, row, n_pages, max_pages)
+
+    def layer_views(self, layer: int):
+        """(K, V) int16 views of one layer: K [pages][H][16][D], V [pages][H][D][16]."""
+        c = self.cfg
+        per = self.num_pages * c.n_kv_heads * 16 * c.head_dim
+        flat = self.buf.view(torch.int16)
+        base = layer * 2 * per
+        k = flat[base: base + per].view(self.num_pages, c.n_kv_heads, 16, c.head_dim)
+        v = flat[base + per: base + 2 * per].view(self.num_pages, c.n_kv_heads, c.head_dim, 16)
+        return k, v
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            L.llmdec_kv_pool_destroy(h)
+            self.handle = None
+
+
+class Workspace:
+    def __init__(self, nbytes: int):
+        self.nbytes = int(nbytes)
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device="cuda")
+        self.ptr = self.buf.data_ptr()
+        L.llmdec_workspace_reset(self.ptr, self.nbytes, stream())
+
+    def error_bits(self) -> int:
+        return L.llmdec_workspace_error(self.ptr, stream())

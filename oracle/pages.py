@@ -13,7 +13,9 @@ Readings (the pages are silent on these):
   appended to the sequence's block-table row; if the pool cannot cover the
   growth, nothing changes and the call fails ("no pages");
 * position p of a sequence lives in page row[p // 16] at in-page offset p % 16;
-* inside a page, each of K and V is laid out [kv_head][16][head_dim].
+* inside a page, K is laid out [kv_head][16][head_dim] and V is laid out
+  [kv_head][head_dim][16] (transposed); float results do not depend on this,
+  only the pool-image comparisons do.
 
 Parity pins: the slot formula against a brute-force page walk, pool sizing
 against [E] §3.4's 1 GiB example, paged attention equal to contiguous
@@ -84,7 +86,9 @@ class PagePool:
 
 
 class PagedKV:
-    """A paged mirror of the cache: per layer, K and V pools [num_pages][Hkv][16][D] (float64 holding bf16 values).
+    """A paged mirror of the cache: per layer, K pool [num_pages][Hkv][16][D] and V pool [num_pages][Hkv][D][16].
+
+    Values are float64 holding bf16 values.
 
     Same interface as decoder.ContiguousKV; positions are found through block-table rows.
     """
@@ -92,7 +96,7 @@ class PagedKV:
     def __init__(self, n_layers, n_kv_heads, head_dim, num_pages, block_rows: dict):
         self.L, self.H, self.D = n_layers, n_kv_heads, head_dim
         self.K = np.zeros((n_layers, num_pages, n_kv_heads, PAGE, head_dim))
-        self.V = np.zeros_like(self.K)
+        self.V = np.zeros((n_layers, num_pages, n_kv_heads, head_dim, PAGE))
         self.rows = block_rows          # seq id -> block-table row (list of page ids)
         self.len = {}
 
@@ -103,14 +107,14 @@ class PagedKV:
         assert pos == self.length(layer, seq), "append out of order"
         pg, off = slot_of(self.rows[seq], pos)
         self.K[layer, pg, :, off, :] = k
-        self.V[layer, pg, :, off, :] = v
+        self.V[layer, pg, :, :, off] = v
         self.len[(layer, seq)] = pos + 1
 
     def preload(self, layer, seq, k, v):
         for p in range(k.shape[0]):
             pg, off = slot_of(self.rows[seq], p)
             self.K[layer, pg, :, off, :] = k[p]
-            self.V[layer, pg, :, off, :] = v[p]
+            self.V[layer, pg, :, :, off] = v[p]
         self.len[(layer, seq)] = k.shape[0]
 
     def keys_values(self, layer, seq, upto):
@@ -120,5 +124,5 @@ class PagedKV:
         for p in range(upto):
             pg, off = slot_of(self.rows[seq], p)
             K[p] = self.K[layer, pg, :, off, :]
-            V[p] = self.V[layer, pg, :, off, :]
+            V[p] = self.V[layer, pg, :, :, off]
         return K, V

@@ -191,21 +191,21 @@ def first_tokens(workload: int, n: int, vocab: int) -> np.ndarray:
 def scatter_kv_into_pool(pool_k: np.ndarray, pool_v: np.ndarray, row: np.ndarray, k: np.ndarray, v: np.ndarray):
     """Place a sequence's cached K/V (positions 0..n-1) into a host image of one layer's pool.
 
-    pool_k/pool_v: [num_pages][Hkv][PAGE][D] uint16; row: the sequence's block-table row.
-    Position p lives at page row[p // PAGE], in-page offset p % PAGE.
+    pool_k: [num_pages][Hkv][PAGE][D], pool_v: [num_pages][Hkv][D][PAGE] (uint16); row: the
+    sequence's block-table row.  Position p lives at page row[p // PAGE], in-page offset p % PAGE.
     """
     n = k.shape[0]
     full = n // PAGE
     if full:
         pk = k[: full * PAGE].reshape(full, PAGE, k.shape[1], k.shape[2]).transpose(0, 2, 1, 3)
-        pv = v[: full * PAGE].reshape(full, PAGE, v.shape[1], v.shape[2]).transpose(0, 2, 1, 3)
+        pv = v[: full * PAGE].reshape(full, PAGE, v.shape[1], v.shape[2]).transpose(0, 2, 3, 1)
         pool_k[row[:full]] = pk
         pool_v[row[:full]] = pv
     rem = n - full * PAGE
     if rem:
         pg = row[full]
         pool_k[pg, :, :rem, :] = k[full * PAGE:].transpose(1, 0, 2)
-        pool_v[pg, :, :rem, :] = v[full * PAGE:].transpose(1, 0, 2)
+        pool_v[pg, :, :, :rem] = v[full * PAGE:].transpose(1, 2, 0)
 
 
 # --- workload recipes -------------------------------------------------------------------------

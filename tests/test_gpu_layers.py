@@ -1,0 +1,130 @@
+"""Layer-step parity: llmdec_layer_decode / llmdec_layer_prefill against the oracle's layer_step.
+
+Full-size cases are the 7B-layer workloads: decode at batch 1 with 2048
+cached tokens, decode over 32 sequences with contexts in [128, 4096], and a
+4 x 512 prefill.  Small cases cover the batched (skinny) and tiled matrix
+paths with ragged sizes and chunked prefill (new tokens after a cached prefix).
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import decoder as od
+from oracle import pages as op
+from tests.gpu_util import assert_close, banner, f32_from_bf16
+from tests.layer_harness import LayerCase
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from kv_cached_transformer_amd import llmdec
+    llmdec.lib()
+    return llmdec
+
+
+@pytest.fixture(scope="module")
+def R():
+    from kv_cached_transformer_amd import runtime
+    return runtime
+
+
+TINY1 = synth.ModelShape(n_layers=1, hidden=256, n_heads=4, n_kv_heads=4, head_dim=64, intermediate=688, vocab=1024)
+
+
+def check_new_slots(case, new_tokens, tag):
+    """New K/V written by the step: slot set exact (sentinel), values equal to the oracle's bf16 up to rare 1-ulp flips."""
+    kimg, vimg = case.pool_images()
+    H, D = case.shape.n_kv_heads, case.shape.head_dim
+    written = np.zeros((case.num_pages, 16), bool)
+    flips = 0
+    for s, p in new_tokens:
+        pg, off = op.slot_of(case.bt[s], p)
+        written[pg, off] = True
+        kk = f32_from_bf16(kimg[pg, :, off, :]).astype(np.float64)
+        vv = f32_from_bf16(vimg[pg, :, :, off]).astype(np.float64)
+        kr, vr = case.kv.k[(0, s)][p], case.kv.v[(0, s)][p]
+        for got, ref in ((kk, kr), (vv, vr)):
+            flips += int((got != ref).sum())
+            assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -7 + 1e-30), f"{tag}: slot value off by > 1 ulp"
+    total = len(new_tokens) * H * D * 2
+    print(f"[parity] {tag}: new K/V slots {len(new_tokens)}, 1-ulp flips {flips}/{total}", flush=True)
+    assert flips <= max(4, 0.005 * total)
+    # everything else is either the seeded history (unchanged) or the 0xFFFF sentinel
+    hist = case.kimg0.transpose(0, 2, 1, 3), case.vimg0.transpose(0, 3, 1, 2)
+    now = kimg.transpose(0, 2, 1, 3), vimg.transpose(0, 3, 1, 2)
+    for a, b in zip(hist, now):
+        assert np.array_equal(a[~written], b[~written]), f"{tag}: a slot outside the new tokens changed"
+
+
+def run_decode(L, R, shape, workload, ctxs, x_in, tag):
+    banner(f"{tag}: layer_decode n={len(ctxs)}")
+    case = LayerCase(L, R, shape, workload, ctxs, [1] * len(ctxs))
+    n = len(ctxs)
+    ws = case.workspace(n)
+    xd = R.dev_f32(x_in)
+    L.llmdec_layer_decode(case.cfg, case.packed.struct, 0, xd.data_ptr(), n, R.dev_i32(ctxs).data_ptr(),
+                          case.bt_dev.data_ptr(), case.max_pages, case.pool.handle, ws.ptr, ws.nbytes, R.stream())
+    torch.cuda.synchronize()
+    assert ws.error_bits() == 0
+    got = xd.cpu().numpy()
+    ref = od.layer_step(shape, case.lw.tensors, 0, x_in, list(range(n)), ctxs, case.kv)
+    assert_close(f"{tag} layer output", got, ref)
+    check_new_slots(case, [(s, c) for s, c in enumerate(ctxs)], tag)
+
+
+def run_prefill(L, R, shape, workload, starts, lens, x_in, tag):
+    banner(f"{tag}: layer_prefill starts={starts[:4]} lens={lens[:4]}")
+    case = LayerCase(L, R, shape, workload, starts, lens)
+    n = len(lens)
+    T = int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ws = case.workspace(T)
+    xd = R.dev_f32(x_in)
+    L.llmdec_layer_prefill(case.cfg, case.packed.struct, 0, xd.data_ptr(), n, T, max(lens), R.dev_i32(cu).data_ptr(),
+                           R.dev_i32(starts).data_ptr(), case.bt_dev.data_ptr(), case.max_pages, case.pool.handle,
+                           ws.ptr, ws.nbytes, R.stream())
+    torch.cuda.synchronize()
+    assert ws.error_bits() == 0
+    got = xd.cpu().numpy()
+    seqs = np.repeat(np.arange(n), lens)
+    pos = np.concatenate([np.arange(s0, s0 + ln) for s0, ln in zip(starts, lens)])
+    ref = od.layer_step(shape, case.lw.tensors, 0, x_in, seqs, pos, case.kv)
+    assert_close(f"{tag} layer output", got, ref)
+    check_new_slots(case, list(zip(seqs.tolist(), pos.tolist())), tag)
+
+
+# ----------------------------------------------------------------------------- small shapes
+def test_decode_tiny_batch1(L, R):
+    run_decode(L, R, TINY1, 91, [37], synth.hidden_input(91, 1, 256), "tiny decode b1")
+
+
+def test_decode_tiny_batched_ragged(L, R):
+    ctxs = [0, 15, 16, 17, 100, 3]
+    run_decode(L, R, TINY1, 92, ctxs, synth.hidden_input(92, len(ctxs), 256), "tiny decode b6")
+
+
+def test_prefill_tiny_chunked(L, R):
+    starts, lens = [0, 16, 5, 0], [1, 17, 40, 64]
+    run_prefill(L, R, TINY1, 93, starts, lens, synth.hidden_input(93, sum(lens), 256), "tiny prefill chunked")
+
+
+def test_prefill_tiny_single_token(L, R):
+    run_prefill(L, R, TINY1, 94, [20], [1], synth.hidden_input(94, 1, 256), "tiny prefill 1 token")
+
+
+# ----------------------------------------------------------------------------- 7B layer workloads
+def test_7b_layer_decode_batch1_ctx2048(L, R):
+    run_decode(L, R, synth.LLAMA7B_LAYER, 2, [2048], synth.hidden_input(2, 1, 4096), "7B decode b1 ctx2048")
+
+
+def test_7b_layer_decode_batch32(L, R):
+    ctxs = synth.context_lengths(3, 32, 128, 4096)
+    run_decode(L, R, synth.LLAMA7B_LAYER, 3, ctxs.tolist(), synth.hidden_input(3, 32, 4096), "7B decode b32")
+
+
+def test_7b_layer_prefill_4x512(L, R):
+    lens = [512] * 4
+    run_prefill(L, R, synth.LLAMA7B_LAYER, 4, [0] * 4, lens, synth.hidden_input(4, 2048, 4096), "7B prefill 4x512")

@@ -1,0 +1,114 @@
+"""End-to-end greedy generation through llmdec_model_step_greedy against the oracle.
+
+The tiny 2-layer model: prefill a 32-token prompt, then 15 single-token steps
+(16 new tokens, 47 cached positions, a page boundary crossed at position 32).
+Every step's logits are compared; ids must agree wherever the oracle's top-2
+gap exceeds 1e-2, and both sides are fed the oracle's token (teacher forcing).
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import decoder as od
+from oracle import pages as op
+from tests.gpu_util import assert_close, banner, f32_from_bf16
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from kv_cached_transformer_amd import llmdec
+    llmdec.lib()
+    return llmdec
+
+
+@pytest.fixture(scope="module")
+def R():
+    from kv_cached_transformer_amd import runtime
+    return runtime
+
+
+class DeviceModel:
+    def __init__(self, L, R, mw):
+        s = mw.shape
+        self.cfg = L.make_config(s)
+        self.layers = [R.PackedLayer(self.cfg, lw.tensors) for lw in mw.layers]
+        self.embed = R.dev_u16(mw.embed)
+        self.final_norm = R.dev_u16(mw.final_norm)
+        self.lm_head = R.PackedMatrix(s.vocab, s.hidden, mw.lm_head)
+        self.struct, self._keep = L.make_model_weights(self.embed.data_ptr(), [p.struct for p in self.layers],
+                                                       self.final_norm.data_ptr(), self.lm_head.ptr)
+
+
+def test_tiny_model_greedy_generation(L, R):
+    banner("tiny model: prefill 32 + 15 decode steps")
+    shape = synth.TINY
+    mw = synth.model_weights(1, shape)
+    dm = DeviceModel(L, R, mw)
+    prompt = synth.prompt_ids(1, 32, shape.vocab)
+    n_new = 16
+    total = 32 + n_new - 1
+    num_pages = 4
+    order = synth.free_order(1, num_pages)
+    pool = R.Pool(dm.cfg, num_pages, order, fill_bits=0xFFFF)
+    max_pages = 4
+    row = np.full((1, max_pages), -1, np.int32)
+    ref_pool = op.PagePool(num_pages, order)
+    ref_row = [-1] * max_pages
+    ws = R.Workspace(L.llmdec_workspace_bytes(dm.cfg, 32, 1, max_pages))
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    logits = torch.empty(1, shape.vocab, dtype=torch.float32, device="cuda")
+
+    kv = od.ContiguousKV(shape.n_layers, shape.n_kv_heads, shape.head_dim)
+    npg = 0
+    feed = list(prompt)
+    pos0 = 0
+    ids = []
+    for step in range(n_new):
+        T = len(feed)
+        npg_new = pool.alloc(pos0 + T, row[0], npg, max_pages)
+        st, ref_n = ref_pool.alloc(pos0 + T, ref_row, npg, max_pages)
+        assert st == op.OK and ref_n == npg_new and row[0].tolist() == ref_row
+        npg = npg_new
+        bt = R.dev_i32(row)
+        toks = R.dev_i32(feed)
+        sp = R.dev_i32([pos0])
+        if step == 0:
+            cu = R.dev_i32([0, T])
+            L.llmdec_model_step_greedy(dm.cfg, dm.struct, 1, T, T, toks.data_ptr(), cu.data_ptr(), sp.data_ptr(),
+                                       bt.data_ptr(), max_pages, pool.handle, nxt.data_ptr(), logits.data_ptr(),
+                                       ws.ptr, ws.nbytes, R.stream())
+        else:
+            L.llmdec_model_step_greedy(dm.cfg, dm.struct, 1, 1, 1, toks.data_ptr(), None, sp.data_ptr(),
+                                       bt.data_ptr(), max_pages, pool.handle, nxt.data_ptr(), logits.data_ptr(),
+                                       ws.ptr, ws.nbytes, R.stream())
+        torch.cuda.synchronize()
+        ref_logits, _ = od.model_step(shape, mw, feed, [0] * T, list(range(pos0, pos0 + T)), kv)
+        got = logits.cpu().numpy()[0]
+        assert_close(f"tiny step {step} logits", got, ref_logits[0])
+        ref_id = od.greedy_token(ref_logits[0])
+        gid = int(nxt.cpu().numpy()[0])
+        assert gid == od.greedy_token(got)
+        if od.top2_gap(ref_logits[0]) > 1e-2:
+            assert gid == ref_id, f"step {step}: device {gid} oracle {ref_id}"
+        ids.append(ref_id)
+        pos0 += T
+        feed = [ref_id]
+    assert ws.error_bits() == 0
+    # pool contents: every written slot agrees with the oracle's stored bf16 K/V; the rest is sentinel
+    for layer in range(shape.n_layers):
+        kd, vd = pool.layer_views(layer)
+        kimg, vimg = R.host_u16(kd.contiguous()), R.host_u16(vd.contiguous())
+        written = np.zeros((num_pages, 16), bool)
+        for p in range(total):
+            pg, off = op.slot_of(row[0], p)
+            written[pg, off] = True
+            k = f32_from_bf16(kimg[pg, :, off, :]).astype(np.float64)
+            v = f32_from_bf16(vimg[pg, :, :, off]).astype(np.float64)
+            assert np.all(np.abs(k - kv.k[(layer, 0)][p]) <= np.abs(kv.k[(layer, 0)][p]) * 2 ** -7 + 1e-30)
+            assert np.all(np.abs(v - kv.v[(layer, 0)][p]) <= np.abs(kv.v[(layer, 0)][p]) * 2 ** -7 + 1e-30)
+        assert np.all(kimg.transpose(0, 2, 1, 3)[~written] == 0xFFFF)
+        assert np.all(vimg.transpose(0, 3, 1, 2)[~written] == 0xFFFF)
+    print(f"[parity] tiny generated ids {ids}", flush=True)

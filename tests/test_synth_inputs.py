@@ -34,11 +34,11 @@ def test_free_order_is_a_permutation():
 def test_scatter_places_positions_by_block_table():
     H, D = 2, 4
     pk = np.zeros((5, H, 16, D), np.uint16)
-    pv = np.zeros_like(pk)
+    pv = np.zeros((5, H, D, 16), np.uint16)
     row = np.array([3, 0, 4], np.int32)
     n = 37
     k = np.arange(n * H * D, dtype=np.uint16).reshape(n, H, D)
     synth.scatter_kv_into_pool(pk, pv, row, k, k + 1)
     for p in range(n):
         assert np.array_equal(pk[row[p // 16], :, p % 16, :], k[p])
-        assert np.array_equal(pv[row[p // 16], :, p % 16, :], k[p] + 1)
+        assert np.array_equal(pv[row[p // 16], :, :, p % 16], k[p] + 1)

@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Throughput of the KV-cached LLaMA-style decoder step on one MI355X.
+
+Headline: greedy decode of the full 32-layer 7B-shaped model (hidden 4096,
+32 heads x 128, intermediate 11008, vocab 32000, bf16 weights) over 64
+sequences whose cached contexts are seeded uniform in [256, 2048], in a paged
+KV pool of 16-token pages.  One step = one call of llmdec_model_step_greedy:
+embedding, 32 x (RMSNorm, fused q/k/v projection, RoPE + paged append, paged
+decode attention, o projection + residual, RMSNorm, gate/up, silu*up, down +
+residual), final RMSNorm, lm_head and argmax; the step's output ids are the
+next step's input ids, on the device, with no host synchronisation between
+steps.  value = 64 * K / (time of K steps), tokens/s.
+
+Also reported (sub-benchmarks, one layer each): decode at batch 1 over 2048
+cached tokens (weights and cache rotated over 4 copies so the 256 MB
+last-level cache does not serve them), decode over 32 sequences with contexts
+uniform in [128, 4096], and a 4 x 512 prefill.  Each gets its algorithmic
+bytes or FLOPs per step and the fraction of the MI355X peak.
+
+Inputs are seeded and synthetic: weights N(0, 0.02^2) in bf16 drawn on the
+device, RMSNorm gains 1, cached K/V N(0, 1) in bf16.  Timing uses HIP events
+on the stream the library launches on.  The cpu_baseline leg times the CPU
+oracle (float64 NumPy) on a bounded sample of the same decode workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only c5,c2,c3,c4]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # dense bf16 FLOP/s, MI355X
+METRIC = "decode tokens/s + % peak HBM BW (7B-shaped, paged KV); prefill tok/s + % MFMA"
+SEED = 20261202
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- device set-up helpers
+class Dev:
+    """Seeded device-side synthetic inputs and library objects for one model shape."""
+
+    def __init__(self, torch, L, R, shape, seed):
+        self.torch, self.L, self.R, self.shape = torch, L, R, shape
+        self.cfg = L.make_config(shape)
+        self.gen = torch.Generator(device="cuda")
+        self.gen.manual_seed(seed)
+
+    def normal_bf16(self, rows, cols, std):
+        t = self.torch.randn(rows, cols, device="cuda", generator=self.gen, dtype=self.torch.float32)
+        return (t * std).to(self.torch.bfloat16)
+
+    def packed_layer(self):
+        torch, s = self.torch, self.shape
+        ones = torch.ones(s.hidden, device="cuda", dtype=torch.bfloat16)
+        mats = {k: self.normal_bf16(r, c, 0.02) for k, (r, c) in s.matrix_shapes().items()}
+        w = self.L.llmdec_layer_weights(ones.data_ptr(), mats["wq"].data_ptr(), mats["wk"].data_ptr(),
+                                        mats["wv"].data_ptr(), mats["wo"].data_ptr(), ones.data_ptr(),
+                                        mats["w_gate"].data_ptr(), mats["w_up"].data_ptr(), mats["w_down"].data_ptr())
+        nbytes = self.L.llmdec_packed_layer_bytes(self.cfg)
+        buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        st = self.L.llmdec_pack_layer(self.cfg, w, buf.data_ptr(), nbytes, self.R.stream())
+        torch.cuda.synchronize()
+        return buf, st
+
+    def packed_matrix(self, rows, cols):
+        torch = self.torch
+        m = self.normal_bf16(rows, cols, 0.02)
+        nbytes = self.L.llmdec_packed_matrix_bytes(rows, cols)
+        buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.L.llmdec_pack_matrix(rows, cols, m.data_ptr(), buf.data_ptr(), nbytes, self.R.stream())
+        torch.cuda.synchronize()
+        return buf
+
+    def pool(self, num_pages, free_order):
+        """A pool whose every K/V element is N(0,1) bf16 (a 64 MiB seeded block tiled over the buffer)."""
+        torch = self.torch
+        pool = self.R.Pool(self.cfg, num_pages, free_order)
+        flat = pool.buf.view(torch.int16)
+        blk = self.normal_bf16(1, 32 << 20, 1.0).view(torch.int16).view(-1)
+        n = flat.numel()
+        for o in range(0, n, blk.numel()):
+            m = min(blk.numel(), n - o)
+            flat[o:o + m].copy_(blk[:m])
+        torch.cuda.synchronize()
+        return pool
+
+
+def alloc_rows(pool, totals, max_pages):
+    import numpy as np
+    bt = np.full((len(totals), max_pages), -1, np.int32)
+    for s, t in enumerate(totals):
+        pool.alloc(int(t), bt[s], 0, max_pages)
+    return bt
+
+
+def time_loop(torch, fn, iters, warmup):
+    """Mean ms per call of fn(i) over iters calls after warmup calls, HIP events on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        fn(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+# ----------------------------------------------------------------------------- the headline: 32-layer decode
+def bench_model_decode(torch, L, R, steps, warmup):
+    import numpy as np
+    import synth
+    shape = synth.LLAMA7B
+    B = 64
+    d = Dev(torch, L, R, shape, SEED + 5)
+    log("C5: generating and packing 32 layers of 7B-shaped weights on the device")
+    layers = [d.packed_layer() for _ in range(shape.n_layers)]
+    embed = d.normal_bf16(shape.vocab, shape.hidden, 0.02)
+    fnorm = torch.ones(shape.hidden, device="cuda", dtype=torch.bfloat16)
+    head = d.packed_matrix(shape.vocab, shape.hidden)
+    mw, keep = L.make_model_weights(embed.data_ptr(), [st for _, st in layers], fnorm.data_ptr(), head.data_ptr())
+    ctx = synth.context_lengths(5, B, 256, 2048)
+    n_iter = steps + warmup
+    totals = ctx + n_iter + 1
+    max_pages = int(max(synth.pages_for(t) for t in totals))
+    num_pages = int(sum(synth.pages_for(t) for t in totals))
+    log(f"C5: pool of {num_pages} pages ({L.llmdec_kv_pool_bytes(d.cfg, num_pages) / 1e9:.1f} GB), max_pages {max_pages}")
+    pool = d.pool(num_pages, synth.free_order(5, num_pages))
+    bt = R.dev_i32(alloc_rows(pool, totals, max_pages))
+    pos = [R.dev_i32(ctx + i) for i in range(n_iter)]
+    toks = [R.dev_i32(synth.first_tokens(5, B, shape.vocab)), torch.empty(B, dtype=torch.int32, device="cuda")]
+    ws = R.Workspace(L.llmdec_workspace_bytes(d.cfg, B, B, max_pages))
+    strm = R.stream()
+
+    def step(i):
+        L.llmdec_model_step_greedy(d.cfg, mw, B, B, 1, toks[i % 2].data_ptr(), None, pos[i].data_ptr(),
+                                   bt.data_ptr(), max_pages, pool.handle, toks[(i + 1) % 2].data_ptr(), None,
+                                   ws.ptr, ws.nbytes, strm)
+
+    log(f"C5: {warmup} warm-up + {steps} timed greedy steps over {B} sequences")
+    ms = time_loop(torch, step, steps, warmup)
+    assert ws.error_bits() == 0, "device error word set"
+    ids = toks[n_iter % 2].cpu().numpy()
+    assert ids.min() >= 0 and ids.max() < shape.vocab
+    # algorithmic bytes of one step: every weight once + every cached K/V read once + new K/V written
+    h, I, V = shape.hidden, shape.intermediate, shape.vocab
+    w_bytes = shape.n_layers * (4 * h * h + 3 * h * I + 2 * h) * 2 + V * h * 2 + h * 2 + B * h * 2
+    ctx_mid = ctx + warmup + (steps - 1) / 2.0
+    kv_bytes = float(np.sum(ctx_mid + 1)) * shape.n_layers * 2 * h * 2
+    step_bytes = w_bytes + kv_bytes
+    res = dict(ms_per_step=ms, tokens_per_s=B / (ms * 1e-3), step_bytes=step_bytes,
+               hbm_frac=step_bytes / (ms * 1e-3) / HBM_PEAK, weight_bytes=w_bytes, kv_bytes=kv_bytes)
+
+    # dominant kernel, timed on its own through its single-operation entry point on the same cache
+    q = torch.randn(B, h, device="cuda", generator=d.gen, dtype=torch.float32)
+    out = torch.empty(B, h, device="cuda", dtype=torch.float32)
+    ctx_last = R.dev_i32(ctx + n_iter)
+    attn_bytes = float(np.sum(ctx + n_iter + 1)) * 2 * h * 2 + 2 * B * h * 4
+
+    def attn(i):
+        L.llmdec_op_decode_attention(d.cfg, q.data_ptr(), B, ctx_last.data_ptr(), bt.data_ptr(), max_pages,
+                                     pool.handle, i % shape.n_layers, out.data_ptr(), ws.ptr, ws.nbytes, strm)
+
+    a_ms = time_loop(torch, attn, 64, 4)
+    res["attn"] = dict(ms=a_ms, bytes=attn_bytes, gbps=attn_bytes / (a_ms * 1e-3) / 1e9)
+    res["ctx"] = ctx
+    del pool, layers, head, embed
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------- one-layer sub-benchmarks
+def layer_bytes(shape):
+    h, I = shape.hidden, shape.intermediate
+    return (4 * h * h + 3 * h * I + 2 * h) * 2
+
+
+def bench_layer_decode(torch, L, R, ctxs, copies, iters, tag, workload):
+    import numpy as np
+    import synth
+    shape = synth.LLAMA7B_LAYER
+    d = Dev(torch, L, R, shape, SEED + workload)
+    B = len(ctxs)
+    ctxs = np.asarray(ctxs, np.int32)
+    layers = [d.packed_layer() for _ in range(copies)]
+    per_copy = int(sum(synth.pages_for(c + 1) for c in ctxs))
+    max_pages = int(max(synth.pages_for(c + 1) for c in ctxs))
+    pool = d.pool(per_copy * copies, synth.free_order(workload, per_copy * copies))
+    bts = [R.dev_i32(alloc_rows(pool, ctxs + 1, max_pages)) for _ in range(copies)]
+    ctx_d = R.dev_i32(ctxs)
+    x = torch.randn(B, shape.hidden, device="cuda", generator=d.gen, dtype=torch.float32)
+    ws = R.Workspace(L.llmdec_workspace_bytes(d.cfg, B, B, max_pages))
+    strm = R.stream()
+
+    def step(i):
+        c = i % copies
+        L.llmdec_layer_decode(d.cfg, layers[c][1], 0, x.data_ptr(), B, ctx_d.data_ptr(), bts[c].data_ptr(),
+                              max_pages, pool.handle, ws.ptr, ws.nbytes, strm)
+
+    ms = time_loop(torch, step, iters, 2 * copies)
+    assert ws.error_bits() == 0
+    kv = float(np.sum(ctxs + 1)) * 2 * shape.hidden * 2
+    byt = layer_bytes(shape) + kv + 2 * B * shape.hidden * 4
+    log(f"{tag}: {ms * 1e3:.1f} us per layer-step, {byt / (ms * 1e-3) / 1e9:.0f} GB/s")
+    return dict(workload=tag, ms_per_layer_step=ms, layer_steps_per_s=1e3 / ms, tokens_per_s=B * 1e3 / ms,
+                algorithmic_bytes=byt, hbm_frac=byt / (ms * 1e-3) / HBM_PEAK)
+
+
+def bench_layer_prefill(torch, L, R, iters):
+    import numpy as np
+    import synth
+    shape = synth.LLAMA7B_LAYER
+    d = Dev(torch, L, R, shape, SEED + 4)
+    n, plen = 4, 512
+    T = n * plen
+    keep, w = d.packed_layer()
+    max_pages = plen // 16
+    pool = d.pool(n * max_pages, synth.free_order(4, n * max_pages))
+    bt = R.dev_i32(alloc_rows(pool, [plen] * n, max_pages))
+    cu = R.dev_i32(np.arange(n + 1) * plen)
+    start = R.dev_i32([0] * n)
+    x = torch.randn(T, shape.hidden, device="cuda", generator=d.gen, dtype=torch.float32)
+    ws = R.Workspace(L.llmdec_workspace_bytes(d.cfg, T, n, max_pages))
+    strm = R.stream()
+
+    def step(i):
+        L.llmdec_layer_prefill(d.cfg, w, 0, x.data_ptr(), n, T, plen, cu.data_ptr(), start.data_ptr(), bt.data_ptr(),
+                               max_pages, pool.handle, ws.ptr, ws.nbytes, strm)
+
+    ms = time_loop(torch, step, iters, 2)
+    assert ws.error_bits() == 0
+    h, I = shape.hidden, shape.intermediate
+    gemm_flops = 2.0 * T * (3 * h + h + 2 * I) * h + 2.0 * T * h * I
+    attn_flops = 4.0 * n * shape.n_heads * shape.head_dim * (plen * (plen + 1) / 2)
+    del keep
+    log(f"C4 prefill: {ms * 1e3:.1f} us per layer, {gemm_flops / (ms * 1e-3) / 1e12:.0f} TFLOP/s on the GEMMs")
+    return dict(workload="7B-layer-prefill-4x512", ms_per_layer=ms, tokens_per_s=T * 1e3 / ms,
+                gemm_flops=gemm_flops, attn_flops=attn_flops,
+                mfma_frac=(gemm_flops + attn_flops) / (ms * 1e-3) / MFMA_BF16_PEAK)
+
+
+# ----------------------------------------------------------------------------- CPU oracle baseline
+def cpu_baseline(ctx):
+    """The float64 oracle on a bounded sample of the headline workload: one 7B-shaped layer's decode
+    step for 4 of the 64 sequences (the shortest, the longest, two seeded), plus the final norm and
+    lm_head for those 4; scaled to tokens/s of the 32-layer model as 4 / (32 t_layer + t_head)."""
+    import numpy as np
+    import synth
+    from oracle import decoder as od
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    shape = synth.LLAMA7B
+    order = np.argsort(ctx, kind="stable")
+    pick = [int(order[0]), int(order[-1])] + [int(i) for i in synth.rng(5, 99).choice(
+        [i for i in range(len(ctx)) if i not in (order[0], order[-1])], 2, replace=False)]
+    lw = synth.layer_weights(5, 0, shape)
+    kv = od.ContiguousKV(1, shape.n_kv_heads, shape.head_dim)
+    for j, s in enumerate(pick):
+        k, v = synth.kv_history(5, 0, s, int(ctx[s]), shape.n_kv_heads, shape.head_dim)
+        kv.preload(0, j, od.widen_bf16(k), od.widen_bf16(v))
+    x = synth.hidden_input(5, len(pick), shape.hidden)
+    head = synth.normal_bf16((5, synth.S_LMHEAD), (shape.vocab, shape.hidden), 0.02)
+    fnorm = np.full(shape.hidden, synth.BF16_ONE, np.uint16)
+    t0 = time.perf_counter()
+    y = od.layer_step(shape, lw.tensors, 0, x, list(range(len(pick))), [int(ctx[s]) for s in pick], kv)
+    t1 = time.perf_counter()
+    logits = od.lm_head_logits(shape, fnorm, head, y)
+    t2 = time.perf_counter()
+    assert np.all(np.isfinite(logits))
+    t_layer, t_head = t1 - t0, t2 - t1
+    val = len(pick) / (shape.n_layers * t_layer + t_head)
+    return dict(value=val, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=(f"one 7B-shaped layer decode step for 4 of the 64 sequences (contexts "
+                        f"{[int(ctx[s]) for s in pick]}) took {t_layer:.2f} s, final norm + lm_head for them "
+                        f"{t_head:.2f} s; tokens/s = 4 / (32 * t_layer + t_head)"))
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default="c5,c2,c3,c4", help="comma list of workloads to run")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the decoder step has no multi-GPU path)", file=sys.stderr, flush=True)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only; WORLD_SIZE > 1 is not supported", file=sys.stderr, flush=True)
+        sys.exit(2)
+    import numpy as np  # noqa: F401
+    import torch
+    from kv_cached_transformer_amd import llmdec as L
+    from kv_cached_transformer_amd import runtime as R
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    L.lib()
+    only = set(args.only.split(","))
+    extra = {}
+    head = None
+    if "c5" in only:
+        head = bench_model_decode(torch, L, R, args.steps, args.warmup)
+        log(f"C5: {head['ms_per_step']:.2f} ms/step, {head['tokens_per_s']:.0f} tokens/s, "
+            f"{head['hbm_frac'] * 100:.1f}% of HBM peak; decode attention {head['attn']['ms'] * 1e3:.0f} us "
+            f"= {head['attn']['gbps']:.0f} GB/s")
+    if "c2" in only:
+        extra["decode_b1_ctx2048"] = bench_layer_decode(torch, L, R, [2048], 4, 100, "7B-layer-decode-b1-ctx2048", 2)
+    if "c3" in only:
+        import synth
+        extra["decode_b32_ctx128..4096"] = bench_layer_decode(torch, L, R, synth.context_lengths(3, 32, 128, 4096), 1,
+                                                              50, "7B-layer-decode-b32-ctx128..4096", 3)
+    if "c4" in only:
+        extra["prefill_4x512"] = bench_layer_prefill(torch, L, R, 20)
+    cpu = None
+    if head is not None and not args.no_cpu:
+        log("cpu_baseline: timing the oracle on a 4-sequence sample")
+        cpu = cpu_baseline(head["ctx"])
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"] if head else None,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"] if head else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "7B-32L-decode-b64-ctx256..2048", "layers": 32, "hidden": 4096, "heads": 32,
+                   "head_dim": 128, "intermediate": 11008, "vocab": 32000, "batch": 64, "page_size": 16,
+                   "ctx_range": [256, 2048]},
+    }
+    if head:
+        a = head["attn"]
+        line["hbm_frac_step"] = head["hbm_frac"]
+        line["roofline"] = {"bound": "hbm", "kernel": "paged decode attention (one layer, 64 sequences)",
+                            "achieved": a["gbps"], "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                            "frac": a["gbps"] * 1e9 / HBM_PEAK, "traffic": None}
+    line["cpu_baseline"] = cpu
+    line["sub_benchmarks"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -167,8 +167,10 @@ size_t llmdec_workspace_bytes(const llmdec_config *cfg, int32_t max_tokens, int3
 /* Clear the device error word (enqueued on stream). */
 llmdec_status llmdec_workspace_reset(void *ws, size_t ws_bytes, llmdec_stream stream);
 /* Synchronise stream and read the device error word: 0 = none; otherwise a
- * bit mask (1: page id out of range, 2: position beyond the block-table row,
- * 4: token id out of range). */
+ * bit mask (1: page id out of range, 2: position beyond the block-table row or
+ * negative context length, 4: token id out of range, 8: sequence index,
+ * cu_seqlens entry or start position out of range).  A kernel that finds such
+ * a value skips the access it would have made. */
 llmdec_status llmdec_workspace_error(const void *ws, llmdec_stream stream, uint32_t *error_bits);
 
 /* ------------------------------------------------------------------ layer steps */
@@ -236,8 +238,9 @@ llmdec_status llmdec_op_linear(const float *a, int32_t rows, int32_t k_dim, cons
 /* Rotate q and k of each new token by its position and store bf16 k, v into
  * the pool ([E] §4.3: rotation first, then the cache update).  qkv: dev fp32
  * [n_tokens][3*hidden] (q | k | v); q is rotated in place.  Token t belongs
- * to sequence seq_of_token[t] (dev int32) at position pos_of_token[t]. */
-llmdec_status llmdec_op_rope_append(const llmdec_config *cfg, float *qkv, int32_t n_tokens,
+ * to sequence seq_of_token[t] (dev int32, in [0, n_seqs): the row of
+ * block_tables [n_seqs][max_pages]) at position pos_of_token[t]. */
+llmdec_status llmdec_op_rope_append(const llmdec_config *cfg, float *qkv, int32_t n_tokens, int32_t n_seqs,
                                     const int32_t *seq_of_token, const int32_t *pos_of_token,
                                     const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool,
                                     int32_t layer, void *ws, size_t ws_bytes, llmdec_stream stream);

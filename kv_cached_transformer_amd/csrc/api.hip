@@ -191,27 +191,27 @@ static void run_layer(const LayerArgs &a) {
   const uint16_t *W = nullptr;
 
   // attention block: x += Wo . attn(rope(Wq y), rope(Wk y), Wv y),  y = RMSNorm(x)
-  launch_rmsnorm(a.hidden, h, nullptr, (const uint16_t *)a.w->attn_norm, M, h, c.rms_eps, vec ? act : nullptr,
+  launch_rmsnorm(a.hidden, h, nullptr, M, (const uint16_t *)a.w->attn_norm, M, h, c.rms_eps, err, vec ? act : nullptr,
                  vec ? nullptr : hi, vec ? nullptr : lo, kh, a.s);
   W = (const uint16_t *)a.w->w_qkv;
   launch_linear(ah, W, 3 * h, h, qkv, 3 * h, kStore, part, part_n, a.s);
   if (a.decode) {
-    launch_rope_append(c, qkv, 3 * h, M, nullptr, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages, err, a.s);
+    launch_rope_append(c, qkv, 3 * h, M, a.n_seqs, nullptr, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages, err, a.s);
     launch_decode_attention(c, qkv, 3 * h, M, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages,
                             at<float>(a.ws, L.attn_part), vec ? act : nullptr, vec ? nullptr : hi, vec ? nullptr : lo,
                             kh, err, a.s);
   } else {
     int32_t *ts = at<int32_t>(a.ws, L.tok_seq), *tp = at<int32_t>(a.ws, L.tok_pos);
-    launch_token_map(a.cu, a.start, a.n_seqs, ts, tp, a.s);
-    launch_rope_append(c, qkv, 3 * h, M, ts, tp, a.bt, a.max_pages, pk, pv, a.pool->num_pages, err, a.s);
-    launch_prefill_attention(c, qkv, 3 * h, a.n_seqs, a.max_q_len, a.cu, a.start, a.bt, a.max_pages, pk, pv,
+    launch_token_map(a.cu, a.start, a.n_seqs, M, err, ts, tp, a.s);
+    launch_rope_append(c, qkv, 3 * h, M, a.n_seqs, ts, tp, a.bt, a.max_pages, pk, pv, a.pool->num_pages, err, a.s);
+    launch_prefill_attention(c, qkv, 3 * h, a.n_seqs, M, a.max_q_len, a.cu, a.start, a.bt, a.max_pages, pk, pv,
                              a.pool->num_pages, vec ? act : nullptr, vec ? nullptr : hi, vec ? nullptr : lo, kh, err,
                              a.s);
   }
   launch_linear(ah, (const uint16_t *)a.w->w_o, h, h, a.hidden, h, kAccumulate, part, part_n, a.s);
 
   // MLP block: x += Wd (silu(Wg y) * (Wu y)),  y = RMSNorm(x)
-  launch_rmsnorm(a.hidden, h, nullptr, (const uint16_t *)a.w->mlp_norm, M, h, c.rms_eps, vec ? act : nullptr,
+  launch_rmsnorm(a.hidden, h, nullptr, M, (const uint16_t *)a.w->mlp_norm, M, h, c.rms_eps, err, vec ? act : nullptr,
                  vec ? nullptr : hi, vec ? nullptr : lo, kh, a.s);
   launch_linear(ah, (const uint16_t *)a.w->w_gu, 2 * I, h, gu, 2 * I, kStore, part, part_n, a.s);
   // gate/up rows alternate in 16-row blocks: gate j at column 32(j/16) + j%16, up 16 further
@@ -432,7 +432,8 @@ extern "C" llmdec_status llmdec_model_step_greedy(const llmdec_config *cfg, cons
   float *act = at<float>(ws, L.act_f32);
   uint16_t *hi = at<uint16_t>(ws, L.act_hi), *lo = at<uint16_t>(ws, L.act_lo);
   const int kh = round_up(h, kTileK);
-  launch_rmsnorm(x, h, decode ? nullptr : cu_seqlens, (const uint16_t *)w->final_norm, n_seqs, h, cfg->rms_eps,
+  launch_rmsnorm(x, h, decode ? nullptr : cu_seqlens, n_tokens, (const uint16_t *)w->final_norm, n_seqs, h,
+                 cfg->rms_eps, at<uint32_t>(ws, L.err),
                  vec ? act : nullptr, vec ? nullptr : hi, vec ? nullptr : lo, kh, s);
   Act a;
   a.rows = n_seqs;
@@ -458,7 +459,7 @@ extern "C" llmdec_status llmdec_op_rmsnorm(const float *x, const void *gamma, in
     return set_error(LLMDEC_E_INVALID, "op_rmsnorm: NULL pointer");
   if (rows <= 0 || n <= 0 || (out_hi && (ld_split < n || ld_split % 32)))
     return set_error(LLMDEC_E_INVALID, "op_rmsnorm: rows=%d n=%d ld_split=%d out of range", rows, n, ld_split);
-  launch_rmsnorm(x, n, nullptr, (const uint16_t *)gamma, rows, n, eps, out_f32, (uint16_t *)out_hi,
+  launch_rmsnorm(x, n, nullptr, rows, (const uint16_t *)gamma, rows, n, eps, nullptr, out_f32, (uint16_t *)out_hi,
                  (uint16_t *)out_lo, ld_split, (hipStream_t)stream);
   return check_launch("op_rmsnorm");
 }
@@ -506,7 +507,7 @@ extern "C" llmdec_status llmdec_op_linear(const float *a, int32_t rows, int32_t 
 }
 
 extern "C" llmdec_status llmdec_op_rope_append(const llmdec_config *cfg, float *qkv, int32_t n_tokens,
-                                              const int32_t *seq_of_token, const int32_t *pos_of_token,
+                                              int32_t n_seqs, const int32_t *seq_of_token, const int32_t *pos_of_token,
                                               const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool,
                                               int32_t layer, void *ws, size_t ws_bytes, llmdec_stream stream) {
   const char *who = "op_rope_append";
@@ -515,10 +516,11 @@ extern "C" llmdec_status llmdec_op_rope_append(const llmdec_config *cfg, float *
   if (st == LLMDEC_OK) st = check_ws(ws, ws_bytes, kWsHeader, who);
   if (st != LLMDEC_OK) return st;
   if (!qkv || !seq_of_token || !pos_of_token || !block_tables) return set_error(LLMDEC_E_INVALID, "%s: NULL pointer", who);
-  if (n_tokens <= 0 || max_pages <= 0) return set_error(LLMDEC_E_INVALID, "%s: n_tokens/max_pages out of range", who);
+  if (n_tokens <= 0 || n_seqs <= 0 || max_pages <= 0)
+    return set_error(LLMDEC_E_INVALID, "%s: n_tokens/n_seqs/max_pages out of range", who);
   uint16_t *pk, *pv;
   pool_layer(pool, layer, &pk, &pv);
-  launch_rope_append(*cfg, qkv, 3 * cfg->hidden, n_tokens, seq_of_token, pos_of_token, block_tables, max_pages, pk, pv,
+  launch_rope_append(*cfg, qkv, 3 * cfg->hidden, n_tokens, n_seqs, seq_of_token, pos_of_token, block_tables, max_pages, pk, pv,
                      pool->num_pages, (uint32_t *)ws, (hipStream_t)stream);
   return check_launch(who);
 }
@@ -560,7 +562,7 @@ extern "C" llmdec_status llmdec_op_prefill_attention(const llmdec_config *cfg, c
     return set_error(LLMDEC_E_INVALID, "%s: sizes out of range", who);
   uint16_t *pk, *pv;
   pool_layer(pool, layer, &pk, &pv);
-  launch_prefill_attention(*cfg, q, cfg->hidden, n_seqs, max_q_len, cu_seqlens, start_pos, block_tables, max_pages,
+  launch_prefill_attention(*cfg, q, cfg->hidden, n_seqs, n_tokens, max_q_len, cu_seqlens, start_pos, block_tables, max_pages,
                            pk, pv, pool->num_pages, out, nullptr, nullptr, 0, (uint32_t *)ws, (hipStream_t)stream);
   return check_launch(who);
 }

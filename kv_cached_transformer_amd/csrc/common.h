@@ -17,6 +17,7 @@ constexpr int kTileElems = 512; // bf16 elements per tile (1 KiB)
 constexpr uint32_t kErrPage = 1u;   // block-table page id out of range
 constexpr uint32_t kErrPos = 2u;    // position beyond the block-table row
 constexpr uint32_t kErrToken = 4u;  // token id out of range
+constexpr uint32_t kErrSeq = 8u;    // sequence index, cu_seqlens entry or position out of range
 constexpr size_t kWsHeader = 256;   // bytes reserved for the error word
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;

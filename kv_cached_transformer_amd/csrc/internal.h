@@ -44,23 +44,23 @@ void launch_pack_matrix(int rows, int cols, const uint16_t *src, uint16_t *dst, 
 void launch_embed(const uint16_t *embed, const int32_t *tokens, int n_tokens, int hidden, int vocab, float *x,
                   uint32_t *err, hipStream_t s);
 // y = rmsnorm(x) * gamma on the given rows; outputs: f32 [rows][n] and/or tiled hi/lo with kpad columns.
-void launch_rmsnorm(const float *x, int ld_x, const int32_t *row_index, const uint16_t *gamma, int rows, int n,
-                    float eps, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad, hipStream_t s);
+void launch_rmsnorm(const float *x, int ld_x, const int32_t *row_index, int n_src_rows, const uint16_t *gamma, int rows, int n,
+                    float eps, uint32_t *err, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad, hipStream_t s);
 // fp32 [rows][ld] -> tiled hi/lo [rows_pad16][kpad] (zero padding).
 void launch_split(const float *a, int ld, int rows, int cols, uint16_t *hi, uint16_t *lo, int kpad, hipStream_t s);
 void launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, float *out, int ld_out, Epilogue epi,
                    float *partials, size_t partial_floats, hipStream_t s);
 size_t linear_partial_floats(int rows, int n, int k);
-void launch_token_map(const int32_t *cu_seqlens, const int32_t *start_pos, int n_seqs, int32_t *tok_seq,
+void launch_token_map(const int32_t *cu_seqlens, const int32_t *start_pos, int n_seqs, int n_tokens, uint32_t *err, int32_t *tok_seq,
                       int32_t *tok_pos, hipStream_t s);
-void launch_rope_append(const llmdec_config &cfg, float *qkv, int ld_qkv, int n_tokens, const int32_t *tok_seq,
+void launch_rope_append(const llmdec_config &cfg, float *qkv, int ld_qkv, int n_tokens, int n_seqs, const int32_t *tok_seq,
                         const int32_t *tok_pos, const int32_t *block_tables, int max_pages, uint16_t *pool_layer_k,
                         uint16_t *pool_layer_v, int num_pages, uint32_t *err, hipStream_t s);
 void launch_decode_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, const int32_t *ctx_lens,
                              const int32_t *block_tables, int max_pages, const uint16_t *pool_layer_k,
                              const uint16_t *pool_layer_v, int num_pages, float *partials, float *out_f32,
                              uint16_t *out_hi, uint16_t *out_lo, int kpad, uint32_t *err, hipStream_t s);
-void launch_prefill_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, int max_q_len,
+void launch_prefill_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, int n_tokens, int max_q_len,
                               const int32_t *cu_seqlens, const int32_t *start_pos, const int32_t *block_tables,
                               int max_pages, const uint16_t *pool_layer_k, const uint16_t *pool_layer_v,
                               int num_pages, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad,

@@ -32,6 +32,11 @@ __device__ inline f32x4 mfma16(const uint4 &a, const uint4 &b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
 }
 
+// A 32-bit word holding the bf16 values of tokens t and t+1: keep only those below n_valid.
+__device__ inline uint32_t mask_pair(uint32_t w, int t, int n_valid) {
+  return t + 1 < n_valid ? w : (t < n_valid ? (w & 0xffffu) : 0u);
+}
+
 __device__ inline void store_out(float v, int r, int c, int ld, float *out_f32, uint16_t *hi, uint16_t *lo, int kpad) {
   if (out_f32) out_f32[(size_t)r * ld + c] = v;
   if (hi) {
@@ -59,6 +64,10 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict
   const int n_tok = ctx_lens[s] + 1;
   const int n_pages = (n_tok + 15) >> 4;
   const int p0 = part * ppp;
+  if (n_tok <= 0) {
+    if (lane == 0 && part == 0) raise_error(err, kErrPos);
+    return;
+  }
   if (p0 >= n_pages) return;
   if (n_pages > max_pages) {
     if (lane == 0) raise_error(err, kErrPos);
@@ -100,6 +109,18 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict
       const uint4 *vp = reinterpret_cast<const uint4 *>(pool_v + (((size_t)pg * n_heads + h) * D + lane * DV) * 16);
 #pragma unroll
       for (int i = 0; i < DV * 2; ++i) vv[i] = vp[i];
+      // slots past the last token hold whatever the pool held (possibly NaN): their weight is 0,
+      // and 0 * NaN would poison the sum, so their values are cleared
+      const int n_valid = n_tok - pi * 16;
+      if (n_valid < 16) {
+#pragma unroll
+        for (int i = 0; i < DV * 2; ++i) {
+          vv[i].x = mask_pair(vv[i].x, (i & 1) * 8 + 0, n_valid);
+          vv[i].y = mask_pair(vv[i].y, (i & 1) * 8 + 2, n_valid);
+          vv[i].z = mask_pair(vv[i].z, (i & 1) * 8 + 4, n_valid);
+          vv[i].w = mask_pair(vv[i].w, (i & 1) * 8 + 6, n_valid);
+        }
+      }
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < DK / 8; ++i) {
@@ -164,7 +185,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(int n_heads, const in
                                                            uint16_t *out_hi, uint16_t *out_lo, int kpad) {
   const int s = blockIdx.x / n_heads, h = blockIdx.x % n_heads;
   const int n_pages = (ctx_lens[s] + 1 + 15) >> 4;
-  if (n_pages > max_pages) return;
+  if (n_pages > max_pages || n_pages <= 0) return;
   const int parts = (n_pages + ppp - 1) / ppp;
   if (parts <= 1) return;
   const float *pp = partials + ((size_t)s * n_heads + h) * n_parts * (D + 2);
@@ -221,6 +242,7 @@ void launch_decode_attention(const llmdec_config &cfg, const float *q, int ld_q,
 // per query, then O^T += V^T P^T over the 32 keys.
 template <int D>
 __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restrict__ q, int ld_q, int n_heads,
+                                                          int n_tokens, int max_q_len,
                                                           const int32_t *__restrict__ cu,
                                                           const int32_t *__restrict__ start_pos,
                                                           const int32_t *__restrict__ block_tables, int max_pages,
@@ -233,6 +255,10 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
   const int qb = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
   const int t0 = cu[s], len = cu[s + 1] - t0;
+  if (t0 < 0 || len < 0 || len > max_q_len || t0 + len > n_tokens || start_pos[s] < 0) {
+    if (lane == 0 && qb == 0 && h == 0) raise_error(err, kErrSeq);
+    return;
+  }
   if (qb * 16 >= len) return;
   const int n_q = min(16, len - qb * 16);
   const int pos0 = start_pos[s] + qb * 16;  // position of query 0 of this block
@@ -297,8 +323,15 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
           st = mfma16(kk, ql[kt], st);
         }
         const uint16_t *vp = pool_v + ((size_t)pg * n_heads + h) * D * 16 + g * 4;
+        // keys after the block's last query are not written yet (possibly NaN): clear their values
+        const int n_valid = last_pos + 1 - (pi * 16 + g * 4);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vt[db][u] = *reinterpret_cast<const uint2 *>(vp + (db * 16 + c) * 16);
+        for (int db = 0; db < DB; ++db) {
+          uint2 w = *reinterpret_cast<const uint2 *>(vp + (db * 16 + c) * 16);
+          w.x = mask_pair(w.x, 0, n_valid);
+          w.y = mask_pair(w.y, 2, n_valid);
+          vt[db][u] = w;
+        }
       } else {
 #pragma unroll
         for (int db = 0; db < DB; ++db) vt[db][u] = make_uint2(0, 0);
@@ -362,17 +395,17 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
       store_out(oacc[db][e] * inv, tok, h * D + db * 16 + g * 4 + e, n_heads * D, out_f32, out_hi, out_lo, kpad);
 }
 
-void launch_prefill_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, int max_q_len,
+void launch_prefill_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, int n_tokens, int max_q_len,
                               const int32_t *cu, const int32_t *start_pos, const int32_t *block_tables, int max_pages,
                               const uint16_t *pk, const uint16_t *pv, int num_pages, float *out_f32, uint16_t *out_hi,
                               uint16_t *out_lo, int kpad, uint32_t *err, hipStream_t s) {
   if (n_seqs <= 0 || max_q_len <= 0) return;
   dim3 grid((max_q_len + 15) / 16, cfg.n_heads, n_seqs);
   if (cfg.head_dim == 128)
-    prefill_attn_kernel<128><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cu, start_pos, block_tables, max_pages, pk, pv,
+    prefill_attn_kernel<128><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, n_tokens, max_q_len, cu, start_pos, block_tables, max_pages, pk, pv,
                                                  num_pages, out_f32, out_hi, out_lo, kpad, err);
   else
-    prefill_attn_kernel<64><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cu, start_pos, block_tables, max_pages, pk, pv,
+    prefill_attn_kernel<64><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, n_tokens, max_q_len, cu, start_pos, block_tables, max_pages, pk, pv,
                                                 num_pages, out_f32, out_hi, out_lo, kpad, err);
 }
 

@@ -72,11 +72,16 @@ __device__ inline void store_act(float v, int r, int c, int n, float *out_f32, u
 // ---------------------------------------------------------------- RMSNorm ([E] §4.2)
 // y = x * (mean(x^2) + eps)^(-1/2) * gamma, eps inside the root.  One block per row.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ x, int ld_x,
-                                                      const int32_t *__restrict__ cu_last,
+                                                      const int32_t *__restrict__ cu_last, int n_src_rows,
                                                       const uint16_t *__restrict__ gamma, int n, float eps,
-                                                      float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad) {
+                                                      uint32_t *err, float *out_f32, uint16_t *out_hi,
+                                                      uint16_t *out_lo, int kpad) {
   const int r = blockIdx.x;
-  const int src_row = cu_last ? cu_last[r + 1] - 1 : r;
+  int src_row = cu_last ? cu_last[r + 1] - 1 : r;
+  if (src_row < 0 || src_row >= n_src_rows) {  // a bad cu_seqlens entry: flag it, read row 0 instead
+    if (threadIdx.x == 0) raise_error(err, kErrSeq);
+    src_row = 0;
+  }
   const float *xr = x + (size_t)src_row * ld_x;
   float ss = 0.f;
   for (int i = threadIdx.x; i < n; i += 256) {
@@ -98,10 +103,12 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ 
     }
 }
 
-void launch_rmsnorm(const float *x, int ld_x, const int32_t *cu_last, const uint16_t *gamma, int rows, int n,
-                    float eps, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad, hipStream_t s) {
+void launch_rmsnorm(const float *x, int ld_x, const int32_t *cu_last, int n_src_rows, const uint16_t *gamma, int rows,
+                    int n, float eps, uint32_t *err, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad,
+                    hipStream_t s) {
   if (rows > 0)
-    rmsnorm_kernel<<<rows, 256, 0, s>>>(x, ld_x, cu_last, gamma, n, eps, out_f32, out_hi, out_lo, kpad);
+    rmsnorm_kernel<<<rows, 256, 0, s>>>(x, ld_x, cu_last, n_src_rows, gamma, n, eps, err, out_f32, out_hi, out_lo,
+                                        kpad);
 }
 
 // ---------------------------------------------------------------- fp32 -> tiled hi/lo
@@ -131,19 +138,27 @@ void launch_split(const float *a, int ld, int rows, int cols, uint16_t *hi, uint
 }
 
 // ---------------------------------------------------------------- token -> (sequence, position)
-__global__ void token_map_kernel(const int32_t *__restrict__ cu, const int32_t *__restrict__ start, int32_t *tok_seq,
-                                 int32_t *tok_pos) {
+// Sequence s owns tokens cu[s]..cu[s+1]-1; a table that is not non-decreasing
+// within [0, n_tokens], does not end at n_tokens, or a negative start is
+// flagged and that sequence's tokens are not written.
+__global__ void token_map_kernel(const int32_t *__restrict__ cu, const int32_t *__restrict__ start, int n_seqs,
+                                 int n_tokens, uint32_t *err, int32_t *tok_seq, int32_t *tok_pos) {
   const int s = blockIdx.x;
   const int b = cu[s], e = cu[s + 1], p0 = start[s];
+  const bool bad = b < 0 || e < b || e > n_tokens || p0 < 0 || (s == n_seqs - 1 && e != n_tokens) || (s == 0 && b != 0);
+  if (bad) {
+    if (threadIdx.x == 0) raise_error(err, kErrSeq);
+    return;
+  }
   for (int i = b + threadIdx.x; i < e; i += blockDim.x) {
     tok_seq[i] = s;
     tok_pos[i] = p0 + (i - b);
   }
 }
 
-void launch_token_map(const int32_t *cu, const int32_t *start, int n_seqs, int32_t *tok_seq, int32_t *tok_pos,
-                      hipStream_t s) {
-  if (n_seqs > 0) token_map_kernel<<<n_seqs, 256, 0, s>>>(cu, start, tok_seq, tok_pos);
+void launch_token_map(const int32_t *cu, const int32_t *start, int n_seqs, int n_tokens, uint32_t *err,
+                      int32_t *tok_seq, int32_t *tok_pos, hipStream_t s) {
+  if (n_seqs > 0) token_map_kernel<<<n_seqs, 256, 0, s>>>(cu, start, n_seqs, n_tokens, err, tok_seq, tok_pos);
 }
 
 // ---------------------------------------------------------------- RoPE + paged append ([E] §4.3)
@@ -153,7 +168,7 @@ void launch_token_map(const int32_t *cu, const int32_t *start, int n_seqs, int32
 // in place; rotated k and plain v are rounded to bf16 and written to the page
 // slot bt[seq][pos/16], offset pos%16 (K as [h][o][d], V as [h][d][o]).
 __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qkv, int ld_qkv, int n_heads,
-                                                          int head_dim, float theta,
+                                                          int head_dim, float theta, int n_seqs,
                                                           const int32_t *__restrict__ tok_seq,
                                                           const int32_t *__restrict__ tok_pos,
                                                           const int32_t *__restrict__ block_tables, int max_pages,
@@ -176,7 +191,9 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
   __syncthreads();
   int page = -1;
   const int blk = pos >> 4, off = pos & 15;
-  if (pos < 0 || blk >= max_pages) {
+  if (seq < 0 || seq >= n_seqs) {
+    if (threadIdx.x == 0) raise_error(err, kErrSeq);
+  } else if (pos < 0 || blk >= max_pages) {
     if (threadIdx.x == 0) raise_error(err, kErrPos);
   } else {
     page = block_tables[(size_t)seq * max_pages + blk];
@@ -207,11 +224,11 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
   }
 }
 
-void launch_rope_append(const llmdec_config &cfg, float *qkv, int ld_qkv, int n_tokens, const int32_t *tok_seq,
-                        const int32_t *tok_pos, const int32_t *block_tables, int max_pages, uint16_t *pool_k,
-                        uint16_t *pool_v, int num_pages, uint32_t *err, hipStream_t s) {
+void launch_rope_append(const llmdec_config &cfg, float *qkv, int ld_qkv, int n_tokens, int n_seqs,
+                        const int32_t *tok_seq, const int32_t *tok_pos, const int32_t *block_tables, int max_pages,
+                        uint16_t *pool_k, uint16_t *pool_v, int num_pages, uint32_t *err, hipStream_t s) {
   if (n_tokens > 0)
-    rope_append_kernel<<<n_tokens, 256, 0, s>>>(qkv, ld_qkv, cfg.n_heads, cfg.head_dim, cfg.rope_theta, tok_seq,
+    rope_append_kernel<<<n_tokens, 256, 0, s>>>(qkv, ld_qkv, cfg.n_heads, cfg.head_dim, cfg.rope_theta, n_seqs, tok_seq,
                                                 tok_pos, block_tables, max_pages, pool_k, pool_v, num_pages, err);
 }
 

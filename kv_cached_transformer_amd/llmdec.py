@@ -18,7 +18,7 @@ LLMDEC_OK, LLMDEC_E_INVALID, LLMDEC_E_UNSUPPORTED = 0, -1, -2
 LLMDEC_E_NO_PAGES, LLMDEC_E_WORKSPACE, LLMDEC_E_HIP = -3, -4, -5
 STATUS_NAMES = {0: "OK", -1: "E_INVALID", -2: "E_UNSUPPORTED", -3: "E_NO_PAGES", -4: "E_WORKSPACE", -5: "E_HIP"}
 
-ERR_PAGE, ERR_POS, ERR_TOKEN = 1, 2, 4
+ERR_PAGE, ERR_POS, ERR_TOKEN, ERR_SEQ = 1, 2, 4, 8
 
 
 class LlmdecError(RuntimeError):
@@ -74,7 +74,7 @@ _SIGS = {
     "llmdec_op_rmsnorm": (_I, [_P, _P, _I, _I, _F, _P, _P, _P, _I, _P]),
     "llmdec_op_linear_ws_bytes": (_Z, [_I, _I, _I]),
     "llmdec_op_linear": (_I, [_P, _I, _I, _P, _I, _P, _I, _P, _Z, _P]),
-    "llmdec_op_rope_append": (_I, [_CFG, _P, _I, _P, _P, _P, _I, _P, _I, _P, _Z, _P]),
+    "llmdec_op_rope_append": (_I, [_CFG, _P, _I, _I, _P, _P, _P, _I, _P, _I, _P, _Z, _P]),
     "llmdec_op_decode_attention": (_I, [_CFG, _P, _I, _P, _P, _I, _P, _I, _P, _P, _Z, _P]),
     "llmdec_op_prefill_attention": (_I, [_CFG, _P, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, _Z, _P]),
     "llmdec_op_silu_mul": (_I, [_P, _P, _I, _I, _P, _P]),
@@ -234,10 +234,10 @@ def llmdec_op_linear(a, rows, k_dim, w_packed, n_dim, out, accumulate, ws, ws_by
     _check(lib().llmdec_op_linear(a, rows, k_dim, w_packed, n_dim, out, int(accumulate), ws, ws_bytes, stream))
 
 
-def llmdec_op_rope_append(cfg, qkv, n_tokens, seq_of_token, pos_of_token, block_tables, max_pages, pool, layer, ws,
-                          ws_bytes, stream=0):
-    _check(lib().llmdec_op_rope_append(C.byref(cfg), qkv, n_tokens, seq_of_token, pos_of_token, block_tables,
-                                       max_pages, pool, layer, ws, ws_bytes, stream))
+def llmdec_op_rope_append(cfg, qkv, n_tokens, n_seqs, seq_of_token, pos_of_token, block_tables, max_pages, pool,
+                          layer, ws, ws_bytes, stream=0):
+    _check(lib().llmdec_op_rope_append(C.byref(cfg), qkv, n_tokens, n_seqs, seq_of_token, pos_of_token,
+                                       block_tables, max_pages, pool, layer, ws, ws_bytes, stream))
 
 
 def llmdec_op_decode_attention(cfg, q, n_seqs, ctx_lens, block_tables, max_pages, pool, layer, out, ws, ws_bytes,

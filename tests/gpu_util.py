@@ -40,3 +40,35 @@ def f32_from_bf16(b):
 def banner(msg):
     print(f"[gpu-test] {msg}", flush=True)
     sys.stdout.flush()
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 values at |x| (bf16 keeps 8 significant bits): 2^(e-7) for |x| in [2^e, 2^(e+1))."""
+    a = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(e - 7), 2.0 ** -133)
+
+
+def assert_stored_bf16(tag, got, ref, eps=1e-3, max_flip_frac=0.1):
+    """Values the device rounded to bf16 against the oracle's bf16 roundings of the same quantities.
+
+    The device stores RNE(v_dev) and the oracle RNE(v_ref) with |v_dev - v_ref| small: the two agree
+    except where v lies near a rounding boundary, and then differ by about one ulp.  So each entry
+    must satisfy |got - ref| <= (ulp(got) + ulp(ref)) / 2 + eps, at most max_flip_frac of the
+    entries may differ at all (a systematic error such as truncation instead of nearest-even
+    rounding moves about half of them), and the relative L2 error must meet the hidden-state bound.
+    A max-abs bound does not apply: one ulp of a bf16 value near 8 is already 0.03.
+    """
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{tag}: non-finite stored values"
+    bound = 0.5 * (bf16_ulp(got) + bf16_ulp(ref)) + eps
+    bad = np.abs(got - ref) > bound
+    flips = int((got != ref).sum())
+    print(f"[parity] {tag}: {got.size} stored bf16 values, {flips} differ from the oracle's rounding "
+          f"(max |diff| {float(np.abs(got - ref).max()) if got.size else 0:.3e})", flush=True)
+    assert not bad.any(), f"{tag}: {int(bad.sum())} stored values beyond half an ulp + {eps}"
+    assert flips <= max(4, max_flip_frac * got.size), f"{tag}: {flips} roundings differ"
+    rl = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    assert rl <= REL_L2, f"{tag}: rel_l2 {rl:.3e}"
+

@@ -11,7 +11,7 @@ import pytest
 import synth
 from oracle import decoder as od
 from oracle import pages as op
-from tests.gpu_util import assert_close, banner, f32_from_bf16
+from tests.gpu_util import assert_close, assert_stored_bf16, banner, f32_from_bf16
 from tests.layer_harness import LayerCase
 
 pytestmark = pytest.mark.gpu
@@ -35,23 +35,16 @@ TINY1 = synth.ModelShape(n_layers=1, hidden=256, n_heads=4, n_kv_heads=4, head_d
 
 
 def check_new_slots(case, new_tokens, tag):
-    """New K/V written by the step: slot set exact (sentinel), values equal to the oracle's bf16 up to rare 1-ulp flips."""
+    """New K/V written by the step: the slot set exactly (sentinel), the values as the oracle's bf16 roundings."""
     kimg, vimg = case.pool_images()
-    H, D = case.shape.n_kv_heads, case.shape.head_dim
     written = np.zeros((case.num_pages, 16), bool)
-    flips = 0
+    got, ref = [], []
     for s, p in new_tokens:
         pg, off = op.slot_of(case.bt[s], p)
         written[pg, off] = True
-        kk = f32_from_bf16(kimg[pg, :, off, :]).astype(np.float64)
-        vv = f32_from_bf16(vimg[pg, :, :, off]).astype(np.float64)
-        kr, vr = case.kv.k[(0, s)][p], case.kv.v[(0, s)][p]
-        for got, ref in ((kk, kr), (vv, vr)):
-            flips += int((got != ref).sum())
-            assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -7 + 1e-30), f"{tag}: slot value off by > 1 ulp"
-    total = len(new_tokens) * H * D * 2
-    print(f"[parity] {tag}: new K/V slots {len(new_tokens)}, 1-ulp flips {flips}/{total}", flush=True)
-    assert flips <= max(4, 0.005 * total)
+        got += [f32_from_bf16(kimg[pg, :, off, :]), f32_from_bf16(vimg[pg, :, :, off])]
+        ref += [case.kv.k[(0, s)][p], case.kv.v[(0, s)][p]]
+    assert_stored_bf16(f"{tag} new K/V", np.stack(got), np.stack(ref))
     # everything else is either the seeded history (unchanged) or the 0xFFFF sentinel
     hist = case.kimg0.transpose(0, 2, 1, 3), case.vimg0.transpose(0, 3, 1, 2)
     now = kimg.transpose(0, 2, 1, 3), vimg.transpose(0, 3, 1, 2)
@@ -65,7 +58,8 @@ def run_decode(L, R, shape, workload, ctxs, x_in, tag):
     n = len(ctxs)
     ws = case.workspace(n)
     xd = R.dev_f32(x_in)
-    L.llmdec_layer_decode(case.cfg, case.packed.struct, 0, xd.data_ptr(), n, R.dev_i32(ctxs).data_ptr(),
+    ctx_d = R.dev_i32(ctxs)  # device buffers stay referenced until the stream has run
+    L.llmdec_layer_decode(case.cfg, case.packed.struct, 0, xd.data_ptr(), n, ctx_d.data_ptr(),
                           case.bt_dev.data_ptr(), case.max_pages, case.pool.handle, ws.ptr, ws.nbytes, R.stream())
     torch.cuda.synchronize()
     assert ws.error_bits() == 0
@@ -83,8 +77,9 @@ def run_prefill(L, R, shape, workload, starts, lens, x_in, tag):
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     ws = case.workspace(T)
     xd = R.dev_f32(x_in)
-    L.llmdec_layer_prefill(case.cfg, case.packed.struct, 0, xd.data_ptr(), n, T, max(lens), R.dev_i32(cu).data_ptr(),
-                           R.dev_i32(starts).data_ptr(), case.bt_dev.data_ptr(), case.max_pages, case.pool.handle,
+    cu_d, st_d = R.dev_i32(cu), R.dev_i32(starts)
+    L.llmdec_layer_prefill(case.cfg, case.packed.struct, 0, xd.data_ptr(), n, T, max(lens), cu_d.data_ptr(),
+                           st_d.data_ptr(), case.bt_dev.data_ptr(), case.max_pages, case.pool.handle,
                            ws.ptr, ws.nbytes, R.stream())
     torch.cuda.synchronize()
     assert ws.error_bits() == 0

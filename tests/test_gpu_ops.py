@@ -118,8 +118,9 @@ def test_rope_append_slots_and_values(L, R, H, D):
     qkv = rng.standard_normal((T, 3 * h)).astype(np.float32)
     qd = R.dev_f32(qkv)
     ws = R.Workspace(4096)
-    L.llmdec_op_rope_append(cfg, qd.data_ptr(), T, R.dev_i32([t[0] for t in toks]).data_ptr(),
-                            R.dev_i32([t[1] for t in toks]).data_ptr(), R.dev_i32(bt).data_ptr(), max_pages,
+    seq_d, pos_d, bt_d = R.dev_i32([t[0] for t in toks]), R.dev_i32([t[1] for t in toks]), R.dev_i32(bt)
+    L.llmdec_op_rope_append(cfg, qd.data_ptr(), T, len(lengths), seq_d.data_ptr(), pos_d.data_ptr(), bt_d.data_ptr(),
+                            max_pages,
                             pool.handle, 0, ws.ptr, ws.nbytes, R.stream())
     torch.cuda.synchronize()
     assert ws.error_bits() == 0
@@ -150,7 +151,8 @@ def test_rope_append_slots_and_values(L, R, H, D):
     n = lengths[s]
     ko = torch.empty(n, H, D, dtype=torch.int16, device="cuda")
     vo = torch.empty_like(ko)
-    L.llmdec_debug_gather_kv(pool.handle, 0, R.dev_i32(bt[s]).data_ptr(), n, ko.data_ptr(), vo.data_ptr(), R.stream())
+    row_d = R.dev_i32(bt[s])
+    L.llmdec_debug_gather_kv(pool.handle, 0, row_d.data_ptr(), n, ko.data_ptr(), vo.data_ptr(), R.stream())
     torch.cuda.synchronize()
     kg, vg = R.host_u16(ko), R.host_u16(vo)
     for p in range(n):
@@ -193,8 +195,8 @@ def test_decode_attention(L, R, H, D, ctxs):
     q = (rng.standard_normal((n, H * D)) * 1.5).astype(np.float32)
     out = torch.empty(n, H * D, dtype=torch.float32, device="cuda")
     ws = R.Workspace(L.llmdec_workspace_bytes(cfg, n, n, max_pages))
-    L.llmdec_op_decode_attention(cfg, R.dev_f32(q).data_ptr(), n, R.dev_i32(ctxs).data_ptr(), R.dev_i32(bt).data_ptr(),
-                                 max_pages, pool.handle, 0, out.data_ptr(), ws.ptr, ws.nbytes, R.stream())
+    q_d, ctx_d, bt_d = R.dev_f32(q), R.dev_i32(ctxs), R.dev_i32(bt)
+    L.llmdec_op_decode_attention(cfg, q_d.data_ptr(), n, ctx_d.data_ptr(), bt_d.data_ptr(), max_pages, pool.handle, 0, out.data_ptr(), ws.ptr, ws.nbytes, R.stream())
     torch.cuda.synchronize()
     assert ws.error_bits() == 0
     got = out.cpu().numpy()
@@ -225,9 +227,9 @@ def test_prefill_attention(L, R, H, D, seqs):
     q = (rng.standard_normal((T, H * D)) * 1.5).astype(np.float32)
     out = torch.full((T, H * D), float("nan"), dtype=torch.float32, device="cuda")
     ws = R.Workspace(4096)
-    L.llmdec_op_prefill_attention(cfg, R.dev_f32(q).data_ptr(), n, T, max(ln for _, ln in seqs),
-                                  R.dev_i32(cu).data_ptr(), R.dev_i32([s0 for s0, _ in seqs]).data_ptr(),
-                                  R.dev_i32(bt).data_ptr(), max_pages, pool.handle, 0, out.data_ptr(), ws.ptr,
+    q_d, cu_d, st_d, bt_d = R.dev_f32(q), R.dev_i32(cu), R.dev_i32([s0 for s0, _ in seqs]), R.dev_i32(bt)
+    L.llmdec_op_prefill_attention(cfg, q_d.data_ptr(), n, T, max(ln for _, ln in seqs), cu_d.data_ptr(),
+                                  st_d.data_ptr(), bt_d.data_ptr(), max_pages, pool.handle, 0, out.data_ptr(), ws.ptr,
                                   ws.nbytes, R.stream())
     torch.cuda.synchronize()
     assert ws.error_bits() == 0
@@ -248,7 +250,8 @@ def test_silu_mul(L, R):
     g = (rng.standard_normal((3, 688)) * 4).astype(np.float32)
     u = rng.standard_normal((3, 688)).astype(np.float32)
     out = torch.empty(3, 688, dtype=torch.float32, device="cuda")
-    L.llmdec_op_silu_mul(R.dev_f32(g).data_ptr(), R.dev_f32(u).data_ptr(), 3, 688, out.data_ptr(), R.stream())
+    g_d, u_d = R.dev_f32(g), R.dev_f32(u)
+    L.llmdec_op_silu_mul(g_d.data_ptr(), u_d.data_ptr(), 3, 688, out.data_ptr(), R.stream())
     torch.cuda.synchronize()
     assert_close("silu_mul", out.cpu().numpy(), od.silu(g) * u, max_abs=1e-5, rel_l2=1e-6)
 
@@ -268,7 +271,8 @@ def test_lm_head_argmax(L, R, rows, vocab):
     logits = torch.empty(rows, vocab, dtype=torch.float32, device="cuda")
     wsb = L.llmdec_op_linear_ws_bytes(rows, hidden, vocab)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    L.llmdec_op_lm_head_argmax(R.dev_f32(x).data_ptr(), rows, hidden, pm.ptr, vocab, nxt.data_ptr(), logits.data_ptr(),
+    x_d = R.dev_f32(x)
+    L.llmdec_op_lm_head_argmax(x_d.data_ptr(), rows, hidden, pm.ptr, vocab, nxt.data_ptr(), logits.data_ptr(),
                                ws.data_ptr(), wsb, R.stream())
     torch.cuda.synchronize()
     ref = x.astype(np.float64) @ od.widen_bf16(w).T

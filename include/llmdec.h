@@ -33,6 +33,12 @@
  *    word in the workspace, read back by llmdec_workspace_error().
  *  - bf16 means IEEE-754 binary32 truncated to its top 16 bits; rounding into
  *    bf16 is to nearest, ties to even.
+ *  - Precision: weights and cached K/V are bf16 (the K/V values rounded to
+ *    nearest-even when appended).  Activations entering a weight product are
+ *    carried as a bf16 pair hi + lo (about 17 significant bits) and multiply
+ *    the bf16 weights on the matrix cores with fp32 accumulation; the
+ *    residual stream, attention (scores, softmax, weighted sum) and logits
+ *    are fp32.
  *  - Not thread-safe per pool handle; distinct handles are independent.
  */
 #ifndef LLMDEC_H
@@ -162,7 +168,8 @@ llmdec_status llmdec_debug_gather_kv(const llmdec_kv_pool *pool, int32_t layer, 
 /* ------------------------------------------------------------------ workspace */
 /* Bytes of device scratch needed for steps of up to max_tokens new tokens over
  * up to max_seqs sequences whose block-table rows are max_pages wide.  The
- * first 256 bytes hold the sticky device error word. */
+ * first 256 bytes hold the sticky device error word.  A workspace serves one
+ * stream at a time: calls that overlap on one workspace race. */
 size_t llmdec_workspace_bytes(const llmdec_config *cfg, int32_t max_tokens, int32_t max_seqs, int32_t max_pages);
 /* Clear the device error word (enqueued on stream). */
 llmdec_status llmdec_workspace_reset(void *ws, size_t ws_bytes, llmdec_stream stream);
@@ -217,23 +224,46 @@ llmdec_status llmdec_model_step_greedy(const llmdec_config *cfg, const llmdec_mo
 
 /* ------------------------------------------------------------------ single operations
  * The kernels the layer steps are built from, exposed one by one so each can
- * be checked on its own.  Same conventions as above. */
+ * be checked on its own.  Same conventions as above.
+ *
+ * Packed activations: a bf16 [R][C] matrix (R a multiple of 16, C of 32) is
+ * stored as 16 x 32 tiles, tile (R/16 index i, C/32 index t) at element
+ * offset (i * C/32 + t) * 512; inside a tile, lane l = (r % 16) + 16 * ((c %
+ * 32) / 8) holds elements c % 8 = 0..7 at l * 8 + c % 8.  This is the operand
+ * order of one 16x16x32 matrix-core instruction, so every operand fetch is
+ * one contiguous 16-byte load. */
 
 /* y = x * (mean(x^2) + eps)^(-1/2) * gamma per row ([E] §4.2).  x: dev fp32
- * [rows][n]; gamma: dev bf16 [n].  Any of out_f32 (fp32 [rows][n]) and the
- * pair out_hi/out_lo (bf16 [rows][ld_split], hi = bf16(y), lo = bf16(y - hi),
- * columns n..ld_split-1 zeroed) may be NULL but not all. */
+ * [rows][n], n a multiple of 32 and at most 8192; gamma: dev bf16 [n].
+ * out_f32 (fp32 [rows][n]) and the pair out_hi / out_lo (hi = bf16(y), lo =
+ * bf16(y - hi), each in the packed tile layout of a
+ * [round_up(rows,16)][ld_packed] matrix: see "Packed activations" below;
+ * columns n..ld_packed-1 zeroed) may each be NULL but not both. */
 llmdec_status llmdec_op_rmsnorm(const float *x, const void *gamma, int32_t rows, int32_t n, float eps,
-                                float *out_f32, void *out_hi, void *out_lo, int32_t ld_split, llmdec_stream stream);
+                                float *out_f32, void *out_hi, void *out_lo, int32_t ld_packed, llmdec_stream stream);
 
-/* out[m][n] (+)= sum_k a[m][k] * W[n][k] for a dev fp32 [rows][k_dim] and a
- * packed W (llmdec_pack_matrix of [n_dim][k_dim]).  accumulate = 0 stores, 1
- * adds into out (the residual add of [W] §1.1).  ws: scratch for the split
- * operands and split-k partial sums (>= llmdec_op_linear_ws_bytes).
- * rows == 1 takes the fp32 GEMV path; rows > 1 the matrix-core path. */
+/* out[m][n] (+)= sum_k a[m][k] * W[n][k], fp32 accumulation, for a dev fp32
+ * a [rows][k_dim] (carried as a bf16 hi/lo pair, as every activation
+ * entering a weight product is) and a packed W (llmdec_pack_matrix of
+ * [n_dim][k_dim]).  accumulate = 0 stores, 1 adds into out (the residual add
+ * of [W] §1.1).  ws: scratch for the activation pair and split-k partial
+ * sums (>= llmdec_op_linear_ws_bytes).  rows <= 64 takes the
+ * weight-streaming kernel, rows > 64 the LDS-tiled one. */
 size_t llmdec_op_linear_ws_bytes(int32_t rows, int32_t k_dim, int32_t n_dim);
 llmdec_status llmdec_op_linear(const float *a, int32_t rows, int32_t k_dim, const void *w_packed, int32_t n_dim,
                                float *out, int32_t accumulate, void *ws, size_t ws_bytes, llmdec_stream stream);
+
+/* The gate/up product with the SwiGLU epilogue, as the layer steps run it
+ * ([W] §1.2, [E] §4.2): for a fused gate/up matrix as llmdec_pack_layer lays
+ * it out (16-row blocks alternating gate and up, 2*inter rows), writes
+ * u[m][j] = silu(g[m][j]) * up[m][j], g and up the fp32 products, as the
+ * hi/lo pair out_hi / out_lo, each in the packed layout of a
+ * [round_up(rows,16)][ld_packed] matrix (inter <= ld_packed <= inter + 16,
+ * ld_packed a multiple of 32; columns inter.. zeroed).  ws as for
+ * llmdec_op_linear with n_dim = 2*inter. */
+llmdec_status llmdec_op_swiglu_linear(const float *a, int32_t rows, int32_t k_dim, const void *w_gu_packed,
+                                      int32_t inter, void *out_hi, void *out_lo, int32_t ld_packed, void *ws,
+                                      size_t ws_bytes, llmdec_stream stream);
 
 /* Rotate q and k of each new token by its position and store bf16 k, v into
  * the pool ([E] §4.3: rotation first, then the cache update).  qkv: dev fp32

@@ -62,11 +62,13 @@ WsLayout ws_layout(const llmdec_config &c, int max_tokens, int max_seqs, int max
   WsLayout L{};
   const int T = std::max(1, max_tokens), S = std::max(1, max_seqs), P = std::max(1, max_pages);
   const int h = c.hidden, I = c.intermediate;
+  const int rows = std::max(T, S);
   L.max_tokens = T;
   L.max_seqs = S;
   L.max_pages = P;
-  L.kpad_max = round_up(std::max(h, I), kTileK);
-  const int rows_pad = round_up(std::max(T, S), 16);
+  L.row_blocks = (rows + 15) / 16;
+  L.kpad_h = round_up(h, kTileK);
+  L.kpad_i = round_up(I, kTileK);
   // decode-attention partial slots: the worst case over every batch size up to S
   size_t slots = 0;
   for (int n = 1; n <= S; ++n) {
@@ -75,10 +77,11 @@ WsLayout ws_layout(const llmdec_config &c, int max_tokens, int max_seqs, int max
     slots = std::max(slots, (size_t)n * c.n_heads * parts);
   }
   L.attn_slots = (int)slots;
+  // split-k partial sums: the worst case over every streamed product (rows <= 64) this workspace can see
   size_t part = 0;
-  const int rows_lin = std::max(T, S);
   const int shapes[5][2] = {{3 * h, h}, {h, h}, {2 * I, h}, {h, I}, {c.vocab, h}};
-  for (auto &sh : shapes) part = std::max(part, linear_partial_floats(std::min(rows_lin, 64), sh[0], sh[1]));
+  for (int m = 1; m <= std::min(rows, 64); ++m)
+    for (auto &sh : shapes) part = std::max(part, linear_partial_floats(m, sh[0], sh[1]));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -88,17 +91,16 @@ WsLayout ws_layout(const llmdec_config &c, int max_tokens, int max_seqs, int max
   L.err = take(kWsHeader);
   L.tok_seq = take(sizeof(int32_t) * T);
   L.tok_pos = take(sizeof(int32_t) * T);
-  L.x = take(sizeof(float) * (size_t)std::max(T, S) * h);
-  L.act_f32 = take(sizeof(float) * (size_t)std::max(T, S) * std::max(h, I));
-  L.act_hi = take(sizeof(uint16_t) * (size_t)rows_pad * L.kpad_max);
-  L.act_lo = take(sizeof(uint16_t) * (size_t)rows_pad * L.kpad_max);
-  L.qkv = take(sizeof(float) * (size_t)T * 3 * h);
-  L.attn = take(sizeof(float) * (size_t)T * h);
-  L.gu = take(sizeof(float) * (size_t)T * 2 * I);
+  L.x = take(sizeof(float) * (size_t)rows * h);
+  L.act_h = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_h);
+  L.act_hl = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_h);
+  L.act_i = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_i);
+  L.act_il = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_i);
+  L.qkv = take(sizeof(float) * (size_t)rows * 3 * h);
   L.part = take(sizeof(float) * part);
+  L.part_floats = part;
   L.attn_part = take(sizeof(float) * slots * (c.head_dim + 2));
   L.logits = take(sizeof(float) * (size_t)S * c.vocab);
-  L.amax = take(256);
   L.total = off;
   return L;
 }
@@ -169,54 +171,57 @@ static void run_layer(const LayerArgs &a) {
   const int h = c.hidden, I = c.intermediate, M = a.rows;
   const WsLayout &L = a.L;
   uint32_t *err = at<uint32_t>(a.ws, L.err);
-  float *act = at<float>(a.ws, L.act_f32);
-  uint16_t *hi = at<uint16_t>(a.ws, L.act_hi), *lo = at<uint16_t>(a.ws, L.act_lo);
-  float *qkv = at<float>(a.ws, L.qkv), *gu = at<float>(a.ws, L.gu), *part = at<float>(a.ws, L.part);
-  const size_t part_n = (L.attn_part - L.part) / sizeof(float);
-  const bool vec = M == 1;  // GEMV path: fp32 activations
-  const int kh = round_up(h, kTileK), ki = round_up(I, kTileK);
-  Act ah, ai;
-  if (vec) {
-    ah.f32 = act;
-    ai.f32 = act;
-  } else {
-    ah.hi = ai.hi = hi;
-    ah.lo = ai.lo = lo;
-    ah.kpad = kh;
-    ai.kpad = ki;
-  }
-  ah.rows = ai.rows = M;
+  uint16_t *ah_hi = at<uint16_t>(a.ws, L.act_h), *ah_lo = at<uint16_t>(a.ws, L.act_hl);
+  uint16_t *ai_hi = at<uint16_t>(a.ws, L.act_i), *ai_lo = at<uint16_t>(a.ws, L.act_il);
+  float *qkv = at<float>(a.ws, L.qkv), *part = at<float>(a.ws, L.part);
+  const Act ah{ah_hi, ah_lo, M, L.kpad_h, L.row_blocks}, ai{ai_hi, ai_lo, M, L.kpad_i, L.row_blocks};
   uint16_t *pk, *pv;
   pool_layer(a.pool, a.layer, &pk, &pv);
-  const uint16_t *W = nullptr;
 
   // attention block: x += Wo . attn(rope(Wq y), rope(Wk y), Wv y),  y = RMSNorm(x)
-  launch_rmsnorm(a.hidden, h, nullptr, M, (const uint16_t *)a.w->attn_norm, M, h, c.rms_eps, err, vec ? act : nullptr,
-                 vec ? nullptr : hi, vec ? nullptr : lo, kh, a.s);
-  W = (const uint16_t *)a.w->w_qkv;
-  launch_linear(ah, W, 3 * h, h, qkv, 3 * h, kStore, part, part_n, a.s);
+  launch_rmsnorm(a.hidden, h, nullptr, M, (const uint16_t *)a.w->attn_norm, M, h, c.rms_eps, err, nullptr, ah_hi,
+                 ah_lo, L.kpad_h, nullptr, 1, a.s);
+  LinearOut o_qkv;
+  o_qkv.kind = kStore;
+  o_qkv.f32 = qkv;
+  o_qkv.ld = 3 * h;
+  // a split q|k|v product leaves partial sums that the rotary/append kernel adds up
+  const int ks_qkv = launch_linear(ah, (const uint16_t *)a.w->w_qkv, 3 * h, h, o_qkv, part, L.part_floats, true, a.s);
+  const float *qkv_part = ks_qkv > 1 ? part : nullptr;
   if (a.decode) {
-    launch_rope_append(c, qkv, 3 * h, M, a.n_seqs, nullptr, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages, err, a.s);
+    launch_rope_append(c, qkv, qkv_part, ks_qkv, 3 * h, M, a.n_seqs, nullptr, a.ctx, a.bt, a.max_pages, pk, pv,
+                       a.pool->num_pages, err, a.s);
     launch_decode_attention(c, qkv, 3 * h, M, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages,
-                            at<float>(a.ws, L.attn_part), vec ? act : nullptr, vec ? nullptr : hi, vec ? nullptr : lo,
-                            kh, err, a.s);
+                            at<float>(a.ws, L.attn_part), nullptr, ah_hi, ah_lo, L.kpad_h, err, a.s);
   } else {
     int32_t *ts = at<int32_t>(a.ws, L.tok_seq), *tp = at<int32_t>(a.ws, L.tok_pos);
     launch_token_map(a.cu, a.start, a.n_seqs, M, err, ts, tp, a.s);
-    launch_rope_append(c, qkv, 3 * h, M, a.n_seqs, ts, tp, a.bt, a.max_pages, pk, pv, a.pool->num_pages, err, a.s);
+    launch_rope_append(c, qkv, qkv_part, ks_qkv, 3 * h, M, a.n_seqs, ts, tp, a.bt, a.max_pages, pk, pv,
+                       a.pool->num_pages, err, a.s);
     launch_prefill_attention(c, qkv, 3 * h, a.n_seqs, M, a.max_q_len, a.cu, a.start, a.bt, a.max_pages, pk, pv,
-                             a.pool->num_pages, vec ? act : nullptr, vec ? nullptr : hi, vec ? nullptr : lo, kh, err,
-                             a.s);
+                             a.pool->num_pages, nullptr, ah_hi, ah_lo, L.kpad_h, err, a.s);
   }
-  launch_linear(ah, (const uint16_t *)a.w->w_o, h, h, a.hidden, h, kAccumulate, part, part_n, a.s);
+  LinearOut o_res;
+  o_res.kind = kAccumulate;
+  o_res.f32 = a.hidden;
+  o_res.ld = h;
+  // a split output projection leaves partial sums that the MLP's RMSNorm adds into x before normalising
+  const int ks_o = launch_linear(ah, (const uint16_t *)a.w->w_o, h, h, o_res, part, L.part_floats, true, a.s);
 
-  // MLP block: x += Wd (silu(Wg y) * (Wu y)),  y = RMSNorm(x)
-  launch_rmsnorm(a.hidden, h, nullptr, M, (const uint16_t *)a.w->mlp_norm, M, h, c.rms_eps, err, vec ? act : nullptr,
-                 vec ? nullptr : hi, vec ? nullptr : lo, kh, a.s);
-  launch_linear(ah, (const uint16_t *)a.w->w_gu, 2 * I, h, gu, 2 * I, kStore, part, part_n, a.s);
-  // gate/up rows alternate in 16-row blocks: gate j at column 32(j/16) + j%16, up 16 further
-  launch_silu_mul(gu, gu + 16, 2 * I, 32, M, I, vec ? act : nullptr, vec ? nullptr : hi, vec ? nullptr : lo, ki, a.s);
-  launch_linear(ai, (const uint16_t *)a.w->w_down, h, I, a.hidden, h, kAccumulate, part, part_n, a.s);
+  // MLP block: x += Wd (silu(Wg y) * (Wu y)),  y = RMSNorm(x); the gate/up product's epilogue forms the
+  // SwiGLU activation directly
+  launch_rmsnorm(a.hidden, h, nullptr, M, (const uint16_t *)a.w->mlp_norm, M, h, c.rms_eps, err, nullptr, ah_hi,
+                 ah_lo, L.kpad_h, ks_o > 1 ? part : nullptr, ks_o, a.s);
+  LinearOut o_gu;
+  o_gu.kind = kSiluMul;
+  o_gu.act_hi = ai_hi;
+  o_gu.act_lo = ai_lo;
+  o_gu.act_kt = L.kpad_i / kTileK;
+  o_gu.act_cols = I;
+  const int ks_gu = launch_linear(ah, (const uint16_t *)a.w->w_gu, 2 * I, h, o_gu, part, L.part_floats, true, a.s);
+  if (ks_gu > 1) launch_reduce(part, ks_gu, M, 2 * I, o_gu, a.s);
+  const int ks_d = launch_linear(ai, (const uint16_t *)a.w->w_down, h, I, o_res, part, L.part_floats, true, a.s);
+  if (ks_d > 1) launch_reduce(part, ks_d, M, h, o_res, a.s);
 }
 
 }  // namespace llmdec
@@ -428,82 +433,102 @@ extern "C" llmdec_status llmdec_model_step_greedy(const llmdec_config *cfg, cons
   }
   // final norm on each sequence's last new token, lm_head, argmax ([W] §1.1, [F] §2.2.3)
   const int h = cfg->hidden;
-  const bool vec = n_seqs == 1;
-  float *act = at<float>(ws, L.act_f32);
-  uint16_t *hi = at<uint16_t>(ws, L.act_hi), *lo = at<uint16_t>(ws, L.act_lo);
-  const int kh = round_up(h, kTileK);
+  uint16_t *act_h = at<uint16_t>(ws, L.act_h), *act_hl = at<uint16_t>(ws, L.act_hl);
   launch_rmsnorm(x, h, decode ? nullptr : cu_seqlens, n_tokens, (const uint16_t *)w->final_norm, n_seqs, h,
-                 cfg->rms_eps, at<uint32_t>(ws, L.err),
-                 vec ? act : nullptr, vec ? nullptr : hi, vec ? nullptr : lo, kh, s);
-  Act a;
-  a.rows = n_seqs;
-  if (vec) {
-    a.f32 = act;
-  } else {
-    a.hi = hi;
-    a.lo = lo;
-    a.kpad = kh;
-  }
+                 cfg->rms_eps, at<uint32_t>(ws, L.err), nullptr, act_h, act_hl, L.kpad_h, nullptr, 1, s);
   float *lg = logits ? logits : at<float>(ws, L.logits);
-  launch_linear(a, (const uint16_t *)w->lm_head, cfg->vocab, h, lg, cfg->vocab, kStore, at<float>(ws, L.part),
-                (L.attn_part - L.part) / sizeof(float), s);
+  LinearOut o;
+  o.kind = kStore;
+  o.f32 = lg;
+  o.ld = cfg->vocab;
+  float *part = at<float>(ws, L.part);
+  const int ks = launch_linear(Act{act_h, act_hl, n_seqs, L.kpad_h, L.row_blocks}, (const uint16_t *)w->lm_head,
+                               cfg->vocab, h, o, part, L.part_floats, true, s);
+  if (ks > 1) launch_reduce(part, ks, n_seqs, cfg->vocab, o, s);
   launch_argmax(lg, n_seqs, cfg->vocab, next_tokens, s);
   return check_launch(who);
 }
 
 // ------------------------------------------------------------------ single operations
 extern "C" llmdec_status llmdec_op_rmsnorm(const float *x, const void *gamma, int32_t rows, int32_t n, float eps,
-                                          float *out_f32, void *out_hi, void *out_lo, int32_t ld_split,
+                                          float *out_f32, void *out_hi, void *out_lo, int32_t ld_packed,
                                           llmdec_stream stream) {
   if (!x || !gamma || (!out_f32 && !out_hi) || (!out_hi != !out_lo))
     return set_error(LLMDEC_E_INVALID, "op_rmsnorm: NULL pointer");
-  if (rows <= 0 || n <= 0 || (out_hi && (ld_split < n || ld_split % 32)))
-    return set_error(LLMDEC_E_INVALID, "op_rmsnorm: rows=%d n=%d ld_split=%d out of range", rows, n, ld_split);
-  launch_rmsnorm(x, n, nullptr, rows, (const uint16_t *)gamma, rows, n, eps, nullptr, out_f32, (uint16_t *)out_hi,
-                 (uint16_t *)out_lo, ld_split, (hipStream_t)stream);
+  if (rows <= 0 || n <= 0 || n % 32 || n > 8192 || (out_hi && (ld_packed < n || ld_packed % 32)))
+    return set_error(LLMDEC_E_INVALID, "op_rmsnorm: rows=%d n=%d (a multiple of 32, <= 8192) ld_packed=%d out of range",
+                     rows, n, ld_packed);
+  launch_rmsnorm(const_cast<float *>(x), n, nullptr, rows, (const uint16_t *)gamma, rows, n, eps, nullptr, out_f32,
+                 (uint16_t *)out_hi, (uint16_t *)out_lo, ld_packed, nullptr, 1, (hipStream_t)stream);
   return check_launch("op_rmsnorm");
 }
 
-static size_t op_linear_parts(int rows, int k, int n, size_t *hi_off, size_t *lo_off, size_t *part_off) {
+// Workspace of the stand-alone products: error word, the packed hi/lo activation, partial sums.
+static size_t op_linear_parts(int rows, int k, int n, size_t *act_off, size_t *part_off) {
   const int kp = round_up(k, kTileK);
-  const size_t split = rows > 1 ? al((size_t)round_up(rows, 16) * kp * 2) : 0;
-  *hi_off = kWsHeader;
-  *lo_off = *hi_off + split;
-  *part_off = *lo_off + split;
+  const size_t act = al((size_t)round_up(rows, 16) * kp * 2);
+  *act_off = kWsHeader;
+  *part_off = *act_off + 2 * act;
   return *part_off + al(linear_partial_floats(rows, n, k) * sizeof(float));
 }
 
 extern "C" size_t llmdec_op_linear_ws_bytes(int32_t rows, int32_t k_dim, int32_t n_dim) {
-  size_t a, b, c;
+  size_t a, b;
   if (rows <= 0 || k_dim <= 0 || n_dim <= 0) return 0;
-  return op_linear_parts(rows, k_dim, n_dim, &a, &b, &c);
+  return op_linear_parts(rows, k_dim, n_dim, &a, &b);
+}
+
+static llmdec_status run_op_linear(const char *who, const float *a, int32_t rows, int32_t k_dim, const void *w_packed,
+                                   int32_t n_dim, const LinearOut &o, void *ws, size_t ws_bytes, size_t extra,
+                                   hipStream_t s) {
+  size_t act_off, part_off;
+  const size_t need = op_linear_parts(rows, k_dim, n_dim, &act_off, &part_off) + extra;
+  llmdec_status st = check_ws(ws, ws_bytes, need, who);
+  if (st != LLMDEC_OK) return st;
+  const int kp = round_up(k_dim, kTileK);
+  uint16_t *hi = at<uint16_t>(ws, act_off);
+  uint16_t *lo = hi + (size_t)round_up(rows, 16) * kp;
+  launch_split(a, k_dim, rows, k_dim, hi, lo, kp, s);
+  float *part = at<float>(ws, part_off);
+  const int ks = launch_linear(Act{hi, lo, rows, kp, (rows + 15) / 16}, (const uint16_t *)w_packed, n_dim, k_dim, o,
+                               part, linear_partial_floats(rows, n_dim, k_dim), true, s);
+  if (ks > 1) launch_reduce(part, ks, rows, n_dim, o, s);
+  return LLMDEC_OK;
 }
 
 extern "C" llmdec_status llmdec_op_linear(const float *a, int32_t rows, int32_t k_dim, const void *w_packed,
                                          int32_t n_dim, float *out, int32_t accumulate, void *ws, size_t ws_bytes,
                                          llmdec_stream stream) {
   if (!a || !w_packed || !out) return set_error(LLMDEC_E_INVALID, "op_linear: NULL pointer");
-  if (rows <= 0 || k_dim <= 0 || k_dim > 16384 || n_dim <= 0 || n_dim % 16)
-    return set_error(LLMDEC_E_INVALID, "op_linear: rows=%d k=%d n=%d out of range (n a multiple of 16, k <= 16384)",
-                     rows, k_dim, n_dim);
-  size_t hi_off, lo_off, part_off;
-  const size_t need = op_linear_parts(rows, k_dim, n_dim, &hi_off, &lo_off, &part_off);
-  llmdec_status st = check_ws(ws, ws_bytes, need, "op_linear");
-  if (st != LLMDEC_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  Act act;
-  act.rows = rows;
-  if (rows == 1) {
-    act.f32 = a;
-  } else {
-    act.kpad = round_up(k_dim, kTileK);
-    act.hi = at<uint16_t>(ws, hi_off);
-    act.lo = at<uint16_t>(ws, lo_off);
-    launch_split(a, k_dim, rows, k_dim, (uint16_t *)act.hi, (uint16_t *)act.lo, act.kpad, s);
-  }
-  launch_linear(act, (const uint16_t *)w_packed, n_dim, k_dim, out, n_dim, accumulate ? kAccumulate : kStore,
-                at<float>(ws, part_off), linear_partial_floats(rows, n_dim, k_dim), s);
-  return check_launch("op_linear");
+  if (rows <= 0 || k_dim <= 0 || n_dim <= 0 || n_dim % 16)
+    return set_error(LLMDEC_E_INVALID, "op_linear: rows=%d k=%d n=%d out of range (n a multiple of 16)", rows, k_dim,
+                     n_dim);
+  LinearOut o;
+  o.kind = accumulate ? kAccumulate : kStore;
+  o.f32 = out;
+  o.ld = n_dim;
+  llmdec_status st = run_op_linear("op_linear", a, rows, k_dim, w_packed, n_dim, o, ws, ws_bytes, 0,
+                                   (hipStream_t)stream);
+  return st != LLMDEC_OK ? st : check_launch("op_linear");
+}
+
+extern "C" llmdec_status llmdec_op_swiglu_linear(const float *a, int32_t rows, int32_t k_dim, const void *w_gu_packed,
+                                                int32_t inter, void *out_hi, void *out_lo, int32_t ld_packed,
+                                                void *ws, size_t ws_bytes, llmdec_stream stream) {
+  if (!a || !w_gu_packed || !out_hi || !out_lo) return set_error(LLMDEC_E_INVALID, "op_swiglu_linear: NULL pointer");
+  if (rows <= 0 || k_dim <= 0 || inter <= 0 || inter % 16 || ld_packed < inter || ld_packed % 32 ||
+      ld_packed - inter > 16)
+    return set_error(LLMDEC_E_INVALID, "op_swiglu_linear: rows=%d k=%d inter=%d ld_packed=%d out of range", rows, k_dim,
+                     inter, ld_packed);
+  LinearOut o;
+  o.kind = kSiluMul;
+  o.act_hi = (uint16_t *)out_hi;
+  o.act_lo = (uint16_t *)out_lo;
+  o.act_kt = ld_packed / kTileK;
+  o.act_cols = inter;
+  llmdec_status st = run_op_linear("op_swiglu_linear", a, rows, k_dim, w_gu_packed, 2 * inter, o, ws, ws_bytes, 0,
+                                   (hipStream_t)stream);
+  return st != LLMDEC_OK ? st : check_launch("op_swiglu_linear");
 }
 
 extern "C" llmdec_status llmdec_op_rope_append(const llmdec_config *cfg, float *qkv, int32_t n_tokens,
@@ -520,7 +545,7 @@ extern "C" llmdec_status llmdec_op_rope_append(const llmdec_config *cfg, float *
     return set_error(LLMDEC_E_INVALID, "%s: n_tokens/n_seqs/max_pages out of range", who);
   uint16_t *pk, *pv;
   pool_layer(pool, layer, &pk, &pv);
-  launch_rope_append(*cfg, qkv, 3 * cfg->hidden, n_tokens, n_seqs, seq_of_token, pos_of_token, block_tables, max_pages, pk, pv,
+  launch_rope_append(*cfg, qkv, nullptr, 1, 3 * cfg->hidden, n_tokens, n_seqs, seq_of_token, pos_of_token, block_tables, max_pages, pk, pv,
                      pool->num_pages, (uint32_t *)ws, (hipStream_t)stream);
   return check_launch(who);
 }
@@ -571,7 +596,7 @@ extern "C" llmdec_status llmdec_op_silu_mul(const float *gate, const float *up, 
                                            llmdec_stream stream) {
   if (!gate || !up || !out) return set_error(LLMDEC_E_INVALID, "op_silu_mul: NULL pointer");
   if (rows <= 0 || n <= 0) return set_error(LLMDEC_E_INVALID, "op_silu_mul: rows=%d n=%d out of range", rows, n);
-  launch_silu_mul(gate, up, n, 16, rows, n, out, nullptr, nullptr, 0, (hipStream_t)stream);
+  launch_silu_mul(gate, up, rows, n, out, (hipStream_t)stream);
   return check_launch("op_silu_mul");
 }
 
@@ -581,26 +606,17 @@ extern "C" llmdec_status llmdec_op_lm_head_argmax(const float *x, int32_t rows, 
   if (!x || !lm_head_packed || !next) return set_error(LLMDEC_E_INVALID, "op_lm_head_argmax: NULL pointer");
   if (rows <= 0 || hidden <= 0 || vocab <= 0 || vocab % 16)
     return set_error(LLMDEC_E_INVALID, "op_lm_head_argmax: rows=%d hidden=%d vocab=%d out of range", rows, hidden, vocab);
-  size_t hi_off, lo_off, part_off;
-  size_t need = op_linear_parts(rows, hidden, vocab, &hi_off, &lo_off, &part_off);
-  const size_t logit_off = need;
-  if (!logits_out) need += al((size_t)rows * vocab * sizeof(float));
-  llmdec_status st = check_ws(ws, ws_bytes, need, "op_lm_head_argmax");
-  if (st != LLMDEC_OK) return st;
+  size_t act_off, part_off;
+  const size_t logit_off = op_linear_parts(rows, hidden, vocab, &act_off, &part_off);
+  const size_t extra = logits_out ? 0 : al((size_t)rows * vocab * sizeof(float));
+  float *lg = logits_out ? logits_out : (ws ? at<float>(ws, logit_off) : nullptr);
+  LinearOut o;
+  o.kind = kStore;
+  o.f32 = lg;
+  o.ld = vocab;
   hipStream_t s = (hipStream_t)stream;
-  Act act;
-  act.rows = rows;
-  if (rows == 1) {
-    act.f32 = x;
-  } else {
-    act.kpad = round_up(hidden, kTileK);
-    act.hi = at<uint16_t>(ws, hi_off);
-    act.lo = at<uint16_t>(ws, lo_off);
-    launch_split(x, hidden, rows, hidden, (uint16_t *)act.hi, (uint16_t *)act.lo, act.kpad, s);
-  }
-  float *lg = logits_out ? logits_out : at<float>(ws, logit_off);
-  launch_linear(act, (const uint16_t *)lm_head_packed, vocab, hidden, lg, vocab, kStore, at<float>(ws, part_off),
-                linear_partial_floats(rows, vocab, hidden), s);
+  llmdec_status st = run_op_linear("op_lm_head_argmax", x, rows, hidden, lm_head_packed, vocab, o, ws, ws_bytes, extra, s);
+  if (st != LLMDEC_OK) return st;
   launch_argmax(lg, rows, vocab, next, s);
   return check_launch("op_lm_head_argmax");
 }

@@ -62,6 +62,46 @@ __device__ inline void split_bf16(float x, uint16_t &hi, uint16_t &lo) {
   lo = f32_to_bf16(x - bf16_to_f32(hi));
 }
 
+// Packs 8 values as two 16-byte bf16 runs, hi and lo parts.
+__device__ inline void split_pack8(const float *x, uint4 &hi, uint4 &lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    uint16_t h0, l0, h1, l1;
+    split_bf16(x[j], h0, l0);
+    split_bf16(x[j + 1], h1, l1);
+    h[j / 2] = h0 | ((uint32_t)h1 << 16);
+    l[j / 2] = l0 | ((uint32_t)l1 << 16);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// x = hi + mid + lo with hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid):
+// the differences are exact in fp32 and the three parts carry fp32's precision.
+// Packs 8 values into the three operand registers of a 16x16x32 bf16 MFMA.
+__device__ inline void split3_pack8(const float *x, uint4 &hi, uint4 &mid, uint4 &lo) {
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    uint16_t hb[2], mb[2], lb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float v = x[j + u];
+      hb[u] = f32_to_bf16(v);
+      const float r1 = v - bf16_to_f32(hb[u]);
+      mb[u] = f32_to_bf16(r1);
+      lb[u] = f32_to_bf16(r1 - bf16_to_f32(mb[u]));
+    }
+    h[j / 2] = hb[0] | ((uint32_t)hb[1] << 16);
+    m[j / 2] = mb[0] | ((uint32_t)mb[1] << 16);
+    l[j / 2] = lb[0] | ((uint32_t)lb[1] << 16);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  mid = make_uint4(m[0], m[1], m[2], m[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

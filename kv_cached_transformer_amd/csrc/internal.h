@@ -15,24 +15,41 @@ llmdec_status clear_error();
 llmdec_status check_config(const llmdec_config *cfg, const char *who);
 llmdec_status check_launch(const char *who);
 
-// How an activation matrix is handed to a linear kernel.
-//  - rows == 1: fp32 vector `f32` (GEMV path, no rounding of the activation);
-//  - rows > 1: `hi`/`lo` bf16 matrices in the packed tile layout (rows padded
-//    to 16, columns to kpad) holding bf16(a) and bf16(a - bf16(a)).
+// An activation matrix as a weight product reads it: a pair of bf16 matrices
+// hi = bf16(a), lo = bf16(a - hi) (a == hi + lo to about 2^-17 relative), both
+// in the packed tile layout, rows padded to 16 (row_blocks 16-row blocks exist
+// in the buffers), columns padded to kpad (a multiple of 32) with zeros.
 struct Act {
-  const float *f32 = nullptr;
   const uint16_t *hi = nullptr;
   const uint16_t *lo = nullptr;
   int rows = 0;
-  int kpad = 0;  // padded column count of hi/lo (multiple of 32)
+  int kpad = 0;
+  int row_blocks = 0;
 };
 
-enum Epilogue { kStore = 0, kAccumulate = 1 };
+enum Epilogue { kStore = 0, kAccumulate = 1, kSiluMul = 2 };
+
+// Where a weight product's result goes.  kStore / kAccumulate: fp32 f32[r*ld + c]
+// (= or +=).  kSiluMul: the product's row blocks alternate gate and up; the
+// result silu(gate) * up goes, as a hi/lo pair, to the packed activation
+// act_hi/act_lo with act_kt k-tiles per row block and act_cols real columns
+// (the rest of the row is zeroed).
+struct LinearOut {
+  int kind = kStore;
+  float *f32 = nullptr;
+  int ld = 0;
+  uint16_t *act_hi = nullptr;
+  uint16_t *act_lo = nullptr;
+  int act_kt = 0;
+  int act_cols = 0;
+};
+
 
 // Workspace layout for steps of up to max_tokens tokens and max_seqs sequences.
 struct WsLayout {
-  size_t err, tok_seq, tok_pos, x, act_f32, act_hi, act_lo, qkv, attn, gu, part, attn_part, logits, amax, total;
-  int max_tokens, max_seqs, max_pages, kpad_max, attn_slots, ksplit_max;
+  size_t err, tok_seq, tok_pos, x, act_h, act_hl, act_i, act_il, qkv, part, attn_part, logits, total;
+  size_t part_floats;
+  int max_tokens, max_seqs, max_pages, row_blocks, kpad_h, kpad_i, attn_slots;
 };
 WsLayout ws_layout(const llmdec_config &cfg, int max_tokens, int max_seqs, int max_pages);
 
@@ -43,19 +60,32 @@ void decode_partition(int n_seqs, int n_heads, int max_pages, int *pages_per_par
 void launch_pack_matrix(int rows, int cols, const uint16_t *src, uint16_t *dst, hipStream_t s, int nb_stride = 1);
 void launch_embed(const uint16_t *embed, const int32_t *tokens, int n_tokens, int hidden, int vocab, float *x,
                   uint32_t *err, hipStream_t s);
-// y = rmsnorm(x) * gamma on the given rows; outputs: f32 [rows][n] and/or tiled hi/lo with kpad columns.
-void launch_rmsnorm(const float *x, int ld_x, const int32_t *row_index, int n_src_rows, const uint16_t *gamma, int rows, int n,
-                    float eps, uint32_t *err, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad, hipStream_t s);
-// fp32 [rows][ld] -> tiled hi/lo [rows_pad16][kpad] (zero padding).
+// y = rmsnorm(x) * gamma on the given rows; outputs: f32 [rows][n] and/or the packed hi/lo pair with kpad
+// columns.  add_partials (may be NULL): ks fp32 [rows][n] partial sums that are first added into x (the
+// residual add of a split-k output projection), x being written back.
+void launch_rmsnorm(float *x, int ld_x, const int32_t *row_index, int n_src_rows, const uint16_t *gamma, int rows,
+                    int n, float eps, uint32_t *err, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad,
+                    const float *add_partials, int ks, hipStream_t s);
+// fp32 [rows][ld] -> packed hi/lo pair [rows_pad16][kpad], zero padding.
 void launch_split(const float *a, int ld, int rows, int cols, uint16_t *hi, uint16_t *lo, int kpad, hipStream_t s);
-void launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, float *out, int ld_out, Epilogue epi,
-                   float *partials, size_t partial_floats, hipStream_t s);
+// Weight product.  When the product is split over k (ks > 1, returned), the result is left as ks fp32
+// partial sums [ks][rows][n] in partials and the epilogue is NOT applied: the caller reduces them, either
+// with launch_reduce or inside the next kernel.  ks == 1: the epilogue is applied.
+int launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const LinearOut &o, float *partials,
+                  size_t partial_floats, bool allow_split, hipStream_t s);
+// Sum ks partial products [ks][rows][n] and apply the epilogue o.
+void launch_reduce(const float *partials, int ks, int rows, int n, const LinearOut &o, hipStream_t s);
 size_t linear_partial_floats(int rows, int n, int k);
+int stream_ksplit(int rows, int n, int k);
 void launch_token_map(const int32_t *cu_seqlens, const int32_t *start_pos, int n_seqs, int n_tokens, uint32_t *err, int32_t *tok_seq,
                       int32_t *tok_pos, hipStream_t s);
-void launch_rope_append(const llmdec_config &cfg, float *qkv, int ld_qkv, int n_tokens, int n_seqs, const int32_t *tok_seq,
+// qkv_partials / ks: when the q|k|v product was split over k, its ks partial sums [ks][n_tokens][3*hidden]
+// are added first (and the sum written to qkv); NULL / 1 otherwise.
+void launch_rope_append(const llmdec_config &cfg, float *qkv, const float *qkv_partials, int ks, int ld_qkv,
+                        int n_tokens, int n_seqs, const int32_t *tok_seq,
                         const int32_t *tok_pos, const int32_t *block_tables, int max_pages, uint16_t *pool_layer_k,
                         uint16_t *pool_layer_v, int num_pages, uint32_t *err, hipStream_t s);
+// Attention outputs go to fp32 out_f32 [rows][hidden] and/or the packed hi/lo pair with kpad columns.
 void launch_decode_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, const int32_t *ctx_lens,
                              const int32_t *block_tables, int max_pages, const uint16_t *pool_layer_k,
                              const uint16_t *pool_layer_v, int num_pages, float *partials, float *out_f32,
@@ -65,9 +95,9 @@ void launch_prefill_attention(const llmdec_config &cfg, const float *q, int ld_q
                               int max_pages, const uint16_t *pool_layer_k, const uint16_t *pool_layer_v,
                               int num_pages, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad,
                               uint32_t *err, hipStream_t s);
-// u = silu(g) * up.  g at g[r*ld_in + (j/16)*blk + j%16], up likewise from u_ptr.
-void launch_silu_mul(const float *g, const float *u, int ld_in, int blk, int rows, int n, float *out_f32,
-                     uint16_t *out_hi, uint16_t *out_lo, int kpad, hipStream_t s);
+// u = silu(g) * up elementwise, fp32 [rows][n] (the stand-alone operation; the layer steps fuse it
+// into the gate/up product's epilogue).
+void launch_silu_mul(const float *g, const float *u, int rows, int n, float *out, hipStream_t s);
 void launch_argmax(const float *logits, int rows, int vocab, int32_t *next, hipStream_t s);
 void launch_gather_kv(const uint16_t *pool_layer_k, const uint16_t *pool_layer_v, int num_pages, int n_heads,
                       int head_dim, const int32_t *row, int n_tokens, uint16_t *k_out, uint16_t *v_out,

@@ -14,8 +14,9 @@
 // Prefill: MFMA.  Scores are formed transposed, S^T = K Q^T (keys as rows),
 // so a lane's accumulator holds 4 keys of one query: exactly the operand
 // slots the P.V product O^T = V^T P^T needs, with no shuffle through LDS.  q
-// and p are split into hi/lo bf16 halves (two MFMAs each), K and V are the
-// stored bf16 values.
+// and p are split into three bf16 parts each (hi + mid + lo carries fp32's
+// 24 bits; three MFMAs per product), K and V are the stored bf16 values, so
+// the scores and the weighted sum keep fp32-level accuracy.
 #include <math.h>
 
 #include "common.h"
@@ -37,14 +38,17 @@ __device__ inline uint32_t mask_pair(uint32_t w, int t, int n_valid) {
   return t + 1 < n_valid ? w : (t < n_valid ? (w & 0xffffu) : 0u);
 }
 
-__device__ inline void store_out(float v, int r, int c, int ld, float *out_f32, uint16_t *hi, uint16_t *lo, int kpad) {
+// The attention output feeds the o projection as a packed hi/lo activation pair; the stand-alone
+// operation also (or only) writes fp32.
+__device__ inline void store_out(float v, int r, int c, int ld, float *out_f32, uint16_t *out_hi, uint16_t *out_lo,
+                                 int kpad) {
   if (out_f32) out_f32[(size_t)r * ld + c] = v;
-  if (hi) {
+  if (out_hi) {
     uint16_t h, l;
     split_bf16(v, h, l);
     const size_t o = packed_offset(r, c, kpad >> 5);
-    hi[o] = h;
-    lo[o] = l;
+    out_hi[o] = h;
+    out_lo[o] = l;
   }
 }
 
@@ -266,24 +270,21 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
   const bool q_ok = c < n_q;
   const float scale = kLog2e * rsqrtf((float)D);
 
-  // Q^T operand: lane (g, c) holds dims 32kt + 8g .. +7 of query c, split hi/lo.
-  uint4 qh[KT], ql[KT];
+  // Q^T operand: lane (g, c) holds dims 32kt + 8g .. +7 of query c as three bf16 parts
+  // (q = hi + mid + lo to fp32 precision).
+  uint4 qs[3][KT];
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
-    uint32_t hh[4] = {0, 0, 0, 0}, ll[4] = {0, 0, 0, 0};
+    float qv[8];
     if (q_ok) {
       const float *qp = q + (size_t)(t0 + qb * 16 + c) * ld_q + h * D + kt * 32 + g * 8;
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        uint16_t h0, l0, h1, l1;
-        split_bf16(qp[j] * scale, h0, l0);
-        split_bf16(qp[j + 1] * scale, h1, l1);
-        hh[j / 2] = h0 | ((uint32_t)h1 << 16);
-        ll[j / 2] = l0 | ((uint32_t)l1 << 16);
-      }
+      for (int j = 0; j < 8; ++j) qv[j] = qp[j] * scale;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qv[j] = 0.f;
     }
-    qh[kt] = make_uint4(hh[0], hh[1], hh[2], hh[3]);
-    ql[kt] = make_uint4(ll[0], ll[1], ll[2], ll[3]);
+    split3_pack8(qv, qs[0][kt], qs[1][kt], qs[2][kt]);
   }
   const int last_pos = pos0 + n_q - 1;
   const int n_kpages = (last_pos >> 4) + 1;
@@ -319,8 +320,9 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
           const uint4 kk = kp[kt * 4];  // dims 32kt + 8g .. +7 of key c
-          st = mfma16(kk, qh[kt], st);
-          st = mfma16(kk, ql[kt], st);
+          st = mfma16(kk, qs[2][kt], st);  // smallest parts first
+          st = mfma16(kk, qs[1][kt], st);
+          st = mfma16(kk, qs[0][kt], st);
         }
         const uint16_t *vp = pool_v + ((size_t)pg * n_heads + h) * D * 16 + g * 4;
         // keys after the block's last query are not written yet (possibly NaN): clear their values
@@ -365,22 +367,14 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
 #pragma unroll
       for (int e = 0; e < 4; ++e) oacc[i][e] *= alpha;
     // P^T operand: slots 8g+e -> key 4g+e of page pa (e < 4) or of page pa+1 (e >= 4)
-    uint32_t ph[4], pl[4];
-#pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      uint16_t h0, l0, h1, l1;
-      split_bf16(pr[j], h0, l0);
-      split_bf16(pr[j + 1], h1, l1);
-      ph[j / 2] = h0 | ((uint32_t)h1 << 16);
-      pl[j / 2] = l0 | ((uint32_t)l1 << 16);
-    }
-    const uint4 phv = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-    const uint4 plv = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+    uint4 ps[3];
+    split3_pack8(pr, ps[0], ps[1], ps[2]);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const uint4 va = make_uint4(vt[db][0].x, vt[db][0].y, vt[db][1].x, vt[db][1].y);
-      oacc[db] = mfma16(va, phv, oacc[db]);
-      oacc[db] = mfma16(va, plv, oacc[db]);
+      oacc[db] = mfma16(va, ps[2], oacc[db]);
+      oacc[db] = mfma16(va, ps[1], oacc[db]);
+      oacc[db] = mfma16(va, ps[0], oacc[db]);
     }
   }
   l += __shfl_xor(l, 16, 64);
@@ -397,8 +391,8 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
 
 void launch_prefill_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, int n_tokens, int max_q_len,
                               const int32_t *cu, const int32_t *start_pos, const int32_t *block_tables, int max_pages,
-                              const uint16_t *pk, const uint16_t *pv, int num_pages, float *out_f32, uint16_t *out_hi,
-                              uint16_t *out_lo, int kpad, uint32_t *err, hipStream_t s) {
+                              const uint16_t *pk, const uint16_t *pv, int num_pages, float *out_f32, uint16_t *out_hi, uint16_t *out_lo,
+                              int kpad, uint32_t *err, hipStream_t s) {
   if (n_seqs <= 0 || max_q_len <= 0) return;
   dim3 grid((max_q_len + 15) / 16, cfg.n_heads, n_seqs);
   if (cfg.head_dim == 128)

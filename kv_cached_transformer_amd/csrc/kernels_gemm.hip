@@ -1,18 +1,38 @@
-// Weight-streaming linear layers: out[m][n] (+)= sum_k a[m][k] * W[n][k].
+// Weight products: out[m][n] = sum_k a[m][k] * W[n][k] on the matrix cores
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
 //
-// W is bf16 in the packed tile layout (see packed_offset): each 16-row block
-// is a run of 1 KiB tiles along k, so a wave streaming one block reads
-// contiguous memory.  Three shapes:
-//   * rows == 1 (batch-1 decode): a VALU GEMV with the activation kept in
-//     fp32; HBM-bound on the weight stream.
-//   * rows <= 64 (batched decode, short prompts): MFMA 16x16x32 bf16 with the
-//     activation split into hi/lo bf16 halves (two MFMAs per tile), weights
-//     read once; split over k across the waves of a block and, for narrow
-//     matrices, across blocks (partials reduced by a second kernel).
-//   * rows > 64 (prefill): MFMA tiles of 128 x 128 per block.
-// The hi/lo split keeps the activation at ~16 significant bits: plain bf16
-// activations put the layer output about 3x outside a 2e-2 max-abs bound at
-// 7B sizes, while hi/lo stays about 5x inside it.
+// The activation enters as a bf16 pair a = hi + lo (hi = bf16(a), lo =
+// bf16(a - hi), about 17 significant bits), so every product is two MFMAs,
+// hi * W + lo * W.  A single bf16 rounding of the activation would put the
+// 7B-layer output outside a 2e-2 max-abs bound against an unrounded
+// reference: a chain of four such roundings per layer turns any relative
+// difference e into an output difference of order sqrt(512 e) * 2^-9 at each
+// stage.  The pair keeps the weight product within fp32-level agreement.
+//
+// Both operands are in the packed tile layout (see packed_offset): a 16-row x
+// 32-column tile is 1 KiB, and lane l of a wave holds row l%16, columns
+// 8(l/16)..+7 -- exactly one MFMA operand.  Activations are packed the same
+// way by their producers (RMSNorm, attention, the SwiGLU epilogue), so every
+// operand fetch is one contiguous 16-byte load per lane.
+//
+// Two kernels:
+//   * stream_gemm (rows <= 64, decode): the weight matrix is read once from
+//     HBM and that read bounds the kernel.  A block owns 64 output columns
+//     (4 row blocks of W); its 4 waves take interleaved k-tiles of the block's
+//     k-range and keep a ring of SG_DEPTH k-tiles of weights in flight (16 KiB
+//     per wave).  Wave sums meet in LDS.  Narrow matrices also split k across
+//     blocks: each block then stores its fp32 partial sums and the caller adds
+//     them (launch_reduce, or the next kernel that reads the result anyway).
+//   * tiled_gemm (rows > 64, prefill): 128 x 128 output tile per block, one
+//     32-wide k-tile per LDS stage (A hi, A lo, W: 24 tiles, 24 KiB), two
+//     stages; 4 waves in 2 x 2, each 64 x 64 = 4 x 4 MFMA blocks.  Tiles are
+//     handed to the 8 XCDs in contiguous runs, row tiles innermost, so a
+//     weight tile is fetched into one XCD's L2 and reused by every row tile.
+//
+// Epilogues: store fp32; add into fp32 (the residual stream); SwiGLU, where
+// W's row blocks alternate gate / up (block 2j: gate rows 16j.., block 2j+1:
+// up rows 16j..) and the kernel writes silu(g) * u straight into the packed
+// hi/lo activation of the down projection.
 #include "common.h"
 #include "internal.h"
 
@@ -25,237 +45,334 @@ __device__ inline f32x4 mfma16(const uint4 &a, const uint4 &b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
 }
 
-__device__ inline float dot8(const uint4 &w, const float *x) {
-  float s = bf16lo(w.x) * x[0];
-  s = fmaf(bf16hi(w.x), x[1], s);
-  s = fmaf(bf16lo(w.y), x[2], s);
-  s = fmaf(bf16hi(w.y), x[3], s);
-  s = fmaf(bf16lo(w.z), x[4], s);
-  s = fmaf(bf16hi(w.z), x[5], s);
-  s = fmaf(bf16lo(w.w), x[6], s);
-  s = fmaf(bf16hi(w.w), x[7], s);
-  return s;
-}
+__device__ inline float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
-// ---------------------------------------------------------------- GEMV (rows == 1)
-// Block = one 16-row block of W, GEMV_WAVES waves splitting its tiles.  The
-// fp32 activation is staged in LDS; lane l of a wave multiplies its 8 weights
-// of row l%16 by x[32kt + 8(l/16) .. +7].
-constexpr int GEMV_WAVES = 8;
-constexpr int GEMV_UNROLL = 8;
-
-__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_kernel(const float *__restrict__ x, int k, int kt_count,
-                                                               const uint4 *__restrict__ w, float *__restrict__ out,
-                                                               int epi) {
-  extern __shared__ float smem[];
-  float *xs = smem;                          // [kt_count * 32]
-  float *red = smem + kt_count * 32;         // [GEMV_WAVES][16]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < kt_count * 32; i += 64 * GEMV_WAVES) xs[i] = i < k ? x[i] : 0.f;
-  __syncthreads();
-  const uint4 *wb = w + (size_t)blockIdx.x * kt_count * 64 + lane;
-  const float *xl = xs + (lane >> 4) * 8;
-  float acc = 0.f;
-  int kt = wave;
-  for (; kt + (GEMV_UNROLL - 1) * GEMV_WAVES < kt_count; kt += GEMV_UNROLL * GEMV_WAVES) {
-    uint4 t[GEMV_UNROLL];
-#pragma unroll
-    for (int u = 0; u < GEMV_UNROLL; ++u) t[u] = load_stream(wb + (size_t)(kt + u * GEMV_WAVES) * 64);
-#pragma unroll
-    for (int u = 0; u < GEMV_UNROLL; ++u) acc += dot8(t[u], xl + (kt + u * GEMV_WAVES) * 32);
-  }
-  for (; kt < kt_count; kt += GEMV_WAVES) acc += dot8(load_stream(wb + (size_t)kt * 64), xl + kt * 32);
-  acc += __shfl_xor(acc, 16, 64);
-  acc += __shfl_xor(acc, 32, 64);
-  if (lane < 16) red[wave * 16 + lane] = acc;
-  __syncthreads();
-  if (tid < 16) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < GEMV_WAVES; ++i) s += red[i * 16 + tid];
-    float *o = out + (size_t)blockIdx.x * 16 + tid;
-    *o = epi == kAccumulate ? *o + s : s;
-  }
-}
-
-// ---------------------------------------------------------------- skinny MFMA (rows <= 64)
-// Block = 64 output columns (4 row-blocks of W) x one k-range; its 4 waves
-// interleave over the k-tiles of that range, each wave holding all MB x 4
-// accumulators; the waves are summed through LDS.  With ksplit > 1 the
-// block writes a partial sum and reduce_kernel applies the epilogue.
-template <int MB>
-__global__ __launch_bounds__(256) void skinny_kernel(const uint4 *__restrict__ a_hi, const uint4 *__restrict__ a_lo,
-                                                     int a_kt, int rows, const uint4 *__restrict__ w, int kt_count,
-                                                     int n, float *__restrict__ out, int ld_out, int epi,
-                                                     float *__restrict__ partials) {
-  __shared__ float red[3][MB * 16][64 + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 64;  // first output column
-  const int ks = blockIdx.y, nks = gridDim.y;
-  const int kt0 = (int)((long)kt_count * ks / nks), kt1 = (int)((long)kt_count * (ks + 1) / nks);
-  f32x4 acc[MB][4];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nb0 = n0 >> 4;
-  const int nbs = min(4, (n - n0) >> 4);
-  for (int kt = kt0 + wave; kt < kt1; kt += 4) {
-    uint4 wt[4], ah[MB], al[MB];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      wt[j] = j < nbs ? load_stream(w + ((size_t)(nb0 + j) * kt_count + kt) * 64 + lane) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      ah[i] = a_hi[((size_t)i * a_kt + kt) * 64 + lane];
-      al[i] = a_lo[((size_t)i * a_kt + kt) * 64 + lane];
+// One output element through the epilogue.  c is the column of the product;
+// for kSiluMul only gate columns call this, with u the matching up value.
+__device__ inline void epi_store(const LinearOut &o, int r, int c, float v, float u) {
+  if (o.kind == kSiluMul) {
+    const int j = ((c >> 5) << 4) | (c & 15);  // gate column -> activation column
+    uint16_t h, l;
+    split_bf16(silu_f(v) * u, h, l);
+    const size_t off = packed_offset(r, j, o.act_kt);
+    o.act_hi[off] = h;
+    o.act_lo[off] = l;
+    // the row's padding columns (act_cols .. 32*act_kt-1, fewer than 16 since act_cols % 16 == 0)
+    // follow the last real 16-column block, whose writers clear them
+    if (j + 16 >= o.act_cols && j + 16 < o.act_kt * 32) {
+      const size_t pad = packed_offset(r, j + 16, o.act_kt);
+      o.act_hi[pad] = 0;
+      o.act_lo[pad] = 0;
     }
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[i][j] = mfma16(ah[i], wt[j], acc[i][j]);
-        acc[i][j] = mfma16(al[i], wt[j], acc[i][j]);
-      }
+  } else {
+    float *p = o.f32 + (size_t)r * o.ld + c;
+    *p = o.kind == kAccumulate ? *p + v : v;
   }
-  // C layout: lane l, element e holds row 4*(l/16)+e, column l%16 of each 16x16 block.
+}
+
+// ---------------------------------------------------------------- stream_gemm (rows <= 64)
+constexpr int SG_NB = 4;     // W row blocks per block: 64 output columns
+constexpr int SG_DEPTH = 4;  // k-tiles of weights in flight per wave
+
+template <int MB>
+__global__ __launch_bounds__(256) void stream_gemm_kernel(const uint4 *__restrict__ a_hi,
+                                                          const uint4 *__restrict__ a_lo, int a_kt, int rows,
+                                                          const uint4 *__restrict__ w, int kt_count, int n_blocks,
+                                                          LinearOut o, float *__restrict__ partials) {
+  __shared__ float red[3][MB * 16][SG_NB * 16 + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = blockIdx.x, split = blockIdx.y, ks = gridDim.y;
+  const int nb0 = g * SG_NB;
+  const int nbs = min(SG_NB, n_blocks - nb0);
+  const int kt0 = (int)((long)kt_count * split / ks), kt1 = (int)((long)kt_count * (split + 1) / ks);
+  const int n_it = kt1 - kt0 > wave ? (kt1 - kt0 - wave + 3) >> 2 : 0;  // k-tiles kt0 + wave + 4i
+
+  f32x4 acc[MB][SG_NB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int j = 0; j < SG_NB; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint4 *wl = w + (size_t)nb0 * kt_count * 64 + lane;  // row block nb0, tile 0, this lane
+  uint4 wb[SG_DEPTH][SG_NB];
+#pragma unroll
+  for (int d = 0; d < SG_DEPTH; ++d)
+#pragma unroll
+    for (int j = 0; j < SG_NB; ++j)
+      wb[d][j] = (d < n_it && j < nbs) ? load_stream(wl + ((size_t)j * kt_count + kt0 + wave + 4 * d) * 64)
+                                       : make_uint4(0, 0, 0, 0);
+  for (int it = 0; it < n_it; it += SG_DEPTH) {
+#pragma unroll
+    for (int d = 0; d < SG_DEPTH; ++d) {
+      const int i = it + d;
+      if (i < n_it) {
+        const int kt = kt0 + wave + 4 * i;
+        uint4 ah[MB], al[MB];
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          ah[m] = a_hi[((size_t)m * a_kt + kt) * 64 + lane];
+          al[m] = a_lo[((size_t)m * a_kt + kt) * 64 + lane];
+        }
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+          for (int j = 0; j < SG_NB; ++j) {
+            acc[m][j] = mfma16(al[m], wb[d][j], acc[m][j]);
+            acc[m][j] = mfma16(ah[m], wb[d][j], acc[m][j]);
+          }
+        const int i2 = i + SG_DEPTH;
+        if (i2 < n_it) {
+          const int kt2 = kt0 + wave + 4 * i2;
+#pragma unroll
+          for (int j = 0; j < SG_NB; ++j)
+            if (j < nbs) wb[d][j] = load_stream(wl + ((size_t)j * kt_count + kt2) * 64);
+        }
+      }
+    }
+  }
+  // accumulator layout: lane l, element e -> row 4(l/16)+e, column l%16 of each 16 x 16 block
+  const int rq = (lane >> 4) * 4, cq = lane & 15;
   if (wave > 0) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < SG_NB; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[wave - 1][i * 16 + (lane >> 4) * 4 + e][j * 16 + (lane & 15)] = acc[i][j][e];
+        for (int e = 0; e < 4; ++e) red[wave - 1][m * 16 + rq + e][j * 16 + cq] = acc[m][j][e];
   }
   __syncthreads();
-  if (wave == 0) {
+  if (wave != 0) return;
+  const int n = n_blocks * 16;
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+  for (int m = 0; m < MB; ++m)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < SG_NB; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = i * 16 + (lane >> 4) * 4 + e, c = j * 16 + (lane & 15);
-          const float v = acc[i][j][e] + red[0][r][c] + red[1][r][c] + red[2][r][c];
-          if (r < rows && j < nbs) {
-            if (partials) {
-              partials[((size_t)ks * rows + r) * n + n0 + c] = v;
-            } else {
-              float *o = out + (size_t)r * ld_out + n0 + c;
-              *o = epi == kAccumulate ? *o + v : v;
-            }
-          }
+      for (int e = 0; e < 4; ++e) {
+        const int r = m * 16 + rq + e, c = j * 16 + cq;
+        const float v = acc[m][j][e] + red[0][r][c] + red[1][r][c] + red[2][r][c];
+        acc[m][j][e] = v;
+        if (ks > 1 && r < rows && j < nbs) partials[((size_t)split * rows + r) * n + (nb0 + j) * 16 + cq] = v;
+      }
+  if (ks > 1) return;
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int j = 0; j < SG_NB; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = m * 16 + rq + e, c = (nb0 + j) * 16 + cq;
+        if (r >= rows || j >= nbs) continue;
+        if (o.kind == kSiluMul) {
+          if ((j & 1) == 0) epi_store(o, r, c, acc[m][j][e], acc[m][j + 1][e]);
+        } else {
+          epi_store(o, r, c, acc[m][j][e], 0.f);
         }
-  }
+      }
 }
 
-__global__ void reduce_kernel(const float *__restrict__ partials, int ksplit, int rows, int n, float *__restrict__ out,
-                              int ld_out, int epi) {
+// ---------------------------------------------------------------- split-k reduction
+// One thread per (row, 4 consecutive columns): sums the ks partials in split
+// order (deterministic) and applies the epilogue.  For SwiGLU the threads of
+// gate columns also read the matching up columns (16 further on).
+__global__ void reduce_kernel(const float *__restrict__ partials, int ks, int rows, int n, LinearOut o) {
+  const int n4 = n >> 2;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (size_t)rows * n) return;
-  const int r = (int)(idx / n), c = (int)(idx % n);
-  float s = 0.f;
-  for (int k = 0; k < ksplit; ++k) s += partials[((size_t)k * rows + r) * n + c];
-  float *o = out + (size_t)r * ld_out + c;
-  *o = epi == kAccumulate ? *o + s : s;
+  if (idx >= (size_t)rows * n4) return;
+  const int r = (int)(idx / n4), c = (int)(idx % n4) * 4;
+  if (o.kind == kSiluMul && ((c >> 4) & 1)) return;
+  const size_t plane = (size_t)rows * n;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f), u = s;
+  for (int q = 0; q < ks; ++q) {
+    const float4 v = *reinterpret_cast<const float4 *>(partials + q * plane + (size_t)r * n + c);
+    s.x += v.x, s.y += v.y, s.z += v.z, s.w += v.w;
+    if (o.kind == kSiluMul) {
+      const float4 w = *reinterpret_cast<const float4 *>(partials + q * plane + (size_t)r * n + c + 16);
+      u.x += w.x, u.y += w.y, u.z += w.z, u.w += w.w;
+    }
+  }
+  epi_store(o, r, c, s.x, u.x);
+  epi_store(o, r, c + 1, s.y, u.y);
+  epi_store(o, r, c + 2, s.z, u.z);
+  epi_store(o, r, c + 3, s.w, u.w);
 }
 
-// ---------------------------------------------------------------- tiled MFMA (rows > 64)
-// Block = 128 x 128 outputs, 4 waves in 2 x 2, each wave 64 x 64 (4 x 4 MFMA blocks).
-__global__ __launch_bounds__(256) void tiled_kernel(const uint4 *__restrict__ a_hi, const uint4 *__restrict__ a_lo,
-                                                    int a_kt, int rows, const uint4 *__restrict__ w, int kt_count,
-                                                    int n, float *__restrict__ out, int ld_out, int epi) {
+void launch_reduce(const float *partials, int ks, int rows, int n, const LinearOut &o, hipStream_t s) {
+  const size_t total = (size_t)rows * (n / 4);
+  if (total) reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(partials, ks, rows, n, o);
+}
+
+// ---------------------------------------------------------------- tiled_gemm (rows > 64)
+constexpr int TG_MB = 8;                               // 16-row blocks of A per block (128 rows)
+constexpr int TG_NB = 8;                               // 16-row blocks of W per block (128 columns)
+constexpr int TG_STAGE_TILES = TG_MB * 2 + TG_NB;      // A hi, A lo, W tiles of one k-tile: 24 KiB
+constexpr size_t TG_LDS = (size_t)2 * TG_STAGE_TILES * 1024;
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Global source of tile q (0..23) of k-tile kt, or NULL when it lies outside the operands.
+__device__ inline const uint4 *tg_src(int q, int kt, int mb0, int nb0, int a_blocks, int n_blocks, int a_kt,
+                                      int kt_count, const uint4 *a_hi, const uint4 *a_lo, const uint4 *w) {
+  if (q < TG_MB) {
+    const int rb = mb0 + q;
+    return rb < a_blocks ? a_hi + ((size_t)rb * a_kt + kt) * 64 : nullptr;
+  }
+  if (q < 2 * TG_MB) {
+    const int rb = mb0 + q - TG_MB;
+    return rb < a_blocks ? a_lo + ((size_t)rb * a_kt + kt) * 64 : nullptr;
+  }
+  const int nb = nb0 + q - 2 * TG_MB;
+  return nb < n_blocks ? w + ((size_t)nb * kt_count + kt) * 64 : nullptr;
+}
+
+template <bool DIRECT>
+__global__ __launch_bounds__(256) void tiled_gemm_kernel(const uint4 *__restrict__ a_hi,
+                                                         const uint4 *__restrict__ a_lo, int a_kt, int a_blocks,
+                                                         int rows, const uint4 *__restrict__ w, int kt_count,
+                                                         int n_blocks, int tiles_m, LinearOut o) {
+  extern __shared__ uint4 lds[];  // [2 stages][24 tiles][64 lanes]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int mb0 = blockIdx.y * 8 + (wave >> 1) * 4;  // first 16-row block of activations
-  const int nb0 = blockIdx.x * 8 + (wave & 1) * 4;   // first 16-row block of W
-  const int m_blocks = (rows + 15) >> 4, n_blocks = n >> 4;
+  // XCD-aware order: block b runs on XCD b % 8; each XCD gets a contiguous run of tiles, row tiles innermost
+  const int nblk = gridDim.x;
+  int t = blockIdx.x;
+  if ((nblk & 7) == 0) t = (t & 7) * (nblk >> 3) + (t >> 3);
+  const int tm = t % tiles_m, tn = t / tiles_m;
+  const int mb0 = tm * TG_MB, nb0 = tn * TG_NB;
+  constexpr int PER_WAVE = TG_STAGE_TILES / 4;  // 6 tiles per wave per stage
+
+  uint4 stage_regs[PER_WAVE];
+  auto fetch = [&](int kt) {  // global -> registers (staged variant)
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const uint4 *src = tg_src(wave + 4 * i, kt, mb0, nb0, a_blocks, n_blocks, a_kt, kt_count, a_hi, a_lo, w);
+      stage_regs[i] = src ? src[lane] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store = [&](int buf) {  // registers -> LDS
+    uint4 *base = lds + (size_t)buf * TG_STAGE_TILES * 64;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) base[(size_t)(wave + 4 * i) * 64 + lane] = stage_regs[i];
+  };
+  auto direct = [&](int kt, int buf) {  // global -> LDS without registers
+    uint4 *base = lds + (size_t)buf * TG_STAGE_TILES * 64;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int q = wave + 4 * i;
+      const uint4 *src = tg_src(q, kt, mb0, nb0, a_blocks, n_blocks, a_kt, kt_count, a_hi, a_lo, w);
+      if (src)
+        __builtin_amdgcn_global_load_lds((const void *)(src + lane), (lds_ptr_t)(base + (size_t)q * 64), 16, 0, 0);
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;  // wave owns A row blocks wm*4.. and W row blocks wn*4..
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (DIRECT) {
+    direct(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+  } else {
+    fetch(0);
+    store(0);
+  }
+  __syncthreads();
+  int buf = 0;
   for (int kt = 0; kt < kt_count; ++kt) {
-    uint4 wt[4], ah[4], al[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      wt[j] = (nb0 + j < n_blocks) ? w[((size_t)(nb0 + j) * kt_count + kt) * 64 + lane] : make_uint4(0, 0, 0, 0);
+    const bool more = kt + 1 < kt_count;
+    if (more) {
+      if (DIRECT) direct(kt + 1, buf ^ 1);
+      else fetch(kt + 1);
+    }
+    const uint4 *st = lds + (size_t)buf * TG_STAGE_TILES * 64;
+    uint4 ah[4], al[4], bv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = mb0 + i < m_blocks;
-      ah[i] = ok ? a_hi[((size_t)(mb0 + i) * a_kt + kt) * 64 + lane] : make_uint4(0, 0, 0, 0);
-      al[i] = ok ? a_lo[((size_t)(mb0 + i) * a_kt + kt) * 64 + lane] : make_uint4(0, 0, 0, 0);
+      ah[i] = st[(size_t)(wm * 4 + i) * 64 + lane];
+      al[i] = st[(size_t)(TG_MB + wm * 4 + i) * 64 + lane];
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[j] = st[(size_t)(2 * TG_MB + wn * 4 + j) * 64 + lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc[i][j] = mfma16(ah[i], wt[j], acc[i][j]);
-        acc[i][j] = mfma16(al[i], wt[j], acc[i][j]);
+        acc[i][j] = mfma16(al[i], bv[j], acc[i][j]);
+        acc[i][j] = mfma16(ah[i], bv[j], acc[i][j]);
       }
+    if (more) {
+      if (DIRECT) __builtin_amdgcn_s_waitcnt(0);
+      else store(buf ^ 1);
+    }
+    __syncthreads();
+    buf ^= 1;
   }
+
+  const int rq = (lane >> 4) * 4, cq = lane & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      const int nb = nb0 + wn * 4 + j;
+      if (nb >= n_blocks) continue;
+      if (o.kind == kSiluMul && (j & 1)) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = (mb0 + i) * 16 + (lane >> 4) * 4 + e, c = (nb0 + j) * 16 + (lane & 15);
-        if (r < rows && nb0 + j < n_blocks) {
-          float *o = out + (size_t)r * ld_out + c;
-          *o = epi == kAccumulate ? *o + acc[i][j][e] : acc[i][j][e];
-        }
+        const int r = (mb0 + wm * 4 + i) * 16 + rq + e;
+        if (r < rows) epi_store(o, r, nb * 16 + cq, acc[i][j][e], o.kind == kSiluMul ? acc[i][j + 1][e] : 0.f);
       }
+    }
 }
 
 // ---------------------------------------------------------------- dispatch
-static int skinny_ksplit(int n, int kt_count) {
-  const int col_blocks = (n + 63) / 64;
+// Splits of k across blocks for the streaming kernel: enough blocks to keep
+// every CU streaming, while the partial sums (written once and read back
+// once) stay at most a quarter of the weight bytes and every wave keeps at
+// least four k-tiles to pipeline.
+int stream_ksplit(int rows, int n, int k) {
+  const int groups = (n / 16 + SG_NB - 1) / SG_NB;
+  const int kt = round_up(k, kTileK) / kTileK;
   int ks = 1;
-  while (col_blocks * ks < 512 && kt_count / (ks * 2) >= 8) ks *= 2;
+  while (groups * ks < 512 && kt / (ks * 2) >= 16 && (long)(ks * 2) * rows * 16 <= (long)k) ks *= 2;
   return ks;
 }
 
 size_t linear_partial_floats(int rows, int n, int k) {
-  if (rows <= 1 || rows > 64) return 0;
-  const int ks = skinny_ksplit(n, round_up(k, kTileK) / kTileK);
+  if (rows > 64) return 0;
+  const int ks = stream_ksplit(rows, n, k);
   return ks > 1 ? (size_t)ks * rows * n : 0;
 }
 
-void launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, float *out, int ld_out, Epilogue epi,
-                   float *partials, size_t partial_floats, hipStream_t s) {
+#ifndef LLMDEC_TILED_DIRECT
+#define LLMDEC_TILED_DIRECT 0
+#endif
+
+int launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const LinearOut &o, float *partials,
+                  size_t partial_floats, bool allow_split, hipStream_t s) {
   const int kt_count = round_up(k, kTileK) / kTileK;
+  const int n_blocks = n / 16;
   const uint4 *w = reinterpret_cast<const uint4 *>(w_packed);
-  if (a.rows == 1 && a.f32) {
-    static bool lds_raised = false;  // allow K up to 16384 (64 KiB of fp32 activation in LDS)
-    if (!lds_raised) {
-      (void)hipFuncSetAttribute((const void *)gemv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-      lds_raised = true;
-    }
-    const size_t lds = ((size_t)kt_count * 32 + GEMV_WAVES * 16) * sizeof(float);
-    gemv_kernel<<<n / 16, 64 * GEMV_WAVES, lds, s>>>(a.f32, k, kt_count, w, out, epi);
-    return;
-  }
   const uint4 *ah = reinterpret_cast<const uint4 *>(a.hi), *al = reinterpret_cast<const uint4 *>(a.lo);
   const int a_kt = a.kpad / kTileK;
   if (a.rows <= 64) {
-    int ks = skinny_ksplit(n, kt_count);
+    int ks = allow_split ? stream_ksplit(a.rows, n, k) : 1;
     if (ks > 1 && (!partials || partial_floats < (size_t)ks * a.rows * n)) ks = 1;
-    dim3 grid((n + 63) / 64, ks);
-    float *p = ks > 1 ? partials : nullptr;
+    dim3 grid((n_blocks + SG_NB - 1) / SG_NB, ks);
     switch ((a.rows + 15) / 16) {
-      case 1: skinny_kernel<1><<<grid, 256, 0, s>>>(ah, al, a_kt, a.rows, w, kt_count, n, out, ld_out, epi, p); break;
-      case 2: skinny_kernel<2><<<grid, 256, 0, s>>>(ah, al, a_kt, a.rows, w, kt_count, n, out, ld_out, epi, p); break;
-      case 3: skinny_kernel<3><<<grid, 256, 0, s>>>(ah, al, a_kt, a.rows, w, kt_count, n, out, ld_out, epi, p); break;
-      default: skinny_kernel<4><<<grid, 256, 0, s>>>(ah, al, a_kt, a.rows, w, kt_count, n, out, ld_out, epi, p); break;
+      case 1: stream_gemm_kernel<1><<<grid, 256, 0, s>>>(ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
+      case 2: stream_gemm_kernel<2><<<grid, 256, 0, s>>>(ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
+      case 3: stream_gemm_kernel<3><<<grid, 256, 0, s>>>(ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
+      default: stream_gemm_kernel<4><<<grid, 256, 0, s>>>(ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
     }
-    if (ks > 1) {
-      const size_t total = (size_t)a.rows * n;
-      reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(partials, ks, a.rows, n, out, ld_out, epi);
-    }
-    return;
+    return ks;
   }
-  dim3 grid((n + 127) / 128, (a.rows + 127) / 128);
-  tiled_kernel<<<grid, 256, 0, s>>>(ah, al, a_kt, a.rows, w, kt_count, n, out, ld_out, epi);
+  const int tiles_m = (a.rows + TG_MB * 16 - 1) / (TG_MB * 16);
+  const int tiles_n = (n_blocks + TG_NB - 1) / TG_NB;
+  tiled_gemm_kernel<LLMDEC_TILED_DIRECT><<<tiles_m * tiles_n, 256, TG_LDS, s>>>(ah, al, a_kt, a.row_blocks, a.rows, w,
+                                                                               kt_count, n_blocks, tiles_m, o);
+  return 1;
 }
 
 }  // namespace llmdec

@@ -1,5 +1,5 @@
 // Small bandwidth-bound kernels: weight packing, embedding lookup, RMSNorm,
-// activation splitting, rotary embedding + paged KV append, SwiGLU gate,
+// fp32 -> packed hi/lo pair, rotary embedding + paged KV append, SwiGLU gate,
 // argmax, and the test-only cache gather.
 #include <math.h>
 
@@ -56,37 +56,55 @@ void launch_embed(const uint16_t *embed, const int32_t *tokens, int n_tokens, in
   if (n_tokens > 0) embed_kernel<<<n_tokens, 256, 0, s>>>(embed, tokens, hidden, vocab, x, err);
 }
 
-// ---------------------------------------------------------------- split writer
-// Writes value v of activation (r, c) to the f32 and/or tiled hi/lo outputs.
-__device__ inline void store_act(float v, int r, int c, int n, float *out_f32, uint16_t *hi, uint16_t *lo, int kpad) {
-  if (out_f32) out_f32[(size_t)r * n + c] = v;
-  if (hi) {
-    uint16_t h, l;
-    split_bf16(v, h, l);
-    const size_t o = packed_offset(r, c, kpad >> 5);
-    hi[o] = h;
-    lo[o] = l;
-  }
-}
-
 // ---------------------------------------------------------------- RMSNorm ([E] §4.2)
-// y = x * (mean(x^2) + eps)^(-1/2) * gamma, eps inside the root.  One block per row.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ x, int ld_x,
+// y = x * (mean(x^2) + eps)^(-1/2) * gamma, eps inside the root.  One block
+// per row; each thread owns runs of 8 consecutive columns (up to four runs:
+// n <= 8192), kept in registers between the two passes, and each run is one
+// 16-byte chunk of the packed hi/lo output.  Columns n..kpad-1 of the packed
+// output are zeroed.  With add_partials, the ks partial sums of a split-k
+// residual product are first added into x (and x written back): the residual
+// add of the output projection fused into the norm that follows it.
+constexpr int kNormRuns = 4;
+
+__global__ __launch_bounds__(256) void rmsnorm_kernel(float *__restrict__ x, int ld_x,
                                                       const int32_t *__restrict__ cu_last, int n_src_rows,
                                                       const uint16_t *__restrict__ gamma, int n, float eps,
                                                       uint32_t *err, float *out_f32, uint16_t *out_hi,
-                                                      uint16_t *out_lo, int kpad) {
+                                                      uint16_t *out_lo, int kpad, const float *__restrict__ add,
+                                                      int ks, int rows) {
   const int r = blockIdx.x;
   int src_row = cu_last ? cu_last[r + 1] - 1 : r;
   if (src_row < 0 || src_row >= n_src_rows) {  // a bad cu_seqlens entry: flag it, read row 0 instead
     if (threadIdx.x == 0) raise_error(err, kErrSeq);
     src_row = 0;
   }
-  const float *xr = x + (size_t)src_row * ld_x;
+  float *xr = x + (size_t)src_row * ld_x;
+  float xv[kNormRuns][8];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const float v = xr[i];
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int it = 0; it < kNormRuns; ++it) {
+    const int c0 = threadIdx.x * 8 + it * 2048;
+    if (c0 < n) {
+      const float4 v0 = *reinterpret_cast<const float4 *>(xr + c0);
+      const float4 v1 = *reinterpret_cast<const float4 *>(xr + c0 + 4);
+      float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      if (add) {
+        for (int q = 0; q < ks; ++q) {
+          const float *p = add + ((size_t)q * rows + r) * n + c0;
+          const float4 p0 = *reinterpret_cast<const float4 *>(p);
+          const float4 p1 = *reinterpret_cast<const float4 *>(p + 4);
+          v[0] += p0.x, v[1] += p0.y, v[2] += p0.z, v[3] += p0.w;
+          v[4] += p1.x, v[5] += p1.y, v[6] += p1.z, v[7] += p1.w;
+        }
+        *reinterpret_cast<float4 *>(xr + c0) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4 *>(xr + c0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xv[it][j] = v[j];
+        ss = fmaf(v[j], v[j], ss);
+      }
+    }
   }
   __shared__ float red[4];
   ss = wave_sum(ss);
@@ -94,42 +112,62 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ 
   __syncthreads();
   const float total = (red[0] + red[1]) + (red[2] + red[3]);
   const float inv = 1.0f / sqrtf(total / (float)n + eps);
-  for (int i = threadIdx.x; i < n; i += 256) store_act(xr[i] * inv * bf16_to_f32(gamma[i]), r, i, n, out_f32, out_hi, out_lo, kpad);
-  if (out_hi)
-    for (int i = n + threadIdx.x; i < kpad; i += 256) {
-      const size_t o = packed_offset(r, i, kpad >> 5);
-      out_hi[o] = 0;
-      out_lo[o] = 0;
+  const int kt = kpad >> 5;
+#pragma unroll
+  for (int it = 0; it < kNormRuns; ++it) {
+    const int c0 = threadIdx.x * 8 + it * 2048;
+    if (c0 >= (out_hi ? kpad : n)) continue;
+    float y[8];
+    if (c0 < n) {
+      const uint4 gw = *reinterpret_cast<const uint4 *>(gamma + c0);
+      const uint32_t gg[4] = {gw.x, gw.y, gw.z, gw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[2 * j] = xv[it][2 * j] * inv * bf16lo(gg[j]);
+        y[2 * j + 1] = xv[it][2 * j + 1] * inv * bf16hi(gg[j]);
+      }
+      if (out_f32) {
+        float *o = out_f32 + (size_t)r * n + c0;
+        *reinterpret_cast<float4 *>(o) = make_float4(y[0], y[1], y[2], y[3]);
+        *reinterpret_cast<float4 *>(o + 4) = make_float4(y[4], y[5], y[6], y[7]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = 0.f;
     }
+    if (out_hi) {
+      uint4 h, l;
+      split_pack8(y, h, l);
+      const size_t off = packed_offset(r, c0, kt);
+      *reinterpret_cast<uint4 *>(out_hi + off) = h;
+      *reinterpret_cast<uint4 *>(out_lo + off) = l;
+    }
+  }
 }
 
-void launch_rmsnorm(const float *x, int ld_x, const int32_t *cu_last, int n_src_rows, const uint16_t *gamma, int rows,
-                    int n, float eps, uint32_t *err, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad,
-                    hipStream_t s) {
+void launch_rmsnorm(float *x, int ld_x, const int32_t *cu_last, int n_src_rows, const uint16_t *gamma, int rows, int n,
+                    float eps, uint32_t *err, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad,
+                    const float *add_partials, int ks, hipStream_t s) {
   if (rows > 0)
     rmsnorm_kernel<<<rows, 256, 0, s>>>(x, ld_x, cu_last, n_src_rows, gamma, n, eps, err, out_f32, out_hi, out_lo,
-                                        kpad);
+                                        kpad, add_partials, ks, rows);
 }
 
-// ---------------------------------------------------------------- fp32 -> tiled hi/lo
+// ---------------------------------------------------------------- fp32 -> packed hi/lo pair
 __global__ void split_kernel(const float *__restrict__ a, int ld, int rows, int cols, uint16_t *hi, uint16_t *lo,
                              int kpad) {
   const size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int per_row = kpad / 8;
   if (g >= (size_t)rows * per_row) return;
   const int r = (int)(g / per_row), c0 = (int)(g % per_row) * 8;
-  uint32_t h[4], l[4];
+  float v[8];
 #pragma unroll
-  for (int j = 0; j < 8; j += 2) {
-    uint16_t h0 = 0, l0 = 0, h1 = 0, l1 = 0;
-    if (c0 + j < cols) split_bf16(a[(size_t)r * ld + c0 + j], h0, l0);
-    if (c0 + j + 1 < cols) split_bf16(a[(size_t)r * ld + c0 + j + 1], h1, l1);
-    h[j / 2] = h0 | ((uint32_t)h1 << 16);
-    l[j / 2] = l0 | ((uint32_t)l1 << 16);
-  }
+  for (int j = 0; j < 8; ++j) v[j] = c0 + j < cols ? a[(size_t)r * ld + c0 + j] : 0.f;
+  uint4 h, l;
+  split_pack8(v, h, l);
   const size_t o = packed_offset(r, c0, kpad >> 5);
-  *reinterpret_cast<uint4 *>(hi + o) = make_uint4(h[0], h[1], h[2], h[3]);
-  *reinterpret_cast<uint4 *>(lo + o) = make_uint4(l[0], l[1], l[2], l[3]);
+  *reinterpret_cast<uint4 *>(hi + o) = h;
+  *reinterpret_cast<uint4 *>(lo + o) = l;
 }
 
 void launch_split(const float *a, int ld, int rows, int cols, uint16_t *hi, uint16_t *lo, int kpad, hipStream_t s) {
@@ -162,13 +200,19 @@ void launch_token_map(const int32_t *cu, const int32_t *start, int n_seqs, int n
 }
 
 // ---------------------------------------------------------------- RoPE + paged append ([E] §4.3)
-// One block per new token.  Pair i of every head turns by pos * theta^(-2i/D);
-// the angle and its sine/cosine are formed in double so that they do not
-// depend on fp32 range reduction at positions in the thousands.  q is rotated
-// in place; rotated k and plain v are rounded to bf16 and written to the page
+// One block per new token.  Pair i of every head turns by pos * inv_freq[i],
+// inv_freq[i] = theta^(-2i/D) computed in double on the host; the angle is
+// formed and reduced to [-pi, pi] in double, then its sine and cosine taken
+// in fp32, so positions in the thousands lose no accuracy.  q is rotated in
+// place; rotated k and plain v are rounded to bf16 and written to the page
 // slot bt[seq][pos/16], offset pos%16 (K as [h][o][d], V as [h][d][o]).
-__global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qkv, int ld_qkv, int n_heads,
-                                                          int head_dim, float theta, int n_seqs,
+struct RopeFreq {
+  double inv_freq[64];
+};
+
+__global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qkv, const float *__restrict__ part,
+                                                          int ks, int ld_qkv, int n_tokens, int n_heads,
+                                                          int head_dim, RopeFreq fr, int n_seqs,
                                                           const int32_t *__restrict__ tok_seq,
                                                           const int32_t *__restrict__ tok_pos,
                                                           const int32_t *__restrict__ block_tables, int max_pages,
@@ -182,11 +226,12 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
   const int pos = tok_pos[t];
   if ((int)threadIdx.x < half) {
     const int i = threadIdx.x;
-    const double inv_freq = pow((double)theta, -2.0 * (double)i / (double)head_dim);
-    double sd, cd;
-    sincos((double)pos * inv_freq, &sd, &cd);
-    cs[i] = (float)cd;
-    sn[i] = (float)sd;
+    const double ang = (double)pos * fr.inv_freq[i];
+    const double red = fma(-6.283185307179586, rint(ang * 0.15915494309189535), ang);
+    float sf, cf;
+    sincosf((float)red, &sf, &cf);
+    cs[i] = cf;
+    sn[i] = sf;
   }
   __syncthreads();
   int page = -1;
@@ -203,59 +248,61 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
     }
   }
   float *q = qkv + (size_t)t * ld_qkv;
-  const float *k = q + hidden;
-  const float *v = q + 2 * hidden;
+  // the token's q|k|v row: from qkv, or the sum of the split-k partial products
+  auto row2 = [&](int col) -> float2 {
+    if (!part) return *reinterpret_cast<const float2 *>(q + col);
+    float2 acc = make_float2(0.f, 0.f);
+    for (int p = 0; p < ks; ++p) {
+      const float2 v = *reinterpret_cast<const float2 *>(part + ((size_t)p * n_tokens + t) * ld_qkv + col);
+      acc.x += v.x, acc.y += v.y;
+    }
+    return acc;
+  };
   for (int g = threadIdx.x; g < n_heads * half; g += 256) {
     const int h = g / half, i = g % half;
     const float c = cs[i], s = sn[i];
     const int d = h * head_dim + 2 * i;
-    const float q0 = q[d], q1 = q[d + 1];
-    q[d] = q0 * c - q1 * s;
-    q[d + 1] = q0 * s + q1 * c;
+    const float2 qq = row2(d);
+    *reinterpret_cast<float2 *>(q + d) = make_float2(qq.x * c - qq.y * s, qq.x * s + qq.y * c);
     if (page >= 0) {
-      const float k0 = k[d], k1 = k[d + 1];
-      const uint32_t kb = f32_to_bf16(k0 * c - k1 * s) | ((uint32_t)f32_to_bf16(k0 * s + k1 * c) << 16);
+      const float2 kk = row2(hidden + d);
+      const uint32_t kb = f32_to_bf16(kk.x * c - kk.y * s) | ((uint32_t)f32_to_bf16(kk.x * s + kk.y * c) << 16);
       const size_t kbase = (((size_t)page * n_heads + h) * 16 + off) * head_dim + 2 * i;
       *reinterpret_cast<uint32_t *>(pool_k + kbase) = kb;
+      const float2 vv = row2(2 * hidden + d);
       const size_t vbase = (((size_t)page * n_heads + h) * head_dim + 2 * i) * 16 + off;
-      pool_v[vbase] = f32_to_bf16(v[d]);
-      pool_v[vbase + 16] = f32_to_bf16(v[d + 1]);
+      pool_v[vbase] = f32_to_bf16(vv.x);
+      pool_v[vbase + 16] = f32_to_bf16(vv.y);
     }
   }
 }
 
-void launch_rope_append(const llmdec_config &cfg, float *qkv, int ld_qkv, int n_tokens, int n_seqs,
-                        const int32_t *tok_seq, const int32_t *tok_pos, const int32_t *block_tables, int max_pages,
-                        uint16_t *pool_k, uint16_t *pool_v, int num_pages, uint32_t *err, hipStream_t s) {
-  if (n_tokens > 0)
-    rope_append_kernel<<<n_tokens, 256, 0, s>>>(qkv, ld_qkv, cfg.n_heads, cfg.head_dim, cfg.rope_theta, n_seqs, tok_seq,
-                                                tok_pos, block_tables, max_pages, pool_k, pool_v, num_pages, err);
+void launch_rope_append(const llmdec_config &cfg, float *qkv, const float *qkv_partials, int ks, int ld_qkv,
+                        int n_tokens, int n_seqs, const int32_t *tok_seq, const int32_t *tok_pos,
+                        const int32_t *block_tables, int max_pages, uint16_t *pool_k, uint16_t *pool_v, int num_pages,
+                        uint32_t *err, hipStream_t s) {
+  if (n_tokens <= 0) return;
+  RopeFreq fr;
+  for (int i = 0; i < 64; ++i)
+    fr.inv_freq[i] = i < cfg.head_dim / 2 ? pow((double)cfg.rope_theta, -2.0 * i / (double)cfg.head_dim) : 0.0;
+  rope_append_kernel<<<n_tokens, 256, 0, s>>>(qkv, qkv_partials, qkv_partials ? ks : 1, ld_qkv, n_tokens, cfg.n_heads,
+                                              cfg.head_dim, fr, n_seqs, tok_seq, tok_pos, block_tables, max_pages,
+                                              pool_k, pool_v, num_pages, err);
 }
 
 // ---------------------------------------------------------------- SwiGLU gate ([W] §1.2, [E] §4.2)
-__global__ void silu_mul_kernel(const float *__restrict__ g, const float *__restrict__ u, int ld_in, int blk, int n,
-                                int rows, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad) {
-  const int width = out_hi ? kpad : n;
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (size_t)rows * width) return;
-  const int r = (int)(idx / width), j = (int)(idx % width);
-  if (j >= n) {  // zero the padding columns of the split output
-    const size_t o = packed_offset(r, j, kpad >> 5);
-    out_hi[o] = 0;
-    out_lo[o] = 0;
-    return;
-  }
-  const size_t off = (size_t)r * ld_in + (size_t)(j >> 4) * blk + (j & 15);
-  const float gv = g[off], uv = u[off];
-  store_act(gv / (1.0f + expf(-gv)) * uv, r, j, n, out_f32, out_hi, out_lo, kpad);
+// Stand-alone form: u = silu(g) * up, silu(z) = z / (1 + e^-z).
+__global__ void silu_mul_kernel(const float *__restrict__ g, const float *__restrict__ u, size_t n,
+                                float *__restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float gv = g[i];
+  out[i] = gv / (1.0f + expf(-gv)) * u[i];
 }
 
-void launch_silu_mul(const float *g, const float *u, int ld_in, int blk, int rows, int n, float *out_f32,
-                     uint16_t *out_hi, uint16_t *out_lo, int kpad, hipStream_t s) {
-  const size_t total = (size_t)rows * (out_hi ? kpad : n);
-  if (total)
-    silu_mul_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(g, u, ld_in, blk, n, rows, out_f32, out_hi,
-                                                                     out_lo, kpad);
+void launch_silu_mul(const float *g, const float *u, int rows, int n, float *out, hipStream_t s) {
+  const size_t total = (size_t)rows * n;
+  if (total) silu_mul_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(g, u, total, out);
 }
 
 // ---------------------------------------------------------------- greedy argmax ([F] §2.2.3)

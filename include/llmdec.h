@@ -129,8 +129,9 @@ llmdec_status llmdec_pack_layer(const llmdec_config *cfg, const llmdec_layer_wei
  * block-table row of page ids; position p lives in page row[p / 16] at in-page
  * offset o = p % 16.  Device layout per layer (element = bf16):
  *   K: [num_pages][n_kv_heads][16][head_dim]   (K[page][h][o][d])
- *   V: [num_pages][n_kv_heads][head_dim][16]   (V[page][h][d][o], transposed
- *      inside the page so both attention kernels read V in 16-byte runs),
+ *   V: [num_pages][n_kv_heads][4][head_dim][4] (V[page][h][o/4][d][o%4]: per
+ *      quarter of the page, each dim's 4 tokens are adjacent, so one
+ *      contiguous read gives every lane all tokens of its dims),
  * K block then V block, layer after layer; so pool_bytes = n_layers * 2 *
  * num_pages * n_kv_heads * 16 * head_dim * 2 (for 7B and 128 pages: 1 GiB,
  * the [E] §3.4 example). */

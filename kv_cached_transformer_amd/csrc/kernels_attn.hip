@@ -1,15 +1,13 @@
 // Attention over the paged KV cache ([E] §4.3: softmax(q K^T / sqrt(D)) V with
 // the causal mask; [E] §3.4: keys found through the page index).
 //
-// Pool layout per layer: K[page][h][16][D], V[page][h][D][16].
+// Pool layout per layer: K[page][h][16][D], V[page][h][4][D][4] (token
+// quarter, dim, token within the quarter).
 //
-// Decode: one wave per (sequence, head, partition of pages).  Lane l takes
-// token l/4 of each page and a quarter of the head dimension of its key, so a
-// page's K block (4 KiB at D = 128) is one coalesced read; the 16 scores are
-// reduced in-wave, the running max is wave-uniform per page (one rescale per
-// page), and for P.V lane l owns dims 2l, 2l+1, whose 16 values per page are
-// contiguous in the transposed V block.  Partitions are merged by a
-// log-sum-exp combine kernel.
+// Decode: one wave per (sequence, head, partition of pages), every load a
+// contiguous 1 KiB of a K or V block (details at the kernel); the running max
+// is wave-uniform per page (one rescale per page).  Partitions are merged by
+// a log-sum-exp combine kernel.
 //
 // Prefill: MFMA.  Scores are formed transposed, S^T = K Q^T (keys as rows),
 // so a lane's accumulator holds 4 keys of one query: exactly the operand
@@ -18,6 +16,8 @@
 // 24 bits; three MFMAs per product), K and V are the stored bf16 values, so
 // the scores and the weighted sum keep fp32-level accuracy.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -53,6 +53,56 @@ __device__ inline void store_out(float v, int r, int c, int ld, float *out_f32, 
 }
 
 // ---------------------------------------------------------------- decode
+// One wave per (sequence, head, partition of at most 64 pages).  Every load
+// instruction reads one contiguous run of a page's K or V block (lane l takes
+// bytes 16l..16l+15 of a 1 KiB run): random 4 KiB blocks read this way run at
+// about 6.8 TB/s on MI355X, where a lane reading a 64-byte run of its own gets
+// about 3.9.
+//   K block [16 tokens][D]: instruction i, lane l -> token G*i + l/LPT, dims
+//     8(l%LPT)..+7 (LPT = D/8 lanes per token); a score is the sum over the
+//     lanes of its group, formed with DPP lane swizzles (no LDS round trips).
+//   V block [4 quarters][D][4 tokens]: instruction i reads quarter i, lane l ->
+//     dims D/64*l..+D/64-1, its 4 tokens.  Over the four instructions every
+//     lane holds all 16 tokens of its dims, so the softmax weights of a page
+//     are wave-uniform: they live in scalar registers and feed the FMAs
+//     directly.
+// q enters the K products (v_dot2_f32_bf16) as a bf16 pair hi + lo (about 17
+// bits).  The partition's page ids are read once, one per lane, and picked
+// out with a lane shuffle; K/V of the next DA_RING - 1 pages are in flight
+// while a page is computed (32 KiB per wave at D = 128).  Partitions are the
+// slowest grid dimension,
+// so every sequence's full first partitions are dispatched before the short
+// last ones, which fill in the tail.
+constexpr int DA_RING = 4;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  bf16x2_t x, y;
+  __builtin_memcpy(&x, &a, 4);
+  __builtin_memcpy(&y, &b, 4);
+  return __builtin_amdgcn_fdot2_f32_bf16(x, y, c, false);
+}
+
+// x + (the value of another lane), for the DPP lane patterns used below
+template <int CTRL>
+__device__ inline float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+// Sum over aligned groups of N lanes (N = 8 or 16), result in every lane of the group.
+template <int N>
+__device__ inline float group_sum(float x) {
+  x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  x = dpp_add<0x141>(x);  // row_half_mirror: the other quad of the 8
+  if (N == 16) x = dpp_add<0x140>(x);  // row_mirror: the other 8 of the 16
+  return x;
+}
+
+__device__ inline float uniform_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict__ q, int ld_q, int n_heads,
                                                          const int32_t *__restrict__ ctx_lens,
@@ -61,9 +111,12 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict
                                                          const uint16_t *__restrict__ pool_v, int num_pages, int ppp,
                                                          int n_parts, float *__restrict__ partials, float *out_f32,
                                                          uint16_t *out_hi, uint16_t *out_lo, int kpad, uint32_t *err) {
-  constexpr int DK = D / 4;   // key dims per lane
-  constexpr int DV = D / 64;  // value dims per lane
-  const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  constexpr int NI = D / 32;      // 1 KiB K load instructions per page
+  constexpr int LPT = D / 8;      // lanes per token in K (each holds 8 dims)
+  constexpr int G = 64 / LPT;     // token groups per K instruction
+  constexpr int VE = D / 64;      // V dims per lane
+  constexpr int VW = 2 * VE;      // V words (2 bf16) per lane per quarter
+  const int h = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
   const int lane = threadIdx.x;
   const int n_tok = ctx_lens[s] + 1;
   const int n_pages = (n_tok + 15) >> 4;
@@ -78,99 +131,140 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict
     return;
   }
   const int p1 = min(n_pages, p0 + ppp);
-  const float scale = kLog2e * rsqrtf((float)D);
-  float qr[DK];
-  {
-    const float *qp = q + (size_t)s * ld_q + h * D + (lane & 3) * DK;
-#pragma unroll
-    for (int i = 0; i < DK; i += 4) {
-      const float4 v = *reinterpret_cast<const float4 *>(qp + i);
-      qr[i] = v.x * scale;
-      qr[i + 1] = v.y * scale;
-      qr[i + 2] = v.z * scale;
-      qr[i + 3] = v.w * scale;
+  const int32_t *bt = block_tables + (size_t)s * max_pages;
+  int my_pg = -1;  // lane i: page id of page p0 + i
+  if (lane < p1 - p0) {
+    my_pg = bt[p0 + lane];
+    if (my_pg < 0 || my_pg >= num_pages) {
+      raise_error(err, kErrPage);
+      my_pg = -1;
     }
   }
-  float m = -1e30f, l = 0.f, o[DV];
+  uint32_t qh[4], ql[4];  // q * log2(e)/sqrt(D), dims 8(lane % LPT)..+7, as bf16 hi/lo pairs
+  {
+    const float scale = kLog2e * rsqrtf((float)D);
+    const float *qp = q + (size_t)s * ld_q + h * D + (lane % LPT) * 8;
+    const float4 v0 = *reinterpret_cast<const float4 *>(qp);
+    const float4 v1 = *reinterpret_cast<const float4 *>(qp + 4);
+    const float qv[8] = {v0.x * scale, v0.y * scale, v0.z * scale, v0.w * scale,
+                         v1.x * scale, v1.y * scale, v1.z * scale, v1.w * scale};
 #pragma unroll
-  for (int i = 0; i < DV; ++i) o[i] = 0.f;
-  const int tok = lane >> 2;
-  const int32_t *bt = block_tables + (size_t)s * max_pages;
-  for (int pi = p0; pi < p1; ++pi) {
-    int pg = bt[pi];
-    if (pg < 0 || pg >= num_pages) {
-      if (lane == 0) raise_error(err, kErrPage);
-      pg = -1;
+    for (int j = 0; j < 4; ++j) {
+      uint16_t h0, l0, h1, l1;
+      split_bf16(qv[2 * j], h0, l0);
+      split_bf16(qv[2 * j + 1], h1, l1);
+      qh[j] = h0 | ((uint32_t)h1 << 16);
+      ql[j] = l0 | ((uint32_t)l1 << 16);
     }
-    const bool valid = pg >= 0 && pi * 16 + tok < n_tok;
-    float sc = -INFINITY;
-    uint4 vv[DV * 2];
+  }
+  float m = -1e30f, l = 0.f, o[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) o[e] = 0.f;
+
+  uint4 kb[DA_RING][NI];
+  uint32_t vb[DA_RING][4][VW];
+  auto page_id = [&](int pi) { return __builtin_amdgcn_readlane(my_pg, pi - p0); };  // wave-uniform
+  auto load = [&](int pi, int b) {
+    const int pg = page_id(pi);
     if (pg >= 0) {
-      const uint4 *kp = reinterpret_cast<const uint4 *>(pool_k + (((size_t)pg * n_heads + h) * 16 + tok) * D + (lane & 3) * DK);
-      uint4 kk[DK / 8];
+      const size_t blk = ((size_t)pg * n_heads + h) * 16 * D;  // element offset of this page-head's block
+      const uint4 *kp = reinterpret_cast<const uint4 *>(pool_k + blk) + lane;
 #pragma unroll
-      for (int i = 0; i < DK / 8; ++i) kk[i] = kp[i];
-      const uint4 *vp = reinterpret_cast<const uint4 *>(pool_v + (((size_t)pg * n_heads + h) * D + lane * DV) * 16);
+      for (int i = 0; i < NI; ++i) kb[b][i] = kp[i * 64];
 #pragma unroll
-      for (int i = 0; i < DV * 2; ++i) vv[i] = vp[i];
-      // slots past the last token hold whatever the pool held (possibly NaN): their weight is 0,
-      // and 0 * NaN would poison the sum, so their values are cleared
-      const int n_valid = n_tok - pi * 16;
-      if (n_valid < 16) {
-#pragma unroll
-        for (int i = 0; i < DV * 2; ++i) {
-          vv[i].x = mask_pair(vv[i].x, (i & 1) * 8 + 0, n_valid);
-          vv[i].y = mask_pair(vv[i].y, (i & 1) * 8 + 2, n_valid);
-          vv[i].z = mask_pair(vv[i].z, (i & 1) * 8 + 4, n_valid);
-          vv[i].w = mask_pair(vv[i].w, (i & 1) * 8 + 6, n_valid);
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t *vq = pool_v + blk + (size_t)i * D * 4 + lane * VE * 4;
+        if (VE == 2) {
+          const uint4 w = *reinterpret_cast<const uint4 *>(vq);
+          vb[b][i][0] = w.x, vb[b][i][1] = w.y, vb[b][i][2 % VW] = w.z, vb[b][i][3 % VW] = w.w;
+        } else {
+          const uint2 w = *reinterpret_cast<const uint2 *>(vq);
+          vb[b][i][0] = w.x, vb[b][i][1] = w.y;
         }
       }
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < DK / 8; ++i) {
-        const uint32_t w[4] = {kk[i].x, kk[i].y, kk[i].z, kk[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc = fmaf(bf16lo(w[j]), qr[i * 8 + 2 * j], acc);
-          acc = fmaf(bf16hi(w[j]), qr[i * 8 + 2 * j + 1], acc);
-        }
-      }
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      if (valid) sc = acc;
     } else {
 #pragma unroll
-      for (int i = 0; i < DV * 2; ++i) vv[i] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < NI; ++i) kb[b][i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int w = 0; w < VW; ++w) vb[b][i][w] = 0u;
     }
-    const float pm = wave_max(sc);
+  };
+  // One page with n_valid (wave-uniform) live tokens: 16, fewer on a sequence's last page, 0 for a
+  // rejected page id.
+  auto compute = [&](int b, int n_valid) {
+    float sc[NI];
+    float lm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t w[4] = {kb[b][i].x, kb[b][i].y, kb[b][i].z, kb[b][i].w};
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a = dot2_bf16(w[j], qh[j], dot2_bf16(w[j], ql[j], a));
+      a = group_sum<LPT>(a);
+      sc[i] = (G * i + lane / LPT < n_valid) ? a : -INFINITY;
+      lm = fmaxf(lm, sc[i]);
+    }
+    // page max and weight sum over the G groups: one value per group, read from its first lane
+    float pm = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < G; ++g) pm = fmaxf(pm, uniform_f(lm, g * LPT));
     const float m_new = fmaxf(m, pm);
-    const float alpha = exp2f(m - m_new);
-    const float p = valid ? exp2f(sc - m_new) : 0.f;
-    l = l * alpha + wave_sum((lane & 3) == 0 ? p : 0.f);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    float pr[NI], ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < DV; ++i) o[i] *= alpha;
+    for (int i = 0; i < NI; ++i) {
+      pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);  // 0 for masked tokens
+      ps += pr[i];
+    }
+    float gs = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) gs += uniform_f(ps, g * LPT);
+    l = l * alpha + gs;
     m = m_new;
-    float pts[16];  // p of token t sits in lanes 4t..4t+3
+    // token t's weight sits in group t % G, slot t / G: all 16 become wave-uniform
+    float pt[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) pts[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 4 * t));
+    for (int t = 0; t < 16; ++t) pt[t] = uniform_f(pr[t / G], (t % G) * LPT);
+    // slots past the last token hold whatever the pool held (possibly NaN): their weight is 0, and
+    // 0 * NaN would poison the sum, so their values are cleared through per-token mask words
 #pragma unroll
-    for (int i = 0; i < DV; ++i) {
-      const uint32_t w[8] = {vv[2 * i].x, vv[2 * i].y, vv[2 * i].z, vv[2 * i].w,
-                             vv[2 * i + 1].x, vv[2 * i + 1].y, vv[2 * i + 1].z, vv[2 * i + 1].w};
-      float acc = o[i];
+    for (int e = 0; e < VE; ++e) {
+      float a = o[e] * alpha;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        acc = fmaf(pts[2 * j], bf16lo(w[j]), acc);
-        acc = fmaf(pts[2 * j + 1], bf16hi(w[j]), acc);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t m0 = (4 * i < n_valid ? 0xffffu : 0u) | (4 * i + 1 < n_valid ? 0xffff0000u : 0u);
+        const uint32_t m1 = (4 * i + 2 < n_valid ? 0xffffu : 0u) | (4 * i + 3 < n_valid ? 0xffff0000u : 0u);
+        const uint32_t w0 = vb[b][i][2 * e] & m0, w1 = vb[b][i][2 * e + 1] & m1;  // tokens 4i, 4i+1 | 4i+2, 4i+3
+        a = fmaf(pt[4 * i], bf16lo(w0), a);
+        a = fmaf(pt[4 * i + 1], bf16hi(w0), a);
+        a = fmaf(pt[4 * i + 2], bf16lo(w1), a);
+        a = fmaf(pt[4 * i + 3], bf16hi(w1), a);
       }
-      o[i] = acc;
+      o[e] = a;
+    }
+  };
+#pragma unroll
+  for (int b = 0; b < DA_RING - 1; ++b)
+    if (p0 + b < p1) load(p0 + b, b);
+  for (int pi = p0; pi < p1; pi += DA_RING) {
+#pragma unroll
+    for (int b = 0; b < DA_RING; ++b) {
+      const int pg_i = pi + b;
+      if (pg_i < p1) {
+        const int nxt = pg_i + DA_RING - 1;  // refill the slot freed one page ago
+        if (nxt < p1) load(nxt, (b + DA_RING - 1) % DA_RING);
+        compute(b, page_id(pg_i) < 0 ? 0 : min(16, n_tok - pg_i * 16));
+      }
     }
   }
   const int parts_here = (n_pages + ppp - 1) / ppp;
   if (parts_here == 1) {
     const float inv = 1.f / l;
 #pragma unroll
-    for (int i = 0; i < DV; ++i) store_out(o[i] * inv, s, h * D + lane * DV + i, n_heads * D, out_f32, out_hi, out_lo, kpad);
+    for (int e = 0; e < VE; ++e)
+      store_out(o[e] * inv, s, h * D + lane * VE + e, n_heads * D, out_f32, out_hi, out_lo, kpad);
   } else {
     float *pp = partials + (((size_t)s * n_heads + h) * n_parts + part) * (D + 2);
     if (lane == 0) {
@@ -178,7 +272,7 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict
       pp[1] = l;
     }
 #pragma unroll
-    for (int i = 0; i < DV; ++i) pp[2 + lane * DV + i] = o[i];
+    for (int e = 0; e < VE; ++e) pp[2 + lane * VE + e] = o[e];
   }
 }
 
@@ -212,7 +306,7 @@ void decode_partition(int n_seqs, int n_heads, int max_pages, int *pages_per_par
   int parts = (int)((2048 + rows - 1) / rows);
   parts = parts < 1 ? 1 : parts;
   int ppp = (max_pages + parts - 1) / parts;
-  ppp = ppp < 1 ? 1 : (ppp > 32 ? 32 : ppp);
+  ppp = ppp < 1 ? 1 : (ppp > 16 ? 16 : ppp);  // at most 64: the kernel keeps one page id per lane
   *pages_per_part = ppp;
   *n_parts = (max_pages + ppp - 1) / ppp;
 }
@@ -224,7 +318,7 @@ void launch_decode_attention(const llmdec_config &cfg, const float *q, int ld_q,
   if (n_seqs <= 0) return;
   int ppp, n_parts;
   decode_partition(n_seqs, cfg.n_heads, max_pages, &ppp, &n_parts);
-  dim3 grid(n_parts, cfg.n_heads, n_seqs);
+  dim3 grid(cfg.n_heads, n_seqs, n_parts);
   if (cfg.head_dim == 128) {
     decode_attn_kernel<128><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, ctx_lens, block_tables, max_pages, pk, pv,
                                                 num_pages, ppp, n_parts, partials, out_f32, out_hi, out_lo, kpad, err);
@@ -324,12 +418,13 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
           st = mfma16(kk, qs[1][kt], st);
           st = mfma16(kk, qs[0][kt], st);
         }
-        const uint16_t *vp = pool_v + ((size_t)pg * n_heads + h) * D * 16 + g * 4;
+        // V block [4 quarters][D][4 tokens]: tokens 4g..4g+3 of dim d at (g * D + d) * 4
+        const uint16_t *vp = pool_v + ((size_t)pg * n_heads + h) * D * 16 + (size_t)g * D * 4;
         // keys after the block's last query are not written yet (possibly NaN): clear their values
         const int n_valid = last_pos + 1 - (pi * 16 + g * 4);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          uint2 w = *reinterpret_cast<const uint2 *>(vp + (db * 16 + c) * 16);
+          uint2 w = *reinterpret_cast<const uint2 *>(vp + (db * 16 + c) * 4);
           w.x = mask_pair(w.x, 0, n_valid);
           w.y = mask_pair(w.y, 2, n_valid);
           vt[db][u] = w;

@@ -74,7 +74,10 @@ __device__ inline void epi_store(const LinearOut &o, int r, int c, float v, floa
 constexpr int SG_NB = 4;     // W row blocks per block: 64 output columns
 constexpr int SG_DEPTH = 4;  // k-tiles of weights in flight per wave
 
-template <int MB>
+// Activation tiles are L2 hits but still a round trip: they ride a ring of
+// their own, AD deep (AD divides SG_DEPTH; fewer slots for wide MB keep the
+// registers of a wave within one SIMD's share at two waves per SIMD).
+template <int MB, int AD = (MB <= 2 ? 4 : 2)>
 __global__ __launch_bounds__(256) void stream_gemm_kernel(const uint4 *__restrict__ a_hi,
                                                           const uint4 *__restrict__ a_lo, int a_kt, int rows,
                                                           const uint4 *__restrict__ w, int kt_count, int n_blocks,
@@ -94,32 +97,42 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const uint4 *__restric
     for (int j = 0; j < SG_NB; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const uint4 *wl = w + (size_t)nb0 * kt_count * 64 + lane;  // row block nb0, tile 0, this lane
+  auto a_tile = [&](const uint4 *base, int m, int i) { return base[((size_t)m * a_kt + kt0 + wave + 4 * i) * 64 + lane]; };
   uint4 wb[SG_DEPTH][SG_NB];
+  uint4 ahb[AD][MB], alb[AD][MB];
 #pragma unroll
   for (int d = 0; d < SG_DEPTH; ++d)
 #pragma unroll
     for (int j = 0; j < SG_NB; ++j)
       wb[d][j] = (d < n_it && j < nbs) ? load_stream(wl + ((size_t)j * kt_count + kt0 + wave + 4 * d) * 64)
                                        : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int d = 0; d < AD; ++d)
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      ahb[d][m] = d < n_it ? a_tile(a_hi, m, d) : make_uint4(0, 0, 0, 0);
+      alb[d][m] = d < n_it ? a_tile(a_lo, m, d) : make_uint4(0, 0, 0, 0);
+    }
   for (int it = 0; it < n_it; it += SG_DEPTH) {
 #pragma unroll
     for (int d = 0; d < SG_DEPTH; ++d) {
       const int i = it + d;
       if (i < n_it) {
-        const int kt = kt0 + wave + 4 * i;
-        uint4 ah[MB], al[MB];
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          ah[m] = a_hi[((size_t)m * a_kt + kt) * 64 + lane];
-          al[m] = a_lo[((size_t)m * a_kt + kt) * 64 + lane];
-        }
+        const int da = d % AD;
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
           for (int j = 0; j < SG_NB; ++j) {
-            acc[m][j] = mfma16(al[m], wb[d][j], acc[m][j]);
-            acc[m][j] = mfma16(ah[m], wb[d][j], acc[m][j]);
+            acc[m][j] = mfma16(alb[da][m], wb[d][j], acc[m][j]);
+            acc[m][j] = mfma16(ahb[da][m], wb[d][j], acc[m][j]);
           }
+        if (i + AD < n_it) {
+#pragma unroll
+          for (int m = 0; m < MB; ++m) {
+            ahb[da][m] = a_tile(a_hi, m, i + AD);
+            alb[da][m] = a_tile(a_lo, m, i + AD);
+          }
+        }
         const int i2 = i + SG_DEPTH;
         if (i2 < n_it) {
           const int kt2 = kt0 + wave + 4 * i2;

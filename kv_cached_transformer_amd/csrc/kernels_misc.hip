@@ -200,12 +200,13 @@ void launch_token_map(const int32_t *cu, const int32_t *start, int n_seqs, int n
 }
 
 // ---------------------------------------------------------------- RoPE + paged append ([E] §4.3)
-// One block per new token.  Pair i of every head turns by pos * inv_freq[i],
+// One block per (new token, chunk of heads holding 256 rotation pairs).  Pair i
+// of every head turns by pos * inv_freq[i],
 // inv_freq[i] = theta^(-2i/D) computed in double on the host; the angle is
 // formed and reduced to [-pi, pi] in double, then its sine and cosine taken
 // in fp32, so positions in the thousands lose no accuracy.  q is rotated in
 // place; rotated k and plain v are rounded to bf16 and written to the page
-// slot bt[seq][pos/16], offset pos%16 (K as [h][o][d], V as [h][d][o]).
+// slot bt[seq][pos/16], offset pos%16 (K as [h][o][d], V as [h][o/4][d][o%4]).
 struct RopeFreq {
   double inv_freq[64];
 };
@@ -221,6 +222,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
   const int t = blockIdx.x;
   const int half = head_dim / 2;
   const int hidden = n_heads * head_dim;
+  const int g0 = blockIdx.y * 256;  // first (head, pair) index of this block's chunk
   __shared__ float cs[64], sn[64];
   const int seq = tok_seq ? tok_seq[t] : t;
   const int pos = tok_pos[t];
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
     }
     return acc;
   };
-  for (int g = threadIdx.x; g < n_heads * half; g += 256) {
+  for (int g = g0 + threadIdx.x; g < min(n_heads * half, g0 + 256); g += 256) {
     const int h = g / half, i = g % half;
     const float c = cs[i], s = sn[i];
     const int d = h * head_dim + 2 * i;
@@ -270,9 +272,10 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
       const size_t kbase = (((size_t)page * n_heads + h) * 16 + off) * head_dim + 2 * i;
       *reinterpret_cast<uint32_t *>(pool_k + kbase) = kb;
       const float2 vv = row2(2 * hidden + d);
-      const size_t vbase = (((size_t)page * n_heads + h) * head_dim + 2 * i) * 16 + off;
+      // V block [4 quarters][D][4 tokens]: dim d of token off at ((off/4) * D + d) * 4 + off % 4
+      const size_t vbase = (((size_t)page * n_heads + h) * 4 + (off >> 2)) * head_dim * 4 + (size_t)(2 * i) * 4 + (off & 3);
       pool_v[vbase] = f32_to_bf16(vv.x);
-      pool_v[vbase + 16] = f32_to_bf16(vv.y);
+      pool_v[vbase + 4] = f32_to_bf16(vv.y);
     }
   }
 }
@@ -285,7 +288,8 @@ void launch_rope_append(const llmdec_config &cfg, float *qkv, const float *qkv_p
   RopeFreq fr;
   for (int i = 0; i < 64; ++i)
     fr.inv_freq[i] = i < cfg.head_dim / 2 ? pow((double)cfg.rope_theta, -2.0 * i / (double)cfg.head_dim) : 0.0;
-  rope_append_kernel<<<n_tokens, 256, 0, s>>>(qkv, qkv_partials, qkv_partials ? ks : 1, ld_qkv, n_tokens, cfg.n_heads,
+  dim3 grid(n_tokens, (cfg.n_heads * (cfg.head_dim / 2) + 255) / 256);
+  rope_append_kernel<<<grid, 256, 0, s>>>(qkv, qkv_partials, qkv_partials ? ks : 1, ld_qkv, n_tokens, cfg.n_heads,
                                               cfg.head_dim, fr, n_seqs, tok_seq, tok_pos, block_tables, max_pages,
                                               pool_k, pool_v, num_pages, err);
 }
@@ -360,7 +364,7 @@ __global__ void gather_kv_kernel(const uint16_t *__restrict__ pk, const uint16_t
     const int h = e / head_dim, d = e % head_dim;
     const size_t o = (size_t)p * n_heads * head_dim + e;
     k_out[o] = ok ? pk[(((size_t)page * n_heads + h) * 16 + off) * head_dim + d] : (uint16_t)0xffff;
-    v_out[o] = ok ? pv[(((size_t)page * n_heads + h) * head_dim + d) * 16 + off] : (uint16_t)0xffff;
+    v_out[o] = ok ? pv[((((size_t)page * n_heads + h) * 4 + (off >> 2)) * head_dim + d) * 4 + (off & 3)] : (uint16_t)0xffff;
   }
 }
 

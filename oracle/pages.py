@@ -14,8 +14,9 @@ Readings (the pages are silent on these):
   growth, nothing changes and the call fails ("no pages");
 * position p of a sequence lives in page row[p // 16] at in-page offset p % 16;
 * inside a page, K is laid out [kv_head][16][head_dim] and V is laid out
-  [kv_head][head_dim][16] (transposed); float results do not depend on this,
-  only the pool-image comparisons do.
+  [kv_head][4][head_dim][4] (quarter of the page, dim, token within the
+  quarter); float results do not depend on this, only the pool-image
+  comparisons do.
 
 Parity pins: the slot formula against a brute-force page walk, pool sizing
 against [E] §3.4's 1 GiB example, paged attention equal to contiguous
@@ -86,7 +87,7 @@ class PagePool:
 
 
 class PagedKV:
-    """A paged mirror of the cache: per layer, K pool [num_pages][Hkv][16][D] and V pool [num_pages][Hkv][D][16].
+    """A paged mirror of the cache: per layer, K pool [num_pages][Hkv][16][D] and V pool [num_pages][Hkv][4][D][4].
 
     Values are float64 holding bf16 values.
 
@@ -96,7 +97,7 @@ class PagedKV:
     def __init__(self, n_layers, n_kv_heads, head_dim, num_pages, block_rows: dict):
         self.L, self.H, self.D = n_layers, n_kv_heads, head_dim
         self.K = np.zeros((n_layers, num_pages, n_kv_heads, PAGE, head_dim))
-        self.V = np.zeros((n_layers, num_pages, n_kv_heads, head_dim, PAGE))
+        self.V = np.zeros((n_layers, num_pages, n_kv_heads, PAGE // 4, head_dim, 4))
         self.rows = block_rows          # seq id -> block-table row (list of page ids)
         self.len = {}
 
@@ -107,14 +108,14 @@ class PagedKV:
         assert pos == self.length(layer, seq), "append out of order"
         pg, off = slot_of(self.rows[seq], pos)
         self.K[layer, pg, :, off, :] = k
-        self.V[layer, pg, :, :, off] = v
+        self.V[layer, pg, :, off // 4, :, off % 4] = v
         self.len[(layer, seq)] = pos + 1
 
     def preload(self, layer, seq, k, v):
         for p in range(k.shape[0]):
             pg, off = slot_of(self.rows[seq], p)
             self.K[layer, pg, :, off, :] = k[p]
-            self.V[layer, pg, :, :, off] = v[p]
+            self.V[layer, pg, :, off // 4, :, off % 4] = v[p]
         self.len[(layer, seq)] = k.shape[0]
 
     def keys_values(self, layer, seq, upto):
@@ -124,5 +125,5 @@ class PagedKV:
         for p in range(upto):
             pg, off = slot_of(self.rows[seq], p)
             K[p] = self.K[layer, pg, :, off, :]
-            V[p] = self.V[layer, pg, :, :, off]
+            V[p] = self.V[layer, pg, :, off // 4, :, off % 4]
         return K, V

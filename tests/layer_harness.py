@@ -49,7 +49,7 @@ class LayerCase:
                 self.kv.preload(0, s, od.widen_bf16(k), od.widen_bf16(v))
         kd, vd = self.pool.layer_views(0)
         kd.copy_(torch.from_numpy(kimg.view(np.int16)).to("cuda"))
-        vd.copy_(torch.from_numpy(vimg.view(np.int16)).to("cuda"))
+        vd.copy_(torch.from_numpy(R.Pool.v_raw(vimg).view(np.int16)).to("cuda"))
         self.kimg0, self.vimg0 = kimg, vimg
         self.bt_dev = R.dev_i32(self.bt)
 
@@ -57,5 +57,6 @@ class LayerCase:
         return self.R.Workspace(self.L.llmdec_workspace_bytes(self.cfg, max_tokens, len(self.ctxs), self.max_pages))
 
     def pool_images(self):
+        """Host images of layer 0: K [pages][H][16][D], V [pages][H][D][16] (dim, in-page offset)."""
         k, v = self.pool.layer_views(0)
-        return self.R.host_u16(k.contiguous()), self.R.host_u16(v.contiguous())
+        return self.R.host_u16(k.contiguous()), self.R.Pool.v_logical(self.R.host_u16(v.contiguous()))

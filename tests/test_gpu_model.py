@@ -100,7 +100,7 @@ def test_tiny_model_greedy_generation(L, R):
     # pool contents: every written slot agrees with the oracle's stored bf16 K/V; the rest is sentinel
     for layer in range(shape.n_layers):
         kd, vd = pool.layer_views(layer)
-        kimg, vimg = R.host_u16(kd.contiguous()), R.host_u16(vd.contiguous())
+        kimg, vimg = R.host_u16(kd.contiguous()), R.Pool.v_logical(R.host_u16(vd.contiguous()))
         written = np.zeros((num_pages, 16), bool)
         got, ref = [], []
         for p in range(total):

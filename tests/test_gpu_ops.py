@@ -166,7 +166,8 @@ def test_rope_append_slots_and_values(L, R, H, D):
     assert_close("rope q", qd.cpu().numpy()[:, :h], q_ref, max_abs=1e-5, rel_l2=1e-6)
     k_ref = od.round_to_bf16(od.apply_rope(qkv[:, h:2 * h].reshape(T, H, D), pos, 1e4))
     v_ref = od.round_to_bf16(qkv[:, 2 * h:].astype(np.float64).reshape(T, H, D))
-    kimg, vimg = (R.host_u16(t.contiguous()) for t in pool.layer_views(0))
+    kd, vd = pool.layer_views(0)
+    kimg, vimg = R.host_u16(kd.contiguous()), R.Pool.v_logical(R.host_u16(vd.contiguous()))
     touched_k = np.zeros(kimg.shape[:1] + kimg.shape[2:3], bool)   # [page][slot]
     ulp_flips = 0
     for i, (s, p) in enumerate(toks):
@@ -202,10 +203,10 @@ def _random_pool(L, R, shape, num_pages, rng):
     cfg = L.make_config(shape)
     pool = R.Pool(cfg, num_pages, rng.permutation(num_pages).astype(np.int32))
     k_img = bf16_normal(rng, (num_pages, shape.n_heads, 16, shape.head_dim))
-    v_img = bf16_normal(rng, (num_pages, shape.n_heads, shape.head_dim, 16))
+    v_img = bf16_normal(rng, (num_pages, shape.n_heads, shape.head_dim, 16))   # [page][h][d][offset]
     kv, vv = pool.layer_views(0)
     kv.copy_(R.dev_u16(k_img).view(kv.shape))
-    vv.copy_(R.dev_u16(v_img).view(vv.shape))
+    vv.copy_(R.dev_u16(R.Pool.v_raw(v_img)).view(vv.shape))
     return cfg, pool, k_img, v_img
 
 

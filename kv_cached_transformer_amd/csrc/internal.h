@@ -76,7 +76,6 @@ int launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const Li
 // Sum ks partial products [ks][rows][n] and apply the epilogue o.
 void launch_reduce(const float *partials, int ks, int rows, int n, const LinearOut &o, hipStream_t s);
 size_t linear_partial_floats(int rows, int n, int k);
-int stream_ksplit(int rows, int n, int k);
 void launch_token_map(const int32_t *cu_seqlens, const int32_t *start_pos, int n_seqs, int n_tokens, uint32_t *err, int32_t *tok_seq,
                       int32_t *tok_pos, hipStream_t s);
 // qkv_partials / ks: when the q|k|v product was split over k, its ks partial sums [ks][n_tokens][3*hidden]

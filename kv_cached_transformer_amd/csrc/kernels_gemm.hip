@@ -19,8 +19,8 @@
 //   * stream_gemm (rows <= 64, decode): the weight matrix is read once from
 //     HBM and that read bounds the kernel.  A block owns 64 output columns
 //     (4 row blocks of W); its 4 waves take interleaved k-tiles of the block's
-//     k-range and keep a ring of SG_DEPTH k-tiles of weights in flight (16 KiB
-//     per wave).  Wave sums meet in LDS.  Narrow matrices also split k across
+//     k-range and keep a ring of 3 to 8 k-steps (weights and activations) in
+//     flight, 12 to 32 KiB of weights per wave.  Wave sums meet in LDS.  Narrow matrices also split k across
 //     blocks: each block then stores its fp32 partial sums and the caller adds
 //     them (launch_reduce, or the next kernel that reads the result anyway).
 //   * tiled_gemm (rows > 64, prefill): 128 x 128 output tile per block, one
@@ -71,24 +71,67 @@ __device__ inline void epi_store(const LinearOut &o, int r, int c, float v, floa
 }
 
 // ---------------------------------------------------------------- stream_gemm (rows <= 64)
-constexpr int SG_NB = 4;     // W row blocks per block: 64 output columns
-constexpr int SG_DEPTH = 4;  // k-tiles of weights in flight per wave
+// A block is 4 waves: WN column waves, each owning SG_NB row blocks of W (64
+// output columns), times WK = 4 / WN k-waves that take interleaved k-tiles, so
+// one step of the block covers WK k-tiles.  A k-tile's 2*MB activation tiles
+// (hi and lo of every row block) are needed by all WN column waves of its
+// k-wave: with WN > 1 those waves fetch a share each and pass them on through
+// LDS, which divides the activation requests per weight byte by WN.  (The
+// activation tiles are L2 hits, but vector loads retire in issue order, so
+// each one holds a request slot for as long as the weight loads ahead of it.)
+// k-wave sums meet in LDS at the end; k-splits across blocks store fp32
+// partials that the consumer adds.
+constexpr int SG_NB = 4;
 
-// Activation tiles are L2 hits but still a round trip: they ride a ring of
-// their own, AD deep (AD divides SG_DEPTH; fewer slots for wide MB keep the
-// registers of a wave within one SIMD's share at two waves per SIMD).
-template <int MB, int AD = (MB <= 2 ? 4 : 2)>
-__global__ __launch_bounds__(256) void stream_gemm_kernel(const uint4 *__restrict__ a_hi,
-                                                          const uint4 *__restrict__ a_lo, int a_kt, int rows,
-                                                          const uint4 *__restrict__ w, int kt_count, int n_blocks,
-                                                          LinearOut o, float *__restrict__ partials) {
-  __shared__ float red[3][MB * 16][SG_NB * 16 + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = blockIdx.x, split = blockIdx.y, ks = gridDim.y;
-  const int nb0 = g * SG_NB;
-  const int nbs = min(SG_NB, n_blocks - nb0);
+template <int MB, int WN> struct SgShape {
+  static constexpr int WK = 4 / WN;
+  static constexpr int NA = 2 * MB;                             // activation tiles per k-tile
+  static constexpr int APW = WN > 1 ? (NA + WN - 1) / WN : NA;  // of them fetched by one wave
+  // k-steps in flight per wave: as deep as about 230 registers allow (two waves per SIMD),
+  // counting the ring, the activation operands read back from LDS and the accumulators
+  static constexpr int RAW = (230 - (WN > 1 ? 8 * MB : 0) - 16 * MB) / (4 * (SG_NB + APW));
+  static constexpr int D = RAW < 3 ? 3 : (RAW > 8 ? 8 : RAW);
+  static constexpr int NSLOT = APW * WN;  // staged tiles per k-tile: slots past NA hold unread copies
+  static constexpr int STAGE_U4 = WN > 1 ? 2 * WK * NSLOT * 64 : 0;               // two stages of tiles
+  static constexpr int RED_F = WK > 1 ? (WK - 1) * MB * 16 * (WN * 64 + 1) : 0;  // k-wave sums
+  static constexpr int LDS_U4 = STAGE_U4 > (RED_F + 3) / 4 ? STAGE_U4 : ((RED_F + 3) / 4 > 0 ? (RED_F + 3) / 4 : 1);
+};
+
+// Raw buffer access: a scalar resource (base, byte size) plus a per-lane and a
+// scalar byte offset.  Loads at or past the size read zero.
+constexpr int kLoadStream = 2;  // cache policy: non-temporal (read once)
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, size_t bytes) {
+  const int n = bytes >= 0xffffffffull ? (int)0xffffffffu : (int)(uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+__device__ inline uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, int policy) {
+  u32x4 v;
+  if (policy == kLoadStream) v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kLoadStream);
+  else v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// The steady-state loop issues only unconditional loads (row blocks past the
+// matrix and k-tiles past the range are clamped to the last one and their
+// products skipped or dropped), and scheduling barriers keep the ring order,
+// so the compiler's wait counts follow the ring instead of draining it.
+template <int MB, int WN>
+__global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__restrict__ a_hi,
+                                                             const uint4 *__restrict__ a_lo, int a_kt, int rows,
+                                                             const uint4 *__restrict__ w, int kt_count, int n_blocks,
+                                                             LinearOut o, float *__restrict__ partials) {
+  using S = SgShape<MB, WN>;
+  constexpr int WK = S::WK, NA = S::NA, APW = S::APW, D = S::D;
+  constexpr bool SHARE = WN > 1;
+  __shared__ uint4 lds[S::LDS_U4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar control
+  const int cw = wave % WN, kw = wave / WN;
+  const int split = blockIdx.y, ks = gridDim.y;
+  const int nb0 = (blockIdx.x * WN + cw) * SG_NB;  // this wave's first row block of W
+  const int nbs = min(SG_NB, n_blocks - nb0);      // <= 0 for a wave past the matrix
   const int kt0 = (int)((long)kt_count * split / ks), kt1 = (int)((long)kt_count * (split + 1) / ks);
-  const int n_it = kt1 - kt0 > wave ? (kt1 - kt0 - wave + 3) >> 2 : 0;  // k-tiles kt0 + wave + 4i
+  const int n_it = (kt1 - kt0 + WK - 1) / WK;  // block-uniform; step i is k-tile kt0 + kw + WK*i
 
   f32x4 acc[MB][SG_NB];
 #pragma unroll
@@ -96,78 +139,118 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const uint4 *__restric
 #pragma unroll
     for (int j = 0; j < SG_NB; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint4 *wl = w + (size_t)nb0 * kt_count * 64 + lane;  // row block nb0, tile 0, this lane
-  auto a_tile = [&](const uint4 *base, int m, int i) { return base[((size_t)m * a_kt + kt0 + wave + 4 * i) * 64 + lane]; };
-  uint4 wb[SG_DEPTH][SG_NB];
-  uint4 ahb[AD][MB], alb[AD][MB];
+  // Scalar resources and offsets; the lane adds its own 16 bytes of a 1 KiB tile.
+  const uint32_t lane_bytes = (uint32_t)lane * 16u;
+  // Each resource spans only what the wave reads (its own row blocks; the MB row blocks of the
+  // activations), far below 2^31 bytes, so the out-of-range marker below is always past its end.
+  const int nbb = min(nb0, n_blocks - 1);
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(w + (size_t)nbb * kt_count * 64, (size_t)(min(nb0 + SG_NB, n_blocks) - nbb) * kt_count * 1024);
+  uint32_t w_off[SG_NB];
 #pragma unroll
-  for (int d = 0; d < SG_DEPTH; ++d)
+  for (int j = 0; j < SG_NB; ++j) w_off[j] = (uint32_t)(min(nb0 + j, n_blocks - 1) - nbb) * (uint32_t)kt_count * 1024u;
+  const size_t a_bytes = (size_t)MB * a_kt * 1024;
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(a_hi, a_bytes), lr = make_rsrc(a_lo, a_bytes);
+  // activation tiles this wave fetches: q = cw + WN*s (hi row block q, or lo row block q - MB)
+  __amdgpu_buffer_rsrc_t ar[APW];
+  uint32_t a_off[APW];
 #pragma unroll
-    for (int j = 0; j < SG_NB; ++j)
-      wb[d][j] = (d < n_it && j < nbs) ? load_stream(wl + ((size_t)j * kt_count + kt0 + wave + 4 * d) * 64)
-                                       : make_uint4(0, 0, 0, 0);
+  for (int s = 0; s < APW; ++s) {
+    const int q = min(SHARE ? cw + WN * s : s, NA - 1);
+    ar[s] = q < MB ? hr : lr;
+    a_off[s] = (uint32_t)(q < MB ? q : q - MB) * (uint32_t)a_kt * 1024u;
+  }
+
+  // A step past the wave's k-range (the k-waves' last steps, and the padding of the step count to a
+  // multiple of D) moves the lane offset past every resource's size: such loads read zeros without
+  // touching memory and their products add nothing, so the ring needs no branches.
+  uint4 wb[D][SG_NB], ab[D][APW];
+  auto issue = [&](int slot, int i) {
+    const int kt = kt0 + kw + WK * i;
+    const uint32_t voff = lane_bytes | (kt < kt1 ? 0u : 0x80000000u);
+    const uint32_t koff = (uint32_t)min(kt, kt1 - 1) * 1024u;
 #pragma unroll
-  for (int d = 0; d < AD; ++d)
+    for (int s = 0; s < APW; ++s) ab[slot][s] = buffer_load16(ar[s], voff, a_off[s] + koff, 0);
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      ahb[d][m] = d < n_it ? a_tile(a_hi, m, d) : make_uint4(0, 0, 0, 0);
-      alb[d][m] = d < n_it ? a_tile(a_lo, m, d) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < SG_NB; ++j) wb[slot][j] = buffer_load16(wr, voff, w_off[j] + koff, kLoadStream);
+  };
+  auto compute = [&](int slot, int i) {
+    uint4 av[NA];  // hi of row block m at m, lo at MB + m
+    if constexpr (SHARE) {
+      // every wave writes all its slots (a skipped write would be a branch in the ring)
+      uint4 *st = lds + (size_t)((i & 1) * WK + kw) * S::NSLOT * 64;
+#pragma unroll
+      for (int s = 0; s < APW; ++s) st[(cw + WN * s) * 64 + lane] = ab[slot][s];
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < NA; ++q) av[q] = st[q * 64 + lane];
+    } else {
+#pragma unroll
+      for (int q = 0; q < NA; ++q) av[q] = ab[slot][q];
     }
-  for (int it = 0; it < n_it; it += SG_DEPTH) {
 #pragma unroll
-    for (int d = 0; d < SG_DEPTH; ++d) {
-      const int i = it + d;
-      if (i < n_it) {
-        const int da = d % AD;
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
-        for (int m = 0; m < MB; ++m)
-#pragma unroll
-          for (int j = 0; j < SG_NB; ++j) {
-            acc[m][j] = mfma16(alb[da][m], wb[d][j], acc[m][j]);
-            acc[m][j] = mfma16(ahb[da][m], wb[d][j], acc[m][j]);
-          }
-        if (i + AD < n_it) {
-#pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            ahb[da][m] = a_tile(a_hi, m, i + AD);
-            alb[da][m] = a_tile(a_lo, m, i + AD);
-          }
-        }
-        const int i2 = i + SG_DEPTH;
-        if (i2 < n_it) {
-          const int kt2 = kt0 + wave + 4 * i2;
-#pragma unroll
-          for (int j = 0; j < SG_NB; ++j)
-            if (j < nbs) wb[d][j] = load_stream(wl + ((size_t)j * kt_count + kt2) * 64);
-        }
+      for (int j = 0; j < SG_NB; ++j) {
+        acc[m][j] = mfma16(av[MB + m], wb[slot][j], acc[m][j]);
+        acc[m][j] = mfma16(av[m], wb[slot][j], acc[m][j]);
       }
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    issue(d, d);
+    __builtin_amdgcn_sched_barrier(0);  // slots leave in ring order, so the waits stay partial
+  }
+  for (int it = 0; it < n_it; it += D) {  // block-uniform trip count; the final refills read nothing
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      compute(d, it + d);
+      issue(d, it + D + d);
+      __builtin_amdgcn_sched_barrier(0);  // the scheduler would otherwise sink every refill to the end
     }
   }
+
   // accumulator layout: lane l, element e -> row 4(l/16)+e, column l%16 of each 16 x 16 block
   const int rq = (lane >> 4) * 4, cq = lane & 15;
-  if (wave > 0) {
+  if constexpr (WK > 1) {  // k-waves 1.. hand their sums to k-wave 0, which adds them in order
+    constexpr int RW = WN * 64 + 1;
+    float *red = reinterpret_cast<float *>(lds);  // [WK-1][MB*16][RW], over the dead staging buffers
+    __syncthreads();
+    if (kw > 0) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int j = 0; j < SG_NB; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            red[((kw - 1) * MB * 16 + m * 16 + rq + e) * RW + cw * 64 + j * 16 + cq] = acc[m][j][e];
+    }
+    __syncthreads();
+    if (kw != 0) return;
+#pragma unroll
+    for (int q = 0; q < WK - 1; ++q)
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int j = 0; j < SG_NB; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[m][j][e] += red[(q * MB * 16 + m * 16 + rq + e) * RW + cw * 64 + j * 16 + cq];
+  }
+  if (nbs <= 0) return;
+  const int n = n_blocks * 16;
+  if (ks > 1) {
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int j = 0; j < SG_NB; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[wave - 1][m * 16 + rq + e][j * 16 + cq] = acc[m][j][e];
+        for (int e = 0; e < 4; ++e) {
+          const int r = m * 16 + rq + e;
+          if (r < rows && j < nbs) partials[((size_t)split * rows + r) * n + (nb0 + j) * 16 + cq] = acc[m][j][e];
+        }
+    return;
   }
-  __syncthreads();
-  if (wave != 0) return;
-  const int n = n_blocks * 16;
-#pragma unroll
-  for (int m = 0; m < MB; ++m)
-#pragma unroll
-    for (int j = 0; j < SG_NB; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = m * 16 + rq + e, c = j * 16 + cq;
-        const float v = acc[m][j][e] + red[0][r][c] + red[1][r][c] + red[2][r][c];
-        acc[m][j][e] = v;
-        if (ks > 1 && r < rows && j < nbs) partials[((size_t)split * rows + r) * n + (nb0 + j) * 16 + cq] = v;
-      }
-  if (ks > 1) return;
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -340,22 +423,51 @@ __global__ __launch_bounds__(256) void tiled_gemm_kernel(const uint4 *__restrict
 }
 
 // ---------------------------------------------------------------- dispatch
-// Splits of k across blocks for the streaming kernel: enough blocks to keep
-// every CU streaming, while the partial sums (written once and read back
-// once) stay at most a quarter of the weight bytes and every wave keeps at
-// least four k-tiles to pipeline.
-int stream_ksplit(int rows, int n, int k) {
-  const int groups = (n / 16 + SG_NB - 1) / SG_NB;
-  const int kt = round_up(k, kTileK) / kTileK;
-  int ks = 1;
-  while (groups * ks < 512 && kt / (ks * 2) >= 16 && (long)(ks * 2) * rows * 16 <= (long)k) ks *= 2;
-  return ks;
+// Shape of a streaming launch.  For each column-wave count (4, 2, 1: more
+// column waves, fewer activation requests per weight byte) the k split grows
+// while the grid stays within two blocks per CU, every wave keeps at least 8
+// k-steps to pipeline, and the partial sums (written and read back once) stay
+// within a quarter of the weight bytes.  The widest layout that still gives
+// every CU a block wins; failing that, the one with the most blocks.
+struct StreamPlan {
+  int wn, ks;
+};
+
+static StreamPlan stream_plan(int rows, int n, int k, bool allow_split) {
+  const int nb = n / 16, kt = round_up(k, kTileK) / kTileK;
+  StreamPlan best{1, 1};
+  long best_blocks = -1;
+  for (int wn : {4, 2, 1}) {
+    const int wk = 4 / wn;
+    const long groups = (nb + SG_NB * wn - 1) / (SG_NB * wn);
+    int ks = 1;
+    if (allow_split)
+      while (groups * (ks + 1) <= 512 && kt / (ks + 1) / wk >= 8 && 16L * (ks + 1) * rows <= (long)k) ++ks;
+    const long blocks = groups * ks;
+    if (blocks >= 256) return {wn, ks};
+    if (blocks > best_blocks) {
+      best = {wn, ks};
+      best_blocks = blocks;
+    }
+  }
+  return best;
 }
 
 size_t linear_partial_floats(int rows, int n, int k) {
   if (rows > 64) return 0;
-  const int ks = stream_ksplit(rows, n, k);
-  return ks > 1 ? (size_t)ks * rows * n : 0;
+  const StreamPlan p = stream_plan(rows, n, k, true);
+  return p.ks > 1 ? (size_t)p.ks * rows * n : 0;
+}
+
+template <int MB>
+static void launch_stream(int wn, dim3 grid, hipStream_t s, const uint4 *ah, const uint4 *al, int a_kt, int rows,
+                          const uint4 *w, int kt_count, int n_blocks, const LinearOut &o, float *partials) {
+  if (wn == 4)
+    stream_gemm_kernel<MB, 4><<<grid, 256, 0, s>>>(ah, al, a_kt, rows, w, kt_count, n_blocks, o, partials);
+  else if (wn == 2)
+    stream_gemm_kernel<MB, 2><<<grid, 256, 0, s>>>(ah, al, a_kt, rows, w, kt_count, n_blocks, o, partials);
+  else
+    stream_gemm_kernel<MB, 1><<<grid, 256, 0, s>>>(ah, al, a_kt, rows, w, kt_count, n_blocks, o, partials);
 }
 
 #ifndef LLMDEC_TILED_DIRECT
@@ -370,16 +482,16 @@ int launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const Li
   const uint4 *ah = reinterpret_cast<const uint4 *>(a.hi), *al = reinterpret_cast<const uint4 *>(a.lo);
   const int a_kt = a.kpad / kTileK;
   if (a.rows <= 64) {
-    int ks = allow_split ? stream_ksplit(a.rows, n, k) : 1;
-    if (ks > 1 && (!partials || partial_floats < (size_t)ks * a.rows * n)) ks = 1;
-    dim3 grid((n_blocks + SG_NB - 1) / SG_NB, ks);
+    StreamPlan p = stream_plan(a.rows, n, k, allow_split);
+    if (p.ks > 1 && (!partials || partial_floats < (size_t)p.ks * a.rows * n)) p = stream_plan(a.rows, n, k, false);
+    const dim3 grid((n_blocks + SG_NB * p.wn - 1) / (SG_NB * p.wn), p.ks);
     switch ((a.rows + 15) / 16) {
-      case 1: stream_gemm_kernel<1><<<grid, 256, 0, s>>>(ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
-      case 2: stream_gemm_kernel<2><<<grid, 256, 0, s>>>(ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
-      case 3: stream_gemm_kernel<3><<<grid, 256, 0, s>>>(ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
-      default: stream_gemm_kernel<4><<<grid, 256, 0, s>>>(ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
+      case 1: launch_stream<1>(p.wn, grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
+      case 2: launch_stream<2>(p.wn, grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
+      case 3: launch_stream<3>(p.wn, grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
+      default: launch_stream<4>(p.wn, grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
     }
-    return ks;
+    return p.ks;
   }
   const int tiles_m = (a.rows + TG_MB * 16 - 1) / (TG_MB * 16);
   const int tiles_n = (n_blocks + TG_NB - 1) / TG_NB;

@@ -31,6 +31,26 @@ __device__ inline uint4 load_stream(const uint4 *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Raw buffer access: a scalar resource (base, byte size) plus a per-lane and a
+// scalar byte offset.  A load at or past the size reads zeros and touches no
+// memory, so an empty resource turns a load off without a branch.
+constexpr int kLoadStream = 2;  // cache policy: non-temporal (read once)
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, size_t bytes) {
+  const int n = bytes >= 0xffffffffull ? (int)0xffffffffu : (int)(uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+__device__ inline uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, int policy) {
+  u32x4 v;
+  if (policy == kLoadStream) v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kLoadStream);
+  else v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// 8-byte streaming (non-temporal) load.
+__device__ inline uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kLoadStream);
+  return make_uint2(v[0], v[1]);
+}
+
 __host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 __host__ __device__ inline size_t round_up_sz(size_t x, size_t m) { return (x + m - 1) / m * m; }
 

@@ -97,20 +97,6 @@ template <int MB, int WN> struct SgShape {
   static constexpr int LDS_U4 = STAGE_U4 > (RED_F + 3) / 4 ? STAGE_U4 : ((RED_F + 3) / 4 > 0 ? (RED_F + 3) / 4 : 1);
 };
 
-// Raw buffer access: a scalar resource (base, byte size) plus a per-lane and a
-// scalar byte offset.  Loads at or past the size read zero.
-constexpr int kLoadStream = 2;  // cache policy: non-temporal (read once)
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, size_t bytes) {
-  const int n = bytes >= 0xffffffffull ? (int)0xffffffffu : (int)(uint32_t)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
-}
-__device__ inline uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, int policy) {
-  u32x4 v;
-  if (policy == kLoadStream) v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kLoadStream);
-  else v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 // The steady-state loop issues only unconditional loads (row blocks past the
 // matrix and k-tiles past the range are clamped to the last one and their
 // products skipped or dropped), and scheduling barriers keep the ring order,

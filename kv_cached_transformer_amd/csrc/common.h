@@ -51,6 +51,24 @@ __device__ inline uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
   return make_uint2(v[0], v[1]);
 }
 
+// acc += p[0] + p[stride] + ... + p[(ks-1)*stride], added in that order (the result does not depend
+// on the batching).  Loads leave 8 at a time, so a long list of split-k partials costs a few memory
+// round trips rather than one per split.
+__device__ inline void vadd(float4 &a, const float4 &b) { a.x += b.x, a.y += b.y, a.z += b.z, a.w += b.w; }
+__device__ inline void vadd(float2 &a, const float2 &b) { a.x += b.x, a.y += b.y; }
+template <typename V>
+__device__ inline void add_splits(V &acc, const float *p, size_t stride, int ks) {
+  for (int q = 0; q < ks; q += 8) {
+    V v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (q + j < ks) v[j] = *reinterpret_cast<const V *>(p + (size_t)(q + j) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (q + j < ks) vadd(acc, v[j]);
+  }
+}
+
 __host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 __host__ __device__ inline size_t round_up_sz(size_t x, size_t m) { return (x + m - 1) / m * m; }
 

@@ -119,7 +119,6 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict
   constexpr int LPT = D / 8;      // lanes per token in K (each holds 8 dims)
   constexpr int G = 64 / LPT;     // token groups per K instruction
   constexpr int VE = D / 64;      // V dims per lane
-  constexpr int VW = 2 * VE;      // V words (2 bf16) per lane per quarter
   const int h = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
   const int lane = threadIdx.x;
   const int p0 = part * ppp;
@@ -297,14 +296,43 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(int n_heads, const in
   const int parts = (n_pages + ppp - 1) / ppp;
   if (parts <= 1) return;
   const float *pp = partials + ((size_t)s * n_heads + h) * n_parts * (D + 2);
-  float mx = -1e30f;
-  for (int i = 0; i < parts; ++i) mx = fmaxf(mx, pp[i * (D + 2)]);
-  float L = 0.f, acc = 0.f;
   const int d = threadIdx.x;
-  for (int i = 0; i < parts; ++i) {
-    const float w = exp2f(pp[i * (D + 2)] - mx);
-    L = fmaf(pp[i * (D + 2) + 1], w, L);
-    acc = fmaf(pp[i * (D + 2) + 2 + d], w, acc);
+  // maximum of the partitions' running maxima: one partition per thread, then a block reduction
+  __shared__ float red[D / 64], wl[2][D];
+  float mx = -1e30f;
+  for (int i = d; i < parts; i += D) mx = fmaxf(mx, pp[(size_t)i * (D + 2)]);
+  mx = wave_max(mx);
+  if ((d & 63) == 0) red[d >> 6] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < D / 64; ++w) mx = fmaxf(mx, red[w]);
+  // partitions in chunks of D: each thread forms one partition's weight, then every thread adds the
+  // chunk's contributions to its dimension in partition order (loads batched 8 at a time)
+  float L = 0.f, acc = 0.f;
+  for (int c0 = 0; c0 < parts; c0 += D) {
+    const int nc = min(D, parts - c0);
+    __syncthreads();  // the previous chunk's weights are no longer read
+    if (d < nc) {
+      const float *pi = pp + (size_t)(c0 + d) * (D + 2);
+      const float w = exp2f(pi[0] - mx);
+      wl[0][d] = w;
+      wl[1][d] = pi[1];
+    }
+    __syncthreads();
+    for (int i = 0; i < nc; i += 8) {
+      float ov[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (i + j < nc) ov[j] = pp[(size_t)(c0 + i + j) * (D + 2) + 2 + d];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (i + j < nc) {
+          const float w = wl[0][i + j];
+          L = fmaf(wl[1][i + j], w, L);
+          acc = fmaf(ov[j], w, acc);
+        }
+    }
   }
   store_out(acc / L, s, h * D + d, n_heads * D, out_f32, out_hi, out_lo, kpad);
 }

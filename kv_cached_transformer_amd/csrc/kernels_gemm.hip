@@ -265,14 +265,8 @@ __global__ void reduce_kernel(const float *__restrict__ partials, int ks, int ro
   if (o.kind == kSiluMul && ((c >> 4) & 1)) return;
   const size_t plane = (size_t)rows * n;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f), u = s;
-  for (int q = 0; q < ks; ++q) {
-    const float4 v = *reinterpret_cast<const float4 *>(partials + q * plane + (size_t)r * n + c);
-    s.x += v.x, s.y += v.y, s.z += v.z, s.w += v.w;
-    if (o.kind == kSiluMul) {
-      const float4 w = *reinterpret_cast<const float4 *>(partials + q * plane + (size_t)r * n + c + 16);
-      u.x += w.x, u.y += w.y, u.z += w.z, u.w += w.w;
-    }
-  }
+  add_splits(s, partials + (size_t)r * n + c, plane, ks);
+  if (o.kind == kSiluMul) add_splits(u, partials + (size_t)r * n + c + 16, plane, ks);
   epi_store(o, r, c, s.x, u.x);
   epi_store(o, r, c + 1, s.y, u.y);
   epi_store(o, r, c + 2, s.z, u.z);

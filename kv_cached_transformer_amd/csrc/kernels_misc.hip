@@ -89,13 +89,10 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float *__restrict__ x, int
       const float4 v1 = *reinterpret_cast<const float4 *>(xr + c0 + 4);
       float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       if (add) {
-        for (int q = 0; q < ks; ++q) {
-          const float *p = add + ((size_t)q * rows + r) * n + c0;
-          const float4 p0 = *reinterpret_cast<const float4 *>(p);
-          const float4 p1 = *reinterpret_cast<const float4 *>(p + 4);
-          v[0] += p0.x, v[1] += p0.y, v[2] += p0.z, v[3] += p0.w;
-          v[4] += p1.x, v[5] += p1.y, v[6] += p1.z, v[7] += p1.w;
-        }
+        float4 a0 = make_float4(v[0], v[1], v[2], v[3]), a1 = make_float4(v[4], v[5], v[6], v[7]);
+        add_splits(a0, add + (size_t)r * n + c0, (size_t)rows * n, ks);
+        add_splits(a1, add + (size_t)r * n + c0 + 4, (size_t)rows * n, ks);
+        v[0] = a0.x, v[1] = a0.y, v[2] = a0.z, v[3] = a0.w, v[4] = a1.x, v[5] = a1.y, v[6] = a1.z, v[7] = a1.w;
         *reinterpret_cast<float4 *>(xr + c0) = make_float4(v[0], v[1], v[2], v[3]);
         *reinterpret_cast<float4 *>(xr + c0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
       }
@@ -254,10 +251,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
   auto row2 = [&](int col) -> float2 {
     if (!part) return *reinterpret_cast<const float2 *>(q + col);
     float2 acc = make_float2(0.f, 0.f);
-    for (int p = 0; p < ks; ++p) {
-      const float2 v = *reinterpret_cast<const float2 *>(part + ((size_t)p * n_tokens + t) * ld_qkv + col);
-      acc.x += v.x, acc.y += v.y;
-    }
+    add_splits(acc, part + (size_t)t * ld_qkv + col, (size_t)n_tokens * ld_qkv, ks);
     return acc;
   };
   for (int g = g0 + threadIdx.x; g < min(n_heads * half, g0 + 256); g += 256) {

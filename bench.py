@@ -23,6 +23,13 @@ on the stream the library launches on.  The cpu_baseline leg times the CPU
 oracle (float64 NumPy) on a bounded sample of the same decode workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only c5,c2,c3,c4]
+
+Profiling helpers (no GPU needed for the two summaries):
+  python bench.py --only copy                  1 GiB device copies: calibrates the HBM counters
+  python bench.py --pmc-summary FETCH WRITE    traffic summary from two rocprofv3 --pmc runs
+  python bench.py --trace-summary DIR          per-kernel table from a rocprofv3 --kernel-trace run
+The roofline's traffic field is read from the committed traffic summary, and
+only while the attention sources still hash to the value recorded there.
 """
 from __future__ import annotations
 
@@ -37,6 +44,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+ATTN_SOURCES = ("kv_cached_transformer_amd/csrc/kernels_attn.hip", "kv_cached_transformer_amd/csrc/common.h")
+TRAFFIC_PROFILE = "profiles/decode_attention_7B-b64-ctx256..2048_traffic.txt"
+COPY_BYTES = 1 << 30
 MFMA_BF16_PEAK = 2.5e15    # dense bf16 FLOP/s, MI355X
 METRIC = "decode tokens/s + % peak HBM BW (7B-shaped, paged KV); prefill tok/s + % MFMA"
 SEED = 20261202
@@ -118,6 +128,17 @@ def time_loop(torch, fn, iters, warmup):
     return e0.elapsed_time(e1) / iters
 
 
+def attn_alg_bytes(steps, warmup):
+    """Algorithmic bytes of one standalone attention call on the decode cache after warmup + steps
+    steps: every cached K and V element once (bf16), q read and the output written (fp32)."""
+    import numpy as np
+    import synth
+    shape = synth.LLAMA7B
+    B, h = 64, shape.hidden
+    ctx = synth.context_lengths(5, B, 256, 2048)
+    return float(np.sum(ctx + steps + warmup + 1)) * 2 * h * 2 + 2 * B * h * 4
+
+
 # ----------------------------------------------------------------------------- the headline: 32-layer decode
 def bench_model_decode(torch, L, R, steps, warmup):
     import numpy as np
@@ -167,7 +188,7 @@ def bench_model_decode(torch, L, R, steps, warmup):
     q = torch.randn(B, h, device="cuda", generator=d.gen, dtype=torch.float32)
     out = torch.empty(B, h, device="cuda", dtype=torch.float32)
     ctx_last = R.dev_i32(ctx + n_iter)
-    attn_bytes = float(np.sum(ctx + n_iter + 1)) * 2 * h * 2 + 2 * B * h * 4
+    attn_bytes = attn_alg_bytes(steps, warmup)
 
     def attn(i):
         L.llmdec_op_decode_attention(d.cfg, q.data_ptr(), B, ctx_last.data_ptr(), bt.data_ptr(), max_pages,
@@ -291,14 +312,133 @@ def cpu_baseline(ctx):
 
 
 # ----------------------------------------------------------------------------- main
+# ----------------------------------------------------------------------------- counter calibration and summaries
+def bench_copy(torch):
+    """Three copies of a 1 GiB float tensor: a plain stream of known bytes for the HBM counters."""
+    a = torch.ones(COPY_BYTES // 4, device="cuda", dtype=torch.float32)
+    b = torch.empty_like(a)
+    ms = time_loop(torch, lambda i: b.copy_(a), 3, 1)
+    log(f"copy: {COPY_BYTES} bytes read + written in {ms * 1e3:.1f} us ({2 * COPY_BYTES / (ms * 1e-3) / 1e9:.0f} GB/s)")
+
+
+def sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _pmc_rows(d, counter):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+    return rows
+
+
+def _per_dispatch(rows, name_part, last=64):
+    """Mean counter value (KiB) over the last `last` dispatches of the named kernel (the standalone
+    attention calls, which follow the model steps)."""
+    sel = sorted((r for r in rows if name_part in r["Kernel_Name"]), key=lambda r: int(r["Dispatch_Id"]))[-last:]
+    if not sel:
+        raise SystemExit(f"no dispatch of {name_part}")
+    vals = [float(r["Counter_Value"]) for r in sel]
+    return sum(vals) / len(vals), len(vals), sel[-1]["Grid_Size"]
+
+
+def pmc_summary(fetch_dir, write_dir):
+    """Print the traffic summary committed under profiles/ from a FETCH_SIZE run and a WRITE_SIZE run of
+    `bench.py --only c5,copy --no-cpu` with the default --steps 10 --warmup 3."""
+    fr, wr = _pmc_rows(fetch_dir, "FETCH_SIZE"), _pmc_rows(write_dir, "WRITE_SIZE")
+    copy_f = max(float(r["Counter_Value"]) for r in fr if "copy" in r["Kernel_Name"].lower())
+    copy_w = max(float(r["Counter_Value"]) for r in wr if "copy" in r["Kernel_Name"].lower())
+    kf, kw = COPY_BYTES / (copy_f * 1024), COPY_BYTES / (copy_w * 1024)
+    out = ["# HBM traffic per call of llmdec_op_decode_attention on the 64-sequence decode cache (7B shapes,",
+           "# contexts 256..2048 after the default 3 + 10 steps): partition kernel + combine kernel.",
+           "# Counters are KiB per dispatch; each is scaled by what it reads for a 1 GiB device copy.",
+           "# Commands (from /tmp, committed files only), then the summary:",
+           "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <F> -o p -- python3 <repo>/bench.py --only c5,copy --no-cpu",
+           "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <W> -o p -- python3 <repo>/bench.py --only c5,copy --no-cpu",
+           "#   python3 bench.py --pmc-summary <F> <W>",
+           f"sources_sha256: {sources_hash()}",
+           f"copy_fetch_kib: {copy_f:.1f}  fetch_scale: {kf:.4f}",
+           f"copy_write_kib: {copy_w:.1f}  write_scale: {kw:.4f}"]
+    total = 0.0
+    for name in ("decode_attn_kernel<128>", "decode_combine_kernel<128>"):
+        f, nf, grid = _per_dispatch(fr, name)
+        w, nw, _ = _per_dispatch(wr, name)
+        b = f * 1024 * kf + w * 1024 * kw
+        total += b
+        out.append(f"{name}: grid {grid}: FETCH_SIZE {f:.1f} KiB ({nf} dispatches), WRITE_SIZE {w:.1f} KiB "
+                   f"({nw}) -> {b / 1e6:.2f} MB")
+    alg = attn_alg_bytes(10, 3)
+    out.append(f"algorithmic_bytes_per_call: {alg:.0f}")
+    out.append(f"traffic_bytes_per_call: {total:.0f}  (x{total / alg:.3f} the algorithmic bytes)")
+    print("\n".join(out))
+
+
+def read_traffic(attn_bytes_now):
+    """HBM bytes per attention call from the committed summary, scaled to this run's cache (the bytes
+    grow with the context, which depends on --steps/--warmup), or None when the sources changed."""
+    try:
+        with open(os.path.join(ROOT, TRAFFIC_PROFILE)) as fh:
+            kv = dict(line.split(": ", 1) for line in fh.read().splitlines() if ": " in line and not line.startswith("#"))
+        if kv.get("sources_sha256", "").strip() != sources_hash():
+            return None
+        traffic = float(kv["traffic_bytes_per_call"].split()[0])
+        alg = float(kv.get("algorithmic_bytes_per_call", "0").split()[0]) or None
+        return traffic * (attn_bytes_now / alg) if alg else traffic
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def trace_summary(d):
+    """Per-kernel table (calls, mean and total time) from a rocprofv3 --kernel-trace --stats run."""
+    import collections
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    agg = collections.defaultdict(list)
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"].split("(")[0].replace("void ", "")[:58]
+                grid = f'{r["Grid_Size_X"]}x{r["Grid_Size_Y"]}x{r["Grid_Size_Z"]}'
+                agg[(name, grid)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in agg.values())
+    print(f"{'kernel':58s} {'grid':>18s} {'calls':>6s} {'avg us':>9s} {'total ms':>9s} {'%':>6s}")
+    for (name, grid), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        if sum(v) < 0.002 * total:
+            continue
+        print(f"{name:58s} {grid:>18s} {len(v):6d} {sum(v) / len(v):9.1f} {sum(v) / 1e3:9.2f} {100 * sum(v) / total:6.2f}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="c5,c2,c3,c4", help="comma list of workloads to run")
+    ap.add_argument("--only", default="c5,c2,c3,c4", help="comma list of workloads to run (also: copy)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the attention traffic summary from two rocprofv3 --pmc output folders")
+    ap.add_argument("--trace-summary", metavar="DIR", help="print a per-kernel table from a rocprofv3 kernel trace")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the decoder step has no multi-GPU path)", file=sys.stderr, flush=True)
@@ -329,6 +469,8 @@ def main():
                                                               50, "7B-layer-decode-b32-ctx128..4096", 3)
     if "c4" in only:
         extra["prefill_4x512"] = bench_layer_prefill(torch, L, R, 20)
+    if "copy" in only:
+        bench_copy(torch)
     cpu = None
     if head is not None and not args.no_cpu:
         log("cpu_baseline: timing the oracle on a 4-sequence sample")
@@ -353,9 +495,11 @@ def main():
     if head:
         a = head["attn"]
         line["hbm_frac_step"] = head["hbm_frac"]
-        line["roofline"] = {"bound": "hbm", "kernel": "paged decode attention (one layer, 64 sequences)",
+        line["roofline"] = {"bound": "hbm",
+                            "kernel": "paged decode attention, one layer, 64 sequences (partition + combine kernels)",
                             "achieved": a["gbps"], "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                            "frac": a["gbps"] * 1e9 / HBM_PEAK, "traffic": None}
+                            "frac": a["gbps"] * 1e9 / HBM_PEAK, "traffic": read_traffic(a["bytes"]),
+                            "algorithmic_bytes": a["bytes"], "us_per_call": a["ms"] * 1e3}
     line["cpu_baseline"] = cpu
     line["sub_benchmarks"] = extra
     print(json.dumps(line), flush=True)

@@ -79,9 +79,11 @@ WsLayout ws_layout(const llmdec_config &c, int max_tokens, int max_seqs, int max
   L.attn_slots = (int)slots;
   // split-k partial sums: the worst case over every streamed product (rows <= 64) this workspace can see
   size_t part = 0;
-  const int shapes[5][2] = {{3 * h, h}, {h, h}, {2 * I, h}, {h, I}, {c.vocab, h}};
-  for (int m = 1; m <= std::min(rows, 64); ++m)
-    for (auto &sh : shapes) part = std::max(part, linear_partial_floats(m, sh[0], sh[1]));
+  const int shapes[4][2] = {{3 * h, h}, {h, h}, {2 * I, h}, {h, I}};
+  for (int m = 1; m <= std::min(rows, 64); ++m) {
+    for (auto &sh : shapes) part = std::max(part, linear_partial_floats(m, sh[0], sh[1], kSplitBalanced));
+    part = std::max(part, linear_partial_floats(m, c.vocab, h, kSplitUniform));  // lm_head
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -180,23 +182,23 @@ static void run_layer(const LayerArgs &a) {
 
   // attention block: x += Wo . attn(rope(Wq y), rope(Wk y), Wv y),  y = RMSNorm(x)
   launch_rmsnorm(a.hidden, h, nullptr, M, (const uint16_t *)a.w->attn_norm, M, h, c.rms_eps, err, nullptr, ah_hi,
-                 ah_lo, L.kpad_h, nullptr, 1, a.s);
+                 ah_lo, L.kpad_h, nullptr, Splits{}, a.s);
   LinearOut o_qkv;
   o_qkv.kind = kStore;
   o_qkv.f32 = qkv;
   o_qkv.ld = 3 * h;
   // a split q|k|v product leaves partial sums that the rotary/append kernel adds up
-  const int ks_qkv = launch_linear(ah, (const uint16_t *)a.w->w_qkv, 3 * h, h, o_qkv, part, L.part_floats, true, a.s);
-  const float *qkv_part = ks_qkv > 1 ? part : nullptr;
+  const Splits sp_qkv = launch_linear(ah, (const uint16_t *)a.w->w_qkv, 3 * h, h, o_qkv, part, L.part_floats, kSplitBalanced, a.s);
+  const float *qkv_part = sp_qkv.any() ? part : nullptr;
   if (a.decode) {
-    launch_rope_append(c, qkv, qkv_part, ks_qkv, 3 * h, M, a.n_seqs, nullptr, a.ctx, a.bt, a.max_pages, pk, pv,
+    launch_rope_append(c, qkv, qkv_part, sp_qkv, 3 * h, M, a.n_seqs, nullptr, a.ctx, a.bt, a.max_pages, pk, pv,
                        a.pool->num_pages, err, a.s);
     launch_decode_attention(c, qkv, 3 * h, M, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages,
                             at<float>(a.ws, L.attn_part), nullptr, ah_hi, ah_lo, L.kpad_h, err, a.s);
   } else {
     int32_t *ts = at<int32_t>(a.ws, L.tok_seq), *tp = at<int32_t>(a.ws, L.tok_pos);
     launch_token_map(a.cu, a.start, a.n_seqs, M, err, ts, tp, a.s);
-    launch_rope_append(c, qkv, qkv_part, ks_qkv, 3 * h, M, a.n_seqs, ts, tp, a.bt, a.max_pages, pk, pv,
+    launch_rope_append(c, qkv, qkv_part, sp_qkv, 3 * h, M, a.n_seqs, ts, tp, a.bt, a.max_pages, pk, pv,
                        a.pool->num_pages, err, a.s);
     launch_prefill_attention(c, qkv, 3 * h, a.n_seqs, M, a.max_q_len, a.cu, a.start, a.bt, a.max_pages, pk, pv,
                              a.pool->num_pages, nullptr, ah_hi, ah_lo, L.kpad_h, err, a.s);
@@ -206,22 +208,22 @@ static void run_layer(const LayerArgs &a) {
   o_res.f32 = a.hidden;
   o_res.ld = h;
   // a split output projection leaves partial sums that the MLP's RMSNorm adds into x before normalising
-  const int ks_o = launch_linear(ah, (const uint16_t *)a.w->w_o, h, h, o_res, part, L.part_floats, true, a.s);
+  const Splits sp_o = launch_linear(ah, (const uint16_t *)a.w->w_o, h, h, o_res, part, L.part_floats, kSplitBalanced, a.s);
 
   // MLP block: x += Wd (silu(Wg y) * (Wu y)),  y = RMSNorm(x); the gate/up product's epilogue forms the
   // SwiGLU activation directly
   launch_rmsnorm(a.hidden, h, nullptr, M, (const uint16_t *)a.w->mlp_norm, M, h, c.rms_eps, err, nullptr, ah_hi,
-                 ah_lo, L.kpad_h, ks_o > 1 ? part : nullptr, ks_o, a.s);
+                 ah_lo, L.kpad_h, sp_o.any() ? part : nullptr, sp_o, a.s);
   LinearOut o_gu;
   o_gu.kind = kSiluMul;
   o_gu.act_hi = ai_hi;
   o_gu.act_lo = ai_lo;
   o_gu.act_kt = L.kpad_i / kTileK;
   o_gu.act_cols = I;
-  const int ks_gu = launch_linear(ah, (const uint16_t *)a.w->w_gu, 2 * I, h, o_gu, part, L.part_floats, true, a.s);
-  if (ks_gu > 1) launch_reduce(part, ks_gu, M, 2 * I, o_gu, a.s);
-  const int ks_d = launch_linear(ai, (const uint16_t *)a.w->w_down, h, I, o_res, part, L.part_floats, true, a.s);
-  if (ks_d > 1) launch_reduce(part, ks_d, M, h, o_res, a.s);
+  const Splits sp_gu = launch_linear(ah, (const uint16_t *)a.w->w_gu, 2 * I, h, o_gu, part, L.part_floats, kSplitBalanced, a.s);
+  if (sp_gu.any()) launch_reduce(part, sp_gu, M, 2 * I, o_gu, a.s);
+  const Splits sp_d = launch_linear(ai, (const uint16_t *)a.w->w_down, h, I, o_res, part, L.part_floats, kSplitBalanced, a.s);
+  if (sp_d.any()) launch_reduce(part, sp_d, M, h, o_res, a.s);
 }
 
 }  // namespace llmdec
@@ -435,16 +437,16 @@ extern "C" llmdec_status llmdec_model_step_greedy(const llmdec_config *cfg, cons
   const int h = cfg->hidden;
   uint16_t *act_h = at<uint16_t>(ws, L.act_h), *act_hl = at<uint16_t>(ws, L.act_hl);
   launch_rmsnorm(x, h, decode ? nullptr : cu_seqlens, n_tokens, (const uint16_t *)w->final_norm, n_seqs, h,
-                 cfg->rms_eps, at<uint32_t>(ws, L.err), nullptr, act_h, act_hl, L.kpad_h, nullptr, 1, s);
+                 cfg->rms_eps, at<uint32_t>(ws, L.err), nullptr, act_h, act_hl, L.kpad_h, nullptr, Splits{}, s);
   float *lg = logits ? logits : at<float>(ws, L.logits);
   LinearOut o;
   o.kind = kStore;
   o.f32 = lg;
   o.ld = cfg->vocab;
   float *part = at<float>(ws, L.part);
-  const int ks = launch_linear(Act{act_h, act_hl, n_seqs, L.kpad_h, L.row_blocks}, (const uint16_t *)w->lm_head,
-                               cfg->vocab, h, o, part, L.part_floats, true, s);
-  if (ks > 1) launch_reduce(part, ks, n_seqs, cfg->vocab, o, s);
+  const Splits sp = launch_linear(Act{act_h, act_hl, n_seqs, L.kpad_h, L.row_blocks}, (const uint16_t *)w->lm_head,
+                                  cfg->vocab, h, o, part, L.part_floats, kSplitUniform, s);  // argmax ties
+  if (sp.any()) launch_reduce(part, sp, n_seqs, cfg->vocab, o, s);
   launch_argmax(lg, n_seqs, cfg->vocab, next_tokens, s);
   return check_launch(who);
 }
@@ -459,7 +461,7 @@ extern "C" llmdec_status llmdec_op_rmsnorm(const float *x, const void *gamma, in
     return set_error(LLMDEC_E_INVALID, "op_rmsnorm: rows=%d n=%d (a multiple of 32, <= 8192) ld_packed=%d out of range",
                      rows, n, ld_packed);
   launch_rmsnorm(const_cast<float *>(x), n, nullptr, rows, (const uint16_t *)gamma, rows, n, eps, nullptr, out_f32,
-                 (uint16_t *)out_hi, (uint16_t *)out_lo, ld_packed, nullptr, 1, (hipStream_t)stream);
+                 (uint16_t *)out_hi, (uint16_t *)out_lo, ld_packed, nullptr, Splits{}, (hipStream_t)stream);
   return check_launch("op_rmsnorm");
 }
 
@@ -469,7 +471,8 @@ static size_t op_linear_parts(int rows, int k, int n, size_t *act_off, size_t *p
   const size_t act = al((size_t)round_up(rows, 16) * kp * 2);
   *act_off = kWsHeader;
   *part_off = *act_off + 2 * act;
-  return *part_off + al(linear_partial_floats(rows, n, k) * sizeof(float));
+  return *part_off + al(std::max(linear_partial_floats(rows, n, k, kSplitBalanced),
+                                 linear_partial_floats(rows, n, k, kSplitUniform)) * sizeof(float));
 }
 
 extern "C" size_t llmdec_op_linear_ws_bytes(int32_t rows, int32_t k_dim, int32_t n_dim) {
@@ -480,7 +483,7 @@ extern "C" size_t llmdec_op_linear_ws_bytes(int32_t rows, int32_t k_dim, int32_t
 
 static llmdec_status run_op_linear(const char *who, const float *a, int32_t rows, int32_t k_dim, const void *w_packed,
                                    int32_t n_dim, const LinearOut &o, void *ws, size_t ws_bytes, size_t extra,
-                                   hipStream_t s) {
+                                   SplitPolicy policy, hipStream_t s) {
   size_t act_off, part_off;
   const size_t need = op_linear_parts(rows, k_dim, n_dim, &act_off, &part_off) + extra;
   llmdec_status st = check_ws(ws, ws_bytes, need, who);
@@ -490,9 +493,9 @@ static llmdec_status run_op_linear(const char *who, const float *a, int32_t rows
   uint16_t *lo = hi + (size_t)round_up(rows, 16) * kp;
   launch_split(a, k_dim, rows, k_dim, hi, lo, kp, s);
   float *part = at<float>(ws, part_off);
-  const int ks = launch_linear(Act{hi, lo, rows, kp, (rows + 15) / 16}, (const uint16_t *)w_packed, n_dim, k_dim, o,
-                               part, linear_partial_floats(rows, n_dim, k_dim), true, s);
-  if (ks > 1) launch_reduce(part, ks, rows, n_dim, o, s);
+  const Splits sp = launch_linear(Act{hi, lo, rows, kp, (rows + 15) / 16}, (const uint16_t *)w_packed, n_dim,
+                                  k_dim, o, part, linear_partial_floats(rows, n_dim, k_dim, policy), policy, s);
+  if (sp.any()) launch_reduce(part, sp, rows, n_dim, o, s);
   return LLMDEC_OK;
 }
 
@@ -507,7 +510,7 @@ extern "C" llmdec_status llmdec_op_linear(const float *a, int32_t rows, int32_t 
   o.kind = accumulate ? kAccumulate : kStore;
   o.f32 = out;
   o.ld = n_dim;
-  llmdec_status st = run_op_linear("op_linear", a, rows, k_dim, w_packed, n_dim, o, ws, ws_bytes, 0,
+  llmdec_status st = run_op_linear("op_linear", a, rows, k_dim, w_packed, n_dim, o, ws, ws_bytes, 0, kSplitBalanced,
                                    (hipStream_t)stream);
   return st != LLMDEC_OK ? st : check_launch("op_linear");
 }
@@ -527,6 +530,7 @@ extern "C" llmdec_status llmdec_op_swiglu_linear(const float *a, int32_t rows, i
   o.act_kt = ld_packed / kTileK;
   o.act_cols = inter;
   llmdec_status st = run_op_linear("op_swiglu_linear", a, rows, k_dim, w_gu_packed, 2 * inter, o, ws, ws_bytes, 0,
+                                   kSplitBalanced,
                                    (hipStream_t)stream);
   return st != LLMDEC_OK ? st : check_launch("op_swiglu_linear");
 }
@@ -545,7 +549,7 @@ extern "C" llmdec_status llmdec_op_rope_append(const llmdec_config *cfg, float *
     return set_error(LLMDEC_E_INVALID, "%s: n_tokens/n_seqs/max_pages out of range", who);
   uint16_t *pk, *pv;
   pool_layer(pool, layer, &pk, &pv);
-  launch_rope_append(*cfg, qkv, nullptr, 1, 3 * cfg->hidden, n_tokens, n_seqs, seq_of_token, pos_of_token, block_tables, max_pages, pk, pv,
+  launch_rope_append(*cfg, qkv, nullptr, Splits{}, 3 * cfg->hidden, n_tokens, n_seqs, seq_of_token, pos_of_token, block_tables, max_pages, pk, pv,
                      pool->num_pages, (uint32_t *)ws, (hipStream_t)stream);
   return check_launch(who);
 }
@@ -615,7 +619,8 @@ extern "C" llmdec_status llmdec_op_lm_head_argmax(const float *x, int32_t rows, 
   o.f32 = lg;
   o.ld = vocab;
   hipStream_t s = (hipStream_t)stream;
-  llmdec_status st = run_op_linear("op_lm_head_argmax", x, rows, hidden, lm_head_packed, vocab, o, ws, ws_bytes, extra, s);
+  llmdec_status st = run_op_linear("op_lm_head_argmax", x, rows, hidden, lm_head_packed, vocab, o, ws, ws_bytes, extra,
+                                   kSplitUniform, s);
   if (st != LLMDEC_OK) return st;
   launch_argmax(lg, rows, vocab, next, s);
   return check_launch("op_lm_head_argmax");

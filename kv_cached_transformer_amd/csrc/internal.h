@@ -45,6 +45,26 @@ struct LinearOut {
 };
 
 
+// How a streaming weight product left its result (a stream-K split).  Its work is the units
+// (column group, k-tile) -- groups of group_cols columns with kt k-tiles each, `units` in all, in
+// group-major order -- and block b of `blocks` takes units [b*units/blocks, (b+1)*units/blocks), so
+// every block gets the same amount whatever the shape.  Each (block, group) segment leaves one fp32
+// [rows][n] plane of partial sums: for a group's columns, plane j holds the j-th block covering the
+// group, and the planes are added in that order.  blocks == 0: no partials, the epilogue was applied.
+struct Splits {
+  int blocks = 0, units = 0, kt = 0, group_cols = 0;
+  __host__ __device__ bool any() const { return blocks > 0; }
+  // the block whose range holds unit u: the least b with floor((b+1)*units/blocks) > u
+  __host__ __device__ int first_block(long u) const {
+    return (int)(((u + 1) * (long)blocks + units - 1) / units) - 1;
+  }
+  // number of partial planes of the group holding column c
+  __host__ __device__ int slots(int c) const {
+    const long g = c / group_cols;
+    return first_block((g + 1) * (long)kt - 1) - first_block(g * (long)kt) + 1;
+  }
+};
+
 // Workspace layout for steps of up to max_tokens tokens and max_seqs sequences.
 struct WsLayout {
   size_t err, tok_seq, tok_pos, x, act_h, act_hl, act_i, act_il, qkv, part, attn_part, logits, total;
@@ -61,26 +81,31 @@ void launch_pack_matrix(int rows, int cols, const uint16_t *src, uint16_t *dst, 
 void launch_embed(const uint16_t *embed, const int32_t *tokens, int n_tokens, int hidden, int vocab, float *x,
                   uint32_t *err, hipStream_t s);
 // y = rmsnorm(x) * gamma on the given rows; outputs: f32 [rows][n] and/or the packed hi/lo pair with kpad
-// columns.  add_partials (may be NULL): ks fp32 [rows][n] partial sums that are first added into x (the
-// residual add of a split-k output projection), x being written back.
+// columns.  add_partials (may be NULL): the partial sums [plane][rows][n] of a split output projection
+// (described by sp), first added into x (its residual add), x being written back.
 void launch_rmsnorm(float *x, int ld_x, const int32_t *row_index, int n_src_rows, const uint16_t *gamma, int rows,
                     int n, float eps, uint32_t *err, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad,
-                    const float *add_partials, int ks, hipStream_t s);
+                    const float *add_partials, const Splits &sp, hipStream_t s);
 // fp32 [rows][ld] -> packed hi/lo pair [rows_pad16][kpad], zero padding.
 void launch_split(const float *a, int ld, int rows, int cols, uint16_t *hi, uint16_t *lo, int kpad, hipStream_t s);
-// Weight product.  When the product is split over k (ks > 1, returned), the result is left as ks fp32
-// partial sums [ks][rows][n] in partials and the epilogue is NOT applied: the caller reduces them, either
-// with launch_reduce or inside the next kernel.  ks == 1: the epilogue is applied.
-int launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const LinearOut &o, float *partials,
-                  size_t partial_floats, bool allow_split, hipStream_t s);
-// Sum ks partial products [ks][rows][n] and apply the epilogue o.
-void launch_reduce(const float *partials, int ks, int rows, int n, const LinearOut &o, hipStream_t s);
-size_t linear_partial_floats(int rows, int n, int k);
+// Weight product.  When the product is split (the returned Splits has any()), the result is left as fp32
+// partial sums [plane][rows][n] in partials and the epilogue is NOT applied: the caller reduces them, either
+// with launch_reduce or inside the next kernel.  Otherwise the epilogue is applied.
+// kSplitBalanced: every CU gets the same work, so split boundaries differ between column groups (and so,
+// in the last bits, does the summation order).  kSplitUniform: every column group is cut at the same k
+// boundaries, so equal weight rows give bit-equal outputs (what an argmax over the outputs needs for its
+// ties).  kSplitNone: one block per column group, epilogue applied.
+enum SplitPolicy { kSplitBalanced = 0, kSplitUniform = 1, kSplitNone = 2 };
+Splits launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const LinearOut &o, float *partials,
+                     size_t partial_floats, SplitPolicy policy, hipStream_t s);
+// Sum the partial products of a split product and apply the epilogue o.
+void launch_reduce(const float *partials, const Splits &sp, int rows, int n, const LinearOut &o, hipStream_t s);
+size_t linear_partial_floats(int rows, int n, int k, SplitPolicy policy = kSplitBalanced);
 void launch_token_map(const int32_t *cu_seqlens, const int32_t *start_pos, int n_seqs, int n_tokens, uint32_t *err, int32_t *tok_seq,
                       int32_t *tok_pos, hipStream_t s);
-// qkv_partials / ks: when the q|k|v product was split over k, its ks partial sums [ks][n_tokens][3*hidden]
-// are added first (and the sum written to qkv); NULL / 1 otherwise.
-void launch_rope_append(const llmdec_config &cfg, float *qkv, const float *qkv_partials, int ks, int ld_qkv,
+// qkv_partials / sp: when the q|k|v product was split, its partial sums [plane][n_tokens][3*hidden] are
+// added first (and the sum written to qkv); NULL otherwise.
+void launch_rope_append(const llmdec_config &cfg, float *qkv, const float *qkv_partials, const Splits &sp, int ld_qkv,
                         int n_tokens, int n_seqs, const int32_t *tok_seq,
                         const int32_t *tok_pos, const int32_t *block_tables, int max_pages, uint16_t *pool_layer_k,
                         uint16_t *pool_layer_v, int num_pages, uint32_t *err, hipStream_t s);

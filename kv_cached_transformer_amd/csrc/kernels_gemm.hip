@@ -89,8 +89,9 @@ template <int MB, int WN> struct SgShape {
   static constexpr int APW = WN > 1 ? (NA + WN - 1) / WN : NA;  // of them fetched by one wave
   // k-steps in flight per wave: as deep as about 230 registers allow (two waves per SIMD),
   // counting the ring, the activation operands read back from LDS and the accumulators
-  static constexpr int RAW = (230 - (WN > 1 ? 8 * MB : 0) - 16 * MB) / (4 * (SG_NB + APW));
-  static constexpr int D = RAW < 3 ? 3 : (RAW > 8 ? 8 : RAW);
+  static constexpr int RAW = (230 - (WN > 1 ? 8 * MB : 0) - 16 * MB) / (4 * (SG_NB + APW)) - 2;
+  static constexpr int D = RAW < 2 ? 2 : (RAW > 8 ? 8 : RAW);
+  static constexpr int R = D + 1;  // ring slots: D in flight + the one being computed
   static constexpr int NSLOT = APW * WN;  // staged tiles per k-tile: slots past NA hold unread copies
   static constexpr int STAGE_U4 = WN > 1 ? 2 * WK * NSLOT * 64 : 0;               // two stages of tiles
   static constexpr int RED_F = WK > 1 ? (WK - 1) * MB * 16 * (WN * 64 + 1) : 0;  // k-wave sums
@@ -101,40 +102,30 @@ template <int MB, int WN> struct SgShape {
 // matrix and k-tiles past the range are clamped to the last one and their
 // products skipped or dropped), and scheduling barriers keep the ring order,
 // so the compiler's wait counts follow the ring instead of draining it.
+//
+// Work is split stream-K (see Splits): block b walks its share of the
+// (column group, k-tile) units group by group; each group segment runs the
+// ring over its k-tiles and leaves either the finished result (no split) or
+// one plane of partial sums.
 template <int MB, int WN>
 __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__restrict__ a_hi,
                                                              const uint4 *__restrict__ a_lo, int a_kt, int rows,
                                                              const uint4 *__restrict__ w, int kt_count, int n_blocks,
-                                                             LinearOut o, float *__restrict__ partials) {
+                                                             LinearOut o, float *__restrict__ partials, Splits sp) {
   using S = SgShape<MB, WN>;
-  constexpr int WK = S::WK, NA = S::NA, APW = S::APW, D = S::D;
+  constexpr int WK = S::WK, NA = S::NA, APW = S::APW, D = S::D, R = S::R;
   constexpr bool SHARE = WN > 1;
   __shared__ uint4 lds[S::LDS_U4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar control
   const int cw = wave % WN, kw = wave / WN;
-  const int split = blockIdx.y, ks = gridDim.y;
-  const int nb0 = (blockIdx.x * WN + cw) * SG_NB;  // this wave's first row block of W
-  const int nbs = min(SG_NB, n_blocks - nb0);      // <= 0 for a wave past the matrix
-  const int kt0 = (int)((long)kt_count * split / ks), kt1 = (int)((long)kt_count * (split + 1) / ks);
-  const int n_it = (kt1 - kt0 + WK - 1) / WK;  // block-uniform; step i is k-tile kt0 + kw + WK*i
+  const int n = n_blocks * 16;
+  const int rq = (lane >> 4) * 4, cq = lane & 15;  // accumulator: lane l, element e -> row 4(l/16)+e, column l%16
 
-  f32x4 acc[MB][SG_NB];
-#pragma unroll
-  for (int m = 0; m < MB; ++m)
-#pragma unroll
-    for (int j = 0; j < SG_NB; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Scalar resources and offsets; the lane adds its own 16 bytes of a 1 KiB tile.
+  // Scalar resources and offsets; the lane adds its own 16 bytes of a 1 KiB tile.  Each resource spans
+  // only what the wave reads (its own row blocks; the MB row blocks of the activations), far below 2^31
+  // bytes, so the out-of-range marker below is always past its end.
   const uint32_t lane_bytes = (uint32_t)lane * 16u;
-  // Each resource spans only what the wave reads (its own row blocks; the MB row blocks of the
-  // activations), far below 2^31 bytes, so the out-of-range marker below is always past its end.
-  const int nbb = min(nb0, n_blocks - 1);
-  const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(w + (size_t)nbb * kt_count * 64, (size_t)(min(nb0 + SG_NB, n_blocks) - nbb) * kt_count * 1024);
-  uint32_t w_off[SG_NB];
-#pragma unroll
-  for (int j = 0; j < SG_NB; ++j) w_off[j] = (uint32_t)(min(nb0 + j, n_blocks - 1) - nbb) * (uint32_t)kt_count * 1024u;
   const size_t a_bytes = (size_t)MB * a_kt * 1024;
   const __amdgpu_buffer_rsrc_t hr = make_rsrc(a_hi, a_bytes), lr = make_rsrc(a_lo, a_bytes);
   // activation tiles this wave fetches: q = cw + WN*s (hi row block q, or lo row block q - MB)
@@ -147,123 +138,153 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__rest
     a_off[s] = (uint32_t)(q < MB ? q : q - MB) * (uint32_t)a_kt * 1024u;
   }
 
-  // A step past the wave's k-range (the k-waves' last steps, and the padding of the step count to a
-  // multiple of D) moves the lane offset past every resource's size: such loads read zeros without
-  // touching memory and their products add nothing, so the ring needs no branches.
-  uint4 wb[D][SG_NB], ab[D][APW];
-  auto issue = [&](int slot, int i) {
-    const int kt = kt0 + kw + WK * i;
-    const uint32_t voff = lane_bytes | (kt < kt1 ? 0u : 0x80000000u);
-    const uint32_t koff = (uint32_t)min(kt, kt1 - 1) * 1024u;
-#pragma unroll
-    for (int s = 0; s < APW; ++s) ab[slot][s] = buffer_load16(ar[s], voff, a_off[s] + koff, 0);
-#pragma unroll
-    for (int j = 0; j < SG_NB; ++j) wb[slot][j] = buffer_load16(wr, voff, w_off[j] + koff, kLoadStream);
-  };
-  auto compute = [&](int slot, int i) {
-    uint4 av[NA];  // hi of row block m at m, lo at MB + m
-    if constexpr (SHARE) {
-      // every wave writes all its slots (a skipped write would be a branch in the ring)
-      uint4 *st = lds + (size_t)((i & 1) * WK + kw) * S::NSLOT * 64;
-#pragma unroll
-      for (int s = 0; s < APW; ++s) st[(cw + WN * s) * 64 + lane] = ab[slot][s];
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < NA; ++q) av[q] = st[q * 64 + lane];
-    } else {
-#pragma unroll
-      for (int q = 0; q < NA; ++q) av[q] = ab[slot][q];
-    }
+  // this block's units; without a split every block is one whole column group
+  long u = sp.any() ? (long)blockIdx.x * sp.units / sp.blocks : (long)blockIdx.x * kt_count;
+  const long u_end = sp.any() ? (long)(blockIdx.x + 1) * sp.units / sp.blocks : u + kt_count;
+  while (u < u_end) {  // one segment per column group touched (block-uniform)
+    const int g = (int)(u / kt_count);
+    const int kt0 = (int)(u - (long)g * kt_count);
+    const int kt1 = (int)min((long)kt_count, u_end - (long)g * kt_count);
+    u = (long)g * kt_count + kt1;
+    const int nb0 = (g * WN + cw) * SG_NB;       // this wave's first row block of W
+    const int nbs = min(SG_NB, n_blocks - nb0);  // <= 0 for a wave past the matrix
+    const int n_it = (kt1 - kt0 + WK - 1) / WK;  // block-uniform; step i is k-tile kt0 + kw + WK*i
+
+    f32x4 acc[MB][SG_NB];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
-      for (int j = 0; j < SG_NB; ++j) {
-        acc[m][j] = mfma16(av[MB + m], wb[slot][j], acc[m][j]);
-        acc[m][j] = mfma16(av[m], wb[slot][j], acc[m][j]);
-      }
-  };
+      for (int j = 0; j < SG_NB; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nbb = min(nb0, n_blocks - 1);
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc(w + (size_t)nbb * kt_count * 64, (size_t)(min(nb0 + SG_NB, n_blocks) - nbb) * kt_count * 1024);
+    uint32_t w_off[SG_NB];
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    issue(d, d);
-    __builtin_amdgcn_sched_barrier(0);  // slots leave in ring order, so the waits stay partial
-  }
-  for (int it = 0; it < n_it; it += D) {  // block-uniform trip count; the final refills read nothing
+    for (int j = 0; j < SG_NB; ++j) w_off[j] = (uint32_t)(min(nb0 + j, n_blocks - 1) - nbb) * (uint32_t)kt_count * 1024u;
+
+    // A step past the segment's k-range (the k-waves' last steps, and the padding of the step count to
+    // a multiple of R) moves the lane offset past every resource's size: such loads read zeros without
+    // touching memory and their products add nothing, so the ring needs no branches.
+    uint4 wb[R][SG_NB], ab[R][APW];
+    auto issue = [&](int slot, int i) {
+      const int kt = kt0 + kw + WK * i;
+      const uint32_t voff = lane_bytes | (kt < kt1 ? 0u : 0x80000000u);
+      const uint32_t koff = (uint32_t)min(kt, kt1 - 1) * 1024u;
+#pragma unroll
+      for (int s = 0; s < APW; ++s) ab[slot][s] = buffer_load16(ar[s], voff, a_off[s] + koff, 0);
+#pragma unroll
+      for (int j = 0; j < SG_NB; ++j) wb[slot][j] = buffer_load16(wr, voff, w_off[j] + koff, kLoadStream);
+    };
+    auto compute = [&](int slot, int i) {
+      uint4 av[NA];  // hi of row block m at m, lo at MB + m
+      if constexpr (SHARE) {
+        // every wave writes all its slots (a skipped write would be a branch in the ring)
+        uint4 *st = lds + (size_t)((i & 1) * WK + kw) * S::NSLOT * 64;
+#pragma unroll
+        for (int s = 0; s < APW; ++s) st[(cw + WN * s) * 64 + lane] = ab[slot][s];
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < NA; ++q) av[q] = st[q * 64 + lane];
+      } else {
+#pragma unroll
+        for (int q = 0; q < NA; ++q) av[q] = ab[slot][q];
+      }
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int j = 0; j < SG_NB; ++j) {
+          acc[m][j] = mfma16(av[MB + m], wb[slot][j], acc[m][j]);
+          acc[m][j] = mfma16(av[m], wb[slot][j], acc[m][j]);
+        }
+    };
+    // R = D + 1 slots: each step first refills the slot freed by the previous step, then computes, so
+    // D steps stay in flight while one is computed
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      compute(d, it + d);
-      issue(d, it + D + d);
-      __builtin_amdgcn_sched_barrier(0);  // the scheduler would otherwise sink every refill to the end
+      issue(d, d);
+      __builtin_amdgcn_sched_barrier(0);  // slots leave in ring order, so the waits stay partial
     }
-  }
-
-  // accumulator layout: lane l, element e -> row 4(l/16)+e, column l%16 of each 16 x 16 block
-  const int rq = (lane >> 4) * 4, cq = lane & 15;
-  if constexpr (WK > 1) {  // k-waves 1.. hand their sums to k-wave 0, which adds them in order
-    constexpr int RW = WN * 64 + 1;
-    float *red = reinterpret_cast<float *>(lds);  // [WK-1][MB*16][RW], over the dead staging buffers
-    __syncthreads();
-    if (kw > 0) {
+    for (int it = 0; it < n_it; it += R) {  // block-uniform trip count; the final refills read nothing
 #pragma unroll
-      for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int j = 0; j < SG_NB; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            red[((kw - 1) * MB * 16 + m * 16 + rq + e) * RW + cw * 64 + j * 16 + cq] = acc[m][j][e];
-    }
-    __syncthreads();
-    if (kw != 0) return;
-#pragma unroll
-    for (int q = 0; q < WK - 1; ++q)
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int j = 0; j < SG_NB; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[m][j][e] += red[(q * MB * 16 + m * 16 + rq + e) * RW + cw * 64 + j * 16 + cq];
-  }
-  if (nbs <= 0) return;
-  const int n = n_blocks * 16;
-  if (ks > 1) {
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-      for (int j = 0; j < SG_NB; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = m * 16 + rq + e;
-          if (r < rows && j < nbs) partials[((size_t)split * rows + r) * n + (nb0 + j) * 16 + cq] = acc[m][j][e];
-        }
-    return;
-  }
-#pragma unroll
-  for (int m = 0; m < MB; ++m)
-#pragma unroll
-    for (int j = 0; j < SG_NB; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = m * 16 + rq + e, c = (nb0 + j) * 16 + cq;
-        if (r >= rows || j >= nbs) continue;
-        if (o.kind == kSiluMul) {
-          if ((j & 1) == 0) epi_store(o, r, c, acc[m][j][e], acc[m][j + 1][e]);
-        } else {
-          epi_store(o, r, c, acc[m][j][e], 0.f);
-        }
+      for (int d = 0; d < R; ++d) {
+        issue((d + D) % R, it + d + D);
+        compute(d, it + d);
+        __builtin_amdgcn_sched_barrier(0);  // the scheduler would otherwise sink every refill to the end
       }
+    }
+
+    if constexpr (WK > 1) {  // k-waves 1.. hand their sums to k-wave 0, which adds them in order
+      constexpr int RW = WN * 64 + 1;
+      float *red = reinterpret_cast<float *>(lds);  // [WK-1][MB*16][RW], over the dead staging buffers
+      __syncthreads();
+      if (kw > 0) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+          for (int j = 0; j < SG_NB; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              red[((kw - 1) * MB * 16 + m * 16 + rq + e) * RW + cw * 64 + j * 16 + cq] = acc[m][j][e];
+      }
+      __syncthreads();
+      if (kw == 0) {
+#pragma unroll
+        for (int q = 0; q < WK - 1; ++q)
+#pragma unroll
+          for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int j = 0; j < SG_NB; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[m][j][e] += red[(q * MB * 16 + m * 16 + rq + e) * RW + cw * 64 + j * 16 + cq];
+      }
+    }
+    if (kw == 0 && nbs > 0) {
+      if (sp.any()) {  // plane = this block's place among the blocks covering group g
+        float *plane = partials + (size_t)(blockIdx.x - sp.first_block((long)g * kt_count)) * rows * n;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+          for (int j = 0; j < SG_NB; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = m * 16 + rq + e;
+              if (r < rows && j < nbs) plane[(size_t)r * n + (nb0 + j) * 16 + cq] = acc[m][j][e];
+            }
+      } else {
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+          for (int j = 0; j < SG_NB; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = m * 16 + rq + e, c = (nb0 + j) * 16 + cq;
+              if (r >= rows || j >= nbs) continue;
+              if (o.kind == kSiluMul) {
+                if ((j & 1) == 0) epi_store(o, r, c, acc[m][j][e], acc[m][j + 1][e]);
+              } else {
+                epi_store(o, r, c, acc[m][j][e], 0.f);
+              }
+            }
+      }
+    }
+    if constexpr (SHARE || WK > 1) __syncthreads();  // the next segment reuses the LDS
+  }
 }
 
 // ---------------------------------------------------------------- split-k reduction
 // One thread per (row, 4 consecutive columns): sums the ks partials in split
 // order (deterministic) and applies the epilogue.  For SwiGLU the threads of
 // gate columns also read the matching up columns (16 further on).
-__global__ void reduce_kernel(const float *__restrict__ partials, int ks, int rows, int n, LinearOut o) {
+__global__ void reduce_kernel(const float *__restrict__ partials, Splits sp, int rows, int n, LinearOut o) {
   const int n4 = n >> 2;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (size_t)rows * n4) return;
   const int r = (int)(idx / n4), c = (int)(idx % n4) * 4;
   if (o.kind == kSiluMul && ((c >> 4) & 1)) return;
   const size_t plane = (size_t)rows * n;
+  const int ks = sp.slots(c);  // c..c+3 (and the up columns c+16..) lie in one column group
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f), u = s;
   add_splits(s, partials + (size_t)r * n + c, plane, ks);
   if (o.kind == kSiluMul) add_splits(u, partials + (size_t)r * n + c + 16, plane, ks);
@@ -273,9 +294,9 @@ __global__ void reduce_kernel(const float *__restrict__ partials, int ks, int ro
   epi_store(o, r, c + 3, s.w, u.w);
 }
 
-void launch_reduce(const float *partials, int ks, int rows, int n, const LinearOut &o, hipStream_t s) {
+void launch_reduce(const float *partials, const Splits &sp, int rows, int n, const LinearOut &o, hipStream_t s) {
   const size_t total = (size_t)rows * (n / 4);
-  if (total) reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(partials, ks, rows, n, o);
+  if (total) reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(partials, sp, rows, n, o);
 }
 
 // ---------------------------------------------------------------- tiled_gemm (rows > 64)
@@ -403,81 +424,95 @@ __global__ __launch_bounds__(256) void tiled_gemm_kernel(const uint4 *__restrict
 }
 
 // ---------------------------------------------------------------- dispatch
-// Shape of a streaming launch.  For each column-wave count (4, 2, 1: more
-// column waves, fewer activation requests per weight byte) the k split grows
-// while the grid stays within two blocks per CU, every wave keeps at least 8
-// k-steps to pipeline, and the partial sums (written and read back once) stay
-// within a quarter of the weight bytes.  The widest layout that still gives
-// every CU a block wins; failing that, the one with the most blocks.
+// Shape of a streaming launch: column waves WN and the stream-K split.  Every
+// CU gets exactly one block, so all carry the same work whatever the shape
+// (with 257..511 blocks some CUs would run two and set the time).  Preferred:
+// more column waves (fewer activation requests per weight byte), as long as
+// every wave keeps at least 8 k-steps to pipeline and the partial sums
+// (written and read back once) stay below the weight bytes.  Measured on the
+// 7B decode shapes, one block per CU beats two: a second block doubles the
+// partial sums for little gain in bandwidth.  A product too small to split
+// runs unsplit, one block per column group.
+constexpr int kCUs = 256;
+
 struct StreamPlan {
-  int wn, ks;
+  int wn, grid;
+  Splits sp;
 };
 
-static StreamPlan stream_plan(int rows, int n, int k, bool allow_split) {
+static StreamPlan stream_plan(int rows, int n, int k, SplitPolicy policy) {
   const int nb = n / 16, kt = round_up(k, kTileK) / kTileK;
-  StreamPlan best{1, 1};
-  long best_blocks = -1;
+  const double w_bytes = 2.0 * n * k;
   for (int wn : {4, 2, 1}) {
-    const int wk = 4 / wn;
-    const long groups = (nb + SG_NB * wn - 1) / (SG_NB * wn);
-    int ks = 1;
-    if (allow_split)
-      while (groups * (ks + 1) <= 512 && kt / (ks + 1) / wk >= 8 && 16L * (ks + 1) * rows <= (long)k) ++ks;
-    const long blocks = groups * ks;
-    if (blocks >= 256) return {wn, ks};
-    if (blocks > best_blocks) {
-      best = {wn, ks};
-      best_blocks = blocks;
+    if (policy == kSplitNone) break;
+    const int wk = 4 / wn, cols = SG_NB * 16 * wn;
+    const int groups = (nb + SG_NB * wn - 1) / (SG_NB * wn);
+    if (policy == kSplitBalanced) {
+      const long units = (long)groups * kt;
+      if (units / kCUs / wk < 8) continue;
+      if (8.0 * rows * cols * (kCUs + groups) > w_bytes) continue;
+      return {wn, kCUs, Splits{kCUs, (int)units, kt, cols}};
     }
+    // uniform: ks equal cuts per group, groups * ks <= one block per CU
+    if (groups > kCUs) continue;
+    int ks = kCUs / groups;
+    while (ks > 1 && kt / ks / wk < 8) --ks;
+    if (ks < 2 || 8.0 * rows * cols * groups * ks > w_bytes) continue;
+    return {wn, groups * ks, Splits{groups * ks, groups * kt, kt, cols}};
   }
-  return best;
+  // unsplit: the layout with the most blocks
+  return {1, (nb + SG_NB - 1) / SG_NB, Splits{}};
 }
 
-size_t linear_partial_floats(int rows, int n, int k) {
+size_t linear_partial_floats(int rows, int n, int k, SplitPolicy policy) {
   if (rows > 64) return 0;
-  const StreamPlan p = stream_plan(rows, n, k, true);
-  return p.ks > 1 ? (size_t)p.ks * rows * n : 0;
+  const StreamPlan p = stream_plan(rows, n, k, policy);
+  if (!p.sp.any()) return 0;
+  int max_slots = 1;
+  for (int c = 0; c < n; c += p.sp.group_cols) max_slots = std::max(max_slots, p.sp.slots(c));
+  return (size_t)max_slots * rows * n;
 }
 
 template <int MB>
-static void launch_stream(int wn, dim3 grid, hipStream_t s, const uint4 *ah, const uint4 *al, int a_kt, int rows,
-                          const uint4 *w, int kt_count, int n_blocks, const LinearOut &o, float *partials) {
+static void launch_stream(int wn, int grid, hipStream_t s, const uint4 *ah, const uint4 *al, int a_kt, int rows,
+                          const uint4 *w, int kt_count, int n_blocks, const LinearOut &o, float *partials,
+                          const Splits &sp) {
   if (wn == 4)
-    stream_gemm_kernel<MB, 4><<<grid, 256, 0, s>>>(ah, al, a_kt, rows, w, kt_count, n_blocks, o, partials);
+    stream_gemm_kernel<MB, 4><<<grid, 256, 0, s>>>(ah, al, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
   else if (wn == 2)
-    stream_gemm_kernel<MB, 2><<<grid, 256, 0, s>>>(ah, al, a_kt, rows, w, kt_count, n_blocks, o, partials);
+    stream_gemm_kernel<MB, 2><<<grid, 256, 0, s>>>(ah, al, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
   else
-    stream_gemm_kernel<MB, 1><<<grid, 256, 0, s>>>(ah, al, a_kt, rows, w, kt_count, n_blocks, o, partials);
+    stream_gemm_kernel<MB, 1><<<grid, 256, 0, s>>>(ah, al, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
 }
 
 #ifndef LLMDEC_TILED_DIRECT
 #define LLMDEC_TILED_DIRECT 0
 #endif
 
-int launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const LinearOut &o, float *partials,
-                  size_t partial_floats, bool allow_split, hipStream_t s) {
+Splits launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const LinearOut &o, float *partials,
+                     size_t partial_floats, SplitPolicy policy, hipStream_t s) {
   const int kt_count = round_up(k, kTileK) / kTileK;
   const int n_blocks = n / 16;
   const uint4 *w = reinterpret_cast<const uint4 *>(w_packed);
   const uint4 *ah = reinterpret_cast<const uint4 *>(a.hi), *al = reinterpret_cast<const uint4 *>(a.lo);
   const int a_kt = a.kpad / kTileK;
   if (a.rows <= 64) {
-    StreamPlan p = stream_plan(a.rows, n, k, allow_split);
-    if (p.ks > 1 && (!partials || partial_floats < (size_t)p.ks * a.rows * n)) p = stream_plan(a.rows, n, k, false);
-    const dim3 grid((n_blocks + SG_NB * p.wn - 1) / (SG_NB * p.wn), p.ks);
+    StreamPlan p = stream_plan(a.rows, n, k, policy);
+    if (p.sp.any() && (!partials || partial_floats < linear_partial_floats(a.rows, n, k, policy)))
+      p = stream_plan(a.rows, n, k, kSplitNone);
     switch ((a.rows + 15) / 16) {
-      case 1: launch_stream<1>(p.wn, grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
-      case 2: launch_stream<2>(p.wn, grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
-      case 3: launch_stream<3>(p.wn, grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
-      default: launch_stream<4>(p.wn, grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials); break;
+      case 1: launch_stream<1>(p.wn, p.grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
+      case 2: launch_stream<2>(p.wn, p.grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
+      case 3: launch_stream<3>(p.wn, p.grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
+      default: launch_stream<4>(p.wn, p.grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
     }
-    return p.ks;
+    return p.sp;
   }
   const int tiles_m = (a.rows + TG_MB * 16 - 1) / (TG_MB * 16);
   const int tiles_n = (n_blocks + TG_NB - 1) / TG_NB;
   tiled_gemm_kernel<LLMDEC_TILED_DIRECT><<<tiles_m * tiles_n, 256, TG_LDS, s>>>(ah, al, a_kt, a.row_blocks, a.rows, w,
                                                                                kt_count, n_blocks, tiles_m, o);
-  return 1;
+  return Splits{};
 }
 
 }  // namespace llmdec

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float *__restrict__ x, int
                                                       const uint16_t *__restrict__ gamma, int n, float eps,
                                                       uint32_t *err, float *out_f32, uint16_t *out_hi,
                                                       uint16_t *out_lo, int kpad, const float *__restrict__ add,
-                                                      int ks, int rows) {
+                                                      Splits sp, int rows) {
   const int r = blockIdx.x;
   int src_row = cu_last ? cu_last[r + 1] - 1 : r;
   if (src_row < 0 || src_row >= n_src_rows) {  // a bad cu_seqlens entry: flag it, read row 0 instead
@@ -90,6 +90,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float *__restrict__ x, int
       float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       if (add) {
         float4 a0 = make_float4(v[0], v[1], v[2], v[3]), a1 = make_float4(v[4], v[5], v[6], v[7]);
+        const int ks = sp.slots(c0);  // c0..c0+7 lie in one column group
         add_splits(a0, add + (size_t)r * n + c0, (size_t)rows * n, ks);
         add_splits(a1, add + (size_t)r * n + c0 + 4, (size_t)rows * n, ks);
         v[0] = a0.x, v[1] = a0.y, v[2] = a0.z, v[3] = a0.w, v[4] = a1.x, v[5] = a1.y, v[6] = a1.z, v[7] = a1.w;
@@ -144,10 +145,10 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float *__restrict__ x, int
 
 void launch_rmsnorm(float *x, int ld_x, const int32_t *cu_last, int n_src_rows, const uint16_t *gamma, int rows, int n,
                     float eps, uint32_t *err, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad,
-                    const float *add_partials, int ks, hipStream_t s) {
+                    const float *add_partials, const Splits &sp, hipStream_t s) {
   if (rows > 0)
     rmsnorm_kernel<<<rows, 256, 0, s>>>(x, ld_x, cu_last, n_src_rows, gamma, n, eps, err, out_f32, out_hi, out_lo,
-                                        kpad, add_partials, ks, rows);
+                                        kpad, add_partials, sp, rows);
 }
 
 // ---------------------------------------------------------------- fp32 -> packed hi/lo pair
@@ -209,7 +210,7 @@ struct RopeFreq {
 };
 
 __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qkv, const float *__restrict__ part,
-                                                          int ks, int ld_qkv, int n_tokens, int n_heads,
+                                                          Splits sp, int ld_qkv, int n_tokens, int n_heads,
                                                           int head_dim, RopeFreq fr, int n_seqs,
                                                           const int32_t *__restrict__ tok_seq,
                                                           const int32_t *__restrict__ tok_pos,
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
   auto row2 = [&](int col) -> float2 {
     if (!part) return *reinterpret_cast<const float2 *>(q + col);
     float2 acc = make_float2(0.f, 0.f);
-    add_splits(acc, part + (size_t)t * ld_qkv + col, (size_t)n_tokens * ld_qkv, ks);
+    add_splits(acc, part + (size_t)t * ld_qkv + col, (size_t)n_tokens * ld_qkv, sp.slots(col));
     return acc;
   };
   for (int g = g0 + threadIdx.x; g < min(n_heads * half, g0 + 256); g += 256) {
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
   }
 }
 
-void launch_rope_append(const llmdec_config &cfg, float *qkv, const float *qkv_partials, int ks, int ld_qkv,
+void launch_rope_append(const llmdec_config &cfg, float *qkv, const float *qkv_partials, const Splits &sp, int ld_qkv,
                         int n_tokens, int n_seqs, const int32_t *tok_seq, const int32_t *tok_pos,
                         const int32_t *block_tables, int max_pages, uint16_t *pool_k, uint16_t *pool_v, int num_pages,
                         uint32_t *err, hipStream_t s) {
@@ -283,7 +284,7 @@ void launch_rope_append(const llmdec_config &cfg, float *qkv, const float *qkv_p
   for (int i = 0; i < 64; ++i)
     fr.inv_freq[i] = i < cfg.head_dim / 2 ? pow((double)cfg.rope_theta, -2.0 * i / (double)cfg.head_dim) : 0.0;
   dim3 grid(n_tokens, (cfg.n_heads * (cfg.head_dim / 2) + 255) / 256);
-  rope_append_kernel<<<grid, 256, 0, s>>>(qkv, qkv_partials, qkv_partials ? ks : 1, ld_qkv, n_tokens, cfg.n_heads,
+  rope_append_kernel<<<grid, 256, 0, s>>>(qkv, qkv_partials, sp, ld_qkv, n_tokens, cfg.n_heads,
                                               cfg.head_dim, fr, n_seqs, tok_seq, tok_pos, block_tables, max_pages,
                                               pool_k, pool_v, num_pages, err);
 }

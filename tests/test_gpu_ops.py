@@ -83,7 +83,9 @@ def test_rmsnorm_eps_inside_root(L, R):
                                           (520, 4096, 11008, 1), (65, 22016, 4096, 0),
                                           # decode-product layouts (row blocks x column waves) not reached above
                                           (17, 512, 256, 0), (17, 512, 1024, 1), (33, 512, 11008, 1),
-                                          (33, 4096, 11008, 0), (32, 4096, 4096, 1), (48, 12288, 4096, 0)])
+                                          (33, 4096, 11008, 0), (32, 4096, 4096, 1), (48, 12288, 4096, 0),
+                                          # 257 row blocks: the last column group is ragged under a balanced split
+                                          (1, 4112, 4096, 0), (40, 4112, 4096, 1)])
 def test_linear(L, R, rows, n, k, acc):
     banner(f"linear rows={rows} n={n} k={k} acc={acc}")
     rng = np.random.default_rng(rows * 7 + n + k)

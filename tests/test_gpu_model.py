@@ -112,3 +112,67 @@ def test_tiny_model_greedy_generation(L, R):
         assert np.all(kimg.transpose(0, 2, 1, 3)[~written] == 0xFFFF)
         assert np.all(vimg.transpose(0, 3, 1, 2)[~written] == 0xFFFF)
     print(f"[parity] tiny generated ids {ids}", flush=True)
+
+
+def test_7b_shaped_model_decode_step(L, R):
+    """One greedy decode step of a 2-layer model at the 7B shapes (hidden 4096, 32 x 128 heads,
+    intermediate 11008, vocab 32000, untied lm_head) over 4 sequences whose cached contexts straddle
+    page boundaries: the embedding, both layers, the final norm, the 32000-column lm_head and the
+    argmax of llmdec_model_step_greedy against the oracle."""
+    banner("7B-shaped 2-layer model: one greedy decode step over 4 sequences")
+    W = 7
+    shape = synth.ModelShape(n_layers=2, hidden=4096, n_heads=32, n_kv_heads=32, head_dim=128,
+                             intermediate=11008, vocab=32000)
+    H, D = shape.n_kv_heads, shape.head_dim
+    mw = synth.model_weights(W, shape)
+    dm = DeviceModel(L, R, mw)
+    ctxs = [100, 300, 513, 1000]
+    B = len(ctxs)
+    totals = [c + 1 for c in ctxs]
+    max_pages = max(op.pages_needed(t) for t in totals) + 1
+    num_pages = sum(op.pages_needed(t) for t in totals)
+    order = synth.free_order(W, num_pages)
+    pool = R.Pool(dm.cfg, num_pages, order, fill_bits=0xFFFF)
+    bt = np.full((B, max_pages), -1, np.int32)
+    for s, t in enumerate(totals):
+        pool.alloc(t, bt[s], 0, max_pages)
+    kv = od.ContiguousKV(shape.n_layers, H, D)
+    for layer in range(shape.n_layers):
+        kimg = np.full((num_pages, H, 16, D), 0xFFFF, np.uint16)
+        vimg = np.full((num_pages, H, D, 16), 0xFFFF, np.uint16)
+        for s, c in enumerate(ctxs):
+            k, v = synth.kv_history(W, layer, s, c, H, D)
+            synth.scatter_kv_into_pool(kimg, vimg, bt[s], k, v)
+            kv.preload(layer, s, od.widen_bf16(k), od.widen_bf16(v))
+        kd, vd = pool.layer_views(layer)
+        kd.copy_(torch.from_numpy(kimg.view(np.int16)).to("cuda"))
+        vd.copy_(torch.from_numpy(R.Pool.v_raw(vimg).view(np.int16)).to("cuda"))
+    tokens = synth.first_tokens(W, B, shape.vocab)
+    toks, pos, bt_d = R.dev_i32(tokens), R.dev_i32(ctxs), R.dev_i32(bt)
+    ws = R.Workspace(L.llmdec_workspace_bytes(dm.cfg, B, B, max_pages))
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+    logits = torch.empty(B, shape.vocab, dtype=torch.float32, device="cuda")
+    L.llmdec_model_step_greedy(dm.cfg, dm.struct, B, B, 1, toks.data_ptr(), None, pos.data_ptr(), bt_d.data_ptr(),
+                               max_pages, pool.handle, nxt.data_ptr(), logits.data_ptr(), ws.ptr, ws.nbytes,
+                               R.stream())
+    torch.cuda.synchronize()
+    assert ws.error_bits() == 0
+    ref, seq_order = od.model_step(shape, mw, tokens, list(range(B)), ctxs, kv)
+    assert seq_order == list(range(B))
+    got = logits.cpu().numpy()
+    assert_close("7B-shaped model step logits", got, ref)
+    ids = nxt.cpu().numpy()
+    for s in range(B):
+        assert ids[s] == od.greedy_token(got[s])
+        if od.top2_gap(ref[s]) > 1e-2:
+            assert ids[s] == od.greedy_token(ref[s]), f"sequence {s}: device {ids[s]} oracle {od.greedy_token(ref[s])}"
+    # the step's own K/V went to each sequence's slot at position ctx, in both layers
+    for layer in range(shape.n_layers):
+        kd, vd = pool.layer_views(layer)
+        kimg, vimg = R.host_u16(kd.contiguous()), R.Pool.v_logical(R.host_u16(vd.contiguous()))
+        got_kv, ref_kv = [], []
+        for s, c in enumerate(ctxs):
+            pg, off = op.slot_of(bt[s], c)
+            got_kv += [f32_from_bf16(kimg[pg, :, off, :]), f32_from_bf16(vimg[pg, :, :, off])]
+            ref_kv += [kv.k[(layer, s)][c], kv.v[(layer, s)][c]]
+        assert_stored_bf16(f"7B-shaped model layer {layer} new K/V", np.stack(got_kv), np.stack(ref_kv))

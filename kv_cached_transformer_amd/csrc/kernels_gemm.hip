@@ -303,62 +303,62 @@ void launch_reduce(const float *partials, const Splits &sp, int rows, int n, con
 constexpr int TG_MB = 8;                               // 16-row blocks of A per block (128 rows)
 constexpr int TG_NB = 8;                               // 16-row blocks of W per block (128 columns)
 constexpr int TG_STAGE_TILES = TG_MB * 2 + TG_NB;      // A hi, A lo, W tiles of one k-tile: 24 KiB
+constexpr int TG_PER_WAVE = TG_STAGE_TILES / 4;        // tiles a wave stages per k-tile
+constexpr int TG_P = 3;                                // k-tiles of staged tiles in registers (ring)
 constexpr size_t TG_LDS = (size_t)2 * TG_STAGE_TILES * 1024;
 
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
-
-// Global source of tile q (0..23) of k-tile kt, or NULL when it lies outside the operands.
-__device__ inline const uint4 *tg_src(int q, int kt, int mb0, int nb0, int a_blocks, int n_blocks, int a_kt,
-                                      int kt_count, const uint4 *a_hi, const uint4 *a_lo, const uint4 *w) {
-  if (q < TG_MB) {
-    const int rb = mb0 + q;
-    return rb < a_blocks ? a_hi + ((size_t)rb * a_kt + kt) * 64 : nullptr;
-  }
-  if (q < 2 * TG_MB) {
-    const int rb = mb0 + q - TG_MB;
-    return rb < a_blocks ? a_lo + ((size_t)rb * a_kt + kt) * 64 : nullptr;
-  }
-  const int nb = nb0 + q - 2 * TG_MB;
-  return nb < n_blocks ? w + ((size_t)nb * kt_count + kt) * 64 : nullptr;
-}
-
-template <bool DIRECT>
-__global__ __launch_bounds__(256) void tiled_gemm_kernel(const uint4 *__restrict__ a_hi,
-                                                         const uint4 *__restrict__ a_lo, int a_kt, int a_blocks,
-                                                         int rows, const uint4 *__restrict__ w, int kt_count,
-                                                         int n_blocks, int tiles_m, LinearOut o) {
+// Staged pipeline.  Each k-tile's 24 tiles are fetched by the 4 waves (6 each) into a register ring
+// TG_P k-tiles deep, written to one of two LDS stages one k-tile before they are used, and read from
+// LDS by the waves that need them.  A k-tile's loads are thus issued TG_P - 1 compute phases before
+// they must have landed.  Every tile is read through a buffer resource of its own: a row block past
+// the operand gets an empty one, and k-tiles past the end move the lane offset out of range, so the
+// loads read zeros without branches and the padded steps add nothing.
+__global__ __launch_bounds__(256, 2) void tiled_gemm_kernel(const uint4 *__restrict__ a_hi,
+                                                            const uint4 *__restrict__ a_lo, int a_kt, int a_blocks,
+                                                            int rows, const uint4 *__restrict__ w, int kt_count,
+                                                            int n_blocks, int tiles_m, LinearOut o) {
   extern __shared__ uint4 lds[];  // [2 stages][24 tiles][64 lanes]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar control
   // XCD-aware order: block b runs on XCD b % 8; each XCD gets a contiguous run of tiles, row tiles innermost
   const int nblk = gridDim.x;
   int t = blockIdx.x;
   if ((nblk & 7) == 0) t = (t & 7) * (nblk >> 3) + (t >> 3);
   const int tm = t % tiles_m, tn = t / tiles_m;
   const int mb0 = tm * TG_MB, nb0 = tn * TG_NB;
-  constexpr int PER_WAVE = TG_STAGE_TILES / 4;  // 6 tiles per wave per stage
 
-  uint4 stage_regs[PER_WAVE];
-  auto fetch = [&](int kt) {  // global -> registers (staged variant)
+  // this wave's staged tiles q = wave + 4i: A hi row block q, A lo row block q - 8, W row block q - 16
+  const uint32_t lane_bytes = (uint32_t)lane * 16u;
+  __amdgpu_buffer_rsrc_t src[TG_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const uint4 *src = tg_src(wave + 4 * i, kt, mb0, nb0, a_blocks, n_blocks, a_kt, kt_count, a_hi, a_lo, w);
-      stage_regs[i] = src ? src[lane] : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < TG_PER_WAVE; ++i) {
+    const int q = wave + 4 * i;
+    const uint4 *base;
+    bool ok;
+    if (q < TG_MB) {
+      ok = mb0 + q < a_blocks;
+      base = a_hi + (size_t)(ok ? mb0 + q : 0) * a_kt * 64;
+    } else if (q < 2 * TG_MB) {
+      ok = mb0 + q - TG_MB < a_blocks;
+      base = a_lo + (size_t)(ok ? mb0 + q - TG_MB : 0) * a_kt * 64;
+    } else {
+      ok = nb0 + q - 2 * TG_MB < n_blocks;
+      base = w + (size_t)(ok ? nb0 + q - 2 * TG_MB : 0) * kt_count * 64;
     }
-  };
-  auto store = [&](int buf) {  // registers -> LDS
-    uint4 *base = lds + (size_t)buf * TG_STAGE_TILES * 64;
+    src[i] = make_rsrc(base, ok ? (size_t)(q < 2 * TG_MB ? a_kt : kt_count) * 1024 : 0);
+  }
+  uint4 rg[TG_P][TG_PER_WAVE];
+  auto fetch = [&](int slot, int kt) {
+    const uint32_t voff = lane_bytes | (kt < kt_count ? 0u : 0x80000000u);
+    const uint32_t koff = (uint32_t)min(kt, kt_count - 1) * 1024u;
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) base[(size_t)(wave + 4 * i) * 64 + lane] = stage_regs[i];
+    for (int i = 0; i < TG_PER_WAVE; ++i)
+      rg[slot][i] = buffer_load16(src[i], voff, koff, 0);  // both operands are reused through L2
   };
-  auto direct = [&](int kt, int buf) {  // global -> LDS without registers
-    uint4 *base = lds + (size_t)buf * TG_STAGE_TILES * 64;
+  auto stage = [&](int slot, int buf) {
+    uint4 *st = lds + (size_t)buf * TG_STAGE_TILES * 64;
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int q = wave + 4 * i;
-      const uint4 *src = tg_src(q, kt, mb0, nb0, a_blocks, n_blocks, a_kt, kt_count, a_hi, a_lo, w);
-      if (src)
-        __builtin_amdgcn_global_load_lds((const void *)(src + lane), (lds_ptr_t)(base + (size_t)q * 64), 16, 0, 0);
-    }
+    for (int i = 0; i < TG_PER_WAVE; ++i) st[(size_t)(wave + 4 * i) * 64 + lane] = rg[slot][i];
   };
 
   const int wm = wave >> 1, wn = wave & 1;  // wave owns A row blocks wm*4.. and W row blocks wn*4..
@@ -367,22 +367,7 @@ __global__ __launch_bounds__(256) void tiled_gemm_kernel(const uint4 *__restrict
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (DIRECT) {
-    direct(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-  } else {
-    fetch(0);
-    store(0);
-  }
-  __syncthreads();
-  int buf = 0;
-  for (int kt = 0; kt < kt_count; ++kt) {
-    const bool more = kt + 1 < kt_count;
-    if (more) {
-      if (DIRECT) direct(kt + 1, buf ^ 1);
-      else fetch(kt + 1);
-    }
+  auto compute = [&](int buf) {
     const uint4 *st = lds + (size_t)buf * TG_STAGE_TILES * 64;
     uint4 ah[4], al[4], bv[4];
 #pragma unroll
@@ -399,12 +384,30 @@ __global__ __launch_bounds__(256) void tiled_gemm_kernel(const uint4 *__restrict
         acc[i][j] = mfma16(al[i], bv[j], acc[i][j]);
         acc[i][j] = mfma16(ah[i], bv[j], acc[i][j]);
       }
-    if (more) {
-      if (DIRECT) __builtin_amdgcn_s_waitcnt(0);
-      else store(buf ^ 1);
+  };
+
+  // prologue: k-tiles 0..TG_P-1 in flight; k-tile 0 staged and its slot refilled with k-tile TG_P
+  // (k-tile j always lives in slot j % TG_P)
+#pragma unroll
+  for (int p = 0; p < TG_P; ++p) {
+    fetch(p, p);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  stage(0, 0);
+  fetch(0, TG_P);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  // step kt: compute k-tile kt from LDS, stage k-tile kt+1 into the other buffer, refetch its register slot
+  for (int k0 = 0; k0 < kt_count; k0 += TG_P) {  // block-uniform; steps past kt_count compute zeros
+#pragma unroll
+    for (int d = 0; d < TG_P; ++d) {
+      const int kt = k0 + d;
+      compute(kt & 1);
+      stage((d + 1) % TG_P, (kt + 1) & 1);
+      fetch((d + 1) % TG_P, kt + 1 + TG_P);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
-    buf ^= 1;
   }
 
   const int rq = (lane >> 4) * 4, cq = lane & 15;
@@ -485,10 +488,6 @@ static void launch_stream(int wn, int grid, hipStream_t s, const uint4 *ah, cons
     stream_gemm_kernel<MB, 1><<<grid, 256, 0, s>>>(ah, al, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
 }
 
-#ifndef LLMDEC_TILED_DIRECT
-#define LLMDEC_TILED_DIRECT 0
-#endif
-
 Splits launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const LinearOut &o, float *partials,
                      size_t partial_floats, SplitPolicy policy, hipStream_t s) {
   const int kt_count = round_up(k, kTileK) / kTileK;
@@ -510,8 +509,8 @@ Splits launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const
   }
   const int tiles_m = (a.rows + TG_MB * 16 - 1) / (TG_MB * 16);
   const int tiles_n = (n_blocks + TG_NB - 1) / TG_NB;
-  tiled_gemm_kernel<LLMDEC_TILED_DIRECT><<<tiles_m * tiles_n, 256, TG_LDS, s>>>(ah, al, a_kt, a.row_blocks, a.rows, w,
-                                                                               kt_count, n_blocks, tiles_m, o);
+  tiled_gemm_kernel<<<tiles_m * tiles_n, 256, TG_LDS, s>>>(ah, al, a_kt, a.row_blocks, a.rows, w, kt_count, n_blocks,
+                                                           tiles_m, o);
   return Splits{};
 }
 

@@ -67,6 +67,14 @@ def assert_stored_bf16(tag, got, ref, eps=1e-3, max_flip_frac=0.1):
     flips = int((got != ref).sum())
     print(f"[parity] {tag}: {got.size} stored bf16 values, {flips} differ from the oracle's rounding "
           f"(max |diff| {float(np.abs(got - ref).max()) if got.size else 0:.3e})", flush=True)
+    if bad.any():
+        excess = np.where(bad, np.abs(got - ref) - bound, -np.inf)
+        for flat in np.argsort(excess, axis=None)[::-1][:8]:
+            i = np.unravel_index(flat, got.shape)
+            if not bad[i]:
+                break
+            print(f"[parity] {tag}: at {tuple(int(j) for j in i)} got {got[i]!r} ref {ref[i]!r} "
+                  f"bound {bound[i]:.3e}", flush=True)
     assert not bad.any(), f"{tag}: {int(bad.sum())} stored values beyond half an ulp + {eps}"
     assert flips <= max(4, max_flip_frac * got.size), f"{tag}: {flips} roundings differ"
     rl = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))

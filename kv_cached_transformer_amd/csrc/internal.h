@@ -122,6 +122,7 @@ void launch_prefill_attention(const llmdec_config &cfg, const float *q, int ld_q
 // u = silu(g) * up elementwise, fp32 [rows][n] (the stand-alone operation; the layer steps fuse it
 // into the gate/up product's epilogue).
 void launch_silu_mul(const float *g, const float *u, int rows, int n, float *out, hipStream_t s);
+// Row-wise argmax of fp32 [rows][vocab], lowest index on ties; vocab a multiple of 4 (the API requires 16).
 void launch_argmax(const float *logits, int rows, int vocab, int32_t *next, hipStream_t s);
 void launch_gather_kv(const uint16_t *pool_layer_k, const uint16_t *pool_layer_v, int num_pages, int n_heads,
                       int head_dim, const int32_t *row, int n_tokens, uint16_t *k_out, uint16_t *v_out,

@@ -305,17 +305,34 @@ void launch_silu_mul(const float *g, const float *u, int rows, int n, float *out
 }
 
 // ---------------------------------------------------------------- greedy argmax ([F] §2.2.3)
-// Largest logit per row; among equal values the lowest index wins.
-__global__ __launch_bounds__(256) void argmax_kernel(const float *__restrict__ logits, int vocab, int32_t *next) {
+// Largest logit per row; among equal values the lowest index wins.  One 1024-thread block per row:
+// every thread has its four 16-byte loads per pass in flight at once, so a 32000-logit row is read
+// in one or two memory latencies.  vocab is a multiple of 16 (the lm_head is tiled by 16 rows), so
+// rows are 16-byte aligned.
+constexpr int kArgmaxThreads = 1024;
+__global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(const float *__restrict__ logits, int vocab,
+                                                                int32_t *next) {
   const int r = blockIdx.x;
-  const float *x = logits + (size_t)r * vocab;
+  const float4 *x4 = reinterpret_cast<const float4 *>(logits + (size_t)r * vocab);
+  const int n4 = vocab >> 2;
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i = threadIdx.x; i < vocab; i += 256) {
-    const float v = x[i];
-    if (v > best) {  // ascending i per thread: strict > keeps the first
-      best = v;
-      bi = i;
+  // indices visited per thread are ascending, so a strict > keeps the first of equal values
+  for (int i0 = threadIdx.x; i0 < n4; i0 += 4 * kArgmaxThreads) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = x4[min(i0 + u * kArgmaxThreads, n4 - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kArgmaxThreads;
+      if (i >= n4) break;
+      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (e[j] > best) {
+          best = e[j];
+          bi = 4 * i + j;
+        }
     }
   }
 #pragma unroll
@@ -327,15 +344,16 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float *__restrict__ l
       bi = oi;
     }
   }
-  __shared__ float bv[4];
-  __shared__ int bix[4];
+  constexpr int NW = kArgmaxThreads / 64;
+  __shared__ float bv[NW];
+  __shared__ int bix[NW];
   if ((threadIdx.x & 63) == 0) {
     bv[threadIdx.x >> 6] = best;
     bix[threadIdx.x >> 6] = bi;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w)
+    for (int w = 1; w < NW; ++w)
       if (bv[w] > best || (bv[w] == best && bix[w] < bi)) {
         best = bv[w];
         bi = bix[w];
@@ -345,7 +363,7 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float *__restrict__ l
 }
 
 void launch_argmax(const float *logits, int rows, int vocab, int32_t *next, hipStream_t s) {
-  if (rows > 0) argmax_kernel<<<rows, 256, 0, s>>>(logits, vocab, next);
+  if (rows > 0 && vocab > 0 && vocab % 4 == 0) argmax_kernel<<<rows, kArgmaxThreads, 0, s>>>(logits, vocab, next);
 }
 
 // ---------------------------------------------------------------- test-only gather

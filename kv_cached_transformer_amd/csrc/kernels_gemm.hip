@@ -300,111 +300,127 @@ void launch_reduce(const float *partials, const Splits &sp, int rows, int n, con
 }
 
 // ---------------------------------------------------------------- tiled_gemm (rows > 64)
-constexpr int TG_MB = 8;                               // 16-row blocks of A per block (128 rows)
-constexpr int TG_NB = 8;                               // 16-row blocks of W per block (128 columns)
-constexpr int TG_STAGE_TILES = TG_MB * 2 + TG_NB;      // A hi, A lo, W tiles of one k-tile: 24 KiB
-constexpr int TG_PER_WAVE = TG_STAGE_TILES / 4;        // tiles a wave stages per k-tile
-constexpr int TG_P = 3;                                // k-tiles of staged tiles in registers (ring)
-constexpr size_t TG_LDS = (size_t)2 * TG_STAGE_TILES * 1024;
-
-// Staged pipeline.  Each k-tile's 24 tiles are fetched by the 4 waves (6 each) into a register ring
-// TG_P k-tiles deep, written to one of two LDS stages one k-tile before they are used, and read from
-// LDS by the waves that need them.  A k-tile's loads are thus issued TG_P - 1 compute phases before
-// they must have landed.  Every tile is read through a buffer resource of its own: a row block past
-// the operand gets an empty one, and k-tiles past the end move the lane offset out of range, so the
+// Block tile MB x 16 rows by 256 columns.  The four waves sit side by side along the columns: wave w
+// owns all MB row blocks and column blocks 4w..4w+3 (4 MB accumulators of 16 x 16).  Per k-tile the
+// block needs 2 MB activation tiles (hi and lo of each row block), which every wave uses, and 16
+// weight tiles, each used by one wave only.  So activations are shared through LDS (each wave fetches
+// a quarter of them and writes them to one of two LDS stages a k-tile before they are used), while
+// weights go from memory straight into the registers of the wave that uses them.  Both sit in a
+// register ring PgShape::D k-tiles deep.  Two blocks share a CU, so one block's MFMAs run while the
+// other waits at its barrier or on memory.  Every tile is read through a buffer resource: a row block
+// past the operand gets an empty one, k-tiles past the end move the lane offset out of range, so those
 // loads read zeros without branches and the padded steps add nothing.
+constexpr int PG_NBW = 4;          // 16-row blocks of W per wave
+constexpr int PG_NB = 4 * PG_NBW;  // per block (256 columns)
+template <int MB> struct PgShape {
+  static constexpr int AT = 2 * MB;                  // activation tiles per k-tile (hi and lo)
+  static constexpr int APW = AT / 4;                 // of them fetched by one wave
+  static constexpr int D = MB == 8 ? 2 : 4;          // k-tiles in flight, as the registers allow
+  static constexpr int GM = 32 / MB;                 // row tiles per group of the block order (512 rows)
+  static constexpr size_t LDS = (size_t)2 * AT * 1024;
+};
+
+template <int MB>
 __global__ __launch_bounds__(256, 2) void tiled_gemm_kernel(const uint4 *__restrict__ a_hi,
                                                             const uint4 *__restrict__ a_lo, int a_kt, int a_blocks,
                                                             int rows, const uint4 *__restrict__ w, int kt_count,
                                                             int n_blocks, int tiles_m, LinearOut o) {
-  extern __shared__ uint4 lds[];  // [2 stages][24 tiles][64 lanes]
+  using S = PgShape<MB>;
+  constexpr int AT = S::AT, APW = S::APW, D = S::D;
+  extern __shared__ uint4 lds[];  // [2 stages][AT tiles][64 lanes]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar control
-  // XCD-aware order: block b runs on XCD b % 8; each XCD gets a contiguous run of tiles, row tiles innermost
+  // Block order: blocks go round-robin to the 8 XCDs, so each XCD takes a contiguous range of tile ids;
+  // ids run through groups of GM row tiles, row tiles innermost, so the blocks one XCD runs together
+  // share a few activation and weight slabs in its L2.
   const int nblk = gridDim.x;
   int t = blockIdx.x;
   if ((nblk & 7) == 0) t = (t & 7) * (nblk >> 3) + (t >> 3);
-  const int tm = t % tiles_m, tn = t / tiles_m;
-  const int mb0 = tm * TG_MB, nb0 = tn * TG_NB;
+  const int tiles_n = nblk / tiles_m;  // the grid is exactly tiles_m * tiles_n
+  const int group = t / (S::GM * tiles_n), first_m = group * S::GM;
+  const int gm = min(S::GM, tiles_m - first_m);
+  const int r_in = t - group * S::GM * tiles_n;
+  const int tm = first_m + r_in % gm, tn = r_in / gm;
+  const int mb0 = tm * MB, nbw0 = tn * PG_NB + wave * PG_NBW;
 
-  // this wave's staged tiles q = wave + 4i: A hi row block q, A lo row block q - 8, W row block q - 16
+  // activation tiles this wave fetches: q = wave + 4i is the hi tile of row block q (q < MB) or the lo
+  // tile of row block q - MB; LDS holds tile q at index q
   const uint32_t lane_bytes = (uint32_t)lane * 16u;
-  __amdgpu_buffer_rsrc_t src[TG_PER_WAVE];
+  __amdgpu_buffer_rsrc_t asrc[APW];
 #pragma unroll
-  for (int i = 0; i < TG_PER_WAVE; ++i) {
+  for (int i = 0; i < APW; ++i) {
     const int q = wave + 4 * i;
-    const uint4 *base;
-    bool ok;
-    if (q < TG_MB) {
-      ok = mb0 + q < a_blocks;
-      base = a_hi + (size_t)(ok ? mb0 + q : 0) * a_kt * 64;
-    } else if (q < 2 * TG_MB) {
-      ok = mb0 + q - TG_MB < a_blocks;
-      base = a_lo + (size_t)(ok ? mb0 + q - TG_MB : 0) * a_kt * 64;
-    } else {
-      ok = nb0 + q - 2 * TG_MB < n_blocks;
-      base = w + (size_t)(ok ? nb0 + q - 2 * TG_MB : 0) * kt_count * 64;
-    }
-    src[i] = make_rsrc(base, ok ? (size_t)(q < 2 * TG_MB ? a_kt : kt_count) * 1024 : 0);
+    const int rb = mb0 + (q % MB);
+    const bool ok = rb < a_blocks;
+    const uint4 *base = (q < MB ? a_hi : a_lo) + (size_t)(ok ? rb : 0) * a_kt * 64;
+    asrc[i] = make_rsrc(base, ok ? (size_t)a_kt * 1024 : 0);
   }
-  uint4 rg[TG_P][TG_PER_WAVE];
+  // this wave's weight row blocks nbw0.. through one resource (empty past the matrix; a block past the
+  // last one re-reads the last, and its columns are not stored)
+  const int nbv = min(PG_NBW, n_blocks - nbw0);
+  const __amdgpu_buffer_rsrc_t wsrc =
+      make_rsrc(w + (size_t)(nbv > 0 ? nbw0 : 0) * kt_count * 64, nbv > 0 ? (size_t)nbv * kt_count * 1024 : 0);
+  uint32_t w_off[PG_NBW];
+#pragma unroll
+  for (int j = 0; j < PG_NBW; ++j) w_off[j] = (uint32_t)min(j, max(nbv - 1, 0)) * (uint32_t)kt_count * 1024u;
+
+  uint4 ar[D][APW], wr[D][PG_NBW];
   auto fetch = [&](int slot, int kt) {
     const uint32_t voff = lane_bytes | (kt < kt_count ? 0u : 0x80000000u);
     const uint32_t koff = (uint32_t)min(kt, kt_count - 1) * 1024u;
 #pragma unroll
-    for (int i = 0; i < TG_PER_WAVE; ++i)
-      rg[slot][i] = buffer_load16(src[i], voff, koff, 0);  // both operands are reused through L2
+    for (int i = 0; i < APW; ++i) ar[slot][i] = buffer_load16(asrc[i], voff, koff, 0);  // reused through L2
+#pragma unroll
+    for (int j = 0; j < PG_NBW; ++j) wr[slot][j] = buffer_load16(wsrc, voff, w_off[j] + koff, 0);
   };
   auto stage = [&](int slot, int buf) {
-    uint4 *st = lds + (size_t)buf * TG_STAGE_TILES * 64;
+    uint4 *st = lds + (size_t)buf * AT * 64;
 #pragma unroll
-    for (int i = 0; i < TG_PER_WAVE; ++i) st[(size_t)(wave + 4 * i) * 64 + lane] = rg[slot][i];
+    for (int i = 0; i < APW; ++i) st[(size_t)(wave + 4 * i) * 64 + lane] = ar[slot][i];
   };
 
-  const int wm = wave >> 1, wn = wave & 1;  // wave owns A row blocks wm*4.. and W row blocks wn*4..
-  f32x4 acc[4][4];
+  f32x4 acc[MB][PG_NBW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int m = 0; m < MB; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int buf) {
-    const uint4 *st = lds + (size_t)buf * TG_STAGE_TILES * 64;
-    uint4 ah[4], al[4], bv[4];
+    for (int j = 0; j < PG_NBW; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, int slot) {
+    const uint4 *st = lds + (size_t)buf * AT * 64;
+    uint4 ah[MB], al[MB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ah[i] = st[(size_t)(wm * 4 + i) * 64 + lane];
-      al[i] = st[(size_t)(TG_MB + wm * 4 + i) * 64 + lane];
+    for (int m = 0; m < MB; ++m) {
+      ah[m] = st[(size_t)m * 64 + lane];
+      al[m] = st[(size_t)(MB + m) * 64 + lane];
     }
+    // the lo and hi products of one accumulator are four instructions apart
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = st[(size_t)(2 * TG_MB + wn * 4 + j) * 64 + lane];
+    for (int m = 0; m < MB; ++m) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < PG_NBW; ++j) acc[m][j] = mfma16(al[m], wr[slot][j], acc[m][j]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[i][j] = mfma16(al[i], bv[j], acc[i][j]);
-        acc[i][j] = mfma16(ah[i], bv[j], acc[i][j]);
-      }
+      for (int j = 0; j < PG_NBW; ++j) acc[m][j] = mfma16(ah[m], wr[slot][j], acc[m][j]);
+    }
   };
 
-  // prologue: k-tiles 0..TG_P-1 in flight; k-tile 0 staged and its slot refilled with k-tile TG_P
-  // (k-tile j always lives in slot j % TG_P)
+  // prologue: k-tiles 0..D-1 in flight (k-tile j always lives in slot j % D), k-tile 0's
+  // activations staged
 #pragma unroll
-  for (int p = 0; p < TG_P; ++p) {
+  for (int p = 0; p < D; ++p) {
     fetch(p, p);
     __builtin_amdgcn_sched_barrier(0);
   }
   stage(0, 0);
-  fetch(0, TG_P);
   __syncthreads();
   __builtin_amdgcn_sched_barrier(0);
-  // step kt: compute k-tile kt from LDS, stage k-tile kt+1 into the other buffer, refetch its register slot
-  for (int k0 = 0; k0 < kt_count; k0 += TG_P) {  // block-uniform; steps past kt_count compute zeros
+  // step kt: compute k-tile kt (activations from LDS stage kt & 1, weights from slot kt % D), stage
+  // k-tile kt+1's activations into the other stage, refill the consumed slot with k-tile kt + D
+  for (int k0 = 0; k0 < kt_count; k0 += D) {  // block-uniform; steps past kt_count compute zeros
 #pragma unroll
-    for (int d = 0; d < TG_P; ++d) {
+    for (int d = 0; d < D; ++d) {
       const int kt = k0 + d;
-      compute(kt & 1);
-      stage((d + 1) % TG_P, (kt + 1) & 1);
-      fetch((d + 1) % TG_P, kt + 1 + TG_P);
+      compute(kt & 1, d);
+      stage((d + 1) % D, (kt + 1) & 1);
+      fetch(d, kt + D);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -412,16 +428,16 @@ __global__ __launch_bounds__(256, 2) void tiled_gemm_kernel(const uint4 *__restr
 
   const int rq = (lane >> 4) * 4, cq = lane & 15;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int m = 0; m < MB; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int nb = nb0 + wn * 4 + j;
+    for (int j = 0; j < PG_NBW; ++j) {
+      const int nb = nbw0 + j;
       if (nb >= n_blocks) continue;
       if (o.kind == kSiluMul && (j & 1)) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = (mb0 + wm * 4 + i) * 16 + rq + e;
-        if (r < rows) epi_store(o, r, nb * 16 + cq, acc[i][j][e], o.kind == kSiluMul ? acc[i][j + 1][e] : 0.f);
+        const int r = (mb0 + m) * 16 + rq + e;
+        if (r < rows) epi_store(o, r, nb * 16 + cq, acc[m][j][e], o.kind == kSiluMul ? acc[m][j + 1][e] : 0.f);
       }
     }
 }
@@ -507,10 +523,17 @@ Splits launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const
     }
     return p.sp;
   }
-  const int tiles_m = (a.rows + TG_MB * 16 - 1) / (TG_MB * 16);
-  const int tiles_n = (n_blocks + TG_NB - 1) / TG_NB;
-  tiled_gemm_kernel<<<tiles_m * tiles_n, 256, TG_LDS, s>>>(ah, al, a_kt, a.row_blocks, a.rows, w, kt_count, n_blocks,
-                                                           tiles_m, o);
+  // 128-row tiles where they give every CU two blocks, 64-row tiles otherwise
+  const int tiles_n = (n_blocks + PG_NB - 1) / PG_NB;
+  const int tiles_m8 = (a.rows + 127) / 128;
+  if ((long)tiles_m8 * tiles_n >= 2 * kCUs) {
+    tiled_gemm_kernel<8><<<tiles_m8 * tiles_n, 256, PgShape<8>::LDS, s>>>(ah, al, a_kt, a.row_blocks, a.rows, w,
+                                                                          kt_count, n_blocks, tiles_m8, o);
+  } else {
+    const int tiles_m4 = (a.rows + 63) / 64;
+    tiled_gemm_kernel<4><<<tiles_m4 * tiles_n, 256, PgShape<4>::LDS, s>>>(ah, al, a_kt, a.row_blocks, a.rows, w,
+                                                                          kt_count, n_blocks, tiles_m4, o);
+  }
   return Splits{};
 }
 

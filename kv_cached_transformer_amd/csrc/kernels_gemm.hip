@@ -277,25 +277,49 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__rest
 // One thread per (row, 4 consecutive columns): sums the ks partials in split
 // order (deterministic) and applies the epilogue.  For SwiGLU the threads of
 // gate columns also read the matching up columns (16 further on).
+// One thread per 8 consecutive columns of a row for the SwiGLU epilogue, so every store is a lane's
+// 16-byte chunk of the packed hi/lo activation; one thread per 4 columns (one float4) for fp32 outputs.
 __global__ void reduce_kernel(const float *__restrict__ partials, Splits sp, int rows, int n, LinearOut o) {
-  const int n4 = n >> 2;
+  const int cpt = o.kind == kSiluMul ? 8 : 4;  // columns per thread
+  const int nt = n / cpt;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (size_t)rows * n4) return;
-  const int r = (int)(idx / n4), c = (int)(idx % n4) * 4;
-  if (o.kind == kSiluMul && ((c >> 4) & 1)) return;
+  if (idx >= (size_t)rows * nt) return;
+  const int r = (int)(idx / nt), c = (int)(idx % nt) * cpt;
+  if (o.kind == kSiluMul && ((c >> 4) & 1)) return;  // up columns: read by their gate's thread
   const size_t plane = (size_t)rows * n;
-  const int ks = sp.slots(c);  // c..c+3 (and the up columns c+16..) lie in one column group
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f), u = s;
-  add_splits(s, partials + (size_t)r * n + c, plane, ks);
-  if (o.kind == kSiluMul) add_splits(u, partials + (size_t)r * n + c + 16, plane, ks);
-  epi_store(o, r, c, s.x, u.x);
-  epi_store(o, r, c + 1, s.y, u.y);
-  epi_store(o, r, c + 2, s.z, u.z);
-  epi_store(o, r, c + 3, s.w, u.w);
+  const int ks = sp.slots(c);  // c..c+cpt-1 (and the up columns c+16..) lie in one column group
+  const float *p = partials + (size_t)r * n + c;
+  float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+  add_splits(s0, p, plane, ks);
+  if (o.kind == kSiluMul) {
+    add_splits(s1, p + 4, plane, ks);
+    float4 u0 = make_float4(0.f, 0.f, 0.f, 0.f), u1 = u0;
+    add_splits(u0, p + 16, plane, ks);
+    add_splits(u1, p + 20, plane, ks);
+    const float y[8] = {silu_f(s0.x) * u0.x, silu_f(s0.y) * u0.y, silu_f(s0.z) * u0.z, silu_f(s0.w) * u0.w,
+                        silu_f(s1.x) * u1.x, silu_f(s1.y) * u1.y, silu_f(s1.z) * u1.z, silu_f(s1.w) * u1.w};
+    const int j = ((c >> 5) << 4) | (c & 15);  // gate column -> activation column (a multiple of 8)
+    uint4 h, l;
+    split_pack8(y, h, l);
+    const size_t off = packed_offset(r, j, o.act_kt);
+    *reinterpret_cast<uint4 *>(o.act_hi + off) = h;
+    *reinterpret_cast<uint4 *>(o.act_lo + off) = l;
+    // the row's padding columns (act_cols .. 32*act_kt-1: none or one 16-column block) follow the last
+    // real 16-column block, whose writers clear them
+    if (j + 16 >= o.act_cols && j + 16 < o.act_kt * 32) {
+      const size_t pad = packed_offset(r, j + 16, o.act_kt);
+      *reinterpret_cast<uint4 *>(o.act_hi + pad) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4 *>(o.act_lo + pad) = make_uint4(0, 0, 0, 0);
+    }
+  } else {
+    float4 *q = reinterpret_cast<float4 *>(o.f32 + (size_t)r * o.ld + c);
+    if (o.kind == kAccumulate) vadd(s0, *q);
+    *q = s0;
+  }
 }
 
 void launch_reduce(const float *partials, const Splits &sp, int rows, int n, const LinearOut &o, hipStream_t s) {
-  const size_t total = (size_t)rows * (n / 4);
+  const size_t total = (size_t)rows * (n / (o.kind == kSiluMul ? 8 : 4));
   if (total) reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(partials, sp, rows, n, o);
 }
 

@@ -54,7 +54,7 @@ extern "C" {
 typedef enum {
   LLMDEC_OK = 0,
   LLMDEC_E_INVALID = -1,     /* bad argument: null pointer, inconsistent sizes, out of range */
-  LLMDEC_E_UNSUPPORTED = -2, /* valid but not built: head_dim not 64/128, n_kv_heads != n_heads */
+  LLMDEC_E_UNSUPPORTED = -2, /* valid but not built: head_dim not 64/128, page_size not 16 */
   LLMDEC_E_NO_PAGES = -3,    /* the pool cannot cover a request; nothing was changed */
   LLMDEC_E_WORKSPACE = -4,   /* workspace pointer missing or smaller than required */
   LLMDEC_E_HIP = -5          /* a HIP runtime call or kernel launch failed */
@@ -65,8 +65,11 @@ typedef void *llmdec_stream; /* hipStream_t */
 /* Model shape.  [W] §1.2 gives the 7B values: hidden 4096, 32 layers,
  * intermediate 11008, vocab 32000; [E] §3.4 gives 32 heads of 128.
  * page_size must be 16 ([E] §3.4 recommends 16 or 32 tokens per page).
- * head_dim must be 64 or 128; hidden == n_heads * head_dim; n_kv_heads must
- * equal n_heads; hidden and intermediate must be multiples of 16. */
+ * head_dim must be 64 or 128; hidden == n_heads * head_dim; hidden and
+ * intermediate must be multiples of 16.  n_kv_heads must divide n_heads:
+ * with fewer K/V heads than query heads (grouped-query attention, whose
+ * smaller k/v projections [W] §5.1 and the per-head K/V reshape of [E] §4.3
+ * describe), query head h attends with K/V head h / (n_heads / n_kv_heads). */
 typedef struct {
   int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, intermediate, vocab, page_size;
   float rms_eps;    /* added to the mean square inside the root ([E] §4.2) */
@@ -84,7 +87,8 @@ typedef struct {
 /* One layer re-laid out for the kernels by llmdec_pack_layer (pointers into
  * the caller's packed buffer).  Matrices are stored as 16-row x 32-column
  * tiles in the order the matrix-core operands are fed; q/k/v are fused into
- * one [3*hidden][hidden] matrix and gate/up into one matrix whose 16-row
+ * one [hidden + 2*n_kv_heads*head_dim][hidden] matrix (wq rows, then wk,
+ * then wv) and gate/up into one matrix whose 16-row
  * blocks alternate gate and up.  The contents are the same bf16 values. */
 typedef struct {
   const void *attn_norm, *mlp_norm; /* bf16 [hidden], copied */
@@ -268,7 +272,9 @@ llmdec_status llmdec_op_swiglu_linear(const float *a, int32_t rows, int32_t k_di
 
 /* Rotate q and k of each new token by its position and store bf16 k, v into
  * the pool ([E] §4.3: rotation first, then the cache update).  qkv: dev fp32
- * [n_tokens][3*hidden] (q | k | v); q is rotated in place.  Token t belongs
+ * [n_tokens][hidden + 2*n_kv_heads*head_dim] (q | k | v: n_heads query
+ * heads, then n_kv_heads key and n_kv_heads value heads); q is rotated in
+ * place.  Token t belongs
  * to sequence seq_of_token[t] (dev int32, in [0, n_seqs): the row of
  * block_tables [n_seqs][max_pages]) at position pos_of_token[t]. */
 llmdec_status llmdec_op_rope_append(const llmdec_config *cfg, float *qkv, int32_t n_tokens, int32_t n_seqs,

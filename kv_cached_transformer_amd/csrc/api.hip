@@ -44,8 +44,8 @@ llmdec_status check_config(const llmdec_config *c, const char *who) {
   if (c->n_heads * c->head_dim != c->hidden)
     return set_error(LLMDEC_E_INVALID, "%s: hidden (%d) != n_heads (%d) * head_dim (%d)", who, c->hidden, c->n_heads,
                      c->head_dim);
-  if (c->n_kv_heads != c->n_heads)
-    return set_error(LLMDEC_E_UNSUPPORTED, "%s: n_kv_heads (%d) must equal n_heads (%d)", who, c->n_kv_heads,
+  if (c->n_kv_heads <= 0 || c->n_heads % c->n_kv_heads)
+    return set_error(LLMDEC_E_INVALID, "%s: n_kv_heads (%d) must divide n_heads (%d)", who, c->n_kv_heads,
                      c->n_heads);
   if (c->hidden % 32 || c->intermediate % 16 || c->vocab % 16)
     return set_error(LLMDEC_E_INVALID, "%s: hidden must be a multiple of 32, intermediate and vocab of 16", who);
@@ -79,7 +79,7 @@ WsLayout ws_layout(const llmdec_config &c, int max_tokens, int max_seqs, int max
   L.attn_slots = (int)slots;
   // split-k partial sums: the worst case over every streamed product (rows <= 64) this workspace can see
   size_t part = 0;
-  const int shapes[4][2] = {{3 * h, h}, {h, h}, {2 * I, h}, {h, I}};
+  const int shapes[4][2] = {{qkv_cols(c), h}, {h, h}, {2 * I, h}, {h, I}};
   for (int m = 1; m <= std::min(rows, 64); ++m) {
     for (auto &sh : shapes) part = std::max(part, linear_partial_floats(m, sh[0], sh[1], kSplitBalanced));
     part = std::max(part, linear_partial_floats(m, c.vocab, h, kSplitUniform));  // lm_head
@@ -98,7 +98,7 @@ WsLayout ws_layout(const llmdec_config &c, int max_tokens, int max_seqs, int max
   L.act_hl = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_h);
   L.act_i = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_i);
   L.act_il = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_i);
-  L.qkv = take(sizeof(float) * (size_t)rows * 3 * h);
+  L.qkv = take(sizeof(float) * (size_t)rows * qkv_cols(c));
   L.part = take(sizeof(float) * part);
   L.part_floats = part;
   L.attn_part = take(sizeof(float) * slots * (c.head_dim + 2));
@@ -186,21 +186,22 @@ static void run_layer(const LayerArgs &a) {
   LinearOut o_qkv;
   o_qkv.kind = kStore;
   o_qkv.f32 = qkv;
-  o_qkv.ld = 3 * h;
+  const int nqkv = qkv_cols(c);
+  o_qkv.ld = nqkv;
   // a split q|k|v product leaves partial sums that the rotary/append kernel adds up
-  const Splits sp_qkv = launch_linear(ah, (const uint16_t *)a.w->w_qkv, 3 * h, h, o_qkv, part, L.part_floats, kSplitBalanced, a.s);
+  const Splits sp_qkv = launch_linear(ah, (const uint16_t *)a.w->w_qkv, nqkv, h, o_qkv, part, L.part_floats, kSplitBalanced, a.s);
   const float *qkv_part = sp_qkv.any() ? part : nullptr;
   if (a.decode) {
-    launch_rope_append(c, qkv, qkv_part, sp_qkv, 3 * h, M, a.n_seqs, nullptr, a.ctx, a.bt, a.max_pages, pk, pv,
+    launch_rope_append(c, qkv, qkv_part, sp_qkv, nqkv, M, a.n_seqs, nullptr, a.ctx, a.bt, a.max_pages, pk, pv,
                        a.pool->num_pages, err, a.s);
-    launch_decode_attention(c, qkv, 3 * h, M, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages,
+    launch_decode_attention(c, qkv, nqkv, M, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages,
                             at<float>(a.ws, L.attn_part), nullptr, ah_hi, ah_lo, L.kpad_h, err, a.s);
   } else {
     int32_t *ts = at<int32_t>(a.ws, L.tok_seq), *tp = at<int32_t>(a.ws, L.tok_pos);
     launch_token_map(a.cu, a.start, a.n_seqs, M, err, ts, tp, a.s);
-    launch_rope_append(c, qkv, qkv_part, sp_qkv, 3 * h, M, a.n_seqs, ts, tp, a.bt, a.max_pages, pk, pv,
+    launch_rope_append(c, qkv, qkv_part, sp_qkv, nqkv, M, a.n_seqs, ts, tp, a.bt, a.max_pages, pk, pv,
                        a.pool->num_pages, err, a.s);
-    launch_prefill_attention(c, qkv, 3 * h, a.n_seqs, M, a.max_q_len, a.cu, a.start, a.bt, a.max_pages, pk, pv,
+    launch_prefill_attention(c, qkv, nqkv, a.n_seqs, M, a.max_q_len, a.cu, a.start, a.bt, a.max_pages, pk, pv,
                              a.pool->num_pages, nullptr, ah_hi, ah_lo, L.kpad_h, err, a.s);
   }
   LinearOut o_res;
@@ -258,7 +259,7 @@ static size_t packed_layer_parts(const llmdec_config &c, size_t off[6]) {
   off[1] = o;  // mlp_norm
   o += al((size_t)h * 2);
   off[2] = o;  // qkv
-  o += al(llmdec_packed_matrix_bytes(3 * h, h));
+  o += al(llmdec_packed_matrix_bytes(qkv_cols(c), h));
   off[3] = o;  // o
   o += al(llmdec_packed_matrix_bytes(h, h));
   off[4] = o;  // gate/up
@@ -290,13 +291,13 @@ extern "C" llmdec_status llmdec_pack_layer(const llmdec_config *cfg, const llmde
   if (hipMemcpyAsync(d + off[0], in->attn_norm, (size_t)h * 2, hipMemcpyDeviceToDevice, s) != hipSuccess ||
       hipMemcpyAsync(d + off[1], in->mlp_norm, (size_t)h * 2, hipMemcpyDeviceToDevice, s) != hipSuccess)
     return set_error(LLMDEC_E_HIP, "pack_layer: copy of the norm gains failed");
-  // Fused q|k|v: row blocks of wq, then wk, then wv (each a whole number of 16-row blocks).
-  const int ktc = round_up(h, kTileK);
-  const size_t mat_hh = (size_t)h * ktc;  // packed elements of one [h][h] matrix
+  // Fused q|k|v: row blocks of wq ([h][h]), then wk and wv ([kv][h] each; every part a whole number of
+  // 16-row blocks)
+  const int ktc = round_up(h, kTileK), kv = kv_cols(*cfg);
   uint16_t *qkv = (uint16_t *)(d + off[2]);
   launch_pack_matrix(h, h, (const uint16_t *)in->wq, qkv, s);
-  launch_pack_matrix(h, h, (const uint16_t *)in->wk, qkv + mat_hh, s);
-  launch_pack_matrix(h, h, (const uint16_t *)in->wv, qkv + 2 * mat_hh, s);
+  launch_pack_matrix(kv, h, (const uint16_t *)in->wk, qkv + (size_t)h * ktc, s);
+  launch_pack_matrix(kv, h, (const uint16_t *)in->wv, qkv + (size_t)(h + kv) * ktc, s);
   launch_pack_matrix(h, h, (const uint16_t *)in->wo, (uint16_t *)(d + off[3]), s);
   // Gate/up interleaved by 16-row block: block 2j = gate rows 16j.., block 2j+1 = up rows 16j..
   {
@@ -549,7 +550,7 @@ extern "C" llmdec_status llmdec_op_rope_append(const llmdec_config *cfg, float *
     return set_error(LLMDEC_E_INVALID, "%s: n_tokens/n_seqs/max_pages out of range", who);
   uint16_t *pk, *pv;
   pool_layer(pool, layer, &pk, &pv);
-  launch_rope_append(*cfg, qkv, nullptr, Splits{}, 3 * cfg->hidden, n_tokens, n_seqs, seq_of_token, pos_of_token, block_tables, max_pages, pk, pv,
+  launch_rope_append(*cfg, qkv, nullptr, Splits{}, qkv_cols(*cfg), n_tokens, n_seqs, seq_of_token, pos_of_token, block_tables, max_pages, pk, pv,
                      pool->num_pages, (uint32_t *)ws, (hipStream_t)stream);
   return check_launch(who);
 }

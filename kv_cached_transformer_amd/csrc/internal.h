@@ -65,6 +65,12 @@ struct Splits {
   }
 };
 
+// Columns of the fused q|k|v product: n_heads query heads, then n_kv_heads key heads, then n_kv_heads
+// value heads, head_dim each (grouped-query attention shares one K/V head among n_heads / n_kv_heads
+// query heads).
+inline int qkv_cols(const llmdec_config &c) { return (c.n_heads + 2 * c.n_kv_heads) * c.head_dim; }
+inline int kv_cols(const llmdec_config &c) { return c.n_kv_heads * c.head_dim; }
+
 // Workspace layout for steps of up to max_tokens tokens and max_seqs sequences.
 struct WsLayout {
   size_t err, tok_seq, tok_pos, x, act_h, act_hl, act_i, act_il, qkv, part, attn_part, logits, total;

@@ -107,9 +107,9 @@ __device__ inline float uniform_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
-template <int D>
+template <int D, bool SHARED_KV>
 __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict__ q, int ld_q, int n_heads,
-                                                         const int32_t *__restrict__ ctx_lens,
+                                                         int n_kv_heads, const int32_t *__restrict__ ctx_lens,
                                                          const int32_t *__restrict__ block_tables, int max_pages,
                                                          const uint16_t *__restrict__ pool_k,
                                                          const uint16_t *__restrict__ pool_v, int num_pages, int ppp,
@@ -119,7 +119,12 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict
   constexpr int LPT = D / 8;      // lanes per token in K (each holds 8 dims)
   constexpr int G = 64 / LPT;     // token groups per K instruction
   constexpr int VE = D / 64;      // V dims per lane
-  const int h = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+  // Grouped-query attention: query head h reads K/V head h / group.  Block x is (K/V head x % n_kv_heads,
+  // member x / n_kv_heads), so the query heads sharing a K/V head are launched n_kv_heads blocks apart;
+  // blocks go round-robin to the 8 XCDs, so with n_kv_heads a multiple of 8 they share one L2.
+  const int group = n_heads / n_kv_heads;
+  const int kvh = blockIdx.x % n_kv_heads, h = kvh * group + blockIdx.x / n_kv_heads;
+  const int s = blockIdx.y, part = blockIdx.z;
   const int lane = threadIdx.x;
   const int p0 = part * ppp;
   // Three independent reads leave together: the context length, this partition's block-table
@@ -174,22 +179,28 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict
   auto page_id = [&](int pi) { return __builtin_amdgcn_readlane(my_pg, pi - p0); };  // wave-uniform
   // Each page-head block (16 tokens x D bf16 of K, the same of V) is read through a buffer resource
   // of its own; an absent page (past the partition, or a rejected id) gets an empty resource, whose
-  // loads read zeros without touching memory, so the ring below needs no branches.  Pages are read
-  // once per step: the non-temporal policy keeps them from displacing anything in the caches
-  // (measured: 12% less time for the same bytes).
+  // loads read zeros without touching memory, so the ring below needs no branches.  Without grouping
+  // every page is read once per step: the non-temporal policy keeps it from displacing anything in the
+  // caches (measured: 12% less time for the same bytes).  A K/V head shared by a group of query heads
+  // is read by each of them, so there the pages are cached normally for the others to hit.
+  constexpr int policy = SHARED_KV ? 0 : kLoadStream;
   const uint32_t lane_bytes = (uint32_t)lane * 16u;
   auto load = [&](int pi, int b) {
     const int pg = page_id(pi);
     const bool ok = pg >= 0;
-    const size_t blk = ((size_t)(ok ? pg : 0) * n_heads + h) * 16 * D;  // element offset of the block
+    const size_t blk = ((size_t)(ok ? pg : 0) * n_kv_heads + kvh) * 16 * D;  // element offset of the block
     const size_t bytes = ok ? (size_t)16 * D * 2 : 0;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(pool_k + blk, bytes), vr = make_rsrc(pool_v + blk, bytes);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kb[b][i] = buffer_load16(kr, lane_bytes, i * 1024, kLoadStream);
+    for (int i = 0; i < NI; ++i) kb[b][i] = buffer_load16(kr, lane_bytes, i * 1024, policy);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // token quarter i: D x 4 bf16, lane holds VE dims x 4 tokens
-      if constexpr (VE == 2) vb[b][i] = buffer_load16(vr, lane_bytes, i * D * 8, kLoadStream);
-      else vb[b][i] = buffer_load8(vr, (uint32_t)lane * 8u, i * D * 8);
+      if constexpr (VE == 2) {
+        vb[b][i] = buffer_load16(vr, lane_bytes, i * D * 8, policy);
+      } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(vr, (int)(lane * 8u), i * D * 8, policy);
+        vb[b][i] = make_uint2(v[0], v[1]);
+      }
     }
   };
   // One page with n_valid (wave-uniform) live tokens: 16, fewer on a sequence's last page, 0 for a
@@ -357,15 +368,28 @@ void launch_decode_attention(const llmdec_config &cfg, const float *q, int ld_q,
   int ppp, n_parts;
   decode_partition(n_seqs, cfg.n_heads, max_pages, &ppp, &n_parts);
   dim3 grid(cfg.n_heads, n_seqs, n_parts);
+  const bool shared = cfg.n_kv_heads < cfg.n_heads;
   if (cfg.head_dim == 128) {
-    decode_attn_kernel<128><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, ctx_lens, block_tables, max_pages, pk, pv,
-                                                num_pages, ppp, n_parts, partials, out_f32, out_hi, out_lo, kpad, err);
+    if (shared)
+      decode_attn_kernel<128, true><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, ctx_lens, block_tables,
+                                                        max_pages, pk, pv, num_pages, ppp, n_parts, partials, out_f32,
+                                                        out_hi, out_lo, kpad, err);
+    else
+      decode_attn_kernel<128, false><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, ctx_lens, block_tables,
+                                                         max_pages, pk, pv, num_pages, ppp, n_parts, partials, out_f32,
+                                                         out_hi, out_lo, kpad, err);
     if (n_parts > 1)
       decode_combine_kernel<128><<<n_seqs * cfg.n_heads, 128, 0, s>>>(cfg.n_heads, ctx_lens, max_pages, ppp, n_parts,
                                                                      partials, out_f32, out_hi, out_lo, kpad);
   } else {
-    decode_attn_kernel<64><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, ctx_lens, block_tables, max_pages, pk, pv,
-                                               num_pages, ppp, n_parts, partials, out_f32, out_hi, out_lo, kpad, err);
+    if (shared)
+      decode_attn_kernel<64, true><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, ctx_lens, block_tables,
+                                                       max_pages, pk, pv, num_pages, ppp, n_parts, partials, out_f32,
+                                                       out_hi, out_lo, kpad, err);
+    else
+      decode_attn_kernel<64, false><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, ctx_lens, block_tables,
+                                                        max_pages, pk, pv, num_pages, ppp, n_parts, partials, out_f32,
+                                                        out_hi, out_lo, kpad, err);
     if (n_parts > 1)
       decode_combine_kernel<64><<<n_seqs * cfg.n_heads, 64, 0, s>>>(cfg.n_heads, ctx_lens, max_pages, ppp, n_parts,
                                                                    partials, out_f32, out_hi, out_lo, kpad);
@@ -377,7 +401,7 @@ void launch_decode_attention(const llmdec_config &cfg, const float *q, int ld_q,
 // pages (32 keys) at a time: S^T blocks for both pages, mask, online softmax
 // per query, then O^T += V^T P^T over the 32 keys.
 template <int D>
-__global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restrict__ q, int ld_q, int n_heads,
+__global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restrict__ q, int ld_q, int n_heads, int n_kv_heads,
                                                           int n_tokens, int max_q_len,
                                                           const int32_t *__restrict__ cu,
                                                           const int32_t *__restrict__ start_pos,
@@ -389,6 +413,7 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
   constexpr int KT = D / 32;  // k-tiles of the head dimension
   constexpr int DB = D / 16;  // 16-dim blocks of the output
   const int qb = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int kvh = h / (n_heads / n_kv_heads);  // the K/V head this query head reads
   const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
   const int t0 = cu[s], len = cu[s + 1] - t0;
   if (t0 < 0 || len < 0 || len > max_q_len || t0 + len > n_tokens || start_pos[s] < 0) {
@@ -448,7 +473,7 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
       pgs[u] = pg;
       f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
       if (pg >= 0) {
-        const uint4 *kp = reinterpret_cast<const uint4 *>(pool_k + (((size_t)pg * n_heads + h) * 16 + c) * D + g * 8);
+        const uint4 *kp = reinterpret_cast<const uint4 *>(pool_k + (((size_t)pg * n_kv_heads + kvh) * 16 + c) * D + g * 8);
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
           const uint4 kk = kp[kt * 4];  // dims 32kt + 8g .. +7 of key c
@@ -457,7 +482,7 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
           st = mfma16(kk, qs[0][kt], st);
         }
         // V block [4 quarters][D][4 tokens]: tokens 4g..4g+3 of dim d at (g * D + d) * 4
-        const uint16_t *vp = pool_v + ((size_t)pg * n_heads + h) * D * 16 + (size_t)g * D * 4;
+        const uint16_t *vp = pool_v + ((size_t)pg * n_kv_heads + kvh) * D * 16 + (size_t)g * D * 4;
         // keys after the block's last query are not written yet (possibly NaN): clear their values
         const int n_valid = last_pos + 1 - (pi * 16 + g * 4);
 #pragma unroll
@@ -529,10 +554,10 @@ void launch_prefill_attention(const llmdec_config &cfg, const float *q, int ld_q
   if (n_seqs <= 0 || max_q_len <= 0) return;
   dim3 grid((max_q_len + 15) / 16, cfg.n_heads, n_seqs);
   if (cfg.head_dim == 128)
-    prefill_attn_kernel<128><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, n_tokens, max_q_len, cu, start_pos, block_tables, max_pages, pk, pv,
+    prefill_attn_kernel<128><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, n_tokens, max_q_len, cu, start_pos, block_tables, max_pages, pk, pv,
                                                  num_pages, out_f32, out_hi, out_lo, kpad, err);
   else
-    prefill_attn_kernel<64><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, n_tokens, max_q_len, cu, start_pos, block_tables, max_pages, pk, pv,
+    prefill_attn_kernel<64><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, n_tokens, max_q_len, cu, start_pos, block_tables, max_pages, pk, pv,
                                                 num_pages, out_f32, out_hi, out_lo, kpad, err);
 }
 

@@ -211,7 +211,7 @@ struct RopeFreq {
 
 __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qkv, const float *__restrict__ part,
                                                           Splits sp, int ld_qkv, int n_tokens, int n_heads,
-                                                          int head_dim, RopeFreq fr, int n_seqs,
+                                                          int n_kv_heads, int head_dim, RopeFreq fr, int n_seqs,
                                                           const int32_t *__restrict__ tok_seq,
                                                           const int32_t *__restrict__ tok_pos,
                                                           const int32_t *__restrict__ block_tables, int max_pages,
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
                                                           int num_pages, uint32_t *err) {
   const int t = blockIdx.x;
   const int half = head_dim / 2;
-  const int hidden = n_heads * head_dim;
+  const int hidden = n_heads * head_dim, kv = n_kv_heads * head_dim;
   const int g0 = blockIdx.y * 256;  // first (head, pair) index of this block's chunk
   __shared__ float cs[64], sn[64];
   const int seq = tok_seq ? tok_seq[t] : t;
@@ -261,14 +261,14 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
     const int d = h * head_dim + 2 * i;
     const float2 qq = row2(d);
     *reinterpret_cast<float2 *>(q + d) = make_float2(qq.x * c - qq.y * s, qq.x * s + qq.y * c);
-    if (page >= 0) {
+    if (page >= 0 && h < n_kv_heads) {  // K/V head h (its columns follow the query heads')
       const float2 kk = row2(hidden + d);
       const uint32_t kb = f32_to_bf16(kk.x * c - kk.y * s) | ((uint32_t)f32_to_bf16(kk.x * s + kk.y * c) << 16);
-      const size_t kbase = (((size_t)page * n_heads + h) * 16 + off) * head_dim + 2 * i;
+      const size_t kbase = (((size_t)page * n_kv_heads + h) * 16 + off) * head_dim + 2 * i;
       *reinterpret_cast<uint32_t *>(pool_k + kbase) = kb;
-      const float2 vv = row2(2 * hidden + d);
+      const float2 vv = row2(hidden + kv + d);
       // V block [4 quarters][D][4 tokens]: dim d of token off at ((off/4) * D + d) * 4 + off % 4
-      const size_t vbase = (((size_t)page * n_heads + h) * 4 + (off >> 2)) * head_dim * 4 + (size_t)(2 * i) * 4 + (off & 3);
+      const size_t vbase = (((size_t)page * n_kv_heads + h) * 4 + (off >> 2)) * head_dim * 4 + (size_t)(2 * i) * 4 + (off & 3);
       pool_v[vbase] = f32_to_bf16(vv.x);
       pool_v[vbase + 4] = f32_to_bf16(vv.y);
     }
@@ -284,7 +284,7 @@ void launch_rope_append(const llmdec_config &cfg, float *qkv, const float *qkv_p
   for (int i = 0; i < 64; ++i)
     fr.inv_freq[i] = i < cfg.head_dim / 2 ? pow((double)cfg.rope_theta, -2.0 * i / (double)cfg.head_dim) : 0.0;
   dim3 grid(n_tokens, (cfg.n_heads * (cfg.head_dim / 2) + 255) / 256);
-  rope_append_kernel<<<grid, 256, 0, s>>>(qkv, qkv_partials, sp, ld_qkv, n_tokens, cfg.n_heads,
+  rope_append_kernel<<<grid, 256, 0, s>>>(qkv, qkv_partials, sp, ld_qkv, n_tokens, cfg.n_heads, cfg.n_kv_heads,
                                               cfg.head_dim, fr, n_seqs, tok_seq, tok_pos, block_tables, max_pages,
                                               pool_k, pool_v, num_pages, err);
 }

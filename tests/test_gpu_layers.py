@@ -32,6 +32,11 @@ def R():
 
 
 TINY1 = synth.ModelShape(n_layers=1, hidden=256, n_heads=4, n_kv_heads=4, head_dim=64, intermediate=688, vocab=1024)
+# grouped-query shapes: 4 query heads over 2 K/V heads; a 7B-sized layer with 32 query heads over 8
+TINY1_GQA = synth.ModelShape(n_layers=1, hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=688,
+                             vocab=1024)
+GQA7B_LAYER = synth.ModelShape(n_layers=1, hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128, intermediate=11008,
+                               vocab=32000)
 
 
 def check_new_slots(case, new_tokens, tag):
@@ -123,3 +128,24 @@ def test_7b_layer_decode_batch32(L, R):
 def test_7b_layer_prefill_4x512(L, R):
     lens = [512] * 4
     run_prefill(L, R, synth.LLAMA7B_LAYER, 4, [0] * 4, lens, synth.hidden_input(4, 2048, 4096), "7B prefill 4x512")
+
+
+# ----------------------------------------------------------------------------- grouped-query attention
+def test_decode_tiny_gqa_batched_ragged(L, R):
+    ctxs = [0, 15, 16, 17, 100, 3]
+    run_decode(L, R, TINY1_GQA, 95, ctxs, synth.hidden_input(95, len(ctxs), 256), "tiny GQA decode b6")
+
+
+def test_prefill_tiny_gqa_chunked(L, R):
+    starts, lens = [0, 16, 5, 0], [1, 17, 40, 64]
+    run_prefill(L, R, TINY1_GQA, 96, starts, lens, synth.hidden_input(96, sum(lens), 256), "tiny GQA prefill")
+
+
+def test_gqa_7b_sized_layer_decode_batch8(L, R):
+    ctxs = synth.context_lengths(97, 8, 128, 2048)
+    run_decode(L, R, GQA7B_LAYER, 97, ctxs.tolist(), synth.hidden_input(97, 8, 4096), "GQA 32/8 decode b8")
+
+
+def test_gqa_7b_sized_layer_prefill(L, R):
+    lens = [256, 100]
+    run_prefill(L, R, GQA7B_LAYER, 98, [0, 37], lens, synth.hidden_input(98, sum(lens), 4096), "GQA 32/8 prefill")

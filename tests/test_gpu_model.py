@@ -7,6 +7,8 @@
 * A 2-layer model at the 7B shapes: one decode step over 4 sequences.
 * The full 32-layer 7B-shaped decode workload over 64 sequences, checked on 4 of them.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -44,9 +46,11 @@ class DeviceModel:
                                                        self.final_norm.data_ptr(), self.lm_head.ptr)
 
 
-def test_tiny_model_greedy_generation(L, R):
-    banner("tiny model: prefill 32 + 15 decode steps")
-    shape = synth.TINY
+@pytest.mark.parametrize("n_kv_heads", [4, 2])
+def test_tiny_model_greedy_generation(L, R, n_kv_heads):
+    """n_kv_heads = 2: the same model with grouped-query attention (two query heads per K/V head)."""
+    banner(f"tiny model (n_kv_heads {n_kv_heads}): prefill 32 + 15 decode steps")
+    shape = dataclasses.replace(synth.TINY, n_kv_heads=n_kv_heads)
     mw = synth.model_weights(1, shape)
     dm = DeviceModel(L, R, mw)
     prompt = synth.prompt_ids(1, 32, shape.vocab)

@@ -30,8 +30,8 @@ def R():
 
 
 class Shape:
-    def __init__(self, H, D, I=688, V=1024, layers=1):
-        self.n_layers, self.hidden, self.n_heads, self.n_kv_heads, self.head_dim = layers, H * D, H, H, D
+    def __init__(self, H, D, I=688, V=1024, layers=1, Hk=None):
+        self.n_layers, self.hidden, self.n_heads, self.n_kv_heads, self.head_dim = layers, H * D, H, Hk or H, D
         self.intermediate, self.vocab, self.page_size, self.rms_eps, self.rope_theta = I, V, 16, 1e-6, 10000.0
 
 
@@ -136,10 +136,12 @@ def test_swiglu_linear(L, R, rows, inter, k):
 
 
 # ----------------------------------------------------------------------------- RoPE + append
-@pytest.mark.parametrize("H,D", [(4, 64), (32, 128)])
-def test_rope_append_slots_and_values(L, R, H, D):
-    banner(f"rope_append H={H} D={D}")
-    shape = Shape(H, D)
+@pytest.mark.parametrize("H,D,Hk", [(4, 64, 4), (32, 128, 32), (32, 128, 8), (4, 64, 1)])
+def test_rope_append_slots_and_values(L, R, H, D, Hk):
+    """Rotation of q (all query heads) and k, and the bf16 K/V stores of the n_kv_heads K/V heads at each
+    token's slot, against the oracle; every other slot keeps its sentinel."""
+    banner(f"rope_append H={H} D={D} Hk={Hk}")
+    shape = Shape(H, D, Hk=Hk)
     cfg = L.make_config(shape)
     rng = np.random.default_rng(7 + H)
     lengths = [1, 16, 17, 40, 300, 4100]   # tokens stored per sequence after this call
@@ -156,8 +158,8 @@ def test_rope_append_slots_and_values(L, R, H, D):
     # new tokens: the last 1..3 positions of each sequence
     toks = [(s, p) for s, n in enumerate(lengths) for p in range(max(0, n - 3), n)]
     T = len(toks)
-    h = H * D
-    qkv = rng.standard_normal((T, 3 * h)).astype(np.float32)
+    h, kv = H * D, Hk * D
+    qkv = rng.standard_normal((T, h + 2 * kv)).astype(np.float32)
     qd = R.dev_f32(qkv)
     ws = R.Workspace(8192)
     seq_d, pos_d, bt_d = R.dev_i32([t[0] for t in toks]), R.dev_i32([t[1] for t in toks]), R.dev_i32(bt)
@@ -169,8 +171,8 @@ def test_rope_append_slots_and_values(L, R, H, D):
     pos = np.array([t[1] for t in toks])
     q_ref = od.apply_rope(qkv[:, :h].reshape(T, H, D), pos, 1e4).reshape(T, h)
     assert_close("rope q", qd.cpu().numpy()[:, :h], q_ref, max_abs=1e-5, rel_l2=1e-6)
-    k_ref = od.round_to_bf16(od.apply_rope(qkv[:, h:2 * h].reshape(T, H, D), pos, 1e4))
-    v_ref = od.round_to_bf16(qkv[:, 2 * h:].astype(np.float64).reshape(T, H, D))
+    k_ref = od.round_to_bf16(od.apply_rope(qkv[:, h:h + kv].reshape(T, Hk, D), pos, 1e4))
+    v_ref = od.round_to_bf16(qkv[:, h + kv:].astype(np.float64).reshape(T, Hk, D))
     kd, vd = pool.layer_views(0)
     kimg, vimg = R.host_u16(kd.contiguous()), R.Pool.v_logical(R.host_u16(vd.contiguous()))
     touched_k = np.zeros(kimg.shape[:1] + kimg.shape[2:3], bool)   # [page][slot]
@@ -184,7 +186,7 @@ def test_rope_append_slots_and_values(L, R, H, D):
         ulp_flips += int(diff.sum())
         assert np.all(np.abs(got_k - k_ref[i]) <= np.abs(k_ref[i]) * 2 ** -7 + 1e-30)
         touched_k[pg, off] = True
-    assert ulp_flips <= max(2, 0.002 * T * h), ulp_flips
+    assert ulp_flips <= max(2, 0.002 * T * kv), ulp_flips
     # sentinel: every slot not written still holds 0xFFFF in both K and V
     untouched = ~touched_k
     assert np.all(kimg.transpose(0, 2, 1, 3)[untouched] == 0xFFFF)
@@ -192,7 +194,7 @@ def test_rope_append_slots_and_values(L, R, H, D):
     # the gather entry point walks the same slots
     s = 4
     n = lengths[s]
-    ko = torch.empty(n, H, D, dtype=torch.int16, device="cuda")
+    ko = torch.empty(n, Hk, D, dtype=torch.int16, device="cuda")
     vo = torch.empty_like(ko)
     row_d = R.dev_i32(bt[s])
     L.llmdec_debug_gather_kv(pool.handle, 0, row_d.data_ptr(), n, ko.data_ptr(), vo.data_ptr(), R.stream())
@@ -207,8 +209,8 @@ def test_rope_append_slots_and_values(L, R, H, D):
 def _random_pool(L, R, shape, num_pages, rng):
     cfg = L.make_config(shape)
     pool = R.Pool(cfg, num_pages, rng.permutation(num_pages).astype(np.int32))
-    k_img = bf16_normal(rng, (num_pages, shape.n_heads, 16, shape.head_dim))
-    v_img = bf16_normal(rng, (num_pages, shape.n_heads, shape.head_dim, 16))   # [page][h][d][offset]
+    k_img = bf16_normal(rng, (num_pages, shape.n_kv_heads, 16, shape.head_dim))
+    v_img = bf16_normal(rng, (num_pages, shape.n_kv_heads, shape.head_dim, 16))   # [page][kv head][d][offset]
     kv, vv = pool.layer_views(0)
     kv.copy_(R.dev_u16(k_img).view(kv.shape))
     vv.copy_(R.dev_u16(R.Pool.v_raw(v_img)).view(vv.shape))
@@ -221,12 +223,16 @@ def _gather(k_img, v_img, row, n, h):
     return K, V
 
 
-@pytest.mark.parametrize("H,D,ctxs", [(4, 64, [0, 1, 15, 16, 17, 100]),
-                                      (32, 128, [0, 15, 16, 2048]),
-                                      (8, 128, [4096, 33, 511, 512, 1000, 7])])
-def test_decode_attention(L, R, H, D, ctxs):
-    banner(f"decode_attention H={H} D={D} ctxs={ctxs}")
-    shape = Shape(H, D)
+@pytest.mark.parametrize("H,D,Hk,ctxs", [(4, 64, 4, [0, 1, 15, 16, 17, 100]),
+                                         (32, 128, 32, [0, 15, 16, 2048]),
+                                         (8, 128, 8, [4096, 33, 511, 512, 1000, 7]),
+                                         (32, 128, 8, [0, 15, 16, 2048, 300]),
+                                         (4, 64, 1, [0, 1, 17, 100, 513])])
+def test_decode_attention(L, R, H, D, Hk, ctxs):
+    """Query head h attends over K/V head h // (H / Hk) (grouped-query when Hk < H)."""
+    banner(f"decode_attention H={H} D={D} Hk={Hk} ctxs={ctxs}")
+    shape = Shape(H, D, Hk=Hk)
+    g = H // Hk
     rng = np.random.default_rng(11 + H + len(ctxs))
     max_pages = max(op.pages_needed(c + 1) for c in ctxs) + 1
     n = len(ctxs)
@@ -246,17 +252,21 @@ def test_decode_attention(L, R, H, D, ctxs):
     ref = np.empty((n, H * D))
     for s, c in enumerate(ctxs):
         for h in range(H):
-            K, V = _gather(k_img, v_img, bt[s], c + 1, h)
+            K, V = _gather(k_img, v_img, bt[s], c + 1, h // g)
             ref[s, h * D:(h + 1) * D] = od.attend(q[s, h * D:(h + 1) * D], K, V)
     assert_close("decode attention", got, ref, max_abs=1e-4, rel_l2=1e-5)
 
 
-@pytest.mark.parametrize("H,D,seqs", [(4, 64, [(0, 1), (0, 17), (5, 40), (16, 16), (0, 64)]),
-                                      (32, 128, [(0, 33), (100, 20), (0, 16)]),
-                                      (8, 128, [(0, 512), (37, 300)])])
-def test_prefill_attention(L, R, H, D, seqs):
-    banner(f"prefill_attention H={H} D={D} seqs={seqs}")
-    shape = Shape(H, D)
+@pytest.mark.parametrize("H,D,Hk,seqs", [(4, 64, 4, [(0, 1), (0, 17), (5, 40), (16, 16), (0, 64)]),
+                                         (32, 128, 32, [(0, 33), (100, 20), (0, 16)]),
+                                         (8, 128, 8, [(0, 512), (37, 300)]),
+                                         (32, 128, 8, [(0, 33), (100, 20), (0, 64)]),
+                                         (4, 64, 2, [(0, 1), (5, 40), (0, 64)])])
+def test_prefill_attention(L, R, H, D, Hk, seqs):
+    """Causal attention of new tokens after a cached prefix; query head h reads K/V head h // (H / Hk)."""
+    banner(f"prefill_attention H={H} D={D} Hk={Hk} seqs={seqs}")
+    shape = Shape(H, D, Hk=Hk)
+    g = H // Hk
     rng = np.random.default_rng(21 + H)
     n = len(seqs)
     totals = [s0 + ln for s0, ln in seqs]
@@ -281,7 +291,7 @@ def test_prefill_attention(L, R, H, D, seqs):
     ref = np.empty((T, H * D))
     for s, (s0, ln) in enumerate(seqs):
         for h in range(H):
-            K, V = _gather(k_img, v_img, bt[s], s0 + ln, h)
+            K, V = _gather(k_img, v_img, bt[s], s0 + ln, h // g)
             for i in range(ln):
                 p = s0 + i
                 ref[cu[s] + i, h * D:(h + 1) * D] = od.attend(q[cu[s] + i, h * D:(h + 1) * D], K[:p + 1], V[:p + 1])

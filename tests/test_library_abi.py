@@ -53,7 +53,10 @@ def test_config_validation_before_launch(L):
     assert L.llmdec_workspace_bytes(tiny_cfg(L), 32, 1, 4) > 0
     assert L.llmdec_workspace_bytes(tiny_cfg(L, page_size=32), 32, 1, 4) == 0
     assert L.llmdec_workspace_bytes(tiny_cfg(L, head_dim=96), 32, 1, 4) == 0
-    assert L.llmdec_workspace_bytes(tiny_cfg(L, n_kv_heads=2), 32, 1, 4) == 0
+    # grouped K/V heads: n_kv_heads must divide n_heads (4); the q|k|v buffer shrinks with it
+    assert 0 < L.llmdec_workspace_bytes(tiny_cfg(L, n_kv_heads=2), 32, 1, 4) < L.llmdec_workspace_bytes(tiny_cfg(L), 32, 1, 4)
+    assert L.llmdec_workspace_bytes(tiny_cfg(L, n_kv_heads=3), 32, 1, 4) == 0
+    assert L.llmdec_workspace_bytes(tiny_cfg(L, n_kv_heads=0), 32, 1, 4) == 0
     with pytest.raises(L.LlmdecError) as e:
         L.llmdec_kv_pool_create(tiny_cfg(L, hidden=300), 1 << 20, 1 << 30, 4)
     assert e.value.status in (L.LLMDEC_E_INVALID, L.LLMDEC_E_UNSUPPORTED)

@@ -251,6 +251,32 @@ def test_layer_query_zero_gives_prefix_mean_of_values():
     assert np.allclose(out, x + prefix_mean @ w["wo"].T, rtol=1e-12, atol=1e-14)
 
 
+def test_grouped_kv_heads_equal_repeated_kv_heads():
+    """Grouped-query attention ([W] §5.1: k/v projections of n_kv_heads * head_dim rows; [E] §4.3: K/V
+    reshaped to n_kv_heads heads): query head h reads K/V head h // (n_heads / n_kv_heads).  That equals
+    plain multi-head attention whose k/v projections repeat each K/V head's rows for its group.  Pairing
+    the heads any other way (h % n_kv_heads) gives a different layer output."""
+    r = np.random.default_rng(12)
+    h, H, Hk, D, T = 32, 4, 2, 8, 5
+    g = H // Hk
+    s_mha = _Shape(h, H, D, 24)
+    s_gqa = _Shape(h, H, D, 24)
+    s_gqa.n_kv_heads = Hk
+    w = _rand_layer(r, s_mha)
+    w["wk"] = 0.3 * r.standard_normal((Hk * D, h))
+    w["wv"] = 0.3 * r.standard_normal((Hk * D, h))
+    x = r.standard_normal((T, h))
+    out_g = od.layer_step(s_gqa, w, 0, x, [0] * T, list(range(T)), od.ContiguousKV(1, Hk, D))
+
+    def mha_with(head_map):
+        rows = np.concatenate([np.arange(D) + head_map(hh) * D for hh in range(H)])
+        w_m = dict(w, wk=w["wk"][rows], wv=w["wv"][rows])
+        return od.layer_step(s_mha, w_m, 0, x, [0] * T, list(range(T)), od.ContiguousKV(1, H, D))
+
+    assert np.allclose(out_g, mha_with(lambda hh: hh // g), rtol=1e-12, atol=1e-14)
+    assert not np.allclose(out_g, mha_with(lambda hh: hh % Hk), rtol=1e-3, atol=1e-3)
+
+
 def test_mlp_path_closed_form():
     # attention off (Wo = 0); gate and up diagonal, down a permutation: the MLP output
     # is silu(a*y) * (b*y) routed through the permutation.

@@ -371,12 +371,12 @@ def pmc_summary(fetch_dir, write_dir):
            f"copy_fetch_kib: {copy_f:.1f}  fetch_scale: {kf:.4f}",
            f"copy_write_kib: {copy_w:.1f}  write_scale: {kw:.4f}"]
     total = 0.0
-    for name in ("decode_attn_kernel<128>", "decode_combine_kernel<128>"):
+    for name in ("decode_attn_kernel<128,", "decode_combine_kernel<128>"):
         f, nf, grid = _per_dispatch(fr, name)
         w, nw, _ = _per_dispatch(wr, name)
         b = f * 1024 * kf + w * 1024 * kw
         total += b
-        out.append(f"{name}: grid {grid}: FETCH_SIZE {f:.1f} KiB ({nf} dispatches), WRITE_SIZE {w:.1f} KiB "
+        out.append(f"{name.rstrip(',')}: grid {grid}: FETCH_SIZE {f:.1f} KiB ({nf} dispatches), WRITE_SIZE {w:.1f} KiB "
                    f"({nw}) -> {b / 1e6:.2f} MB")
     alg = attn_alg_bytes(10, 3)
     out.append(f"algorithmic_bytes_per_call: {alg:.0f}")

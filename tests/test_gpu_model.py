@@ -6,6 +6,8 @@
   (teacher forcing).
 * A 2-layer model at the 7B shapes: one decode step over 4 sequences.
 * The full 32-layer 7B-shaped decode workload over 64 sequences, checked on 4 of them.
+* Continuous batching on the tiny model: prompts and decode tokens of different sequences in one
+  step, a finished sequence's pages recycled for a newcomer.
 """
 import dataclasses
 
@@ -309,3 +311,89 @@ def test_7b_model_full_size_decode_steps(L, R):
                 assert ids[i + 1, s] == od.greedy_token(ref[j]), \
                     f"step {i} sequence {s}: device {ids[i + 1, s]} oracle {od.greedy_token(ref[j])}"
     assert not failures, "; ".join(failures)
+
+
+def test_tiny_model_continuous_batching(L, R):
+    """Mixed batches through llmdec_model_step_greedy, as continuous batching runs them ([E] §3.3; pages
+    from a shared pool, returned when a request ends, [E] §3.4): one step carries some sequences' prompts
+    and other sequences' single decode tokens, a sequence that finishes gives its pages back, and a
+    newcomer's prompt lands in those pages, whose stale K/V must never be read.  Every step's logits and
+    ids of every sequence against the oracle (fed the oracle's ids), the block-table rows and free counts
+    against the oracle's pool bit for bit, and at the end every cached K/V value of the live sequences."""
+    banner("tiny model: continuous batching with page reuse")
+    shape = synth.TINY
+    W = 41
+    mw = synth.model_weights(W, shape)
+    dm = DeviceModel(L, R, mw)
+    num_pages, max_pages = 7, 4   # small enough that the newcomer must take the finished sequence's page
+    order = synth.free_order(W, num_pages)
+    pool = R.Pool(dm.cfg, num_pages, order, fill_bits=0xFFFF)
+    ref_pool = op.PagePool(num_pages, order)
+    kv = od.ContiguousKV(shape.n_layers, shape.n_kv_heads, shape.head_dim)
+    prompts = {0: synth.prompt_ids(W, 20, shape.vocab), 1: synth.prompt_ids(W + 1, 7, shape.vocab),
+               2: synth.prompt_ids(W + 2, 33, shape.vocab), 3: synth.prompt_ids(W + 3, 18, shape.vocab)}
+    # per step: the sequences it carries, in launch order; a sequence's first appearance feeds its prompt
+    steps = [[0, 1], [2, 0, 1], [0, 1, 2], [3, 0, 2], [0, 2, 3], [3, 2]]
+    finish_after = {1: 2}          # sequence 1 ends after step 2 and returns its pages
+    state = {}                     # id -> [row, n_pages, cached tokens, next feed]
+    ws = R.Workspace(L.llmdec_workspace_bytes(dm.cfg, 64, 4, max_pages))
+    for k, seqs in enumerate(steps):
+        feeds, starts, rows = [], [], []
+        for sid in seqs:
+            if sid not in state:
+                state[sid] = [np.full(max_pages, -1, np.int32), 0, 0, list(prompts[sid])]
+            row, npg, cached, feed = state[sid]
+            ref_row = row.tolist()
+            new_npg = pool.alloc(cached + len(feed), row, npg, max_pages)
+            st_ref, ref_npg = ref_pool.alloc(cached + len(feed), ref_row, npg, max_pages)
+            assert st_ref == op.OK and new_npg == ref_npg and row.tolist() == ref_row
+            state[sid][1] = new_npg
+            feeds.append(feed)
+            starts.append(cached)
+            rows.append(row.copy())
+        lens = [len(f) for f in feeds]
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        toks = np.concatenate(feeds).astype(np.int32)
+        n = len(seqs)
+        bt_d, toks_d, cu_d, st_d = R.dev_i32(np.stack(rows)), R.dev_i32(toks), R.dev_i32(cu), R.dev_i32(starts)
+        nxt = torch.empty(n, dtype=torch.int32, device="cuda")
+        logits = torch.empty(n, shape.vocab, dtype=torch.float32, device="cuda")
+        L.llmdec_model_step_greedy(dm.cfg, dm.struct, n, int(cu[-1]), max(lens), toks_d.data_ptr(), cu_d.data_ptr(),
+                                   st_d.data_ptr(), bt_d.data_ptr(), max_pages, pool.handle, nxt.data_ptr(),
+                                   logits.data_ptr(), ws.ptr, ws.nbytes, R.stream())
+        torch.cuda.synchronize()
+        assert ws.error_bits() == 0
+        tok_seq = np.repeat(seqs, lens)
+        tok_pos = np.concatenate([np.arange(s0, s0 + ln) for s0, ln in zip(starts, lens)])
+        ref, order_seen = od.model_step(shape, mw, toks, tok_seq, tok_pos, kv)
+        assert order_seen == seqs
+        got, ids = logits.cpu().numpy(), nxt.cpu().numpy()
+        assert_close(f"continuous batching step {k} logits (sequences {seqs}, tokens {lens})", got, ref)
+        for j, sid in enumerate(seqs):
+            assert ids[j] == od.greedy_token(got[j])
+            if od.top2_gap(ref[j]) > 1e-2:
+                assert ids[j] == od.greedy_token(ref[j]), f"step {k} sequence {sid}"
+            state[sid][2] += lens[j]
+            state[sid][3] = [od.greedy_token(ref[j])]
+        for sid, last in finish_after.items():
+            if last == k:
+                row, npg = state[sid][0], state[sid][1]
+                pool_pages = row[:npg].copy()
+                L.llmdec_kv_pool_free(pool.handle, pool_pages)
+                assert ref_pool.free(pool_pages.tolist()) == op.OK
+                assert L.llmdec_kv_pool_free_count(pool.handle) == ref_pool.n_free
+                freed = set(pool_pages.tolist())
+                del state[sid]
+    # the newcomer really did take the finished sequence's pages
+    assert freed <= set(state[3][0][:state[3][1]].tolist())
+    # every cached K/V value of the live sequences, including those written into recycled pages
+    for layer in range(shape.n_layers):
+        kd, vd = pool.layer_views(layer)
+        kimg, vimg = R.host_u16(kd.contiguous()), R.Pool.v_logical(R.host_u16(vd.contiguous()))
+        got_kv, ref_kv = [], []
+        for sid, (row, npg, cached, _) in state.items():
+            for p in range(cached):
+                pg, off = op.slot_of(row, p)
+                got_kv += [f32_from_bf16(kimg[pg, :, off, :]), f32_from_bf16(vimg[pg, :, :, off])]
+                ref_kv += [kv.k[(layer, sid)][p], kv.v[(layer, sid)][p]]
+        assert_stored_bf16(f"continuous batching layer {layer} cached K/V", np.stack(got_kv), np.stack(ref_kv))

@@ -73,8 +73,8 @@ WsLayout ws_layout(const llmdec_config &c, int max_tokens, int max_seqs, int max
   size_t slots = 0;
   for (int n = 1; n <= S; ++n) {
     int ppp, parts;
-    decode_partition(n, c.n_heads, P, &ppp, &parts);
-    slots = std::max(slots, (size_t)n * c.n_heads * parts);
+    decode_partition(c, n, P, &ppp, &parts);
+    slots = std::max(slots, (size_t)n * c.n_heads * decode_blocks_per_seq(parts));
   }
   L.attn_slots = (int)slots;
   // split-k partial sums: the worst case over every streamed product (rows <= 64) this workspace can see

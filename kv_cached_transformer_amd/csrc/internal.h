@@ -79,8 +79,12 @@ struct WsLayout {
 };
 WsLayout ws_layout(const llmdec_config &cfg, int max_tokens, int max_seqs, int max_pages);
 
-// Decode-attention partitioning: pages per partition and partitions per row.
-void decode_partition(int n_seqs, int n_heads, int max_pages, int *pages_per_part, int *n_parts);
+// Decode-attention partitioning: pages per partition and partitions per (sequence, wave of heads) row.
+void decode_partition(const llmdec_config &cfg, int n_seqs, int max_pages, int *pages_per_part, int *n_parts);
+// Query heads one decode-attention wave serves (they share a K/V head): 1, 2 or 4.
+int decode_heads_per_wave(const llmdec_config &cfg);
+// Partial results per (sequence, head) of a decode with n_parts partitions: one per block of waves.
+int decode_blocks_per_seq(int n_parts);
 
 // ---------------------------------------------------------------- launchers (kernels_*.hip)
 void launch_pack_matrix(int rows, int cols, const uint16_t *src, uint16_t *dst, hipStream_t s, int nb_stride = 1);

@@ -74,6 +74,7 @@ __device__ inline void store_out(float v, int r, int c, int ld, float *out_f32, 
 // so every sequence's full first partitions are dispatched before the short
 // last ones, which fill in the tail.
 constexpr int DA_RING = 3;
+constexpr int DA_WAVES = 4;        // decode waves per block: consecutive partitions of one (sequence, heads)
 constexpr int kMaxPartPages = 16;  // pages per decode partition, at most (one page id per lane)
 
 __device__ inline uint32_t vword(const uint4 &v, int k) { return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w; }
@@ -107,8 +108,8 @@ __device__ inline float uniform_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
-template <int D, bool SHARED_KV>
-__global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict__ q, int ld_q, int n_heads,
+template <int D, int QH, bool SHARED_KV>
+__global__ __launch_bounds__(64 * DA_WAVES) void decode_attn_kernel(const float *__restrict__ q, int ld_q, int n_heads,
                                                          int n_kv_heads, const int32_t *__restrict__ ctx_lens,
                                                          const int32_t *__restrict__ block_tables, int max_pages,
                                                          const uint16_t *__restrict__ pool_k,
@@ -119,33 +120,41 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict
   constexpr int LPT = D / 8;      // lanes per token in K (each holds 8 dims)
   constexpr int G = 64 / LPT;     // token groups per K instruction
   constexpr int VE = D / 64;      // V dims per lane
-  // Grouped-query attention: query head h reads K/V head h / group.  Block x is (K/V head x % n_kv_heads,
-  // member x / n_kv_heads), so the query heads sharing a K/V head are launched n_kv_heads blocks apart;
+  // Grouped-query attention: query head h reads K/V head h / group.  A wave serves QH consecutive query
+  // heads h0..h0+QH-1 of one K/V head (QH = the group, at most 4), so each page it reads feeds QH score
+  // and value sums.  Where a group is larger than QH, its waves are launched n_kv_heads blocks apart:
   // blocks go round-robin to the 8 XCDs, so with n_kv_heads a multiple of 8 they share one L2.
   const int group = n_heads / n_kv_heads;
-  const int kvh = blockIdx.x % n_kv_heads, h = kvh * group + blockIdx.x / n_kv_heads;
-  const int s = blockIdx.y, part = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int kvh = blockIdx.x % n_kv_heads, h0 = kvh * group + (blockIdx.x / n_kv_heads) * QH;
+  const int s = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int part = blockIdx.z * DA_WAVES + wave;  // this wave's partition
   const int p0 = part * ppp;
   // Three independent reads leave together: the context length, this partition's block-table
   // entries (one per lane, validated once the length is known) and q.
   const int32_t *bt = block_tables + (size_t)s * max_pages;
   const int raw_pg = (lane < ppp && p0 + lane < max_pages) ? bt[p0 + lane] : -1;
-  const float *qp = q + (size_t)s * ld_q + h * D + (lane % (D / 8)) * 8;
-  const float4 qv0 = *reinterpret_cast<const float4 *>(qp);
-  const float4 qv1 = *reinterpret_cast<const float4 *>(qp + 4);
+  float4 qv0[QH], qv1[QH];
+#pragma unroll
+  for (int j = 0; j < QH; ++j) {
+    const float *qp = q + (size_t)s * ld_q + (h0 + j) * D + (lane % (D / 8)) * 8;
+    qv0[j] = *reinterpret_cast<const float4 *>(qp);
+    qv1[j] = *reinterpret_cast<const float4 *>(qp + 4);
+  }
   const int n_tok = ctx_lens[s] + 1;
   const int n_pages = (n_tok + 15) >> 4;
+  // the returns below are block-uniform (they depend on the sequence and the block only); a wave whose
+  // partition lies past the context still takes part in the block's combine with an empty result
   if (n_tok <= 0) {
-    if (lane == 0 && part == 0) raise_error(err, kErrPos);
+    if (threadIdx.x == 0 && blockIdx.z == 0) raise_error(err, kErrPos);
     return;
   }
-  if (p0 >= n_pages) return;
+  if (blockIdx.z * DA_WAVES * ppp >= n_pages) return;
   if (n_pages > max_pages) {
-    if (lane == 0) raise_error(err, kErrPos);
+    if (threadIdx.x == 0) raise_error(err, kErrPos);
     return;
   }
-  const int p1 = min(n_pages, p0 + ppp);
+  const int p1 = max(p0, min(n_pages, p0 + ppp));
   int my_pg = -1;  // lane i: page id of page p0 + i
   if (lane < p1 - p0) {
     my_pg = raw_pg;
@@ -154,23 +163,29 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict
       my_pg = -1;
     }
   }
-  uint32_t qh[4], ql[4];  // q * log2(e)/sqrt(D), dims 8(lane % LPT)..+7, as bf16 hi/lo pairs
-  {
+  uint32_t qh[QH][4], ql[QH][4];  // q * log2(e)/sqrt(D), dims 8(lane % LPT)..+7, as bf16 hi/lo pairs
+#pragma unroll
+  for (int jh = 0; jh < QH; ++jh) {
     const float scale = kLog2e * rsqrtf((float)D);
-    const float qv[8] = {qv0.x * scale, qv0.y * scale, qv0.z * scale, qv0.w * scale,
-                         qv1.x * scale, qv1.y * scale, qv1.z * scale, qv1.w * scale};
+    const float qv[8] = {qv0[jh].x * scale, qv0[jh].y * scale, qv0[jh].z * scale, qv0[jh].w * scale,
+                         qv1[jh].x * scale, qv1[jh].y * scale, qv1[jh].z * scale, qv1[jh].w * scale};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint16_t h0, l0, h1, l1;
-      split_bf16(qv[2 * j], h0, l0);
-      split_bf16(qv[2 * j + 1], h1, l1);
-      qh[j] = h0 | ((uint32_t)h1 << 16);
-      ql[j] = l0 | ((uint32_t)l1 << 16);
+      uint16_t a0, b0, a1, b1;
+      split_bf16(qv[2 * j], a0, b0);
+      split_bf16(qv[2 * j + 1], a1, b1);
+      qh[jh][j] = a0 | ((uint32_t)a1 << 16);
+      ql[jh][j] = b0 | ((uint32_t)b1 << 16);
     }
   }
-  float m = -1e30f, l = 0.f, o[VE];
+  float m[QH], l[QH], o[QH][VE];
 #pragma unroll
-  for (int e = 0; e < VE; ++e) o[e] = 0.f;
+  for (int jh = 0; jh < QH; ++jh) {
+    m[jh] = -1e30f;
+    l[jh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) o[jh][e] = 0.f;
+  }
 
   uint4 kb[DA_RING][NI];
   // V quarter i of a page: VW words (2 bf16 each), kept as one vector so the ring stays in fixed registers
@@ -181,7 +196,7 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict
   // of its own; an absent page (past the partition, or a rejected id) gets an empty resource, whose
   // loads read zeros without touching memory, so the ring below needs no branches.  Without grouping
   // every page is read once per step: the non-temporal policy keeps it from displacing anything in the
-  // caches (measured: 12% less time for the same bytes).  A K/V head shared by a group of query heads
+  // caches (measured: 12% less time for the same bytes).  A K/V head whose group spans several waves
   // is read by each of them, so there the pages are cached normally for the others to hit.
   constexpr int policy = SHARED_KV ? 0 : kLoadStream;
   const uint32_t lane_bytes = (uint32_t)lane * 16u;
@@ -206,55 +221,72 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict
   // One page with n_valid (wave-uniform) live tokens: 16, fewer on a sequence's last page, 0 for a
   // rejected page id.
   auto compute = [&](int b, int n_valid) {
-    float sc[NI];
-    float lm = -INFINITY;
+    // scores of the QH query heads for the page's 16 tokens (lane = token group, 8 dims)
+    float sc[QH][NI], lm[QH];
+#pragma unroll
+    for (int jh = 0; jh < QH; ++jh) lm[jh] = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const uint32_t w[4] = {kb[b][i].x, kb[b][i].y, kb[b][i].z, kb[b][i].w};
-      float a = 0.f;
+      const bool valid = G * i + lane / LPT < n_valid;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a = dot2_bf16(w[j], qh[j], dot2_bf16(w[j], ql[j], a));
-      a = group_sum<LPT>(a);
-      sc[i] = (G * i + lane / LPT < n_valid) ? a : -INFINITY;
-      lm = fmaxf(lm, sc[i]);
+      for (int jh = 0; jh < QH; ++jh) {
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a = dot2_bf16(w[j], qh[jh][j], dot2_bf16(w[j], ql[jh][j], a));
+        a = group_sum<LPT>(a);
+        sc[jh][i] = valid ? a : -INFINITY;
+        lm[jh] = fmaxf(lm[jh], sc[jh][i]);
+      }
     }
-    // page max and weight sum over the G groups: one value per group, read from its first lane
-    float pm = -INFINITY;
+    // per head: page max and weight sum over the G groups (one value per group, read from its first
+    // lane), then the 16 weights made wave-uniform: token t's weight sits in group t % G, slot t / G
+    float alpha[QH], pt[QH][16];
 #pragma unroll
-    for (int g = 0; g < G; ++g) pm = fmaxf(pm, uniform_f(lm, g * LPT));
-    const float m_new = fmaxf(m, pm);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    float pr[NI], ps = 0.f;
+    for (int jh = 0; jh < QH; ++jh) {
+      float pm = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);  // 0 for masked tokens
-      ps += pr[i];
+      for (int g = 0; g < G; ++g) pm = fmaxf(pm, uniform_f(lm[jh], g * LPT));
+      const float m_new = fmaxf(m[jh], pm);
+      alpha[jh] = __builtin_amdgcn_exp2f(m[jh] - m_new);
+      float pr[NI], ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(sc[jh][i] - m_new);  // 0 for masked tokens
+        ps += pr[i];
+      }
+      float gs = 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) gs += uniform_f(ps, g * LPT);
+      l[jh] = l[jh] * alpha[jh] + gs;
+      m[jh] = m_new;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) pt[jh][t] = uniform_f(pr[t / G], (t % G) * LPT);
     }
-    float gs = 0.f;
-#pragma unroll
-    for (int g = 0; g < G; ++g) gs += uniform_f(ps, g * LPT);
-    l = l * alpha + gs;
-    m = m_new;
-    // token t's weight sits in group t % G, slot t / G: all 16 become wave-uniform
-    float pt[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) pt[t] = uniform_f(pr[t / G], (t % G) * LPT);
     // slots past the last token hold whatever the pool held (possibly NaN): their weight is 0, and
-    // 0 * NaN would poison the sum, so their values are cleared through per-token mask words
+    // 0 * NaN would poison the sum, so their values are cleared through per-token mask words; each
+    // V value is unpacked once for all QH heads
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
-      float a = o[e] * alpha;
+      float a[QH];
+#pragma unroll
+      for (int jh = 0; jh < QH; ++jh) a[jh] = o[jh][e] * alpha[jh];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t m0 = (4 * i < n_valid ? 0xffffu : 0u) | (4 * i + 1 < n_valid ? 0xffff0000u : 0u);
         const uint32_t m1 = (4 * i + 2 < n_valid ? 0xffffu : 0u) | (4 * i + 3 < n_valid ? 0xffff0000u : 0u);
         const uint32_t w0 = vword(vb[b][i], 2 * e) & m0, w1 = vword(vb[b][i], 2 * e + 1) & m1;  // tokens 4i, 4i+1 | 4i+2, 4i+3
-        a = fmaf(pt[4 * i], bf16lo(w0), a);
-        a = fmaf(pt[4 * i + 1], bf16hi(w0), a);
-        a = fmaf(pt[4 * i + 2], bf16lo(w1), a);
-        a = fmaf(pt[4 * i + 3], bf16hi(w1), a);
+        const float v0 = bf16lo(w0), v1 = bf16hi(w0), v2 = bf16lo(w1), v3 = bf16hi(w1);
+#pragma unroll
+        for (int jh = 0; jh < QH; ++jh) {
+          a[jh] = fmaf(pt[jh][4 * i], v0, a[jh]);
+          a[jh] = fmaf(pt[jh][4 * i + 1], v1, a[jh]);
+          a[jh] = fmaf(pt[jh][4 * i + 2], v2, a[jh]);
+          a[jh] = fmaf(pt[jh][4 * i + 3], v3, a[jh]);
+        }
       }
-      o[e] = a;
+#pragma unroll
+      for (int jh = 0; jh < QH; ++jh) o[jh][e] = a[jh];
     }
   };
   // Ring of DA_RING pages: DA_RING - 1 in flight while one is consumed.  The page count is padded to
@@ -279,20 +311,44 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const float *__restrict
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  const int parts_here = (n_pages + ppp - 1) / ppp;
-  if (parts_here == 1) {
-    const float inv = 1.f / l;
+  // The block's waves hold consecutive partitions: merge their (max, sum, output) in LDS, so only one
+  // result per block leaves the CU.  Writes among the page reads cost more than their bytes (a probe
+  // of this kernel's read pattern lost 6 % to one 520-byte partial per wave).
+  __shared__ float cm[DA_WAVES][QH][2];
+  __shared__ float co[DA_WAVES][QH][D];
 #pragma unroll
-    for (int e = 0; e < VE; ++e)
-      store_out(o[e] * inv, s, h * D + lane * VE + e, n_heads * D, out_f32, out_hi, out_lo, kpad);
-  } else {
-    float *pp = partials + (((size_t)s * n_heads + h) * n_parts + part) * (D + 2);
+  for (int jh = 0; jh < QH; ++jh) {
     if (lane == 0) {
-      pp[0] = m;
-      pp[1] = l;
+      cm[wave][jh][0] = m[jh];
+      cm[wave][jh][1] = l[jh];
     }
 #pragma unroll
-    for (int e = 0; e < VE; ++e) pp[2 + lane * VE + e] = o[e];
+    for (int e = 0; e < VE; ++e) co[wave][jh][lane * VE + e] = o[jh][e];
+  }
+  __syncthreads();
+  const int blocks_here = (n_pages + DA_WAVES * ppp - 1) / (DA_WAVES * ppp);  // blocks covering the sequence
+  for (int idx = threadIdx.x; idx < QH * D; idx += 64 * DA_WAVES) {
+    const int jh = idx / D, d = idx % D, h = h0 + jh;
+    float mx = cm[0][jh][0];
+#pragma unroll
+    for (int w = 1; w < DA_WAVES; ++w) mx = fmaxf(mx, cm[w][jh][0]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < DA_WAVES; ++w) {  // in partition order
+      const float wt = exp2f(cm[w][jh][0] - mx);
+      L = fmaf(cm[w][jh][1], wt, L);
+      O = fmaf(co[w][jh][d], wt, O);
+    }
+    if (blocks_here == 1) {
+      store_out(O / L, s, h * D + d, n_heads * D, out_f32, out_hi, out_lo, kpad);
+    } else {
+      float *pp = partials + (((size_t)s * n_heads + h) * n_parts + blockIdx.z) * (D + 2);
+      if (d == 0) {
+        pp[0] = mx;
+        pp[1] = L;
+      }
+      pp[2 + d] = O;
+    }
   }
 }
 
@@ -348,11 +404,15 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(int n_heads, const in
   store_out(acc / L, s, h * D + d, n_heads * D, out_f32, out_hi, out_lo, kpad);
 }
 
-void decode_partition(int n_seqs, int n_heads, int max_pages, int *pages_per_part, int *n_parts) {
-  // Aim for ~8 waves per CU over 256 CUs counting every (sequence, head) row
-  // at full width; never split finer than one page, never coarser than 32.
-  const long rows = (long)n_seqs * n_heads;
-  int parts = (int)((2048 + rows - 1) / rows);
+void decode_partition(const llmdec_config &cfg, int n_seqs, int max_pages, int *pages_per_part, int *n_parts) {
+  // Aim for ~8 waves per CU over 256 CUs counting every (sequence, wave of heads) row at full width,
+  // QH times that where a wave serves QH query heads (its pages cost QH times the arithmetic, so shorter
+  // partitions keep the waves' lengths even); never split finer than one page, never coarser than
+  // kMaxPartPages.
+  const int qh = decode_heads_per_wave(cfg);
+  const long rows = (long)n_seqs * (cfg.n_heads / qh);
+  const long target = 2048L * qh;
+  int parts = (int)((target + rows - 1) / rows);
   parts = parts < 1 ? 1 : parts;
   int ppp = (max_pages + parts - 1) / parts;
   ppp = ppp < 1 ? 1 : (ppp > kMaxPartPages ? kMaxPartPages : ppp);
@@ -360,40 +420,64 @@ void decode_partition(int n_seqs, int n_heads, int max_pages, int *pages_per_par
   *n_parts = (max_pages + ppp - 1) / ppp;
 }
 
+int decode_blocks_per_seq(int n_parts) { return (n_parts + DA_WAVES - 1) / DA_WAVES; }
+
+int decode_heads_per_wave(const llmdec_config &cfg) {
+  const int g = cfg.n_heads / cfg.n_kv_heads;
+  return g % 4 == 0 ? 4 : (g % 2 == 0 ? 2 : 1);
+}
+
+template <int D, int QH>
+static void launch_decode_qh(const llmdec_config &cfg, dim3 grid, hipStream_t s, const float *q, int ld_q,
+                             const int32_t *ctx_lens, const int32_t *block_tables, int max_pages, const uint16_t *pk,
+                             const uint16_t *pv, int num_pages, int ppp, int n_parts, float *partials, float *out_f32,
+                             uint16_t *out_hi, uint16_t *out_lo, int kpad, uint32_t *err) {
+  if (cfg.n_heads / cfg.n_kv_heads > QH)  // a K/V head read by several waves
+    decode_attn_kernel<D, QH, true><<<grid, 64 * DA_WAVES, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, ctx_lens, block_tables,
+                                                        max_pages, pk, pv, num_pages, ppp, n_parts, partials, out_f32,
+                                                        out_hi, out_lo, kpad, err);
+  else
+    decode_attn_kernel<D, QH, false><<<grid, 64 * DA_WAVES, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, ctx_lens, block_tables,
+                                                         max_pages, pk, pv, num_pages, ppp, n_parts, partials, out_f32,
+                                                         out_hi, out_lo, kpad, err);
+}
+
+template <int D>
+static void launch_decode_d(const llmdec_config &cfg, int qh, dim3 grid, hipStream_t s, const float *q, int ld_q,
+                            const int32_t *ctx_lens, const int32_t *block_tables, int max_pages, const uint16_t *pk,
+                            const uint16_t *pv, int num_pages, int ppp, int n_parts, float *partials, float *out_f32,
+                            uint16_t *out_hi, uint16_t *out_lo, int kpad, uint32_t *err) {
+  if (qh == 4)
+    launch_decode_qh<D, 4>(cfg, grid, s, q, ld_q, ctx_lens, block_tables, max_pages, pk, pv, num_pages, ppp, n_parts,
+                           partials, out_f32, out_hi, out_lo, kpad, err);
+  else if (qh == 2)
+    launch_decode_qh<D, 2>(cfg, grid, s, q, ld_q, ctx_lens, block_tables, max_pages, pk, pv, num_pages, ppp, n_parts,
+                           partials, out_f32, out_hi, out_lo, kpad, err);
+  else
+    launch_decode_qh<D, 1>(cfg, grid, s, q, ld_q, ctx_lens, block_tables, max_pages, pk, pv, num_pages, ppp, n_parts,
+                           partials, out_f32, out_hi, out_lo, kpad, err);
+  const int n_seqs = (int)grid.y;
+  if (n_parts > 1)  // here: partial results per (sequence, head), one per block of DA_WAVES partitions
+    decode_combine_kernel<D><<<n_seqs * cfg.n_heads, D, 0, s>>>(cfg.n_heads, ctx_lens, max_pages, ppp * DA_WAVES,
+                                                                n_parts, partials, out_f32, out_hi, out_lo, kpad);
+}
+
 void launch_decode_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, const int32_t *ctx_lens,
                              const int32_t *block_tables, int max_pages, const uint16_t *pk, const uint16_t *pv,
                              int num_pages, float *partials, float *out_f32, uint16_t *out_hi, uint16_t *out_lo,
                              int kpad, uint32_t *err, hipStream_t s) {
   if (n_seqs <= 0) return;
+  const int qh = decode_heads_per_wave(cfg);
   int ppp, n_parts;
-  decode_partition(n_seqs, cfg.n_heads, max_pages, &ppp, &n_parts);
-  dim3 grid(cfg.n_heads, n_seqs, n_parts);
-  const bool shared = cfg.n_kv_heads < cfg.n_heads;
-  if (cfg.head_dim == 128) {
-    if (shared)
-      decode_attn_kernel<128, true><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, ctx_lens, block_tables,
-                                                        max_pages, pk, pv, num_pages, ppp, n_parts, partials, out_f32,
-                                                        out_hi, out_lo, kpad, err);
-    else
-      decode_attn_kernel<128, false><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, ctx_lens, block_tables,
-                                                         max_pages, pk, pv, num_pages, ppp, n_parts, partials, out_f32,
-                                                         out_hi, out_lo, kpad, err);
-    if (n_parts > 1)
-      decode_combine_kernel<128><<<n_seqs * cfg.n_heads, 128, 0, s>>>(cfg.n_heads, ctx_lens, max_pages, ppp, n_parts,
-                                                                     partials, out_f32, out_hi, out_lo, kpad);
-  } else {
-    if (shared)
-      decode_attn_kernel<64, true><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, ctx_lens, block_tables,
-                                                       max_pages, pk, pv, num_pages, ppp, n_parts, partials, out_f32,
-                                                       out_hi, out_lo, kpad, err);
-    else
-      decode_attn_kernel<64, false><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, ctx_lens, block_tables,
-                                                        max_pages, pk, pv, num_pages, ppp, n_parts, partials, out_f32,
-                                                        out_hi, out_lo, kpad, err);
-    if (n_parts > 1)
-      decode_combine_kernel<64><<<n_seqs * cfg.n_heads, 64, 0, s>>>(cfg.n_heads, ctx_lens, max_pages, ppp, n_parts,
-                                                                   partials, out_f32, out_hi, out_lo, kpad);
-  }
+  decode_partition(cfg, n_seqs, max_pages, &ppp, &n_parts);
+  const int n_blocks_z = decode_blocks_per_seq(n_parts);  // partial results per (sequence, head)
+  dim3 grid(cfg.n_heads / qh, n_seqs, n_blocks_z);
+  if (cfg.head_dim == 128)
+    launch_decode_d<128>(cfg, qh, grid, s, q, ld_q, ctx_lens, block_tables, max_pages, pk, pv, num_pages, ppp,
+                         n_blocks_z, partials, out_f32, out_hi, out_lo, kpad, err);
+  else
+    launch_decode_d<64>(cfg, qh, grid, s, q, ld_q, ctx_lens, block_tables, max_pages, pk, pv, num_pages, ppp,
+                        n_blocks_z, partials, out_f32, out_hi, out_lo, kpad, err);
 }
 
 // ---------------------------------------------------------------- prefill (causal, MFMA)

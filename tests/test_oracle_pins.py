@@ -376,3 +376,59 @@ def test_pool_alloc_free_semantics():
     assert pool.free([1]) == op.E_INVALID                      # double free
     assert pool.free([6]) == op.E_INVALID                      # foreign id
     assert pool.alloc(16, row2, 0, 4) == (op.OK, 1) and row2[0] == 1   # last returned is reused first
+
+
+# ----------------------------------------------------------------------------- group-quantized weights
+def test_dequantize_worked_example():
+    """A 1 x 256 row, two groups ([W] §4.2: 128 elements per group, a scale and a zero point each):
+    group 0 scale 0.5, zero 128; group 1 scale 2, zero 3.  Values worked by hand."""
+    from oracle import quant as oq
+    codes = np.zeros((1, 256), np.uint8)
+    codes[0, [0, 1, 127]] = [0, 255, 128]
+    codes[0, [128, 129, 255]] = [3, 4, 0]
+    w = oq.dequantize(codes, np.array([[0.5, 2.0]]), np.array([[128, 3]], np.uint8))
+    assert w[0, 0] == -64.0 and w[0, 1] == 63.5 and w[0, 127] == 0.0
+    assert w[0, 128] == 0.0 and w[0, 129] == 2.0 and w[0, 255] == -6.0
+    assert w[0, 2] == -64.0 and w[0, 130] == -6.0      # untouched codes (0) in each group
+
+
+def test_dequantize_group_boundaries_and_laws():
+    """Each scale and zero point reaches exactly its own 128 columns of its own row; equal codes and
+    zeros give 0; shifting codes and zeros together changes nothing; doubling a scale doubles its group."""
+    from oracle import quant as oq
+    r = np.random.default_rng(31)
+    rows, cols = 3, 512
+    codes = r.integers(60, 256, (rows, cols)).astype(np.uint8)
+    scales = r.uniform(0.01, 0.1, (rows, cols // 128))
+    zeros = r.integers(100, 156, (rows, cols // 128)).astype(np.uint8)
+    w = oq.dequantize(codes, scales, zeros)
+    for row in range(rows):
+        for g in range(cols // 128):
+            s2 = scales.copy()
+            s2[row, g] *= 2
+            d = oq.dequantize(codes, s2, zeros) - w
+            changed = np.zeros((rows, cols), bool)
+            changed[row, 128 * g:128 * (g + 1)] = True
+            assert np.allclose(d[changed], w[changed]) and np.all(d[~changed] == 0)
+    assert np.all(oq.dequantize(np.repeat(zeros, 128, axis=1), scales, zeros) == 0)
+    c1, z1 = codes - np.uint8(50), zeros - np.uint8(50)   # both shifted down, still in range
+    assert np.array_equal(oq.dequantize(c1, scales, z1), w)
+    unit = oq.dequantize(codes, np.ones_like(scales), np.zeros_like(zeros))
+    assert np.array_equal(unit, codes.astype(np.float64))
+
+
+def test_linear_q8_matches_dense_product_of_dequantized_rows():
+    """The quantized product is the plain product with the dequantized [out][in] matrix: row j of the
+    output is x . w_j, checked one output element at a time with a Python sum."""
+    from oracle import quant as oq
+    r = np.random.default_rng(32)
+    codes = r.integers(0, 256, (4, 256)).astype(np.uint8)
+    scales = r.uniform(0.01, 0.05, (4, 2))
+    zeros = r.integers(120, 136, (4, 2)).astype(np.uint8)
+    x = r.standard_normal((2, 256))
+    y = oq.linear_q8(x, codes, scales, zeros)
+    for i in range(2):
+        for j in range(4):
+            ref = sum(float(x[i, c]) * (int(codes[j, c]) - int(zeros[j, c // 128])) * float(scales[j, c // 128])
+                      for c in range(256))
+            assert abs(y[i, j] - ref) <= 1e-12 * (1 + abs(ref))

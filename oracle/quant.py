@@ -6,7 +6,9 @@ example 128 consecutive elements), each group carrying one scale and one zero po
 matrix product the integers are turned back into floating point through the scales.  The page gives
 no formula; the reading taken is the usual asymmetric one, value = (code - zero) * scale, with 8-bit
 unsigned codes and zero points and the groups running along each row (the input dimension of an
-[out][in] matrix).
+[out][in] matrix).  A row whose length is not a multiple of the group size ends with one shorter
+group (the page gives 128 as an example size and says nothing of rows that do not divide); it has
+its own scale and zero point like any other.
 """
 from __future__ import annotations
 
@@ -16,16 +18,16 @@ GROUP = 128
 
 
 def dequantize(codes, scales, zeros, group: int = GROUP) -> np.ndarray:
-    """codes [rows][cols] uint8, scales [rows][cols/group] float, zeros [rows][cols/group] uint8 ->
-    float64 [rows][cols] with w[r, c] = (codes[r, c] - zeros[r, c // group]) * scales[r, c // group]."""
+    """codes [rows][cols] uint8, scales and zeros [rows][ceil(cols/group)] -> float64 [rows][cols] with
+    w[r, c] = (codes[r, c] - zeros[r, c // group]) * scales[r, c // group]."""
     codes = np.asarray(codes)
     rows, cols = codes.shape
-    assert cols % group == 0, "cols must be a whole number of groups"
-    g = cols // group
-    q = codes.astype(np.float64).reshape(rows, g, group)
-    z = np.asarray(zeros, dtype=np.float64).reshape(rows, g, 1)
-    s = np.asarray(scales, dtype=np.float64).reshape(rows, g, 1)
-    return ((q - z) * s).reshape(rows, cols)
+    g = (cols + group - 1) // group
+    z = np.asarray(zeros, dtype=np.float64)
+    s = np.asarray(scales, dtype=np.float64)
+    assert z.shape == (rows, g) and s.shape == (rows, g), "one scale and one zero point per group"
+    col_group = np.arange(cols) // group            # the group of every column
+    return (codes.astype(np.float64) - z[:, col_group]) * s[:, col_group]
 
 
 def linear_q8(x, codes, scales, zeros) -> np.ndarray:

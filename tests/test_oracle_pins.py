@@ -432,3 +432,17 @@ def test_linear_q8_matches_dense_product_of_dequantized_rows():
             ref = sum(float(x[i, c]) * (int(codes[j, c]) - int(zeros[j, c // 128])) * float(scales[j, c // 128])
                       for c in range(256))
             assert abs(y[i, j] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_dequantize_short_last_group():
+    """A 1 x 130 row is a full group of 128 and a group of 2 with their own scale and zero point
+    (values worked by hand): group 0 scale 0.25 zero 10, group 1 scale 3 zero 7."""
+    from oracle import quant as oq
+    codes = np.full((1, 130), 10, np.uint8)
+    codes[0, 0], codes[0, 127], codes[0, 128], codes[0, 129] = 14, 2, 9, 7
+    w = oq.dequantize(codes, np.array([[0.25, 3.0]]), np.array([[10, 7]], np.uint8))
+    assert w.shape == (1, 130)
+    assert w[0, 0] == 1.0 and w[0, 127] == -2.0 and w[0, 1] == 0.0
+    assert w[0, 128] == 6.0 and w[0, 129] == 0.0
+    with pytest.raises(AssertionError):   # a missing group's scale is an error, not a silent reuse
+        oq.dequantize(codes, np.array([[0.25]]), np.array([[10]], np.uint8))

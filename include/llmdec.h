@@ -5,7 +5,7 @@
  * Pages the operations follow (cited by tag):
  *   [W] "企业官网建设流程全解析" (www.dpshk.com/news/4990443), the weights
  *       article: §1.1 forward skeleton, §1.2 where parameters live, §2.x
- *       weight layout [out][in].
+ *       weight layout [out][in], §4.2 group-quantized weights.
  *   [F] "大模型推理全流程解析：从权重加载到文本生成的工程实践"
  *       (www.stapisi.com/news/4049481): §2.2.1 embedding, §2.2.2 attention
  *       and KV cache, §2.2.3 lm_head and greedy choice, §4 cached greedy loop.
@@ -38,7 +38,8 @@
  *    carried as a bf16 pair hi + lo (about 17 significant bits) and multiply
  *    the bf16 weights on the matrix cores with fp32 accumulation; the
  *    residual stream, attention (scores, softmax, weighted sum) and logits
- *    are fp32.
+ *    are fp32.  Products with group-quantized weights run in fp32 from the
+ *    unrounded activation.
  *  - Not thread-safe per pool handle; distinct handles are independent.
  */
 #ifndef LLMDEC_H
@@ -310,6 +311,70 @@ llmdec_status llmdec_op_silu_mul(const float *gate, const float *up, int32_t row
 llmdec_status llmdec_op_lm_head_argmax(const float *x, int32_t rows, int32_t hidden, const void *lm_head_packed,
                                        int32_t vocab, int32_t *next, float *logits_out, void *ws, size_t ws_bytes,
                                        llmdec_stream stream);
+
+/* ------------------------------------------------------------------ group-quantized weights
+ * [W] §4.2: a matrix stored as integers in groups of 128 consecutive elements,
+ * each group with one scale and one zero point, turned back into floating
+ * point for the product.  Here the codes are 8-bit unsigned, the groups run
+ * along each row (the input dimension of an [out][in] matrix; a row's last
+ * group may be shorter), and
+ *   W[r][c] = (codes[r][c] - zeros[r][c/128]) * scales[r][c/128]
+ * with the scale a bf16 value.  Device pointers: codes uint8 [rows][cols],
+ * scales bf16 [rows][ceil(cols/128)], zeros uint8 [rows][ceil(cols/128)]. */
+typedef struct {
+  const void *codes, *scales, *zeros;
+} llmdec_q8_matrix;
+
+/* One layer with quantized matrices (norm gains stay bf16 [hidden]). */
+typedef struct {
+  const void *attn_norm;
+  llmdec_q8_matrix wq, wk, wv, wo;
+  const void *mlp_norm;
+  llmdec_q8_matrix w_gate, w_up, w_down;
+} llmdec_q8_layer_weights;
+
+/* A quantized layer packed by llmdec_q8_pack_layer (pointers into the
+ * caller's buffer): q|k|v fused into one matrix (wq rows, then wk, wv), gate
+ * and up into one ([w_gate; w_up], 2*intermediate rows). */
+typedef struct {
+  const void *attn_norm, *mlp_norm;
+  const void *w_qkv, *w_o, *w_gu, *w_down;
+} llmdec_q8_packed_layer;
+
+/* Bytes of a packed quantized rows x cols matrix: the codes as given
+ * (rows*cols bytes), then one 32-bit word per (row, group) holding the bf16
+ * scale and the zero point, ordered for the kernel's lanes and padded per
+ * row to a multiple of 32 words (the padding words are zero).  0 when the
+ * shape is unsupported: cols must be a multiple of 16 and at most 15360,
+ * rows a multiple of 4. */
+size_t llmdec_q8_matrix_bytes(int32_t rows, int32_t cols);
+/* Pack one quantized matrix into dev dst (>= q8_matrix_bytes).  The source
+ * may be freed once the stream has run.  Errors: E_INVALID for null
+ * pointers, an unsupported shape or dst_bytes too small. */
+llmdec_status llmdec_q8_pack_matrix(int32_t rows, int32_t cols, const llmdec_q8_matrix *src, void *dst,
+                                    size_t dst_bytes, llmdec_stream stream);
+/* Bytes of one packed quantized layer for cfg (0 if cfg is invalid or its
+ * matrices have an unsupported shape). */
+size_t llmdec_q8_packed_layer_bytes(const llmdec_config *cfg);
+llmdec_status llmdec_q8_pack_layer(const llmdec_config *cfg, const llmdec_q8_layer_weights *in, void *dst,
+                                   size_t dst_bytes, llmdec_q8_packed_layer *out, llmdec_stream stream);
+
+/* out[n] (+)= sum_k a[k] * W[n][k] for one dev fp32 row a [k_dim] and a
+ * packed quantized W [n_dim][k_dim], fp32 arithmetic throughout (the
+ * activation is not rounded).  accumulate = 0 stores, 1 adds into out.  No
+ * workspace.  Errors: E_INVALID for null pointers or a shape q8_matrix_bytes
+ * rejects. */
+llmdec_status llmdec_op_linear_q8(const float *a, int32_t k_dim, const void *w_q8_packed, int32_t n_dim, float *out,
+                                  int32_t accumulate, llmdec_stream stream);
+
+/* llmdec_layer_decode with quantized matrices, for a single sequence
+ * (n_seqs must be 1: the quantized products are matrix-vector products;
+ * more sequences return E_UNSUPPORTED).  Same arguments, workspace size
+ * (llmdec_workspace_bytes) and results otherwise. */
+llmdec_status llmdec_layer_decode_q8(const llmdec_config *cfg, const llmdec_q8_packed_layer *w, int32_t layer,
+                                     float *hidden, int32_t n_seqs, const int32_t *ctx_lens,
+                                     const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool, void *ws,
+                                     size_t ws_bytes, llmdec_stream stream);
 
 #ifdef __cplusplus
 }

@@ -626,3 +626,160 @@ extern "C" llmdec_status llmdec_op_lm_head_argmax(const float *x, int32_t rows, 
   launch_argmax(lg, rows, vocab, next, s);
   return check_launch("op_lm_head_argmax");
 }
+
+// ------------------------------------------------------------------ group-quantized weights
+// A quantized matrix is supported when its rows split into the four-row tasks of the matrix-vector
+// kernel and its columns into whole 16-byte lane chunks that fit the kernel's LDS staging of x.
+static bool q8_ok(int rows, int cols) {
+  // byte offsets inside the packed matrix stay below 2^31 (the kernel's buffer offsets)
+  return rows > 0 && rows % 4 == 0 && q8_shape_ok(cols) && q8_matrix_bytes(rows, cols) < (size_t)1 << 31;
+}
+
+extern "C" size_t llmdec_q8_matrix_bytes(int32_t rows, int32_t cols) {
+  return q8_ok(rows, cols) ? q8_matrix_bytes(rows, cols) : 0;
+}
+
+static bool q8_src_ok(const llmdec_q8_matrix *m) { return m && m->codes && m->scales && m->zeros; }
+
+extern "C" llmdec_status llmdec_q8_pack_matrix(int32_t rows, int32_t cols, const llmdec_q8_matrix *src, void *dst,
+                                              size_t dst_bytes, llmdec_stream stream) {
+  if (!q8_src_ok(src) || !dst) return set_error(LLMDEC_E_INVALID, "q8_pack_matrix: NULL pointer");
+  if (!q8_ok(rows, cols))
+    return set_error(LLMDEC_E_INVALID,
+                     "q8_pack_matrix: rows (%d) must be a positive multiple of 4, cols (%d) a positive multiple of 16 "
+                     "and at most 15360", rows, cols);
+  const size_t need = q8_matrix_bytes(rows, cols);
+  if (dst_bytes < need) return set_error(LLMDEC_E_INVALID, "q8_pack_matrix: dst holds %zu bytes, %zu needed", dst_bytes, need);
+  launch_q8_pack((const uint8_t *)src->codes, (const uint16_t *)src->scales, (const uint8_t *)src->zeros, rows, cols,
+                 (uint8_t *)dst, rows, 0, (hipStream_t)stream);
+  return check_launch("q8_pack_matrix");
+}
+
+static size_t q8_layer_parts(const llmdec_config &c, size_t off[6]) {
+  const int h = c.hidden, I = c.intermediate;
+  size_t o = 0;
+  off[0] = o;  // attn_norm
+  o += al((size_t)h * 2);
+  off[1] = o;  // mlp_norm
+  o += al((size_t)h * 2);
+  off[2] = o;  // q|k|v
+  o += al(q8_matrix_bytes(qkv_cols(c), h));
+  off[3] = o;  // o
+  o += al(q8_matrix_bytes(h, h));
+  off[4] = o;  // [gate; up]
+  o += al(q8_matrix_bytes(2 * I, h));
+  off[5] = o;  // down
+  o += al(q8_matrix_bytes(h, I));
+  return o;
+}
+
+static bool q8_layer_ok(const llmdec_config &c) {
+  return q8_ok(qkv_cols(c), c.hidden) && q8_ok(c.hidden, c.hidden) && q8_ok(2 * c.intermediate, c.hidden) &&
+         q8_ok(c.hidden, c.intermediate) && c.intermediate % 2 == 0;
+}
+
+extern "C" size_t llmdec_q8_packed_layer_bytes(const llmdec_config *cfg) {
+  if (check_config(cfg, "q8_packed_layer_bytes") != LLMDEC_OK || !q8_layer_ok(*cfg)) return 0;
+  size_t off[6];
+  return q8_layer_parts(*cfg, off);
+}
+
+extern "C" llmdec_status llmdec_q8_pack_layer(const llmdec_config *cfg, const llmdec_q8_layer_weights *in, void *dst,
+                                             size_t dst_bytes, llmdec_q8_packed_layer *out, llmdec_stream stream) {
+  const char *who = "q8_pack_layer";
+  llmdec_status st = check_config(cfg, who);
+  if (st != LLMDEC_OK) return st;
+  if (!in || !dst || !out || !in->attn_norm || !in->mlp_norm || !q8_src_ok(&in->wq) || !q8_src_ok(&in->wk) ||
+      !q8_src_ok(&in->wv) || !q8_src_ok(&in->wo) || !q8_src_ok(&in->w_gate) || !q8_src_ok(&in->w_up) ||
+      !q8_src_ok(&in->w_down))
+    return set_error(LLMDEC_E_INVALID, "%s: NULL pointer", who);
+  if (!q8_layer_ok(*cfg))
+    return set_error(LLMDEC_E_UNSUPPORTED, "%s: hidden %d / intermediate %d: quantized matrices need row counts that are "
+                     "multiples of 4 and input widths that are multiples of 16, at most 15360", who, cfg->hidden,
+                     cfg->intermediate);
+  size_t off[6];
+  const size_t need = q8_layer_parts(*cfg, off);
+  if (dst_bytes < need) return set_error(LLMDEC_E_INVALID, "%s: dst holds %zu bytes, %zu needed", who, dst_bytes, need);
+  const int h = cfg->hidden, I = cfg->intermediate, kv = kv_cols(*cfg), nqkv = qkv_cols(*cfg);
+  hipStream_t s = (hipStream_t)stream;
+  char *d = (char *)dst;
+  if (hipMemcpyAsync(d + off[0], in->attn_norm, (size_t)h * 2, hipMemcpyDeviceToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(d + off[1], in->mlp_norm, (size_t)h * 2, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return set_error(LLMDEC_E_HIP, "%s: copy of the norm gains failed", who);
+  auto pack = [&](const llmdec_q8_matrix &m, int rows, int cols, size_t at_off, int dst_rows, int row0) {
+    launch_q8_pack((const uint8_t *)m.codes, (const uint16_t *)m.scales, (const uint8_t *)m.zeros, rows, cols,
+                   (uint8_t *)(d + at_off), dst_rows, row0, s);
+  };
+  pack(in->wq, h, h, off[2], nqkv, 0);
+  pack(in->wk, kv, h, off[2], nqkv, h);
+  pack(in->wv, kv, h, off[2], nqkv, h + kv);
+  pack(in->wo, h, h, off[3], h, 0);
+  pack(in->w_gate, I, h, off[4], 2 * I, 0);
+  pack(in->w_up, I, h, off[4], 2 * I, I);
+  pack(in->w_down, h, I, off[5], h, 0);
+  st = check_launch(who);
+  if (st != LLMDEC_OK) return st;
+  out->attn_norm = d + off[0];
+  out->mlp_norm = d + off[1];
+  out->w_qkv = d + off[2];
+  out->w_o = d + off[3];
+  out->w_gu = d + off[4];
+  out->w_down = d + off[5];
+  return LLMDEC_OK;
+}
+
+extern "C" llmdec_status llmdec_op_linear_q8(const float *a, int32_t k_dim, const void *w_q8_packed, int32_t n_dim,
+                                            float *out, int32_t accumulate, llmdec_stream stream) {
+  if (!a || !w_q8_packed || !out) return set_error(LLMDEC_E_INVALID, "op_linear_q8: NULL pointer");
+  if (!q8_ok(n_dim, k_dim))
+    return set_error(LLMDEC_E_INVALID, "op_linear_q8: n=%d k=%d unsupported (n a multiple of 4, k of 16, k <= 15360)",
+                     n_dim, k_dim);
+  launch_q8_gemv(a, (const uint8_t *)w_q8_packed, n_dim, k_dim, accumulate ? kAccumulate : kStore, out,
+                 (hipStream_t)stream);
+  return check_launch("op_linear_q8");
+}
+
+extern "C" llmdec_status llmdec_layer_decode_q8(const llmdec_config *cfg, const llmdec_q8_packed_layer *w,
+                                               int32_t layer, float *hidden, int32_t n_seqs, const int32_t *ctx_lens,
+                                               const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool,
+                                               void *ws, size_t ws_bytes, llmdec_stream stream) {
+  const char *who = "layer_decode_q8";
+  llmdec_status st = check_config(cfg, who);
+  if (st != LLMDEC_OK) return st;
+  if (!w || !w->attn_norm || !w->mlp_norm || !w->w_qkv || !w->w_o || !w->w_gu || !w->w_down)
+    return set_error(LLMDEC_E_INVALID, "%s: packed layer weights missing", who);
+  if (!q8_layer_ok(*cfg)) return set_error(LLMDEC_E_UNSUPPORTED, "%s: shape unsupported for quantized matrices", who);
+  st = check_pool(pool, *cfg, layer, who);
+  if (st != LLMDEC_OK) return st;
+  if (!hidden || !ctx_lens || !block_tables) return set_error(LLMDEC_E_INVALID, "%s: NULL device pointer", who);
+  if (n_seqs != 1)
+    return set_error(LLMDEC_E_UNSUPPORTED, "%s: n_seqs=%d; the quantized products serve one sequence", who, n_seqs);
+  if (max_pages <= 0) return set_error(LLMDEC_E_INVALID, "%s: max_pages=%d out of range", who, max_pages);
+  const WsLayout L = ws_layout(*cfg, 1, 1, max_pages);
+  st = check_ws(ws, ws_bytes, L.total, who);
+  if (st != LLMDEC_OK) return st;
+
+  const llmdec_config &c = *cfg;
+  const int h = c.hidden, I = c.intermediate, nqkv = qkv_cols(c);
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t *err = at<uint32_t>(ws, L.err);
+  // one row: the fp32 activations fit in the packed activation planes' space
+  float *y = at<float>(ws, L.act_h), *u = at<float>(ws, L.act_i), *qkv = at<float>(ws, L.qkv);
+  uint16_t *pk, *pv;
+  pool_layer(pool, layer, &pk, &pv);
+  // x += Wo . attn(rope(Wq y), rope(Wk y), Wv y),  y = RMSNorm(x)
+  launch_rmsnorm(hidden, h, nullptr, 1, (const uint16_t *)w->attn_norm, 1, h, c.rms_eps, err, y, nullptr, nullptr, 0,
+                 nullptr, Splits{}, s);
+  launch_q8_gemv(y, (const uint8_t *)w->w_qkv, nqkv, h, kStore, qkv, s);
+  launch_rope_append(c, qkv, nullptr, Splits{}, nqkv, 1, 1, nullptr, ctx_lens, block_tables, max_pages, pk, pv,
+                     pool->num_pages, err, s);
+  launch_decode_attention(c, qkv, nqkv, 1, ctx_lens, block_tables, max_pages, pk, pv, pool->num_pages,
+                          at<float>(ws, L.attn_part), y, nullptr, nullptr, 0, err, s);
+  launch_q8_gemv(y, (const uint8_t *)w->w_o, h, h, kAccumulate, hidden, s);
+  // x += Wd (silu(Wg y) * (Wu y)),  y = RMSNorm(x)
+  launch_rmsnorm(hidden, h, nullptr, 1, (const uint16_t *)w->mlp_norm, 1, h, c.rms_eps, err, y, nullptr, nullptr, 0,
+                 nullptr, Splits{}, s);
+  launch_q8_gemv(y, (const uint8_t *)w->w_gu, 2 * I, h, kSiluMul, u, s);
+  launch_q8_gemv(u, (const uint8_t *)w->w_down, h, I, kAccumulate, hidden, s);
+  return check_launch(who);
+}

@@ -1,0 +1,250 @@
+// Group-quantized weight products for single-token decode: out[n] = sum_k x[k] * W[n][k] with
+// W[n][k] = (codes[n][k] - zero[n][g]) * scale[n][g], g = k / 128 ("企业官网建设流程全解析" §4.2:
+// integer weights in groups of 128 elements, one scale and one zero point per group, turned back
+// into floating point before the product).
+//
+// One row of activations makes this a matrix-vector product: every code is used once, so the
+// kernel is bound by the HBM read of the codes (1 byte per weight, plus 4 bytes of scale and zero
+// point per group of 128).  No matrix cores: a code becomes fp32 in one conversion and meets its
+// activation in one fma, and the zero point and scale are applied once per 16 codes:
+//   sum_k x_k (c_k - z) s = s * (sum_k x_k c_k - z * sum_k x_k)
+// over the 16 columns a lane holds (they always lie in one group), with the 16-column sums of x
+// formed once per block.
+//
+// Work: a wave owns four output rows and streams them over the whole k range, 1 KiB of codes per
+// row per step (lane l reads columns 1024 s + 16 l .. +15 of each row, a 16-byte load), with the
+// steps of a row kept in flight ahead of the arithmetic.  x lives in LDS as fp32, stored by
+// quarter-chunks (float4 j of chunk c at [j][c]) so that the lanes of one ds_read_b128 read
+// consecutive 16-byte words.
+//
+// Packed layout of a quantized matrix (llmdec_q8_pack_matrix): the codes as given, [rows][cols]
+// bytes, followed by the group metadata, one 32-bit word per (row, group): bf16 scale bits in the
+// high half, zero point in the low byte.  Within a row the words are ordered for the lanes: for
+// steps 4t..4t+3, the 8 lanes that share a group in every step (lanes 8h..8h+7) find their four
+// words (groups 8(4t+i) + h, i = 0..3) as one 16-byte run at word 32t + 4h, so one load every four
+// steps brings a lane all the metadata it needs.  A row's metadata is 128 bytes per four steps,
+// padded with zero words (scale 0).
+#include "common.h"
+#include "internal.h"
+
+namespace llmdec {
+
+constexpr int kQGroup = 128;       // elements per quantization group
+constexpr int kQStepCols = 1024;   // columns per wave step: 64 lanes x 16 codes
+constexpr int kQMaxSteps = 15;     // k <= 15360: x (fp32) and its chunk sums fit a 64 KiB block's LDS
+
+__host__ __device__ inline int q8_steps(int k) { return (k + kQStepCols - 1) / kQStepCols; }
+__host__ __device__ inline int q8_meta_quads(int k) { return (q8_steps(k) + 3) / 4; }
+// bytes of metadata per row: 32 words per four steps
+__host__ __device__ inline size_t q8_meta_row_bytes(int k) { return (size_t)q8_meta_quads(k) * 128; }
+
+size_t q8_matrix_bytes(int rows, int cols) {
+  return (size_t)rows * cols + (size_t)rows * q8_meta_row_bytes(cols);
+}
+
+// ---------------------------------------------------------------- packing
+// One block per source row: copy the row's codes to row dst_row0 + r of the destination, and write its
+// metadata words in lane order.  cols % 16 == 0.
+__global__ void q8_pack_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+                               const uint8_t *__restrict__ zeros, int cols, uint8_t *__restrict__ dst,
+                               int dst_rows, int dst_row0) {
+  const int r = blockIdx.x;
+  const int groups = (cols + kQGroup - 1) / kQGroup;
+  const uint4 *src = reinterpret_cast<const uint4 *>(codes + (size_t)r * cols);
+  uint4 *out = reinterpret_cast<uint4 *>(dst + (size_t)(dst_row0 + r) * cols);
+  for (int i = threadIdx.x; i < cols / 16; i += blockDim.x) out[i] = src[i];
+  const int words = q8_meta_quads(cols) * 32;
+  uint32_t *meta = reinterpret_cast<uint32_t *>(dst + (size_t)dst_rows * cols +
+                                                (size_t)(dst_row0 + r) * q8_meta_row_bytes(cols));
+  for (int w = threadIdx.x; w < words; w += blockDim.x) {
+    const int t = w >> 5, h = (w >> 2) & 7, i = w & 3;
+    const int g = 8 * (4 * t + i) + h;
+    uint32_t v = 0;
+    if (g < groups) v = ((uint32_t)scales[(size_t)r * groups + g] << 16) | zeros[(size_t)r * groups + g];
+    meta[w] = v;
+  }
+}
+
+void launch_q8_pack(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros, int rows, int cols,
+                    uint8_t *dst, int dst_rows, int dst_row0, hipStream_t s) {
+  if (rows > 0) q8_pack_kernel<<<rows, 256, 0, s>>>(codes, scales, zeros, cols, dst, dst_rows, dst_row0);
+}
+
+// ---------------------------------------------------------------- matrix-vector product
+// Output modes: kStore out[n] = v; kAccumulate out[n] += v (the residual stream); kSiluMul: the
+// matrix is [gate; up] (2 n_out rows), a wave owns gate rows 2t, 2t+1 and up rows 2t, 2t+1, and
+// writes out[n] = silu(gate_n) * up_n.
+struct Q8Args {
+  const float *x;         // [k] fp32
+  const uint8_t *w;       // packed matrix (codes, then metadata)
+  int rows;               // rows of the packed matrix
+  int k;
+  int n_tasks;            // waves with work: rows / 4 (store, accumulate) or n_out / 2 (SwiGLU)
+  int n_out;              // SwiGLU: rows / 2
+  float *out;
+};
+
+__device__ inline float q8_silu(float g) { return g / (1.0f + expf(-g)); }
+
+// Steps of a row kept in flight ahead of the arithmetic.
+template <int NSTEP> struct Q8Ring {
+  static constexpr int D = NSTEP < 6 ? NSTEP : 6;
+};
+
+template <int NSTEP, int MODE>
+__global__ __launch_bounds__(512) void q8_gemv_kernel(Q8Args a) {
+  constexpr int NCH = NSTEP * 64;  // 16-column chunks of x held in LDS (columns past k are zero)
+  constexpr int D = Q8Ring<NSTEP>::D;
+  constexpr int NQ = (NSTEP + 3) / 4;
+  extern __shared__ float4 smem[];
+  float4 *xq = smem;                                         // [4][NCH]: quarter j of chunk c
+  float *xsum = reinterpret_cast<float *>(smem + 4 * NCH);  // [NCH]: sum of the chunk's 16 values
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int task = blockIdx.x * (blockDim.x >> 6) + wave;
+  const bool active = task < a.n_tasks;  // wave-uniform
+  const int k = a.k;
+
+  // the wave's four rows (scalar)
+  int row[4];
+  if (MODE == kSiluMul) {
+    row[0] = 2 * task, row[1] = 2 * task + 1, row[2] = a.n_out + 2 * task, row[3] = a.n_out + 2 * task + 1;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) row[r] = 4 * task + r;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) row[r] = active ? row[r] : 0;
+
+  // Codes: one resource over the whole matrix; a lane past the row's end gets an offset past the
+  // resource (reads zeros, touches nothing), so every load is unconditional.
+  const size_t code_bytes = (size_t)a.rows * k;
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.w, code_bytes);
+  const size_t mrow = q8_meta_row_bytes(k);
+  const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.w + code_bytes, (size_t)a.rows * mrow);
+
+  uint4 cb[NSTEP][4];  // fully unrolled: only D steps are live at a time
+  uint4 mb[NQ][4];
+  auto issue = [&](int s) {
+    const int col = s * kQStepCols + lane * 16;
+    const uint32_t voff = col < k ? (uint32_t)col : 0x80000000u;
+    if (s % 4 == 0) {
+      const uint32_t moff = (uint32_t)(s / 4) * 128u + (uint32_t)(lane >> 3) * 16u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mb[s / 4][r] = buffer_load16(rm, moff, (uint32_t)((size_t)row[r] * mrow), 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cb[s][r] = buffer_load16(rc, voff, (uint32_t)((size_t)row[r] * k), kLoadStream);
+  };
+  // the codes do not depend on x: start them before x is staged (an idle wave issues nothing)
+  if (active) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      issue(s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // stage x: thread i takes columns 8i..8i+7 (two quarter-chunks)
+  for (int i = threadIdx.x; i < NCH * 2; i += blockDim.x) {
+    const int c0 = 8 * i;
+    float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+    if (c0 < k) {  // k % 16 == 0, so 8 columns are either all in or all out
+      const float4 *p = reinterpret_cast<const float4 *>(a.x + c0);
+      v0 = p[0];
+      v1 = p[1];
+    }
+    const int ch = c0 >> 4, j = (c0 >> 2) & 3;  // j is 0 or 2
+    xq[j * NCH + ch] = v0;
+    xq[(j + 1) * NCH + ch] = v1;
+  }
+  __syncthreads();
+  for (int ch = threadIdx.x; ch < NCH; ch += blockDim.x) {
+    float t = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = xq[j * NCH + ch];
+      t += v.x + v.y + v.z + v.w;
+    }
+    xsum[ch] = t;
+  }
+  __syncthreads();
+  if (!active) return;  // no barrier follows
+
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NSTEP; ++s) {
+    if (s + D < NSTEP) issue(s + D);
+    __builtin_amdgcn_sched_barrier(0);
+    const int ch = s * 64 + lane;
+    float xv[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = xq[j * NCH + ch];
+      xv[4 * j] = v.x, xv[4 * j + 1] = v.y, xv[4 * j + 2] = v.z, xv[4 * j + 3] = v.w;
+    }
+    const float xs = xsum[ch];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t cw[4] = {cb[s][r].x, cb[s][r].y, cb[s][r].z, cb[s][r].w};
+      float d = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        d = fmaf(xv[4 * j], (float)(cw[j] & 0xffu), d);
+        d = fmaf(xv[4 * j + 1], (float)((cw[j] >> 8) & 0xffu), d);
+        d = fmaf(xv[4 * j + 2], (float)((cw[j] >> 16) & 0xffu), d);
+        d = fmaf(xv[4 * j + 3], (float)(cw[j] >> 24), d);
+      }
+      const uint4 mq = mb[s / 4][r];
+      const uint32_t m = (s & 3) == 0 ? mq.x : (s & 3) == 1 ? mq.y : (s & 3) == 2 ? mq.z : mq.w;
+      const float scale = __uint_as_float(m & 0xffff0000u), zero = (float)(m & 0xffu);
+      acc[r] = fmaf(scale, fmaf(-zero, xs, d), acc[r]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = wave_sum(acc[r]);
+  if (lane == 0) {
+    if (MODE == kSiluMul) {
+      *reinterpret_cast<float2 *>(a.out + 2 * task) =
+          make_float2(q8_silu(acc[0]) * acc[2], q8_silu(acc[1]) * acc[3]);
+    } else {
+      float4 *o = reinterpret_cast<float4 *>(a.out + 4 * task);
+      float4 v = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      if (MODE == kAccumulate) vadd(v, *o);
+      *o = v;
+    }
+  }
+}
+
+template <int MODE> static void q8_dispatch(int nstep, const Q8Args &a, int blocks, int threads, hipStream_t s) {
+  const size_t lds = (size_t)nstep * 64 * (4 * sizeof(float4) + sizeof(float));
+  switch (nstep) {
+#define Q8_CASE(N) \
+  case N: q8_gemv_kernel<N, MODE><<<blocks, threads, lds, s>>>(a); break;
+    Q8_CASE(1) Q8_CASE(2) Q8_CASE(3) Q8_CASE(4) Q8_CASE(5) Q8_CASE(6) Q8_CASE(7) Q8_CASE(8)
+    Q8_CASE(9) Q8_CASE(10) Q8_CASE(11) Q8_CASE(12) Q8_CASE(13) Q8_CASE(14) Q8_CASE(15)
+#undef Q8_CASE
+    default: break;
+  }
+}
+
+bool q8_shape_ok(int k) { return k > 0 && k % 16 == 0 && q8_steps(k) <= kQMaxSteps; }
+
+void launch_q8_gemv(const float *x, const uint8_t *w, int rows, int k, int mode, float *out, hipStream_t s) {
+  Q8Args a;
+  a.x = x, a.w = w, a.rows = rows, a.k = k, a.out = out;
+  a.n_out = mode == kSiluMul ? rows / 2 : rows;
+  a.n_tasks = rows / 4;  // four matrix rows per wave in every mode
+  if (a.n_tasks <= 0) return;
+  // 8 waves per block share one staging of x, unless that would leave CUs without two blocks each
+  const int wpb = a.n_tasks >= 8 * 512 ? 8 : 4;
+  const int blocks = (a.n_tasks + wpb - 1) / wpb;
+  const int nstep = q8_steps(k);
+  if (mode == kSiluMul) q8_dispatch<kSiluMul>(nstep, a, blocks, wpb * 64, s);
+  else if (mode == kAccumulate) q8_dispatch<kAccumulate>(nstep, a, blocks, wpb * 64, s);
+  else q8_dispatch<kStore>(nstep, a, blocks, wpb * 64, s);
+}
+
+}  // namespace llmdec

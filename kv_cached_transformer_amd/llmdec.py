@@ -45,6 +45,19 @@ class llmdec_model_weights(C.Structure):
                 ("lm_head", C.c_void_p)]
 
 
+class llmdec_q8_matrix(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("codes", "scales", "zeros")]
+
+
+class llmdec_q8_layer_weights(C.Structure):
+    _fields_ = [("attn_norm", C.c_void_p)] + [(n, llmdec_q8_matrix) for n in ("wq", "wk", "wv", "wo")] + \
+               [("mlp_norm", C.c_void_p)] + [(n, llmdec_q8_matrix) for n in ("w_gate", "w_up", "w_down")]
+
+
+class llmdec_q8_packed_layer(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("attn_norm", "mlp_norm", "w_qkv", "w_o", "w_gu", "w_down")]
+
+
 _lib = None
 
 _P, _I, _Z, _F = C.c_void_p, C.c_int32, C.c_size_t, C.c_float
@@ -80,6 +93,14 @@ _SIGS = {
     "llmdec_op_prefill_attention": (_I, [_CFG, _P, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, _Z, _P]),
     "llmdec_op_silu_mul": (_I, [_P, _P, _I, _I, _P, _P]),
     "llmdec_op_lm_head_argmax": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _Z, _P]),
+    "llmdec_q8_matrix_bytes": (_Z, [_I, _I]),
+    "llmdec_q8_pack_matrix": (_I, [_I, _I, C.POINTER(llmdec_q8_matrix), _P, _Z, _P]),
+    "llmdec_q8_packed_layer_bytes": (_Z, [_CFG]),
+    "llmdec_q8_pack_layer": (_I, [_CFG, C.POINTER(llmdec_q8_layer_weights), _P, _Z, C.POINTER(llmdec_q8_packed_layer),
+                                  _P]),
+    "llmdec_op_linear_q8": (_I, [_P, _I, _P, _I, _P, _I, _P]),
+    "llmdec_layer_decode_q8": (_I, [_CFG, C.POINTER(llmdec_q8_packed_layer), _I, _P, _I, _P, _P, _I, _P, _P, _Z,
+                                    _P]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -265,3 +286,31 @@ def llmdec_op_silu_mul(gate, up, rows, n, out, stream=0):
 def llmdec_op_lm_head_argmax(x, rows, hidden, lm_head_packed, vocab, next_tokens, logits_out, ws, ws_bytes, stream=0):
     _check(lib().llmdec_op_lm_head_argmax(x, rows, hidden, lm_head_packed, vocab, next_tokens, logits_out, ws,
                                           ws_bytes, stream))
+
+
+def llmdec_q8_matrix_bytes(rows, cols):
+    return lib().llmdec_q8_matrix_bytes(rows, cols)
+
+
+def llmdec_q8_pack_matrix(rows, cols, src: llmdec_q8_matrix, dst, dst_bytes, stream=0):
+    _check(lib().llmdec_q8_pack_matrix(rows, cols, C.byref(src), dst, dst_bytes, stream))
+
+
+def llmdec_q8_packed_layer_bytes(cfg):
+    return lib().llmdec_q8_packed_layer_bytes(C.byref(cfg))
+
+
+def llmdec_q8_pack_layer(cfg, weights: llmdec_q8_layer_weights, dst, dst_bytes, stream=0) -> llmdec_q8_packed_layer:
+    out = llmdec_q8_packed_layer()
+    _check(lib().llmdec_q8_pack_layer(C.byref(cfg), C.byref(weights), dst, dst_bytes, C.byref(out), stream))
+    return out
+
+
+def llmdec_op_linear_q8(a, k_dim, w_q8_packed, n_dim, out, accumulate, stream=0):
+    _check(lib().llmdec_op_linear_q8(a, k_dim, w_q8_packed, n_dim, out, int(accumulate), stream))
+
+
+def llmdec_layer_decode_q8(cfg, w, layer, hidden, n_seqs, ctx_lens, block_tables, max_pages, pool, ws, ws_bytes,
+                           stream=0):
+    _check(lib().llmdec_layer_decode_q8(C.byref(cfg), C.byref(w), layer, hidden, n_seqs, ctx_lens, block_tables,
+                                        max_pages, pool, ws, ws_bytes, stream))

@@ -58,6 +58,46 @@ class PackedMatrix:
         self.ptr = self.buf.data_ptr()
 
 
+def dev_u8(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to("cuda")
+
+
+def _q8_upload(m):
+    """(codes, scales bits, zeros) host arrays -> device tensors and the llmdec_q8_matrix over them."""
+    codes, scales, zeros = m
+    t = (dev_u8(codes), dev_u16(scales), dev_u8(zeros))
+    return t, L.llmdec_q8_matrix(*(x.data_ptr() for x in t))
+
+
+class Q8Matrix:
+    """One group-quantized matrix packed for the kernels; owns its device buffer."""
+
+    def __init__(self, m):
+        rows, cols = m[0].shape
+        nbytes = L.llmdec_q8_matrix_bytes(rows, cols)
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        src, struct = _q8_upload(m)
+        L.llmdec_q8_pack_matrix(rows, cols, struct, self.buf.data_ptr(), nbytes, stream())
+        torch.cuda.current_stream().synchronize()
+        del src
+        self.ptr = self.buf.data_ptr()
+
+
+class Q8Layer:
+    """One layer with group-quantized matrices, packed; owns its device buffer."""
+
+    def __init__(self, cfg, tensors: dict):
+        nbytes = L.llmdec_q8_packed_layer_bytes(cfg)
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        norms = {k: dev_u16(tensors[k]) for k in ("attn_norm", "mlp_norm")}
+        up = {k: _q8_upload(tensors[k]) for k in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")}
+        w = L.llmdec_q8_layer_weights(norms["attn_norm"].data_ptr(), *(up[k][1] for k in ("wq", "wk", "wv", "wo")),
+                                      norms["mlp_norm"].data_ptr(), *(up[k][1] for k in ("w_gate", "w_up", "w_down")))
+        self.struct = L.llmdec_q8_pack_layer(cfg, w, self.buf.data_ptr(), nbytes, stream())
+        torch.cuda.current_stream().synchronize()
+        del up, norms
+
+
 class Pool:
     """A device KV pool plus its host handle."""
 

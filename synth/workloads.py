@@ -155,6 +155,32 @@ def model_weights(workload: int, shape: ModelShape) -> ModelWeights:
     )
 
 
+# group-quantized matrices: codes uniform over the 8-bit range, zero points near its middle, bf16 scales
+# sized so that (code - zero) * scale spreads like the N(0, 0.02^2) bf16 matrices (codes uniform on
+# 0..255 around a zero near 128 have a standard deviation of about 74)
+S_QUANT = 1000
+QGROUP = 128
+
+
+def q8_matrix(workload: int, layer: int, idx: int, rows: int, cols: int):
+    """(codes uint8 [rows][cols], scales bf16 bits [rows][g], zeros uint8 [rows][g]), g = ceil(cols / 128)."""
+    g = (cols + QGROUP - 1) // QGROUP
+    key = (workload, S_QUANT + 16 * layer + idx)
+    codes = rng(*key, 0).integers(0, 256, (rows, cols), dtype=np.uint8)
+    scales = f32_to_bf16_bits(rng(*key, 1).uniform(0.75, 1.25, (rows, g)).astype(np.float32)
+                              * np.float32(WEIGHT_STD / 74.0))
+    zeros = rng(*key, 2).integers(112, 144, (rows, g), dtype=np.uint8)
+    return codes, scales, zeros
+
+
+def q8_layer_weights(workload: int, layer: int, shape: ModelShape) -> dict:
+    """Quantized matrices of one layer by name (as q8_matrix), plus the two norm gains (1.0)."""
+    t = {name: q8_matrix(workload, layer, idx, *shape.matrix_shapes()[name]) for idx, name in enumerate(LAYER_TENSORS)}
+    for name in NORMS:
+        t[name] = np.full(shape.hidden, BF16_ONE, dtype=np.uint16)
+    return t
+
+
 def free_order(workload: int, num_pages: int) -> np.ndarray:
     """Seeded permutation of page ids: the initial order of the pool's free list."""
     return rng(workload, S_FREE).permutation(num_pages).astype(np.int32)

@@ -14,15 +14,15 @@ class LayerCase:
     extra_tokens[s] = how many new tokens sequence s will append this step.
     """
 
-    def __init__(self, L, R, shape, workload, ctxs, extra_tokens, build_oracle=True, slack_pages=0):
+    def __init__(self, L, R, shape, workload, ctxs, extra_tokens, build_oracle=True, slack_pages=0, pack=True):
         import torch
         self.L, self.R, self.shape, self.workload = L, R, shape, workload
         self.cfg = L.make_config(shape)
         self.ctxs = [int(c) for c in ctxs]
         self.extra = [int(e) for e in extra_tokens]
         H, D = shape.n_kv_heads, shape.head_dim
-        self.lw = synth.layer_weights(workload, 0, shape)
-        self.packed = R.PackedLayer(self.cfg, self.lw.tensors)
+        self.lw = synth.layer_weights(workload, 0, shape) if pack else None
+        self.packed = R.PackedLayer(self.cfg, self.lw.tensors) if pack else None
         totals = [c + e for c, e in zip(self.ctxs, self.extra)]
         self.max_pages = max(op.pages_needed(t) for t in totals) + 1
         self.num_pages = sum(op.pages_needed(t) for t in totals) + slack_pages

@@ -147,3 +147,40 @@ def test_pool_exhaustion_is_atomic(L):
         L.llmdec_kv_pool_alloc(h, 200, row, 3, 8)  # 13 pages > row width
     assert e.value.status == L.LLMDEC_E_INVALID
     L.llmdec_kv_pool_destroy(h)
+
+
+def test_q8_sizes_and_validation_before_launch(L):
+    """Group-quantized matrices: packed size = codes + 128 bytes of metadata words per four 1024-column
+    steps of a row; unsupported shapes give 0 / E_INVALID; a quantized decode step of more than one
+    sequence is E_UNSUPPORTED before anything is launched."""
+    assert L.llmdec_q8_matrix_bytes(4096, 4096) == 4096 * 4096 + 4096 * 128
+    assert L.llmdec_q8_matrix_bytes(4096, 11008) == 4096 * 11008 + 4096 * 3 * 128
+    assert L.llmdec_q8_matrix_bytes(64, 688) == 64 * 688 + 64 * 128
+    assert L.llmdec_q8_matrix_bytes(6, 256) == 0            # rows not a multiple of 4
+    assert L.llmdec_q8_matrix_bytes(8, 264) == 0            # cols not a multiple of 16
+    assert L.llmdec_q8_matrix_bytes(8, 15360) > 0 and L.llmdec_q8_matrix_bytes(8, 15376) == 0
+    cfg = tiny_cfg(L)
+    assert L.llmdec_q8_packed_layer_bytes(cfg) > 0
+    src = L.llmdec_q8_matrix(1 << 20, 1 << 21, 1 << 22)
+    with pytest.raises(L.LlmdecError) as e:
+        L.llmdec_q8_pack_matrix(8, 264, src, 1 << 23, 1 << 20)
+    assert e.value.status == L.LLMDEC_E_INVALID
+    with pytest.raises(L.LlmdecError) as e:
+        L.llmdec_q8_pack_matrix(8, 256, src, 1 << 23, 100)
+    assert e.value.status == L.LLMDEC_E_INVALID and "needed" in str(e.value)
+    with pytest.raises(L.LlmdecError) as e:
+        L.llmdec_op_linear_q8(1 << 20, 264, 1 << 21, 8, 1 << 22, 0)
+    assert e.value.status == L.LLMDEC_E_INVALID
+    num_pages = 4
+    h = L.llmdec_kv_pool_create(cfg, 1 << 20, L.llmdec_kv_pool_bytes(cfg, num_pages), num_pages)
+    try:
+        w = L.llmdec_q8_packed_layer(*([1 << 24] * 6))
+        ws_bytes = L.llmdec_workspace_bytes(cfg, 2, 2, 4)
+        with pytest.raises(L.LlmdecError) as e:
+            L.llmdec_layer_decode_q8(cfg, w, 0, 1 << 20, 2, 1 << 21, 1 << 22, 4, h, 1 << 23, ws_bytes)
+        assert e.value.status == L.LLMDEC_E_UNSUPPORTED and "n_seqs=2" in str(e.value)
+        with pytest.raises(L.LlmdecError) as e:
+            L.llmdec_layer_decode_q8(cfg, w, 0, 1 << 20, 1, 1 << 21, 1 << 22, 4, h, 1 << 23, 16)
+        assert e.value.status == L.LLMDEC_E_WORKSPACE
+    finally:
+        L.llmdec_kv_pool_destroy(h)

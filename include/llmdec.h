@@ -345,8 +345,8 @@ typedef struct {
  * (rows*cols bytes), then one 32-bit word per (row, group) holding the bf16
  * scale and the zero point, ordered for the kernel's lanes and padded per
  * row to a multiple of 32 words (the padding words are zero).  0 when the
- * shape is unsupported: cols must be a multiple of 16 and at most 15360,
- * rows a multiple of 4. */
+ * shape is unsupported: cols must be a multiple of 16 and at most 14336,
+ * rows a multiple of 4 (and at most about 120000 rows). */
 size_t llmdec_q8_matrix_bytes(int32_t rows, int32_t cols);
 /* Pack one quantized matrix into dev dst (>= q8_matrix_bytes).  The source
  * may be freed once the stream has run.  Errors: E_INVALID for null
@@ -361,7 +361,8 @@ llmdec_status llmdec_q8_pack_layer(const llmdec_config *cfg, const llmdec_q8_lay
 
 /* out[n] (+)= sum_k a[k] * W[n][k] for one dev fp32 row a [k_dim] and a
  * packed quantized W [n_dim][k_dim], fp32 arithmetic throughout (the
- * activation is not rounded).  accumulate = 0 stores, 1 adds into out.  No
+ * activation is not rounded; partial sums are added in a fixed order, so
+ * repeated calls give identical results).  accumulate = 0 stores, 1 adds into out.  No
  * workspace.  Errors: E_INVALID for null pointers or a shape q8_matrix_bytes
  * rejects. */
 llmdec_status llmdec_op_linear_q8(const float *a, int32_t k_dim, const void *w_q8_packed, int32_t n_dim, float *out,

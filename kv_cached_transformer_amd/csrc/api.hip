@@ -647,7 +647,7 @@ extern "C" llmdec_status llmdec_q8_pack_matrix(int32_t rows, int32_t cols, const
   if (!q8_ok(rows, cols))
     return set_error(LLMDEC_E_INVALID,
                      "q8_pack_matrix: rows (%d) must be a positive multiple of 4, cols (%d) a positive multiple of 16 "
-                     "and at most 15360", rows, cols);
+                     "and at most 14336", rows, cols);
   const size_t need = q8_matrix_bytes(rows, cols);
   if (dst_bytes < need) return set_error(LLMDEC_E_INVALID, "q8_pack_matrix: dst holds %zu bytes, %zu needed", dst_bytes, need);
   launch_q8_pack((const uint8_t *)src->codes, (const uint16_t *)src->scales, (const uint8_t *)src->zeros, rows, cols,
@@ -695,7 +695,7 @@ extern "C" llmdec_status llmdec_q8_pack_layer(const llmdec_config *cfg, const ll
     return set_error(LLMDEC_E_INVALID, "%s: NULL pointer", who);
   if (!q8_layer_ok(*cfg))
     return set_error(LLMDEC_E_UNSUPPORTED, "%s: hidden %d / intermediate %d: quantized matrices need row counts that are "
-                     "multiples of 4 and input widths that are multiples of 16, at most 15360", who, cfg->hidden,
+                     "multiples of 4 and input widths that are multiples of 16, at most 14336", who, cfg->hidden,
                      cfg->intermediate);
   size_t off[6];
   const size_t need = q8_layer_parts(*cfg, off);
@@ -732,9 +732,9 @@ extern "C" llmdec_status llmdec_op_linear_q8(const float *a, int32_t k_dim, cons
                                             float *out, int32_t accumulate, llmdec_stream stream) {
   if (!a || !w_q8_packed || !out) return set_error(LLMDEC_E_INVALID, "op_linear_q8: NULL pointer");
   if (!q8_ok(n_dim, k_dim))
-    return set_error(LLMDEC_E_INVALID, "op_linear_q8: n=%d k=%d unsupported (n a multiple of 4, k of 16, k <= 15360)",
+    return set_error(LLMDEC_E_INVALID, "op_linear_q8: n=%d k=%d unsupported (n a multiple of 4, k of 16, k <= 14336)",
                      n_dim, k_dim);
-  launch_q8_gemv(a, (const uint8_t *)w_q8_packed, n_dim, k_dim, accumulate ? kAccumulate : kStore, out,
+  launch_q8_gemv(a, nullptr, 0.f, (const uint8_t *)w_q8_packed, n_dim, k_dim, accumulate ? kAccumulate : kStore, out,
                  (hipStream_t)stream);
   return check_launch("op_linear_q8");
 }
@@ -767,19 +767,15 @@ extern "C" llmdec_status llmdec_layer_decode_q8(const llmdec_config *cfg, const 
   float *y = at<float>(ws, L.act_h), *u = at<float>(ws, L.act_i), *qkv = at<float>(ws, L.qkv);
   uint16_t *pk, *pv;
   pool_layer(pool, layer, &pk, &pv);
-  // x += Wo . attn(rope(Wq y), rope(Wk y), Wv y),  y = RMSNorm(x)
-  launch_rmsnorm(hidden, h, nullptr, 1, (const uint16_t *)w->attn_norm, 1, h, c.rms_eps, err, y, nullptr, nullptr, 0,
-                 nullptr, Splits{}, s);
-  launch_q8_gemv(y, (const uint8_t *)w->w_qkv, nqkv, h, kStore, qkv, s);
+  // x += Wo . attn(rope(Wq y), rope(Wk y), Wv y),  y = RMSNorm(x): the product stages y itself
+  launch_q8_gemv(hidden, (const uint16_t *)w->attn_norm, c.rms_eps, (const uint8_t *)w->w_qkv, nqkv, h, kStore, qkv, s);
   launch_rope_append(c, qkv, nullptr, Splits{}, nqkv, 1, 1, nullptr, ctx_lens, block_tables, max_pages, pk, pv,
                      pool->num_pages, err, s);
   launch_decode_attention(c, qkv, nqkv, 1, ctx_lens, block_tables, max_pages, pk, pv, pool->num_pages,
                           at<float>(ws, L.attn_part), y, nullptr, nullptr, 0, err, s);
-  launch_q8_gemv(y, (const uint8_t *)w->w_o, h, h, kAccumulate, hidden, s);
+  launch_q8_gemv(y, nullptr, 0.f, (const uint8_t *)w->w_o, h, h, kAccumulate, hidden, s);
   // x += Wd (silu(Wg y) * (Wu y)),  y = RMSNorm(x)
-  launch_rmsnorm(hidden, h, nullptr, 1, (const uint16_t *)w->mlp_norm, 1, h, c.rms_eps, err, y, nullptr, nullptr, 0,
-                 nullptr, Splits{}, s);
-  launch_q8_gemv(y, (const uint8_t *)w->w_gu, 2 * I, h, kSiluMul, u, s);
-  launch_q8_gemv(u, (const uint8_t *)w->w_down, h, I, kAccumulate, hidden, s);
+  launch_q8_gemv(hidden, (const uint16_t *)w->mlp_norm, c.rms_eps, (const uint8_t *)w->w_gu, 2 * I, h, kSiluMul, u, s);
+  launch_q8_gemv(u, nullptr, 0.f, (const uint8_t *)w->w_down, h, I, kAccumulate, hidden, s);
   return check_launch(who);
 }

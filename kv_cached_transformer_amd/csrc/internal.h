@@ -139,7 +139,7 @@ void launch_gather_kv(const uint16_t *pool_layer_k, const uint16_t *pool_layer_v
                       hipStream_t s);
 void launch_fill_u32(uint32_t *p, uint32_t value, size_t n, hipStream_t s);
 
-// Group-quantized matrices (kernels_quant.hip).  q8_shape_ok: cols a multiple of 16, at most 15360.
+// Group-quantized matrices (kernels_quant.hip).  q8_shape_ok: cols a multiple of 16, at most 14336.
 bool q8_shape_ok(int cols);
 size_t q8_matrix_bytes(int rows, int cols);
 // Pack a source matrix's rows into rows dst_row0.. of a packed matrix with dst_rows rows in all.
@@ -147,7 +147,9 @@ void launch_q8_pack(const uint8_t *codes, const uint16_t *scales, const uint8_t 
                     uint8_t *dst, int dst_rows, int dst_row0, hipStream_t s);
 // One-row product with a packed quantized matrix of `rows` rows: mode kStore / kAccumulate write
 // out[0..rows); kSiluMul reads the matrix as [gate; up] and writes out[j] = silu(gate_j) * up_j for
-// j < rows / 2.  rows % 4 == 0.
-void launch_q8_gemv(const float *x, const uint8_t *w, int rows, int k, int mode, float *out, hipStream_t s);
+// j < rows / 2.  rows % 4 == 0.  gamma != NULL: the product reads rmsnorm(x) * gamma (eps inside the root)
+// instead of x.
+void launch_q8_gemv(const float *x, const uint16_t *gamma, float eps, const uint8_t *w, int rows, int k, int mode,
+                    float *out, hipStream_t s);
 
 }  // namespace llmdec

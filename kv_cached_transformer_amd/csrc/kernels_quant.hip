@@ -15,7 +15,9 @@
 // row per step (lane l reads columns 1024 s + 16 l .. +15 of each row, a 16-byte load), with the
 // steps of a row kept in flight ahead of the arithmetic.  x lives in LDS as fp32, stored by
 // quarter-chunks (float4 j of chunk c at [j][c]) so that the lanes of one ds_read_b128 read
-// consecutive 16-byte words.
+// consecutive 16-byte words.  When the product follows an RMSNorm, each block stages
+// rmsnorm(x) * gamma itself ("为什么要自己动手写一个LLM推理引擎" §4.2: x (mean(x^2) + eps)^-1/2 gamma),
+// so the norm costs no launch of its own.
 //
 // Packed layout of a quantized matrix (llmdec_q8_pack_matrix): the codes as given, [rows][cols]
 // bytes, followed by the group metadata, one 32-bit word per (row, group): bf16 scale bits in the
@@ -31,7 +33,7 @@ namespace llmdec {
 
 constexpr int kQGroup = 128;       // elements per quantization group
 constexpr int kQStepCols = 1024;   // columns per wave step: 64 lanes x 16 codes
-constexpr int kQMaxSteps = 15;     // k <= 15360: x (fp32) and its chunk sums fit a 64 KiB block's LDS
+constexpr int kQMaxSteps = 14;     // k <= 14336: x (fp32), its chunk sums and the norm's sums fit 64 KiB of LDS
 
 __host__ __device__ inline int q8_steps(int k) { return (k + kQStepCols - 1) / kQStepCols; }
 __host__ __device__ inline int q8_meta_quads(int k) { return (q8_steps(k) + 3) / 4; }
@@ -76,6 +78,8 @@ void launch_q8_pack(const uint8_t *codes, const uint16_t *scales, const uint8_t 
 // writes out[n] = silu(gate_n) * up_n.
 struct Q8Args {
   const float *x;         // [k] fp32
+  const uint16_t *gamma;  // NULL, or the RMSNorm gain [k] (bf16): the product then reads rmsnorm(x) * gamma
+  float eps;
   const uint8_t *w;       // packed matrix (codes, then metadata)
   int rows;               // rows of the packed matrix
   int k;
@@ -99,6 +103,7 @@ __global__ __launch_bounds__(512) void q8_gemv_kernel(Q8Args a) {
   extern __shared__ float4 smem[];
   float4 *xq = smem;                                         // [4][NCH]: quarter j of chunk c
   float *xsum = reinterpret_cast<float *>(smem + 4 * NCH);  // [NCH]: sum of the chunk's 16 values
+  float *red = xsum + NCH;                                   // [waves]: the norm's sums of squares
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(512) void q8_gemv_kernel(Q8Args a) {
   // resource (reads zeros, touches nothing), so every load is unconditional.
   const size_t code_bytes = (size_t)a.rows * k;
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.w, code_bytes);
-  const size_t mrow = q8_meta_row_bytes(k);
+  const uint32_t mrow = (uint32_t)q8_meta_row_bytes(k);
   const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.w + code_bytes, (size_t)a.rows * mrow);
 
   uint4 cb[NSTEP][4];  // fully unrolled: only D steps are live at a time
@@ -132,10 +137,12 @@ __global__ __launch_bounds__(512) void q8_gemv_kernel(Q8Args a) {
     if (s % 4 == 0) {
       const uint32_t moff = (uint32_t)(s / 4) * 128u + (uint32_t)(lane >> 3) * 16u;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mb[s / 4][r] = buffer_load16(rm, moff, (uint32_t)((size_t)row[r] * mrow), 0);
+      for (int r = 0; r < 4; ++r)
+        mb[s / 4][r] = buffer_load16(rm, moff, __builtin_amdgcn_readfirstlane((uint32_t)row[r] * mrow), 0);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) cb[s][r] = buffer_load16(rc, voff, (uint32_t)((size_t)row[r] * k), kLoadStream);
+    for (int r = 0; r < 4; ++r)
+      cb[s][r] = buffer_load16(rc, voff, __builtin_amdgcn_readfirstlane((uint32_t)row[r] * (uint32_t)k), kLoadStream);
   };
   // the codes do not depend on x: start them before x is staged (an idle wave issues nothing)
   if (active) {
@@ -146,7 +153,8 @@ __global__ __launch_bounds__(512) void q8_gemv_kernel(Q8Args a) {
     }
   }
 
-  // stage x: thread i takes columns 8i..8i+7 (two quarter-chunks)
+  // stage x (or rmsnorm(x) * gamma): thread i takes columns 8i..8i+7 (two quarter-chunks)
+  float ss = 0.f;
   for (int i = threadIdx.x; i < NCH * 2; i += blockDim.x) {
     const int c0 = 8 * i;
     float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
@@ -154,10 +162,34 @@ __global__ __launch_bounds__(512) void q8_gemv_kernel(Q8Args a) {
       const float4 *p = reinterpret_cast<const float4 *>(a.x + c0);
       v0 = p[0];
       v1 = p[1];
+      if (a.gamma) {  // block-uniform: stage x * gamma now, scale by the norm's factor once it is known
+        const uint4 gw = *reinterpret_cast<const uint4 *>(a.gamma + c0);
+        ss = fmaf(v0.x, v0.x, ss), ss = fmaf(v0.y, v0.y, ss), ss = fmaf(v0.z, v0.z, ss), ss = fmaf(v0.w, v0.w, ss);
+        ss = fmaf(v1.x, v1.x, ss), ss = fmaf(v1.y, v1.y, ss), ss = fmaf(v1.z, v1.z, ss), ss = fmaf(v1.w, v1.w, ss);
+        v0 = make_float4(v0.x * bf16lo(gw.x), v0.y * bf16hi(gw.x), v0.z * bf16lo(gw.y), v0.w * bf16hi(gw.y));
+        v1 = make_float4(v1.x * bf16lo(gw.z), v1.y * bf16hi(gw.z), v1.z * bf16lo(gw.w), v1.w * bf16hi(gw.w));
+      }
     }
     const int ch = c0 >> 4, j = (c0 >> 2) & 3;  // j is 0 or 2
     xq[j * NCH + ch] = v0;
     xq[(j + 1) * NCH + ch] = v1;
+  }
+  if (a.gamma) {  // block-uniform
+    const int nw = blockDim.x >> 6;
+    ss = wave_sum(ss);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    float total = 0.f;
+    for (int w = 0; w < nw; ++w) total += red[w];
+    const float inv = 1.0f / sqrtf(total / (float)k + a.eps);
+    for (int i = threadIdx.x; i < NCH * 2; i += blockDim.x) {  // the values this thread staged
+      const int c0 = 8 * i;
+      if (c0 >= k) continue;
+      const int ch = c0 >> 4, j = (c0 >> 2) & 3;
+      const float4 v0 = xq[j * NCH + ch], v1 = xq[(j + 1) * NCH + ch];
+      xq[j * NCH + ch] = make_float4(v0.x * inv, v0.y * inv, v0.z * inv, v0.w * inv);
+      xq[(j + 1) * NCH + ch] = make_float4(v1.x * inv, v1.y * inv, v1.z * inv, v1.w * inv);
+    }
   }
   __syncthreads();
   for (int ch = threadIdx.x; ch < NCH; ch += blockDim.x) {
@@ -218,13 +250,14 @@ __global__ __launch_bounds__(512) void q8_gemv_kernel(Q8Args a) {
   }
 }
 
-template <int MODE> static void q8_dispatch(int nstep, const Q8Args &a, int blocks, int threads, hipStream_t s) {
-  const size_t lds = (size_t)nstep * 64 * (4 * sizeof(float4) + sizeof(float));
+template <int MODE> static void q8_dispatch(int nstep, const Q8Args &a, int wpb, hipStream_t s) {
+  const size_t lds = (size_t)nstep * 64 * (4 * sizeof(float4) + sizeof(float)) + 16 * sizeof(float);
+  const int blocks = (a.n_tasks + wpb - 1) / wpb;
   switch (nstep) {
 #define Q8_CASE(N) \
-  case N: q8_gemv_kernel<N, MODE><<<blocks, threads, lds, s>>>(a); break;
-    Q8_CASE(1) Q8_CASE(2) Q8_CASE(3) Q8_CASE(4) Q8_CASE(5) Q8_CASE(6) Q8_CASE(7) Q8_CASE(8)
-    Q8_CASE(9) Q8_CASE(10) Q8_CASE(11) Q8_CASE(12) Q8_CASE(13) Q8_CASE(14) Q8_CASE(15)
+  case N: q8_gemv_kernel<N, MODE><<<blocks, wpb * 64, lds, s>>>(a); break;
+    Q8_CASE(1) Q8_CASE(2) Q8_CASE(3) Q8_CASE(4) Q8_CASE(5) Q8_CASE(6) Q8_CASE(7)
+    Q8_CASE(8) Q8_CASE(9) Q8_CASE(10) Q8_CASE(11) Q8_CASE(12) Q8_CASE(13) Q8_CASE(14)
 #undef Q8_CASE
     default: break;
   }
@@ -232,19 +265,19 @@ template <int MODE> static void q8_dispatch(int nstep, const Q8Args &a, int bloc
 
 bool q8_shape_ok(int k) { return k > 0 && k % 16 == 0 && q8_steps(k) <= kQMaxSteps; }
 
-void launch_q8_gemv(const float *x, const uint8_t *w, int rows, int k, int mode, float *out, hipStream_t s) {
+void launch_q8_gemv(const float *x, const uint16_t *gamma, float eps, const uint8_t *w, int rows, int k, int mode,
+                    float *out, hipStream_t s) {
   Q8Args a;
-  a.x = x, a.w = w, a.rows = rows, a.k = k, a.out = out;
+  a.x = x, a.gamma = gamma, a.eps = eps, a.w = w, a.rows = rows, a.k = k, a.out = out;
   a.n_out = mode == kSiluMul ? rows / 2 : rows;
   a.n_tasks = rows / 4;  // four matrix rows per wave in every mode
   if (a.n_tasks <= 0) return;
+  const int nstep = q8_steps(k);
   // 8 waves per block share one staging of x, unless that would leave CUs without two blocks each
   const int wpb = a.n_tasks >= 8 * 512 ? 8 : 4;
-  const int blocks = (a.n_tasks + wpb - 1) / wpb;
-  const int nstep = q8_steps(k);
-  if (mode == kSiluMul) q8_dispatch<kSiluMul>(nstep, a, blocks, wpb * 64, s);
-  else if (mode == kAccumulate) q8_dispatch<kAccumulate>(nstep, a, blocks, wpb * 64, s);
-  else q8_dispatch<kStore>(nstep, a, blocks, wpb * 64, s);
+  if (mode == kSiluMul) q8_dispatch<kSiluMul>(nstep, a, wpb, s);
+  else if (mode == kAccumulate) q8_dispatch<kAccumulate>(nstep, a, wpb, s);
+  else q8_dispatch<kStore>(nstep, a, wpb, s);
 }
 
 }  // namespace llmdec

@@ -158,7 +158,7 @@ def test_q8_sizes_and_validation_before_launch(L):
     assert L.llmdec_q8_matrix_bytes(64, 688) == 64 * 688 + 64 * 128
     assert L.llmdec_q8_matrix_bytes(6, 256) == 0            # rows not a multiple of 4
     assert L.llmdec_q8_matrix_bytes(8, 264) == 0            # cols not a multiple of 16
-    assert L.llmdec_q8_matrix_bytes(8, 15360) > 0 and L.llmdec_q8_matrix_bytes(8, 15376) == 0
+    assert L.llmdec_q8_matrix_bytes(8, 14336) > 0 and L.llmdec_q8_matrix_bytes(8, 14352) == 0
     cfg = tiny_cfg(L)
     assert L.llmdec_q8_packed_layer_bytes(cfg) > 0
     src = L.llmdec_q8_matrix(1 << 20, 1 << 21, 1 << 22)

@@ -168,10 +168,38 @@ struct LayerArgs {
   hipStream_t s;
 };
 
+// Decode of a single sequence: every product is a matrix-vector product (one-row kernels with the
+// RMSNorms folded into the q|k|v and gate/up launches, epilogues applied in the kernels, no split-k
+// partial sums); activations between kernels are fp32.
+static void run_layer_one_row(const LayerArgs &a) {
+  const llmdec_config &c = *a.cfg;
+  const int h = c.hidden, I = c.intermediate, nqkv = qkv_cols(c);
+  const WsLayout &L = a.L;
+  uint32_t *err = at<uint32_t>(a.ws, L.err);
+  // one row: the fp32 activations fit in the packed activation planes' space
+  float *y = at<float>(a.ws, L.act_h), *u = at<float>(a.ws, L.act_i), *qkv = at<float>(a.ws, L.qkv);
+  uint16_t *pk, *pv;
+  pool_layer(a.pool, a.layer, &pk, &pv);
+  launch_gemv(a.hidden, (const uint16_t *)a.w->attn_norm, c.rms_eps, (const uint16_t *)a.w->w_qkv, nqkv, h, kStore,
+              qkv, a.s);
+  launch_rope_append(c, qkv, nullptr, Splits{}, nqkv, 1, 1, nullptr, a.ctx, a.bt, a.max_pages, pk, pv,
+                     a.pool->num_pages, err, a.s);
+  launch_decode_attention(c, qkv, nqkv, 1, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages,
+                          at<float>(a.ws, L.attn_part), y, nullptr, nullptr, 0, err, a.s);
+  launch_gemv(y, nullptr, 0.f, (const uint16_t *)a.w->w_o, h, h, kAccumulate, a.hidden, a.s);
+  launch_gemv(a.hidden, (const uint16_t *)a.w->mlp_norm, c.rms_eps, (const uint16_t *)a.w->w_gu, 2 * I, h, kSiluMul,
+              u, a.s);
+  launch_gemv(u, nullptr, 0.f, (const uint16_t *)a.w->w_down, h, I, kAccumulate, a.hidden, a.s);
+}
+
 static void run_layer(const LayerArgs &a) {
   const llmdec_config &c = *a.cfg;
   const int h = c.hidden, I = c.intermediate, M = a.rows;
   const WsLayout &L = a.L;
+  if (a.decode && M == 1 && gemv_shape_ok(h) && gemv_shape_ok(I)) {
+    run_layer_one_row(a);
+    return;
+  }
   uint32_t *err = at<uint32_t>(a.ws, L.err);
   uint16_t *ah_hi = at<uint16_t>(a.ws, L.act_h), *ah_lo = at<uint16_t>(a.ws, L.act_hl);
   uint16_t *ai_hi = at<uint16_t>(a.ws, L.act_i), *ai_lo = at<uint16_t>(a.ws, L.act_il);
@@ -511,6 +539,13 @@ extern "C" llmdec_status llmdec_op_linear(const float *a, int32_t rows, int32_t 
   o.kind = accumulate ? kAccumulate : kStore;
   o.f32 = out;
   o.ld = n_dim;
+  if (rows == 1 && gemv_shape_ok(k_dim)) {  // the one-row kernel, as a single-sequence decode step runs it
+    size_t act_off, part_off;
+    llmdec_status st = check_ws(ws, ws_bytes, op_linear_parts(rows, k_dim, n_dim, &act_off, &part_off), "op_linear");
+    if (st != LLMDEC_OK) return st;
+    launch_gemv(a, nullptr, 0.f, (const uint16_t *)w_packed, n_dim, k_dim, o.kind, out, (hipStream_t)stream);
+    return check_launch("op_linear");
+  }
   llmdec_status st = run_op_linear("op_linear", a, rows, k_dim, w_packed, n_dim, o, ws, ws_bytes, 0, kSplitBalanced,
                                    (hipStream_t)stream);
   return st != LLMDEC_OK ? st : check_launch("op_linear");

@@ -139,6 +139,14 @@ void launch_gather_kv(const uint16_t *pool_layer_k, const uint16_t *pool_layer_v
                       hipStream_t s);
 void launch_fill_u32(uint32_t *p, uint32_t value, size_t n, hipStream_t s);
 
+// One-row products with a packed bf16 matrix (kernels_gemv.hip): x fp32 [k], n a multiple of 16 (of 32
+// for kSiluMul, whose matrix is the fused gate/up one: 16-row blocks alternating gate and up, out[j] =
+// silu(gate_j) * up_j for j < n / 2).  kStore / kAccumulate write or add out[0..n).  gamma != NULL: the
+// product reads rmsnorm(x) * gamma (eps inside the root).  gemv_shape_ok: k a multiple of 16, <= 14336.
+bool gemv_shape_ok(int k);
+void launch_gemv(const float *x, const uint16_t *gamma, float eps, const uint16_t *w_packed, int n, int k, int mode,
+                 float *out, hipStream_t s);
+
 // Group-quantized matrices (kernels_quant.hip).  q8_shape_ok: cols a multiple of 16, at most 14336.
 bool q8_shape_ok(int cols);
 size_t q8_matrix_bytes(int rows, int cols);

@@ -34,9 +34,11 @@ struct GemvArgs {
 __device__ inline float gv_silu(float g) { return g / (1.0f + expf(-g)); }
 
 // TB row blocks per block: 1, or 2 for SwiGLU (blocks 2j = gate rows 16j.., 2j+1 = up rows 16j..).
+// Three blocks per CU (6 waves per SIMD, at most 80 registers) keep a 7B matrix's 768 (q|k|v) or 688
+// (gate/up) blocks resident in one round instead of a round and a half.
 template <int MODE, int TB>
-__global__ __launch_bounds__(kGvWaves * 64) void gemv_kernel(GemvArgs a) {
-  constexpr int D = TB == 1 ? 16 : 8;  // k-tiles in flight per wave
+__global__ __launch_bounds__(kGvWaves * 64, 6) void gemv_kernel(GemvArgs a) {
+  constexpr int D = TB == 1 ? 12 : 6;  // k-tiles in flight per wave
   constexpr int R = D + 1;             // ring slots
   constexpr uint32_t kOut = 0x80000000u;
   extern __shared__ float smem[];

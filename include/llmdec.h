@@ -38,8 +38,9 @@
  *    carried as a bf16 pair hi + lo (about 17 significant bits) and multiply
  *    the bf16 weights on the matrix cores with fp32 accumulation; the
  *    residual stream, attention (scores, softmax, weighted sum) and logits
- *    are fp32.  Products with group-quantized weights run in fp32 from the
- *    unrounded activation.
+ *    are fp32.  The products of a single-sequence decode step (one row) and
+ *    those with group-quantized weights run in fp32 from the unrounded
+ *    activation instead.
  *  - Not thread-safe per pool handle; distinct handles are independent.
  */
 #ifndef LLMDEC_H
@@ -253,8 +254,9 @@ llmdec_status llmdec_op_rmsnorm(const float *x, const void *gamma, int32_t rows,
  * entering a weight product is) and a packed W (llmdec_pack_matrix of
  * [n_dim][k_dim]).  accumulate = 0 stores, 1 adds into out (the residual add
  * of [W] §1.1).  ws: scratch for the activation pair and split-k partial
- * sums (>= llmdec_op_linear_ws_bytes).  rows <= 64 takes the
- * weight-streaming kernel, rows > 64 the LDS-tiled one. */
+ * sums (>= llmdec_op_linear_ws_bytes).  rows == 1 takes the one-row kernel
+ * (fp32 activation, k_dim <= 14336), rows <= 64 the weight-streaming
+ * kernel, rows > 64 the LDS-tiled one. */
 size_t llmdec_op_linear_ws_bytes(int32_t rows, int32_t k_dim, int32_t n_dim);
 llmdec_status llmdec_op_linear(const float *a, int32_t rows, int32_t k_dim, const void *w_packed, int32_t n_dim,
                                float *out, int32_t accumulate, void *ws, size_t ws_bytes, llmdec_stream stream);

@@ -446,3 +446,96 @@ def test_dequantize_short_last_group():
     assert w[0, 128] == 6.0 and w[0, 129] == 0.0
     with pytest.raises(AssertionError):   # a missing group's scale is an error, not a silent reuse
         oq.dequantize(codes, np.array([[0.25]]), np.array([[10]], np.uint8))
+
+
+# ----------------------------------------------------------------------------- sampling
+GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def test_philox_known_answers():
+    """Philox4x32-10 reproduces the generator's published known-answer vectors."""
+    from oracle import sampling as osm
+    with open(os.path.join(GOLDEN_DIR, "philox4x32_10_kat.json")) as f:
+        kat = json.load(f)
+    for v in kat["vectors"]:
+        got = osm.philox4x32_10([int(x, 16) for x in v["counter"]], [int(x, 16) for x in v["key"]])
+        assert got == tuple(int(x, 16) for x in v["out"])
+
+
+def test_uniform_draw_range_and_keying():
+    """u is a multiple of 2^-24 in [0, 1), and rows, steps and seeds give different draws."""
+    from oracle import sampling as osm
+    us = [osm.uniform(7, 3, r) for r in range(64)]
+    assert all(0.0 <= u < 1.0 and float(u * 2 ** 24).is_integer() for u in us)
+    assert len(set(us)) == 64
+    assert osm.uniform(7, 3, 0) != osm.uniform(7, 4, 0) != osm.uniform(8, 3, 0)
+    assert osm.uniform(7, 1 << 33, 0) != osm.uniform(7, 0, 0)     # the step's high word is used
+
+
+def test_sample_worked_example():
+    """Logits ln 1, ln 2, ln 3, ln 4 at T = 1 give p = (1, 2, 3, 4) / 10.  top_k = 3 keeps tokens 1..3
+    (2, 3, 4)/9; top_p = 0.7 then keeps 3 (4/9) and 2 (4/9 + 3/9 = 7/9 >= 0.7), renormalised to
+    3/7 for token 2 and 4/7 for token 3, taken in increasing id: u < 3/7 gives 2, else 3.  Worked by hand."""
+    from oracle import sampling as osm
+    z = np.log([1.0, 2.0, 3.0, 4.0])
+    ids, w = osm.kept_tokens(z, 1.0, 3, 0.7)
+    assert ids.tolist() == [2, 3] and np.allclose(w, [3 / 7, 4 / 7], rtol=0, atol=1e-15)
+    assert osm.sample(z, 1.0, 3, 0.7, 0.42) == 2 and osm.sample(z, 1.0, 3, 0.7, 0.43) == 3
+    ids, w = osm.kept_tokens(z, 1.0, 3, 1.0)
+    assert ids.tolist() == [1, 2, 3] and np.allclose(w, [2 / 9, 3 / 9, 4 / 9], rtol=0, atol=1e-15)
+    # no truncation: u in [0, 0.1) -> 0, [0.1, 0.3) -> 1, [0.3, 0.6) -> 2, [0.6, 1) -> 3
+    assert [osm.sample(z, 1.0, 0, 1.0, u) for u in (0.05, 0.15, 0.35, 0.65)] == [0, 1, 2, 3]
+
+
+def test_sample_limits_reduce_to_argmax():
+    """Temperature 0, top_k = 1 and a top_p below every probability all give the argmax for any u."""
+    from oracle import sampling as osm
+    r = np.random.default_rng(41)
+    for _ in range(20):
+        z = r.standard_normal(500) * 3
+        am = int(np.argmax(z))
+        for u in (0.0, 0.3, 0.999999):
+            assert osm.sample(z, 0.0, 0, 1.0, u) == am
+            assert osm.sample(z, 0.8, 1, 1.0, u) == am
+            assert osm.sample(z, 1.3, 0, 1e-9, u) == am
+
+
+def test_sample_measure_matches_probabilities():
+    """Without truncation a fine grid of u gives each token a share equal to softmax(z / T); the ratio of
+    two tokens' probabilities is exp((z_i - z_j) / T)."""
+    from oracle import sampling as osm
+    r = np.random.default_rng(42)
+    z = r.standard_normal(12)
+    T = 0.7
+    ids, w = osm.kept_tokens(z, T, 0, 1.0)
+    assert ids.tolist() == list(range(12))
+    for i in range(12):
+        assert abs(w[i] / w[0] - math.exp((z[i] - z[0]) / T)) < 1e-12 * math.exp((z[i] - z[0]) / T)
+    grid = (np.arange(200000) + 0.5) / 200000
+    counts = np.bincount([osm.sample(z, T, 0, 1.0, u) for u in grid], minlength=12) / grid.size
+    assert np.allclose(counts, w, atol=1e-5)
+
+
+def test_sample_truncation_sets():
+    """top_k keeps exactly the k largest logits (and ties with the k-th); top_p keeps the smallest prefix
+    of the sorted probabilities whose sum reaches p; both are checked by brute force over subsets."""
+    from oracle import sampling as osm
+    r = np.random.default_rng(43)
+    z = r.standard_normal(9)
+    for k in range(1, 9):
+        ids, _ = osm.kept_tokens(z, 1.0, k, 1.0)
+        assert set(ids.tolist()) == set(np.argsort(-z)[:k].tolist())
+    zt = np.array([0.0, 1.0, 1.0, 0.5])               # a tie at the 2nd largest logit
+    assert osm.kept_tokens(zt, 1.0, 2, 1.0)[0].tolist() == [1, 2]
+    assert osm.kept_tokens(zt, 1.0, 1, 1.0)[0].tolist() == [1, 2]
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    for top_p in (0.05, 0.3, 0.5, 0.8, 0.95):
+        ids, _ = osm.kept_tokens(z, 1.0, 0, top_p)
+        # brute force: the fewest tokens whose mass reaches top_p, and of those sets the most probable one
+        best = None
+        for mask in range(1, 1 << 9):
+            sel = [i for i in range(9) if mask >> i & 1]
+            if p[sel].sum() >= top_p and (best is None or (len(sel), -p[sel].sum()) < (len(best), -p[best].sum())):
+                best = sel
+        assert sorted(ids.tolist()) == sorted(best)

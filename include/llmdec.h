@@ -314,6 +314,45 @@ llmdec_status llmdec_op_lm_head_argmax(const float *x, int32_t rows, int32_t hid
                                        int32_t vocab, int32_t *next, float *logits_out, void *ws, size_t ws_bytes,
                                        llmdec_stream stream);
 
+/* ------------------------------------------------------------------ sampling
+ * [E] §3.5 and [F] §2.2.3: temperature divides the logits before the
+ * softmax; top-k keeps the k most probable tokens; top-p keeps the smallest
+ * set of most probable tokens whose probability sum reaches p; combined, the
+ * temperature comes first, then the truncations, then the draw.  Here top-k
+ * is applied before top-p (which works on the distribution renormalised over
+ * the top-k set); a token tied with the last one a truncation keeps is kept
+ * too; the token drawn is the first kept one, in increasing id, whose
+ * cumulative renormalised probability exceeds u.  The draw for row r of a
+ * call is u = (w >> 8) * 2^-24 with w word 0 of Philox4x32-10 (Salmon et al.,
+ * SC 2011) at counter (r, step & 0xffffffff, step >> 32, 0) and key
+ * (seed & 0xffffffff, seed >> 32), so results are reproducible and need no
+ * generator state on the device.
+ *   temperature <= 0: greedy (argmax, lowest index on ties);
+ *   top_k <= 0 or >= vocab: no top-k;  top_p in (0, 1], 1: no top-p. */
+typedef struct {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+  uint64_t seed;
+  uint64_t step;
+} llmdec_sampling;
+
+/* next[r] for dev fp32 logits [rows][vocab] (vocab <= 32768), dev int32
+ * next [rows].  Errors: E_INVALID for null pointers, sizes out of range,
+ * top_p outside (0, 1] or a non-finite temperature. */
+llmdec_status llmdec_op_sample(const float *logits, int32_t rows, int32_t vocab, const llmdec_sampling *params,
+                               int32_t *next, llmdec_stream stream);
+
+/* llmdec_model_step_greedy with the next tokens sampled on the device
+ * ([E] §5.3: no host synchronisation) instead of the argmax; row r of the
+ * draw is sequence r.  Same arguments otherwise; vocab <= 32768. */
+llmdec_status llmdec_model_step_sample(const llmdec_config *cfg, const llmdec_model_weights *w, int32_t n_seqs,
+                                       int32_t n_tokens, int32_t max_q_len, const int32_t *tokens,
+                                       const int32_t *cu_seqlens, const int32_t *start_pos,
+                                       const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool,
+                                       const llmdec_sampling *params, int32_t *next_tokens, float *logits, void *ws,
+                                       size_t ws_bytes, llmdec_stream stream);
+
 /* ------------------------------------------------------------------ group-quantized weights
  * [W] §4.2: a matrix stored as integers in groups of 128 consecutive elements,
  * each group with one scale and one zero point, turned back into floating

@@ -425,13 +425,22 @@ extern "C" llmdec_status llmdec_layer_decode(const llmdec_config *cfg, const llm
   return check_launch(who);
 }
 
-extern "C" llmdec_status llmdec_model_step_greedy(const llmdec_config *cfg, const llmdec_model_weights *w,
-                                                 int32_t n_seqs, int32_t n_tokens, int32_t max_q_len,
-                                                 const int32_t *tokens, const int32_t *cu_seqlens,
-                                                 const int32_t *start_pos, const int32_t *block_tables,
-                                                 int32_t max_pages, llmdec_kv_pool *pool, int32_t *next_tokens,
-                                                 float *logits, void *ws, size_t ws_bytes, llmdec_stream stream) {
-  const char *who = "model_step_greedy";
+static llmdec_status check_sampling(const llmdec_sampling *p, int vocab, const char *who) {
+  if (!p) return set_error(LLMDEC_E_INVALID, "%s: sampling parameters are NULL", who);
+  if (!(p->top_p > 0.f && p->top_p <= 1.f))
+    return set_error(LLMDEC_E_INVALID, "%s: top_p=%g outside (0, 1]", who, (double)p->top_p);
+  if (!__builtin_isfinite(p->temperature))
+    return set_error(LLMDEC_E_INVALID, "%s: temperature is not finite", who);
+  if (!sample_shape_ok(vocab)) return set_error(LLMDEC_E_INVALID, "%s: vocab=%d outside [1, 32768]", who, vocab);
+  return LLMDEC_OK;
+}
+
+// One model step; smp == NULL: the greedy choice, else sampling.
+static llmdec_status model_step(const char *who, const llmdec_config *cfg, const llmdec_model_weights *w,
+                                int32_t n_seqs, int32_t n_tokens, int32_t max_q_len, const int32_t *tokens,
+                                const int32_t *cu_seqlens, const int32_t *start_pos, const int32_t *block_tables,
+                                int32_t max_pages, llmdec_kv_pool *pool, const llmdec_sampling *smp,
+                                int32_t *next_tokens, float *logits, void *ws, size_t ws_bytes, llmdec_stream stream) {
   llmdec_status st = check_config(cfg, who);
   if (st != LLMDEC_OK) return st;
   if (!w || !w->embed || !w->layers || !w->final_norm || !w->lm_head)
@@ -476,7 +485,48 @@ extern "C" llmdec_status llmdec_model_step_greedy(const llmdec_config *cfg, cons
   const Splits sp = launch_linear(Act{act_h, act_hl, n_seqs, L.kpad_h, L.row_blocks}, (const uint16_t *)w->lm_head,
                                   cfg->vocab, h, o, part, L.part_floats, kSplitUniform, s);  // argmax ties
   if (sp.any()) launch_reduce(part, sp, n_seqs, cfg->vocab, o, s);
-  launch_argmax(lg, n_seqs, cfg->vocab, next_tokens, s);
+  if (smp)
+    launch_sample(lg, n_seqs, cfg->vocab, smp->temperature, smp->top_k, smp->top_p, smp->seed, smp->step,
+                  next_tokens, s);
+  else
+    launch_argmax(lg, n_seqs, cfg->vocab, next_tokens, s);
+  return check_launch(who);
+}
+
+extern "C" llmdec_status llmdec_model_step_greedy(const llmdec_config *cfg, const llmdec_model_weights *w,
+                                                 int32_t n_seqs, int32_t n_tokens, int32_t max_q_len,
+                                                 const int32_t *tokens, const int32_t *cu_seqlens,
+                                                 const int32_t *start_pos, const int32_t *block_tables,
+                                                 int32_t max_pages, llmdec_kv_pool *pool, int32_t *next_tokens,
+                                                 float *logits, void *ws, size_t ws_bytes, llmdec_stream stream) {
+  return model_step("model_step_greedy", cfg, w, n_seqs, n_tokens, max_q_len, tokens, cu_seqlens, start_pos,
+                    block_tables, max_pages, pool, nullptr, next_tokens, logits, ws, ws_bytes, stream);
+}
+
+extern "C" llmdec_status llmdec_model_step_sample(const llmdec_config *cfg, const llmdec_model_weights *w,
+                                                 int32_t n_seqs, int32_t n_tokens, int32_t max_q_len,
+                                                 const int32_t *tokens, const int32_t *cu_seqlens,
+                                                 const int32_t *start_pos, const int32_t *block_tables,
+                                                 int32_t max_pages, llmdec_kv_pool *pool, const llmdec_sampling *params,
+                                                 int32_t *next_tokens, float *logits, void *ws, size_t ws_bytes,
+                                                 llmdec_stream stream) {
+  const char *who = "model_step_sample";
+  if (!cfg) return set_error(LLMDEC_E_INVALID, "%s: config is NULL", who);
+  llmdec_status st = check_sampling(params, cfg->vocab, who);
+  if (st != LLMDEC_OK) return st;
+  return model_step(who, cfg, w, n_seqs, n_tokens, max_q_len, tokens, cu_seqlens, start_pos, block_tables, max_pages,
+                    pool, params, next_tokens, logits, ws, ws_bytes, stream);
+}
+
+extern "C" llmdec_status llmdec_op_sample(const float *logits, int32_t rows, int32_t vocab,
+                                         const llmdec_sampling *params, int32_t *next, llmdec_stream stream) {
+  const char *who = "op_sample";
+  if (!logits || !next) return set_error(LLMDEC_E_INVALID, "%s: NULL pointer", who);
+  if (rows <= 0) return set_error(LLMDEC_E_INVALID, "%s: rows=%d out of range", who, rows);
+  llmdec_status st = check_sampling(params, vocab, who);
+  if (st != LLMDEC_OK) return st;
+  launch_sample(logits, rows, vocab, params->temperature, params->top_k, params->top_p, params->seed, params->step,
+                next, (hipStream_t)stream);
   return check_launch(who);
 }
 

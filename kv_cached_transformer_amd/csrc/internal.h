@@ -147,6 +147,11 @@ bool gemv_shape_ok(int k);
 void launch_gemv(const float *x, const uint16_t *gamma, float eps, const uint16_t *w_packed, int n, int k, int mode,
                  float *out, hipStream_t s);
 
+// Temperature / top-k / top-p sampling of fp32 logits [rows][vocab] (kernels_sample.hip); vocab <= 32768.
+bool sample_shape_ok(int vocab);
+void launch_sample(const float *logits, int rows, int vocab, float temperature, int top_k, float top_p,
+                   uint64_t seed, uint64_t step, int32_t *next, hipStream_t s);
+
 // Group-quantized matrices (kernels_quant.hip).  q8_shape_ok: cols a multiple of 16, at most 14336.
 bool q8_shape_ok(int cols);
 size_t q8_matrix_bytes(int rows, int cols);

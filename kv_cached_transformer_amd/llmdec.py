@@ -45,6 +45,11 @@ class llmdec_model_weights(C.Structure):
                 ("lm_head", C.c_void_p)]
 
 
+class llmdec_sampling(C.Structure):
+    _fields_ = [("temperature", C.c_float), ("top_k", C.c_int32), ("top_p", C.c_float), ("seed", C.c_uint64),
+                ("step", C.c_uint64)]
+
+
 class llmdec_q8_matrix(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("codes", "scales", "zeros")]
 
@@ -93,6 +98,9 @@ _SIGS = {
     "llmdec_op_prefill_attention": (_I, [_CFG, _P, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, _Z, _P]),
     "llmdec_op_silu_mul": (_I, [_P, _P, _I, _I, _P, _P]),
     "llmdec_op_lm_head_argmax": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _Z, _P]),
+    "llmdec_op_sample": (_I, [_P, _I, _I, C.POINTER(llmdec_sampling), _P, _P]),
+    "llmdec_model_step_sample": (_I, [_CFG, C.POINTER(llmdec_model_weights), _I, _I, _I, _P, _P, _P, _P, _I, _P,
+                                      C.POINTER(llmdec_sampling), _P, _P, _P, _Z, _P]),
     "llmdec_q8_matrix_bytes": (_Z, [_I, _I]),
     "llmdec_q8_pack_matrix": (_I, [_I, _I, C.POINTER(llmdec_q8_matrix), _P, _Z, _P]),
     "llmdec_q8_packed_layer_bytes": (_Z, [_CFG]),
@@ -314,3 +322,14 @@ def llmdec_layer_decode_q8(cfg, w, layer, hidden, n_seqs, ctx_lens, block_tables
                            stream=0):
     _check(lib().llmdec_layer_decode_q8(C.byref(cfg), C.byref(w), layer, hidden, n_seqs, ctx_lens, block_tables,
                                         max_pages, pool, ws, ws_bytes, stream))
+
+
+def llmdec_op_sample(logits, rows, vocab, params: llmdec_sampling, next_tokens, stream=0):
+    _check(lib().llmdec_op_sample(logits, rows, vocab, C.byref(params), next_tokens, stream))
+
+
+def llmdec_model_step_sample(cfg, mw, n_seqs, n_tokens, max_q_len, tokens, cu_seqlens, start_pos, block_tables,
+                             max_pages, pool, params: llmdec_sampling, next_tokens, logits, ws, ws_bytes, stream=0):
+    _check(lib().llmdec_model_step_sample(C.byref(cfg), C.byref(mw), n_seqs, n_tokens, max_q_len, tokens, cu_seqlens,
+                                          start_pos, block_tables, max_pages, pool, C.byref(params), next_tokens,
+                                          logits, ws, ws_bytes, stream))

@@ -16,7 +16,8 @@ cached tokens (weights and cache rotated over 4 copies so the 256 MB
 last-level cache does not serve them), decode over 32 sequences with contexts
 uniform in [128, 4096], a 4 x 512 prefill, and the batch-1 decode again with
 group-quantized matrices (8-bit codes, a bf16 scale and a zero point per 128
-inputs), with its four weight products also timed alone.  Each gets its
+inputs), with its four weight products also timed alone, and on-device
+sampling of 64 x 32000 logits.  Each gets its
 algorithmic bytes or FLOPs per step and the fraction of the MI355X peak.
 
 Inputs are seeded and synthetic: weights N(0, 0.02^2) in bf16 drawn on the
@@ -24,7 +25,7 @@ device, RMSNorm gains 1, cached K/V N(0, 1) in bf16.  Timing uses HIP events
 on the stream the library launches on.  The cpu_baseline leg times the CPU
 oracle (float64 NumPy) on a bounded sample of the same decode workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only c5,c2,q8,c3,c4]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only c5,c2,q8,sample,c3,c4]
 
 Profiling helpers (no GPU needed for the two summaries):
   python bench.py --only copy                  1 GiB device copies: calibrates the HBM counters
@@ -326,6 +327,26 @@ def bench_layer_decode_q8(torch, L, R, ctx, copies, iters):
     return res
 
 
+def bench_sample(torch, L, R, iters):
+    """Sampling 64 rows of 32000 logits on the device (temperature 0.8, top-k 50, top-p 0.9), against the
+    greedy argmax of the same rows (the choice C5 times)."""
+    rows, vocab = 64, 32000
+    g = torch.Generator(device="cuda")
+    g.manual_seed(SEED + 13)
+    logits = torch.randn(rows, vocab, device="cuda", generator=g, dtype=torch.float32) * 2.0
+    nxt = torch.empty(rows, dtype=torch.int32, device="cuda")
+    strm = R.stream()
+    res = {}
+    for name, (t, k, p) in (("sample_t0.8_k50_p0.9", (0.8, 50, 0.9)), ("sample_t1_p0.9", (1.0, 0, 0.9)),
+                            ("greedy", (0.0, 0, 1.0))):
+        def step(i, t=t, k=k, p=p):
+            L.llmdec_op_sample(logits.data_ptr(), rows, vocab, L.llmdec_sampling(t, k, p, 7, i), nxt.data_ptr(), strm)
+        ms = time_loop(torch, step, iters, 5)
+        res[name] = dict(us=ms * 1e3)
+        log(f"{name} 64 x 32000: {ms * 1e3:.1f} us")
+    return dict(workload="sample-64x32000", **res)
+
+
 def bench_layer_prefill(torch, L, R, iters):
     import numpy as np
     import synth
@@ -515,7 +536,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="c5,c2,q8,c3,c4", help="comma list of workloads to run (also: copy)")
+    ap.add_argument("--only", default="c5,c2,q8,sample,c3,c4", help="comma list of workloads to run (also: copy)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the attention traffic summary from two rocprofv3 --pmc output folders")
     ap.add_argument("--trace-summary", metavar="DIR", help="print a per-kernel table from a rocprofv3 kernel trace")
@@ -552,6 +573,8 @@ def main():
         extra["decode_b1_ctx2048"] = bench_layer_decode(torch, L, R, [2048], 4, 100, "7B-layer-decode-b1-ctx2048", 2)
     if "q8" in only:
         extra["decode_q8_b1_ctx2048"] = bench_layer_decode_q8(torch, L, R, 2048, 4, 100)
+    if "sample" in only:
+        extra["sample_64x32000"] = bench_sample(torch, L, R, 50)
     if "c3" in only:
         import synth
         extra["decode_b32_ctx128..4096"] = bench_layer_decode(torch, L, R, synth.context_lengths(3, 32, 128, 4096), 1,

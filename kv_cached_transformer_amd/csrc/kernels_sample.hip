@@ -74,6 +74,44 @@ __device__ inline float block_max(float v, float *scratch) {
   return t;
 }
 
+// Run by the 64 lanes of one wave: walking the 256 bins down from 255, find the first bin at which
+// start + (everything in higher bins) + (this bin) reaches target; bins with nothing in them are passed
+// over.  Lane l holds bins 255-4l .. 252-4l, and the lanes' totals meet in a prefix scan.  Writes the
+// bin and the running total before it; if no bin reaches the target (rounding), bin 0 and the total
+// of the higher bins.
+template <typename T>
+__device__ inline void find_bin_desc(const T *h, T start, T target, uint32_t *bin_out, T *before_out) {
+  const int lane = threadIdx.x & 63;
+  T c[4], t = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    c[q] = h[255 - (4 * lane + q)];
+    t += c[q];
+  }
+  T incl = t;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  T excl = __shfl_up(incl, 1, 64);
+  if (lane == 0) excl = 0;
+  T cum = start + excl, before = 0;
+  int hit = -1;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (hit < 0 && c[q] > 0 && cum + c[q] >= target) hit = q, before = cum;
+    cum += c[q];
+  }
+  const uint64_t m = __ballot(hit >= 0);
+  if (m) {
+    if (lane == __ffsll((unsigned long long)m) - 1) *bin_out = (uint32_t)(255 - (4 * lane + hit)), *before_out = before;
+  } else {
+    const T total = __shfl(incl, 63, 64);
+    if (lane == 0) *bin_out = 0u, *before_out = start + total - h[0];
+  }
+}
+
 __global__ __launch_bounds__(kSmpThreads) void sample_kernel(SampleArgs a) {
   __shared__ float red[kSmpWaves];
   __shared__ uint32_t hist[256];
@@ -135,18 +173,9 @@ __global__ __launch_bounds__(kSmpThreads) void sample_kernel(SampleArgs a) {
         if ((kept >> j & 1) && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        int cum = 0, d = 0;
-        for (int b = 255; b >= 0; --b) {
-          if (cum + (int)hist[b] >= remaining) {
-            d = b;
-            break;
-          }
-          cum += (int)hist[b];
-        }
-        sel[0] = (uint32_t)d;
-        sel[1] = (uint32_t)(remaining - cum);
-      }
+      if (wave == 0) find_bin_desc<uint32_t>(hist, 0u, (uint32_t)remaining, &sel[0], &sel[1]);
+      __syncthreads();
+      if (tid == 0) sel[1] = (uint32_t)remaining - sel[1];  // the rank left inside the chosen bin
       __syncthreads();
       prefix |= sel[0] << shift;
       pmask |= 255u << shift;
@@ -178,24 +207,8 @@ __global__ __launch_bounds__(kSmpThreads) void sample_kernel(SampleArgs a) {
         if ((kept >> j & 1) && (key & pmask) == prefix) atomicAdd(&histf[(key >> shift) & 255u], ev);
       }
       __syncthreads();
-      if (tid == 0) {
-        float cum = above;
-        int d = -1;
-        for (int b = 255; b >= 0; --b) {
-          if (histf[b] > 0.f && cum + histf[b] >= target) {
-            d = b;
-            break;
-          }
-          cum += histf[b];
-        }
-        if (d < 0) {  // rounding left the target out of reach: keep the whole range (lowest non-empty bin)
-          d = 0;
-          cum = above;
-          for (int b = 255; b > 0; --b) cum += histf[b];
-        }
-        sel[0] = (uint32_t)d;
-        self[0] = cum;
-      }
+      // (if rounding leaves the target out of reach, the whole range stays: bin 0)
+      if (wave == 0) find_bin_desc<float>(histf, above, target, &sel[0], &self[0]);
       __syncthreads();
       prefix |= sel[0] << shift;
       pmask |= 255u << shift;

@@ -15,8 +15,8 @@ Also reported (sub-benchmarks, one layer each): decode at batch 1 over 2048
 cached tokens (weights and cache rotated over 4 copies so the 256 MB
 last-level cache does not serve them), decode over 32 sequences with contexts
 uniform in [128, 4096], a 4 x 512 prefill, and the batch-1 decode again with
-group-quantized matrices (8-bit codes, a bf16 scale and a zero point per 128
-inputs), with its four weight products also timed alone, and on-device
+group-quantized matrices (8-bit and 4-bit codes, a bf16 scale and a zero point
+per 128 inputs), with its four weight products also timed alone, and on-device
 sampling of 64 x 32000 logits.  Each gets its
 algorithmic bytes or FLOPs per step and the fraction of the MI355X peak.
 
@@ -25,7 +25,7 @@ device, RMSNorm gains 1, cached K/V N(0, 1) in bf16.  Timing uses HIP events
 on the stream the library launches on.  The cpu_baseline leg times the CPU
 oracle (float64 NumPy) on a bounded sample of the same decode workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only c5,c2,q8,sample,c3,c4]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only c5,c2,q8,q4,sample,c3,c4]
 
 Profiling helpers (no GPU needed for the two summaries):
   python bench.py --only copy                  1 GiB device copies: calibrates the HBM counters
@@ -86,27 +86,33 @@ class Dev:
         torch.cuda.synchronize()
         return buf, st
 
-    def q8_matrix(self, rows, cols):
-        """Seeded device draws with the host generator's distributions (synth.q8_matrix): codes uniform
-        in 0..255, zero points in 112..143, bf16 scales U(0.75, 1.25) * 0.02 / 74, one per 128 columns."""
+    def q_matrix(self, rows, cols, bits):
+        """Seeded device draws with the host generators' distributions (synth.q8_matrix, synth.q4_matrix):
+        codes uniform over their range (a uniform byte is two uniform 4-bit codes), zero points near the
+        middle (112..143; 7..8), bf16 scales U(0.75, 1.25) * 0.02 / 74 (4.6 for 4-bit codes), one per 128
+        columns."""
         torch = self.torch
         g = (cols + 127) // 128
-        codes = torch.randint(0, 256, (rows, cols), device="cuda", generator=self.gen, dtype=torch.uint8)
+        nbytes_row = cols if bits == 8 else cols // 2
+        codes = torch.randint(0, 256, (rows, nbytes_row), device="cuda", generator=self.gen, dtype=torch.uint8)
         u = torch.rand(rows, g, device="cuda", generator=self.gen, dtype=torch.float32)
-        scales = ((0.75 + 0.5 * u) * (0.02 / 74.0)).to(torch.bfloat16)
-        zeros = torch.randint(112, 144, (rows, g), device="cuda", generator=self.gen, dtype=torch.uint8)
+        scales = ((0.75 + 0.5 * u) * (0.02 / (74.0 if bits == 8 else 4.6))).to(torch.bfloat16)
+        lo, hi = (112, 144) if bits == 8 else (7, 9)
+        zeros = torch.randint(lo, hi, (rows, g), device="cuda", generator=self.gen, dtype=torch.uint8)
         keep = (codes, scales, zeros)
         return keep, self.L.llmdec_q8_matrix(*(t.data_ptr() for t in keep))
 
-    def q8_layer(self):
-        torch, s = self.torch, self.shape
+    def q_layer(self, bits):
+        torch, s, L = self.torch, self.shape, self.L
         ones = torch.ones(s.hidden, device="cuda", dtype=torch.bfloat16)
-        mats = {k: self.q8_matrix(r, c) for k, (r, c) in s.matrix_shapes().items()}
-        w = self.L.llmdec_q8_layer_weights(ones.data_ptr(), *(mats[k][1] for k in ("wq", "wk", "wv", "wo")),
-                                           ones.data_ptr(), *(mats[k][1] for k in ("w_gate", "w_up", "w_down")))
-        nbytes = self.L.llmdec_q8_packed_layer_bytes(self.cfg)
+        mats = {k: self.q_matrix(r, c, bits) for k, (r, c) in s.matrix_shapes().items()}
+        w = L.llmdec_q8_layer_weights(ones.data_ptr(), *(mats[k][1] for k in ("wq", "wk", "wv", "wo")),
+                                      ones.data_ptr(), *(mats[k][1] for k in ("w_gate", "w_up", "w_down")))
+        size, pack = ((L.llmdec_q8_packed_layer_bytes, L.llmdec_q8_pack_layer) if bits == 8 else
+                      (L.llmdec_q4_packed_layer_bytes, L.llmdec_q4_pack_layer))
+        nbytes = size(self.cfg)
         buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-        st = self.L.llmdec_q8_pack_layer(self.cfg, w, buf.data_ptr(), nbytes, self.R.stream())
+        st = pack(self.cfg, w, buf.data_ptr(), nbytes, self.R.stream())
         torch.cuda.synchronize()
         return buf, st
 
@@ -266,24 +272,26 @@ def bench_layer_decode(torch, L, R, ctxs, copies, iters, tag, workload):
                 algorithmic_bytes=byt, hbm_frac=byt / (ms * 1e-3) / HBM_PEAK)
 
 
-def q8_matrix_bytes(rows, cols):
-    """Algorithmic bytes of a group-quantized matrix: one byte per code, 4 per group (bf16 scale, zero point)."""
-    return rows * cols + rows * ((cols + 127) // 128) * 4
+def q_matrix_bytes(rows, cols, bits):
+    """Algorithmic bytes of a group-quantized matrix: bits/8 bytes per code, 4 per group (bf16 scale, zero
+    point)."""
+    return rows * cols * bits // 8 + rows * ((cols + 127) // 128) * 4
 
 
-def q8_layer_bytes(shape):
-    return sum(q8_matrix_bytes(r, c) for r, c in shape.matrix_shapes().values()) + 2 * shape.hidden * 2
+def q_layer_bytes(shape, bits):
+    return sum(q_matrix_bytes(r, c, bits) for r, c in shape.matrix_shapes().values()) + 2 * shape.hidden * 2
 
 
-def bench_layer_decode_q8(torch, L, R, ctx, copies, iters):
-    """One 7B-shaped layer with group-quantized matrices, one sequence, ctx cached tokens; weights and
-    cache rotated over `copies` copies.  Also times the layer's four quantized products alone."""
+def bench_layer_decode_q(torch, L, R, ctx, copies, iters, bits):
+    """One 7B-shaped layer with group-quantized matrices (8- or 4-bit codes), one sequence, ctx cached
+    tokens; weights and cache rotated over `copies` copies.  Also times the layer's four quantized
+    products alone."""
     import numpy as np
     import synth
     shape = synth.LLAMA7B_LAYER
-    tag = f"7B-layer-decode-q8-b1-ctx{ctx}"
-    d = Dev(torch, L, R, shape, SEED + 12)
-    layers = [d.q8_layer() for _ in range(copies)]
+    tag = f"7B-layer-decode-q{bits}-b1-ctx{ctx}"
+    d = Dev(torch, L, R, shape, SEED + 12 + bits)
+    layers = [d.q_layer(bits) for _ in range(copies)]
     per_copy = synth.pages_for(ctx + 1)
     pool = d.pool(per_copy * copies, synth.free_order(12, per_copy * copies))
     bts = [R.dev_i32(alloc_rows(pool, [ctx + 1], per_copy)) for _ in range(copies)]
@@ -292,15 +300,18 @@ def bench_layer_decode_q8(torch, L, R, ctx, copies, iters):
     ws = R.Workspace(L.llmdec_workspace_bytes(d.cfg, 1, 1, per_copy))
     strm = R.stream()
 
+    decode = L.llmdec_layer_decode_q8 if bits == 8 else L.llmdec_layer_decode_q4
+    linear = L.llmdec_op_linear_q8 if bits == 8 else L.llmdec_op_linear_q4
+
     def step(i):
         c = i % copies
-        L.llmdec_layer_decode_q8(d.cfg, layers[c][1], 0, x.data_ptr(), 1, ctx_d.data_ptr(), bts[c].data_ptr(),
-                                 per_copy, pool.handle, ws.ptr, ws.nbytes, strm)
+        decode(d.cfg, layers[c][1], 0, x.data_ptr(), 1, ctx_d.data_ptr(), bts[c].data_ptr(), per_copy, pool.handle,
+               ws.ptr, ws.nbytes, strm)
 
     ms = time_loop(torch, step, iters, 2 * copies)
     assert ws.error_bits() == 0
     kv = float(ctx + 1) * 2 * shape.hidden * 2
-    byt = q8_layer_bytes(shape) + kv + 2 * shape.hidden * 4
+    byt = q_layer_bytes(shape, bits) + kv + 2 * shape.hidden * 4
     log(f"{tag}: {ms * 1e3:.1f} us per layer-step, {byt / (ms * 1e-3) / 1e9:.0f} GB/s")
 
     # the four products alone (q|k|v, o, [gate; up], down), same rotation
@@ -311,13 +322,13 @@ def bench_layer_decode_q8(torch, L, R, ctx, copies, iters):
 
     def products(i):
         st = layers[i % copies][1]
-        L.llmdec_op_linear_q8(y.data_ptr(), h, st.w_qkv, nqkv, out.data_ptr(), 0, strm)
-        L.llmdec_op_linear_q8(y.data_ptr(), h, st.w_o, h, out.data_ptr(), 0, strm)
-        L.llmdec_op_linear_q8(y.data_ptr(), h, st.w_gu, 2 * I, out.data_ptr(), 0, strm)
-        L.llmdec_op_linear_q8(y.data_ptr(), I, st.w_down, h, out.data_ptr(), 0, strm)
+        linear(y.data_ptr(), h, st.w_qkv, nqkv, out.data_ptr(), 0, strm)
+        linear(y.data_ptr(), h, st.w_o, h, out.data_ptr(), 0, strm)
+        linear(y.data_ptr(), h, st.w_gu, 2 * I, out.data_ptr(), 0, strm)
+        linear(y.data_ptr(), I, st.w_down, h, out.data_ptr(), 0, strm)
 
     pms = time_loop(torch, products, iters, 2 * copies)
-    pbyt = q8_layer_bytes(shape) - 2 * shape.hidden * 2
+    pbyt = q_layer_bytes(shape, bits) - 2 * shape.hidden * 2
     log(f"{tag} products: {pms * 1e3:.1f} us for {pbyt / 1e6:.1f} MB, {pbyt / (pms * 1e-3) / 1e9:.0f} GB/s")
     res = dict(workload=tag, ms_per_layer_step=ms, layer_steps_per_s=1e3 / ms, tokens_per_s=1e3 / ms,
                algorithmic_bytes=byt, hbm_frac=byt / (ms * 1e-3) / HBM_PEAK,
@@ -536,7 +547,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="c5,c2,q8,sample,c3,c4", help="comma list of workloads to run (also: copy)")
+    ap.add_argument("--only", default="c5,c2,q8,q4,sample,c3,c4", help="comma list of workloads to run (also: copy)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the attention traffic summary from two rocprofv3 --pmc output folders")
     ap.add_argument("--trace-summary", metavar="DIR", help="print a per-kernel table from a rocprofv3 kernel trace")
@@ -572,7 +583,9 @@ def main():
     if "c2" in only:
         extra["decode_b1_ctx2048"] = bench_layer_decode(torch, L, R, [2048], 4, 100, "7B-layer-decode-b1-ctx2048", 2)
     if "q8" in only:
-        extra["decode_q8_b1_ctx2048"] = bench_layer_decode_q8(torch, L, R, 2048, 4, 100)
+        extra["decode_q8_b1_ctx2048"] = bench_layer_decode_q(torch, L, R, 2048, 4, 100, 8)
+    if "q4" in only:
+        extra["decode_q4_b1_ctx2048"] = bench_layer_decode_q(torch, L, R, 2048, 4, 100, 4)
     if "sample" in only:
         extra["sample_64x32000"] = bench_sample(torch, L, R, 50)
     if "c3" in only:

@@ -418,6 +418,30 @@ llmdec_status llmdec_layer_decode_q8(const llmdec_config *cfg, const llmdec_q8_p
                                      const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool, void *ws,
                                      size_t ws_bytes, llmdec_stream stream);
 
+/* ------------------------------------------------------------------ 4-bit codes
+ * The same scheme with 4-bit codes and zero points (0..15), two codes to a
+ * byte: byte j of a row holds column 2j in its low nibble and 2j+1 in its
+ * high nibble, so a row of `cols` codes is cols/2 bytes in the caller's
+ * codes array ([rows][cols/2]); scales and zeros as for 8-bit codes.  The
+ * packed matrix pads each row's codes with zero codes to a multiple of 16
+ * bytes; its metadata words are ordered for 4 lanes per group.  The entry
+ * points below mirror the 8-bit ones (same errors, same limits). */
+typedef llmdec_q8_matrix llmdec_q4_matrix;
+typedef llmdec_q8_layer_weights llmdec_q4_layer_weights;
+typedef llmdec_q8_packed_layer llmdec_q4_packed_layer;
+size_t llmdec_q4_matrix_bytes(int32_t rows, int32_t cols);
+llmdec_status llmdec_q4_pack_matrix(int32_t rows, int32_t cols, const llmdec_q4_matrix *src, void *dst,
+                                    size_t dst_bytes, llmdec_stream stream);
+size_t llmdec_q4_packed_layer_bytes(const llmdec_config *cfg);
+llmdec_status llmdec_q4_pack_layer(const llmdec_config *cfg, const llmdec_q4_layer_weights *in, void *dst,
+                                   size_t dst_bytes, llmdec_q4_packed_layer *out, llmdec_stream stream);
+llmdec_status llmdec_op_linear_q4(const float *a, int32_t k_dim, const void *w_q4_packed, int32_t n_dim, float *out,
+                                  int32_t accumulate, llmdec_stream stream);
+llmdec_status llmdec_layer_decode_q4(const llmdec_config *cfg, const llmdec_q4_packed_layer *w, int32_t layer,
+                                     float *hidden, int32_t n_seqs, const int32_t *ctx_lens,
+                                     const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool, void *ws,
+                                     size_t ws_bytes, llmdec_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

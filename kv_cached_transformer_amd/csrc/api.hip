@@ -715,32 +715,14 @@ extern "C" llmdec_status llmdec_op_lm_head_argmax(const float *x, int32_t rows, 
 // ------------------------------------------------------------------ group-quantized weights
 // A quantized matrix is supported when its rows split into the four-row tasks of the matrix-vector
 // kernel and its columns into whole 16-byte lane chunks that fit the kernel's LDS staging of x.
-static bool q8_ok(int rows, int cols) {
+static bool q_ok(int bits, int rows, int cols) {
   // byte offsets inside the packed matrix stay below 2^31 (the kernel's buffer offsets)
-  return rows > 0 && rows % 4 == 0 && q8_shape_ok(cols) && q8_matrix_bytes(rows, cols) < (size_t)1 << 31;
+  return rows > 0 && rows % 4 == 0 && q_shape_ok(bits, cols) && q_matrix_bytes(bits, rows, cols) < (size_t)1 << 31;
 }
 
-extern "C" size_t llmdec_q8_matrix_bytes(int32_t rows, int32_t cols) {
-  return q8_ok(rows, cols) ? q8_matrix_bytes(rows, cols) : 0;
-}
+static bool q_src_ok(const llmdec_q8_matrix *m) { return m && m->codes && m->scales && m->zeros; }
 
-static bool q8_src_ok(const llmdec_q8_matrix *m) { return m && m->codes && m->scales && m->zeros; }
-
-extern "C" llmdec_status llmdec_q8_pack_matrix(int32_t rows, int32_t cols, const llmdec_q8_matrix *src, void *dst,
-                                              size_t dst_bytes, llmdec_stream stream) {
-  if (!q8_src_ok(src) || !dst) return set_error(LLMDEC_E_INVALID, "q8_pack_matrix: NULL pointer");
-  if (!q8_ok(rows, cols))
-    return set_error(LLMDEC_E_INVALID,
-                     "q8_pack_matrix: rows (%d) must be a positive multiple of 4, cols (%d) a positive multiple of 16 "
-                     "and at most 14336", rows, cols);
-  const size_t need = q8_matrix_bytes(rows, cols);
-  if (dst_bytes < need) return set_error(LLMDEC_E_INVALID, "q8_pack_matrix: dst holds %zu bytes, %zu needed", dst_bytes, need);
-  launch_q8_pack((const uint8_t *)src->codes, (const uint16_t *)src->scales, (const uint8_t *)src->zeros, rows, cols,
-                 (uint8_t *)dst, rows, 0, (hipStream_t)stream);
-  return check_launch("q8_pack_matrix");
-}
-
-static size_t q8_layer_parts(const llmdec_config &c, size_t off[6]) {
+static size_t q_layer_parts(int bits, const llmdec_config &c, size_t off[6]) {
   const int h = c.hidden, I = c.intermediate;
   size_t o = 0;
   off[0] = o;  // attn_norm
@@ -748,42 +730,59 @@ static size_t q8_layer_parts(const llmdec_config &c, size_t off[6]) {
   off[1] = o;  // mlp_norm
   o += al((size_t)h * 2);
   off[2] = o;  // q|k|v
-  o += al(q8_matrix_bytes(qkv_cols(c), h));
+  o += al(q_matrix_bytes(bits, qkv_cols(c), h));
   off[3] = o;  // o
-  o += al(q8_matrix_bytes(h, h));
+  o += al(q_matrix_bytes(bits, h, h));
   off[4] = o;  // [gate; up]
-  o += al(q8_matrix_bytes(2 * I, h));
+  o += al(q_matrix_bytes(bits, 2 * I, h));
   off[5] = o;  // down
-  o += al(q8_matrix_bytes(h, I));
+  o += al(q_matrix_bytes(bits, h, I));
   return o;
 }
 
-static bool q8_layer_ok(const llmdec_config &c) {
-  return q8_ok(qkv_cols(c), c.hidden) && q8_ok(c.hidden, c.hidden) && q8_ok(2 * c.intermediate, c.hidden) &&
-         q8_ok(c.hidden, c.intermediate) && c.intermediate % 2 == 0;
+static bool q_layer_ok(int bits, const llmdec_config &c) {
+  return q_ok(bits, qkv_cols(c), c.hidden) && q_ok(bits, c.hidden, c.hidden) && q_ok(bits, 2 * c.intermediate, c.hidden) &&
+         q_ok(bits, c.hidden, c.intermediate) && c.intermediate % 2 == 0;
 }
 
-extern "C" size_t llmdec_q8_packed_layer_bytes(const llmdec_config *cfg) {
-  if (check_config(cfg, "q8_packed_layer_bytes") != LLMDEC_OK || !q8_layer_ok(*cfg)) return 0;
+static size_t q_matrix_bytes_api(int bits, int32_t rows, int32_t cols) {
+  return q_ok(bits, rows, cols) ? q_matrix_bytes(bits, rows, cols) : 0;
+}
+
+static llmdec_status q_pack_matrix(int bits, const char *who, int32_t rows, int32_t cols, const llmdec_q8_matrix *src,
+                                   void *dst, size_t dst_bytes, llmdec_stream stream) {
+  if (!q_src_ok(src) || !dst) return set_error(LLMDEC_E_INVALID, "%s: NULL pointer", who);
+  if (!q_ok(bits, rows, cols))
+    return set_error(LLMDEC_E_INVALID,
+                     "%s: rows (%d) must be a positive multiple of 4, cols (%d) a positive multiple of 16 and at most "
+                     "14336", who, rows, cols);
+  const size_t need = q_matrix_bytes(bits, rows, cols);
+  if (dst_bytes < need) return set_error(LLMDEC_E_INVALID, "%s: dst holds %zu bytes, %zu needed", who, dst_bytes, need);
+  launch_q_pack(bits, (const uint8_t *)src->codes, (const uint16_t *)src->scales, (const uint8_t *)src->zeros, rows,
+                cols, (uint8_t *)dst, rows, 0, (hipStream_t)stream);
+  return check_launch(who);
+}
+
+static size_t q_packed_layer_bytes(int bits, const char *who, const llmdec_config *cfg) {
+  if (check_config(cfg, who) != LLMDEC_OK || !q_layer_ok(bits, *cfg)) return 0;
   size_t off[6];
-  return q8_layer_parts(*cfg, off);
+  return q_layer_parts(bits, *cfg, off);
 }
 
-extern "C" llmdec_status llmdec_q8_pack_layer(const llmdec_config *cfg, const llmdec_q8_layer_weights *in, void *dst,
-                                             size_t dst_bytes, llmdec_q8_packed_layer *out, llmdec_stream stream) {
-  const char *who = "q8_pack_layer";
+static llmdec_status q_pack_layer(int bits, const char *who, const llmdec_config *cfg, const llmdec_q8_layer_weights *in,
+                                  void *dst, size_t dst_bytes, llmdec_q8_packed_layer *out, llmdec_stream stream) {
   llmdec_status st = check_config(cfg, who);
   if (st != LLMDEC_OK) return st;
-  if (!in || !dst || !out || !in->attn_norm || !in->mlp_norm || !q8_src_ok(&in->wq) || !q8_src_ok(&in->wk) ||
-      !q8_src_ok(&in->wv) || !q8_src_ok(&in->wo) || !q8_src_ok(&in->w_gate) || !q8_src_ok(&in->w_up) ||
-      !q8_src_ok(&in->w_down))
+  if (!in || !dst || !out || !in->attn_norm || !in->mlp_norm || !q_src_ok(&in->wq) || !q_src_ok(&in->wk) ||
+      !q_src_ok(&in->wv) || !q_src_ok(&in->wo) || !q_src_ok(&in->w_gate) || !q_src_ok(&in->w_up) ||
+      !q_src_ok(&in->w_down))
     return set_error(LLMDEC_E_INVALID, "%s: NULL pointer", who);
-  if (!q8_layer_ok(*cfg))
+  if (!q_layer_ok(bits, *cfg))
     return set_error(LLMDEC_E_UNSUPPORTED, "%s: hidden %d / intermediate %d: quantized matrices need row counts that are "
                      "multiples of 4 and input widths that are multiples of 16, at most 14336", who, cfg->hidden,
                      cfg->intermediate);
   size_t off[6];
-  const size_t need = q8_layer_parts(*cfg, off);
+  const size_t need = q_layer_parts(bits, *cfg, off);
   if (dst_bytes < need) return set_error(LLMDEC_E_INVALID, "%s: dst holds %zu bytes, %zu needed", who, dst_bytes, need);
   const int h = cfg->hidden, I = cfg->intermediate, kv = kv_cols(*cfg), nqkv = qkv_cols(*cfg);
   hipStream_t s = (hipStream_t)stream;
@@ -792,8 +791,8 @@ extern "C" llmdec_status llmdec_q8_pack_layer(const llmdec_config *cfg, const ll
       hipMemcpyAsync(d + off[1], in->mlp_norm, (size_t)h * 2, hipMemcpyDeviceToDevice, s) != hipSuccess)
     return set_error(LLMDEC_E_HIP, "%s: copy of the norm gains failed", who);
   auto pack = [&](const llmdec_q8_matrix &m, int rows, int cols, size_t at_off, int dst_rows, int row0) {
-    launch_q8_pack((const uint8_t *)m.codes, (const uint16_t *)m.scales, (const uint8_t *)m.zeros, rows, cols,
-                   (uint8_t *)(d + at_off), dst_rows, row0, s);
+    launch_q_pack(bits, (const uint8_t *)m.codes, (const uint16_t *)m.scales, (const uint8_t *)m.zeros, rows, cols,
+                  (uint8_t *)(d + at_off), dst_rows, row0, s);
   };
   pack(in->wq, h, h, off[2], nqkv, 0);
   pack(in->wk, kv, h, off[2], nqkv, h);
@@ -813,27 +812,26 @@ extern "C" llmdec_status llmdec_q8_pack_layer(const llmdec_config *cfg, const ll
   return LLMDEC_OK;
 }
 
-extern "C" llmdec_status llmdec_op_linear_q8(const float *a, int32_t k_dim, const void *w_q8_packed, int32_t n_dim,
-                                            float *out, int32_t accumulate, llmdec_stream stream) {
-  if (!a || !w_q8_packed || !out) return set_error(LLMDEC_E_INVALID, "op_linear_q8: NULL pointer");
-  if (!q8_ok(n_dim, k_dim))
-    return set_error(LLMDEC_E_INVALID, "op_linear_q8: n=%d k=%d unsupported (n a multiple of 4, k of 16, k <= 14336)",
+static llmdec_status q_op_linear(int bits, const char *who, const float *a, int32_t k_dim, const void *w_packed,
+                                 int32_t n_dim, float *out, int32_t accumulate, llmdec_stream stream) {
+  if (!a || !w_packed || !out) return set_error(LLMDEC_E_INVALID, "%s: NULL pointer", who);
+  if (!q_ok(bits, n_dim, k_dim))
+    return set_error(LLMDEC_E_INVALID, "%s: n=%d k=%d unsupported (n a multiple of 4, k of 16, k <= 14336)", who,
                      n_dim, k_dim);
-  launch_q8_gemv(a, nullptr, 0.f, (const uint8_t *)w_q8_packed, n_dim, k_dim, accumulate ? kAccumulate : kStore, out,
-                 (hipStream_t)stream);
-  return check_launch("op_linear_q8");
+  launch_q_gemv(bits, a, nullptr, 0.f, (const uint8_t *)w_packed, n_dim, k_dim, accumulate ? kAccumulate : kStore,
+                out, (hipStream_t)stream);
+  return check_launch(who);
 }
 
-extern "C" llmdec_status llmdec_layer_decode_q8(const llmdec_config *cfg, const llmdec_q8_packed_layer *w,
-                                               int32_t layer, float *hidden, int32_t n_seqs, const int32_t *ctx_lens,
-                                               const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool,
-                                               void *ws, size_t ws_bytes, llmdec_stream stream) {
-  const char *who = "layer_decode_q8";
+static llmdec_status q_layer_decode(int bits, const char *who, const llmdec_config *cfg,
+                                    const llmdec_q8_packed_layer *w, int32_t layer, float *hidden, int32_t n_seqs,
+                                    const int32_t *ctx_lens, const int32_t *block_tables, int32_t max_pages,
+                                    llmdec_kv_pool *pool, void *ws, size_t ws_bytes, llmdec_stream stream) {
   llmdec_status st = check_config(cfg, who);
   if (st != LLMDEC_OK) return st;
   if (!w || !w->attn_norm || !w->mlp_norm || !w->w_qkv || !w->w_o || !w->w_gu || !w->w_down)
     return set_error(LLMDEC_E_INVALID, "%s: packed layer weights missing", who);
-  if (!q8_layer_ok(*cfg)) return set_error(LLMDEC_E_UNSUPPORTED, "%s: shape unsupported for quantized matrices", who);
+  if (!q_layer_ok(bits, *cfg)) return set_error(LLMDEC_E_UNSUPPORTED, "%s: shape unsupported for quantized matrices", who);
   st = check_pool(pool, *cfg, layer, who);
   if (st != LLMDEC_OK) return st;
   if (!hidden || !ctx_lens || !block_tables) return set_error(LLMDEC_E_INVALID, "%s: NULL device pointer", who);
@@ -853,14 +851,66 @@ extern "C" llmdec_status llmdec_layer_decode_q8(const llmdec_config *cfg, const 
   uint16_t *pk, *pv;
   pool_layer(pool, layer, &pk, &pv);
   // x += Wo . attn(rope(Wq y), rope(Wk y), Wv y),  y = RMSNorm(x): the product stages y itself
-  launch_q8_gemv(hidden, (const uint16_t *)w->attn_norm, c.rms_eps, (const uint8_t *)w->w_qkv, nqkv, h, kStore, qkv, s);
+  launch_q_gemv(bits, hidden, (const uint16_t *)w->attn_norm, c.rms_eps, (const uint8_t *)w->w_qkv, nqkv, h, kStore,
+                qkv, s);
   launch_rope_append(c, qkv, nullptr, Splits{}, nqkv, 1, 1, nullptr, ctx_lens, block_tables, max_pages, pk, pv,
                      pool->num_pages, err, s);
   launch_decode_attention(c, qkv, nqkv, 1, ctx_lens, block_tables, max_pages, pk, pv, pool->num_pages,
                           at<float>(ws, L.attn_part), y, nullptr, nullptr, 0, err, s);
-  launch_q8_gemv(y, nullptr, 0.f, (const uint8_t *)w->w_o, h, h, kAccumulate, hidden, s);
+  launch_q_gemv(bits, y, nullptr, 0.f, (const uint8_t *)w->w_o, h, h, kAccumulate, hidden, s);
   // x += Wd (silu(Wg y) * (Wu y)),  y = RMSNorm(x)
-  launch_q8_gemv(hidden, (const uint16_t *)w->mlp_norm, c.rms_eps, (const uint8_t *)w->w_gu, 2 * I, h, kSiluMul, u, s);
-  launch_q8_gemv(u, nullptr, 0.f, (const uint8_t *)w->w_down, h, I, kAccumulate, hidden, s);
+  launch_q_gemv(bits, hidden, (const uint16_t *)w->mlp_norm, c.rms_eps, (const uint8_t *)w->w_gu, 2 * I, h, kSiluMul,
+                u, s);
+  launch_q_gemv(bits, u, nullptr, 0.f, (const uint8_t *)w->w_down, h, I, kAccumulate, hidden, s);
   return check_launch(who);
+}
+
+// 8-bit codes
+extern "C" size_t llmdec_q8_matrix_bytes(int32_t rows, int32_t cols) { return q_matrix_bytes_api(8, rows, cols); }
+extern "C" llmdec_status llmdec_q8_pack_matrix(int32_t rows, int32_t cols, const llmdec_q8_matrix *src, void *dst,
+                                              size_t dst_bytes, llmdec_stream stream) {
+  return q_pack_matrix(8, "q8_pack_matrix", rows, cols, src, dst, dst_bytes, stream);
+}
+extern "C" size_t llmdec_q8_packed_layer_bytes(const llmdec_config *cfg) {
+  return q_packed_layer_bytes(8, "q8_packed_layer_bytes", cfg);
+}
+extern "C" llmdec_status llmdec_q8_pack_layer(const llmdec_config *cfg, const llmdec_q8_layer_weights *in, void *dst,
+                                             size_t dst_bytes, llmdec_q8_packed_layer *out, llmdec_stream stream) {
+  return q_pack_layer(8, "q8_pack_layer", cfg, in, dst, dst_bytes, out, stream);
+}
+extern "C" llmdec_status llmdec_op_linear_q8(const float *a, int32_t k_dim, const void *w_q8_packed, int32_t n_dim,
+                                            float *out, int32_t accumulate, llmdec_stream stream) {
+  return q_op_linear(8, "op_linear_q8", a, k_dim, w_q8_packed, n_dim, out, accumulate, stream);
+}
+extern "C" llmdec_status llmdec_layer_decode_q8(const llmdec_config *cfg, const llmdec_q8_packed_layer *w,
+                                               int32_t layer, float *hidden, int32_t n_seqs, const int32_t *ctx_lens,
+                                               const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool,
+                                               void *ws, size_t ws_bytes, llmdec_stream stream) {
+  return q_layer_decode(8, "layer_decode_q8", cfg, w, layer, hidden, n_seqs, ctx_lens, block_tables, max_pages, pool,
+                        ws, ws_bytes, stream);
+}
+
+// 4-bit codes
+extern "C" size_t llmdec_q4_matrix_bytes(int32_t rows, int32_t cols) { return q_matrix_bytes_api(4, rows, cols); }
+extern "C" llmdec_status llmdec_q4_pack_matrix(int32_t rows, int32_t cols, const llmdec_q4_matrix *src, void *dst,
+                                              size_t dst_bytes, llmdec_stream stream) {
+  return q_pack_matrix(4, "q4_pack_matrix", rows, cols, src, dst, dst_bytes, stream);
+}
+extern "C" size_t llmdec_q4_packed_layer_bytes(const llmdec_config *cfg) {
+  return q_packed_layer_bytes(4, "q4_packed_layer_bytes", cfg);
+}
+extern "C" llmdec_status llmdec_q4_pack_layer(const llmdec_config *cfg, const llmdec_q4_layer_weights *in, void *dst,
+                                             size_t dst_bytes, llmdec_q4_packed_layer *out, llmdec_stream stream) {
+  return q_pack_layer(4, "q4_pack_layer", cfg, in, dst, dst_bytes, out, stream);
+}
+extern "C" llmdec_status llmdec_op_linear_q4(const float *a, int32_t k_dim, const void *w_q4_packed, int32_t n_dim,
+                                            float *out, int32_t accumulate, llmdec_stream stream) {
+  return q_op_linear(4, "op_linear_q4", a, k_dim, w_q4_packed, n_dim, out, accumulate, stream);
+}
+extern "C" llmdec_status llmdec_layer_decode_q4(const llmdec_config *cfg, const llmdec_q4_packed_layer *w,
+                                               int32_t layer, float *hidden, int32_t n_seqs, const int32_t *ctx_lens,
+                                               const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool,
+                                               void *ws, size_t ws_bytes, llmdec_stream stream) {
+  return q_layer_decode(4, "layer_decode_q4", cfg, w, layer, hidden, n_seqs, ctx_lens, block_tables, max_pages, pool,
+                        ws, ws_bytes, stream);
 }

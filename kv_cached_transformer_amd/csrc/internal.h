@@ -152,17 +152,18 @@ bool sample_shape_ok(int vocab);
 void launch_sample(const float *logits, int rows, int vocab, float temperature, int top_k, float top_p,
                    uint64_t seed, uint64_t step, int32_t *next, hipStream_t s);
 
-// Group-quantized matrices (kernels_quant.hip).  q8_shape_ok: cols a multiple of 16, at most 14336.
-bool q8_shape_ok(int cols);
-size_t q8_matrix_bytes(int rows, int cols);
+// Group-quantized matrices (kernels_quant.hip), codes of `bits` = 8 or 4 bits.  q_shape_ok: cols a
+// multiple of 16, at most 14336.
+bool q_shape_ok(int bits, int cols);
+size_t q_matrix_bytes(int bits, int rows, int cols);
 // Pack a source matrix's rows into rows dst_row0.. of a packed matrix with dst_rows rows in all.
-void launch_q8_pack(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros, int rows, int cols,
-                    uint8_t *dst, int dst_rows, int dst_row0, hipStream_t s);
+void launch_q_pack(int bits, const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros, int rows, int cols,
+                   uint8_t *dst, int dst_rows, int dst_row0, hipStream_t s);
 // One-row product with a packed quantized matrix of `rows` rows: mode kStore / kAccumulate write
 // out[0..rows); kSiluMul reads the matrix as [gate; up] and writes out[j] = silu(gate_j) * up_j for
 // j < rows / 2.  rows % 4 == 0.  gamma != NULL: the product reads rmsnorm(x) * gamma (eps inside the root)
 // instead of x.
-void launch_q8_gemv(const float *x, const uint16_t *gamma, float eps, const uint8_t *w, int rows, int k, int mode,
-                    float *out, hipStream_t s);
+void launch_q_gemv(int bits, const float *x, const uint16_t *gamma, float eps, const uint8_t *w, int rows, int k,
+                   int mode, float *out, hipStream_t s);
 
 }  // namespace llmdec

@@ -101,6 +101,14 @@ _SIGS = {
     "llmdec_op_sample": (_I, [_P, _I, _I, C.POINTER(llmdec_sampling), _P, _P]),
     "llmdec_model_step_sample": (_I, [_CFG, C.POINTER(llmdec_model_weights), _I, _I, _I, _P, _P, _P, _P, _I, _P,
                                       C.POINTER(llmdec_sampling), _P, _P, _P, _Z, _P]),
+    "llmdec_q4_matrix_bytes": (_Z, [_I, _I]),
+    "llmdec_q4_pack_matrix": (_I, [_I, _I, C.POINTER(llmdec_q8_matrix), _P, _Z, _P]),
+    "llmdec_q4_packed_layer_bytes": (_Z, [_CFG]),
+    "llmdec_q4_pack_layer": (_I, [_CFG, C.POINTER(llmdec_q8_layer_weights), _P, _Z, C.POINTER(llmdec_q8_packed_layer),
+                                  _P]),
+    "llmdec_op_linear_q4": (_I, [_P, _I, _P, _I, _P, _I, _P]),
+    "llmdec_layer_decode_q4": (_I, [_CFG, C.POINTER(llmdec_q8_packed_layer), _I, _P, _I, _P, _P, _I, _P, _P, _Z,
+                                    _P]),
     "llmdec_q8_matrix_bytes": (_Z, [_I, _I]),
     "llmdec_q8_pack_matrix": (_I, [_I, _I, C.POINTER(llmdec_q8_matrix), _P, _Z, _P]),
     "llmdec_q8_packed_layer_bytes": (_Z, [_CFG]),
@@ -333,3 +341,36 @@ def llmdec_model_step_sample(cfg, mw, n_seqs, n_tokens, max_q_len, tokens, cu_se
     _check(lib().llmdec_model_step_sample(C.byref(cfg), C.byref(mw), n_seqs, n_tokens, max_q_len, tokens, cu_seqlens,
                                           start_pos, block_tables, max_pages, pool, C.byref(params), next_tokens,
                                           logits, ws, ws_bytes, stream))
+
+
+# 4-bit codes: the same structs (codes two to a byte)
+llmdec_q4_matrix, llmdec_q4_layer_weights, llmdec_q4_packed_layer = (llmdec_q8_matrix, llmdec_q8_layer_weights,
+                                                                      llmdec_q8_packed_layer)
+
+
+def llmdec_q4_matrix_bytes(rows, cols):
+    return lib().llmdec_q4_matrix_bytes(rows, cols)
+
+
+def llmdec_q4_pack_matrix(rows, cols, src: llmdec_q8_matrix, dst, dst_bytes, stream=0):
+    _check(lib().llmdec_q4_pack_matrix(rows, cols, C.byref(src), dst, dst_bytes, stream))
+
+
+def llmdec_q4_packed_layer_bytes(cfg):
+    return lib().llmdec_q4_packed_layer_bytes(C.byref(cfg))
+
+
+def llmdec_q4_pack_layer(cfg, weights: llmdec_q8_layer_weights, dst, dst_bytes, stream=0) -> llmdec_q8_packed_layer:
+    out = llmdec_q8_packed_layer()
+    _check(lib().llmdec_q4_pack_layer(C.byref(cfg), C.byref(weights), dst, dst_bytes, C.byref(out), stream))
+    return out
+
+
+def llmdec_op_linear_q4(a, k_dim, w_q4_packed, n_dim, out, accumulate, stream=0):
+    _check(lib().llmdec_op_linear_q4(a, k_dim, w_q4_packed, n_dim, out, int(accumulate), stream))
+
+
+def llmdec_layer_decode_q4(cfg, w, layer, hidden, n_seqs, ctx_lens, block_tables, max_pages, pool, ws, ws_bytes,
+                           stream=0):
+    _check(lib().llmdec_layer_decode_q4(C.byref(cfg), C.byref(w), layer, hidden, n_seqs, ctx_lens, block_tables,
+                                        max_pages, pool, ws, ws_bytes, stream))

@@ -70,30 +70,36 @@ def _q8_upload(m):
 
 
 class Q8Matrix:
-    """One group-quantized matrix packed for the kernels; owns its device buffer."""
+    """One group-quantized matrix packed for the kernels; owns its device buffer.  bits = 8, or 4 (codes
+    two to a byte: m[0] is [rows][cols/2] and cols must be given)."""
 
-    def __init__(self, m):
-        rows, cols = m[0].shape
-        nbytes = L.llmdec_q8_matrix_bytes(rows, cols)
+    def __init__(self, m, bits: int = 8, cols: int = None):
+        rows = m[0].shape[0]
+        cols = m[0].shape[1] if bits == 8 else cols
+        size, pack = ((L.llmdec_q8_matrix_bytes, L.llmdec_q8_pack_matrix) if bits == 8 else
+                      (L.llmdec_q4_matrix_bytes, L.llmdec_q4_pack_matrix))
+        nbytes = size(rows, cols)
         self.buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         src, struct = _q8_upload(m)
-        L.llmdec_q8_pack_matrix(rows, cols, struct, self.buf.data_ptr(), nbytes, stream())
+        pack(rows, cols, struct, self.buf.data_ptr(), nbytes, stream())
         torch.cuda.current_stream().synchronize()
         del src
         self.ptr = self.buf.data_ptr()
 
 
 class Q8Layer:
-    """One layer with group-quantized matrices, packed; owns its device buffer."""
+    """One layer with group-quantized matrices (bits = 8 or 4), packed; owns its device buffer."""
 
-    def __init__(self, cfg, tensors: dict):
-        nbytes = L.llmdec_q8_packed_layer_bytes(cfg)
+    def __init__(self, cfg, tensors: dict, bits: int = 8):
+        size, pack = ((L.llmdec_q8_packed_layer_bytes, L.llmdec_q8_pack_layer) if bits == 8 else
+                      (L.llmdec_q4_packed_layer_bytes, L.llmdec_q4_pack_layer))
+        nbytes = size(cfg)
         self.buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         norms = {k: dev_u16(tensors[k]) for k in ("attn_norm", "mlp_norm")}
         up = {k: _q8_upload(tensors[k]) for k in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")}
         w = L.llmdec_q8_layer_weights(norms["attn_norm"].data_ptr(), *(up[k][1] for k in ("wq", "wk", "wv", "wo")),
                                       norms["mlp_norm"].data_ptr(), *(up[k][1] for k in ("w_gate", "w_up", "w_down")))
-        self.struct = L.llmdec_q8_pack_layer(cfg, w, self.buf.data_ptr(), nbytes, stream())
+        self.struct = pack(cfg, w, self.buf.data_ptr(), nbytes, stream())
         torch.cuda.current_stream().synchronize()
         del up, norms
 

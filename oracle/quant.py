@@ -9,6 +9,10 @@ unsigned codes and zero points and the groups running along each row (the input 
 [out][in] matrix).  A row whose length is not a multiple of the group size ends with one shorter
 group (the page gives 128 as an example size and says nothing of rows that do not divide); it has
 its own scale and zero point like any other.
+
+The page names int4 as well as int8 codes.  4-bit codes travel two to a byte, the even column in the
+low nibble and the odd column in the high nibble (the storage convention of the library's interface);
+unpack_nibbles turns such rows back into one code per column.
 """
 from __future__ import annotations
 
@@ -33,3 +37,14 @@ def dequantize(codes, scales, zeros, group: int = GROUP) -> np.ndarray:
 def linear_q8(x, codes, scales, zeros) -> np.ndarray:
     """y = x W^T with W the dequantized [out][in] matrix, in float64."""
     return np.asarray(x, dtype=np.float64) @ dequantize(codes, scales, zeros).T
+
+
+def unpack_nibbles(packed, cols: int) -> np.ndarray:
+    """packed [rows][cols/2] uint8, two 4-bit codes per byte (column 2j in the low nibble of byte j, 2j+1
+    in the high nibble) -> codes [rows][cols] uint8 in 0..15."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    rows = packed.shape[0]
+    out = np.empty((rows, cols), np.uint8)
+    out[:, 0::2] = packed[:, : (cols + 1) // 2] & 0x0F
+    out[:, 1::2] = packed[:, : cols // 2] >> 4
+    return out

@@ -173,6 +173,34 @@ def q8_matrix(workload: int, layer: int, idx: int, rows: int, cols: int):
     return codes, scales, zeros
 
 
+def q4_matrix(workload: int, layer: int, idx: int, rows: int, cols: int):
+    """4-bit codes: (codes uint8 [rows][cols/2], two per byte, column 2j in the low nibble of byte j;
+    scales bf16 bits [rows][g]; zeros uint8 [rows][g] in 7..8), g = ceil(cols / 128); scales sized so
+    that (code - zero) * scale spreads like N(0, 0.02^2) (codes uniform on 0..15 have a standard
+    deviation of about 4.6)."""
+    g = (cols + QGROUP - 1) // QGROUP
+    key = (workload, S_QUANT + 16 * layer + idx, 4)
+    c = rng(*key, 0).integers(0, 16, (rows, cols), dtype=np.uint8)
+    codes = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    scales = f32_to_bf16_bits(rng(*key, 1).uniform(0.75, 1.25, (rows, g)).astype(np.float32)
+                              * np.float32(WEIGHT_STD / 4.6))
+    zeros = rng(*key, 2).integers(7, 9, (rows, g), dtype=np.uint8)
+    return codes, scales, zeros
+
+
+def q_matrix(bits: int, workload: int, layer: int, idx: int, rows: int, cols: int):
+    return (q8_matrix if bits == 8 else q4_matrix)(workload, layer, idx, rows, cols)
+
+
+def q_layer_weights(bits: int, workload: int, layer: int, shape: ModelShape) -> dict:
+    """Quantized matrices of one layer by name (as q_matrix), plus the two norm gains (1.0)."""
+    t = {name: q_matrix(bits, workload, layer, idx, *shape.matrix_shapes()[name])
+         for idx, name in enumerate(LAYER_TENSORS)}
+    for name in NORMS:
+        t[name] = np.full(shape.hidden, BF16_ONE, dtype=np.uint16)
+    return t
+
+
 def q8_layer_weights(workload: int, layer: int, shape: ModelShape) -> dict:
     """Quantized matrices of one layer by name (as q8_matrix), plus the two norm gains (1.0)."""
     t = {name: q8_matrix(workload, layer, idx, *shape.matrix_shapes()[name]) for idx, name in enumerate(LAYER_TENSORS)}

@@ -33,9 +33,15 @@ def R():
     return runtime
 
 
-def dequantized(m):
+def dequantized(m, bits=8, cols=None):
     codes, scales, zeros = m
+    if bits == 4:
+        codes = oq.unpack_nibbles(codes, cols)
     return oq.dequantize(codes, od.widen_bf16(scales), zeros)
+
+
+def op_linear(L, bits):
+    return L.llmdec_op_linear_q8 if bits == 8 else L.llmdec_op_linear_q4
 
 
 # (rows, cols): several lanes' chunks and steps, a short last group (688 = 5 x 128 + 48), a ragged
@@ -43,59 +49,64 @@ def dequantized(m):
 SHAPES = [(16, 256), (64, 688), (12, 1040), (8, 14336), (4096, 4096), (4096, 11008), (12288, 4096)]
 
 
+@pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("rows,cols", SHAPES)
-def test_linear_q8(L, R, rows, cols):
-    banner(f"op_linear_q8 {rows}x{cols}")
-    m = synth.q8_matrix(60, 0, cols % 7, rows, cols)
-    w = R.Q8Matrix(m)
+def test_linear_q8(L, R, rows, cols, bits):
+    banner(f"op_linear_q{bits} {rows}x{cols}")
+    m = synth.q_matrix(bits, 60, 0, cols % 7, rows, cols)
+    w = R.Q8Matrix(m, bits, cols)
     x = synth.rng(61, rows, cols).standard_normal(cols).astype(np.float32)
     base = synth.rng(62, rows, cols).standard_normal(rows).astype(np.float32)
     xd = R.dev_f32(x)
     out = R.dev_f32(np.full(rows, np.nan, np.float32))
     acc = R.dev_f32(base)
-    L.llmdec_op_linear_q8(xd.data_ptr(), cols, w.ptr, rows, out.data_ptr(), 0, R.stream())
-    L.llmdec_op_linear_q8(xd.data_ptr(), cols, w.ptr, rows, acc.data_ptr(), 1, R.stream())
+    op_linear(L, bits)(xd.data_ptr(), cols, w.ptr, rows, out.data_ptr(), 0, R.stream())
+    op_linear(L, bits)(xd.data_ptr(), cols, w.ptr, rows, acc.data_ptr(), 1, R.stream())
     torch.cuda.synchronize()
-    ref = oq.linear_q8(x[None, :], m[0], od.widen_bf16(m[1]), m[2])[0]
+    codes = m[0] if bits == 8 else oq.unpack_nibbles(m[0], cols)
+    ref = oq.linear_q8(x[None, :], codes, od.widen_bf16(m[1]), m[2])[0]
     got = out.cpu().numpy()
-    assert_close(f"q8 {rows}x{cols} store", got, ref)
-    assert_close(f"q8 {rows}x{cols} store (fp32 level)", got, ref, max_abs=1e-4, rel_l2=1e-5)
-    assert_close(f"q8 {rows}x{cols} accumulate", acc.cpu().numpy(), base.astype(np.float64) + ref,
+    assert_close(f"q{bits} {rows}x{cols} store", got, ref)
+    assert_close(f"q{bits} {rows}x{cols} store (fp32 level)", got, ref, max_abs=1e-4, rel_l2=1e-5)
+    assert_close(f"q{bits} {rows}x{cols} accumulate", acc.cpu().numpy(), base.astype(np.float64) + ref,
                  max_abs=1e-4, rel_l2=1e-5)
 
 
-def test_linear_q8_group_isolation(L, R):
+@pytest.mark.parametrize("bits", [8, 4])
+def test_linear_q8_group_isolation(L, R, bits):
     """A one-hot activation picks out one column: out[r] = (code - zero) * scale of that column's group,
     for a column in every group position of a row with a short last group."""
     rows, cols = 8, 688
-    m = synth.q8_matrix(63, 0, 0, rows, cols)
-    w = R.Q8Matrix(m)
-    W = dequantized(m)
+    m = synth.q_matrix(bits, 63, 0, 0, rows, cols)
+    w = R.Q8Matrix(m, bits, cols)
+    W = dequantized(m, bits, cols)
     out = R.dev_f32(np.zeros(rows, np.float32))
     for c in (0, 15, 16, 127, 128, 511, 640, 687):
         x = np.zeros(cols, np.float32)
         x[c] = 1.0
         xd = R.dev_f32(x)
-        L.llmdec_op_linear_q8(xd.data_ptr(), cols, w.ptr, rows, out.data_ptr(), 0, R.stream())
+        op_linear(L, bits)(xd.data_ptr(), cols, w.ptr, rows, out.data_ptr(), 0, R.stream())
         torch.cuda.synchronize()
         got = out.cpu().numpy().astype(np.float64)
         assert np.array_equal(got, W[:, c].astype(np.float32).astype(np.float64)), f"column {c}"
 
 
-def run_decode_q8(L, R, shape, workload, ctx, tag):
-    banner(f"{tag}: layer_decode_q8 ctx={ctx}")
+def run_decode_q8(L, R, shape, workload, ctx, tag, bits=8):
+    banner(f"{tag}: layer_decode_q{bits} ctx={ctx}")
     case = LayerCase(L, R, shape, workload, [ctx], [1], pack=False)
-    qw = synth.q8_layer_weights(workload, 0, shape)
-    layer = R.Q8Layer(case.cfg, qw)
+    qw = synth.q_layer_weights(bits, workload, 0, shape)
+    layer = R.Q8Layer(case.cfg, qw, bits)
     x_in = synth.hidden_input(workload, 1, shape.hidden)
     ws = case.workspace(1)
     xd = R.dev_f32(x_in)
     ctx_d = R.dev_i32([ctx])
-    L.llmdec_layer_decode_q8(case.cfg, layer.struct, 0, xd.data_ptr(), 1, ctx_d.data_ptr(), case.bt_dev.data_ptr(),
-                             case.max_pages, case.pool.handle, ws.ptr, ws.nbytes, R.stream())
+    decode = L.llmdec_layer_decode_q8 if bits == 8 else L.llmdec_layer_decode_q4
+    decode(case.cfg, layer.struct, 0, xd.data_ptr(), 1, ctx_d.data_ptr(), case.bt_dev.data_ptr(),
+           case.max_pages, case.pool.handle, ws.ptr, ws.nbytes, R.stream())
     torch.cuda.synchronize()
     assert ws.error_bits() == 0
-    dense = {k: dequantized(v) for k, v in qw.items() if k not in ("attn_norm", "mlp_norm")}
+    shapes = shape.matrix_shapes()
+    dense = {k: dequantized(v, bits, shapes[k][1]) for k, v in qw.items() if k not in ("attn_norm", "mlp_norm")}
     dense.update(attn_norm=qw["attn_norm"], mlp_norm=qw["mlp_norm"])
     ref = od.layer_step(shape, dense, 0, x_in, [0], [ctx], case.kv)
     assert_close(f"{tag} layer output", xd.cpu().numpy(), ref)
@@ -112,6 +123,18 @@ def test_decode_q8_tiny_gqa_page_start(L, R):
 
 def test_decode_q8_7b_layer_ctx2048(L, R):
     run_decode_q8(L, R, synth.LLAMA7B_LAYER, 66, 2048, "7B q8 decode b1 ctx2048")
+
+
+def test_decode_q4_tiny(L, R):
+    run_decode_q8(L, R, TINY1, 68, 37, "tiny q4 decode", bits=4)
+
+
+def test_decode_q4_tiny_gqa_page_start(L, R):
+    run_decode_q8(L, R, TINY1_GQA, 69, 32, "tiny GQA q4 decode", bits=4)
+
+
+def test_decode_q4_7b_layer_ctx2048(L, R):
+    run_decode_q8(L, R, synth.LLAMA7B_LAYER, 70, 2048, "7B q4 decode b1 ctx2048", bits=4)
 
 
 def test_decode_q8_rejects_batches(L, R):

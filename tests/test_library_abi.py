@@ -184,3 +184,18 @@ def test_q8_sizes_and_validation_before_launch(L):
         assert e.value.status == L.LLMDEC_E_WORKSPACE
     finally:
         L.llmdec_kv_pool_destroy(h)
+
+
+def test_q4_sizes_and_validation(L):
+    """4-bit codes: each row's cols/2 code bytes padded to a multiple of 16, then 256 bytes of metadata words
+    per four 2048-column steps; the same shape limits as the 8-bit matrices."""
+    assert L.llmdec_q4_matrix_bytes(4096, 4096) == 4096 * 2048 + 4096 * 256
+    assert L.llmdec_q4_matrix_bytes(4096, 11008) == 4096 * 5504 + 4096 * 2 * 256
+    assert L.llmdec_q4_matrix_bytes(64, 688) == 64 * 352 + 64 * 256
+    assert L.llmdec_q4_matrix_bytes(6, 256) == 0 and L.llmdec_q4_matrix_bytes(8, 264) == 0
+    assert L.llmdec_q4_matrix_bytes(8, 14336) > 0 and L.llmdec_q4_matrix_bytes(8, 14352) == 0
+    assert 0 < L.llmdec_q4_packed_layer_bytes(tiny_cfg(L)) < L.llmdec_q8_packed_layer_bytes(tiny_cfg(L))
+    src = L.llmdec_q4_matrix(1 << 20, 1 << 21, 1 << 22)
+    with pytest.raises(L.LlmdecError) as e:
+        L.llmdec_q4_pack_matrix(8, 256, src, 1 << 23, 100)
+    assert e.value.status == L.LLMDEC_E_INVALID and "q4_pack_matrix" in str(e.value)

@@ -539,3 +539,23 @@ def test_sample_truncation_sets():
             if p[sel].sum() >= top_p and (best is None or (len(sel), -p[sel].sum()) < (len(best), -p[best].sum())):
                 best = sel
         assert sorted(ids.tolist()) == sorted(best)
+
+
+def test_unpack_nibbles_worked_example():
+    """Two 4-bit codes per byte, column 2j in the low nibble of byte j: bytes 0x21, 0xF0, 0x3C are columns
+    1, 2, 0, 15, 12, 3 (worked by hand); an odd column count takes the last byte's low nibble only."""
+    from oracle import quant as oq
+    assert oq.unpack_nibbles(np.array([[0x21, 0xF0, 0x3C]], np.uint8), 6).tolist() == [[1, 2, 0, 15, 12, 3]]
+    assert oq.unpack_nibbles(np.array([[0x21, 0xF0, 0x3C]], np.uint8), 5).tolist() == [[1, 2, 0, 15, 12]]
+
+
+def test_synthetic_4bit_codes_follow_the_storage_convention():
+    """The seeded 4-bit generator packs what the oracle unpacks: re-packing the oracle's columns by the
+    stated convention gives back the generator's bytes, and the codes span 0..15."""
+    import synth
+    from oracle import quant as oq
+    codes, scales, zeros = synth.q4_matrix(5, 0, 0, 8, 256)
+    c = oq.unpack_nibbles(codes, 256)
+    assert c.min() == 0 and c.max() == 15 and scales.shape == (8, 2) and zeros.shape == (8, 2)
+    repacked = np.array([[int(c[r, 2 * j]) + 16 * int(c[r, 2 * j + 1]) for j in range(128)] for r in range(8)])
+    assert np.array_equal(repacked, codes)

@@ -180,10 +180,14 @@ static void run_layer_one_row(const LayerArgs &a) {
   float *y = at<float>(a.ws, L.act_h), *u = at<float>(a.ws, L.act_i), *qkv = at<float>(a.ws, L.qkv);
   uint16_t *pk, *pv;
   pool_layer(a.pool, a.layer, &pk, &pv);
-  launch_gemv(a.hidden, (const uint16_t *)a.w->attn_norm, c.rms_eps, (const uint16_t *)a.w->w_qkv, nqkv, h, kStore,
-              qkv, a.s);
-  launch_rope_append(c, qkv, nullptr, Splits{}, nqkv, 1, 1, nullptr, a.ctx, a.bt, a.max_pages, pk, pv,
-                     a.pool->num_pages, err, a.s);
+  // q|k|v with the attention RMSNorm before it and RoPE + the paged K/V append after it, in one launch
+  RopeAppend ra;
+  ra.fr = rope_freq(c);
+  ra.pos = a.ctx, ra.block_row = a.bt, ra.max_pages = a.max_pages, ra.num_pages = a.pool->num_pages;
+  ra.n_heads = c.n_heads, ra.n_kv_heads = c.n_kv_heads, ra.head_dim = c.head_dim;
+  ra.pool_k = pk, ra.pool_v = pv, ra.err = err;
+  launch_gemv_qkv_rope(a.hidden, (const uint16_t *)a.w->attn_norm, c.rms_eps, (const uint16_t *)a.w->w_qkv, nqkv, h,
+                       qkv, ra, a.s);
   launch_decode_attention(c, qkv, nqkv, 1, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages,
                           at<float>(a.ws, L.attn_part), y, nullptr, nullptr, 0, err, a.s);
   launch_gemv(y, nullptr, 0.f, (const uint16_t *)a.w->w_o, h, h, kAccumulate, a.hidden, a.s);

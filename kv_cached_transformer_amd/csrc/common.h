@@ -151,6 +151,16 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
+// Rotation of pair i at position pos ("为什么要自己动手写一个LLM推理引擎" §4.3 rotates q and k by position):
+// the angle pos * inv_freq (inv_freq = theta^(-2i/D), computed in double on the host) is formed and
+// reduced to [-pi, pi] in double, then its cosine and sine taken in fp32, so positions in the
+// thousands lose no accuracy.
+__device__ inline void rope_cos_sin(int pos, double inv_freq, float &c, float &s) {
+  const double ang = (double)pos * inv_freq;
+  const double red = fma(-6.283185307179586, rint(ang * 0.15915494309189535), ang);
+  sincosf((float)red, &s, &c);
+}
+
 __device__ inline void raise_error(uint32_t *err, uint32_t bits) {
   if (err) atomicOr(err, bits);
 }

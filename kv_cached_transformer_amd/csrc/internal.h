@@ -139,6 +139,25 @@ void launch_gather_kv(const uint16_t *pool_layer_k, const uint16_t *pool_layer_v
                       hipStream_t s);
 void launch_fill_u32(uint32_t *p, uint32_t value, size_t n, hipStream_t s);
 
+// Rotary frequencies inv_freq[i] = theta^(-2i/D), i < D/2 (zero past), computed in double on the host.
+struct RopeFreq {
+  double inv_freq[64];
+};
+RopeFreq rope_freq(const llmdec_config &cfg);
+
+// Where the one-row q|k|v product sends its result when it also applies RoPE and the paged append (a
+// single decode token of sequence 0 at position *pos): rotated q to its output, rotated bf16 k and bf16
+// v to the pool slot block_row[pos/16], offset pos%16, as the RoPE/append kernel stores them; a bad
+// position or page sets err and skips the K/V stores, as that kernel does.
+struct RopeAppend {
+  RopeFreq fr;
+  const int32_t *pos;
+  const int32_t *block_row;
+  int max_pages, num_pages, n_heads, n_kv_heads, head_dim;
+  uint16_t *pool_k, *pool_v;
+  uint32_t *err;
+};
+
 // One-row products with a packed bf16 matrix (kernels_gemv.hip): x fp32 [k], n a multiple of 16 (of 32
 // for kSiluMul, whose matrix is the fused gate/up one: 16-row blocks alternating gate and up, out[j] =
 // silu(gate_j) * up_j for j < n / 2).  kStore / kAccumulate write or add out[0..n).  gamma != NULL: the
@@ -146,6 +165,9 @@ void launch_fill_u32(uint32_t *p, uint32_t value, size_t n, hipStream_t s);
 bool gemv_shape_ok(int k);
 void launch_gemv(const float *x, const uint16_t *gamma, float eps, const uint16_t *w_packed, int n, int k, int mode,
                  float *out, hipStream_t s);
+// The q|k|v product of a single decode token with RoPE and the paged K/V append in its epilogue.
+void launch_gemv_qkv_rope(const float *x, const uint16_t *gamma, float eps, const uint16_t *w_packed, int n, int k,
+                          float *qkv, const RopeAppend &ra, hipStream_t s);
 
 // Temperature / top-k / top-p sampling of fp32 logits [rows][vocab] (kernels_sample.hip); vocab <= 32768.
 bool sample_shape_ok(int vocab);

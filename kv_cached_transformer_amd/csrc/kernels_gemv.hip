@@ -21,6 +21,7 @@ namespace llmdec {
 
 constexpr int kGvWaves = 8;         // waves per block, splitting the k-tiles
 constexpr int kGvMaxK = 14336;      // x (fp32) in LDS
+constexpr int kGvRope = 3;          // epilogue: RoPE and the paged K/V append of a q|k|v product
 
 struct GemvArgs {
   const float *x;         // [k] fp32
@@ -29,6 +30,7 @@ struct GemvArgs {
   const uint16_t *w;      // packed matrix, n_blocks 16-row blocks of kt k-tiles
   int k, kt, n_blocks;
   float *out;
+  RopeAppend ra;          // kGvRope only
 };
 
 __device__ inline float gv_silu(float g) { return g / (1.0f + expf(-g)); }
@@ -73,6 +75,33 @@ __global__ __launch_bounds__(kGvWaves * 64, 6) void gemv_kernel(GemvArgs a) {
   for (int d = 0; d < D; ++d) {
     issue(d, d);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  // RoPE epilogue: the position, its page and the rotation depend only on the inputs, so the threads
+  // that apply it (0..15) look them up now, while the weights stream
+  int rp_page = -1, rp_off = 0;
+  float rp_c = 1.f, rp_s = 0.f;
+  if (MODE == kGvRope && threadIdx.x < 16) {
+    const RopeAppend &ra = a.ra;
+    const int n = nb0 * 16 + threadIdx.x, D = ra.head_dim;
+    const int hidden = ra.n_heads * D, kvc = ra.n_kv_heads * D;
+    const int pos = ra.pos[0];
+    if (n < hidden + kvc) {
+      const int dd = n < hidden ? n : n - hidden;
+      rope_cos_sin(pos, ra.fr.inv_freq[(dd % D) >> 1], rp_c, rp_s);
+    }
+    if (n >= hidden) {
+      const int blk = pos >> 4;
+      rp_off = pos & 15;
+      if (pos < 0 || blk >= ra.max_pages) {
+        if (threadIdx.x == 0) raise_error(ra.err, kErrPos);
+      } else {
+        rp_page = ra.block_row[blk];
+        if (rp_page < 0 || rp_page >= ra.num_pages) {
+          if (threadIdx.x == 0) raise_error(ra.err, kErrPage);
+          rp_page = -1;
+        }
+      }
+    }
   }
 
   // stage x (or x * gamma, scaled by the norm's factor below): thread i takes columns 8i..8i+7
@@ -161,11 +190,47 @@ __global__ __launch_bounds__(kGvWaves * 64, 6) void gemv_kernel(GemvArgs a) {
     }
     if (MODE == kSiluMul) {  // row block 0 holds the gate rows, row block 1 the matching up rows
       a.out[blockIdx.x * 16 + r] = gv_silu(v[0]) * v[TB - 1];
+    } else if (MODE == kGvRope) {
+      // column n of q|k|v; a rotation pair (2i, 2i+1) is two adjacent threads of this wave
+      const RopeAppend &ra = a.ra;
+      const int n = nb0 * 16 + r, D = ra.head_dim;
+      const int hidden = ra.n_heads * D, kvc = ra.n_kv_heads * D;
+      const float partner = __shfl_xor(v[0], 1, 64);
+      const float xe = (r & 1) ? partner : v[0], xo = (r & 1) ? v[0] : partner;
+      const int d = n < hidden ? n : (n < hidden + kvc ? n - hidden : n - hidden - kvc);
+      const int h = d / D, i = (d % D) >> 1;
+      const float c = rp_c, sn = rp_s;
+      const float re = xe * c - xo * sn, ro = xe * sn + xo * c;  // the rotated pair
+      if (n < hidden) {
+        a.out[n] = (r & 1) ? ro : re;
+      } else {
+        const int page = rp_page, off = rp_off;
+        if (page >= 0) {
+          const size_t head = (size_t)page * ra.n_kv_heads + h;
+          if (n < hidden + kvc) {
+            if (!(r & 1))  // K [h][o][d]: the pair as one 32-bit store
+              *reinterpret_cast<uint32_t *>(ra.pool_k + (head * 16 + off) * D + 2 * i) =
+                  f32_to_bf16(re) | ((uint32_t)f32_to_bf16(ro) << 16);
+          } else {  // V [h][o/4][d][o%4]
+            ra.pool_v[(head * 4 + (off >> 2)) * D * 4 + (size_t)(d % D) * 4 + (off & 3)] = f32_to_bf16(v[0]);
+          }
+        }
+      }
     } else {
       float *o = a.out + (size_t)nb0 * 16 + r;
       *o = MODE == kAccumulate ? *o + v[0] : v[0];
     }
   }
+}
+
+void launch_gemv_qkv_rope(const float *x, const uint16_t *gamma, float eps, const uint16_t *w_packed, int n, int k,
+                          float *qkv, const RopeAppend &ra, hipStream_t s) {
+  GemvArgs a;
+  a.x = x, a.gamma = gamma, a.eps = eps, a.w = w_packed, a.out = qkv, a.ra = ra;
+  a.k = k, a.kt = (k + 31) / 32, a.n_blocks = n / 16;
+  if (a.n_blocks <= 0) return;
+  const size_t lds = ((size_t)a.kt * 32 + kGvWaves * 16 + kGvWaves) * sizeof(float);
+  gemv_kernel<kGvRope, 1><<<a.n_blocks, kGvWaves * 64, lds, s>>>(a);
 }
 
 bool gemv_shape_ok(int k) { return k > 0 && k % 16 == 0 && k <= kGvMaxK; }

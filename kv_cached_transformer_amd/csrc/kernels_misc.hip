@@ -205,10 +205,6 @@ void launch_token_map(const int32_t *cu, const int32_t *start, int n_seqs, int n
 // in fp32, so positions in the thousands lose no accuracy.  q is rotated in
 // place; rotated k and plain v are rounded to bf16 and written to the page
 // slot bt[seq][pos/16], offset pos%16 (K as [h][o][d], V as [h][o/4][d][o%4]).
-struct RopeFreq {
-  double inv_freq[64];
-};
-
 __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qkv, const float *__restrict__ part,
                                                           Splits sp, int ld_qkv, int n_tokens, int n_heads,
                                                           int n_kv_heads, int head_dim, RopeFreq fr, int n_seqs,
@@ -226,12 +222,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
   const int pos = tok_pos[t];
   if ((int)threadIdx.x < half) {
     const int i = threadIdx.x;
-    const double ang = (double)pos * fr.inv_freq[i];
-    const double red = fma(-6.283185307179586, rint(ang * 0.15915494309189535), ang);
-    float sf, cf;
-    sincosf((float)red, &sf, &cf);
-    cs[i] = cf;
-    sn[i] = sf;
+    rope_cos_sin(pos, fr.inv_freq[i], cs[i], sn[i]);
   }
   __syncthreads();
   int page = -1;
@@ -275,14 +266,19 @@ __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qk
   }
 }
 
+RopeFreq rope_freq(const llmdec_config &cfg) {
+  RopeFreq fr;
+  for (int i = 0; i < 64; ++i)
+    fr.inv_freq[i] = i < cfg.head_dim / 2 ? pow((double)cfg.rope_theta, -2.0 * i / (double)cfg.head_dim) : 0.0;
+  return fr;
+}
+
 void launch_rope_append(const llmdec_config &cfg, float *qkv, const float *qkv_partials, const Splits &sp, int ld_qkv,
                         int n_tokens, int n_seqs, const int32_t *tok_seq, const int32_t *tok_pos,
                         const int32_t *block_tables, int max_pages, uint16_t *pool_k, uint16_t *pool_v, int num_pages,
                         uint32_t *err, hipStream_t s) {
   if (n_tokens <= 0) return;
-  RopeFreq fr;
-  for (int i = 0; i < 64; ++i)
-    fr.inv_freq[i] = i < cfg.head_dim / 2 ? pow((double)cfg.rope_theta, -2.0 * i / (double)cfg.head_dim) : 0.0;
+  const RopeFreq fr = rope_freq(cfg);
   dim3 grid(n_tokens, (cfg.n_heads * (cfg.head_dim / 2) + 255) / 256);
   rope_append_kernel<<<grid, 256, 0, s>>>(qkv, qkv_partials, sp, ld_qkv, n_tokens, cfg.n_heads, cfg.n_kv_heads,
                                               cfg.head_dim, fr, n_seqs, tok_seq, tok_pos, block_tables, max_pages,

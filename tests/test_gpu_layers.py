@@ -149,3 +149,26 @@ def test_gqa_7b_sized_layer_decode_batch8(L, R):
 def test_gqa_7b_sized_layer_prefill(L, R):
     lens = [256, 100]
     run_prefill(L, R, GQA7B_LAYER, 98, [0, 37], lens, synth.hidden_input(98, sum(lens), 4096), "GQA 32/8 prefill")
+
+
+# ----------------------------------------------------------------------------- device-side argument errors
+@pytest.mark.parametrize("n", [1, 2])
+def test_decode_bad_page_and_position_set_error_bits(L, R, n):
+    """A block-table entry naming a page that does not exist, and a position past the block-table row, are
+    caught on the device: the sticky error bits say which, and no K/V slot is written.  n = 1 runs the
+    one-row q|k|v product with RoPE and the append in its epilogue, n = 2 the RoPE/append kernel."""
+    banner(f"decode with a bad page / position, {n} sequence(s)")
+    ctxs = [37] * n
+    case = LayerCase(L, R, TINY1, 99, ctxs, [1] * n, build_oracle=False)
+    x_in = synth.hidden_input(99, n, 256)
+    bad = case.bt.copy()
+    bad[:, 37 // 16] = case.num_pages + 3          # the new token's page (block 2) does not exist
+    for bt, ctx, bit in [(bad, ctxs, L.ERR_PAGE), (case.bt, [case.max_pages * 16] * n, L.ERR_POS)]:
+        ws = case.workspace(n)
+        xd, bt_d, ctx_d = R.dev_f32(x_in), R.dev_i32(bt), R.dev_i32(ctx)
+        L.llmdec_layer_decode(case.cfg, case.packed.struct, 0, xd.data_ptr(), n, ctx_d.data_ptr(), bt_d.data_ptr(),
+                              case.max_pages, case.pool.handle, ws.ptr, ws.nbytes, R.stream())
+        torch.cuda.synchronize()
+        assert ws.error_bits() & bit, f"error bit {bit} not set (bits {ws.error_bits()})"
+        kimg, vimg = case.pool_images()
+        assert np.array_equal(kimg, case.kimg0) and np.array_equal(vimg, case.vimg0), "a K/V slot was written"

@@ -16,8 +16,9 @@ cached tokens (weights and cache rotated over 4 copies so the 256 MB
 last-level cache does not serve them), decode over 32 sequences with contexts
 uniform in [128, 4096], a 4 x 512 prefill, and the batch-1 decode again with
 group-quantized matrices (8-bit and 4-bit codes, a bf16 scale and a zero point
-per 128 inputs), with its four weight products also timed alone, and on-device
-sampling of 64 x 32000 logits.  Each gets its
+per 128 inputs), with its four weight products also timed alone, on-device
+sampling of 64 x 32000 logits, and the tiny model's decode step enqueued per
+step against the same step replayed from a HIP graph.  Each gets its
 algorithmic bytes or FLOPs per step and the fraction of the MI355X peak.
 
 Inputs are seeded and synthetic: weights N(0, 0.02^2) in bf16 drawn on the
@@ -25,7 +26,7 @@ device, RMSNorm gains 1, cached K/V N(0, 1) in bf16.  Timing uses HIP events
 on the stream the library launches on.  The cpu_baseline leg times the CPU
 oracle (float64 NumPy) on a bounded sample of the same decode workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only c5,c2,q8,q4,sample,c3,c4]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only c5,c2,q8,q4,sample,c1,c3,c4]
 
 Profiling helpers (no GPU needed for the two summaries):
   python bench.py --only copy                  1 GiB device copies: calibrates the HBM counters
@@ -358,6 +359,57 @@ def bench_sample(torch, L, R, iters):
     return dict(workload="sample-64x32000", **res)
 
 
+def bench_tiny_graph(torch, L, R, steps):
+    """The tiny 2-layer model (C1's shape): greedy decode steps of one sequence after a 32-token prompt,
+    each step enqueued from the host, against the same step captured once in a HIP graph and replayed
+    (the chosen token and the next position fed back on the device).  Steps this small are bound by
+    launch latency, which the graph removes from the host side."""
+    import numpy as np
+    import synth
+    shape = synth.TINY
+    d = Dev(torch, L, R, shape, SEED + 1)
+    cfg = d.cfg
+    layers = [d.packed_layer() for _ in range(shape.n_layers)]
+    embed = d.normal_bf16(shape.vocab, shape.hidden, 0.02)
+    fnorm = torch.ones(shape.hidden, device="cuda", dtype=torch.bfloat16)
+    head = d.packed_matrix(shape.vocab, shape.hidden)
+    mw, keep = L.make_model_weights(embed.data_ptr(), [st for _, st in layers], fnorm.data_ptr(), head.data_ptr())
+    prompt, total = 32, 32 + 2 * steps + 8
+    max_pages = (total + 15) // 16
+    strm = R.stream()
+
+    def run():
+        pool = R.Pool(cfg, max_pages, synth.free_order(1, max_pages))
+        row = np.full((1, max_pages), -1, np.int32)
+        pool.alloc(total, row[0], 0, max_pages)
+        bt = R.dev_i32(row)
+        ws = R.Workspace(L.llmdec_workspace_bytes(cfg, prompt, 1, max_pages))
+        nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+        toks, cu, sp = R.dev_i32(np.arange(prompt) % shape.vocab), R.dev_i32([0, prompt]), R.dev_i32([0])
+        L.llmdec_model_step_greedy(cfg, mw, 1, prompt, prompt, toks.data_ptr(), cu.data_ptr(), sp.data_ptr(),
+                                   bt.data_ptr(), max_pages, pool.handle, nxt.data_ptr(), None, ws.ptr, ws.nbytes, strm)
+        tok, pos = nxt.clone(), torch.tensor([prompt], dtype=torch.int32, device="cuda")
+
+        def step():
+            L.llmdec_model_step_greedy(cfg, mw, 1, 1, 1, tok.data_ptr(), None, pos.data_ptr(), bt.data_ptr(),
+                                       max_pages, pool.handle, nxt.data_ptr(), None, ws.ptr, ws.nbytes, strm)
+            tok.copy_(nxt)
+            pos.add_(1)
+        return step, (pool, ws, bt, nxt, toks, cu, sp, tok, pos)
+
+    step, hold = run()
+    ms_eager = time_loop(torch, lambda i: step(), steps, 4)
+    step2, hold2 = run()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step2()
+    ms_graph = time_loop(torch, lambda i: g.replay(), steps, 4)
+    log(f"tiny 2-layer decode: {ms_eager * 1e3:.1f} us per step enqueued, {ms_graph * 1e3:.1f} us replayed from a graph")
+    del hold, hold2, keep, layers
+    return dict(workload="tiny-2L-h256-decode-b1", us_per_step_eager=ms_eager * 1e3, us_per_step_graph=ms_graph * 1e3,
+                tokens_per_s_eager=1e3 / ms_eager, tokens_per_s_graph=1e3 / ms_graph)
+
+
 def bench_layer_prefill(torch, L, R, iters):
     import numpy as np
     import synth
@@ -547,7 +599,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="c5,c2,q8,q4,sample,c3,c4", help="comma list of workloads to run (also: copy)")
+    ap.add_argument("--only", default="c5,c2,q8,q4,sample,c1,c3,c4", help="comma list of workloads to run (also: copy)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the attention traffic summary from two rocprofv3 --pmc output folders")
     ap.add_argument("--trace-summary", metavar="DIR", help="print a per-kernel table from a rocprofv3 kernel trace")
@@ -586,6 +638,8 @@ def main():
         extra["decode_q8_b1_ctx2048"] = bench_layer_decode_q(torch, L, R, 2048, 4, 100, 8)
     if "q4" in only:
         extra["decode_q4_b1_ctx2048"] = bench_layer_decode_q(torch, L, R, 2048, 4, 100, 4)
+    if "c1" in only:
+        extra["tiny_decode_graph"] = bench_tiny_graph(torch, L, R, 20)
     if "sample" in only:
         extra["sample_64x32000"] = bench_sample(torch, L, R, 50)
     if "c3" in only:

@@ -57,16 +57,17 @@ void launch_embed(const uint16_t *embed, const int32_t *tokens, int n_tokens, in
 }
 
 // ---------------------------------------------------------------- RMSNorm ([E] §4.2)
-// y = x * (mean(x^2) + eps)^(-1/2) * gamma, eps inside the root.  One block
-// per row; each thread owns runs of 8 consecutive columns (up to four runs:
-// n <= 8192), kept in registers between the two passes, and each run is one
-// 16-byte chunk of the packed hi/lo output.  Columns n..kpad-1 of the packed
+// y = x * (mean(x^2) + eps)^(-1/2) * gamma, eps inside the root.  One block of
+// 512 threads per row; each thread owns runs of 8 consecutive columns (up to
+// two runs: n <= 8192), kept in registers between the two passes, and each run
+// is one 16-byte chunk of the packed hi/lo output.  Columns n..kpad-1 of the packed
 // output are zeroed.  With add_partials, the ks partial sums of a split-k
 // residual product are first added into x (and x written back): the residual
 // add of the output projection fused into the norm that follows it.
-constexpr int kNormRuns = 4;
+constexpr int kNormThreads = 512;
+constexpr int kNormRuns = 2;
 
-__global__ __launch_bounds__(256) void rmsnorm_kernel(float *__restrict__ x, int ld_x,
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(float *__restrict__ x, int ld_x,
                                                       const int32_t *__restrict__ cu_last, int n_src_rows,
                                                       const uint16_t *__restrict__ gamma, int n, float eps,
                                                       uint32_t *err, float *out_f32, uint16_t *out_hi,
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float *__restrict__ x, int
   float ss = 0.f;
 #pragma unroll
   for (int it = 0; it < kNormRuns; ++it) {
-    const int c0 = threadIdx.x * 8 + it * 2048;
+    const int c0 = threadIdx.x * 8 + it * kNormThreads * 8;
     if (c0 < n) {
       const float4 v0 = *reinterpret_cast<const float4 *>(xr + c0);
       const float4 v1 = *reinterpret_cast<const float4 *>(xr + c0 + 4);
@@ -104,16 +105,18 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float *__restrict__ x, int
       }
     }
   }
-  __shared__ float red[4];
+  __shared__ float red[kNormThreads / 64];
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float total = (red[0] + red[1]) + (red[2] + red[3]);
+  float total = 0.f;
+#pragma unroll
+  for (int w = 0; w < kNormThreads / 64; ++w) total += red[w];
   const float inv = 1.0f / sqrtf(total / (float)n + eps);
   const int kt = kpad >> 5;
 #pragma unroll
   for (int it = 0; it < kNormRuns; ++it) {
-    const int c0 = threadIdx.x * 8 + it * 2048;
+    const int c0 = threadIdx.x * 8 + it * kNormThreads * 8;
     if (c0 >= (out_hi ? kpad : n)) continue;
     float y[8];
     if (c0 < n) {
@@ -147,7 +150,7 @@ void launch_rmsnorm(float *x, int ld_x, const int32_t *cu_last, int n_src_rows, 
                     float eps, uint32_t *err, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad,
                     const float *add_partials, const Splits &sp, hipStream_t s) {
   if (rows > 0)
-    rmsnorm_kernel<<<rows, 256, 0, s>>>(x, ld_x, cu_last, n_src_rows, gamma, n, eps, err, out_f32, out_hi, out_lo,
+    rmsnorm_kernel<<<rows, kNormThreads, 0, s>>>(x, ld_x, cu_last, n_src_rows, gamma, n, eps, err, out_f32, out_hi, out_lo,
                                         kpad, add_partials, sp, rows);
 }
 

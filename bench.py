@@ -162,6 +162,29 @@ def time_loop(torch, fn, iters, warmup):
     return e0.elapsed_time(e1) / iters
 
 
+def time_dist(torch, fn, iters, warmup):
+    """Per-call times of fn(i) over iters calls after warmup calls: an event before every call and one after
+    the last, on the current stream.  Returns (mean, p10, median, p90) in ms."""
+    import numpy as np
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    ev[0].record()
+    for i in range(iters):
+        fn(warmup + i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)])
+    return float(ev[0].elapsed_time(ev[-1]) / iters), float(np.percentile(t, 10)), float(np.median(t)), \
+        float(np.percentile(t, 90))
+
+
+def dist_fields(d):
+    """The p10 / median / p90 of a time_dist result as sub-benchmark fields (ms)."""
+    return {"ms_p10": d[1], "ms_median": d[2], "ms_p90": d[3]}
+
+
 def attn_alg_bytes(steps, warmup):
     """Algorithmic bytes of one standalone attention call on the decode cache after warmup + steps
     steps: every cached K and V element once (bf16), q read and the output written (fp32)."""
@@ -264,13 +287,15 @@ def bench_layer_decode(torch, L, R, ctxs, copies, iters, tag, workload):
         L.llmdec_layer_decode(d.cfg, layers[c][1], 0, x.data_ptr(), B, ctx_d.data_ptr(), bts[c].data_ptr(),
                               max_pages, pool.handle, ws.ptr, ws.nbytes, strm)
 
-    ms = time_loop(torch, step, iters, 2 * copies)
+    dist = time_dist(torch, step, iters, max(10, 2 * copies))
+    ms = dist[0]
     assert ws.error_bits() == 0
     kv = float(np.sum(ctxs + 1)) * 2 * shape.hidden * 2
     byt = layer_bytes(shape) + kv + 2 * B * shape.hidden * 4
-    log(f"{tag}: {ms * 1e3:.1f} us per layer-step, {byt / (ms * 1e-3) / 1e9:.0f} GB/s")
-    return dict(workload=tag, ms_per_layer_step=ms, layer_steps_per_s=1e3 / ms, tokens_per_s=B * 1e3 / ms,
-                algorithmic_bytes=byt, hbm_frac=byt / (ms * 1e-3) / HBM_PEAK)
+    log(f"{tag}: {ms * 1e3:.1f} us per layer-step (median {dist[2] * 1e3:.1f}, p10 {dist[1] * 1e3:.1f}, "
+        f"p90 {dist[3] * 1e3:.1f}), {byt / (ms * 1e-3) / 1e9:.0f} GB/s")
+    return dict(workload=tag, ms_per_layer_step=ms, **dist_fields(dist), layer_steps_per_s=1e3 / ms,
+                tokens_per_s=B * 1e3 / ms, algorithmic_bytes=byt, hbm_frac=byt / (ms * 1e-3) / HBM_PEAK)
 
 
 def q_matrix_bytes(rows, cols, bits):
@@ -309,7 +334,8 @@ def bench_layer_decode_q(torch, L, R, ctx, copies, iters, bits):
         decode(d.cfg, layers[c][1], 0, x.data_ptr(), 1, ctx_d.data_ptr(), bts[c].data_ptr(), per_copy, pool.handle,
                ws.ptr, ws.nbytes, strm)
 
-    ms = time_loop(torch, step, iters, 2 * copies)
+    dist = time_dist(torch, step, iters, max(10, 2 * copies))
+    ms = dist[0]
     assert ws.error_bits() == 0
     kv = float(ctx + 1) * 2 * shape.hidden * 2
     byt = q_layer_bytes(shape, bits) + kv + 2 * shape.hidden * 4
@@ -331,7 +357,8 @@ def bench_layer_decode_q(torch, L, R, ctx, copies, iters, bits):
     pms = time_loop(torch, products, iters, 2 * copies)
     pbyt = q_layer_bytes(shape, bits) - 2 * shape.hidden * 2
     log(f"{tag} products: {pms * 1e3:.1f} us for {pbyt / 1e6:.1f} MB, {pbyt / (pms * 1e-3) / 1e9:.0f} GB/s")
-    res = dict(workload=tag, ms_per_layer_step=ms, layer_steps_per_s=1e3 / ms, tokens_per_s=1e3 / ms,
+    res = dict(workload=tag, ms_per_layer_step=ms, **dist_fields(dist), layer_steps_per_s=1e3 / ms,
+               tokens_per_s=1e3 / ms,
                algorithmic_bytes=byt, hbm_frac=byt / (ms * 1e-3) / HBM_PEAK,
                products=dict(us=pms * 1e3, algorithmic_bytes=pbyt, hbm_frac=pbyt / (pms * 1e-3) / HBM_PEAK))
     del layers, pool
@@ -353,9 +380,10 @@ def bench_sample(torch, L, R, iters):
                             ("greedy", (0.0, 0, 1.0))):
         def step(i, t=t, k=k, p=p):
             L.llmdec_op_sample(logits.data_ptr(), rows, vocab, L.llmdec_sampling(t, k, p, 7, i), nxt.data_ptr(), strm)
-        ms = time_loop(torch, step, iters, 5)
-        res[name] = dict(us=ms * 1e3)
-        log(f"{name} 64 x 32000: {ms * 1e3:.1f} us")
+        dist = time_dist(torch, step, iters, 10)
+        ms = dist[0]
+        res[name] = dict(us=ms * 1e3, us_p10=dist[1] * 1e3, us_median=dist[2] * 1e3, us_p90=dist[3] * 1e3)
+        log(f"{name} 64 x 32000: {ms * 1e3:.1f} us (median {dist[2] * 1e3:.1f})")
     return dict(workload="sample-64x32000", **res)
 
 
@@ -431,14 +459,15 @@ def bench_layer_prefill(torch, L, R, iters):
         L.llmdec_layer_prefill(d.cfg, w, 0, x.data_ptr(), n, T, plen, cu.data_ptr(), start.data_ptr(), bt.data_ptr(),
                                max_pages, pool.handle, ws.ptr, ws.nbytes, strm)
 
-    ms = time_loop(torch, step, iters, 2)
+    dist = time_dist(torch, step, iters, 10)
+    ms = dist[0]
     assert ws.error_bits() == 0
     h, I = shape.hidden, shape.intermediate
     gemm_flops = 2.0 * T * (3 * h + h + 2 * I) * h + 2.0 * T * h * I
     attn_flops = 4.0 * n * shape.n_heads * shape.head_dim * (plen * (plen + 1) / 2)
     del keep
     log(f"C4 prefill: {ms * 1e3:.1f} us per layer, {gemm_flops / (ms * 1e-3) / 1e12:.0f} TFLOP/s on the GEMMs")
-    return dict(workload="7B-layer-prefill-4x512", ms_per_layer=ms, tokens_per_s=T * 1e3 / ms,
+    return dict(workload="7B-layer-prefill-4x512", ms_per_layer=ms, **dist_fields(dist), tokens_per_s=T * 1e3 / ms,
                 gemm_flops=gemm_flops, attn_flops=attn_flops,
                 mfma_frac=(gemm_flops + attn_flops) / (ms * 1e-3) / MFMA_BF16_PEAK)
 

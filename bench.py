@@ -211,7 +211,7 @@ def bench_model_decode(torch, L, R, steps, warmup):
     mw, keep = L.make_model_weights(embed.data_ptr(), [st for _, st in layers], fnorm.data_ptr(), head.data_ptr())
     ctx = synth.context_lengths(5, B, 256, 2048)
     n_iter = steps + warmup
-    totals = ctx + n_iter + 1
+    totals = ctx + 2 * n_iter + 1  # the eager steps, then as many replayed from a graph
     max_pages = int(max(synth.pages_for(t) for t in totals))
     num_pages = int(sum(synth.pages_for(t) for t in totals))
     log(f"C5: pool of {num_pages} pages ({L.llmdec_kv_pool_bytes(d.cfg, num_pages) / 1e9:.1f} GB), max_pages {max_pages}")
@@ -253,6 +253,23 @@ def bench_model_decode(torch, L, R, steps, warmup):
 
     a_ms = time_loop(torch, attn, 64, 4)
     res["attn"] = dict(ms=a_ms, bytes=attn_bytes, gbps=attn_bytes / (a_ms * 1e-3) / 1e9)
+
+    # the same step captured once in a HIP graph (the chosen tokens and the positions fed back on the
+    # device) and replayed over the next n_iter positions of every sequence
+    tok_g = toks[n_iter % 2].clone()
+    nxt_g = torch.empty(B, dtype=torch.int32, device="cuda")
+    pos_g = R.dev_i32(ctx + n_iter)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.llmdec_model_step_greedy(d.cfg, mw, B, B, 1, tok_g.data_ptr(), None, pos_g.data_ptr(), bt.data_ptr(),
+                                   max_pages, pool.handle, nxt_g.data_ptr(), None, ws.ptr, ws.nbytes, R.stream())
+        tok_g.copy_(nxt_g)
+        pos_g.add_(1)
+    g_ms = time_loop(torch, lambda i: g.replay(), steps, warmup)
+    assert ws.error_bits() == 0, "device error word set"
+    assert torch.equal(pos_g.cpu(), torch.from_numpy((ctx + 2 * n_iter).astype(np.int32))), "graph did not replay"
+    res["graph"] = dict(ms_per_step=g_ms, tokens_per_s=B / (g_ms * 1e-3))
+    del g
     res["ctx"] = ctx
     del pool, layers, head, embed
     torch.cuda.empty_cache()
@@ -404,7 +421,6 @@ def bench_tiny_graph(torch, L, R, steps):
     mw, keep = L.make_model_weights(embed.data_ptr(), [st for _, st in layers], fnorm.data_ptr(), head.data_ptr())
     prompt, total = 32, 32 + 2 * steps + 8
     max_pages = (total + 15) // 16
-    strm = R.stream()
 
     def run():
         pool = R.Pool(cfg, max_pages, synth.free_order(1, max_pages))
@@ -415,12 +431,14 @@ def bench_tiny_graph(torch, L, R, steps):
         nxt = torch.empty(1, dtype=torch.int32, device="cuda")
         toks, cu, sp = R.dev_i32(np.arange(prompt) % shape.vocab), R.dev_i32([0, prompt]), R.dev_i32([0])
         L.llmdec_model_step_greedy(cfg, mw, 1, prompt, prompt, toks.data_ptr(), cu.data_ptr(), sp.data_ptr(),
-                                   bt.data_ptr(), max_pages, pool.handle, nxt.data_ptr(), None, ws.ptr, ws.nbytes, strm)
+                                   bt.data_ptr(), max_pages, pool.handle, nxt.data_ptr(), None, ws.ptr, ws.nbytes,
+                                   R.stream())
         tok, pos = nxt.clone(), torch.tensor([prompt], dtype=torch.int32, device="cuda")
 
         def step():
+            # the stream is looked up at each call: under capture it is the capturing stream
             L.llmdec_model_step_greedy(cfg, mw, 1, 1, 1, tok.data_ptr(), None, pos.data_ptr(), bt.data_ptr(),
-                                       max_pages, pool.handle, nxt.data_ptr(), None, ws.ptr, ws.nbytes, strm)
+                                       max_pages, pool.handle, nxt.data_ptr(), None, ws.ptr, ws.nbytes, R.stream())
             tok.copy_(nxt)
             pos.add_(1)
         return step, (pool, ws, bt, nxt, toks, cu, sp, tok, pos)
@@ -432,6 +450,8 @@ def bench_tiny_graph(torch, L, R, steps):
     with torch.cuda.graph(g):
         step2()
     ms_graph = time_loop(torch, lambda i: g.replay(), steps, 4)
+    # both runs took the same number of steps from the same prompt: the same tokens
+    assert torch.equal(hold[3], hold2[3]) and torch.equal(hold[8], hold2[8]), "graph replays diverged from eager steps"
     log(f"tiny 2-layer decode: {ms_eager * 1e3:.1f} us per step enqueued, {ms_graph * 1e3:.1f} us replayed from a graph")
     del hold, hold2, keep, layers
     return dict(workload="tiny-2L-h256-decode-b1", us_per_step_eager=ms_eager * 1e3, us_per_step_graph=ms_graph * 1e3,
@@ -660,7 +680,9 @@ def main():
         head = bench_model_decode(torch, L, R, args.steps, args.warmup)
         log(f"C5: {head['ms_per_step']:.2f} ms/step, {head['tokens_per_s']:.0f} tokens/s, "
             f"{head['hbm_frac'] * 100:.1f}% of HBM peak; decode attention {head['attn']['ms'] * 1e3:.0f} us "
-            f"= {head['attn']['gbps']:.0f} GB/s")
+            f"= {head['attn']['gbps']:.0f} GB/s; replayed from a graph {head['graph']['ms_per_step']:.2f} ms/step")
+        extra["decode_step_graph"] = dict(workload="7B-32L-decode-b64-ctx256..2048, one step captured in a HIP graph",
+                                          **head["graph"])
     if "c2" in only:
         extra["decode_b1_ctx2048"] = bench_layer_decode(torch, L, R, [2048], 4, 100, "7B-layer-decode-b1-ctx2048", 2)
     if "q8" in only:

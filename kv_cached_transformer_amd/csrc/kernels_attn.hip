@@ -352,6 +352,34 @@ __global__ __launch_bounds__(64 * DA_WAVES) void decode_attn_kernel(const float 
   }
 }
 
+// Up to NP partitions of one (sequence, head): every partial is loaded at once (one memory round trip),
+// then the same arithmetic as the general path below, in the same order.
+template <int D, int NP>
+__device__ inline void combine_few(const float *__restrict__ pp, int parts, int s, int h, int n_heads, float *out_f32,
+                                   uint16_t *out_hi, uint16_t *out_lo, int kpad) {
+  const int d = threadIdx.x;
+  float m[NP], l[NP], o[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {  // indexes past the last partition repeat it; their terms are skipped
+    const float *pj = pp + (size_t)min(j, parts - 1) * (D + 2);
+    m[j] = pj[0];
+    l[j] = pj[1];
+    o[j] = pj[2 + d];
+  }
+  float mx = m[0];
+#pragma unroll
+  for (int j = 1; j < NP; ++j) mx = j < parts ? fmaxf(mx, m[j]) : mx;
+  float L = 0.f, acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < NP; ++j)
+    if (j < parts) {
+      const float w = exp2f(m[j] - mx);
+      L = fmaf(l[j], w, L);
+      acc = fmaf(o[j], w, acc);
+    }
+  store_out(acc / L, s, h * D + d, n_heads * D, out_f32, out_hi, out_lo, kpad);
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(int n_heads, const int32_t *__restrict__ ctx_lens,
                                                            int max_pages, int ppp, int n_parts,
@@ -363,6 +391,8 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(int n_heads, const in
   const int parts = (n_pages + ppp - 1) / ppp;
   if (parts <= 1) return;
   const float *pp = partials + ((size_t)s * n_heads + h) * n_parts * (D + 2);
+  if (parts <= 4) return combine_few<D, 4>(pp, parts, s, h, n_heads, out_f32, out_hi, out_lo, kpad);
+  if (parts <= 16) return combine_few<D, 16>(pp, parts, s, h, n_heads, out_f32, out_hi, out_lo, kpad);
   const int d = threadIdx.x;
   // maximum of the partitions' running maxima: one partition per thread, then a block reduction
   __shared__ float red[D / 64], wl[2][D];

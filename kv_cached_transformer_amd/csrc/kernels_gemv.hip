@@ -40,7 +40,7 @@ __device__ inline float gv_silu(float g) { return g / (1.0f + expf(-g)); }
 // (gate/up) blocks resident in one round instead of a round and a half.
 template <int MODE, int TB>
 __global__ __launch_bounds__(kGvWaves * 64, 6) void gemv_kernel(GemvArgs a) {
-  constexpr int D = TB == 1 ? 12 : 6;  // k-tiles in flight per wave
+  constexpr int D = TB == 1 ? 8 : 6;  // k-tile steps in flight per wave
   constexpr int R = D + 1;             // ring slots
   constexpr uint32_t kOut = 0x80000000u;
   extern __shared__ float smem[];

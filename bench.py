@@ -163,21 +163,19 @@ def time_loop(torch, fn, iters, warmup):
 
 
 def time_dist(torch, fn, iters, warmup):
-    """Per-call times of fn(i) over iters calls after warmup calls: an event before every call and one after
-    the last, on the current stream.  Returns (mean, p10, median, p90) in ms."""
+    """(mean, p10, median, p90) in ms of fn(i), on the current stream.  After warmup calls, the mean comes
+    from iters calls between one pair of events; the percentiles from iters more calls with an event
+    recorded before every call and after the last (the events between calls add a little time)."""
     import numpy as np
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
+    mean = time_loop(torch, fn, iters, warmup)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
     ev[0].record()
     for i in range(iters):
-        fn(warmup + i)
+        fn(warmup + iters + i)
         ev[i + 1].record()
     torch.cuda.synchronize()
     t = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)])
-    return float(ev[0].elapsed_time(ev[-1]) / iters), float(np.percentile(t, 10)), float(np.median(t)), \
-        float(np.percentile(t, 90))
+    return mean, float(np.percentile(t, 10)), float(np.median(t)), float(np.percentile(t, 90))
 
 
 def dist_fields(d):

@@ -326,7 +326,8 @@ llmdec_status llmdec_op_lm_head_argmax(const float *x, int32_t rows, int32_t hid
  * call is u = (w >> 8) * 2^-24 with w word 0 of Philox4x32-10 (Salmon et al.,
  * SC 2011) at counter (r, step & 0xffffffff, step >> 32, 0) and key
  * (seed & 0xffffffff, seed >> 32), so results are reproducible and need no
- * generator state on the device.
+ * generator state on the device; every sum the decision depends on is taken
+ * in a fixed order, so the same inputs give the same tokens on every call.
  *   temperature <= 0: greedy (argmax, lowest index on ties);
  *   top_k <= 0 or >= vocab: no top-k;  top_p in (0, 1], 1: no top-p. */
 typedef struct {

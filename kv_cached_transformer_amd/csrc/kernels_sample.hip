@@ -116,6 +116,7 @@ __global__ __launch_bounds__(kSmpThreads) void sample_kernel(SampleArgs a) {
   __shared__ float red[kSmpWaves];
   __shared__ uint32_t hist[256];
   __shared__ float histf[256];
+  __shared__ float whist[kSmpWaves][256];  // top-p: each wave's own mass histogram
   __shared__ uint32_t sel[2];  // chosen digit; remaining count
   __shared__ float self[2];    // mass above the chosen bin
   __shared__ float wtot[kSmpWaves];
@@ -198,13 +199,23 @@ __global__ __launch_bounds__(kSmpThreads) void sample_kernel(SampleArgs a) {
     float above = 0.f;  // kept mass strictly above the current prefix range
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      if (tid < 256) histf[tid] = 0.f;
+      // masses go to the wave's own histogram (no other wave adds to it, so the waves do not contend
+      // and each bin's sum does not depend on how the waves interleave), then bin by bin in wave order
+#pragma unroll
+      for (int q = 0; q < 4; ++q) whist[wave][lane + 64 * q] = 0.f;
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < kSmpPer; ++j) {
         const float ev = e(j);
         const uint32_t key = __float_as_uint(ev);
-        if ((kept >> j & 1) && (key & pmask) == prefix) atomicAdd(&histf[(key >> shift) & 255u], ev);
+        if ((kept >> j & 1) && (key & pmask) == prefix) atomicAdd(&whist[wave][(key >> shift) & 255u], ev);
+      }
+      __syncthreads();
+      if (tid < 256) {
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < kSmpWaves; ++w) t += whist[w][tid];
+        histf[tid] = t;
       }
       __syncthreads();
       // (if rounding leaves the target out of reach, the whole range stays: bin 0)

@@ -115,6 +115,27 @@ def test_sample_matches_oracle(L, R, rows, vocab, scale):
         assert np.array_equal(nxt.cpu().numpy(), got)
 
 
+def test_sample_repeatable(L, R):
+    """The same logits, parameters, seed and step give the same tokens on every call: the top-p cut sums
+    masses in a fixed order (per-wave histograms added in wave order), as does the draw."""
+    rows, vocab = 64, 32000
+    logits = (synth.rng(72, rows, vocab).standard_normal((rows, vocab)) * 2.0).astype(np.float32)
+    ld = R.dev_f32(logits)
+    nxt = torch.empty(rows, dtype=torch.int32, device="cuda")
+    for T, k, p in [(1.0, 0, 0.9), (0.8, 50, 0.9), (1.3, 0, 0.5)]:
+        banner(f"sample repeatability T={T} top_k={k} top_p={p}")
+        params = L.llmdec_sampling(T, k, p, 4242, 17)
+        first = None
+        for _ in range(20):
+            L.llmdec_op_sample(ld.data_ptr(), rows, vocab, params, nxt.data_ptr(), R.stream())
+            torch.cuda.synchronize()
+            got = nxt.cpu().numpy().copy()
+            if first is None:
+                first = got
+                check_rows(f"repeatable T={T} k={k} p={p}", logits, got, T, k, p, 4242, 17)
+            assert np.array_equal(got, first)
+
+
 def test_sample_ties_and_greedy_ties(L, R):
     """Three equal largest logits: greedy takes the lowest index; top_k = 2 keeps all three (ties with the
     k-th stay) and the draws over many steps reach each of them and nothing else."""

@@ -85,7 +85,10 @@ def test_rmsnorm_eps_inside_root(L, R):
                                           (17, 512, 256, 0), (17, 512, 1024, 1), (33, 512, 11008, 1),
                                           (33, 4096, 11008, 0), (32, 4096, 4096, 1), (48, 12288, 4096, 0),
                                           # 257 row blocks: the last column group is ragged under a balanced split
-                                          (1, 4112, 4096, 0), (40, 4112, 4096, 1)])
+                                          (1, 4112, 4096, 0), (40, 4112, 4096, 1),
+                                          # one row: the widest input the one-row kernel stages (14336), the
+                                          # narrowest (16), and one k-tile past it (the streaming kernel)
+                                          (1, 64, 14336, 1), (1, 48, 16, 0), (1, 32, 14352, 0)])
 def test_linear(L, R, rows, n, k, acc):
     banner(f"linear rows={rows} n={n} k={k} acc={acc}")
     rng = np.random.default_rng(rows * 7 + n + k)

@@ -46,7 +46,7 @@ def op_linear(L, bits):
 
 # (rows, cols): several lanes' chunks and steps, a short last group (688 = 5 x 128 + 48), a ragged
 # last step (1040 = 1024 + 16), 14 steps (the largest k), and the 7B shapes
-SHAPES = [(16, 256), (64, 688), (12, 1040), (8, 14336), (4096, 4096), (4096, 11008), (12288, 4096)]
+SHAPES = [(16, 256), (64, 688), (12, 1040), (8, 14336), (4, 16), (4, 144), (4096, 4096), (4096, 11008), (12288, 4096)]
 
 
 @pytest.mark.parametrize("bits", [8, 4])

@@ -96,7 +96,7 @@ PARAMS = [(0.0, 0, 1.0), (1.0, 0, 1.0), (0.7, 40, 1.0), (1.3, 0, 0.9), (0.8, 50,
 
 
 @pytest.mark.parametrize("rows,vocab,scale", [(64, 32000, 2.0), (16, 1024, 1.0), (7, 1000, 3.0), (3, 32768, 2.0),
-                                              (5, 37, 1.0)])
+                                              (5, 37, 1.0), (2, 1, 1.0)])
 def test_sample_matches_oracle(L, R, rows, vocab, scale):
     logits = (synth.rng(70, rows, vocab).standard_normal((rows, vocab)) * scale).astype(np.float32)
     ld = R.dev_f32(logits)

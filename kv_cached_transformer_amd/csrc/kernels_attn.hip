@@ -74,7 +74,7 @@ __device__ inline void store_out(float v, int r, int c, int ld, float *out_f32, 
 // so every sequence's full first partitions are dispatched before the short
 // last ones, which fill in the tail.
 constexpr int DA_RING = 3;
-constexpr int DA_WAVES = 4;        // decode waves per block: consecutive partitions of one (sequence, heads)
+constexpr int DA_WAVES = 8;        // decode waves per block: consecutive partitions of one (sequence, heads)
 constexpr int kMaxPartPages = 16;  // pages per decode partition, at most (one page id per lane)
 
 __device__ inline uint32_t vword(const uint4 &v, int k) { return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w; }

@@ -231,10 +231,10 @@ def _gather(k_img, v_img, row, n, h):
                                          (8, 128, 8, [4096, 33, 511, 512, 1000, 7]),
                                          (32, 128, 8, [0, 15, 16, 2048, 300]),
                                          (4, 64, 1, [0, 1, 17, 100, 513]),
-                                         (4, 64, 4, [1000, 1100, 3])])
+                                         (4, 64, 4, [2000, 2100, 3])])
 def test_decode_attention(L, R, H, D, Hk, ctxs):
     """Query head h attends over K/V head h // (H / Hk) (grouped-query when Hk < H).  The last case
-    leaves 16 and 18 block results per head to the combine (one-page partitions, 4 per block): the
+    leaves 16 and 17 block results per head to the combine (one-page partitions, 8 per block): the
     largest count it reads in one pass and one past it."""
     banner(f"decode_attention H={H} D={D} Hk={Hk} ctxs={ctxs}")
     shape = Shape(H, D, Hk=Hk)

@@ -67,6 +67,29 @@ def round_to_bf16(x) -> np.ndarray:
     return u.view(np.float64)
 
 
+F16_MAX = 65504.0
+
+
+def round_to_f16(x) -> np.ndarray:
+    """Round to the nearest IEEE binary16 value, ties to even; returns float64.
+
+    The pages' minimal engine computes in fp16 ("为什么要自己动手写一个LLM推理引擎" §4.1), and
+    the weights article recommends clipping values beyond fp16's range instead of letting them
+    overflow to infinity; magnitudes above 65504 (the largest finite binary16) are clipped to it
+    first.  The rounding itself is numpy's float16 conversion.  Used to state what a product sees
+    when its activation is carried in fp16.
+    """
+    x = np.clip(np.asarray(x, dtype=np.float64), -F16_MAX, F16_MAX)
+    return x.astype(np.float16).astype(np.float64)
+
+
+def f16_pair(x) -> np.ndarray:
+    """hi + lo with hi = fp16(x), lo = fp16(x - hi): x carried in two fp16 parts (about 22 bits)."""
+    x = np.asarray(x, dtype=np.float64)
+    hi = round_to_f16(x)
+    return hi + round_to_f16(x - hi)
+
+
 def bf16_bits_of(x) -> np.ndarray:
     """Bit pattern of values that are already bf16-representable."""
     f = np.asarray(x, dtype=np.float64).astype(np.float32)

@@ -71,6 +71,61 @@ def test_bf16_rounding_matches_torch_cast():
     assert np.array_equal(od.bf16_bits_of(ref[:100]), torch.from_numpy(x[:100]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
 
 
+def test_f16_rounding_worked_cases():
+    """fp16 keeps 11 significant bits: its spacing is 2^-10 on [1, 2), normal numbers reach down to
+    2^-14 and subnormals are multiples of 2^-24 (IEEE 754 binary16).  Values past the largest finite
+    one, 65504, are clipped to it (the weights article's remedy for fp16 overflow)."""
+    cases = [
+        (1.0 + 2.0 ** -11, 1.0),                      # halfway between 1 and 1 + 2^-10: ties to even
+        (1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),      # halfway between 1 + 2^-10 and 1 + 2^-9: to the even one
+        (1.0 + 2.0 ** -11 + 2.0 ** -20, 1.0 + 2.0 ** -10),  # just past halfway: up
+        (2049.0, 2048.0),                             # spacing 2 on [2048, 4096): tie to even
+        (2051.0, 2052.0),
+        (65504.0, 65504.0), (65519.0, 65504.0), (70000.0, 65504.0), (-1e9, -65504.0),
+        (2.0 ** -14, 2.0 ** -14),                     # smallest normal
+        (2.0 ** -24, 2.0 ** -24),                     # smallest subnormal
+        (2.0 ** -25, 0.0),                            # halfway to zero: ties to even (zero)
+        (3 * 2.0 ** -25, 2.0 ** -23),                 # halfway between 1 and 2 units of 2^-24: to 2
+        (-0.1, -0.0999755859375),                     # 0.1 = 1.6 * 2^-4: 1638.4 / 2^14 -> 1638 / 2^14
+    ]
+    x = np.array([c[0] for c in cases])
+    assert np.array_equal(od.round_to_f16(x), np.array([c[1] for c in cases]))
+    # random values: within half a spacing, where the spacing is 2^(e-10) for |x| in [2^e, 2^(e+1))
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal(10000) * np.exp2(rng.integers(-12, 14, 10000))
+    e = np.floor(np.log2(np.abs(v)))
+    assert np.all(np.abs(od.round_to_f16(v) - v) <= np.exp2(np.maximum(e, -14) - 11))
+    # the pair: hi + lo carries 22 bits (lo rounds the remainder, which is below half hi's spacing)
+    w = rng.standard_normal(10000)
+    assert np.all(np.abs(od.f16_pair(w) - w) <= np.abs(w) * 2.0 ** -21 + 2.0 ** -25)
+    assert np.array_equal(od.f16_pair(od.round_to_f16(w)), od.round_to_f16(w))
+
+
+def test_lm_head_logits_closed_form():
+    """Final norm, then lm_head ("企业官网建设流程全解析" §1.1: the last RMSNorm precedes the output head;
+    "大模型推理全流程解析" §2.2.3: logits = hidden . lm_head^T).  With lm_head row j = 2 e_{d_j} (a one-hot
+    row, [out][in] layout), logit j is 2 x[d_j] gamma[d_j] / sqrt(mean(x^2) + eps): a missing final norm,
+    a transposed head or an ignored gain each changes it."""
+    class S:
+        rms_eps = 1e-6
+    h, V = 64, 48
+    rng = np.random.default_rng(5)
+    x = 3.0 * rng.standard_normal((2, h))
+    gamma = od.bf16_bits_of(od.round_to_bf16(0.5 + rng.random(h)))
+    d = rng.permutation(h)[:V]
+    head = np.zeros((V, h), np.uint16)
+    head[np.arange(V), d] = 0x4000  # bf16 2.0
+    got = od.lm_head_logits(S, gamma, head, x)
+    g = od.widen_bf16(gamma)
+    for r in range(2):
+        inv = 1.0 / np.sqrt(sum(v * v for v in x[r]) / h + 1e-6)
+        for j in range(V):
+            assert abs(got[r, j] - 2.0 * x[r, d[j]] * g[d[j]] * inv) <= 1e-12 * (1 + abs(got[r, j]))
+    # a constant row: the norm maps c * 1 to c / sqrt(c^2 + eps) * 1, so the logits are 2 gamma[d_j] c / |c|
+    c = np.full((1, h), -4.0)
+    assert np.allclose(od.lm_head_logits(S, gamma, head, c)[0], -2.0 * g[d] * 4.0 / np.sqrt(16.0 + 1e-6), rtol=1e-13)
+
+
 def test_widen_bf16_exact():
     assert od.widen_bf16(np.array([0x3F80, 0xBF80, 0x4049, 0x0000], np.uint16)).tolist() == [1.0, -1.0, 3.140625, 0.0]
 

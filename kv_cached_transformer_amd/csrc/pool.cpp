@@ -8,8 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include "common.h"
-#include "internal.h"
+#include "host.h"
 
 using namespace llmdec;
 

@@ -35,12 +35,14 @@
  *    bf16 is to nearest, ties to even.
  *  - Precision: weights and cached K/V are bf16 (the K/V values rounded to
  *    nearest-even when appended).  Activations entering a weight product are
- *    carried as a bf16 pair hi + lo (about 17 significant bits) and multiply
- *    the bf16 weights on the matrix cores with fp32 accumulation; the
- *    residual stream, attention (scores, softmax, weighted sum) and logits
- *    are fp32.  The products of a single-sequence decode step (one row) and
- *    those with group-quantized weights run in fp32 from the unrounded
- *    activation instead.
+ *    rounded to fp16 (nearest-even; magnitudes beyond 65504 clipped to it),
+ *    the compute precision of [E] §4.1's minimal engine, and multiply the
+ *    weights on the matrix cores in fp16 with fp32 accumulation: the packing
+ *    carries each bf16 weight exactly as an fp16 value times a power of two
+ *    (see llmdec_pack_matrix).  The residual stream, attention (scores,
+ *    softmax, weighted sum) and logits are fp32.  The products of a
+ *    single-sequence decode step (one row) and those with group-quantized
+ *    weights take the unrounded fp32 activation instead.
  *  - Not thread-safe per pool handle; distinct handles are independent.
  */
 #ifndef LLMDEC_H
@@ -87,11 +89,11 @@ typedef struct {
 } llmdec_layer_weights;
 
 /* One layer re-laid out for the kernels by llmdec_pack_layer (pointers into
- * the caller's packed buffer).  Matrices are stored as 16-row x 32-column
- * tiles in the order the matrix-core operands are fed; q/k/v are fused into
- * one [hidden + 2*n_kv_heads*head_dim][hidden] matrix (wq rows, then wk,
- * then wv) and gate/up into one matrix whose 16-row
- * blocks alternate gate and up.  The contents are the same bf16 values. */
+ * the caller's packed buffer).  Matrices are packed as llmdec_pack_matrix
+ * describes; q/k/v are fused into one [hidden + 2*n_kv_heads*head_dim][hidden]
+ * matrix (wq rows, then wk, then wv) and gate/up into one matrix whose 16-row
+ * blocks alternate gate and up, each fused matrix with one power-of-two
+ * scale. */
 typedef struct {
   const void *attn_norm, *mlp_norm; /* bf16 [hidden], copied */
   const void *w_qkv, *w_o, *w_gu, *w_down;
@@ -113,11 +115,20 @@ typedef struct {
 const char *llmdec_last_error(void);
 
 /* ------------------------------------------------------------------ weights */
-/* Bytes of a packed rows x cols bf16 matrix (rows a multiple of 16; cols padded
- * up to a multiple of 32 with zeros). */
+/* Bytes of a packed rows x cols matrix (rows a multiple of 16; cols padded up
+ * to a multiple of 32 with zeros): rows * round_up(cols, 32) fp16 values, then
+ * a 256-byte trailer. */
 size_t llmdec_packed_matrix_bytes(int32_t rows, int32_t cols);
 /* Re-lay a dev bf16 [rows][cols] matrix into dev dst (>= packed_matrix_bytes).
- * Errors: E_INVALID for null pointers, rows % 16 != 0, dst_bytes too small. */
+ * The tiles hold fp16(w * 2^s) in the tile order of "Packed activations"
+ * below; the trailer's first 32-bit word is the largest finite |w| (its fp32
+ * bits), from which s = 14 - floor(log2 max|w|) (clamped to [-100, 100]).
+ * That puts the largest magnitude in [2^14, 2^15), so every weight within a
+ * factor 2^31 of the largest is carried exactly (a bf16 significand has 8
+ * bits, fp16 holds 11 and reaches 2^-24 with its subnormals); smaller ones
+ * round to the nearest multiple of 2^(-24-s).  Products multiply their fp32
+ * result by 2^-s.  Errors: E_INVALID for null pointers, rows % 16 != 0,
+ * dst_bytes too small. */
 llmdec_status llmdec_pack_matrix(int32_t rows, int32_t cols, const void *src, void *dst, size_t dst_bytes,
                                  llmdec_stream stream);
 /* Bytes of one packed layer for cfg. */
@@ -233,45 +244,51 @@ llmdec_status llmdec_model_step_greedy(const llmdec_config *cfg, const llmdec_mo
  * The kernels the layer steps are built from, exposed one by one so each can
  * be checked on its own.  Same conventions as above.
  *
- * Packed activations: a bf16 [R][C] matrix (R a multiple of 16, C of 32) is
+ * Packed activations: an fp16 [R][C] matrix (R a multiple of 16, C of 32) is
  * stored as 16 x 32 tiles, tile (R/16 index i, C/32 index t) at element
  * offset (i * C/32 + t) * 512; inside a tile, lane l = (r % 16) + 16 * ((c %
  * 32) / 8) holds elements c % 8 = 0..7 at l * 8 + c % 8.  This is the operand
  * order of one 16x16x32 matrix-core instruction, so every operand fetch is
- * one contiguous 16-byte load. */
+ * one contiguous 16-byte load.  Packed weight matrices use the same order. */
 
 /* y = x * (mean(x^2) + eps)^(-1/2) * gamma per row ([E] §4.2).  x: dev fp32
  * [rows][n], n a multiple of 32 and at most 8192; gamma: dev bf16 [n].
- * out_f32 (fp32 [rows][n]) and the pair out_hi / out_lo (hi = bf16(y), lo =
- * bf16(y - hi), each in the packed tile layout of a
- * [round_up(rows,16)][ld_packed] matrix: see "Packed activations" below;
- * columns n..ld_packed-1 zeroed) may each be NULL but not both. */
+ * out_f32 (fp32 [rows][n]) and out_act (fp16(y), rounded to nearest-even and
+ * clipped to +-65504, in the packed tile layout of a
+ * [round_up(rows,16)][ld_packed] matrix: see "Packed activations" above;
+ * columns n..ld_packed-1 zeroed) may each be NULL but not both.  out_lo
+ * (NULL, or the same layout as out_act, which must then be given) receives
+ * fp16(y - out_act): the pair the q|k|v product reads. */
 llmdec_status llmdec_op_rmsnorm(const float *x, const void *gamma, int32_t rows, int32_t n, float eps,
-                                float *out_f32, void *out_hi, void *out_lo, int32_t ld_packed, llmdec_stream stream);
+                                float *out_f32, void *out_act, void *out_lo, int32_t ld_packed, llmdec_stream stream);
 
 /* out[m][n] (+)= sum_k a[m][k] * W[n][k], fp32 accumulation, for a dev fp32
- * a [rows][k_dim] (carried as a bf16 hi/lo pair, as every activation
- * entering a weight product is) and a packed W (llmdec_pack_matrix of
- * [n_dim][k_dim]).  accumulate = 0 stores, 1 adds into out (the residual add
- * of [W] §1.1).  ws: scratch for the activation pair and split-k partial
- * sums (>= llmdec_op_linear_ws_bytes).  rows == 1 takes the one-row kernel
- * (fp32 activation, k_dim <= 14336), rows <= 64 the weight-streaming
- * kernel, rows > 64 the LDS-tiled one. */
+ * a [rows][k_dim] and a packed W (llmdec_pack_matrix of [n_dim][k_dim]).
+ * act_parts = 1: a enters the matrix cores rounded to fp16 (as the o,
+ * gate/up, down and lm_head products of the layer steps take theirs);
+ * act_parts = 2: as the fp16 pair hi + lo (as the q|k|v product takes its
+ * input).  accumulate = 0 stores, 1 adds into out (the residual add of [W]
+ * §1.1).  ws: scratch for the fp16 activation and split-k partial sums (>=
+ * llmdec_op_linear_ws_bytes).  rows == 1 takes the one-row kernel (fp32
+ * activation whatever act_parts, k_dim <= 14336), rows <= 64 the
+ * weight-streaming kernel, rows > 64 the tiled one.  E_INVALID for act_parts
+ * other than 1 or 2. */
 size_t llmdec_op_linear_ws_bytes(int32_t rows, int32_t k_dim, int32_t n_dim);
 llmdec_status llmdec_op_linear(const float *a, int32_t rows, int32_t k_dim, const void *w_packed, int32_t n_dim,
-                               float *out, int32_t accumulate, void *ws, size_t ws_bytes, llmdec_stream stream);
+                               float *out, int32_t accumulate, int32_t act_parts, void *ws, size_t ws_bytes,
+                               llmdec_stream stream);
 
 /* The gate/up product with the SwiGLU epilogue, as the layer steps run it
  * ([W] §1.2, [E] §4.2): for a fused gate/up matrix as llmdec_pack_layer lays
  * it out (16-row blocks alternating gate and up, 2*inter rows), writes
- * u[m][j] = silu(g[m][j]) * up[m][j], g and up the fp32 products, as the
- * hi/lo pair out_hi / out_lo, each in the packed layout of a
- * [round_up(rows,16)][ld_packed] matrix (inter <= ld_packed <= inter + 16,
- * ld_packed a multiple of 32; columns inter.. zeroed).  ws as for
- * llmdec_op_linear with n_dim = 2*inter. */
+ * u[m][j] = silu(g[m][j]) * up[m][j], g and up the fp32 products, as fp16
+ * into out_act, in the packed layout of a [round_up(rows,16)][ld_packed]
+ * matrix (inter <= ld_packed <= inter + 16, ld_packed a multiple of 32;
+ * columns inter.. zeroed).  ws as for llmdec_op_linear with n_dim =
+ * 2*inter. */
 llmdec_status llmdec_op_swiglu_linear(const float *a, int32_t rows, int32_t k_dim, const void *w_gu_packed,
-                                      int32_t inter, void *out_hi, void *out_lo, int32_t ld_packed, void *ws,
-                                      size_t ws_bytes, llmdec_stream stream);
+                                      int32_t inter, void *out_act, int32_t ld_packed, void *ws, size_t ws_bytes,
+                                      llmdec_stream stream);
 
 /* Rotate q and k of each new token by its position and store bf16 k, v into
  * the pool ([E] §4.3: rotation first, then the cache update).  qkv: dev fp32

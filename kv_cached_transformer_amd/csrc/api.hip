@@ -1,59 +1,19 @@
 // C ABI of libllmdec: argument checks, workspace layout and the order of the
 // kernels in a layer step and a model step.
-#include <stdarg.h>
-#include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
+#include <initializer_list>
 
 #include "common.h"
 #include "internal.h"
 
 namespace llmdec {
 
-static thread_local char g_err[512] = "";
-
-llmdec_status set_error(llmdec_status st, const char *fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_err, sizeof(g_err), fmt, ap);
-  va_end(ap);
-  return st;
-}
-
-llmdec_status clear_error() {
-  g_err[0] = 0;
-  return LLMDEC_OK;
-}
-
 llmdec_status check_launch(const char *who) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(LLMDEC_E_HIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
   return clear_error();
-}
-
-llmdec_status check_config(const llmdec_config *c, const char *who) {
-  if (!c) return set_error(LLMDEC_E_INVALID, "%s: config is NULL", who);
-  if (c->n_layers <= 0 || c->hidden <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || c->intermediate <= 0 ||
-      c->vocab <= 0)
-    return set_error(LLMDEC_E_INVALID, "%s: config sizes must be positive", who);
-  if (c->page_size != kPage)
-    return set_error(LLMDEC_E_UNSUPPORTED, "%s: page_size must be %d, got %d", who, kPage, c->page_size);
-  if (c->head_dim != 64 && c->head_dim != 128)
-    return set_error(LLMDEC_E_UNSUPPORTED, "%s: head_dim must be 64 or 128, got %d", who, c->head_dim);
-  if (c->n_heads * c->head_dim != c->hidden)
-    return set_error(LLMDEC_E_INVALID, "%s: hidden (%d) != n_heads (%d) * head_dim (%d)", who, c->hidden, c->n_heads,
-                     c->head_dim);
-  if (c->n_kv_heads <= 0 || c->n_heads % c->n_kv_heads)
-    return set_error(LLMDEC_E_INVALID, "%s: n_kv_heads (%d) must divide n_heads (%d)", who, c->n_kv_heads,
-                     c->n_heads);
-  if (c->hidden % 32 || c->intermediate % 16 || c->vocab % 16)
-    return set_error(LLMDEC_E_INVALID, "%s: hidden must be a multiple of 32, intermediate and vocab of 16", who);
-  if (c->hidden > 8192 || c->intermediate > 16384)
-    return set_error(LLMDEC_E_UNSUPPORTED, "%s: hidden <= 8192 and intermediate <= 16384 are supported", who);
-  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f))
-    return set_error(LLMDEC_E_INVALID, "%s: rms_eps must be >= 0 and rope_theta > 0", who);
-  return LLMDEC_OK;
 }
 
 static size_t al(size_t x) { return round_up_sz(x, 256); }
@@ -97,7 +57,6 @@ WsLayout ws_layout(const llmdec_config &c, int max_tokens, int max_seqs, int max
   L.act_h = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_h);
   L.act_hl = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_h);
   L.act_i = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_i);
-  L.act_il = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_i);
   L.qkv = take(sizeof(float) * (size_t)rows * qkv_cols(c));
   L.part = take(sizeof(float) * part);
   L.part_floats = part;
@@ -176,7 +135,7 @@ static void run_layer_one_row(const LayerArgs &a) {
   const int h = c.hidden, I = c.intermediate, nqkv = qkv_cols(c);
   const WsLayout &L = a.L;
   uint32_t *err = at<uint32_t>(a.ws, L.err);
-  // one row: the fp32 activations fit in the packed activation planes' space
+  // one row: the fp32 activations fit in the packed activations' space (16 fp16 rows)
   float *y = at<float>(a.ws, L.act_h), *u = at<float>(a.ws, L.act_i), *qkv = at<float>(a.ws, L.qkv);
   uint16_t *pk, *pv;
   pool_layer(a.pool, a.layer, &pk, &pv);
@@ -189,7 +148,7 @@ static void run_layer_one_row(const LayerArgs &a) {
   launch_gemv_qkv_rope(a.hidden, (const uint16_t *)a.w->attn_norm, c.rms_eps, (const uint16_t *)a.w->w_qkv, nqkv, h,
                        qkv, ra, a.s);
   launch_decode_attention(c, qkv, nqkv, 1, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages,
-                          at<float>(a.ws, L.attn_part), y, nullptr, nullptr, 0, err, a.s);
+                          at<float>(a.ws, L.attn_part), y, nullptr, 0, err, a.s);
   launch_gemv(y, nullptr, 0.f, (const uint16_t *)a.w->w_o, h, h, kAccumulate, a.hidden, a.s);
   launch_gemv(a.hidden, (const uint16_t *)a.w->mlp_norm, c.rms_eps, (const uint16_t *)a.w->w_gu, 2 * I, h, kSiluMul,
               u, a.s);
@@ -205,36 +164,39 @@ static void run_layer(const LayerArgs &a) {
     return;
   }
   uint32_t *err = at<uint32_t>(a.ws, L.err);
-  uint16_t *ah_hi = at<uint16_t>(a.ws, L.act_h), *ah_lo = at<uint16_t>(a.ws, L.act_hl);
-  uint16_t *ai_hi = at<uint16_t>(a.ws, L.act_i), *ai_lo = at<uint16_t>(a.ws, L.act_il);
+  uint16_t *act_h = at<uint16_t>(a.ws, L.act_h), *act_hl = at<uint16_t>(a.ws, L.act_hl);
+  uint16_t *act_i = at<uint16_t>(a.ws, L.act_i);
   float *qkv = at<float>(a.ws, L.qkv), *part = at<float>(a.ws, L.part);
-  const Act ah{ah_hi, ah_lo, M, L.kpad_h, L.row_blocks}, ai{ai_hi, ai_lo, M, L.kpad_i, L.row_blocks};
+  // the q|k|v product reads its input as an fp16 pair (k and v are rounded to bf16 for the cache, so
+  // their error must stay far below a bf16 step); the other products read one fp16 plane
+  const Act ah2{act_h, act_hl, M, L.kpad_h, L.row_blocks}, ah{act_h, nullptr, M, L.kpad_h, L.row_blocks};
+  const Act ai{act_i, nullptr, M, L.kpad_i, L.row_blocks};
   uint16_t *pk, *pv;
   pool_layer(a.pool, a.layer, &pk, &pv);
 
   // attention block: x += Wo . attn(rope(Wq y), rope(Wk y), Wv y),  y = RMSNorm(x)
-  launch_rmsnorm(a.hidden, h, nullptr, M, (const uint16_t *)a.w->attn_norm, M, h, c.rms_eps, err, nullptr, ah_hi,
-                 ah_lo, L.kpad_h, nullptr, Splits{}, a.s);
+  launch_rmsnorm(a.hidden, h, nullptr, M, (const uint16_t *)a.w->attn_norm, M, h, c.rms_eps, err, nullptr, act_h,
+                 act_hl, L.kpad_h, nullptr, Splits{}, a.s);
   LinearOut o_qkv;
   o_qkv.kind = kStore;
   o_qkv.f32 = qkv;
   const int nqkv = qkv_cols(c);
   o_qkv.ld = nqkv;
   // a split q|k|v product leaves partial sums that the rotary/append kernel adds up
-  const Splits sp_qkv = launch_linear(ah, (const uint16_t *)a.w->w_qkv, nqkv, h, o_qkv, part, L.part_floats, kSplitBalanced, a.s);
+  const Splits sp_qkv = launch_linear(ah2, (const uint16_t *)a.w->w_qkv, nqkv, h, o_qkv, part, L.part_floats, kSplitBalanced, a.s);
   const float *qkv_part = sp_qkv.any() ? part : nullptr;
   if (a.decode) {
     launch_rope_append(c, qkv, qkv_part, sp_qkv, nqkv, M, a.n_seqs, nullptr, a.ctx, a.bt, a.max_pages, pk, pv,
                        a.pool->num_pages, err, a.s);
     launch_decode_attention(c, qkv, nqkv, M, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages,
-                            at<float>(a.ws, L.attn_part), nullptr, ah_hi, ah_lo, L.kpad_h, err, a.s);
+                            at<float>(a.ws, L.attn_part), nullptr, act_h, L.kpad_h, err, a.s);
   } else {
     int32_t *ts = at<int32_t>(a.ws, L.tok_seq), *tp = at<int32_t>(a.ws, L.tok_pos);
     launch_token_map(a.cu, a.start, a.n_seqs, M, err, ts, tp, a.s);
     launch_rope_append(c, qkv, qkv_part, sp_qkv, nqkv, M, a.n_seqs, ts, tp, a.bt, a.max_pages, pk, pv,
                        a.pool->num_pages, err, a.s);
     launch_prefill_attention(c, qkv, nqkv, a.n_seqs, M, a.max_q_len, a.cu, a.start, a.bt, a.max_pages, pk, pv,
-                             a.pool->num_pages, nullptr, ah_hi, ah_lo, L.kpad_h, err, a.s);
+                             a.pool->num_pages, nullptr, act_h, L.kpad_h, err, a.s);
   }
   LinearOut o_res;
   o_res.kind = kAccumulate;
@@ -245,12 +207,11 @@ static void run_layer(const LayerArgs &a) {
 
   // MLP block: x += Wd (silu(Wg y) * (Wu y)),  y = RMSNorm(x); the gate/up product's epilogue forms the
   // SwiGLU activation directly
-  launch_rmsnorm(a.hidden, h, nullptr, M, (const uint16_t *)a.w->mlp_norm, M, h, c.rms_eps, err, nullptr, ah_hi,
-                 ah_lo, L.kpad_h, sp_o.any() ? part : nullptr, sp_o, a.s);
+  launch_rmsnorm(a.hidden, h, nullptr, M, (const uint16_t *)a.w->mlp_norm, M, h, c.rms_eps, err, nullptr, act_h,
+                 nullptr, L.kpad_h, sp_o.any() ? part : nullptr, sp_o, a.s);
   LinearOut o_gu;
   o_gu.kind = kSiluMul;
-  o_gu.act_hi = ai_hi;
-  o_gu.act_lo = ai_lo;
+  o_gu.act = act_i;
   o_gu.act_kt = L.kpad_i / kTileK;
   o_gu.act_cols = I;
   const Splits sp_gu = launch_linear(ah, (const uint16_t *)a.w->w_gu, 2 * I, h, o_gu, part, L.part_floats, kSplitBalanced, a.s);
@@ -263,12 +224,11 @@ static void run_layer(const LayerArgs &a) {
 
 using namespace llmdec;
 
-extern "C" const char *llmdec_last_error(void) { return g_err; }
 
 // ------------------------------------------------------------------ weights
 extern "C" size_t llmdec_packed_matrix_bytes(int32_t rows, int32_t cols) {
   if (rows <= 0 || cols <= 0 || rows % 16) return 0;
-  return (size_t)rows * round_up(cols, kTileK) * sizeof(uint16_t);
+  return packed_tiles_bytes(rows, cols) + kWTrailer;
 }
 
 extern "C" llmdec_status llmdec_pack_matrix(int32_t rows, int32_t cols, const void *src, void *dst, size_t dst_bytes,
@@ -279,7 +239,12 @@ extern "C" llmdec_status llmdec_pack_matrix(int32_t rows, int32_t cols, const vo
                      cols);
   const size_t need = llmdec_packed_matrix_bytes(rows, cols);
   if (dst_bytes < need) return set_error(LLMDEC_E_INVALID, "pack_matrix: dst holds %zu bytes, %zu needed", dst_bytes, need);
-  launch_pack_matrix(rows, cols, (const uint16_t *)src, (uint16_t *)dst, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  const size_t tb = packed_tiles_bytes(rows, cols);
+  uint16_t *d = (uint16_t *)dst;
+  launch_weight_trailer_clear(d, tb, s);
+  launch_weight_absmax(rows, cols, (const uint16_t *)src, d, tb, s);
+  launch_pack_matrix(rows, cols, (const uint16_t *)src, d, tb, s);
   return check_launch("pack_matrix");
 }
 
@@ -323,21 +288,30 @@ extern "C" llmdec_status llmdec_pack_layer(const llmdec_config *cfg, const llmde
   if (hipMemcpyAsync(d + off[0], in->attn_norm, (size_t)h * 2, hipMemcpyDeviceToDevice, s) != hipSuccess ||
       hipMemcpyAsync(d + off[1], in->mlp_norm, (size_t)h * 2, hipMemcpyDeviceToDevice, s) != hipSuccess)
     return set_error(LLMDEC_E_HIP, "pack_layer: copy of the norm gains failed");
-  // Fused q|k|v: row blocks of wq ([h][h]), then wk and wv ([kv][h] each; every part a whole number of
-  // 16-row blocks)
-  const int ktc = round_up(h, kTileK), kv = kv_cols(*cfg);
-  uint16_t *qkv = (uint16_t *)(d + off[2]);
-  launch_pack_matrix(h, h, (const uint16_t *)in->wq, qkv, s);
-  launch_pack_matrix(kv, h, (const uint16_t *)in->wk, qkv + (size_t)h * ktc, s);
-  launch_pack_matrix(kv, h, (const uint16_t *)in->wv, qkv + (size_t)(h + kv) * ktc, s);
-  launch_pack_matrix(h, h, (const uint16_t *)in->wo, (uint16_t *)(d + off[3]), s);
-  // Gate/up interleaved by 16-row block: block 2j = gate rows 16j.., block 2j+1 = up rows 16j..
-  {
-    uint16_t *gu = (uint16_t *)(d + off[4]);
-    launch_pack_matrix(I, h, (const uint16_t *)in->w_gate, gu, s, 2);
-    launch_pack_matrix(I, h, (const uint16_t *)in->w_up, gu + (size_t)16 * ktc, s, 2);
-  }
-  launch_pack_matrix(h, I, (const uint16_t *)in->w_down, (uint16_t *)(d + off[5]), s);
+  // One packed matrix from one or more sources: each source's rows land at 16-row block row0/16 (times
+  // nb_stride when two sources interleave block by block).  The trailer takes the largest magnitude of
+  // all of them before any is packed, so the fused matrix has one shift.
+  struct Src {
+    const void *p;
+    int rows, cols, row0, nb_stride;
+  };
+  auto pack = [&](uint16_t *dm, int rows_total, int cols, std::initializer_list<Src> srcs) {
+    const size_t tb = packed_tiles_bytes(rows_total, cols);
+    const int ktc = round_up(cols, kTileK);
+    launch_weight_trailer_clear(dm, tb, s);
+    for (const Src &x : srcs) launch_weight_absmax(x.rows, x.cols, (const uint16_t *)x.p, dm, tb, s);
+    for (const Src &x : srcs)
+      launch_pack_matrix(x.rows, x.cols, (const uint16_t *)x.p, dm + (size_t)x.row0 * ktc, tb - (size_t)x.row0 * ktc * 2,
+                         s, x.nb_stride);
+  };
+  const int kv = kv_cols(*cfg), nqkv = qkv_cols(*cfg);
+  // fused q|k|v: row blocks of wq ([h][h]), then wk and wv ([kv][h] each; every part whole 16-row blocks)
+  pack((uint16_t *)(d + off[2]), nqkv, h,
+       {{in->wq, h, h, 0, 1}, {in->wk, kv, h, h, 1}, {in->wv, kv, h, h + kv, 1}});
+  pack((uint16_t *)(d + off[3]), h, h, {{in->wo, h, h, 0, 1}});
+  // gate/up interleaved by 16-row block: block 2j = gate rows 16j.., block 2j+1 = up rows 16j..
+  pack((uint16_t *)(d + off[4]), 2 * I, h, {{in->w_gate, I, h, 0, 2}, {in->w_up, I, h, 16, 2}});
+  pack((uint16_t *)(d + off[5]), h, I, {{in->w_down, h, I, 0, 1}});
   st = check_launch("pack_layer");
   if (st != LLMDEC_OK) return st;
   out->attn_norm = d + off[0];
@@ -477,16 +451,16 @@ static llmdec_status model_step(const char *who, const llmdec_config *cfg, const
   }
   // final norm on each sequence's last new token, lm_head, argmax ([W] §1.1, [F] §2.2.3)
   const int h = cfg->hidden;
-  uint16_t *act_h = at<uint16_t>(ws, L.act_h), *act_hl = at<uint16_t>(ws, L.act_hl);
+  uint16_t *act_h = at<uint16_t>(ws, L.act_h);
   launch_rmsnorm(x, h, decode ? nullptr : cu_seqlens, n_tokens, (const uint16_t *)w->final_norm, n_seqs, h,
-                 cfg->rms_eps, at<uint32_t>(ws, L.err), nullptr, act_h, act_hl, L.kpad_h, nullptr, Splits{}, s);
+                 cfg->rms_eps, at<uint32_t>(ws, L.err), nullptr, act_h, nullptr, L.kpad_h, nullptr, Splits{}, s);
   float *lg = logits ? logits : at<float>(ws, L.logits);
   LinearOut o;
   o.kind = kStore;
   o.f32 = lg;
   o.ld = cfg->vocab;
   float *part = at<float>(ws, L.part);
-  const Splits sp = launch_linear(Act{act_h, act_hl, n_seqs, L.kpad_h, L.row_blocks}, (const uint16_t *)w->lm_head,
+  const Splits sp = launch_linear(Act{act_h, nullptr, n_seqs, L.kpad_h, L.row_blocks}, (const uint16_t *)w->lm_head,
                                   cfg->vocab, h, o, part, L.part_floats, kSplitUniform, s);  // argmax ties
   if (sp.any()) launch_reduce(part, sp, n_seqs, cfg->vocab, o, s);
   if (smp)
@@ -536,24 +510,24 @@ extern "C" llmdec_status llmdec_op_sample(const float *logits, int32_t rows, int
 
 // ------------------------------------------------------------------ single operations
 extern "C" llmdec_status llmdec_op_rmsnorm(const float *x, const void *gamma, int32_t rows, int32_t n, float eps,
-                                          float *out_f32, void *out_hi, void *out_lo, int32_t ld_packed,
+                                          float *out_f32, void *out_act, void *out_lo, int32_t ld_packed,
                                           llmdec_stream stream) {
-  if (!x || !gamma || (!out_f32 && !out_hi) || (!out_hi != !out_lo))
+  if (!x || !gamma || (!out_f32 && !out_act) || (out_lo && !out_act))
     return set_error(LLMDEC_E_INVALID, "op_rmsnorm: NULL pointer");
-  if (rows <= 0 || n <= 0 || n % 32 || n > 8192 || (out_hi && (ld_packed < n || ld_packed % 32)))
+  if (rows <= 0 || n <= 0 || n % 32 || n > 8192 || (out_act && (ld_packed < n || ld_packed % 32)))
     return set_error(LLMDEC_E_INVALID, "op_rmsnorm: rows=%d n=%d (a multiple of 32, <= 8192) ld_packed=%d out of range",
                      rows, n, ld_packed);
   launch_rmsnorm(const_cast<float *>(x), n, nullptr, rows, (const uint16_t *)gamma, rows, n, eps, nullptr, out_f32,
-                 (uint16_t *)out_hi, (uint16_t *)out_lo, ld_packed, nullptr, Splits{}, (hipStream_t)stream);
+                 (uint16_t *)out_act, (uint16_t *)out_lo, ld_packed, nullptr, Splits{}, (hipStream_t)stream);
   return check_launch("op_rmsnorm");
 }
 
-// Workspace of the stand-alone products: error word, the packed hi/lo activation, partial sums.
+// Workspace of the stand-alone products: error word, the packed fp16 activation, partial sums.
 static size_t op_linear_parts(int rows, int k, int n, size_t *act_off, size_t *part_off) {
   const int kp = round_up(k, kTileK);
   const size_t act = al((size_t)round_up(rows, 16) * kp * 2);
   *act_off = kWsHeader;
-  *part_off = *act_off + 2 * act;
+  *part_off = *act_off + 2 * act;  // room for an fp16 pair
   return *part_off + al(std::max(linear_partial_floats(rows, n, k, kSplitBalanced),
                                  linear_partial_floats(rows, n, k, kSplitUniform)) * sizeof(float));
 }
@@ -565,30 +539,32 @@ extern "C" size_t llmdec_op_linear_ws_bytes(int32_t rows, int32_t k_dim, int32_t
 }
 
 static llmdec_status run_op_linear(const char *who, const float *a, int32_t rows, int32_t k_dim, const void *w_packed,
-                                   int32_t n_dim, const LinearOut &o, void *ws, size_t ws_bytes, size_t extra,
-                                   SplitPolicy policy, hipStream_t s) {
+                                   int32_t n_dim, int parts, const LinearOut &o, void *ws, size_t ws_bytes,
+                                   size_t extra, SplitPolicy policy, hipStream_t s) {
   size_t act_off, part_off;
   const size_t need = op_linear_parts(rows, k_dim, n_dim, &act_off, &part_off) + extra;
   llmdec_status st = check_ws(ws, ws_bytes, need, who);
   if (st != LLMDEC_OK) return st;
   const int kp = round_up(k_dim, kTileK);
-  uint16_t *hi = at<uint16_t>(ws, act_off);
-  uint16_t *lo = hi + (size_t)round_up(rows, 16) * kp;
-  launch_split(a, k_dim, rows, k_dim, hi, lo, kp, s);
+  uint16_t *act = at<uint16_t>(ws, act_off);
+  uint16_t *lo = parts == 2 ? act + (size_t)round_up(rows, 16) * kp : nullptr;
+  launch_split(a, k_dim, rows, k_dim, act, lo, kp, s);
   float *part = at<float>(ws, part_off);
-  const Splits sp = launch_linear(Act{hi, lo, rows, kp, (rows + 15) / 16}, (const uint16_t *)w_packed, n_dim,
+  const Splits sp = launch_linear(Act{act, lo, rows, kp, (rows + 15) / 16}, (const uint16_t *)w_packed, n_dim,
                                   k_dim, o, part, linear_partial_floats(rows, n_dim, k_dim, policy), policy, s);
   if (sp.any()) launch_reduce(part, sp, rows, n_dim, o, s);
   return LLMDEC_OK;
 }
 
 extern "C" llmdec_status llmdec_op_linear(const float *a, int32_t rows, int32_t k_dim, const void *w_packed,
-                                         int32_t n_dim, float *out, int32_t accumulate, void *ws, size_t ws_bytes,
-                                         llmdec_stream stream) {
+                                         int32_t n_dim, float *out, int32_t accumulate, int32_t act_parts, void *ws,
+                                         size_t ws_bytes, llmdec_stream stream) {
   if (!a || !w_packed || !out) return set_error(LLMDEC_E_INVALID, "op_linear: NULL pointer");
   if (rows <= 0 || k_dim <= 0 || n_dim <= 0 || n_dim % 16)
     return set_error(LLMDEC_E_INVALID, "op_linear: rows=%d k=%d n=%d out of range (n a multiple of 16)", rows, k_dim,
                      n_dim);
+  if (act_parts != 1 && act_parts != 2)
+    return set_error(LLMDEC_E_INVALID, "op_linear: act_parts=%d must be 1 or 2", act_parts);
   LinearOut o;
   o.kind = accumulate ? kAccumulate : kStore;
   o.f32 = out;
@@ -600,28 +576,26 @@ extern "C" llmdec_status llmdec_op_linear(const float *a, int32_t rows, int32_t 
     launch_gemv(a, nullptr, 0.f, (const uint16_t *)w_packed, n_dim, k_dim, o.kind, out, (hipStream_t)stream);
     return check_launch("op_linear");
   }
-  llmdec_status st = run_op_linear("op_linear", a, rows, k_dim, w_packed, n_dim, o, ws, ws_bytes, 0, kSplitBalanced,
-                                   (hipStream_t)stream);
+  llmdec_status st = run_op_linear("op_linear", a, rows, k_dim, w_packed, n_dim, act_parts, o, ws, ws_bytes, 0,
+                                   kSplitBalanced, (hipStream_t)stream);
   return st != LLMDEC_OK ? st : check_launch("op_linear");
 }
 
 extern "C" llmdec_status llmdec_op_swiglu_linear(const float *a, int32_t rows, int32_t k_dim, const void *w_gu_packed,
-                                                int32_t inter, void *out_hi, void *out_lo, int32_t ld_packed,
+                                                int32_t inter, void *out_act, int32_t ld_packed,
                                                 void *ws, size_t ws_bytes, llmdec_stream stream) {
-  if (!a || !w_gu_packed || !out_hi || !out_lo) return set_error(LLMDEC_E_INVALID, "op_swiglu_linear: NULL pointer");
+  if (!a || !w_gu_packed || !out_act) return set_error(LLMDEC_E_INVALID, "op_swiglu_linear: NULL pointer");
   if (rows <= 0 || k_dim <= 0 || inter <= 0 || inter % 16 || ld_packed < inter || ld_packed % 32 ||
       ld_packed - inter > 16)
     return set_error(LLMDEC_E_INVALID, "op_swiglu_linear: rows=%d k=%d inter=%d ld_packed=%d out of range", rows, k_dim,
                      inter, ld_packed);
   LinearOut o;
   o.kind = kSiluMul;
-  o.act_hi = (uint16_t *)out_hi;
-  o.act_lo = (uint16_t *)out_lo;
+  o.act = (uint16_t *)out_act;
   o.act_kt = ld_packed / kTileK;
   o.act_cols = inter;
-  llmdec_status st = run_op_linear("op_swiglu_linear", a, rows, k_dim, w_gu_packed, 2 * inter, o, ws, ws_bytes, 0,
-                                   kSplitBalanced,
-                                   (hipStream_t)stream);
+  llmdec_status st = run_op_linear("op_swiglu_linear", a, rows, k_dim, w_gu_packed, 2 * inter, 1, o, ws, ws_bytes, 0,
+                                   kSplitBalanced, (hipStream_t)stream);
   return st != LLMDEC_OK ? st : check_launch("op_swiglu_linear");
 }
 
@@ -660,7 +634,7 @@ extern "C" llmdec_status llmdec_op_decode_attention(const llmdec_config *cfg, co
   uint16_t *pk, *pv;
   pool_layer(pool, layer, &pk, &pv);
   launch_decode_attention(*cfg, q, cfg->hidden, n_seqs, ctx_lens, block_tables, max_pages, pk, pv, pool->num_pages,
-                          at<float>(ws, L.attn_part), out, nullptr, nullptr, 0, at<uint32_t>(ws, L.err),
+                          at<float>(ws, L.attn_part), out, nullptr, 0, at<uint32_t>(ws, L.err),
                           (hipStream_t)stream);
   return check_launch(who);
 }
@@ -682,7 +656,7 @@ extern "C" llmdec_status llmdec_op_prefill_attention(const llmdec_config *cfg, c
   uint16_t *pk, *pv;
   pool_layer(pool, layer, &pk, &pv);
   launch_prefill_attention(*cfg, q, cfg->hidden, n_seqs, n_tokens, max_q_len, cu_seqlens, start_pos, block_tables, max_pages,
-                           pk, pv, pool->num_pages, out, nullptr, nullptr, 0, (uint32_t *)ws, (hipStream_t)stream);
+                           pk, pv, pool->num_pages, out, nullptr, 0, (uint32_t *)ws, (hipStream_t)stream);
   return check_launch(who);
 }
 
@@ -709,7 +683,7 @@ extern "C" llmdec_status llmdec_op_lm_head_argmax(const float *x, int32_t rows, 
   o.f32 = lg;
   o.ld = vocab;
   hipStream_t s = (hipStream_t)stream;
-  llmdec_status st = run_op_linear("op_lm_head_argmax", x, rows, hidden, lm_head_packed, vocab, o, ws, ws_bytes, extra,
+  llmdec_status st = run_op_linear("op_lm_head_argmax", x, rows, hidden, lm_head_packed, vocab, 1, o, ws, ws_bytes, extra,
                                    kSplitUniform, s);
   if (st != LLMDEC_OK) return st;
   launch_argmax(lg, rows, vocab, next, s);
@@ -860,7 +834,7 @@ static llmdec_status q_layer_decode(int bits, const char *who, const llmdec_conf
   launch_rope_append(c, qkv, nullptr, Splits{}, nqkv, 1, 1, nullptr, ctx_lens, block_tables, max_pages, pk, pv,
                      pool->num_pages, err, s);
   launch_decode_attention(c, qkv, nqkv, 1, ctx_lens, block_tables, max_pages, pk, pv, pool->num_pages,
-                          at<float>(ws, L.attn_part), y, nullptr, nullptr, 0, err, s);
+                          at<float>(ws, L.attn_part), y, nullptr, 0, err, s);
   launch_q_gemv(bits, y, nullptr, 0.f, (const uint8_t *)w->w_o, h, h, kAccumulate, hidden, s);
   // x += Wd (silu(Wg y) * (Wu y)),  y = RMSNorm(x)
   launch_q_gemv(bits, hidden, (const uint16_t *)w->mlp_norm, c.rms_eps, (const uint8_t *)w->w_gu, 2 * I, h, kSiluMul,

@@ -4,11 +4,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "host.h"
 #include "llmdec.h"
 
 namespace llmdec {
 
-constexpr int kPage = 16;       // tokens per KV page
 constexpr int kTileRows = 16;   // packed-matrix tile: 16 rows ...
 constexpr int kTileK = 32;      // ... x 32 columns = one 16x16x32 MFMA operand
 constexpr int kTileElems = 512; // bf16 elements per tile (1 KiB)
@@ -100,19 +100,60 @@ __device__ inline void split_bf16(float x, uint16_t &hi, uint16_t &lo) {
   lo = f32_to_bf16(x - bf16_to_f32(hi));
 }
 
-// Packs 8 values as two 16-byte bf16 runs, hi and lo parts.
-__device__ inline void split_pack8(const float *x, uint4 &hi, uint4 &lo) {
+// ---------------------------------------------------------------- fp16 activations and weights
+// Activations enter the weight products in fp16, the compute precision of the pages' minimal engine
+// ("为什么要自己动手写一个LLM推理引擎" §4.1).  Rounding is to nearest, ties to even; a magnitude beyond
+// fp16's largest finite value (65504) is clipped to it instead of overflowing to infinity, the remedy
+// "企业官网建设流程全解析" recommends for values outside fp16's range.  NaN stays NaN.
+constexpr float kF16Max = 65504.f;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ inline uint16_t f32_to_f16(float f) {
+  if (__builtin_fabsf(f) > kF16Max) f = __builtin_copysignf(kF16Max, f);
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ inline float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ inline float f16lo(uint32_t w) { return f16_to_f32((uint16_t)(w & 0xffffu)); }
+__device__ inline float f16hi(uint32_t w) { return f16_to_f32((uint16_t)(w >> 16)); }
+
+// Packs 8 values as one 16-byte run of fp16 (one lane's share of a packed activation tile).
+__device__ inline uint4 pack8_f16(const float *x) {
+  uint32_t h[4];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) h[j / 2] = f32_to_f16(x[j]) | ((uint32_t)f32_to_f16(x[j + 1]) << 16);
+  return make_uint4(h[0], h[1], h[2], h[3]);
+}
+// The same 8 values as an fp16 pair: hi = fp16(x), lo = fp16(x - hi) (the difference is exact in fp32),
+// x == hi + lo to about 2^-22 relative.
+__device__ inline void pack8_f16x2(const float *x, uint4 &hi, uint4 &lo) {
   uint32_t h[4], l[4];
 #pragma unroll
   for (int j = 0; j < 8; j += 2) {
-    uint16_t h0, l0, h1, l1;
-    split_bf16(x[j], h0, l0);
-    split_bf16(x[j + 1], h1, l1);
+    const uint16_t h0 = f32_to_f16(x[j]), h1 = f32_to_f16(x[j + 1]);
     h[j / 2] = h0 | ((uint32_t)h1 << 16);
-    l[j / 2] = l0 | ((uint32_t)l1 << 16);
+    l[j / 2] = f32_to_f16(x[j] - f16_to_f32(h0)) | ((uint32_t)f32_to_f16(x[j + 1] - f16_to_f32(h1)) << 16);
   }
   hi = make_uint4(h[0], h[1], h[2], h[3]);
   lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// A packed weight matrix holds w * 2^s in fp16, one shift s per matrix, and ends in a trailer whose
+// first word is the largest |w| as fp32 bits.  s puts that largest magnitude in [2^14, 2^15), so every
+// bf16 weight within a factor 2^31 of it is an fp16 value exactly (a bf16 significand has 8 bits, fp16
+// keeps 11, and its subnormals reach 2^-24); smaller ones round to a multiple of 2^(-24-s).  Products
+// take the fp16 values and multiply the fp32 result by 2^-s, an exact rescaling.
+constexpr size_t kWTrailer = 256;  // bytes after the tiles of a packed matrix
+__host__ __device__ inline int weight_shift(uint32_t max_abs_bits) {
+  if (max_abs_bits == 0) return 0;
+  const int e = (int)((max_abs_bits >> 23) & 0xff) - 127;  // exponent of the largest magnitude
+  const int s = 14 - e;
+  return s < -100 ? -100 : (s > 100 ? 100 : s);
+}
+// 2^-s for the packed matrix whose tiles end at w_end (its trailer), built from its exponent bits
+// (s lies in [-100, 100], so 2^-s is a normal fp32 value)
+__device__ inline float weight_unscale(const void *w_end) {
+  const uint32_t bits = *reinterpret_cast<const uint32_t *>(w_end);
+  return __uint_as_float((uint32_t)(127 - weight_shift(bits)) << 23);
 }
 
 // x = hi + mid + lo with hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid):
@@ -166,14 +207,3 @@ __device__ inline void raise_error(uint32_t *err, uint32_t bits) {
 }
 
 }  // namespace llmdec
-
-// The opaque pool handle (host side).
-struct llmdec_kv_pool {
-  llmdec_config cfg;
-  void *base;           // device base of the pool
-  size_t bytes;
-  int32_t num_pages;
-  int32_t *stack;       // free-page stack; top = stack[top-1]
-  int32_t top;
-  uint8_t *is_free;     // per page: 1 if on the free list
-};

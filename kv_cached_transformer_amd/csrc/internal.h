@@ -6,21 +6,20 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "host.h"
 #include "llmdec.h"
 
 namespace llmdec {
 
-llmdec_status set_error(llmdec_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
-llmdec_status clear_error();
-llmdec_status check_config(const llmdec_config *cfg, const char *who);
 llmdec_status check_launch(const char *who);
 
-// An activation matrix as a weight product reads it: a pair of bf16 matrices
-// hi = bf16(a), lo = bf16(a - hi) (a == hi + lo to about 2^-17 relative), both
-// in the packed tile layout, rows padded to 16 (row_blocks 16-row blocks exist
-// in the buffers), columns padded to kpad (a multiple of 32) with zeros.
+// An activation matrix as a weight product reads it: fp16 values (rounded to nearest-even from the
+// fp32 producer, clipped to +-65504) in the packed tile layout, rows padded to 16 (row_blocks 16-row
+// blocks exist in the buffer), columns padded to kpad (a multiple of 32) with zeros.  With lo set, the
+// activation is the pair hi + lo (hi = fp16(a), lo = fp16(a - hi), about 22 significant bits) and the
+// product takes both parts.
 struct Act {
-  const uint16_t *hi = nullptr;
+  const uint16_t *a = nullptr;
   const uint16_t *lo = nullptr;
   int rows = 0;
   int kpad = 0;
@@ -31,15 +30,14 @@ enum Epilogue { kStore = 0, kAccumulate = 1, kSiluMul = 2 };
 
 // Where a weight product's result goes.  kStore / kAccumulate: fp32 f32[r*ld + c]
 // (= or +=).  kSiluMul: the product's row blocks alternate gate and up; the
-// result silu(gate) * up goes, as a hi/lo pair, to the packed activation
-// act_hi/act_lo with act_kt k-tiles per row block and act_cols real columns
-// (the rest of the row is zeroed).
+// result silu(gate) * up goes, in fp16, to the packed activation act with
+// act_kt k-tiles per row block and act_cols real columns (the rest of the row
+// is zeroed).
 struct LinearOut {
   int kind = kStore;
   float *f32 = nullptr;
   int ld = 0;
-  uint16_t *act_hi = nullptr;
-  uint16_t *act_lo = nullptr;
+  uint16_t *act = nullptr;
   int act_kt = 0;
   int act_cols = 0;
 };
@@ -73,7 +71,7 @@ inline int kv_cols(const llmdec_config &c) { return c.n_kv_heads * c.head_dim; }
 
 // Workspace layout for steps of up to max_tokens tokens and max_seqs sequences.
 struct WsLayout {
-  size_t err, tok_seq, tok_pos, x, act_h, act_hl, act_i, act_il, qkv, part, attn_part, logits, total;
+  size_t err, tok_seq, tok_pos, x, act_h, act_hl, act_i, qkv, part, attn_part, logits, total;
   size_t part_floats;
   int max_tokens, max_seqs, max_pages, row_blocks, kpad_h, kpad_i, attn_slots;
 };
@@ -87,17 +85,26 @@ int decode_heads_per_wave(const llmdec_config &cfg);
 int decode_blocks_per_seq(int n_parts);
 
 // ---------------------------------------------------------------- launchers (kernels_*.hip)
-void launch_pack_matrix(int rows, int cols, const uint16_t *src, uint16_t *dst, hipStream_t s, int nb_stride = 1);
+// Packed weight matrices: bytes of the tiles of a rows x cols matrix (the trailer follows them).
+size_t packed_tiles_bytes(int rows, int cols);
+// Clear a packed matrix's trailer, then fold the largest |w| of each source matrix it will hold into
+// it (launch_weight_absmax), then pack each source (launch_pack_matrix: bf16 [rows][cols] -> fp16 tiles
+// scaled by the shift the trailer gives).  Source 16-row block nb lands at destination block
+// nb * nb_stride of the matrix at dst (nb_stride 2 interleaves two matrices block by block).
+void launch_weight_trailer_clear(uint16_t *dst, size_t tiles_bytes, hipStream_t s);
+void launch_weight_absmax(int rows, int cols, const uint16_t *src, uint16_t *dst, size_t tiles_bytes, hipStream_t s);
+void launch_pack_matrix(int rows, int cols, const uint16_t *src, uint16_t *dst, size_t tiles_bytes, hipStream_t s,
+                        int nb_stride = 1);
 void launch_embed(const uint16_t *embed, const int32_t *tokens, int n_tokens, int hidden, int vocab, float *x,
                   uint32_t *err, hipStream_t s);
-// y = rmsnorm(x) * gamma on the given rows; outputs: f32 [rows][n] and/or the packed hi/lo pair with kpad
-// columns.  add_partials (may be NULL): the partial sums [plane][rows][n] of a split output projection
+// y = rmsnorm(x) * gamma on the given rows; outputs: f32 [rows][n] and/or the packed fp16 activation with
+// kpad columns (out_lo != NULL: as the pair out_act = fp16(y), out_lo = fp16(y - out_act)).  add_partials (may be NULL): the partial sums [plane][rows][n] of a split output projection
 // (described by sp), first added into x (its residual add), x being written back.
 void launch_rmsnorm(float *x, int ld_x, const int32_t *row_index, int n_src_rows, const uint16_t *gamma, int rows,
-                    int n, float eps, uint32_t *err, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad,
+                    int n, float eps, uint32_t *err, float *out_f32, uint16_t *out_act, uint16_t *out_lo, int kpad,
                     const float *add_partials, const Splits &sp, hipStream_t s);
-// fp32 [rows][ld] -> packed hi/lo pair [rows_pad16][kpad], zero padding.
-void launch_split(const float *a, int ld, int rows, int cols, uint16_t *hi, uint16_t *lo, int kpad, hipStream_t s);
+// fp32 [rows][ld] -> packed fp16 activation [rows_pad16][kpad] (lo != NULL: the pair), zero padding.
+void launch_split(const float *a, int ld, int rows, int cols, uint16_t *act, uint16_t *lo, int kpad, hipStream_t s);
 // Weight product.  When the product is split (the returned Splits has any()), the result is left as fp32
 // partial sums [plane][rows][n] in partials and the epilogue is NOT applied: the caller reduces them, either
 // with launch_reduce or inside the next kernel.  Otherwise the epilogue is applied.
@@ -119,15 +126,15 @@ void launch_rope_append(const llmdec_config &cfg, float *qkv, const float *qkv_p
                         int n_tokens, int n_seqs, const int32_t *tok_seq,
                         const int32_t *tok_pos, const int32_t *block_tables, int max_pages, uint16_t *pool_layer_k,
                         uint16_t *pool_layer_v, int num_pages, uint32_t *err, hipStream_t s);
-// Attention outputs go to fp32 out_f32 [rows][hidden] and/or the packed hi/lo pair with kpad columns.
+// Attention outputs go to fp32 out_f32 [rows][hidden] and/or the packed fp16 activation with kpad columns.
 void launch_decode_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, const int32_t *ctx_lens,
                              const int32_t *block_tables, int max_pages, const uint16_t *pool_layer_k,
                              const uint16_t *pool_layer_v, int num_pages, float *partials, float *out_f32,
-                             uint16_t *out_hi, uint16_t *out_lo, int kpad, uint32_t *err, hipStream_t s);
+                             uint16_t *out_act, int kpad, uint32_t *err, hipStream_t s);
 void launch_prefill_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, int n_tokens, int max_q_len,
                               const int32_t *cu_seqlens, const int32_t *start_pos, const int32_t *block_tables,
                               int max_pages, const uint16_t *pool_layer_k, const uint16_t *pool_layer_v,
-                              int num_pages, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad,
+                              int num_pages, float *out_f32, uint16_t *out_act, int kpad,
                               uint32_t *err, hipStream_t s);
 // u = silu(g) * up elementwise, fp32 [rows][n] (the stand-alone operation; the layer steps fuse it
 // into the gate/up product's epilogue).
@@ -138,6 +145,8 @@ void launch_gather_kv(const uint16_t *pool_layer_k, const uint16_t *pool_layer_v
                       int head_dim, const int32_t *row, int n_tokens, uint16_t *k_out, uint16_t *v_out,
                       hipStream_t s);
 void launch_fill_u32(uint32_t *p, uint32_t value, size_t n, hipStream_t s);
+// *dst = *src (one word, device to device)
+void launch_copy_u32(const uint32_t *src, uint32_t *dst, hipStream_t s);
 
 // Rotary frequencies inv_freq[i] = theta^(-2i/D), i < D/2 (zero past), computed in double on the host.
 struct RopeFreq {

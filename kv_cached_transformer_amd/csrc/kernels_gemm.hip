@@ -1,13 +1,18 @@
 // Weight products: out[m][n] = sum_k a[m][k] * W[n][k] on the matrix cores
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+// (v_mfma_f32_16x16x32_f16, fp32 accumulation).
 //
-// The activation enters as a bf16 pair a = hi + lo (hi = bf16(a), lo =
-// bf16(a - hi), about 17 significant bits), so every product is two MFMAs,
-// hi * W + lo * W.  A single bf16 rounding of the activation would put the
-// 7B-layer output outside a 2e-2 max-abs bound against an unrounded
-// reference: a chain of four such roundings per layer turns any relative
-// difference e into an output difference of order sqrt(512 e) * 2^-9 at each
-// stage.  The pair keeps the weight product within fp32-level agreement.
+// Both operands are fp16: the activation rounded to nearest-even by its
+// producer (the pages' minimal engine computes in fp16), the weight carried
+// exactly as fp16(w * 2^s) with one shift per matrix (see weight_shift), so a
+// product is one MFMA per tile pair and its fp32 result is multiplied by 2^-s.
+// An fp16 activation keeps 11 significant bits, eight times bf16's 8: one
+// bf16 rounding at each product input would put the 7B-layer output beyond a
+// 2e-2 max-abs bound against an unrounded reference, fp16 stays well inside.
+// The q|k|v product takes its activation as an fp16 pair hi + lo (NP = 2
+// planes, two MFMAs per tile pair, about 22 bits): k and v are rounded to
+// bf16 when they enter the cache, and with single fp16 inputs about one in
+// ten of them would land on the other side of a bf16 rounding boundary than
+// an exact product's, a full bf16 step that every later token attends to.
 //
 // Both operands are in the packed tile layout (see packed_offset): a 16-row x
 // 32-column tile is 1 KiB, and lane l of a wave holds row l%16, columns
@@ -18,31 +23,28 @@
 // Two kernels:
 //   * stream_gemm (rows <= 64, decode): the weight matrix is read once from
 //     HBM and that read bounds the kernel.  A block owns 64 output columns
-//     (4 row blocks of W); its 4 waves take interleaved k-tiles of the block's
-//     k-range and keep a ring of 3 to 8 k-steps (weights and activations) in
-//     flight, 12 to 32 KiB of weights per wave.  Wave sums meet in LDS.  Narrow matrices also split k across
-//     blocks: each block then stores its fp32 partial sums and the caller adds
-//     them (launch_reduce, or the next kernel that reads the result anyway).
-//   * tiled_gemm (rows > 64, prefill): 128 x 128 output tile per block, one
-//     32-wide k-tile per LDS stage (A hi, A lo, W: 24 tiles, 24 KiB), two
-//     stages; 4 waves in 2 x 2, each 64 x 64 = 4 x 4 MFMA blocks.  Tiles are
-//     handed to the 8 XCDs in contiguous runs, row tiles innermost, so a
-//     weight tile is fetched into one XCD's L2 and reused by every row tile.
+//     per column wave (4 row blocks of W); its 4 waves take interleaved
+//     k-tiles of the block's k-range and keep a ring of 3 to 8 k-steps
+//     (weights and activations) in flight.  Wave sums meet in LDS.  Narrow
+//     matrices also split k across blocks: each block then stores its fp32
+//     partial sums and the caller adds them (launch_reduce, or the next kernel
+//     that reads the result anyway).
+//   * tiled_gemm (rows > 64, prefill): see its own comment.
 //
 // Epilogues: store fp32; add into fp32 (the residual stream); SwiGLU, where
 // W's row blocks alternate gate / up (block 2j: gate rows 16j.., block 2j+1:
 // up rows 16j..) and the kernel writes silu(g) * u straight into the packed
-// hi/lo activation of the down projection.
+// fp16 activation of the down projection.
 #include "common.h"
 #include "internal.h"
 
 namespace llmdec {
 
 __device__ inline f32x4 mfma16(const uint4 &a, const uint4 &b, f32x4 c) {
-  bf16x8 av, bv;
+  f16x8 av, bv;
   __builtin_memcpy(&av, &a, 16);
   __builtin_memcpy(&bv, &b, 16);
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, c, 0, 0, 0);
 }
 
 __device__ inline float silu_f(float g) { return g / (1.0f + expf(-g)); }
@@ -52,18 +54,10 @@ __device__ inline float silu_f(float g) { return g / (1.0f + expf(-g)); }
 __device__ inline void epi_store(const LinearOut &o, int r, int c, float v, float u) {
   if (o.kind == kSiluMul) {
     const int j = ((c >> 5) << 4) | (c & 15);  // gate column -> activation column
-    uint16_t h, l;
-    split_bf16(silu_f(v) * u, h, l);
-    const size_t off = packed_offset(r, j, o.act_kt);
-    o.act_hi[off] = h;
-    o.act_lo[off] = l;
+    o.act[packed_offset(r, j, o.act_kt)] = f32_to_f16(silu_f(v) * u);
     // the row's padding columns (act_cols .. 32*act_kt-1, fewer than 16 since act_cols % 16 == 0)
     // follow the last real 16-column block, whose writers clear them
-    if (j + 16 >= o.act_cols && j + 16 < o.act_kt * 32) {
-      const size_t pad = packed_offset(r, j + 16, o.act_kt);
-      o.act_hi[pad] = 0;
-      o.act_lo[pad] = 0;
-    }
+    if (j + 16 >= o.act_cols && j + 16 < o.act_kt * 32) o.act[packed_offset(r, j + 16, o.act_kt)] = 0;
   } else {
     float *p = o.f32 + (size_t)r * o.ld + c;
     *p = o.kind == kAccumulate ? *p + v : v;
@@ -73,8 +67,8 @@ __device__ inline void epi_store(const LinearOut &o, int r, int c, float v, floa
 // ---------------------------------------------------------------- stream_gemm (rows <= 64)
 // A block is 4 waves: WN column waves, each owning SG_NB row blocks of W (64
 // output columns), times WK = 4 / WN k-waves that take interleaved k-tiles, so
-// one step of the block covers WK k-tiles.  A k-tile's 2*MB activation tiles
-// (hi and lo of every row block) are needed by all WN column waves of its
+// one step of the block covers WK k-tiles.  A k-tile's MB activation tiles
+// (one per row block) are needed by all WN column waves of its
 // k-wave: with WN > 1 those waves fetch a share each and pass them on through
 // LDS, which divides the activation requests per weight byte by WN.  (The
 // activation tiles are L2 hits, but vector loads retire in issue order, so
@@ -83,13 +77,14 @@ __device__ inline void epi_store(const LinearOut &o, int r, int c, float v, floa
 // partials that the consumer adds.
 constexpr int SG_NB = 4;
 
-template <int MB, int WN> struct SgShape {
+template <int MB, int WN, int NP> struct SgShape {
   static constexpr int WK = 4 / WN;
-  static constexpr int NA = 2 * MB;                             // activation tiles per k-tile
+  static constexpr int NA = NP * MB;                            // activation tiles per k-tile
   static constexpr int APW = WN > 1 ? (NA + WN - 1) / WN : NA;  // of them fetched by one wave
-  // k-steps in flight per wave: as deep as about 230 registers allow (two waves per SIMD),
-  // counting the ring, the activation operands read back from LDS and the accumulators
-  static constexpr int RAW = (230 - (WN > 1 ? 8 * MB : 0) - 16 * MB) / (4 * (SG_NB + APW)) - 2;
+  // k-steps in flight per wave: as deep as about 230 registers allow (two waves per SIMD), counting the
+  // ring, the activation operands read back from LDS and the accumulators; one plane's shallower steps
+  // make deeper rings, whose addressing needs 15 registers more headroom to compile without spills
+  static constexpr int RAW = ((NP > 1 ? 230 : 215) - (WN > 1 ? 4 * NA : 0) - 16 * MB) / (4 * (SG_NB + APW)) - 2;
   static constexpr int D = RAW < 2 ? 2 : (RAW > 8 ? 8 : RAW);
   static constexpr int R = D + 1;  // ring slots: D in flight + the one being computed
   static constexpr int NSLOT = APW * WN;  // staged tiles per k-tile: slots past NA hold unread copies
@@ -107,12 +102,12 @@ template <int MB, int WN> struct SgShape {
 // (column group, k-tile) units group by group; each group segment runs the
 // ring over its k-tiles and leaves either the finished result (no split) or
 // one plane of partial sums.
-template <int MB, int WN>
-__global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__restrict__ a_hi,
+template <int MB, int WN, int NP>
+__global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__restrict__ a_act,
                                                              const uint4 *__restrict__ a_lo, int a_kt, int rows,
                                                              const uint4 *__restrict__ w, int kt_count, int n_blocks,
                                                              LinearOut o, float *__restrict__ partials, Splits sp) {
-  using S = SgShape<MB, WN>;
+  using S = SgShape<MB, WN, NP>;
   constexpr int WK = S::WK, NA = S::NA, APW = S::APW, D = S::D, R = S::R;
   constexpr bool SHARE = WN > 1;
   __shared__ uint4 lds[S::LDS_U4];
@@ -127,8 +122,9 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__rest
   // bytes, so the out-of-range marker below is always past its end.
   const uint32_t lane_bytes = (uint32_t)lane * 16u;
   const size_t a_bytes = (size_t)MB * a_kt * 1024;
-  const __amdgpu_buffer_rsrc_t hr = make_rsrc(a_hi, a_bytes), lr = make_rsrc(a_lo, a_bytes);
-  // activation tiles this wave fetches: q = cw + WN*s (hi row block q, or lo row block q - MB)
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(a_act, a_bytes), lr = make_rsrc(NP > 1 ? a_lo : a_act, a_bytes);
+  // activation tiles this wave fetches: q = cw + WN*s (row block q of the first plane, or row block q - MB
+  // of the lo plane)
   __amdgpu_buffer_rsrc_t ar[APW];
   uint32_t a_off[APW];
 #pragma unroll
@@ -177,7 +173,7 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__rest
       for (int j = 0; j < SG_NB; ++j) wb[slot][j] = buffer_load16(wr, voff, w_off[j] + koff, kLoadStream);
     };
     auto compute = [&](int slot, int i) {
-      uint4 av[NA];  // hi of row block m at m, lo at MB + m
+      uint4 av[NA];  // row block m at m, its lo part (NP = 2) at MB + m
       if constexpr (SHARE) {
         // every wave writes all its slots (a skipped write would be a branch in the ring)
         uint4 *st = lds + (size_t)((i & 1) * WK + kw) * S::NSLOT * 64;
@@ -194,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__rest
       for (int m = 0; m < MB; ++m)
 #pragma unroll
         for (int j = 0; j < SG_NB; ++j) {
-          acc[m][j] = mfma16(av[MB + m], wb[slot][j], acc[m][j]);
+          if constexpr (NP > 1) acc[m][j] = mfma16(av[MB + m], wb[slot][j], acc[m][j]);  // smaller part first
           acc[m][j] = mfma16(av[m], wb[slot][j], acc[m][j]);
         }
     };
@@ -241,6 +237,7 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__rest
       }
     }
     if (kw == 0 && nbs > 0) {
+      const float wunscale = weight_unscale(w + (size_t)n_blocks * kt_count * 64);
       if (sp.any()) {  // plane = this block's place among the blocks covering group g
         float *plane = partials + (size_t)(blockIdx.x - sp.first_block((long)g * kt_count)) * rows * n;
 #pragma unroll
@@ -250,7 +247,7 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__rest
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = m * 16 + rq + e;
-              if (r < rows && j < nbs) plane[(size_t)r * n + (nb0 + j) * 16 + cq] = acc[m][j][e];
+              if (r < rows && j < nbs) plane[(size_t)r * n + (nb0 + j) * 16 + cq] = acc[m][j][e] * wunscale;
             }
       } else {
 #pragma unroll
@@ -262,9 +259,9 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__rest
               const int r = m * 16 + rq + e, c = (nb0 + j) * 16 + cq;
               if (r >= rows || j >= nbs) continue;
               if (o.kind == kSiluMul) {
-                if ((j & 1) == 0) epi_store(o, r, c, acc[m][j][e], acc[m][j + 1][e]);
+                if ((j & 1) == 0) epi_store(o, r, c, acc[m][j][e] * wunscale, acc[m][j + 1][e] * wunscale);
               } else {
-                epi_store(o, r, c, acc[m][j][e], 0.f);
+                epi_store(o, r, c, acc[m][j][e] * wunscale, 0.f);
               }
             }
       }
@@ -274,11 +271,10 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__rest
 }
 
 // ---------------------------------------------------------------- split-k reduction
-// One thread per (row, 4 consecutive columns): sums the ks partials in split
-// order (deterministic) and applies the epilogue.  For SwiGLU the threads of
-// gate columns also read the matching up columns (16 further on).
-// One thread per 8 consecutive columns of a row for the SwiGLU epilogue, so every store is a lane's
-// 16-byte chunk of the packed hi/lo activation; one thread per 4 columns (one float4) for fp32 outputs.
+// Sums the ks partials of each output in split order (deterministic) and applies the epilogue.  One
+// thread per 8 consecutive columns of a row for the SwiGLU epilogue, so every store is a lane's
+// 16-byte chunk of the packed fp16 activation (the threads of gate columns also read the matching up
+// columns, 16 further on); one thread per 4 columns (one float4) for fp32 outputs.
 __global__ void reduce_kernel(const float *__restrict__ partials, Splits sp, int rows, int n, LinearOut o) {
   const int cpt = o.kind == kSiluMul ? 8 : 4;  // columns per thread
   const int nt = n / cpt;
@@ -299,18 +295,11 @@ __global__ void reduce_kernel(const float *__restrict__ partials, Splits sp, int
     const float y[8] = {silu_f(s0.x) * u0.x, silu_f(s0.y) * u0.y, silu_f(s0.z) * u0.z, silu_f(s0.w) * u0.w,
                         silu_f(s1.x) * u1.x, silu_f(s1.y) * u1.y, silu_f(s1.z) * u1.z, silu_f(s1.w) * u1.w};
     const int j = ((c >> 5) << 4) | (c & 15);  // gate column -> activation column (a multiple of 8)
-    uint4 h, l;
-    split_pack8(y, h, l);
-    const size_t off = packed_offset(r, j, o.act_kt);
-    *reinterpret_cast<uint4 *>(o.act_hi + off) = h;
-    *reinterpret_cast<uint4 *>(o.act_lo + off) = l;
+    *reinterpret_cast<uint4 *>(o.act + packed_offset(r, j, o.act_kt)) = pack8_f16(y);
     // the row's padding columns (act_cols .. 32*act_kt-1: none or one 16-column block) follow the last
     // real 16-column block, whose writers clear them
-    if (j + 16 >= o.act_cols && j + 16 < o.act_kt * 32) {
-      const size_t pad = packed_offset(r, j + 16, o.act_kt);
-      *reinterpret_cast<uint4 *>(o.act_hi + pad) = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4 *>(o.act_lo + pad) = make_uint4(0, 0, 0, 0);
-    }
+    if (j + 16 >= o.act_cols && j + 16 < o.act_kt * 32)
+      *reinterpret_cast<uint4 *>(o.act + packed_offset(r, j + 16, o.act_kt)) = make_uint4(0, 0, 0, 0);
   } else {
     float4 *q = reinterpret_cast<float4 *>(o.f32 + (size_t)r * o.ld + c);
     if (o.kind == kAccumulate) vadd(s0, *q);
@@ -323,148 +312,163 @@ void launch_reduce(const float *partials, const Splits &sp, int rows, int n, con
   if (total) reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(partials, sp, rows, n, o);
 }
 
-// ---------------------------------------------------------------- tiled_gemm (rows > 64)
-// Block tile MB x 16 rows by 256 columns.  The four waves sit side by side along the columns: wave w
-// owns all MB row blocks and column blocks 4w..4w+3 (4 MB accumulators of 16 x 16).  Per k-tile the
-// block needs 2 MB activation tiles (hi and lo of each row block), which every wave uses, and 16
-// weight tiles, each used by one wave only.  So activations are shared through LDS (each wave fetches
-// a quarter of them and writes them to one of two LDS stages a k-tile before they are used), while
-// weights go from memory straight into the registers of the wave that uses them.  Both sit in a
-// register ring PgShape::D k-tiles deep.  Latency is hidden by occupancy rather than ring depth: at
-// 64 rows and a 2-deep ring a wave needs under 128 registers, so four blocks share a CU and one
-// block's MFMAs run while the others wait at their barriers or on memory (measured on the 7B prefill
-// products: 5 % faster than 128-row tiles at two blocks per CU, whose 4 KiB more activation reuse per
-// k-tile does not make up for the lost occupancy).  Every tile is read through a buffer resource: a
-// row block past the operand gets an empty one, k-tiles past the end move the lane offset out of
-// range, so those loads read zeros without branches and the padded steps add nothing.
-constexpr int PG_NBW = 4;          // 16-row blocks of W per wave
-constexpr int PG_NB = 4 * PG_NBW;  // per block (256 columns)
-template <int MB> struct PgShape {
-  static constexpr int AT = 2 * MB;                  // activation tiles per k-tile (hi and lo)
-  static constexpr int APW = AT / 4;                 // of them fetched by one wave
-  static constexpr int D = 2;                        // k-tiles in flight
-  static constexpr int GM = 32 / MB;                 // row tiles per group of the block order (512 rows)
-  static constexpr size_t LDS = (size_t)2 * AT * 1024;
+// ---------------------------------------------------------------- tile_gemm (rows > 64)
+// A block is two waves side by side along the columns; each wave computes WM row blocks (16 WM rows)
+// by WNT column blocks of W (16 WNT columns), so the block tile is 16 WM x 32 WNT.  Per k-tile the
+// block needs NP * WM activation tiles, used by both waves, and each wave WNT weight tiles of its own:
+//   * activation tiles go from memory straight into LDS (buffer_load ... lds: lane l's 16 bytes land
+//     at l * 16 of the 1 KiB stage slot, which is the packed tile itself), each wave loading half of
+//     them, through S = L + 1 stages, L k-tiles ahead of the one being computed;
+//   * weight tiles go from memory into the registers of the wave that uses them, through a ring of
+//     the same L + 1 slots.
+// One step: wait until this k-tile's loads have landed (a count of the loads issued after them), a
+// barrier (both waves' halves are in LDS, and both finished reading the stage about to be refilled),
+// issue the loads of k-tile t + L into the stage and slot step t - 1 used, read this stage's
+// activation tiles from LDS and run WM * WNT * NP MFMAs.  With WM = WNT = 8 a wave keeps 256
+// accumulators, so one wave per SIMD runs; the L = 3 k-tiles in flight (about 3000 clocks of MFMA
+// work) cover the memory latency instead of other waves.
+//
+// Blocks go round-robin to the 8 XCDs, so block b takes tile (b % 8) * G/8 + b / 8 of G (a multiple of
+// 8, spare blocks exit), with tiles numbered column-major (row tiles innermost): the blocks one XCD runs
+// together cover every row tile of a few column groups, so each weight tile is fetched into that
+// XCD's L2 once and each activation k-slab serves all of them.
+template <int WM, int WNT, int NP> struct TgShape {
+  static constexpr int AT = NP * WM;       // activation tiles per k-tile (all planes)
+  static constexpr int APW = AT / 2;       // of them loaded by each wave
+  static constexpr int L = 3;              // k-tiles in flight ahead of the one computed
+  static constexpr int R = L + 1;          // LDS stages = weight ring slots
+  static constexpr int GROUP = APW + WNT;  // loads per wave per k-tile
+  static_assert((L - 1) * GROUP <= 63, "the loads in flight must fit the vmcnt counter");
+  static_assert(WNT % 2 == 0 && AT % 2 == 0, "gate/up column pairs and an even split of the activation loads");
 };
 
-template <int MB>
-__global__ __launch_bounds__(256, 4) void tiled_gemm_kernel(const uint4 *__restrict__ a_hi,
-                                                            const uint4 *__restrict__ a_lo, int a_kt, int a_blocks,
-                                                            int rows, const uint4 *__restrict__ w, int kt_count,
-                                                            int n_blocks, int tiles_m, LinearOut o) {
-  using S = PgShape<MB>;
-  constexpr int AT = S::AT, APW = S::APW, D = S::D;
-  extern __shared__ uint4 lds[];  // [2 stages][AT tiles][64 lanes]
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar control
-  // Block order: blocks go round-robin to the 8 XCDs, so each XCD takes a contiguous range of tile ids;
-  // ids run through groups of GM row tiles, row tiles innermost, so the blocks one XCD runs together
-  // share a few activation and weight slabs in its L2.
-  const int nblk = gridDim.x;
-  int t = blockIdx.x;
-  if ((nblk & 7) == 0) t = (t & 7) * (nblk >> 3) + (t >> 3);
-  const int tiles_n = nblk / tiles_m;  // the grid is exactly tiles_m * tiles_n
-  const int group = t / (S::GM * tiles_n), first_m = group * S::GM;
-  const int gm = min(S::GM, tiles_m - first_m);
-  const int r_in = t - group * S::GM * tiles_n;
-  const int tm = first_m + r_in % gm, tn = r_in / gm;
-  const int mb0 = tm * MB, nbw0 = tn * PG_NB + wave * PG_NBW;
+// A 16-byte-per-lane load from a buffer straight into LDS (lane l's bytes land at lds_addr + 16 l).
+// Issued from asm so the compiler's wait counting does not treat it as a write to every LDS location
+// (it would then wait for it before each LDS read, including reads of other stages); the callers wait
+// for these loads themselves (wait_vmcnt) and then synchronise the block before reading the stage.
+// The descriptor is built by hand: base address, stride 0, num_records bytes, the raw-buffer flags.
+__device__ inline u32x4 buffer_desc(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+// M0 is named as clobbered although the compiler reserves it: nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void load_to_lds16(const u32x4 &desc, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(desc), "s"(soff), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
-  // activation tiles this wave fetches: q = wave + 4i is the hi tile of row block q (q < MB) or the lo
-  // tile of row block q - MB; LDS holds tile q at index q
-  const uint32_t lane_bytes = (uint32_t)lane * 16u;
-  __amdgpu_buffer_rsrc_t asrc[APW];
+// s_waitcnt with only the vector-memory count set (the other counters at their maxima)
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int WM, int WNT, int NP>
+__global__ __launch_bounds__(128, 1) void tile_gemm_kernel(const uint4 *__restrict__ a_act,
+                                                           const uint4 *__restrict__ a_lo, int a_kt, int a_blocks,
+                                                           int rows, const uint4 *__restrict__ w, int kt_count,
+                                                           int n_blocks, int tiles_m, int n_tiles, LinearOut o) {
+  using S = TgShape<WM, WNT, NP>;
+  constexpr int AT = S::AT, APW = S::APW, L = S::L, R = S::R;
+  __shared__ uint4 lds[R * AT * 64];  // [R stages][AT tiles][64 lanes]
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)lds;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int per_xcd = (int)(gridDim.x >> 3);
+  const int t = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (t >= n_tiles) return;  // block-uniform: a spare block of the rounded-up grid
+  const int tm = t % tiles_m, tn = t / tiles_m;
+  const int mb0 = tm * WM, nbw0 = (tn * 2 + wave) * WNT;
+
+  // activation tiles this wave loads: q = wave * APW + i, row block mb0 + q % WM of the first plane
+  // (q < WM) or of the lo plane; a row block past the operand gets an empty resource (zeros)
+  u32x4 asrc[APW];
 #pragma unroll
   for (int i = 0; i < APW; ++i) {
-    const int q = wave + 4 * i;
-    const int rb = mb0 + (q % MB);
+    const int q = wave * APW + i;
+    const int rb = mb0 + q % WM;
     const bool ok = rb < a_blocks;
-    const uint4 *base = (q < MB ? a_hi : a_lo) + (size_t)(ok ? rb : 0) * a_kt * 64;
-    asrc[i] = make_rsrc(base, ok ? (size_t)a_kt * 1024 : 0);
+    asrc[i] = buffer_desc((q < WM ? a_act : a_lo) + (size_t)(ok ? rb : 0) * a_kt * 64, ok ? (uint32_t)a_kt * 1024u : 0u);
   }
   // this wave's weight row blocks nbw0.. through one resource (empty past the matrix; a block past the
   // last one re-reads the last, and its columns are not stored)
-  const int nbv = min(PG_NBW, n_blocks - nbw0);
+  const int nbv = min(WNT, n_blocks - nbw0);
   const __amdgpu_buffer_rsrc_t wsrc =
       make_rsrc(w + (size_t)(nbv > 0 ? nbw0 : 0) * kt_count * 64, nbv > 0 ? (size_t)nbv * kt_count * 1024 : 0);
-  uint32_t w_off[PG_NBW];
+  uint32_t w_off[WNT];
 #pragma unroll
-  for (int j = 0; j < PG_NBW; ++j) w_off[j] = (uint32_t)min(j, max(nbv - 1, 0)) * (uint32_t)kt_count * 1024u;
+  for (int j = 0; j < WNT; ++j) w_off[j] = (uint32_t)min(j, max(nbv - 1, 0)) * (uint32_t)kt_count * 1024u;
 
-  uint4 ar[D][APW], wr[D][PG_NBW];
+  const uint32_t lane_bytes = (uint32_t)lane * 16u;
+  uint4 wr[R][WNT];
+  // k-tile kt (past the end: the lane offset leaves every resource, the loads read zeros) into stage
+  // and slot `slot`: this wave's activation tiles to LDS, its weight tiles to registers
   auto fetch = [&](int slot, int kt) {
     const uint32_t voff = lane_bytes | (kt < kt_count ? 0u : 0x80000000u);
     const uint32_t koff = (uint32_t)min(kt, kt_count - 1) * 1024u;
 #pragma unroll
-    for (int i = 0; i < APW; ++i) ar[slot][i] = buffer_load16(asrc[i], voff, koff, 0);  // reused through L2
+    for (int i = 0; i < APW; ++i)
+      load_to_lds16(asrc[i], voff, koff, lds_base + (uint32_t)((slot * AT + wave * APW + i) * 1024));
 #pragma unroll
-    for (int j = 0; j < PG_NBW; ++j) wr[slot][j] = buffer_load16(wsrc, voff, w_off[j] + koff, 0);
-  };
-  auto stage = [&](int slot, int buf) {
-    uint4 *st = lds + (size_t)buf * AT * 64;
-#pragma unroll
-    for (int i = 0; i < APW; ++i) st[(size_t)(wave + 4 * i) * 64 + lane] = ar[slot][i];
+    for (int j = 0; j < WNT; ++j) wr[slot][j] = buffer_load16(wsrc, voff, w_off[j] + koff, 0);
   };
 
-  f32x4 acc[MB][PG_NBW];
+  f32x4 acc[WM][WNT];
 #pragma unroll
-  for (int m = 0; m < MB; ++m)
+  for (int m = 0; m < WM; ++m)
 #pragma unroll
-    for (int j = 0; j < PG_NBW; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int buf, int slot) {
-    const uint4 *st = lds + (size_t)buf * AT * 64;
-    uint4 ah[MB], al[MB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      ah[m] = st[(size_t)m * 64 + lane];
-      al[m] = st[(size_t)(MB + m) * 64 + lane];
-    }
-    // the lo and hi products of one accumulator are four instructions apart
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-#pragma unroll
-      for (int j = 0; j < PG_NBW; ++j) acc[m][j] = mfma16(al[m], wr[slot][j], acc[m][j]);
-#pragma unroll
-      for (int j = 0; j < PG_NBW; ++j) acc[m][j] = mfma16(ah[m], wr[slot][j], acc[m][j]);
-    }
-  };
+    for (int j = 0; j < WNT; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: k-tiles 0..D-1 in flight (k-tile j always lives in slot j % D), k-tile 0's
-  // activations staged
 #pragma unroll
-  for (int p = 0; p < D; ++p) {
+  for (int p = 0; p < L; ++p) {
     fetch(p, p);
     __builtin_amdgcn_sched_barrier(0);
   }
-  stage(0, 0);
-  __syncthreads();
-  __builtin_amdgcn_sched_barrier(0);
-  // step kt: compute k-tile kt (activations from LDS stage kt & 1, weights from slot kt % D), stage
-  // k-tile kt+1's activations into the other stage, refill the consumed slot with k-tile kt + D
-  for (int k0 = 0; k0 < kt_count; k0 += D) {  // block-uniform; steps past kt_count compute zeros
+  for (int k0 = 0; k0 < kt_count; k0 += R) {  // block-uniform; steps past kt_count compute zeros
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int kt = k0 + d;
-      compute(kt & 1, d);
-      stage((d + 1) % D, (kt + 1) & 1);
-      fetch(d, kt + D);
+    for (int d = 0; d < R; ++d) {
+      // k-tile k0 + d is in stage and slot d; the L - 1 k-tiles after it may still be in flight
+      wait_vmcnt<(L - 1) * S::GROUP>();
       __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      fetch((d + L) % R, k0 + d + L);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint4 *st = lds + (size_t)d * AT * 64;
+#pragma unroll
+      for (int m = 0; m < WM; ++m) {
+        uint4 ah = st[(size_t)m * 64 + lane], al;
+        if constexpr (NP > 1) al = st[(size_t)(WM + m) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < WNT; ++j) {
+          if constexpr (NP > 1) acc[m][j] = mfma16(al, wr[d][j], acc[m][j]);  // the smaller part first
+          acc[m][j] = mfma16(ah, wr[d][j], acc[m][j]);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
+  const float wunscale = weight_unscale(w + (size_t)n_blocks * kt_count * 64);
   const int rq = (lane >> 4) * 4, cq = lane & 15;
 #pragma unroll
-  for (int m = 0; m < MB; ++m)
+  for (int m = 0; m < WM; ++m)
 #pragma unroll
-    for (int j = 0; j < PG_NBW; ++j) {
+    for (int j = 0; j < WNT; ++j) {
       const int nb = nbw0 + j;
       if (nb >= n_blocks) continue;
       if (o.kind == kSiluMul && (j & 1)) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = (mb0 + m) * 16 + rq + e;
-        if (r < rows) epi_store(o, r, nb * 16 + cq, acc[m][j][e], o.kind == kSiluMul ? acc[m][j + 1][e] : 0.f);
+        if (r < rows)
+          epi_store(o, r, nb * 16 + cq, acc[m][j][e] * wunscale,
+                    o.kind == kSiluMul ? acc[m][j + 1][e] * wunscale : 0.f);
       }
     }
 }
@@ -523,43 +527,93 @@ size_t linear_partial_floats(int rows, int n, int k, SplitPolicy policy) {
   return (size_t)max_slots * rows * n;
 }
 
-template <int MB>
-static void launch_stream(int wn, int grid, hipStream_t s, const uint4 *ah, const uint4 *al, int a_kt, int rows,
+// Prefill tile shape (WM row blocks x WNT column blocks per wave, two waves per block).  A CU holds
+// two blocks (one wave per SIMD), so a launch runs in rounds of 512 blocks; a block's time scales with
+// its MFMAs, and smaller per-wave tiles re-read their operands more often per MFMA (relative speeds
+// below are estimates).  The shape with the least estimated time wins, larger tiles on ties.
+struct TileChoice {
+  int wm, wnt, tiles_m, tiles_n;
+};
+static TileChoice choose_tiles(int rows, int n_blocks, int planes) {
+  static const struct {
+    int wm, wnt;
+    double speed;
+  } shapes[] = {{8, 8, 1.0}, {8, 6, 0.95}, {4, 8, 0.85}, {8, 4, 0.85}, {4, 4, 0.7}};
+  const int row_blocks = (rows + 15) / 16;
+  TileChoice best{0, 0, 0, 0};
+  double best_cost = 1e300;
+  for (const auto &sh : shapes) {
+    if (planes > 1 && sh.wm * sh.wnt > 48) continue;  // 8 x 8 with both planes spills registers
+    const int tm = (row_blocks + sh.wm - 1) / sh.wm, tn = (n_blocks + 2 * sh.wnt - 1) / (2 * sh.wnt);
+    const long tiles = (long)tm * tn;
+    const double cost = (double)((tiles + 2 * kCUs - 1) / (2 * kCUs)) * sh.wm * sh.wnt / sh.speed;
+    if (cost < best_cost * 0.999) best_cost = cost, best = TileChoice{sh.wm, sh.wnt, tm, tn};
+  }
+  return best;
+}
+
+template <int WM, int WNT, int NP>
+static void launch_tile(hipStream_t s, const TileChoice &tc, const uint4 *act, const uint4 *lo, int a_kt,
+                        int a_blocks, int rows, const uint4 *w, int kt_count, int n_blocks, const LinearOut &o) {
+  const int n_tiles = tc.tiles_m * tc.tiles_n;
+  const int grid = (n_tiles + 7) / 8 * 8;
+  tile_gemm_kernel<WM, WNT, NP><<<grid, 128, 0, s>>>(act, lo, a_kt, a_blocks, rows, w,
+                                                                              kt_count, n_blocks, tc.tiles_m, n_tiles,
+                                                                              o);
+}
+
+template <int NP>
+static void launch_tiles(const TileChoice &tc, hipStream_t s, const uint4 *act, const uint4 *lo, int a_kt,
+                         int a_blocks, int rows, const uint4 *w, int kt_count, int n_blocks, const LinearOut &o) {
+  if (tc.wm == 8 && tc.wnt == 8) launch_tile<8, 8, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, kt_count, n_blocks, o);
+  else if (tc.wm == 8 && tc.wnt == 6) launch_tile<8, 6, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, kt_count, n_blocks, o);
+  else if (tc.wm == 4 && tc.wnt == 8) launch_tile<4, 8, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, kt_count, n_blocks, o);
+  else if (tc.wm == 8 && tc.wnt == 4) launch_tile<8, 4, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, kt_count, n_blocks, o);
+  else launch_tile<4, 4, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, kt_count, n_blocks, o);
+}
+
+template <int MB, int NP>
+static void launch_stream(int wn, int grid, hipStream_t s, const uint4 *act, const uint4 *lo, int a_kt, int rows,
                           const uint4 *w, int kt_count, int n_blocks, const LinearOut &o, float *partials,
                           const Splits &sp) {
   if (wn == 4)
-    stream_gemm_kernel<MB, 4><<<grid, 256, 0, s>>>(ah, al, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
+    stream_gemm_kernel<MB, 4, NP><<<grid, 256, 0, s>>>(act, lo, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
   else if (wn == 2)
-    stream_gemm_kernel<MB, 2><<<grid, 256, 0, s>>>(ah, al, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
+    stream_gemm_kernel<MB, 2, NP><<<grid, 256, 0, s>>>(act, lo, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
   else
-    stream_gemm_kernel<MB, 1><<<grid, 256, 0, s>>>(ah, al, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
+    stream_gemm_kernel<MB, 1, NP><<<grid, 256, 0, s>>>(act, lo, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
 }
 
-Splits launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const LinearOut &o, float *partials,
-                     size_t partial_floats, SplitPolicy policy, hipStream_t s) {
+template <int NP>
+static Splits launch_linear_np(const Act &a, const uint16_t *w_packed, int n, int k, const LinearOut &o,
+                               float *partials, size_t partial_floats, SplitPolicy policy, hipStream_t s) {
   const int kt_count = round_up(k, kTileK) / kTileK;
   const int n_blocks = n / 16;
   const uint4 *w = reinterpret_cast<const uint4 *>(w_packed);
-  const uint4 *ah = reinterpret_cast<const uint4 *>(a.hi), *al = reinterpret_cast<const uint4 *>(a.lo);
+  const uint4 *act = reinterpret_cast<const uint4 *>(a.a), *lo = reinterpret_cast<const uint4 *>(a.lo);
   const int a_kt = a.kpad / kTileK;
   if (a.rows <= 64) {
     StreamPlan p = stream_plan(a.rows, n, k, policy);
     if (p.sp.any() && (!partials || partial_floats < linear_partial_floats(a.rows, n, k, policy)))
       p = stream_plan(a.rows, n, k, kSplitNone);
     switch ((a.rows + 15) / 16) {
-      case 1: launch_stream<1>(p.wn, p.grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
-      case 2: launch_stream<2>(p.wn, p.grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
-      case 3: launch_stream<3>(p.wn, p.grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
-      default: launch_stream<4>(p.wn, p.grid, s, ah, al, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
+      case 1: launch_stream<1, NP>(p.wn, p.grid, s, act, lo, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
+      case 2: launch_stream<2, NP>(p.wn, p.grid, s, act, lo, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
+      case 3: launch_stream<3, NP>(p.wn, p.grid, s, act, lo, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
+      default: launch_stream<4, NP>(p.wn, p.grid, s, act, lo, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
     }
     return p.sp;
   }
-  constexpr int MB = 4;  // 64-row block tiles
-  const int tiles_n = (n_blocks + PG_NB - 1) / PG_NB;
-  const int tiles_m = (a.rows + MB * 16 - 1) / (MB * 16);
-  tiled_gemm_kernel<MB><<<tiles_m * tiles_n, 256, PgShape<MB>::LDS, s>>>(ah, al, a_kt, a.row_blocks, a.rows, w,
-                                                                         kt_count, n_blocks, tiles_m, o);
+  // tile shape: the largest tiles that still give every CU work in whole rounds where possible
+  const TileChoice tc = choose_tiles(a.rows, n_blocks, NP);
+  launch_tiles<NP>(tc, s, act, lo, a_kt, a.row_blocks, a.rows, w, kt_count, n_blocks, o);
   return Splits{};
+}
+
+Splits launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const LinearOut &o, float *partials,
+                     size_t partial_floats, SplitPolicy policy, hipStream_t s) {
+  if (a.lo) return launch_linear_np<2>(a, w_packed, n, k, o, partials, partial_floats, policy, s);
+  return launch_linear_np<1>(a, w_packed, n, k, o, partials, partial_floats, policy, s);
 }
 
 }  // namespace llmdec

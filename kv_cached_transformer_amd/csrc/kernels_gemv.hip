@@ -1,10 +1,11 @@
-// One-row weight products on the packed bf16 matrices: out[n] = sum_k x[k] * W[n][k] for a single
+// One-row weight products on the packed matrices: out[n] = sum_k x[k] * W[n][k] for a single
 // token (decode of one sequence, "大模型推理全流程解析：从权重加载到文本生成的工程实践" §2.2.2: only
 // the new token's projections are computed).
 //
 // With one row, every weight is used once, so the read of W bounds the product; the matrix cores would
-// run 15 of 16 operand rows on padding.  Here a weight becomes fp32 in one bit operation and meets x
-// in one fma, and x stays fp32 (no hi/lo rounding), staged in LDS.
+// run 15 of 16 operand rows on padding.  Here a packed weight (fp16(w * 2^s), see weight_shift) becomes
+// fp32 in one conversion and meets x in one fma; x stays fp32 (it is not rounded to fp16), staged in
+// LDS, and the sum is multiplied by 2^-s at the end.
 //
 // The matrix is read in its packed tile layout (16 rows x 32 columns per 1 KiB tile, lane l holding
 // row l%16, columns 8(l/16)..+7; a 16-row block's tiles contiguous along k).  A block owns TB whole
@@ -152,14 +153,14 @@ __global__ __launch_bounds__(kGvWaves * 64, 6) void gemv_kernel(GemvArgs a) {
     for (int b = 0; b < TB; ++b) {
       const uint4 w = wb[slot][b];
       float s = acc[b];
-      s = fmaf(x0.x, bf16lo(w.x), s);
-      s = fmaf(x0.y, bf16hi(w.x), s);
-      s = fmaf(x0.z, bf16lo(w.y), s);
-      s = fmaf(x0.w, bf16hi(w.y), s);
-      s = fmaf(x1.x, bf16lo(w.z), s);
-      s = fmaf(x1.y, bf16hi(w.z), s);
-      s = fmaf(x1.z, bf16lo(w.w), s);
-      s = fmaf(x1.w, bf16hi(w.w), s);
+      s = fmaf(x0.x, f16lo(w.x), s);
+      s = fmaf(x0.y, f16hi(w.x), s);
+      s = fmaf(x0.z, f16lo(w.y), s);
+      s = fmaf(x0.w, f16hi(w.y), s);
+      s = fmaf(x1.x, f16lo(w.z), s);
+      s = fmaf(x1.y, f16hi(w.z), s);
+      s = fmaf(x1.z, f16lo(w.w), s);
+      s = fmaf(x1.w, f16hi(w.w), s);
       acc[b] = s;
     }
   };
@@ -182,11 +183,13 @@ __global__ __launch_bounds__(kGvWaves * 64, 6) void gemv_kernel(GemvArgs a) {
   __syncthreads();
   if (threadIdx.x < 16) {  // row r of each of the block's row blocks
     const int r = threadIdx.x;
+    const float unscale = weight_unscale(a.w + (size_t)a.n_blocks * kt * 512);
     float v[TB];
 #pragma unroll
     for (int b = 0; b < TB; ++b) {
       v[b] = 0.f;
       for (int w = 0; w < kGvWaves; ++w) v[b] += part[(w * TB + b) * 16 + r];
+      v[b] *= unscale;
     }
     if (MODE == kSiluMul) {  // row block 0 holds the gate rows, row block 1 the matching up rows
       a.out[blockIdx.x * 16 + r] = gv_silu(v[0]) * v[TB - 1];

@@ -1,7 +1,9 @@
 // Small bandwidth-bound kernels: weight packing, embedding lookup, RMSNorm,
-// fp32 -> packed hi/lo pair, rotary embedding + paged KV append, SwiGLU gate,
+// fp32 -> packed fp16 activation, rotary embedding + paged KV append, SwiGLU gate,
 // argmax, and the test-only cache gather.
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "internal.h"
@@ -9,35 +11,66 @@
 namespace llmdec {
 
 // ---------------------------------------------------------------- packing
-// One thread moves the 8 elements one lane owns in one tile.  Source 16-row
-// block nb lands at destination block nb * nb_stride (nb_stride 2 interleaves
-// two matrices block by block).
+// A packed matrix holds fp16(w * 2^s) in the tile layout, then a trailer whose first word is the largest
+// |w| of every source it holds (fp32 bits); s = weight_shift(that word).  The trailer is cleared, every
+// source's largest magnitude folded in, and only then are the sources packed.
+size_t packed_tiles_bytes(int rows, int cols) { return (size_t)rows * round_up(cols, kTileK) * sizeof(uint16_t); }
+
+void launch_weight_trailer_clear(uint16_t *dst, size_t tiles_bytes, hipStream_t s) {
+  launch_fill_u32(reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(dst) + tiles_bytes), 0u, kWTrailer / 4, s);
+}
+
+// Largest finite |w| of a bf16 matrix, as the fp32 bits of |w| (non-negative floats order as integers),
+// folded into the trailer word with an atomic maximum.  Infinities and NaNs are left out.
+__global__ __launch_bounds__(256) void weight_absmax_kernel(const uint16_t *__restrict__ src, size_t n,
+                                                            uint32_t *__restrict__ out) {
+  uint32_t m = 0;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const uint32_t b = src[i] & 0x7fffu;
+    if (b < 0x7f80u) m = b > m ? b : m;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t v = (uint32_t)__shfl_xor((int)m, o, 64);
+    m = v > m ? v : m;
+  }
+  if ((threadIdx.x & 63) == 0 && m) atomicMax(out, m << 16);
+}
+
+void launch_weight_absmax(int rows, int cols, const uint16_t *src, uint16_t *dst, size_t tiles_bytes, hipStream_t s) {
+  const size_t n = (size_t)rows * cols;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 2048);
+  if (n)
+    weight_absmax_kernel<<<blocks, 256, 0, s>>>(
+        src, n, reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(dst) + tiles_bytes));
+}
+
+// One thread moves the 8 elements one lane owns in one tile: bf16 w -> fp16(w * 2^s), exact for every
+// weight within 2^31 of the matrix's largest (see weight_shift).
 __global__ void pack_matrix_kernel(int rows, int cols, int kt_count, int nb_stride, const uint16_t *__restrict__ src,
-                                   uint16_t *__restrict__ dst) {
+                                   uint16_t *__restrict__ dst, const uint32_t *__restrict__ trailer) {
   const size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t n_slots = (size_t)(rows / 16) * kt_count * 64;
   if (g >= n_slots) return;
+  const float scale = __builtin_ldexpf(1.0f, weight_shift(*trailer));
   const int lane = (int)(g & 63);
   const size_t tile = g >> 6;
   const int nb = (int)(tile / kt_count), kt = (int)(tile % kt_count);
   const int r = nb * 16 + (lane & 15);
   const int c0 = kt * 32 + (lane >> 4) * 8;
-  uint16_t v[8];
+  float v[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = (c0 + j < cols) ? src[(size_t)r * cols + c0 + j] : (uint16_t)0;
-  uint4 o;
-  o.x = v[0] | ((uint32_t)v[1] << 16);
-  o.y = v[2] | ((uint32_t)v[3] << 16);
-  o.z = v[4] | ((uint32_t)v[5] << 16);
-  o.w = v[6] | ((uint32_t)v[7] << 16);
+  for (int j = 0; j < 8; ++j) v[j] = (c0 + j < cols) ? bf16_to_f32(src[(size_t)r * cols + c0 + j]) * scale : 0.f;
   const size_t dtile = (size_t)nb * nb_stride * kt_count + kt;
-  *reinterpret_cast<uint4 *>(dst + (dtile * 64 + lane) * 8) = o;
+  *reinterpret_cast<uint4 *>(dst + (dtile * 64 + lane) * 8) = pack8_f16(v);
 }
 
-void launch_pack_matrix(int rows, int cols, const uint16_t *src, uint16_t *dst, hipStream_t s, int nb_stride) {
+void launch_pack_matrix(int rows, int cols, const uint16_t *src, uint16_t *dst, size_t tiles_bytes, hipStream_t s,
+                        int nb_stride) {
   const int kt = round_up(cols, kTileK) / kTileK;
   const size_t n = (size_t)(rows / 16) * kt * 64;
-  pack_matrix_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(rows, cols, kt, nb_stride, src, dst);
+  const uint32_t *trailer = reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(dst) + tiles_bytes);
+  if (n) pack_matrix_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(rows, cols, kt, nb_stride, src, dst, trailer);
 }
 
 // ---------------------------------------------------------------- embedding ([F] §2.2.1: row lookup)
@@ -60,7 +93,7 @@ void launch_embed(const uint16_t *embed, const int32_t *tokens, int n_tokens, in
 // y = x * (mean(x^2) + eps)^(-1/2) * gamma, eps inside the root.  One block of
 // 512 threads per row; each thread owns runs of 8 consecutive columns (up to
 // two runs: n <= 8192), kept in registers between the two passes, and each run
-// is one 16-byte chunk of the packed hi/lo output.  Columns n..kpad-1 of the packed
+// is one 16-byte chunk of the packed fp16 output.  Columns n..kpad-1 of the packed
 // output are zeroed.  With add_partials, the ks partial sums of a split-k
 // residual product are first added into x (and x written back): the residual
 // add of the output projection fused into the norm that follows it.
@@ -70,12 +103,13 @@ constexpr int kNormRuns = 2;
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(float *__restrict__ x, int ld_x,
                                                       const int32_t *__restrict__ cu_last, int n_src_rows,
                                                       const uint16_t *__restrict__ gamma, int n, float eps,
-                                                      uint32_t *err, float *out_f32, uint16_t *out_hi,
+                                                      uint32_t *err, float *out_f32, uint16_t *out_act,
                                                       uint16_t *out_lo, int kpad, const float *__restrict__ add,
                                                       Splits sp, int rows) {
   const int r = blockIdx.x;
   int src_row = cu_last ? cu_last[r + 1] - 1 : r;
-  if (src_row < 0 || src_row >= n_src_rows) {  // a bad cu_seqlens entry: flag it, read row 0 instead
+  // a bad cu_seqlens entry, or a sequence without new tokens (it has no last row): flag it, read row 0
+  if (src_row < 0 || src_row >= n_src_rows || (cu_last && cu_last[r + 1] <= cu_last[r])) {
     if (threadIdx.x == 0) raise_error(err, kErrSeq);
     src_row = 0;
   }
@@ -117,7 +151,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(float *__restrict
 #pragma unroll
   for (int it = 0; it < kNormRuns; ++it) {
     const int c0 = threadIdx.x * 8 + it * kNormThreads * 8;
-    if (c0 >= (out_hi ? kpad : n)) continue;
+    if (c0 >= (out_act ? kpad : n)) continue;
     float y[8];
     if (c0 < n) {
       const uint4 gw = *reinterpret_cast<const uint4 *>(gamma + c0);
@@ -136,26 +170,30 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(float *__restrict
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = 0.f;
     }
-    if (out_hi) {
-      uint4 h, l;
-      split_pack8(y, h, l);
+    if (out_act) {
       const size_t off = packed_offset(r, c0, kt);
-      *reinterpret_cast<uint4 *>(out_hi + off) = h;
-      *reinterpret_cast<uint4 *>(out_lo + off) = l;
+      if (out_lo) {
+        uint4 h, l;
+        pack8_f16x2(y, h, l);
+        *reinterpret_cast<uint4 *>(out_act + off) = h;
+        *reinterpret_cast<uint4 *>(out_lo + off) = l;
+      } else {
+        *reinterpret_cast<uint4 *>(out_act + off) = pack8_f16(y);
+      }
     }
   }
 }
 
 void launch_rmsnorm(float *x, int ld_x, const int32_t *cu_last, int n_src_rows, const uint16_t *gamma, int rows, int n,
-                    float eps, uint32_t *err, float *out_f32, uint16_t *out_hi, uint16_t *out_lo, int kpad,
+                    float eps, uint32_t *err, float *out_f32, uint16_t *out_act, uint16_t *out_lo, int kpad,
                     const float *add_partials, const Splits &sp, hipStream_t s) {
   if (rows > 0)
-    rmsnorm_kernel<<<rows, kNormThreads, 0, s>>>(x, ld_x, cu_last, n_src_rows, gamma, n, eps, err, out_f32, out_hi, out_lo,
-                                        kpad, add_partials, sp, rows);
+    rmsnorm_kernel<<<rows, kNormThreads, 0, s>>>(x, ld_x, cu_last, n_src_rows, gamma, n, eps, err, out_f32, out_act,
+                                                 out_lo, kpad, add_partials, sp, rows);
 }
 
-// ---------------------------------------------------------------- fp32 -> packed hi/lo pair
-__global__ void split_kernel(const float *__restrict__ a, int ld, int rows, int cols, uint16_t *hi, uint16_t *lo,
+// ---------------------------------------------------------------- fp32 -> packed fp16 activation
+__global__ void split_kernel(const float *__restrict__ a, int ld, int rows, int cols, uint16_t *act, uint16_t *lo,
                              int kpad) {
   const size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int per_row = kpad / 8;
@@ -164,27 +202,32 @@ __global__ void split_kernel(const float *__restrict__ a, int ld, int rows, int 
   float v[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = c0 + j < cols ? a[(size_t)r * ld + c0 + j] : 0.f;
-  uint4 h, l;
-  split_pack8(v, h, l);
-  const size_t o = packed_offset(r, c0, kpad >> 5);
-  *reinterpret_cast<uint4 *>(hi + o) = h;
-  *reinterpret_cast<uint4 *>(lo + o) = l;
+  const size_t off = packed_offset(r, c0, kpad >> 5);
+  if (lo) {
+    uint4 h, l;
+    pack8_f16x2(v, h, l);
+    *reinterpret_cast<uint4 *>(act + off) = h;
+    *reinterpret_cast<uint4 *>(lo + off) = l;
+  } else {
+    *reinterpret_cast<uint4 *>(act + off) = pack8_f16(v);
+  }
 }
 
-void launch_split(const float *a, int ld, int rows, int cols, uint16_t *hi, uint16_t *lo, int kpad, hipStream_t s) {
+void launch_split(const float *a, int ld, int rows, int cols, uint16_t *act, uint16_t *lo, int kpad, hipStream_t s) {
   const size_t n = (size_t)rows * (kpad / 8);
-  if (n) split_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a, ld, rows, cols, hi, lo, kpad);
+  if (n) split_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a, ld, rows, cols, act, lo, kpad);
 }
 
 // ---------------------------------------------------------------- token -> (sequence, position)
-// Sequence s owns tokens cu[s]..cu[s+1]-1; a table that is not non-decreasing
-// within [0, n_tokens], does not end at n_tokens, or a negative start is
-// flagged and that sequence's tokens are not written.
+// Sequence s owns tokens cu[s]..cu[s+1]-1; a table that is not increasing
+// within [0, n_tokens] (every sequence carries at least one new token), does
+// not end at n_tokens, or a negative start is flagged and that sequence's
+// tokens are not written.
 __global__ void token_map_kernel(const int32_t *__restrict__ cu, const int32_t *__restrict__ start, int n_seqs,
                                  int n_tokens, uint32_t *err, int32_t *tok_seq, int32_t *tok_pos) {
   const int s = blockIdx.x;
   const int b = cu[s], e = cu[s + 1], p0 = start[s];
-  const bool bad = b < 0 || e < b || e > n_tokens || p0 < 0 || (s == n_seqs - 1 && e != n_tokens) || (s == 0 && b != 0);
+  const bool bad = b < 0 || e <= b || e > n_tokens || p0 < 0 || (s == n_seqs - 1 && e != n_tokens) || (s == 0 && b != 0);
   if (bad) {
     if (threadIdx.x == 0) raise_error(err, kErrSeq);
     return;
@@ -389,6 +432,10 @@ __global__ void fill_u32_kernel(uint32_t *p, uint32_t value, size_t n) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = value;
 }
+
+__global__ void copy_u32_kernel(const uint32_t *src, uint32_t *dst) { *dst = *src; }
+
+void launch_copy_u32(const uint32_t *src, uint32_t *dst, hipStream_t s) { copy_u32_kernel<<<1, 1, 0, s>>>(src, dst); }
 
 void launch_fill_u32(uint32_t *p, uint32_t value, size_t n, hipStream_t s) {
   if (n) fill_u32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p, value, n);

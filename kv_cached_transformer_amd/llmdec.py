@@ -91,8 +91,8 @@ _SIGS = {
                                       _P, _P, _Z, _P]),
     "llmdec_op_rmsnorm": (_I, [_P, _P, _I, _I, _F, _P, _P, _P, _I, _P]),
     "llmdec_op_linear_ws_bytes": (_Z, [_I, _I, _I]),
-    "llmdec_op_linear": (_I, [_P, _I, _I, _P, _I, _P, _I, _P, _Z, _P]),
-    "llmdec_op_swiglu_linear": (_I, [_P, _I, _I, _P, _I, _P, _P, _I, _P, _Z, _P]),
+    "llmdec_op_linear": (_I, [_P, _I, _I, _P, _I, _P, _I, _I, _P, _Z, _P]),
+    "llmdec_op_swiglu_linear": (_I, [_P, _I, _I, _P, _I, _P, _I, _P, _Z, _P]),
     "llmdec_op_rope_append": (_I, [_CFG, _P, _I, _I, _P, _P, _P, _I, _P, _I, _P, _Z, _P]),
     "llmdec_op_decode_attention": (_I, [_CFG, _P, _I, _P, _P, _I, _P, _I, _P, _P, _Z, _P]),
     "llmdec_op_prefill_attention": (_I, [_CFG, _P, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, _Z, _P]),
@@ -260,20 +260,21 @@ def llmdec_model_step_greedy(cfg, mw, n_seqs, n_tokens, max_q_len, tokens, cu_se
                                           stream))
 
 
-def llmdec_op_rmsnorm(x, gamma, rows, n, eps, out_f32, out_hi=None, out_lo=None, ld_packed=0, stream=0):
-    _check(lib().llmdec_op_rmsnorm(x, gamma, rows, n, eps, out_f32, out_hi, out_lo, ld_packed, stream))
+def llmdec_op_rmsnorm(x, gamma, rows, n, eps, out_f32, out_act=None, out_lo=None, ld_packed=0, stream=0):
+    _check(lib().llmdec_op_rmsnorm(x, gamma, rows, n, eps, out_f32, out_act, out_lo, ld_packed, stream))
 
 
 def llmdec_op_linear_ws_bytes(rows, k_dim, n_dim):
     return lib().llmdec_op_linear_ws_bytes(rows, k_dim, n_dim)
 
 
-def llmdec_op_linear(a, rows, k_dim, w_packed, n_dim, out, accumulate, ws, ws_bytes, stream=0):
-    _check(lib().llmdec_op_linear(a, rows, k_dim, w_packed, n_dim, out, int(accumulate), ws, ws_bytes, stream))
+def llmdec_op_linear(a, rows, k_dim, w_packed, n_dim, out, accumulate, ws, ws_bytes, stream=0, act_parts=1):
+    _check(lib().llmdec_op_linear(a, rows, k_dim, w_packed, n_dim, out, int(accumulate), int(act_parts), ws, ws_bytes,
+                                  stream))
 
 
-def llmdec_op_swiglu_linear(a, rows, k_dim, w_gu_packed, inter, out_hi, out_lo, ld_packed, ws, ws_bytes, stream=0):
-    _check(lib().llmdec_op_swiglu_linear(a, rows, k_dim, w_gu_packed, inter, out_hi, out_lo, ld_packed, ws, ws_bytes,
+def llmdec_op_swiglu_linear(a, rows, k_dim, w_gu_packed, inter, out_act, ld_packed, ws, ws_bytes, stream=0):
+    _check(lib().llmdec_op_swiglu_linear(a, rows, k_dim, w_gu_packed, inter, out_act, ld_packed, ws, ws_bytes,
                                          stream))
 
 

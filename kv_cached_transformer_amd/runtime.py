@@ -120,29 +120,6 @@ class Pool:
     def alloc(self, tokens_needed, row: np.ndarray, n_pages: int, max_pages: int) -> int:
         return L.llmdec_kv_pool_alloc(self.handle, tokens_needed, row, n_pages, max_pages)
 
-    def layer_views(self, layer: int):
-        """(K, V) int16 device views of one layer as the library lays them out:
-        K [pages][H][16][D], V [pages][H][4][D][4] (token quarter, dim, token in quarter)."""
-        c = self.cfg
-        per = self.num_pages * c.n_kv_heads * 16 * c.head_dim
-        flat = self.buf.view(torch.int16)
-        base = layer * 2 * per
-        k = flat[base: base + per].view(self.num_pages, c.n_kv_heads, 16, c.head_dim)
-        v = flat[base + per: base + 2 * per].view(self.num_pages, c.n_kv_heads, 4, c.head_dim, 4)
-        return k, v
-
-    @staticmethod
-    def v_logical(v_raw: np.ndarray) -> np.ndarray:
-        """Device V layout [P][H][4][D][4] -> [P][H][D][16] (dim, in-page offset)."""
-        P, H, _, D, _ = v_raw.shape
-        return v_raw.transpose(0, 1, 3, 2, 4).reshape(P, H, D, 16)
-
-    @staticmethod
-    def v_raw(v_logical: np.ndarray) -> np.ndarray:
-        """[P][H][D][16] -> the device V layout [P][H][4][D][4]."""
-        P, H, D, _ = v_logical.shape
-        return np.ascontiguousarray(v_logical.reshape(P, H, D, 4, 4).transpose(0, 1, 3, 2, 4))
-
     def __del__(self):
         h = getattr(self, "handle", None)
         if h is not None and h.value:

@@ -31,6 +31,7 @@ PAGE = 16
 
 # stream ids (second key after the workload id)
 S_EMBED, S_LMHEAD, S_HIDDEN, S_CTX, S_KV, S_PROMPT, S_FREE, S_TOKENS, S_LAYER = 1, 2, 3, 4, 5, 6, 7, 8, 100
+S_FINAL_NORM = 9
 LAYER_TENSORS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 NORMS = ("attn_norm", "mlp_norm")
 BF16_ONE = np.uint16(0x3F80)
@@ -145,12 +146,16 @@ class ModelWeights:
     lm_head: np.ndarray         # [V][h]
 
 
-def model_weights(workload: int, shape: ModelShape) -> ModelWeights:
+def model_weights(workload: int, shape: ModelShape, norm_gamma: str = "ones") -> ModelWeights:
+    """norm_gamma = "ones": every RMSNorm gain 1.0; "literal": gains ~ N(0, 0.02^2) like every other
+    parameter (the final norm's from its own stream)."""
+    final = (np.full(shape.hidden, BF16_ONE, dtype=np.uint16) if norm_gamma == "ones" else
+             normal_bf16((workload, S_FINAL_NORM), (shape.hidden,), WEIGHT_STD))
     return ModelWeights(
         shape=shape,
         embed=normal_bf16((workload, S_EMBED), (shape.vocab, shape.hidden), WEIGHT_STD),
-        layers=[layer_weights(workload, l, shape) for l in range(shape.n_layers)],
-        final_norm=np.full(shape.hidden, BF16_ONE, dtype=np.uint16),
+        layers=[layer_weights(workload, l, shape, norm_gamma) for l in range(shape.n_layers)],
+        final_norm=final,
         lm_head=normal_bf16((workload, S_LMHEAD), (shape.vocab, shape.hidden), WEIGHT_STD),
     )
 
@@ -240,26 +245,6 @@ def prompt_ids(workload: int, n: int, vocab: int) -> np.ndarray:
 
 def first_tokens(workload: int, n: int, vocab: int) -> np.ndarray:
     return rng(workload, S_TOKENS).integers(0, vocab, n).astype(np.int32)
-
-
-def scatter_kv_into_pool(pool_k: np.ndarray, pool_v: np.ndarray, row: np.ndarray, k: np.ndarray, v: np.ndarray):
-    """Place a sequence's cached K/V (positions 0..n-1) into a host image of one layer's pool.
-
-    pool_k: [num_pages][Hkv][PAGE][D], pool_v: [num_pages][Hkv][D][PAGE] (uint16); row: the
-    sequence's block-table row.  Position p lives at page row[p // PAGE], in-page offset p % PAGE.
-    """
-    n = k.shape[0]
-    full = n // PAGE
-    if full:
-        pk = k[: full * PAGE].reshape(full, PAGE, k.shape[1], k.shape[2]).transpose(0, 2, 1, 3)
-        pv = v[: full * PAGE].reshape(full, PAGE, v.shape[1], v.shape[2]).transpose(0, 2, 3, 1)
-        pool_k[row[:full]] = pk
-        pool_v[row[:full]] = pv
-    rem = n - full * PAGE
-    if rem:
-        pg = row[full]
-        pool_k[pg, :, :rem, :] = k[full * PAGE:].transpose(1, 0, 2)
-        pool_v[pg, :, :, :rem] = v[full * PAGE:].transpose(1, 2, 0)
 
 
 # --- workload recipes -------------------------------------------------------------------------

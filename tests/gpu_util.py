@@ -37,6 +37,43 @@ def f32_from_bf16(b):
     return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def f64_from_f16(b):
+    return np.asarray(b, np.uint16).view(np.float16).astype(np.float64)
+
+
+def f16_ulp(x):
+    """Spacing of fp16 values at |x|: 2^(e-10) for |x| in [2^e, 2^(e+1)), 2^-24 below 2^-14."""
+    a = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.exp2(np.maximum(e, -14) - 10)
+
+
+def assert_rounded(tag, got, ref, rounder, ulp, max_flip_frac, abs_slack=0.0):
+    """got = the device's rounding of its own value of a quantity whose exact value is ref.  The device
+    value differs from ref only by fp32 arithmetic (at most abs_slack), so got equals rounder(ref)
+    except where ref lies near a rounding boundary; there it is a neighbour, within one spacing
+    ulp(ref) + abs_slack of ref (near zero the spacing is far below the fp32 error)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{tag}: non-finite values"
+    flips = got != rounder(ref)
+    far = np.abs(got - ref) > ulp(ref) + abs_slack
+    print(f"[parity] {tag}: {got.size} rounded values, {int(flips.sum())} on the other side of a rounding "
+          f"boundary (bound {max_flip_frac:.2%}), {int(far.sum())} beyond one spacing", flush=True)
+    assert not far.any(), f"{tag}: {int(far.sum())} values beyond one spacing of the exact value"
+    assert flips.sum() <= max(4, max_flip_frac * got.size), f"{tag}: {int(flips.sum())} roundings differ"
+
+
+def assert_within_rounding_bound(tag, got, exact, abs_a, abs_w, u, slack):
+    """|got - exact| <= u * (|a| |W|^T) + slack elementwise: the bound that rounding every activation
+    element a_k to relative precision u puts on sum_k a_k W[n][k] (slack covers fp32 accumulation)."""
+    bound = u * (np.asarray(abs_a, np.float64) @ np.asarray(abs_w, np.float64).T) + slack
+    d = np.abs(np.asarray(got, np.float64) - np.asarray(exact, np.float64))
+    ratio = float(np.max(d / bound)) if d.size else 0.0
+    print(f"[parity] {tag}: error / a-priori rounding bound <= {ratio:.3f}", flush=True)
+    assert np.all(d <= bound), f"{tag}: error beyond the rounding bound (ratio {ratio:.3f})"
+
+
 def banner(msg):
     print(f"[gpu-test] {msg}", flush=True)
     sys.stdout.flush()
@@ -49,15 +86,24 @@ def bf16_ulp(x):
     return np.where(a > 0, np.exp2(e - 7), 2.0 ** -133)
 
 
-def assert_stored_bf16(tag, got, ref, eps=1e-3, max_flip_frac=0.1):
+def assert_stored_bf16(tag, got, ref, eps=1e-5, max_flip_frac=0.01):
     """Values the device rounded to bf16 against the oracle's bf16 roundings of the same quantities.
 
     The device stores RNE(v_dev) and the oracle RNE(v_ref) with |v_dev - v_ref| small: the two agree
-    except where v lies near a rounding boundary, and then differ by about one ulp.  So each entry
-    must satisfy |got - ref| <= (ulp(got) + ulp(ref)) / 2 + eps, at most max_flip_frac of the
-    entries may differ at all (a systematic error such as truncation instead of nearest-even
-    rounding moves about half of them), and the relative L2 error must meet the hidden-state bound.
-    A max-abs bound does not apply: one ulp of a bf16 value near 8 is already 0.03.
+    except where v lies near a rounding boundary, and then differ by one ulp.  So each entry must
+    satisfy |got - ref| <= (ulp(got) + ulp(ref)) / 2 + eps, at most max_flip_frac of the entries may
+    differ at all (a systematic error such as truncation instead of nearest-even rounding moves about
+    half of them), and the relative L2 error must meet the hidden-state bound.  A max-abs bound does not
+    apply: one ulp of a bf16 value near 8 is already 0.03.
+
+    Defaults, for K/V computed from a layer's own input: the q|k|v product takes its input as an fp16
+    pair (about 22 bits) and accumulates in fp32, so v_dev differs from v_ref by about 1e-6 (fp32
+    accumulation over k = 4096 terms in 32-term MFMA steps, sqrt(2 * 128) * 2^-24 times a running sum
+    near 1.3, plus fp32 RMSNorm and rotation), a few times that at the largest of millions of values:
+    eps = 1e-5 covers it where the bf16 spacing is smaller (values near zero), and a value flips with
+    probability about |v_dev - v_ref| / ulp(v) ~ 1e-6 * 2^8, so 1 % bounds the flips with margin.  K/V of
+    later layers of a model depend on hidden states held to the 2e-2 / 5e-3 hidden-state bound, and those
+    tests pass wider eps and flip bounds.
     """
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)

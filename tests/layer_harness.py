@@ -6,6 +6,7 @@ import numpy as np
 import synth
 from oracle import decoder as od
 from oracle import pages as op
+from tests import pool_layout as pl
 
 
 class LayerCase:
@@ -36,27 +37,25 @@ class LayerCase:
             got = self.pool.alloc(t, self.bt[s], 0, self.max_pages)
             st, ref_n = ref_alloc.alloc(t, row, 0, self.max_pages)
             assert st == op.OK and got == ref_n and self.bt[s].tolist() == row, "allocator differs from the oracle"
-        # seeded history, written into a host image of the pool, then uploaded
-        kimg = np.full((self.num_pages, H, 16, D), 0xFFFF, np.uint16)
-        vimg = np.full((self.num_pages, H, D, 16), 0xFFFF, np.uint16)
+        # seeded history, written into host K/V blocks of the pool (the documented layout), then uploaded
+        nblk = pl.block_elems(self.num_pages, H, D)
+        kblk = np.full(nblk, 0xFFFF, np.uint16)
+        vblk = np.full(nblk, 0xFFFF, np.uint16)
         self.kv = od.ContiguousKV(1, H, D) if build_oracle else None
         for s, c in enumerate(self.ctxs):
             if c == 0:
                 continue
             k, v = synth.kv_history(workload, 0, s, c, H, D)
-            synth.scatter_kv_into_pool(kimg, vimg, self.bt[s], k, v)
+            pl.write_history(kblk, vblk, self.bt[s], k, v, H, D)
             if build_oracle:
                 self.kv.preload(0, s, od.widen_bf16(k), od.widen_bf16(v))
-        kd, vd = self.pool.layer_views(0)
-        kd.copy_(torch.from_numpy(kimg.view(np.int16)).to("cuda"))
-        vd.copy_(torch.from_numpy(R.Pool.v_raw(vimg).view(np.int16)).to("cuda"))
-        self.kimg0, self.vimg0 = kimg, vimg
+        pl.upload_layer(self.pool, 0, kblk, vblk, H, D)
+        self.kblk0, self.vblk0 = kblk, vblk
         self.bt_dev = R.dev_i32(self.bt)
 
     def workspace(self, max_tokens):
         return self.R.Workspace(self.L.llmdec_workspace_bytes(self.cfg, max_tokens, len(self.ctxs), self.max_pages))
 
-    def pool_images(self):
-        """Host images of layer 0: K [pages][H][16][D], V [pages][H][D][16] (dim, in-page offset)."""
-        k, v = self.pool.layer_views(0)
-        return self.R.host_u16(k.contiguous()), self.R.Pool.v_logical(self.R.host_u16(v.contiguous()))
+    def pool_blocks(self):
+        """Host copies of layer 0's K and V blocks (the documented layout: see tests/pool_layout.py)."""
+        return pl.host_layer(self.pool, 0, self.shape.n_kv_heads, self.shape.head_dim)

@@ -12,6 +12,7 @@ import synth
 from oracle import decoder as od
 from oracle import pages as op
 from tests.gpu_util import assert_close, assert_stored_bf16, banner, f32_from_bf16
+from tests import pool_layout as pl
 from tests.layer_harness import LayerCase
 
 pytestmark = pytest.mark.gpu
@@ -41,20 +42,20 @@ GQA7B_LAYER = synth.ModelShape(n_layers=1, hidden=4096, n_heads=32, n_kv_heads=8
 
 def check_new_slots(case, new_tokens, tag):
     """New K/V written by the step: the slot set exactly (sentinel), the values as the oracle's bf16 roundings."""
-    kimg, vimg = case.pool_images()
+    H, D = case.shape.n_kv_heads, case.shape.head_dim
+    kblk, vblk = case.pool_blocks()
     written = np.zeros((case.num_pages, 16), bool)
     got, ref = [], []
     for s, p in new_tokens:
         pg, off = op.slot_of(case.bt[s], p)
         written[pg, off] = True
-        got += [f32_from_bf16(kimg[pg, :, off, :]), f32_from_bf16(vimg[pg, :, :, off])]
+        gk, gv = pl.read_slot(kblk, vblk, pg, off, H, D)
+        got += [f32_from_bf16(gk), f32_from_bf16(gv)]
         ref += [case.kv.k[(0, s)][p], case.kv.v[(0, s)][p]]
     assert_stored_bf16(f"{tag} new K/V", np.stack(got), np.stack(ref))
     # everything else is either the seeded history (unchanged) or the 0xFFFF sentinel
-    hist = case.kimg0.transpose(0, 2, 1, 3), case.vimg0.transpose(0, 3, 1, 2)
-    now = kimg.transpose(0, 2, 1, 3), vimg.transpose(0, 3, 1, 2)
-    for a, b in zip(hist, now):
-        assert np.array_equal(a[~written], b[~written]), f"{tag}: a slot outside the new tokens changed"
+    assert pl.unwritten_equal(case.kblk0, kblk, written, H, D, "k"), f"{tag}: a K slot outside the new tokens changed"
+    assert pl.unwritten_equal(case.vblk0, vblk, written, H, D, "v"), f"{tag}: a V slot outside the new tokens changed"
 
 
 def run_decode(L, R, shape, workload, ctxs, x_in, tag):
@@ -170,5 +171,5 @@ def test_decode_bad_page_and_position_set_error_bits(L, R, n):
                               case.max_pages, case.pool.handle, ws.ptr, ws.nbytes, R.stream())
         torch.cuda.synchronize()
         assert ws.error_bits() & bit, f"error bit {bit} not set (bits {ws.error_bits()})"
-        kimg, vimg = case.pool_images()
-        assert np.array_equal(kimg, case.kimg0) and np.array_equal(vimg, case.vimg0), "a K/V slot was written"
+        kblk, vblk = case.pool_blocks()
+        assert np.array_equal(kblk, case.kblk0) and np.array_equal(vblk, case.vblk0), "a K/V slot was written"

@@ -3,11 +3,22 @@
 * The tiny 2-layer model: prefill a 32-token prompt, then 15 single-token steps (16 new tokens, 47
   cached positions, a page boundary crossed at position 32).  Every step's logits are compared; ids
   must agree wherever the oracle's top-2 gap exceeds 1e-2, and both sides are fed the oracle's token
-  (teacher forcing).
+  (teacher forcing).  Also with every RMSNorm gain drawn N(0, 0.02^2) like the other parameters (the
+  literal reading of the workload's "all weights"), and layer by layer for the prompt's prefill.
 * A 2-layer model at the 7B shapes: one decode step over 4 sequences.
-* The full 32-layer 7B-shaped decode workload over 64 sequences, checked on 4 of them.
+* The full 32-layer 7B-shaped decode workload over 64 sequences, checked on 4 of them over 25 steps
+  (the benchmark's warm-up and timed steps).
 * Continuous batching on the tiny model: prompts and decode tokens of different sequences in one
   step, a finished sequence's pages recycled for a newcomer.
+
+K/V in layer 0 of a model come from the exact embedding rows and are held to the single-layer bound
+(tests/gpu_util.assert_stored_bf16's defaults).  Later layers' K/V come from hidden states that differ
+from the oracle's within the hidden-state bound, so beyond the rounding allowance they get that bound
+(eps = 2e-2).  A relative difference e of a layer's input moves a stored value across a bf16 rounding
+boundary with probability about e |v| / ulp(v), near 1 for values close to zero; the fp16 products of
+the layers before leave e at a few 1e-4 after the RMSNorm rescales the row, and 8-9 % (tiny model) to
+19 % (7B shapes) of the later layers' values flip (measured).  Those layers are held to at most 30 %:
+a systematic rounding error such as truncation instead of nearest-even moves about half of them.
 """
 import dataclasses
 
@@ -17,6 +28,7 @@ import pytest
 import synth
 from oracle import decoder as od
 from oracle import pages as op
+from tests import pool_layout as pl
 from tests.gpu_util import MAX_ABS, assert_close, assert_stored_bf16, banner, f32_from_bf16, report
 
 pytestmark = pytest.mark.gpu
@@ -36,6 +48,11 @@ def R():
     return runtime
 
 
+def kv_bounds(layer):
+    """(eps, max_flip_frac) for stored K/V of a layer of a model (see the module doc)."""
+    return (1e-5, 0.01) if layer == 0 else (MAX_ABS, 0.3)
+
+
 class DeviceModel:
     def __init__(self, L, R, mw):
         s = mw.shape
@@ -48,12 +65,14 @@ class DeviceModel:
                                                        self.final_norm.data_ptr(), self.lm_head.ptr)
 
 
-@pytest.mark.parametrize("n_kv_heads", [4, 2])
-def test_tiny_model_greedy_generation(L, R, n_kv_heads):
-    """n_kv_heads = 2: the same model with grouped-query attention (two query heads per K/V head)."""
-    banner(f"tiny model (n_kv_heads {n_kv_heads}): prefill 32 + 15 decode steps")
+@pytest.mark.parametrize("n_kv_heads,gamma", [(4, "ones"), (2, "ones"), (4, "literal")])
+def test_tiny_model_greedy_generation(L, R, n_kv_heads, gamma):
+    """n_kv_heads = 2: the same model with grouped-query attention (two query heads per K/V head).
+    gamma = "literal": every norm gain N(0, 0.02^2); the logits then spread over a few 1e-3, so the
+    token check applies almost nowhere and the logits' relative L2 bound carries the comparison."""
+    banner(f"tiny model (n_kv_heads {n_kv_heads}, gains {gamma}): prefill 32 + 15 decode steps")
     shape = dataclasses.replace(synth.TINY, n_kv_heads=n_kv_heads)
-    mw = synth.model_weights(1, shape)
+    mw = synth.model_weights(1, shape, norm_gamma=gamma)
     dm = DeviceModel(L, R, mw)
     prompt = synth.prompt_ids(1, 32, shape.vocab)
     n_new = 16
@@ -106,20 +125,62 @@ def test_tiny_model_greedy_generation(L, R, n_kv_heads):
         feed = [ref_id]
     assert ws.error_bits() == 0
     # pool contents: every written slot agrees with the oracle's stored bf16 K/V; the rest is sentinel
+    H, D = shape.n_kv_heads, shape.head_dim
     for layer in range(shape.n_layers):
-        kd, vd = pool.layer_views(layer)
-        kimg, vimg = R.host_u16(kd.contiguous()), R.Pool.v_logical(R.host_u16(vd.contiguous()))
+        kblk, vblk = pl.host_layer(pool, layer, H, D)
         written = np.zeros((num_pages, 16), bool)
         got, ref = [], []
         for p in range(total):
             pg, off = op.slot_of(row[0], p)
             written[pg, off] = True
-            got += [f32_from_bf16(kimg[pg, :, off, :]), f32_from_bf16(vimg[pg, :, :, off])]
+            gk, gv = pl.read_slot(kblk, vblk, pg, off, H, D)
+            got += [f32_from_bf16(gk), f32_from_bf16(gv)]
             ref += [kv.k[(layer, 0)][p], kv.v[(layer, 0)][p]]
-        assert_stored_bf16(f"tiny model layer {layer} cached K/V", np.stack(got), np.stack(ref))
-        assert np.all(kimg.transpose(0, 2, 1, 3)[~written] == 0xFFFF)
-        assert np.all(vimg.transpose(0, 3, 1, 2)[~written] == 0xFFFF)
+        eps, flips = kv_bounds(layer)
+        assert_stored_bf16(f"tiny model layer {layer} cached K/V", np.stack(got), np.stack(ref), eps, flips)
+        sentinel = np.full_like(kblk, 0xFFFF)
+        assert pl.unwritten_equal(kblk, sentinel, written, H, D, "k")
+        assert pl.unwritten_equal(vblk, sentinel, written, H, D, "v")
     print(f"[parity] tiny generated ids {ids}", flush=True)
+
+
+@pytest.mark.parametrize("gamma", ["ones", "literal"])
+def test_tiny_model_prefill_hidden_per_layer(L, R, gamma):
+    """The tiny model's 32-token prompt, layer by layer: llmdec_layer_prefill on each layer in turn, the
+    device's own output feeding the next, against the oracle's residual stream after every layer (its
+    chain from the same embedding rows), and each layer's K/V in the pool."""
+    banner(f"tiny model prefill, per-layer hidden states (gains {gamma})")
+    shape = synth.TINY
+    H, D = shape.n_kv_heads, shape.head_dim
+    mw = synth.model_weights(1, shape, norm_gamma=gamma)
+    dm = DeviceModel(L, R, mw)
+    prompt = synth.prompt_ids(1, 32, shape.vocab)
+    T, max_pages, num_pages = 32, 4, 4
+    order = synth.free_order(1, num_pages)
+    pool = R.Pool(dm.cfg, num_pages, order, fill_bits=0xFFFF)
+    row = np.full((1, max_pages), -1, np.int32)
+    pool.alloc(T, row[0], 0, max_pages)
+    ws = R.Workspace(L.llmdec_workspace_bytes(dm.cfg, T, 1, max_pages))
+    x0 = od.widen_bf16(mw.embed[prompt])
+    xd = R.dev_f32(x0)
+    cu, st, bt = R.dev_i32([0, T]), R.dev_i32([0]), R.dev_i32(row)
+    ref_x = {}
+    kv = od.ContiguousKV(shape.n_layers, H, D)
+    od.model_step(shape, mw, prompt, [0] * T, list(range(T)), kv, layer_hook=lambda l, x: ref_x.__setitem__(l, x))
+    for layer in range(shape.n_layers):
+        L.llmdec_layer_prefill(dm.cfg, dm.layers[layer].struct, layer, xd.data_ptr(), 1, T, T, cu.data_ptr(),
+                               st.data_ptr(), bt.data_ptr(), max_pages, pool.handle, ws.ptr, ws.nbytes, R.stream())
+        torch.cuda.synchronize()
+        assert ws.error_bits() == 0
+        assert_close(f"tiny prefill (gains {gamma}) hidden after layer {layer}", xd.cpu().numpy(), ref_x[layer])
+        kblk, vblk = pl.host_layer(pool, layer, H, D)
+        got, ref = [], []
+        for p in range(T):
+            gk, gv = pl.read_slot(kblk, vblk, *op.slot_of(row[0], p), H, D)
+            got += [f32_from_bf16(gk), f32_from_bf16(gv)]
+            ref += [kv.k[(layer, 0)][p], kv.v[(layer, 0)][p]]
+        eps, flips = kv_bounds(layer)
+        assert_stored_bf16(f"tiny prefill (gains {gamma}) layer {layer} K/V", np.stack(got), np.stack(ref), eps, flips)
 
 
 def test_7b_shaped_model_decode_step(L, R):
@@ -146,15 +207,13 @@ def test_7b_shaped_model_decode_step(L, R):
         pool.alloc(t, bt[s], 0, max_pages)
     kv = od.ContiguousKV(shape.n_layers, H, D)
     for layer in range(shape.n_layers):
-        kimg = np.full((num_pages, H, 16, D), 0xFFFF, np.uint16)
-        vimg = np.full((num_pages, H, D, 16), 0xFFFF, np.uint16)
+        kblk = np.full(pl.block_elems(num_pages, H, D), 0xFFFF, np.uint16)
+        vblk = kblk.copy()
         for s, c in enumerate(ctxs):
             k, v = synth.kv_history(W, layer, s, c, H, D)
-            synth.scatter_kv_into_pool(kimg, vimg, bt[s], k, v)
+            pl.write_history(kblk, vblk, bt[s], k, v, H, D)
             kv.preload(layer, s, od.widen_bf16(k), od.widen_bf16(v))
-        kd, vd = pool.layer_views(layer)
-        kd.copy_(torch.from_numpy(kimg.view(np.int16)).to("cuda"))
-        vd.copy_(torch.from_numpy(R.Pool.v_raw(vimg).view(np.int16)).to("cuda"))
+        pl.upload_layer(pool, layer, kblk, vblk, H, D)
     tokens = synth.first_tokens(W, B, shape.vocab)
     toks, pos, bt_d = R.dev_i32(tokens), R.dev_i32(ctxs), R.dev_i32(bt)
     ws = R.Workspace(L.llmdec_workspace_bytes(dm.cfg, B, B, max_pages))
@@ -176,17 +235,18 @@ def test_7b_shaped_model_decode_step(L, R):
             assert ids[s] == od.greedy_token(ref[s]), f"sequence {s}: device {ids[s]} oracle {od.greedy_token(ref[s])}"
     # the step's own K/V went to each sequence's slot at position ctx, in both layers
     for layer in range(shape.n_layers):
-        kd, vd = pool.layer_views(layer)
-        kimg, vimg = R.host_u16(kd.contiguous()), R.Pool.v_logical(R.host_u16(vd.contiguous()))
+        kblk, vblk = pl.host_layer(pool, layer, H, D)
         got_kv, ref_kv = [], []
         for s, c in enumerate(ctxs):
             pg, off = op.slot_of(bt[s], c)
-            got_kv += [f32_from_bf16(kimg[pg, :, off, :]), f32_from_bf16(vimg[pg, :, :, off])]
+            gk, gv = pl.read_slot(kblk, vblk, pg, off, H, D)
+            got_kv += [f32_from_bf16(gk), f32_from_bf16(gv)]
             ref_kv += [kv.k[(layer, s)][c], kv.v[(layer, s)][c]]
-        assert_stored_bf16(f"7B-shaped model layer {layer} new K/V", np.stack(got_kv), np.stack(ref_kv))
+        eps, flips = kv_bounds(layer)
+        assert_stored_bf16(f"7B-shaped model layer {layer} new K/V", np.stack(got_kv), np.stack(ref_kv), eps, flips)
 
 
-@pytest.mark.timeout(900)
+@pytest.mark.timeout(1500)
 def test_7b_model_full_size_decode_steps(L, R):
     """The headline decode workload at its full size and in the launch configuration the benchmark
     times: the 32-layer 7B-shaped model (vocab 32000, untied lm_head) over 64 sequences whose cached
@@ -197,8 +257,9 @@ def test_7b_model_full_size_decode_steps(L, R):
     seeded ones) are checked exactly against the oracle at every step: logits, ids, and the K/V each
     step appended in every layer.  The other 60 sequences attend over a tiled seeded block.  The
     oracle follows the device's ids from step to step after checking them wherever its top-2 gap
-    exceeds 1e-2, so both sides always see the same tokens."""
-    W, B, n_steps = 5, 64, 4
+    exceeds 1e-2, so both sides always see the same tokens.  25 steps: the benchmark's 5 warm-up and
+    20 timed steps."""
+    W, B, n_steps = 5, 64, 25
     shape = synth.LLAMA7B
     H, D, V = shape.n_kv_heads, shape.head_dim, shape.vocab
     banner(f"7B 32-layer model, 64 sequences, {n_steps} greedy steps: generating weights")
@@ -228,17 +289,11 @@ def test_7b_model_full_size_decode_steps(L, R):
         flat[o:o + m].copy_(blk[:m])
     hist = {}
     for layer in range(shape.n_layers):
-        kd, vd = pool.layer_views(layer)
+        kb, vb = pl.layer_blocks(flat, layer, num_pages, H, D)
         for s in pick:
             k, v = synth.kv_history(W, layer, s, int(ctx[s]), H, D)
             hist[(layer, s)] = (k, v)
-            npg = op.pages_needed(int(ctx[s]))
-            idx = torch.from_numpy(bt[s, :npg].astype(np.int64)).to("cuda")
-            kimg = R.host_u16(kd[idx].contiguous())
-            vimg = R.Pool.v_logical(R.host_u16(vd[idx].contiguous()))
-            synth.scatter_kv_into_pool(kimg, vimg, np.arange(npg), k, v)
-            kd[idx] = torch.from_numpy(kimg.view(np.int16)).to("cuda")
-            vd[idx] = torch.from_numpy(R.Pool.v_raw(vimg).view(np.int16)).to("cuda")
+            pl.write_sequence_pages(kb, vb, num_pages, bt[s, :op.pages_needed(int(ctx[s]))], k, v, H, D)
     torch.cuda.synchronize()
 
     banner("running the greedy steps")
@@ -257,16 +312,11 @@ def test_7b_model_full_size_decode_steps(L, R):
     ids = np.stack([t.cpu().numpy() for t in toks])            # [n_steps + 1][B]
     got = logits[:, pick].cpu().numpy()                          # [n_steps][4][V]
     new_kv = {}
+    slots = [op.slot_of(bt[s], int(ctx[s]) + i) for s in pick for i in range(n_steps)]
     for layer in range(shape.n_layers):
-        kd, vd = pool.layer_views(layer)
-        kl, vl = [], []
-        for s in pick:
-            for i in range(n_steps):
-                pg, off = op.slot_of(bt[s], int(ctx[s]) + i)
-                kl.append(kd[pg, :, off, :])
-                vl.append(vd[pg, :, off // 4, :, off % 4])
-        new_kv[layer] = (R.host_u16(torch.stack(kl)), R.host_u16(torch.stack(vl)))
-    del pool, dm
+        kb, vb = pl.layer_blocks(flat, layer, num_pages, H, D)
+        new_kv[layer] = pl.gather_slots(kb, vb, slots, H, D)
+    del pool, dm, flat
     torch.cuda.empty_cache()
 
     banner("oracle, layer by layer over the checked sequences and steps")
@@ -283,6 +333,7 @@ def test_7b_model_full_size_decode_steps(L, R):
                                  [int(ctx[s]) + i for s in pick], kv)
         ref_k = np.stack([kv.k[(layer, j)][int(ctx[s]) + i] for j, s in enumerate(pick) for i in range(n_steps)])
         ref_v = np.stack([kv.v[(layer, j)][int(ctx[s]) + i] for j, s in enumerate(pick) for i in range(n_steps)])
+        print(f"[gpu-test] oracle layer {layer} done ({n_steps} steps, {len(pick)} sequences)", flush=True)
         gk, gv = new_kv[layer]
         # [K or V][sequence][step][head][dim].  Past the first step the two caches already differ: each side
         # stored its own bf16 rounding of the earlier steps' K/V, and where a value sat next to a rounding
@@ -292,7 +343,8 @@ def test_7b_model_full_size_decode_steps(L, R):
         try:
             assert_stored_bf16(f"7B 32-layer model layer {layer} appended K/V",
                                np.stack([f32_from_bf16(gk), f32_from_bf16(gv)]).reshape(2, len(pick), n_steps, H, D),
-                               np.stack([ref_k, ref_v]).reshape(2, len(pick), n_steps, H, D), eps=MAX_ABS)
+                               np.stack([ref_k, ref_v]).reshape(2, len(pick), n_steps, H, D),
+                               *kv_bounds(layer))
         except AssertionError as e:
             failures.append(str(e))
         del lw, kv
@@ -387,13 +439,16 @@ def test_tiny_model_continuous_batching(L, R):
     # the newcomer really did take the finished sequence's pages
     assert freed <= set(state[3][0][:state[3][1]].tolist())
     # every cached K/V value of the live sequences, including those written into recycled pages
+    H, D = shape.n_kv_heads, shape.head_dim
     for layer in range(shape.n_layers):
-        kd, vd = pool.layer_views(layer)
-        kimg, vimg = R.host_u16(kd.contiguous()), R.Pool.v_logical(R.host_u16(vd.contiguous()))
+        kblk, vblk = pl.host_layer(pool, layer, H, D)
         got_kv, ref_kv = [], []
         for sid, (row, npg, cached, _) in state.items():
             for p in range(cached):
                 pg, off = op.slot_of(row, p)
-                got_kv += [f32_from_bf16(kimg[pg, :, off, :]), f32_from_bf16(vimg[pg, :, :, off])]
+                gk, gv = pl.read_slot(kblk, vblk, pg, off, H, D)
+                got_kv += [f32_from_bf16(gk), f32_from_bf16(gv)]
                 ref_kv += [kv.k[(layer, sid)][p], kv.v[(layer, sid)][p]]
-        assert_stored_bf16(f"continuous batching layer {layer} cached K/V", np.stack(got_kv), np.stack(ref_kv))
+        eps, flips = kv_bounds(layer)
+        assert_stored_bf16(f"continuous batching layer {layer} cached K/V", np.stack(got_kv), np.stack(ref_kv),
+                           eps, flips)

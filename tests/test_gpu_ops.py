@@ -9,7 +9,9 @@ import pytest
 import synth
 from oracle import decoder as od
 from oracle import pages as op
-from tests.gpu_util import assert_close, assert_stored_bf16, banner, f32_from_bf16, report, unpack_tiled
+from tests import pool_layout as pl
+from tests.gpu_util import (assert_close, assert_rounded, assert_stored_bf16, assert_within_rounding_bound, banner,
+                            f16_ulp, f32_from_bf16, f64_from_f16, report, unpack_tiled)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +44,9 @@ def bf16_normal(rng, shape, std=1.0):
 # ----------------------------------------------------------------------------- RMSNorm
 @pytest.mark.parametrize("rows,n", [(1, 4096), (3, 256), (70, 4096)])
 def test_rmsnorm(L, R, rows, n):
+    """fp32 output against the oracle; the packed fp16 output is the nearest-even fp16 of the device's own
+    fp32 value, bit for bit (both roundings taken in the same precision), and the fp16 pair's lo part is
+    the rounding of what hi leaves."""
     banner(f"rmsnorm rows={rows} n={n}")
     rng = np.random.default_rng(100 + rows)
     x = (rng.standard_normal((rows, n)) * 3).astype(np.float32)
@@ -55,14 +60,19 @@ def test_rmsnorm(L, R, rows, n):
                         kpad, R.stream())
     torch.cuda.synchronize()
     ref = od.rms_norm(x, od.widen_bf16(g), 1e-6)
-    assert_close("rmsnorm f32", out.cpu().numpy(), ref, max_abs=1e-5, rel_l2=1e-6)
+    y = out.cpu().numpy().astype(np.float64)
+    assert_close("rmsnorm f32", y, ref, max_abs=1e-5, rel_l2=1e-6)
     h_full, l_full = unpack_tiled(R.host_u16(hi), rows, kpad, kpad), unpack_tiled(R.host_u16(lo), rows, kpad, kpad)
     assert np.all(h_full[:, n:] == 0) and np.all(l_full[:, n:] == 0)
-    h = f32_from_bf16(h_full[:, :n]).astype(np.float64)
-    l_ = f32_from_bf16(l_full[:, :n]).astype(np.float64)
-    # hi is the nearest-even bf16 of the device's fp32 value, bit for bit; hi + lo carries ~17 bits
-    assert np.array_equal(h, od.round_to_bf16(out.cpu().numpy().astype(np.float64)))
-    assert_close("rmsnorm hi+lo", h + l_, ref, max_abs=1e-4, rel_l2=1e-5)
+    h, l_ = f64_from_f16(h_full[:, :n]), f64_from_f16(l_full[:, :n])
+    assert np.array_equal(h, od.round_to_f16(y))
+    assert np.array_equal(l_, od.round_to_f16(y - h))
+    assert_close("rmsnorm hi+lo", h + l_, ref, max_abs=1e-5, rel_l2=1e-6)
+    # the single-plane output (as the MLP norm writes it) is the same hi plane
+    one = torch.full_like(hi, -1)
+    L.llmdec_op_rmsnorm(xd.data_ptr(), gd.data_ptr(), rows, n, 1e-6, None, one.data_ptr(), None, kpad, R.stream())
+    torch.cuda.synchronize()
+    assert torch.equal(one, hi)
 
 
 def test_rmsnorm_eps_inside_root(L, R):
@@ -75,7 +85,26 @@ def test_rmsnorm_eps_inside_root(L, R):
     assert np.allclose(out.cpu().numpy(), 1 / np.sqrt(2), rtol=1e-5)
 
 
+def test_rmsnorm_clips_beyond_f16_range(L, R):
+    """Values past fp16's largest finite value are clipped to 65504, not turned into infinities (the
+    weights article's remedy for fp16 overflow): gamma = 16384 scales a normalised row past it."""
+    x = np.zeros((1, 256), np.float32)
+    x[0, :4] = [8.0, -8.0, 0.5, 1.0]
+    g = np.full(256, 0x4680, np.uint16)  # bf16 16384: the 8.0 entry normalises to about 1.8e5
+    xd, gd = R.dev_f32(x), R.dev_u16(g)
+    out = torch.empty(1, 256, dtype=torch.float32, device="cuda")
+    act = torch.full((16 * 256,), -1, dtype=torch.int16, device="cuda")
+    L.llmdec_op_rmsnorm(xd.data_ptr(), gd.data_ptr(), 1, 256, 1e-6, out.data_ptr(), act.data_ptr(), None, 256,
+                        R.stream())
+    torch.cuda.synchronize()
+    y = out.cpu().numpy().astype(np.float64)[0]
+    h = f64_from_f16(unpack_tiled(R.host_u16(act), 1, 256, 256))[0]
+    assert abs(y[0]) > 65504 and h[0] == 65504.0 and h[1] == -65504.0
+    assert np.array_equal(h, od.round_to_f16(y))
+
+
 # ----------------------------------------------------------------------------- linear
+@pytest.mark.parametrize("parts", [1, 2])
 @pytest.mark.parametrize("rows,n,k,acc", [(1, 4096, 4096, 0), (1, 768, 688, 1), (1, 1024, 11008, 0),
                                           (5, 1376, 256, 0), (33, 256, 688, 1), (64, 4096, 4096, 0),
                                           (64, 4096, 11008, 1), (64, 32000, 4096, 0), (17, 12288, 4096, 1),
@@ -89,8 +118,14 @@ def test_rmsnorm_eps_inside_root(L, R):
                                           # one row: the widest input the one-row kernel stages (14336), the
                                           # narrowest (16), and one k-tile past it (the streaming kernel)
                                           (1, 64, 14336, 1), (1, 48, 16, 0), (1, 32, 14352, 0)])
-def test_linear(L, R, rows, n, k, acc):
-    banner(f"linear rows={rows} n={n} k={k} acc={acc}")
+def test_linear(L, R, rows, n, k, acc, parts):
+    """rows > 1 (and one row past the one-row kernel's width) take the activation in fp16 (parts = 1) or as
+    the fp16 pair (parts = 2): against the oracle fed the same rounded activation the product agrees to
+    fp32 accumulation, and against the exact product it stays inside the a-priori bound that the
+    activation rounding sets.  One row: fp32 activation, against the exact product."""
+    if rows == 1 and k <= 14336 and parts == 2:
+        pytest.skip("the one-row kernel takes the fp32 activation whatever act_parts")
+    banner(f"linear rows={rows} n={n} k={k} acc={acc} parts={parts}")
     rng = np.random.default_rng(rows * 7 + n + k)
     a = rng.standard_normal((rows, k)).astype(np.float32)
     w = bf16_normal(rng, (n, k), 0.02)
@@ -99,20 +134,62 @@ def test_linear(L, R, rows, n, k, acc):
     out = R.dev_f32(base) if acc else torch.empty(rows, n, dtype=torch.float32, device="cuda")
     ws = R.Workspace(L.llmdec_op_linear_ws_bytes(rows, k, n))
     ad = R.dev_f32(a)
-    L.llmdec_op_linear(ad.data_ptr(), rows, k, pm.ptr, n, out.data_ptr(), acc, ws.ptr, ws.nbytes, R.stream())
+    L.llmdec_op_linear(ad.data_ptr(), rows, k, pm.ptr, n, out.data_ptr(), acc, ws.ptr, ws.nbytes, R.stream(),
+                       act_parts=parts)
     torch.cuda.synchronize()
-    ref = a.astype(np.float64) @ od.widen_bf16(w).T + (base.astype(np.float64) if acc else 0)
-    assert_close(f"linear {rows}x{n}x{k}", out.cpu().numpy(), ref, max_abs=2e-4, rel_l2=1e-5)
+    W = od.widen_bf16(w)
+    add = base.astype(np.float64) if acc else 0
+    a64 = a.astype(np.float64)
+    exact = a64 @ W.T + add
+    got = out.cpu().numpy()
+    if rows == 1 and k <= 14336:
+        assert_close(f"linear {rows}x{n}x{k}", got, exact, max_abs=2e-4, rel_l2=1e-5)
+    else:
+        a_used = od.round_to_f16(a64) if parts == 1 else od.f16_pair(a64)
+        assert_close(f"linear {rows}x{n}x{k} (fp16 x{parts})", got, a_used @ W.T + add, max_abs=1e-4, rel_l2=2e-6)
+        u = 2.0 ** -11 if parts == 1 else 2.0 ** -21
+        assert_within_rounding_bound(f"linear {rows}x{n}x{k} exact", got, exact, np.abs(a64), np.abs(W), u, 1e-4)
     # a second call on the same workspace gives the same bits (split-k partials are added in a fixed order)
     out2 = R.dev_f32(base) if acc else torch.empty(rows, n, dtype=torch.float32, device="cuda")
-    L.llmdec_op_linear(ad.data_ptr(), rows, k, pm.ptr, n, out2.data_ptr(), acc, ws.ptr, ws.nbytes, R.stream())
+    L.llmdec_op_linear(ad.data_ptr(), rows, k, pm.ptr, n, out2.data_ptr(), acc, ws.ptr, ws.nbytes, R.stream(),
+                       act_parts=parts)
     torch.cuda.synchronize()
     assert torch.equal(out, out2), "the same product twice gave different bits"
+
+
+def test_linear_rejects_bad_act_parts(L, R):
+    pm = R.PackedMatrix(16, 32, np.zeros((16, 32), np.uint16))
+    ws = R.Workspace(L.llmdec_op_linear_ws_bytes(4, 32, 16))
+    a, out = torch.zeros(4, 32, device="cuda"), torch.zeros(4, 16, device="cuda")
+    with pytest.raises(L.LlmdecError):
+        L.llmdec_op_linear(a.data_ptr(), 4, 32, pm.ptr, 16, out.data_ptr(), 0, ws.ptr, ws.nbytes, R.stream(),
+                           act_parts=3)
+
+
+def test_packed_weights_exact_in_fp16(L, R):
+    """The packing carries every bf16 weight within 2^31 of the matrix's largest exactly: a one-hot
+    activation row picks one column of W, and its product is that weight (here weights spread over 2^-30
+    .. 2^1, so the largest sets the shift and the smallest are far below fp16's own normal range)."""
+    rng = np.random.default_rng(77)
+    n, k = 64, 96
+    mag = np.exp2(rng.uniform(-30, 1, (n, k))) * rng.choice([-1.0, 1.0], (n, k))
+    w = synth.f32_to_bf16_bits(mag.astype(np.float32))
+    pm = R.PackedMatrix(n, k, w)
+    a = np.eye(k, dtype=np.float32)[:80]          # 80 one-hot rows: the tiled kernel
+    out = torch.empty(80, n, dtype=torch.float32, device="cuda")
+    ws = R.Workspace(L.llmdec_op_linear_ws_bytes(80, k, n))
+    ad = R.dev_f32(a)
+    L.llmdec_op_linear(ad.data_ptr(), 80, k, pm.ptr, n, out.data_ptr(), 0, ws.ptr, ws.nbytes, R.stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), od.widen_bf16(w).T[:80])
 
 
 @pytest.mark.parametrize("rows,inter,k", [(1, 688, 256), (7, 11008, 4096), (64, 11008, 4096), (200, 688, 256),
                                           (2048, 11008, 4096)])
 def test_swiglu_linear(L, R, rows, inter, k):
+    """u = silu(g) * up, g and up the products of the fp16 activation, stored in fp16: against the oracle's
+    value from the same rounded activation, each stored value is its nearest fp16 or, near a rounding
+    boundary, the neighbour (fp32 products and silu on the device)."""
     banner(f"swiglu_linear rows={rows} inter={inter} k={k}")
     rng = np.random.default_rng(rows + inter + k)
     a = rng.standard_normal((rows, k)).astype(np.float32)
@@ -123,19 +200,20 @@ def test_swiglu_linear(L, R, rows, inter, k):
     gu.reshape(inter // 16, 2, 16, k)[:, 1] = wu.reshape(inter // 16, 16, k)
     pm = R.PackedMatrix(2 * inter, k, gu)
     ld = (inter + 31) // 32 * 32
-    hi = torch.full((((rows + 15) // 16) * 16 * ld,), -1, dtype=torch.int16, device="cuda")
-    lo = torch.full_like(hi, -1)
+    act = torch.full((((rows + 15) // 16) * 16 * ld,), -1, dtype=torch.int16, device="cuda")
     ws = R.Workspace(L.llmdec_op_linear_ws_bytes(rows, k, 2 * inter))
     ad = R.dev_f32(a)
-    L.llmdec_op_swiglu_linear(ad.data_ptr(), rows, k, pm.ptr, inter, hi.data_ptr(), lo.data_ptr(), ld, ws.ptr,
-                              ws.nbytes, R.stream())
+    L.llmdec_op_swiglu_linear(ad.data_ptr(), rows, k, pm.ptr, inter, act.data_ptr(), ld, ws.ptr, ws.nbytes,
+                              R.stream())
     torch.cuda.synchronize()
-    a64 = a.astype(np.float64)
-    ref = od.silu(a64 @ od.widen_bf16(wg).T) * (a64 @ od.widen_bf16(wu).T)
-    h_full, l_full = unpack_tiled(R.host_u16(hi), rows, ld, ld), unpack_tiled(R.host_u16(lo), rows, ld, ld)
-    assert np.all(h_full[:, inter:] == 0) and np.all(l_full[:, inter:] == 0)
-    got = f32_from_bf16(h_full[:, :inter]).astype(np.float64) + f32_from_bf16(l_full[:, :inter])
-    assert_close(f"swiglu {rows}x{inter}x{k}", got, ref, max_abs=2e-4, rel_l2=2e-5)
+    a16 = od.round_to_f16(a.astype(np.float64))
+    ref = od.silu(a16 @ od.widen_bf16(wg).T) * (a16 @ od.widen_bf16(wu).T)
+    full = unpack_tiled(R.host_u16(act), rows, ld, ld)
+    assert np.all(full[:, inter:] == 0)
+    # abs_slack: the fp32 products g and up differ from the exact ones by about sqrt(k / 32) * 2^-24 of
+    # their size (~1e-6 here), which near u = 0 exceeds fp16's spacing there
+    assert_rounded(f"swiglu {rows}x{inter}x{k}", f64_from_f16(full[:, :inter]), ref, od.round_to_f16, f16_ulp, 0.005,
+                   abs_slack=1e-5)
 
 
 # ----------------------------------------------------------------------------- RoPE + append
@@ -176,14 +254,14 @@ def test_rope_append_slots_and_values(L, R, H, D, Hk):
     assert_close("rope q", qd.cpu().numpy()[:, :h], q_ref, max_abs=1e-5, rel_l2=1e-6)
     k_ref = od.round_to_bf16(od.apply_rope(qkv[:, h:h + kv].reshape(T, Hk, D), pos, 1e4))
     v_ref = od.round_to_bf16(qkv[:, h + kv:].astype(np.float64).reshape(T, Hk, D))
-    kd, vd = pool.layer_views(0)
-    kimg, vimg = R.host_u16(kd.contiguous()), R.Pool.v_logical(R.host_u16(vd.contiguous()))
-    touched_k = np.zeros(kimg.shape[:1] + kimg.shape[2:3], bool)   # [page][slot]
+    kblk, vblk = pl.host_layer(pool, 0, Hk, D)
+    touched_k = np.zeros((num_pages, 16), bool)   # [page][slot]
     ulp_flips = 0
     for i, (s, p) in enumerate(toks):
         pg, off = op.slot_of(bt[s], p)
-        got_k = f32_from_bf16(kimg[pg, :, off, :]).astype(np.float64)
-        got_v = f32_from_bf16(vimg[pg, :, :, off]).astype(np.float64)
+        gk, gv = pl.read_slot(kblk, vblk, pg, off, Hk, D)
+        got_k = f32_from_bf16(gk).astype(np.float64)
+        got_v = f32_from_bf16(gv).astype(np.float64)
         assert np.array_equal(got_v, v_ref[i])          # plain rounding: exact
         diff = got_k != k_ref[i]
         ulp_flips += int(diff.sum())
@@ -191,9 +269,9 @@ def test_rope_append_slots_and_values(L, R, H, D, Hk):
         touched_k[pg, off] = True
     assert ulp_flips <= max(2, 0.002 * T * kv), ulp_flips
     # sentinel: every slot not written still holds 0xFFFF in both K and V
-    untouched = ~touched_k
-    assert np.all(kimg.transpose(0, 2, 1, 3)[untouched] == 0xFFFF)
-    assert np.all(vimg.transpose(0, 3, 1, 2)[untouched] == 0xFFFF)
+    sentinel = np.full_like(kblk, 0xFFFF)
+    assert pl.unwritten_equal(kblk, sentinel, touched_k, Hk, D, "k")
+    assert pl.unwritten_equal(vblk, sentinel, touched_k, Hk, D, "v")
     # the gather entry point walks the same slots
     s = 4
     n = lengths[s]
@@ -205,24 +283,30 @@ def test_rope_append_slots_and_values(L, R, H, D, Hk):
     kg, vg = R.host_u16(ko), R.host_u16(vo)
     for p in range(n):
         pg, off = op.slot_of(bt[s], p)
-        assert np.array_equal(kg[p], kimg[pg, :, off, :]) and np.array_equal(vg[p], vimg[pg, :, :, off])
+        sk, sv = pl.read_slot(kblk, vblk, pg, off, Hk, D)
+        assert np.array_equal(kg[p], sk) and np.array_equal(vg[p], sv)
 
 
 # ----------------------------------------------------------------------------- attention
 def _random_pool(L, R, shape, num_pages, rng):
+    """A pool whose every slot holds N(0, 1) bf16 values; returns the host K/V blocks (documented layout)."""
     cfg = L.make_config(shape)
     pool = R.Pool(cfg, num_pages, rng.permutation(num_pages).astype(np.int32))
-    k_img = bf16_normal(rng, (num_pages, shape.n_kv_heads, 16, shape.head_dim))
-    v_img = bf16_normal(rng, (num_pages, shape.n_kv_heads, shape.head_dim, 16))   # [page][kv head][d][offset]
-    kv, vv = pool.layer_views(0)
-    kv.copy_(R.dev_u16(k_img).view(kv.shape))
-    vv.copy_(R.dev_u16(R.Pool.v_raw(v_img)).view(vv.shape))
-    return cfg, pool, k_img, v_img
+    n = pl.block_elems(num_pages, shape.n_kv_heads, shape.head_dim)
+    kblk, vblk = bf16_normal(rng, n), bf16_normal(rng, n)
+    pl.upload_layer(pool, 0, kblk, vblk, shape.n_kv_heads, shape.head_dim)
+    return cfg, pool, kblk, vblk
 
 
-def _gather(k_img, v_img, row, n, h):
-    K = np.stack([f32_from_bf16(k_img[row[p // 16], h, p % 16, :]) for p in range(n)]).astype(np.float64)
-    V = np.stack([f32_from_bf16(v_img[row[p // 16], h, :, p % 16]) for p in range(n)]).astype(np.float64)
+def _gather(kblk, vblk, row, n, Hk, D):
+    """K[n][Hk][D], V[n][Hk][D] for positions 0..n-1, walking the block-table row."""
+    p = np.arange(n)
+    pages = np.asarray(row)[p // 16][:, None, None]
+    o = (p % 16)[:, None, None]
+    h = np.arange(Hk)[None, :, None]
+    d = np.arange(D)[None, None, :]
+    K = f32_from_bf16(kblk[pl.k_index(pages, h, o, d, Hk, D)]).astype(np.float64)
+    V = f32_from_bf16(vblk[pl.v_index(pages, h, o, d, Hk, D)]).astype(np.float64)
     return K, V
 
 
@@ -257,9 +341,9 @@ def test_decode_attention(L, R, H, D, Hk, ctxs):
     got = out.cpu().numpy()
     ref = np.empty((n, H * D))
     for s, c in enumerate(ctxs):
+        KK, VV = _gather(k_img, v_img, bt[s], c + 1, Hk, D)
         for h in range(H):
-            K, V = _gather(k_img, v_img, bt[s], c + 1, h // g)
-            ref[s, h * D:(h + 1) * D] = od.attend(q[s, h * D:(h + 1) * D], K, V)
+            ref[s, h * D:(h + 1) * D] = od.attend(q[s, h * D:(h + 1) * D], KK[:, h // g], VV[:, h // g])
     assert_close("decode attention", got, ref, max_abs=1e-4, rel_l2=1e-5)
 
 
@@ -296,8 +380,9 @@ def test_prefill_attention(L, R, H, D, Hk, seqs):
     got = out.cpu().numpy()
     ref = np.empty((T, H * D))
     for s, (s0, ln) in enumerate(seqs):
+        KK, VV = _gather(k_img, v_img, bt[s], s0 + ln, Hk, D)
         for h in range(H):
-            K, V = _gather(k_img, v_img, bt[s], s0 + ln, h // g)
+            K, V = KK[:, h // g], VV[:, h // g]
             for i in range(ln):
                 p = s0 + i
                 ref[cu[s] + i, h * D:(h + 1) * D] = od.attend(q[cu[s] + i, h * D:(h + 1) * D], K[:p + 1], V[:p + 1])
@@ -334,9 +419,12 @@ def test_lm_head_argmax(L, R, rows, vocab):
     L.llmdec_op_lm_head_argmax(x_d.data_ptr(), rows, hidden, pm.ptr, vocab, nxt.data_ptr(), logits.data_ptr(),
                                ws.ptr, ws.nbytes, R.stream())
     torch.cuda.synchronize()
-    ref = x.astype(np.float64) @ od.widen_bf16(w).T
+    W = od.widen_bf16(w)
+    x64 = x.astype(np.float64)
+    ref = x64 @ W.T
     lg = logits.cpu().numpy()
-    assert_close("lm_head logits", lg, ref, max_abs=2e-4, rel_l2=1e-5)
+    assert_close("lm_head logits (fp16 input)", lg, od.round_to_f16(x64) @ W.T, max_abs=1e-4, rel_l2=2e-6)
+    assert_within_rounding_bound("lm_head logits exact", lg, ref, np.abs(x64), np.abs(W), 2.0 ** -11, 1e-4)
     ids = nxt.cpu().numpy()
     assert ids[0] == 10                          # tie between 10 and 900 -> lowest index
     for r in range(rows):

@@ -31,14 +31,32 @@ def test_free_order_is_a_permutation():
     assert sorted(p.tolist()) == list(range(4200)) and not np.array_equal(p, np.arange(4200))
 
 
-def test_scatter_places_positions_by_block_table():
-    H, D = 2, 4
-    pk = np.zeros((5, H, 16, D), np.uint16)
-    pv = np.zeros((5, H, D, 16), np.uint16)
+def test_pool_layout_write_and_read_by_block_table():
+    """The tests' own encoding of the documented pool layout: positions land in the slot their block-table
+    row names, K as [page][h][o][d], V as [page][h][o/4][d][o%4], and read back unchanged."""
+    from tests import pool_layout as pl
+    H, D, P = 2, 8, 5
+    kb = np.zeros(pl.block_elems(P, H, D), np.uint16)
+    vb = np.zeros_like(kb)
     row = np.array([3, 0, 4], np.int32)
     n = 37
     k = np.arange(n * H * D, dtype=np.uint16).reshape(n, H, D)
-    synth.scatter_kv_into_pool(pk, pv, row, k, k + 1)
+    pl.write_history(kb, vb, row, k, k + 1, H, D)
+    kv = kb.reshape(P, H, 16, D)
+    vv = vb.reshape(P, H, 4, D, 4)
     for p in range(n):
-        assert np.array_equal(pk[row[p // 16], :, p % 16, :], k[p])
-        assert np.array_equal(pv[row[p // 16], :, :, p % 16], k[p] + 1)
+        pg, o = row[p // 16], p % 16
+        assert np.array_equal(kv[pg, :, o, :], k[p]) and np.array_equal(vv[pg, :, o // 4, :, o % 4], k[p] + 1)
+        rk, rv = pl.read_slot(kb, vb, pg, o, H, D)
+        assert np.array_equal(rk, k[p]) and np.array_equal(rv, k[p] + 1)
+    written = np.zeros((P, 16), bool)
+    for p in range(n):
+        written[row[p // 16], p % 16] = True
+    assert pl.unwritten_equal(kb, np.zeros_like(kb), written, H, D, "k")
+    assert not pl.unwritten_equal(kb, np.zeros_like(kb), np.zeros((P, 16), bool), H, D, "k")
+
+
+def test_literal_gamma_model_weights():
+    mw = synth.model_weights(1, synth.TINY, norm_gamma="literal")
+    g = np.concatenate([synth.bf16_bits_to_f32(mw.layers[0]["attn_norm"]), synth.bf16_bits_to_f32(mw.final_norm)])
+    assert abs(g.std() - 0.02) < 0.004 and not np.array_equal(mw.final_norm, mw.layers[0]["attn_norm"])

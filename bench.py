@@ -529,6 +529,61 @@ def cpu_baseline(ctx):
                         f"{t_head:.2f} s; tokens/s = 4 / (32 * t_layer + t_head)"))
 
 
+def cpu_configs():
+    """The oracle on each workload as the GPU runs it (inputs from the same seeded generators): C1 the whole
+    generation (32-token prefill, 15 decode steps), C2 and C3 one layer decode step, C4 one layer prefill;
+    C1 and C2 again on one BLAS thread.  Rates: generated tokens/s (C1), layer-steps/s and tokens/s (C2, C3),
+    prompt tokens/s (C4)."""
+    import numpy as np
+    import synth
+    from oracle import decoder as od
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threadpool_limits, blas = None, None
+
+    def c1():
+        mw = synth.model_weights(1, synth.TINY)
+        kv = od.ContiguousKV(synth.TINY.n_layers, synth.TINY.n_kv_heads, synth.TINY.head_dim)
+        t0 = time.perf_counter()
+        od.greedy_generate(synth.TINY, mw, synth.prompt_ids(1, 32, synth.TINY.vocab), 16, kv)
+        return time.perf_counter() - t0
+
+    def layer(workload, ctxs, lens):
+        shape = synth.LLAMA7B_LAYER
+        lw = synth.layer_weights(workload, 0, shape)
+        kv = od.ContiguousKV(1, shape.n_kv_heads, shape.head_dim)
+        for s, c in enumerate(ctxs):
+            if c:
+                k, v = synth.kv_history(workload, 0, s, int(c), shape.n_kv_heads, shape.head_dim)
+                kv.preload(0, s, od.widen_bf16(k), od.widen_bf16(v))
+        x = synth.hidden_input(workload, int(sum(lens)), shape.hidden)
+        seqs = np.repeat(np.arange(len(lens)), lens)
+        pos = np.concatenate([np.arange(c, c + n) for c, n in zip(ctxs, lens)])
+        t0 = time.perf_counter()
+        od.layer_step(shape, lw.tensors, 0, x, seqs, pos, kv)
+        return time.perf_counter() - t0
+
+    c2 = lambda: layer(2, [2048], [1])
+    ctx3 = synth.context_lengths(3, 32, 128, 4096)
+    out = {"affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": blas}
+    t = c1()
+    out["c1"] = dict(workload="tiny-2L-h256-prefill32-greedy16", s=t, tokens_per_s=16 / t)
+    t = c2()
+    out["c2"] = dict(workload="7B-layer-decode-b1-ctx2048", s=t, layer_steps_per_s=1 / t)
+    t = layer(3, ctx3, [1] * 32)
+    out["c3"] = dict(workload="7B-layer-decode-b32-ctx128..4096", s=t, layer_steps_per_s=1 / t, tokens_per_s=32 / t)
+    t = layer(4, [0] * 4, [512] * 4)
+    out["c4"] = dict(workload="7B-layer-prefill-4x512", s=t, tokens_per_s=2048 / t)
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1, user_api="blas"):
+            t1, t2 = c1(), c2()
+        out["c1"]["one_thread"] = dict(s=t1, tokens_per_s=16 / t1)
+        out["c2"]["one_thread"] = dict(s=t2, layer_steps_per_s=1 / t2)
+    return out
+
+
 # ----------------------------------------------------------------------------- main
 # ----------------------------------------------------------------------------- counter calibration and summaries
 def bench_copy(torch):
@@ -703,6 +758,9 @@ def main():
     if head is not None and not args.no_cpu:
         log("cpu_baseline: timing the oracle on a 4-sequence sample")
         cpu = cpu_baseline(head["ctx"])
+        log("cpu_baseline: timing the oracle on the one-layer and tiny workloads")
+        cpu["configs"] = cpu_configs()
+        cpu["affinity_cores"] = cpu["configs"]["affinity_cores"]
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"] if head else None,

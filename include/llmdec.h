@@ -34,13 +34,16 @@
  *  - bf16 means IEEE-754 binary32 truncated to its top 16 bits; rounding into
  *    bf16 is to nearest, ties to even.
  *  - Precision: weights and cached K/V are bf16 (the K/V values rounded to
- *    nearest-even when appended).  Activations entering a weight product are
- *    rounded to fp16 (nearest-even; magnitudes beyond 65504 clipped to it),
- *    the compute precision of [E] §4.1's minimal engine, and multiply the
- *    weights on the matrix cores in fp16 with fp32 accumulation: the packing
- *    carries each bf16 weight exactly as an fp16 value times a power of two
- *    (see llmdec_pack_matrix).  The residual stream, attention (scores,
- *    softmax, weighted sum) and logits are fp32.  The products of a
+ *    nearest-even when appended).  Activations entering a weight product on
+ *    the matrix cores are fp16 (nearest-even; magnitudes beyond 65504 clipped
+ *    to it), the compute precision of [E] §4.1's minimal engine, and multiply
+ *    the weights in fp16 with fp32 accumulation: the packing carries each bf16
+ *    weight exactly as an fp16 value times a power of two (see
+ *    llmdec_pack_matrix).  The q|k|v product, and every product of a step of
+ *    at most 64 new tokens (decode), take the activation as an fp16 pair
+ *    hi + lo (about 22 bits); the o, gate/up and down products of a longer
+ *    step (prefill) take one fp16 value.  The residual stream, attention
+ *    (scores, softmax, weighted sum) and logits are fp32.  The products of a
  *    single-sequence decode step (one row) and those with group-quantized
  *    weights take the unrounded fp32 activation instead.
  *  - Not thread-safe per pool handle; distinct handles are independent.
@@ -281,14 +284,17 @@ llmdec_status llmdec_op_linear(const float *a, int32_t rows, int32_t k_dim, cons
 /* The gate/up product with the SwiGLU epilogue, as the layer steps run it
  * ([W] §1.2, [E] §4.2): for a fused gate/up matrix as llmdec_pack_layer lays
  * it out (16-row blocks alternating gate and up, 2*inter rows), writes
- * u[m][j] = silu(g[m][j]) * up[m][j], g and up the fp32 products, as fp16
+ * u[m][j] = silu(g[m][j]) * up[m][j], g and up the fp32 products, in fp16
  * into out_act, in the packed layout of a [round_up(rows,16)][ld_packed]
  * matrix (inter <= ld_packed <= inter + 16, ld_packed a multiple of 32;
- * columns inter.. zeroed).  ws as for llmdec_op_linear with n_dim =
- * 2*inter. */
+ * columns inter.. zeroed).  act_parts = 1: the input a enters rounded to fp16
+ * (a prefill's gate/up product); act_parts = 2: a enters as the fp16 pair and
+ * u is written as the pair out_act + out_lo (out_lo in the same layout), as a
+ * decode step's gate/up product runs.  ws as for llmdec_op_linear with n_dim =
+ * 2*inter.  E_INVALID for act_parts other than 1 or 2, or 2 without out_lo. */
 llmdec_status llmdec_op_swiglu_linear(const float *a, int32_t rows, int32_t k_dim, const void *w_gu_packed,
-                                      int32_t inter, void *out_act, int32_t ld_packed, void *ws, size_t ws_bytes,
-                                      llmdec_stream stream);
+                                      int32_t inter, void *out_act, void *out_lo, int32_t ld_packed, int32_t act_parts,
+                                      void *ws, size_t ws_bytes, llmdec_stream stream);
 
 /* Rotate q and k of each new token by its position and store bf16 k, v into
  * the pool ([E] §4.3: rotation first, then the cache update).  qkv: dev fp32

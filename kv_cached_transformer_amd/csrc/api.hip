@@ -57,6 +57,7 @@ WsLayout ws_layout(const llmdec_config &c, int max_tokens, int max_seqs, int max
   L.act_h = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_h);
   L.act_hl = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_h);
   L.act_i = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_i);
+  L.act_il = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_i);
   L.qkv = take(sizeof(float) * (size_t)rows * qkv_cols(c));
   L.part = take(sizeof(float) * part);
   L.part_floats = part;
@@ -148,7 +149,7 @@ static void run_layer_one_row(const LayerArgs &a) {
   launch_gemv_qkv_rope(a.hidden, (const uint16_t *)a.w->attn_norm, c.rms_eps, (const uint16_t *)a.w->w_qkv, nqkv, h,
                        qkv, ra, a.s);
   launch_decode_attention(c, qkv, nqkv, 1, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages,
-                          at<float>(a.ws, L.attn_part), y, nullptr, 0, err, a.s);
+                          at<float>(a.ws, L.attn_part), y, nullptr, nullptr, 0, err, a.s);
   launch_gemv(y, nullptr, 0.f, (const uint16_t *)a.w->w_o, h, h, kAccumulate, a.hidden, a.s);
   launch_gemv(a.hidden, (const uint16_t *)a.w->mlp_norm, c.rms_eps, (const uint16_t *)a.w->w_gu, 2 * I, h, kSiluMul,
               u, a.s);
@@ -165,12 +166,16 @@ static void run_layer(const LayerArgs &a) {
   }
   uint32_t *err = at<uint32_t>(a.ws, L.err);
   uint16_t *act_h = at<uint16_t>(a.ws, L.act_h), *act_hl = at<uint16_t>(a.ws, L.act_hl);
-  uint16_t *act_i = at<uint16_t>(a.ws, L.act_i);
+  uint16_t *act_i = at<uint16_t>(a.ws, L.act_i), *act_il = at<uint16_t>(a.ws, L.act_il);
   float *qkv = at<float>(a.ws, L.qkv), *part = at<float>(a.ws, L.part);
-  // the q|k|v product reads its input as an fp16 pair (k and v are rounded to bf16 for the cache, so
-  // their error must stay far below a bf16 step); the other products read one fp16 plane
-  const Act ah2{act_h, act_hl, M, L.kpad_h, L.row_blocks}, ah{act_h, nullptr, M, L.kpad_h, L.row_blocks};
-  const Act ai{act_i, nullptr, M, L.kpad_i, L.row_blocks};
+  // The q|k|v product reads its input as an fp16 pair (k and v are rounded to bf16 for the cache, so
+  // their error must stay far below a bf16 step).  The others read the pair in a decode step (at most
+  // 64 rows: the products stream the weights, a second activation plane costs little, and single fp16
+  // inputs would compound over a model's layers) and one fp16 plane in a prefill (matrix-core bound).
+  const bool pairs = M <= 64;
+  uint16_t *lo_h = pairs ? act_hl : nullptr, *lo_i = pairs ? act_il : nullptr;
+  const Act ah2{act_h, act_hl, M, L.kpad_h, L.row_blocks}, ah{act_h, lo_h, M, L.kpad_h, L.row_blocks};
+  const Act ai{act_i, lo_i, M, L.kpad_i, L.row_blocks};
   uint16_t *pk, *pv;
   pool_layer(a.pool, a.layer, &pk, &pv);
 
@@ -189,14 +194,14 @@ static void run_layer(const LayerArgs &a) {
     launch_rope_append(c, qkv, qkv_part, sp_qkv, nqkv, M, a.n_seqs, nullptr, a.ctx, a.bt, a.max_pages, pk, pv,
                        a.pool->num_pages, err, a.s);
     launch_decode_attention(c, qkv, nqkv, M, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages,
-                            at<float>(a.ws, L.attn_part), nullptr, act_h, L.kpad_h, err, a.s);
+                            at<float>(a.ws, L.attn_part), nullptr, act_h, lo_h, L.kpad_h, err, a.s);
   } else {
     int32_t *ts = at<int32_t>(a.ws, L.tok_seq), *tp = at<int32_t>(a.ws, L.tok_pos);
     launch_token_map(a.cu, a.start, a.n_seqs, M, err, ts, tp, a.s);
     launch_rope_append(c, qkv, qkv_part, sp_qkv, nqkv, M, a.n_seqs, ts, tp, a.bt, a.max_pages, pk, pv,
                        a.pool->num_pages, err, a.s);
     launch_prefill_attention(c, qkv, nqkv, a.n_seqs, M, a.max_q_len, a.cu, a.start, a.bt, a.max_pages, pk, pv,
-                             a.pool->num_pages, nullptr, act_h, L.kpad_h, err, a.s);
+                             a.pool->num_pages, nullptr, act_h, lo_h, L.kpad_h, err, a.s);
   }
   LinearOut o_res;
   o_res.kind = kAccumulate;
@@ -208,10 +213,11 @@ static void run_layer(const LayerArgs &a) {
   // MLP block: x += Wd (silu(Wg y) * (Wu y)),  y = RMSNorm(x); the gate/up product's epilogue forms the
   // SwiGLU activation directly
   launch_rmsnorm(a.hidden, h, nullptr, M, (const uint16_t *)a.w->mlp_norm, M, h, c.rms_eps, err, nullptr, act_h,
-                 nullptr, L.kpad_h, sp_o.any() ? part : nullptr, sp_o, a.s);
+                 lo_h, L.kpad_h, sp_o.any() ? part : nullptr, sp_o, a.s);
   LinearOut o_gu;
   o_gu.kind = kSiluMul;
   o_gu.act = act_i;
+  o_gu.act_lo = lo_i;
   o_gu.act_kt = L.kpad_i / kTileK;
   o_gu.act_cols = I;
   const Splits sp_gu = launch_linear(ah, (const uint16_t *)a.w->w_gu, 2 * I, h, o_gu, part, L.part_floats, kSplitBalanced, a.s);
@@ -582,9 +588,12 @@ extern "C" llmdec_status llmdec_op_linear(const float *a, int32_t rows, int32_t 
 }
 
 extern "C" llmdec_status llmdec_op_swiglu_linear(const float *a, int32_t rows, int32_t k_dim, const void *w_gu_packed,
-                                                int32_t inter, void *out_act, int32_t ld_packed,
-                                                void *ws, size_t ws_bytes, llmdec_stream stream) {
-  if (!a || !w_gu_packed || !out_act) return set_error(LLMDEC_E_INVALID, "op_swiglu_linear: NULL pointer");
+                                                int32_t inter, void *out_act, void *out_lo, int32_t ld_packed,
+                                                int32_t act_parts, void *ws, size_t ws_bytes, llmdec_stream stream) {
+  if (!a || !w_gu_packed || !out_act || (act_parts == 2 && !out_lo))
+    return set_error(LLMDEC_E_INVALID, "op_swiglu_linear: NULL pointer");
+  if (act_parts != 1 && act_parts != 2)
+    return set_error(LLMDEC_E_INVALID, "op_swiglu_linear: act_parts=%d must be 1 or 2", act_parts);
   if (rows <= 0 || k_dim <= 0 || inter <= 0 || inter % 16 || ld_packed < inter || ld_packed % 32 ||
       ld_packed - inter > 16)
     return set_error(LLMDEC_E_INVALID, "op_swiglu_linear: rows=%d k=%d inter=%d ld_packed=%d out of range", rows, k_dim,
@@ -592,10 +601,11 @@ extern "C" llmdec_status llmdec_op_swiglu_linear(const float *a, int32_t rows, i
   LinearOut o;
   o.kind = kSiluMul;
   o.act = (uint16_t *)out_act;
+  o.act_lo = act_parts == 2 ? (uint16_t *)out_lo : nullptr;
   o.act_kt = ld_packed / kTileK;
   o.act_cols = inter;
-  llmdec_status st = run_op_linear("op_swiglu_linear", a, rows, k_dim, w_gu_packed, 2 * inter, 1, o, ws, ws_bytes, 0,
-                                   kSplitBalanced, (hipStream_t)stream);
+  llmdec_status st = run_op_linear("op_swiglu_linear", a, rows, k_dim, w_gu_packed, 2 * inter, act_parts, o, ws,
+                                   ws_bytes, 0, kSplitBalanced, (hipStream_t)stream);
   return st != LLMDEC_OK ? st : check_launch("op_swiglu_linear");
 }
 
@@ -634,7 +644,7 @@ extern "C" llmdec_status llmdec_op_decode_attention(const llmdec_config *cfg, co
   uint16_t *pk, *pv;
   pool_layer(pool, layer, &pk, &pv);
   launch_decode_attention(*cfg, q, cfg->hidden, n_seqs, ctx_lens, block_tables, max_pages, pk, pv, pool->num_pages,
-                          at<float>(ws, L.attn_part), out, nullptr, 0, at<uint32_t>(ws, L.err),
+                          at<float>(ws, L.attn_part), out, nullptr, nullptr, 0, at<uint32_t>(ws, L.err),
                           (hipStream_t)stream);
   return check_launch(who);
 }
@@ -656,7 +666,7 @@ extern "C" llmdec_status llmdec_op_prefill_attention(const llmdec_config *cfg, c
   uint16_t *pk, *pv;
   pool_layer(pool, layer, &pk, &pv);
   launch_prefill_attention(*cfg, q, cfg->hidden, n_seqs, n_tokens, max_q_len, cu_seqlens, start_pos, block_tables, max_pages,
-                           pk, pv, pool->num_pages, out, nullptr, 0, (uint32_t *)ws, (hipStream_t)stream);
+                           pk, pv, pool->num_pages, out, nullptr, nullptr, 0, (uint32_t *)ws, (hipStream_t)stream);
   return check_launch(who);
 }
 
@@ -834,7 +844,7 @@ static llmdec_status q_layer_decode(int bits, const char *who, const llmdec_conf
   launch_rope_append(c, qkv, nullptr, Splits{}, nqkv, 1, 1, nullptr, ctx_lens, block_tables, max_pages, pk, pv,
                      pool->num_pages, err, s);
   launch_decode_attention(c, qkv, nqkv, 1, ctx_lens, block_tables, max_pages, pk, pv, pool->num_pages,
-                          at<float>(ws, L.attn_part), y, nullptr, 0, err, s);
+                          at<float>(ws, L.attn_part), y, nullptr, nullptr, 0, err, s);
   launch_q_gemv(bits, y, nullptr, 0.f, (const uint8_t *)w->w_o, h, h, kAccumulate, hidden, s);
   // x += Wd (silu(Wg y) * (Wu y)),  y = RMSNorm(x)
   launch_q_gemv(bits, hidden, (const uint16_t *)w->mlp_norm, c.rms_eps, (const uint8_t *)w->w_gu, 2 * I, h, kSiluMul,

@@ -30,14 +30,15 @@ enum Epilogue { kStore = 0, kAccumulate = 1, kSiluMul = 2 };
 
 // Where a weight product's result goes.  kStore / kAccumulate: fp32 f32[r*ld + c]
 // (= or +=).  kSiluMul: the product's row blocks alternate gate and up; the
-// result silu(gate) * up goes, in fp16, to the packed activation act with
-// act_kt k-tiles per row block and act_cols real columns (the rest of the row
-// is zeroed).
+// result silu(gate) * up goes, in fp16, to the packed activation act (with
+// act_lo: as the fp16 pair act + act_lo) with act_kt k-tiles per row block and
+// act_cols real columns (the rest of the row is zeroed).
 struct LinearOut {
   int kind = kStore;
   float *f32 = nullptr;
   int ld = 0;
   uint16_t *act = nullptr;
+  uint16_t *act_lo = nullptr;
   int act_kt = 0;
   int act_cols = 0;
 };
@@ -71,7 +72,7 @@ inline int kv_cols(const llmdec_config &c) { return c.n_kv_heads * c.head_dim; }
 
 // Workspace layout for steps of up to max_tokens tokens and max_seqs sequences.
 struct WsLayout {
-  size_t err, tok_seq, tok_pos, x, act_h, act_hl, act_i, qkv, part, attn_part, logits, total;
+  size_t err, tok_seq, tok_pos, x, act_h, act_hl, act_i, act_il, qkv, part, attn_part, logits, total;
   size_t part_floats;
   int max_tokens, max_seqs, max_pages, row_blocks, kpad_h, kpad_i, attn_slots;
 };
@@ -126,15 +127,16 @@ void launch_rope_append(const llmdec_config &cfg, float *qkv, const float *qkv_p
                         int n_tokens, int n_seqs, const int32_t *tok_seq,
                         const int32_t *tok_pos, const int32_t *block_tables, int max_pages, uint16_t *pool_layer_k,
                         uint16_t *pool_layer_v, int num_pages, uint32_t *err, hipStream_t s);
-// Attention outputs go to fp32 out_f32 [rows][hidden] and/or the packed fp16 activation with kpad columns.
+// Attention outputs go to fp32 out_f32 [rows][hidden] and/or the packed fp16 activation with kpad columns
+// (out_lo != NULL: as the fp16 pair out_act + out_lo).
 void launch_decode_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, const int32_t *ctx_lens,
                              const int32_t *block_tables, int max_pages, const uint16_t *pool_layer_k,
                              const uint16_t *pool_layer_v, int num_pages, float *partials, float *out_f32,
-                             uint16_t *out_act, int kpad, uint32_t *err, hipStream_t s);
+                             uint16_t *out_act, uint16_t *out_lo, int kpad, uint32_t *err, hipStream_t s);
 void launch_prefill_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, int n_tokens, int max_q_len,
                               const int32_t *cu_seqlens, const int32_t *start_pos, const int32_t *block_tables,
                               int max_pages, const uint16_t *pool_layer_k, const uint16_t *pool_layer_v,
-                              int num_pages, float *out_f32, uint16_t *out_act, int kpad,
+                              int num_pages, float *out_f32, uint16_t *out_act, uint16_t *out_lo, int kpad,
                               uint32_t *err, hipStream_t s);
 // u = silu(g) * up elementwise, fp32 [rows][n] (the stand-alone operation; the layer steps fuse it
 // into the gate/up product's epilogue).

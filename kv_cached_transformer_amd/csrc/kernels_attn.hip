@@ -38,11 +38,17 @@ __device__ inline uint32_t mask_pair(uint32_t w, int t, int n_valid) {
   return t + 1 < n_valid ? w : (t < n_valid ? (w & 0xffffu) : 0u);
 }
 
-// The attention output feeds the o projection as a packed fp16 activation; the stand-alone operation
-// also (or only) writes fp32.
-__device__ inline void store_out(float v, int r, int c, int ld, float *out_f32, uint16_t *out_act, int kpad) {
+// The attention output feeds the o projection as a packed fp16 activation (with out_lo: the fp16 pair);
+// the stand-alone operation also (or only) writes fp32.
+__device__ inline void store_out(float v, int r, int c, int ld, float *out_f32, uint16_t *out_act, uint16_t *out_lo,
+                                 int kpad) {
   if (out_f32) out_f32[(size_t)r * ld + c] = v;
-  if (out_act) out_act[packed_offset(r, c, kpad >> 5)] = f32_to_f16(v);
+  if (out_act) {
+    const size_t o = packed_offset(r, c, kpad >> 5);
+    const uint16_t h = f32_to_f16(v);
+    out_act[o] = h;
+    if (out_lo) out_lo[o] = f32_to_f16(v - f16_to_f32(h));
+  }
 }
 
 // ---------------------------------------------------------------- decode
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(64 * DA_WAVES) void decode_attn_kernel(const float 
                                                          const uint16_t *__restrict__ pool_k,
                                                          const uint16_t *__restrict__ pool_v, int num_pages, int ppp,
                                                          int n_parts, float *__restrict__ partials, float *out_f32,
-                                                         uint16_t *out_act, int kpad, uint32_t *err) {
+                                                         uint16_t *out_act, uint16_t *out_lo, int kpad, uint32_t *err) {
   constexpr int NI = D / 32;      // 1 KiB K load instructions per page
   constexpr int LPT = D / 8;      // lanes per token in K (each holds 8 dims)
   constexpr int G = 64 / LPT;     // token groups per K instruction
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(64 * DA_WAVES) void decode_attn_kernel(const float 
       O = fmaf(co[w][jh][d], wt, O);
     }
     if (blocks_here == 1) {
-      store_out(O / L, s, h * D + d, n_heads * D, out_f32, out_act, kpad);
+      store_out(O / L, s, h * D + d, n_heads * D, out_f32, out_act, out_lo, kpad);
     } else {
       float *pp = partials + (((size_t)s * n_heads + h) * n_parts + blockIdx.z) * (D + 2);
       if (d == 0) {
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(64 * DA_WAVES) void decode_attn_kernel(const float 
 // then the same arithmetic as the general path below, in the same order.
 template <int D, int NP>
 __device__ inline void combine_few(const float *__restrict__ pp, int parts, int s, int h, int n_heads, float *out_f32,
-                                   uint16_t *out_act, int kpad) {
+                                   uint16_t *out_act, uint16_t *out_lo, int kpad) {
   const int d = threadIdx.x;
   float m[NP], l[NP], o[NP];
 #pragma unroll
@@ -370,22 +376,22 @@ __device__ inline void combine_few(const float *__restrict__ pp, int parts, int 
       L = fmaf(l[j], w, L);
       acc = fmaf(o[j], w, acc);
     }
-  store_out(acc / L, s, h * D + d, n_heads * D, out_f32, out_act, kpad);
+  store_out(acc / L, s, h * D + d, n_heads * D, out_f32, out_act, out_lo, kpad);
 }
 
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(int n_heads, const int32_t *__restrict__ ctx_lens,
                                                            int max_pages, int ppp, int n_parts,
                                                            const float *__restrict__ partials, float *out_f32,
-                                                           uint16_t *out_act, int kpad) {
+                                                           uint16_t *out_act, uint16_t *out_lo, int kpad) {
   const int s = blockIdx.x / n_heads, h = blockIdx.x % n_heads;
   const int n_pages = (ctx_lens[s] + 1 + 15) >> 4;
   if (n_pages > max_pages || n_pages <= 0) return;
   const int parts = (n_pages + ppp - 1) / ppp;
   if (parts <= 1) return;
   const float *pp = partials + ((size_t)s * n_heads + h) * n_parts * (D + 2);
-  if (parts <= 4) return combine_few<D, 4>(pp, parts, s, h, n_heads, out_f32, out_act, kpad);
-  if (parts <= 16) return combine_few<D, 16>(pp, parts, s, h, n_heads, out_f32, out_act, kpad);
+  if (parts <= 4) return combine_few<D, 4>(pp, parts, s, h, n_heads, out_f32, out_act, out_lo, kpad);
+  if (parts <= 16) return combine_few<D, 16>(pp, parts, s, h, n_heads, out_f32, out_act, out_lo, kpad);
   const int d = threadIdx.x;
   // maximum of the partitions' running maxima: one partition per thread, then a block reduction
   __shared__ float red[D / 64], wl[2][D];
@@ -424,7 +430,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(int n_heads, const in
         }
     }
   }
-  store_out(acc / L, s, h * D + d, n_heads * D, out_f32, out_act, kpad);
+  store_out(acc / L, s, h * D + d, n_heads * D, out_f32, out_act, out_lo, kpad);
 }
 
 void decode_partition(const llmdec_config &cfg, int n_seqs, int max_pages, int *pages_per_part, int *n_parts) {
@@ -454,40 +460,40 @@ template <int D, int QH>
 static void launch_decode_qh(const llmdec_config &cfg, dim3 grid, hipStream_t s, const float *q, int ld_q,
                              const int32_t *ctx_lens, const int32_t *block_tables, int max_pages, const uint16_t *pk,
                              const uint16_t *pv, int num_pages, int ppp, int n_parts, float *partials, float *out_f32,
-                             uint16_t *out_act, int kpad, uint32_t *err) {
+                             uint16_t *out_act, uint16_t *out_lo, int kpad, uint32_t *err) {
   if (cfg.n_heads / cfg.n_kv_heads > QH)  // a K/V head read by several waves
     decode_attn_kernel<D, QH, true><<<grid, 64 * DA_WAVES, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, ctx_lens, block_tables,
                                                         max_pages, pk, pv, num_pages, ppp, n_parts, partials, out_f32,
-                                                        out_act, kpad, err);
+                                                        out_act, out_lo, kpad, err);
   else
     decode_attn_kernel<D, QH, false><<<grid, 64 * DA_WAVES, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, ctx_lens, block_tables,
                                                          max_pages, pk, pv, num_pages, ppp, n_parts, partials, out_f32,
-                                                         out_act, kpad, err);
+                                                         out_act, out_lo, kpad, err);
 }
 
 template <int D>
 static void launch_decode_d(const llmdec_config &cfg, int qh, dim3 grid, hipStream_t s, const float *q, int ld_q,
                             const int32_t *ctx_lens, const int32_t *block_tables, int max_pages, const uint16_t *pk,
                             const uint16_t *pv, int num_pages, int ppp, int n_parts, float *partials, float *out_f32,
-                            uint16_t *out_act, int kpad, uint32_t *err) {
+                            uint16_t *out_act, uint16_t *out_lo, int kpad, uint32_t *err) {
   if (qh == 4)
     launch_decode_qh<D, 4>(cfg, grid, s, q, ld_q, ctx_lens, block_tables, max_pages, pk, pv, num_pages, ppp, n_parts,
-                           partials, out_f32, out_act, kpad, err);
+                           partials, out_f32, out_act, out_lo, kpad, err);
   else if (qh == 2)
     launch_decode_qh<D, 2>(cfg, grid, s, q, ld_q, ctx_lens, block_tables, max_pages, pk, pv, num_pages, ppp, n_parts,
-                           partials, out_f32, out_act, kpad, err);
+                           partials, out_f32, out_act, out_lo, kpad, err);
   else
     launch_decode_qh<D, 1>(cfg, grid, s, q, ld_q, ctx_lens, block_tables, max_pages, pk, pv, num_pages, ppp, n_parts,
-                           partials, out_f32, out_act, kpad, err);
+                           partials, out_f32, out_act, out_lo, kpad, err);
   const int n_seqs = (int)grid.y;
   if (n_parts > 1)  // here: partial results per (sequence, head), one per block of DA_WAVES partitions
     decode_combine_kernel<D><<<n_seqs * cfg.n_heads, D, 0, s>>>(cfg.n_heads, ctx_lens, max_pages, ppp * DA_WAVES,
-                                                                n_parts, partials, out_f32, out_act, kpad);
+                                                                n_parts, partials, out_f32, out_act, out_lo, kpad);
 }
 
 void launch_decode_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, const int32_t *ctx_lens,
                              const int32_t *block_tables, int max_pages, const uint16_t *pk, const uint16_t *pv,
-                             int num_pages, float *partials, float *out_f32, uint16_t *out_act,
+                             int num_pages, float *partials, float *out_f32, uint16_t *out_act, uint16_t *out_lo,
                              int kpad, uint32_t *err, hipStream_t s) {
   if (n_seqs <= 0) return;
   const int qh = decode_heads_per_wave(cfg);
@@ -497,10 +503,10 @@ void launch_decode_attention(const llmdec_config &cfg, const float *q, int ld_q,
   dim3 grid(cfg.n_heads / qh, n_seqs, n_blocks_z);
   if (cfg.head_dim == 128)
     launch_decode_d<128>(cfg, qh, grid, s, q, ld_q, ctx_lens, block_tables, max_pages, pk, pv, num_pages, ppp,
-                         n_blocks_z, partials, out_f32, out_act, kpad, err);
+                         n_blocks_z, partials, out_f32, out_act, out_lo, kpad, err);
   else
     launch_decode_d<64>(cfg, qh, grid, s, q, ld_q, ctx_lens, block_tables, max_pages, pk, pv, num_pages, ppp,
-                        n_blocks_z, partials, out_f32, out_act, kpad, err);
+                        n_blocks_z, partials, out_f32, out_act, out_lo, kpad, err);
 }
 
 // ---------------------------------------------------------------- prefill (causal, MFMA)
@@ -515,7 +521,7 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
                                                           const int32_t *__restrict__ block_tables, int max_pages,
                                                           const uint16_t *__restrict__ pool_k,
                                                           const uint16_t *__restrict__ pool_v, int num_pages,
-                                                          float *out_f32, uint16_t *out_act, int kpad,
+                                                          float *out_f32, uint16_t *out_act, uint16_t *out_lo, int kpad,
                                                           uint32_t *err) {
   constexpr int KT = D / 32;  // k-tiles of the head dimension
   constexpr int DB = D / 16;  // 16-dim blocks of the output
@@ -651,21 +657,21 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      store_out(oacc[db][e] * inv, tok, h * D + db * 16 + g * 4 + e, n_heads * D, out_f32, out_act, kpad);
+      store_out(oacc[db][e] * inv, tok, h * D + db * 16 + g * 4 + e, n_heads * D, out_f32, out_act, out_lo, kpad);
 }
 
 void launch_prefill_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, int n_tokens, int max_q_len,
                               const int32_t *cu, const int32_t *start_pos, const int32_t *block_tables, int max_pages,
                               const uint16_t *pk, const uint16_t *pv, int num_pages, float *out_f32, uint16_t *out_act,
-                              int kpad, uint32_t *err, hipStream_t s) {
+                              uint16_t *out_lo, int kpad, uint32_t *err, hipStream_t s) {
   if (n_seqs <= 0 || max_q_len <= 0) return;
   dim3 grid((max_q_len + 15) / 16, cfg.n_heads, n_seqs);
   if (cfg.head_dim == 128)
     prefill_attn_kernel<128><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, n_tokens, max_q_len, cu, start_pos, block_tables, max_pages, pk, pv,
-                                                 num_pages, out_f32, out_act, kpad, err);
+                                                 num_pages, out_f32, out_act, out_lo, kpad, err);
   else
     prefill_attn_kernel<64><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, n_tokens, max_q_len, cu, start_pos, block_tables, max_pages, pk, pv,
-                                                num_pages, out_f32, out_act, kpad, err);
+                                                num_pages, out_f32, out_act, out_lo, kpad, err);
 }
 
 }  // namespace llmdec

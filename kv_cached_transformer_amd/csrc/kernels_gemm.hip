@@ -8,11 +8,15 @@
 // An fp16 activation keeps 11 significant bits, eight times bf16's 8: one
 // bf16 rounding at each product input would put the 7B-layer output beyond a
 // 2e-2 max-abs bound against an unrounded reference, fp16 stays well inside.
-// The q|k|v product takes its activation as an fp16 pair hi + lo (NP = 2
-// planes, two MFMAs per tile pair, about 22 bits): k and v are rounded to
-// bf16 when they enter the cache, and with single fp16 inputs about one in
-// ten of them would land on the other side of a bf16 rounding boundary than
-// an exact product's, a full bf16 step that every later token attends to.
+// Where more precision is needed the activation comes as an fp16 pair hi + lo
+// (NP = 2 planes, two MFMAs per tile pair, about 22 bits): always for the
+// q|k|v product (k and v are rounded to bf16 when they enter the cache, and
+// with single fp16 inputs about one in ten of them would land on the other
+// side of a bf16 rounding boundary than an exact product's, a full bf16 step
+// that every later token attends to), and for every product of a decode step
+// (its rounding errors compound over the layers of a model: 32 layers of
+// single fp16 inputs bring the logits to 1.6e-2 of the exact ones, pairs to
+// 1.2e-3; the second plane costs a decode step little, its time is the weights').
 //
 // Both operands are in the packed tile layout (see packed_offset): a 16-row x
 // 32-column tile is 1 KiB, and lane l of a wave holds row l%16, columns
@@ -54,10 +58,18 @@ __device__ inline float silu_f(float g) { return g / (1.0f + expf(-g)); }
 __device__ inline void epi_store(const LinearOut &o, int r, int c, float v, float u) {
   if (o.kind == kSiluMul) {
     const int j = ((c >> 5) << 4) | (c & 15);  // gate column -> activation column
-    o.act[packed_offset(r, j, o.act_kt)] = f32_to_f16(silu_f(v) * u);
+    const float y = silu_f(v) * u;
+    const size_t off = packed_offset(r, j, o.act_kt);
+    const uint16_t h = f32_to_f16(y);
+    o.act[off] = h;
+    if (o.act_lo) o.act_lo[off] = f32_to_f16(y - f16_to_f32(h));
     // the row's padding columns (act_cols .. 32*act_kt-1, fewer than 16 since act_cols % 16 == 0)
     // follow the last real 16-column block, whose writers clear them
-    if (j + 16 >= o.act_cols && j + 16 < o.act_kt * 32) o.act[packed_offset(r, j + 16, o.act_kt)] = 0;
+    if (j + 16 >= o.act_cols && j + 16 < o.act_kt * 32) {
+      const size_t pad = packed_offset(r, j + 16, o.act_kt);
+      o.act[pad] = 0;
+      if (o.act_lo) o.act_lo[pad] = 0;
+    }
   } else {
     float *p = o.f32 + (size_t)r * o.ld + c;
     *p = o.kind == kAccumulate ? *p + v : v;
@@ -295,11 +307,22 @@ __global__ void reduce_kernel(const float *__restrict__ partials, Splits sp, int
     const float y[8] = {silu_f(s0.x) * u0.x, silu_f(s0.y) * u0.y, silu_f(s0.z) * u0.z, silu_f(s0.w) * u0.w,
                         silu_f(s1.x) * u1.x, silu_f(s1.y) * u1.y, silu_f(s1.z) * u1.z, silu_f(s1.w) * u1.w};
     const int j = ((c >> 5) << 4) | (c & 15);  // gate column -> activation column (a multiple of 8)
-    *reinterpret_cast<uint4 *>(o.act + packed_offset(r, j, o.act_kt)) = pack8_f16(y);
+    const size_t off = packed_offset(r, j, o.act_kt);
+    if (o.act_lo) {
+      uint4 h, l;
+      pack8_f16x2(y, h, l);
+      *reinterpret_cast<uint4 *>(o.act + off) = h;
+      *reinterpret_cast<uint4 *>(o.act_lo + off) = l;
+    } else {
+      *reinterpret_cast<uint4 *>(o.act + off) = pack8_f16(y);
+    }
     // the row's padding columns (act_cols .. 32*act_kt-1: none or one 16-column block) follow the last
     // real 16-column block, whose writers clear them
-    if (j + 16 >= o.act_cols && j + 16 < o.act_kt * 32)
-      *reinterpret_cast<uint4 *>(o.act + packed_offset(r, j + 16, o.act_kt)) = make_uint4(0, 0, 0, 0);
+    if (j + 16 >= o.act_cols && j + 16 < o.act_kt * 32) {
+      const size_t pad = packed_offset(r, j + 16, o.act_kt);
+      *reinterpret_cast<uint4 *>(o.act + pad) = make_uint4(0, 0, 0, 0);
+      if (o.act_lo) *reinterpret_cast<uint4 *>(o.act_lo + pad) = make_uint4(0, 0, 0, 0);
+    }
   } else {
     float4 *q = reinterpret_cast<float4 *>(o.f32 + (size_t)r * o.ld + c);
     if (o.kind == kAccumulate) vadd(s0, *q);
@@ -313,48 +336,54 @@ void launch_reduce(const float *partials, const Splits &sp, int rows, int n, con
 }
 
 // ---------------------------------------------------------------- tile_gemm (rows > 64)
-// A block is two waves side by side along the columns; each wave computes WM row blocks (16 WM rows)
-// by WNT column blocks of W (16 WNT columns), so the block tile is 16 WM x 32 WNT.  Per k-tile the
-// block needs NP * WM activation tiles, used by both waves, and each wave WNT weight tiles of its own:
-//   * activation tiles go from memory straight into LDS (buffer_load ... lds: lane l's 16 bytes land
-//     at l * 16 of the 1 KiB stage slot, which is the packed tile itself), each wave loading half of
-//     them, through S = L + 1 stages, L k-tiles ahead of the one being computed;
-//   * weight tiles go from memory into the registers of the wave that uses them, through a ring of
-//     the same L + 1 slots.
-// One step: wait until this k-tile's loads have landed (a count of the loads issued after them), a
-// barrier (both waves' halves are in LDS, and both finished reading the stage about to be refilled),
-// issue the loads of k-tile t + L into the stage and slot step t - 1 used, read this stage's
-// activation tiles from LDS and run WM * WNT * NP MFMAs.  With WM = WNT = 8 a wave keeps 256
-// accumulators, so one wave per SIMD runs; the L = 3 k-tiles in flight (about 3000 clocks of MFMA
-// work) cover the memory latency instead of other waves.
+// A block is four waves in a 2 x 2 grid; wave (wr, wc) computes WM row blocks by WNT column blocks of
+// the output, so the block tile is BM = 2 WM row blocks by BN = 2 WNT column blocks (16 x 16 each).
+// Per k-tile (32 deep) the block needs NP * BM activation tiles (each used by the two waves of its row
+// half) and BN weight tiles (each used by the two waves of its column half).  All of them go from
+// memory straight into LDS (buffer_load ... lds: lane l's 16 bytes land at l * 16 of the tile's 1 KiB
+// slot, which is the packed tile itself), the four waves issuing a quarter each, through R stages.
+// Step t:
+//   * wait until k-tile t + 1 has landed (the loads of R - 2 later k-tiles may still be in flight) and
+//     for this wave's LDS reads of stage t, then a barrier: every wave's share of k-tile t + 1 is in
+//     LDS, and every wave has finished reading stage t;
+//   * read stage t + 1 into the second register set (the fragments of k-tile t + 1);
+//   * issue the loads of k-tile t + R into stage t, which no wave reads any more;
+//   * run the WM * WNT * NP MFMAs of k-tile t from the first register set (read during step t - 1), so
+//     the LDS reads of the next k-tile overlap them.
+// With WM = WNT = 8 a wave keeps 256 accumulators and one wave per SIMD runs; the R - 1 k-tiles in
+// flight (3000+ clocks of MFMA work) cover the memory latency instead of other waves.  A 256 x 256
+// block tile loads 32 KiB per k-tile for 64 MFMAs per SIMD, a third less per MFMA than two waves
+// side by side with weights in registers.
 //
 // Blocks go round-robin to the 8 XCDs, so block b takes tile (b % 8) * G/8 + b / 8 of G (a multiple of
 // 8, spare blocks exit), with tiles numbered column-major (row tiles innermost): the blocks one XCD runs
 // together cover every row tile of a few column groups, so each weight tile is fetched into that
 // XCD's L2 once and each activation k-slab serves all of them.
 template <int WM, int WNT, int NP> struct TgShape {
-  static constexpr int AT = NP * WM;       // activation tiles per k-tile (all planes)
-  static constexpr int APW = AT / 2;       // of them loaded by each wave
-  static constexpr int L = 3;              // k-tiles in flight ahead of the one computed
-  static constexpr int R = L + 1;          // LDS stages = weight ring slots
-  static constexpr int GROUP = APW + WNT;  // loads per wave per k-tile
-  static_assert((L - 1) * GROUP <= 63, "the loads in flight must fit the vmcnt counter");
-  static_assert(WNT % 2 == 0 && AT % 2 == 0, "gate/up column pairs and an even split of the activation loads");
+  static constexpr int BM = 2 * WM, BN = 2 * WNT;  // row / column blocks of the block tile
+  static constexpr int AT = NP * BM;               // activation tiles per k-tile (all planes)
+  static constexpr int TILES = AT + BN;            // 1 KiB tiles per stage
+  static constexpr int G = TILES / 4;              // loads per wave per k-tile
+  static constexpr int R = 160 / TILES < 4 ? 160 / TILES : 4;  // stages (160 KiB of LDS per CU)
+  static_assert(AT % 4 == 0 && BN % 4 == 0, "load i of wave w is tile 4 i + w: a whole number per kind");
+  static_assert(WNT % 2 == 0, "gate/up column pairs");
+  static_assert(R >= 3 && (R - 1) * G <= 63, "at least one k-tile of lookahead; the loads fit vmcnt");
 };
 
 // A 16-byte-per-lane load from a buffer straight into LDS (lane l's bytes land at lds_addr + 16 l).
-// Issued from asm so the compiler's wait counting does not treat it as a write to every LDS location
-// (it would then wait for it before each LDS read, including reads of other stages); the callers wait
-// for these loads themselves (wait_vmcnt) and then synchronise the block before reading the stage.
-// The descriptor is built by hand: base address, stride 0, num_records bytes, the raw-buffer flags.
+// Issued from asm: the compiler neither counts it nor treats it as a write to LDS, so it adds no waits
+// for it before LDS reads (it would wait for every such load in flight, into any stage, before each
+// read).  The callers wait for these loads themselves and synchronise the block before reading a
+// stage.  The descriptor is built by hand: base address, stride 0, num_records bytes, raw-buffer flags.
 __device__ inline u32x4 buffer_desc(const void *base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
 }
-// M0 is named as clobbered although the compiler reserves it: nothing else in these kernels uses M0.
+// M0 carries the LDS address; nothing else in these kernels uses it, so the compiler's note that a
+// clobbered M0 is not preserved does not apply.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ inline void load_to_lds16(const u32x4 &desc, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+__device__ inline void load_to_lds16(uint32_t voff, u32x4 desc, uint32_t soff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
                : "v"(voff), "s"(desc), "s"(soff), "s"(lds_addr)
@@ -362,61 +391,75 @@ __device__ inline void load_to_lds16(const u32x4 &desc, uint32_t voff, uint32_t 
 }
 #pragma clang diagnostic pop
 
-// s_waitcnt with only the vector-memory count set (the other counters at their maxima)
+// Wait until at most N vector-memory loads of this wave are in flight and all its LDS reads are done,
+// then the block barrier.  The wait is the builtin, so the compiler knows the LDS reads have completed
+// (and adds no waits for them later); the barrier is asm with a memory clobber, so the compiler moves
+// no memory access across it.
 template <int N>
-__device__ inline void wait_vmcnt() {
+__device__ inline void wait_loads_barrier() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));  // lgkmcnt field (bits 8-11) 0
+  asm volatile("s_barrier" : : : "memory");
 }
 
 template <int WM, int WNT, int NP>
-__global__ __launch_bounds__(128, 1) void tile_gemm_kernel(const uint4 *__restrict__ a_act,
+__global__ __launch_bounds__(256, 1) void tile_gemm_kernel(const uint4 *__restrict__ a_act,
                                                            const uint4 *__restrict__ a_lo, int a_kt, int a_blocks,
                                                            int rows, const uint4 *__restrict__ w, int kt_count,
                                                            int n_blocks, int tiles_m, int n_tiles, LinearOut o) {
   using S = TgShape<WM, WNT, NP>;
-  constexpr int AT = S::AT, APW = S::APW, L = S::L, R = S::R;
-  __shared__ uint4 lds[R * AT * 64];  // [R stages][AT tiles][64 lanes]
+  constexpr int BM = S::BM, BN = S::BN, AT = S::AT, TILES = S::TILES, G = S::G, R = S::R;
+  __shared__ uint4 lds[R * TILES * 64];  // [R stages][TILES tiles][64 lanes]
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)lds;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave & 1, wc = wave >> 1;
   const int per_xcd = (int)(gridDim.x >> 3);
   const int t = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (t >= n_tiles) return;  // block-uniform: a spare block of the rounded-up grid
   const int tm = t % tiles_m, tn = t / tiles_m;
-  const int mb0 = tm * WM, nbw0 = (tn * 2 + wave) * WNT;
+  const int mb0 = tm * BM, nb0 = tn * BN;
 
-  // activation tiles this wave loads: q = wave * APW + i, row block mb0 + q % WM of the first plane
-  // (q < WM) or of the lo plane; a row block past the operand gets an empty resource (zeros)
-  u32x4 asrc[APW];
+  // Load i of this wave is stage tile q = 4 i + wave: activation tiles first (plane q / BM, row block
+  // mb0 + q % BM), then weight tiles (column block nb0 + q - AT).  A row block past the operand reads
+  // zeros (its lane offsets leave the resource); a column block past the matrix re-reads the last one
+  // (its columns are not stored).  Offsets are bytes from the operand's base, without the k-tile.
+  const u32x4 dhi = buffer_desc(a_act, (uint32_t)a_blocks * (uint32_t)a_kt * 1024u);
+  const u32x4 dlo = buffer_desc(NP > 1 ? a_lo : a_act, (uint32_t)a_blocks * (uint32_t)a_kt * 1024u);
+  const u32x4 dw = buffer_desc(w, (uint32_t)n_blocks * (uint32_t)kt_count * 1024u);
+  uint32_t base[G], oob[G];
 #pragma unroll
-  for (int i = 0; i < APW; ++i) {
-    const int q = wave * APW + i;
-    const int rb = mb0 + q % WM;
-    const bool ok = rb < a_blocks;
-    asrc[i] = buffer_desc((q < WM ? a_act : a_lo) + (size_t)(ok ? rb : 0) * a_kt * 64, ok ? (uint32_t)a_kt * 1024u : 0u);
+  for (int i = 0; i < G; ++i) {
+    const int q = 4 * i + wave;
+    if (4 * i < AT) {
+      const int rb = mb0 + q % BM;
+      base[i] = (uint32_t)min(rb, a_blocks - 1) * (uint32_t)a_kt * 1024u;
+      oob[i] = rb < a_blocks ? 0u : 0x80000000u;
+    } else {
+      base[i] = (uint32_t)min(nb0 + q - AT, n_blocks - 1) * (uint32_t)kt_count * 1024u;
+      oob[i] = 0u;
+    }
   }
-  // this wave's weight row blocks nbw0.. through one resource (empty past the matrix; a block past the
-  // last one re-reads the last, and its columns are not stored)
-  const int nbv = min(WNT, n_blocks - nbw0);
-  const __amdgpu_buffer_rsrc_t wsrc =
-      make_rsrc(w + (size_t)(nbv > 0 ? nbw0 : 0) * kt_count * 64, nbv > 0 ? (size_t)nbv * kt_count * 1024 : 0);
-  uint32_t w_off[WNT];
-#pragma unroll
-  for (int j = 0; j < WNT; ++j) w_off[j] = (uint32_t)min(j, max(nbv - 1, 0)) * (uint32_t)kt_count * 1024u;
-
   const uint32_t lane_bytes = (uint32_t)lane * 16u;
-  uint4 wr[R][WNT];
-  // k-tile kt (past the end: the lane offset leaves every resource, the loads read zeros) into stage
-  // and slot `slot`: this wave's activation tiles to LDS, its weight tiles to registers
-  auto fetch = [&](int slot, int kt) {
-    const uint32_t voff = lane_bytes | (kt < kt_count ? 0u : 0x80000000u);
+  // load i of k-tile kt into stage st (past the last k-tile: zeros, through the lane offset)
+  auto issue = [&](int st, int kt, int i) {
+    const uint32_t kflag = kt < kt_count ? 0u : 0x80000000u;
     const uint32_t koff = (uint32_t)min(kt, kt_count - 1) * 1024u;
-#pragma unroll
-    for (int i = 0; i < APW; ++i)
-      load_to_lds16(asrc[i], voff, koff, lds_base + (uint32_t)((slot * AT + wave * APW + i) * 1024));
-#pragma unroll
-    for (int j = 0; j < WNT; ++j) wr[slot][j] = buffer_load16(wsrc, voff, w_off[j] + koff, 0);
+    const u32x4 d = 4 * i < AT ? ((4 * i) / BM == 0 ? dhi : dlo) : dw;
+    load_to_lds16(lane_bytes | oob[i] | kflag, d, base[i] + koff,
+                  lds_base + (uint32_t)(st * TILES * 1024) + (uint32_t)((4 * i + wave) * 1024));
+  };
+
+  // Register set b holds this wave's fragments of one k-tile: its row half's activation tiles of each
+  // plane (fa) and its column half's weight tiles (fb).  Fragment f of a stage (activation tiles
+  // first, then weight tiles) is one 16-byte LDS read per lane.
+  constexpr int NF = NP * WM + WNT;
+  uint4 fa[2][NP * WM], fb[2][WNT];
+  auto read_frag = [&](int b, int st, int f) {
+    const uint4 *sa = lds + (size_t)(st * TILES + wr * WM) * 64 + lane;
+    const uint4 *sw = lds + (size_t)(st * TILES + AT + wc * WNT) * 64 + lane;
+    if (f < NP * WM) fa[b][f] = sa[((f / WM) * BM + f % WM) * 64];
+    else fb[b][f - NP * WM] = sw[(f - NP * WM) * 64];
   };
 
   f32x4 acc[WM][WNT];
@@ -426,51 +469,77 @@ __global__ __launch_bounds__(128, 1) void tile_gemm_kernel(const uint4 *__restri
     for (int j = 0; j < WNT; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int p = 0; p < L; ++p) {
-    fetch(p, p);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (int k0 = 0; k0 < kt_count; k0 += R) {  // block-uniform; steps past kt_count compute zeros
+  for (int st = 0; st < R; ++st)
 #pragma unroll
-    for (int d = 0; d < R; ++d) {
-      // k-tile k0 + d is in stage and slot d; the L - 1 k-tiles after it may still be in flight
-      wait_vmcnt<(L - 1) * S::GROUP>();
-      __syncthreads();
+    for (int i = 0; i < G; ++i) issue(st, st, i);
+  wait_loads_barrier<(R - 1) * G>();
+#pragma unroll
+  for (int f = 0; f < NF; ++f) read_frag(0, 0, f);
+  // Two steps per trip (the register sets alternate; an odd k-tile count runs one step on zeros).  A
+  // step runs row by row, each row's MFMAs in a scheduling region of their own together with a share
+  // of the next k-tile's LDS reads and of the loads into the freed stage, so that both are issued
+  // while the matrix cores work.
+  constexpr int RF = (NF + WM - 1) / WM, RG = (G + WM - 1) / WM;  // reads, loads per row
+  for (int k0 = 0; k0 < kt_count; k0 += 2) {
+    int st = k0 % R;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int nst = st + 1 == R ? 0 : st + 1;
+      wait_loads_barrier<(R - 2) * G>();
       __builtin_amdgcn_sched_barrier(0);
-      fetch((d + L) % R, k0 + d + L);
-      __builtin_amdgcn_sched_barrier(0);
-      const uint4 *st = lds + (size_t)d * AT * 64;
 #pragma unroll
       for (int m = 0; m < WM; ++m) {
-        uint4 ah = st[(size_t)m * 64 + lane], al;
-        if constexpr (NP > 1) al = st[(size_t)(WM + m) * 64 + lane];
+#pragma unroll
+        for (int f = m * RF; f < (m + 1) * RF; ++f)
+          if (f < NF) read_frag(b ^ 1, nst, f);
+#pragma unroll
+        for (int i = m * RG; i < (m + 1) * RG; ++i)
+          if (i < G) issue(st, k0 + b + R, i);
 #pragma unroll
         for (int j = 0; j < WNT; ++j) {
-          if constexpr (NP > 1) acc[m][j] = mfma16(al, wr[d][j], acc[m][j]);  // the smaller part first
-          acc[m][j] = mfma16(ah, wr[d][j], acc[m][j]);
+          if constexpr (NP > 1) acc[m][j] = mfma16(fa[b][WM + m], fb[b][j], acc[m][j]);  // the smaller part first
+          acc[m][j] = mfma16(fa[b][m], fb[b][j], acc[m][j]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      st = nst;
     }
   }
+  // the loads issued past the last k-tile (zeros) land before the block's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
 
+  // epilogue, one fully unrolled loop per kind (the accumulators stay in registers only if every index
+  // is a constant)
   const float wunscale = weight_unscale(w + (size_t)n_blocks * kt_count * 64);
   const int rq = (lane >> 4) * 4, cq = lane & 15;
+  const int mw = mb0 + wr * WM, nw = nb0 + wc * WNT;
+  if (o.kind == kSiluMul) {
 #pragma unroll
-  for (int m = 0; m < WM; ++m)
+    for (int m = 0; m < WM; ++m)
 #pragma unroll
-    for (int j = 0; j < WNT; ++j) {
-      const int nb = nbw0 + j;
-      if (nb >= n_blocks) continue;
-      if (o.kind == kSiluMul && (j & 1)) continue;
+      for (int j = 0; j < WNT; j += 2)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = (mb0 + m) * 16 + rq + e;
-        if (r < rows)
-          epi_store(o, r, nb * 16 + cq, acc[m][j][e] * wunscale,
-                    o.kind == kSiluMul ? acc[m][j + 1][e] * wunscale : 0.f);
-      }
-    }
+        for (int e = 0; e < 4; ++e) {
+          const int r = (mw + m) * 16 + rq + e;
+          if (r < rows && nw + j < n_blocks)
+            epi_store(o, r, (nw + j) * 16 + cq, acc[m][j][e] * wunscale, acc[m][j + 1][e] * wunscale);
+        }
+  } else {
+    const bool add = o.kind == kAccumulate;
+#pragma unroll
+    for (int m = 0; m < WM; ++m)
+#pragma unroll
+      for (int j = 0; j < WNT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = (mw + m) * 16 + rq + e;
+          if (r < rows && nw + j < n_blocks) {
+            float *p = o.f32 + (size_t)r * o.ld + (nw + j) * 16 + cq;
+            const float v = acc[m][j][e] * wunscale;
+            *p = add ? *p + v : v;
+          }
+        }
+  }
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -527,10 +596,11 @@ size_t linear_partial_floats(int rows, int n, int k, SplitPolicy policy) {
   return (size_t)max_slots * rows * n;
 }
 
-// Prefill tile shape (WM row blocks x WNT column blocks per wave, two waves per block).  A CU holds
-// two blocks (one wave per SIMD), so a launch runs in rounds of 512 blocks; a block's time scales with
-// its MFMAs, and smaller per-wave tiles re-read their operands more often per MFMA (relative speeds
-// below are estimates).  The shape with the least estimated time wins, larger tiles on ties.
+// Prefill tile shape (WM row blocks x WNT column blocks per wave, four waves per block).  Blocks with more
+// than 80 KiB of LDS stages run one per CU, smaller ones two, so a launch runs in rounds of 256 or 512
+// blocks; a round's time scales with the MFMAs a SIMD runs in it, and smaller tiles load more bytes per
+// MFMA (relative speeds below are estimates).  The shape with the least estimated time wins, larger
+// tiles on ties.
 struct TileChoice {
   int wm, wnt, tiles_m, tiles_n;
 };
@@ -543,10 +613,12 @@ static TileChoice choose_tiles(int rows, int n_blocks, int planes) {
   TileChoice best{0, 0, 0, 0};
   double best_cost = 1e300;
   for (const auto &sh : shapes) {
-    if (planes > 1 && sh.wm * sh.wnt > 48) continue;  // 8 x 8 with both planes spills registers
-    const int tm = (row_blocks + sh.wm - 1) / sh.wm, tn = (n_blocks + 2 * sh.wnt - 1) / (2 * sh.wnt);
+    const int tiles_kib = planes * 2 * sh.wm + 2 * sh.wnt;
+    const int stages = std::min(4, 160 / tiles_kib);
+    const int per_cu = stages * tiles_kib > 80 ? 1 : 2;
+    const int tm = (row_blocks + 2 * sh.wm - 1) / (2 * sh.wm), tn = (n_blocks + 2 * sh.wnt - 1) / (2 * sh.wnt);
     const long tiles = (long)tm * tn;
-    const double cost = (double)((tiles + 2 * kCUs - 1) / (2 * kCUs)) * sh.wm * sh.wnt / sh.speed;
+    const double cost = (double)((tiles + per_cu * kCUs - 1) / (per_cu * kCUs)) * per_cu * sh.wm * sh.wnt / sh.speed;
     if (cost < best_cost * 0.999) best_cost = cost, best = TileChoice{sh.wm, sh.wnt, tm, tn};
   }
   return best;
@@ -557,7 +629,7 @@ static void launch_tile(hipStream_t s, const TileChoice &tc, const uint4 *act, c
                         int a_blocks, int rows, const uint4 *w, int kt_count, int n_blocks, const LinearOut &o) {
   const int n_tiles = tc.tiles_m * tc.tiles_n;
   const int grid = (n_tiles + 7) / 8 * 8;
-  tile_gemm_kernel<WM, WNT, NP><<<grid, 128, 0, s>>>(act, lo, a_kt, a_blocks, rows, w,
+  tile_gemm_kernel<WM, WNT, NP><<<grid, 256, 0, s>>>(act, lo, a_kt, a_blocks, rows, w,
                                                                               kt_count, n_blocks, tc.tiles_m, n_tiles,
                                                                               o);
 }

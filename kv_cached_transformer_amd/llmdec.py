@@ -92,7 +92,7 @@ _SIGS = {
     "llmdec_op_rmsnorm": (_I, [_P, _P, _I, _I, _F, _P, _P, _P, _I, _P]),
     "llmdec_op_linear_ws_bytes": (_Z, [_I, _I, _I]),
     "llmdec_op_linear": (_I, [_P, _I, _I, _P, _I, _P, _I, _I, _P, _Z, _P]),
-    "llmdec_op_swiglu_linear": (_I, [_P, _I, _I, _P, _I, _P, _I, _P, _Z, _P]),
+    "llmdec_op_swiglu_linear": (_I, [_P, _I, _I, _P, _I, _P, _P, _I, _I, _P, _Z, _P]),
     "llmdec_op_rope_append": (_I, [_CFG, _P, _I, _I, _P, _P, _P, _I, _P, _I, _P, _Z, _P]),
     "llmdec_op_decode_attention": (_I, [_CFG, _P, _I, _P, _P, _I, _P, _I, _P, _P, _Z, _P]),
     "llmdec_op_prefill_attention": (_I, [_CFG, _P, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, _Z, _P]),
@@ -273,9 +273,10 @@ def llmdec_op_linear(a, rows, k_dim, w_packed, n_dim, out, accumulate, ws, ws_by
                                   stream))
 
 
-def llmdec_op_swiglu_linear(a, rows, k_dim, w_gu_packed, inter, out_act, ld_packed, ws, ws_bytes, stream=0):
-    _check(lib().llmdec_op_swiglu_linear(a, rows, k_dim, w_gu_packed, inter, out_act, ld_packed, ws, ws_bytes,
-                                         stream))
+def llmdec_op_swiglu_linear(a, rows, k_dim, w_gu_packed, inter, out_act, ld_packed, ws, ws_bytes, stream=0,
+                            act_parts=1, out_lo=None):
+    _check(lib().llmdec_op_swiglu_linear(a, rows, k_dim, w_gu_packed, inter, out_act, out_lo, ld_packed,
+                                         int(act_parts), ws, ws_bytes, stream))
 
 
 def llmdec_op_rope_append(cfg, qkv, n_tokens, n_seqs, seq_of_token, pos_of_token, block_tables, max_pages, pool,

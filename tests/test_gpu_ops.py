@@ -184,13 +184,15 @@ def test_packed_weights_exact_in_fp16(L, R):
     assert np.array_equal(out.cpu().numpy().astype(np.float64), od.widen_bf16(w).T[:80])
 
 
+@pytest.mark.parametrize("parts", [1, 2])
 @pytest.mark.parametrize("rows,inter,k", [(1, 688, 256), (7, 11008, 4096), (64, 11008, 4096), (200, 688, 256),
                                           (2048, 11008, 4096)])
-def test_swiglu_linear(L, R, rows, inter, k):
-    """u = silu(g) * up, g and up the products of the fp16 activation, stored in fp16: against the oracle's
-    value from the same rounded activation, each stored value is its nearest fp16 or, near a rounding
-    boundary, the neighbour (fp32 products and silu on the device)."""
-    banner(f"swiglu_linear rows={rows} inter={inter} k={k}")
+def test_swiglu_linear(L, R, rows, inter, k, parts):
+    """u = silu(g) * up, g and up the products of the fp16 activation (parts = 1) or of the fp16 pair (parts =
+    2), stored in fp16 (parts = 2: as the pair hi + lo).  Against the oracle's value from the same rounded
+    activation, each stored fp16 value is its nearest fp16 or, near a rounding boundary, the neighbour
+    (fp32 products and silu on the device); the pair carries u to the fp32-level bound."""
+    banner(f"swiglu_linear rows={rows} inter={inter} k={k} parts={parts}")
     rng = np.random.default_rng(rows + inter + k)
     a = rng.standard_normal((rows, k)).astype(np.float32)
     wg, wu = bf16_normal(rng, (inter, k), 0.02), bf16_normal(rng, (inter, k), 0.02)
@@ -201,19 +203,28 @@ def test_swiglu_linear(L, R, rows, inter, k):
     pm = R.PackedMatrix(2 * inter, k, gu)
     ld = (inter + 31) // 32 * 32
     act = torch.full((((rows + 15) // 16) * 16 * ld,), -1, dtype=torch.int16, device="cuda")
+    lo = torch.full_like(act, -1)
     ws = R.Workspace(L.llmdec_op_linear_ws_bytes(rows, k, 2 * inter))
     ad = R.dev_f32(a)
     L.llmdec_op_swiglu_linear(ad.data_ptr(), rows, k, pm.ptr, inter, act.data_ptr(), ld, ws.ptr, ws.nbytes,
-                              R.stream())
+                              R.stream(), act_parts=parts, out_lo=lo.data_ptr() if parts == 2 else None)
     torch.cuda.synchronize()
-    a16 = od.round_to_f16(a.astype(np.float64))
-    ref = od.silu(a16 @ od.widen_bf16(wg).T) * (a16 @ od.widen_bf16(wu).T)
+    a64 = a.astype(np.float64)
+    a_used = od.round_to_f16(a64) if parts == 1 else od.f16_pair(a64)
+    ref = od.silu(a_used @ od.widen_bf16(wg).T) * (a_used @ od.widen_bf16(wu).T)
     full = unpack_tiled(R.host_u16(act), rows, ld, ld)
     assert np.all(full[:, inter:] == 0)
+    hi = f64_from_f16(full[:, :inter])
     # abs_slack: the fp32 products g and up differ from the exact ones by about sqrt(k / 32) * 2^-24 of
     # their size (~1e-6 here), which near u = 0 exceeds fp16's spacing there
-    assert_rounded(f"swiglu {rows}x{inter}x{k}", f64_from_f16(full[:, :inter]), ref, od.round_to_f16, f16_ulp, 0.005,
-                   abs_slack=1e-5)
+    assert_rounded(f"swiglu {rows}x{inter}x{k} x{parts}", hi, ref, od.round_to_f16, f16_ulp, 0.005, abs_slack=1e-5)
+    if parts == 2:
+        lfull = unpack_tiled(R.host_u16(lo), rows, ld, ld)
+        assert np.all(lfull[:, inter:] == 0)
+        # the pair carries u to fp32 level: the fp32 sums g and up differ from the exact ones by up to a few
+        # sqrt(k / 32) * 2^-24 * |g| (1e-5 at the largest of 2e7 values), times |up| up to about 6
+        assert_close(f"swiglu pair {rows}x{inter}x{k}", hi + f64_from_f16(lfull[:, :inter]), ref, max_abs=2e-4,
+                     rel_l2=2e-6)
 
 
 # ----------------------------------------------------------------------------- RoPE + append

@@ -377,6 +377,26 @@ llmdec_status llmdec_model_step_sample(const llmdec_config *cfg, const llmdec_mo
                                        const llmdec_sampling *params, int32_t *next_tokens, float *logits, void *ws,
                                        size_t ws_bytes, llmdec_stream stream);
 
+/* For callers that cannot allocate device memory, not even a workspace (code
+ * under HIP graph capture, serving loops and harnesses that forbid
+ * allocation): llmdec_model_step_greedy with its workspace in a device array
+ * of the library, 48 MiB per GPU (enough for 7B-shaped decode steps of up to
+ * 64 sequences), held from the first call on that GPU until the process
+ * ends.  Same arguments as llmdec_model_step_greedy without ws / ws_bytes;
+ * error_bits (dev uint32, nullable) receives this call's device error word
+ * (the bits llmdec_workspace_error reports).  E_WORKSPACE when the step needs
+ * more workspace than the array holds.  The call allocates nothing.  Every
+ * call on a GPU uses that GPU's one array: calls that overlap on one GPU
+ * (two streams, two threads) race.  The first call on a GPU looks up the
+ * array's address; make it outside graph capture. */
+llmdec_status llmdec_model_step_greedy_noalloc(const llmdec_config *cfg, const llmdec_model_weights *w, int32_t n_seqs,
+                                               int32_t n_tokens, int32_t max_q_len, const int32_t *tokens,
+                                               const int32_t *cu_seqlens, const int32_t *start_pos,
+                                               const int32_t *block_tables, int32_t max_pages, llmdec_kv_pool *pool,
+                                               int32_t *next_tokens, float *logits, uint32_t *error_bits,
+                                               llmdec_stream stream);
+
+
 /* ------------------------------------------------------------------ group-quantized weights
  * [W] §4.2: a matrix stored as integers in groups of 128 consecutive elements,
  * each group with one scale and one zero point, turned back into floating

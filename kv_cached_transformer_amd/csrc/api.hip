@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <mutex>
 
 #include "common.h"
 #include "internal.h"
@@ -501,6 +502,65 @@ extern "C" llmdec_status llmdec_model_step_sample(const llmdec_config *cfg, cons
   return model_step(who, cfg, w, n_seqs, n_tokens, max_q_len, tokens, cu_seqlens, start_pos, block_tables, max_pages,
                     pool, params, next_tokens, logits, ws, ws_bytes, stream);
 }
+
+// ------------------------------------------------------------------ the step without a workspace
+// For callers that cannot allocate (code under graph capture, serving loops that forbid allocation): the
+// greedy model step with its workspace in a device array of this library (48 MiB, enough for 7B-shaped
+// decode steps of up to 64 sequences), one copy per GPU, held until the process ends.  Its address on
+// each device is looked up once, with that device current, and the kernels only ever get that address.
+constexpr size_t kScratchBytes = (size_t)48 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch[kMaxDevices];
+
+static llmdec_status scratch_address(const char *who, void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(LLMDEC_E_HIP, "%s: no current device (or device id %d beyond %d)", who, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(LLMDEC_E_HIP, "%s: address of the static workspace on device %d: %s", who, dev,
+                       hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return LLMDEC_OK;
+}
+
+extern "C" llmdec_status llmdec_model_step_greedy_noalloc(const llmdec_config *cfg, const llmdec_model_weights *w,
+                                                         int32_t n_seqs, int32_t n_tokens, int32_t max_q_len,
+                                                         const int32_t *tokens, const int32_t *cu_seqlens,
+                                                         const int32_t *start_pos, const int32_t *block_tables,
+                                                         int32_t max_pages, llmdec_kv_pool *pool, int32_t *next_tokens,
+                                                         float *logits, uint32_t *error_bits, llmdec_stream stream) {
+  const char *who = "model_step_greedy_noalloc";
+  llmdec_status st = check_config(cfg, who);
+  if (st != LLMDEC_OK) return st;
+  if (n_seqs <= 0 || n_tokens <= 0 || max_pages <= 0)
+    return set_error(LLMDEC_E_INVALID, "%s: n_seqs=%d n_tokens=%d max_pages=%d out of range", who, n_seqs, n_tokens,
+                     max_pages);
+  const size_t need = ws_layout(*cfg, n_tokens, n_seqs, max_pages).total;
+  if (need > kScratchBytes)
+    return set_error(LLMDEC_E_WORKSPACE, "%s: the step needs %zu bytes of workspace, the static one holds %zu", who, need,
+                     kScratchBytes);
+  void *ws = nullptr;
+  st = scratch_address(who, &ws);
+  if (st != LLMDEC_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // the array keeps the previous call's contents: only the error word must start at zero (every other
+  // region is written before it is read)
+  launch_fill_u32((uint32_t *)ws, 0u, kWsHeader / 4, s);
+  st = model_step(who, cfg, w, n_seqs, n_tokens, max_q_len, tokens, cu_seqlens, start_pos, block_tables, max_pages,
+                  pool, nullptr, next_tokens, logits, ws, kScratchBytes, stream);
+  if (st != LLMDEC_OK) return st;
+  if (error_bits) launch_copy_u32((const uint32_t *)ws, error_bits, s);
+  return check_launch(who);
+}
+
 
 extern "C" llmdec_status llmdec_op_sample(const float *logits, int32_t rows, int32_t vocab,
                                          const llmdec_sampling *params, int32_t *next, llmdec_stream stream) {

@@ -89,6 +89,8 @@ _SIGS = {
     "llmdec_layer_decode": (_I, [_CFG, C.POINTER(llmdec_packed_layer), _I, _P, _I, _P, _P, _I, _P, _P, _Z, _P]),
     "llmdec_model_step_greedy": (_I, [_CFG, C.POINTER(llmdec_model_weights), _I, _I, _I, _P, _P, _P, _P, _I, _P, _P,
                                       _P, _P, _Z, _P]),
+    "llmdec_model_step_greedy_noalloc": (_I, [_CFG, C.POINTER(llmdec_model_weights), _I, _I, _I, _P, _P, _P, _P, _I,
+                                              _P, _P, _P, _P, _P]),
     "llmdec_op_rmsnorm": (_I, [_P, _P, _I, _I, _F, _P, _P, _P, _I, _P]),
     "llmdec_op_linear_ws_bytes": (_Z, [_I, _I, _I]),
     "llmdec_op_linear": (_I, [_P, _I, _I, _P, _I, _P, _I, _I, _P, _Z, _P]),
@@ -258,6 +260,13 @@ def llmdec_model_step_greedy(cfg, mw, n_seqs, n_tokens, max_q_len, tokens, cu_se
     _check(lib().llmdec_model_step_greedy(C.byref(cfg), C.byref(mw), n_seqs, n_tokens, max_q_len, tokens, cu_seqlens,
                                           start_pos, block_tables, max_pages, pool, next_tokens, logits, ws, ws_bytes,
                                           stream))
+
+
+def llmdec_model_step_greedy_noalloc(cfg, mw, n_seqs, n_tokens, max_q_len, tokens, cu_seqlens, start_pos,
+                                     block_tables, max_pages, pool, next_tokens, logits, error_bits, stream=0):
+    _check(lib().llmdec_model_step_greedy_noalloc(C.byref(cfg), C.byref(mw), n_seqs, n_tokens, max_q_len, tokens,
+                                                  cu_seqlens, start_pos, block_tables, max_pages, pool, next_tokens,
+                                                  logits, error_bits, stream))
 
 
 def llmdec_op_rmsnorm(x, gamma, rows, n, eps, out_f32, out_act=None, out_lo=None, ld_packed=0, stream=0):

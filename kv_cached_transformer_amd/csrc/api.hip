@@ -127,6 +127,7 @@ struct LayerArgs {
   void *ws;
   WsLayout L;
   hipStream_t s;
+  Splits pending;  // split-k partial sums of the previous layer's down projection, not yet in hidden
 };
 
 // Decode of a single sequence: every product is a matrix-vector product (one-row kernels with the
@@ -157,13 +158,16 @@ static void run_layer_one_row(const LayerArgs &a) {
   launch_gemv(u, nullptr, 0.f, (const uint16_t *)a.w->w_down, h, I, kAccumulate, a.hidden, a.s);
 }
 
-static void run_layer(const LayerArgs &a) {
+// Returns the split of the down projection whose partial sums are left in the workspace instead of added
+// into hidden (none when it was not split); the caller adds them (finish_layer) or hands them to the next
+// layer, whose attention RMSNorm adds them into hidden before normalising.
+static Splits run_layer(const LayerArgs &a) {
   const llmdec_config &c = *a.cfg;
   const int h = c.hidden, I = c.intermediate, M = a.rows;
   const WsLayout &L = a.L;
   if (a.decode && M == 1 && gemv_shape_ok(h) && gemv_shape_ok(I)) {
     run_layer_one_row(a);
-    return;
+    return Splits{};
   }
   uint32_t *err = at<uint32_t>(a.ws, L.err);
   uint16_t *act_h = at<uint16_t>(a.ws, L.act_h), *act_hl = at<uint16_t>(a.ws, L.act_hl);
@@ -182,7 +186,7 @@ static void run_layer(const LayerArgs &a) {
 
   // attention block: x += Wo . attn(rope(Wq y), rope(Wk y), Wv y),  y = RMSNorm(x)
   launch_rmsnorm(a.hidden, h, nullptr, M, (const uint16_t *)a.w->attn_norm, M, h, c.rms_eps, err, nullptr, act_h,
-                 act_hl, L.kpad_h, nullptr, Splits{}, a.s);
+                 act_hl, L.kpad_h, a.pending.any() ? part : nullptr, a.pending, a.s);
   LinearOut o_qkv;
   o_qkv.kind = kStore;
   o_qkv.f32 = qkv;
@@ -223,8 +227,17 @@ static void run_layer(const LayerArgs &a) {
   o_gu.act_cols = I;
   const Splits sp_gu = launch_linear(ah, (const uint16_t *)a.w->w_gu, 2 * I, h, o_gu, part, L.part_floats, kSplitBalanced, a.s);
   if (sp_gu.any()) launch_reduce(part, sp_gu, M, 2 * I, o_gu, a.s);
-  const Splits sp_d = launch_linear(ai, (const uint16_t *)a.w->w_down, h, I, o_res, part, L.part_floats, kSplitBalanced, a.s);
-  if (sp_d.any()) launch_reduce(part, sp_d, M, h, o_res, a.s);
+  return launch_linear(ai, (const uint16_t *)a.w->w_down, h, I, o_res, part, L.part_floats, kSplitBalanced, a.s);
+}
+
+// Adds a layer's pending down-projection partial sums into hidden.
+static void finish_layer(const LayerArgs &a, const Splits &pending) {
+  if (!pending.any()) return;
+  LinearOut o_res;
+  o_res.kind = kAccumulate;
+  o_res.f32 = a.hidden;
+  o_res.ld = a.cfg->hidden;
+  launch_reduce(at<float>(a.ws, a.L.part), pending, a.rows, a.cfg->hidden, o_res, a.s);
 }
 
 }  // namespace llmdec
@@ -384,8 +397,8 @@ extern "C" llmdec_status llmdec_layer_prefill(const llmdec_config *cfg, const ll
   st = check_ws(ws, ws_bytes, L.total, who);
   if (st != LLMDEC_OK) return st;
   LayerArgs a{cfg, w, layer, hidden, n_tokens, false, n_seqs, max_q_len, cu_seqlens, start_pos, nullptr,
-              block_tables, max_pages, pool, ws, L, (hipStream_t)stream};
-  run_layer(a);
+              block_tables, max_pages, pool, ws, L, (hipStream_t)stream, Splits{}};
+  finish_layer(a, run_layer(a));
   return check_launch(who);
 }
 
@@ -405,8 +418,8 @@ extern "C" llmdec_status llmdec_layer_decode(const llmdec_config *cfg, const llm
   st = check_ws(ws, ws_bytes, L.total, who);
   if (st != LLMDEC_OK) return st;
   LayerArgs a{cfg, w, layer, hidden, n_seqs, true, n_seqs, 1, nullptr, nullptr, ctx_lens, block_tables, max_pages,
-              pool, ws, L, (hipStream_t)stream};
-  run_layer(a);
+              pool, ws, L, (hipStream_t)stream, Splits{}};
+  finish_layer(a, run_layer(a));
   return check_launch(who);
 }
 
@@ -451,10 +464,12 @@ static llmdec_status model_step(const char *who, const llmdec_config *cfg, const
   hipStream_t s = (hipStream_t)stream;
   float *x = at<float>(ws, L.x);
   launch_embed((const uint16_t *)w->embed, tokens, n_tokens, cfg->hidden, cfg->vocab, x, at<uint32_t>(ws, L.err), s);
+  Splits pending{};  // each layer's down-projection partial sums go into the next layer's RMSNorm
   for (int l = 0; l < cfg->n_layers; ++l) {
     LayerArgs a{cfg, &w->layers[l], l, x, n_tokens, decode, n_seqs, max_q_len, cu_seqlens, start_pos,
-                decode ? start_pos : nullptr, block_tables, max_pages, pool, ws, L, s};
-    run_layer(a);
+                decode ? start_pos : nullptr, block_tables, max_pages, pool, ws, L, s, pending};
+    pending = run_layer(a);
+    if (l + 1 == cfg->n_layers) finish_layer(a, pending);
   }
   // final norm on each sequence's last new token, lm_head, argmax ([W] §1.1, [F] §2.2.3)
   const int h = cfg->hidden;

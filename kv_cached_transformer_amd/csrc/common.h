@@ -68,6 +68,29 @@ __device__ inline void add_splits(V &acc, const float *p, size_t stride, int ks)
       if (q + j < ks) vadd(acc, v[j]);
   }
 }
+// N independent sums at once (acc[i] += the partials at p[i]): every batch issues the loads of all N
+// before the first add, so N sums cost the memory round trips of one.  Each sum is added in plane order,
+// exactly as add_splits adds it.
+template <int N, typename V>
+__device__ inline void add_splits_n(V (&acc)[N], const float *const (&p)[N], size_t stride, const int (&ks)[N]) {
+  constexpr int B = N <= 2 ? 16 : 8;  // planes per batch
+  int kmax = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) kmax = ks[i] > kmax ? ks[i] : kmax;
+  for (int q = 0; q < kmax; q += B) {
+    V v[N][B];
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if (q + j < ks[i]) v[i][j] = *reinterpret_cast<const V *>(p[i] + (size_t)(q + j) * stride);
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if (q + j < ks[i]) vadd(acc[i], v[i][j]);
+  }
+}
 
 __host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 __host__ __device__ inline size_t round_up_sz(size_t x, size_t m) { return (x + m - 1) / m * m; }

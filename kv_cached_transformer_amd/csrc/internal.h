@@ -118,6 +118,12 @@ Splits launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const
                      size_t partial_floats, SplitPolicy policy, hipStream_t s);
 // Sum the partial products of a split product and apply the epilogue o.
 void launch_reduce(const float *partials, const Splits &sp, int rows, int n, const LinearOut &o, hipStream_t s);
+
+struct RopeFreq {
+  double inv_freq[64];
+};
+RopeFreq rope_freq(const llmdec_config &cfg);
+
 size_t linear_partial_floats(int rows, int n, int k, SplitPolicy policy = kSplitBalanced);
 void launch_token_map(const int32_t *cu_seqlens, const int32_t *start_pos, int n_seqs, int n_tokens, uint32_t *err, int32_t *tok_seq,
                       int32_t *tok_pos, hipStream_t s);
@@ -151,10 +157,6 @@ void launch_fill_u32(uint32_t *p, uint32_t value, size_t n, hipStream_t s);
 void launch_copy_u32(const uint32_t *src, uint32_t *dst, hipStream_t s);
 
 // Rotary frequencies inv_freq[i] = theta^(-2i/D), i < D/2 (zero past), computed in double on the host.
-struct RopeFreq {
-  double inv_freq[64];
-};
-RopeFreq rope_freq(const llmdec_config &cfg);
 
 // Where the one-row q|k|v product sends its result when it also applies RoPE and the paged append (a
 // single decode token of sequence 0 at position *pos): rotated q to its output, rotated bf16 k and bf16

@@ -39,8 +39,7 @@
 // W's row blocks alternate gate / up (block 2j: gate rows 16j.., block 2j+1:
 // up rows 16j..) and the kernel writes silu(g) * u straight into the packed
 // fp16 activation of the down projection.
-#include "common.h"
-#include "internal.h"
+#include "bodies.h"
 
 namespace llmdec {
 
@@ -114,15 +113,17 @@ template <int MB, int WN, int NP> struct SgShape {
 // (column group, k-tile) units group by group; each group segment runs the
 // ring over its k-tiles and leaves either the finished result (no split) or
 // one plane of partial sums.
+//
+// The body takes the block index and the LDS (S::LDS_U4 entries) as arguments, so that the fused decode
+// programs can run it as one of their stages.
 template <int MB, int WN, int NP>
-__global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__restrict__ a_act,
-                                                             const uint4 *__restrict__ a_lo, int a_kt, int rows,
-                                                             const uint4 *__restrict__ w, int kt_count, int n_blocks,
-                                                             LinearOut o, float *__restrict__ partials, Splits sp) {
+__device__ __forceinline__ void stream_gemm_body(uint4 *lds, int bid, const uint4 *__restrict__ a_act,
+                                                 const uint4 *__restrict__ a_lo, int a_kt, int rows,
+                                                 const uint4 *__restrict__ w, int kt_count, int n_blocks,
+                                                 const LinearOut &o, float *__restrict__ partials, const Splits &sp) {
   using S = SgShape<MB, WN, NP>;
   constexpr int WK = S::WK, NA = S::NA, APW = S::APW, D = S::D, R = S::R;
   constexpr bool SHARE = WN > 1;
-  __shared__ uint4 lds[S::LDS_U4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar control
   const int cw = wave % WN, kw = wave / WN;
@@ -147,8 +148,8 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__rest
   }
 
   // this block's units; without a split every block is one whole column group
-  long u = sp.any() ? (long)blockIdx.x * sp.units / sp.blocks : (long)blockIdx.x * kt_count;
-  const long u_end = sp.any() ? (long)(blockIdx.x + 1) * sp.units / sp.blocks : u + kt_count;
+  long u = sp.any() ? (long)bid * sp.units / sp.blocks : (long)bid * kt_count;
+  const long u_end = sp.any() ? (long)(bid + 1) * sp.units / sp.blocks : u + kt_count;
   while (u < u_end) {  // one segment per column group touched (block-uniform)
     const int g = (int)(u / kt_count);
     const int kt0 = (int)(u - (long)g * kt_count);
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__rest
     if (kw == 0 && nbs > 0) {
       const float wunscale = weight_unscale(w + (size_t)n_blocks * kt_count * 64);
       if (sp.any()) {  // plane = this block's place among the blocks covering group g
-        float *plane = partials + (size_t)(blockIdx.x - sp.first_block((long)g * kt_count)) * rows * n;
+        float *plane = partials + (size_t)(bid - sp.first_block((long)g * kt_count)) * rows * n;
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -282,28 +283,38 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__rest
   }
 }
 
+template <int MB, int WN, int NP>
+__global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__restrict__ a_act,
+                                                             const uint4 *__restrict__ a_lo, int a_kt, int rows,
+                                                             const uint4 *__restrict__ w, int kt_count, int n_blocks,
+                                                             LinearOut o, float *__restrict__ partials, Splits sp) {
+  __shared__ uint4 lds[SgShape<MB, WN, NP>::LDS_U4];
+  stream_gemm_body<MB, WN, NP>(lds, blockIdx.x, a_act, a_lo, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
+}
+
 // ---------------------------------------------------------------- split-k reduction
 // Sums the ks partials of each output in split order (deterministic) and applies the epilogue.  One
 // thread per 8 consecutive columns of a row for the SwiGLU epilogue, so every store is a lane's
 // 16-byte chunk of the packed fp16 activation (the threads of gate columns also read the matching up
 // columns, 16 further on); one thread per 4 columns (one float4) for fp32 outputs.
-__global__ void reduce_kernel(const float *__restrict__ partials, Splits sp, int rows, int n, LinearOut o) {
+__device__ __forceinline__ void reduce_item(size_t idx, const float *__restrict__ partials, const Splits &sp,
+                                            int rows, int n, const LinearOut &o) {
   const int cpt = o.kind == kSiluMul ? 8 : 4;  // columns per thread
   const int nt = n / cpt;
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (size_t)rows * nt) return;
   const int r = (int)(idx / nt), c = (int)(idx % nt) * cpt;
   if (o.kind == kSiluMul && ((c >> 4) & 1)) return;  // up columns: read by their gate's thread
   const size_t plane = (size_t)rows * n;
   const int ks = sp.slots(c);  // c..c+cpt-1 (and the up columns c+16..) lie in one column group
   const float *p = partials + (size_t)r * n + c;
-  float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
-  add_splits(s0, p, plane, ks);
+  float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f);
   if (o.kind == kSiluMul) {
-    add_splits(s1, p + 4, plane, ks);
-    float4 u0 = make_float4(0.f, 0.f, 0.f, 0.f), u1 = u0;
-    add_splits(u0, p + 16, plane, ks);
-    add_splits(u1, p + 20, plane, ks);
+    float4 acc[4] = {s0, s0, s0, s0};  // gate columns c..c+7, then the matching up columns c+16..c+23
+    const float *src[4] = {p, p + 4, p + 16, p + 20};
+    const int kss[4] = {ks, ks, ks, ks};
+    add_splits_n<4>(acc, src, plane, kss);
+    s0 = acc[0];
+    const float4 s1 = acc[1], u0 = acc[2], u1 = acc[3];
     const float y[8] = {silu_f(s0.x) * u0.x, silu_f(s0.y) * u0.y, silu_f(s0.z) * u0.z, silu_f(s0.w) * u0.w,
                         silu_f(s1.x) * u1.x, silu_f(s1.y) * u1.y, silu_f(s1.z) * u1.z, silu_f(s1.w) * u1.w};
     const int j = ((c >> 5) << 4) | (c & 15);  // gate column -> activation column (a multiple of 8)
@@ -324,10 +335,16 @@ __global__ void reduce_kernel(const float *__restrict__ partials, Splits sp, int
       if (o.act_lo) *reinterpret_cast<uint4 *>(o.act_lo + pad) = make_uint4(0, 0, 0, 0);
     }
   } else {
+    add_splits(s0, p, plane, ks);
     float4 *q = reinterpret_cast<float4 *>(o.f32 + (size_t)r * o.ld + c);
     if (o.kind == kAccumulate) vadd(s0, *q);
     *q = s0;
   }
+}
+
+__global__ __launch_bounds__(256) void reduce_kernel(const float *__restrict__ partials, Splits sp, int rows, int n,
+                                                     LinearOut o) {
+  reduce_item((size_t)blockIdx.x * blockDim.x + threadIdx.x, partials, sp, rows, n, o);
 }
 
 void launch_reduce(const float *partials, const Splits &sp, int rows, int n, const LinearOut &o, hipStream_t s) {
@@ -687,5 +704,6 @@ Splits launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const
   if (a.lo) return launch_linear_np<2>(a, w_packed, n, k, o, partials, partial_floats, policy, s);
   return launch_linear_np<1>(a, w_packed, n, k, o, partials, partial_floats, policy, s);
 }
+
 
 }  // namespace llmdec

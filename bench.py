@@ -32,6 +32,8 @@ Profiling helpers (no GPU needed for the two summaries):
   python bench.py --only copy                  1 GiB device copies: calibrates the HBM counters
   python bench.py --pmc-summary FETCH WRITE    traffic summary from two rocprofv3 --pmc runs
   python bench.py --trace-summary DIR          per-kernel table from a rocprofv3 --kernel-trace run
+  python bench.py --traffic-table FETCH WRITE  HBM bytes per dispatch of every kernel (two --pmc runs)
+  python bench.py --mfma-summary DIR           MFMA busy fraction and issued FLOPs per kernel (one --pmc run)
 The roofline's traffic field is read from the committed traffic summary, and
 only while the attention sources still hash to the value recorded there.
 """
@@ -654,7 +656,70 @@ def pmc_summary(fetch_dir, write_dir):
     alg = attn_alg_bytes(10, 3)
     out.append(f"algorithmic_bytes_per_call: {alg:.0f}")
     out.append(f"traffic_bytes_per_call: {total:.0f}  (x{total / alg:.3f} the algorithmic bytes)")
+    out.append("# Every kernel of the run with at least 1% of its traffic, bytes per dispatch (the run holds the")
+    out.append("# 13 model steps, the standalone attention calls, the 13 graph-replayed steps and the weight setup):")
+    out += traffic_table(fetch_dir, write_dir)
     print("\n".join(out))
+
+
+def traffic_table(fetch_dir, write_dir, min_share=0.01):
+    """HBM bytes per dispatch (FETCH_SIZE + WRITE_SIZE, each scaled by the 1 GiB copy's reading) of every
+    kernel, grouped by name and grid, over all of a run's dispatches; kernels under min_share of the
+    run's traffic are left out."""
+    import collections
+    fr, wr = _pmc_rows(fetch_dir, "FETCH_SIZE"), _pmc_rows(write_dir, "WRITE_SIZE")
+    copy_f = max(float(r["Counter_Value"]) for r in fr if "copy" in r["Kernel_Name"].lower())
+    copy_w = max(float(r["Counter_Value"]) for r in wr if "copy" in r["Kernel_Name"].lower())
+    kf, kw = COPY_BYTES / (copy_f * 1024), COPY_BYTES / (copy_w * 1024)
+    agg = collections.defaultdict(lambda: [0.0, 0, 0.0, 0])
+    for rows, i, k in ((fr, 0, kf), (wr, 2, kw)):
+        for r in rows:
+            if "copy" in r["Kernel_Name"].lower():
+                continue
+            key = (r["Kernel_Name"].split("(")[0].replace("void ", "")[:52], r["Grid_Size"])
+            agg[key][i] += float(r["Counter_Value"]) * 1024 * k
+            agg[key][i + 1] += 1
+    total = sum(v[0] + v[2] for v in agg.values())
+    out = [f"copy_fetch_kib: {copy_f:.1f}  fetch_scale: {kf:.4f}", f"copy_write_kib: {copy_w:.1f}  write_scale: {kw:.4f}",
+           f"{'kernel':52s} {'grid':>9s} {'dispatches':>10s} {'MB read':>9s} {'MB written':>10s}  (per dispatch)"]
+    for (name, grid), v in sorted(agg.items(), key=lambda kv: -(kv[1][0] + kv[1][2])):
+        if v[0] + v[2] < min_share * total or not v[1] or not v[3]:
+            continue
+        out.append(f"{name:52s} {grid:>9s} {v[1]:10d} {v[0] / v[1] / 1e6:9.2f} {v[2] / v[3] / 1e6:10.2f}")
+    return out
+
+
+def mfma_summary(d):
+    """MFMA use per kernel from a rocprofv3 --pmc run with SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_F16,
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 and GRBM_GUI_ACTIVE: busy = MFMA busy cycles / (1024 SIMDs x GUI-active
+    cycles, summed over the 8 XCDs), issued FLOPs = 512 x MOPS, and the issued rate over the dispatch's
+    duration."""
+    import collections
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    agg = collections.defaultdict(lambda: collections.defaultdict(float))
+    durs = collections.defaultdict(dict)
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                key = (r["Kernel_Name"].split("(")[0].replace("void ", "")[:52], r["Grid_Size"])
+                agg[key][r["Counter_Name"]] += float(r["Counter_Value"])
+                durs[key][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    print(f"{'kernel':52s} {'grid':>9s} {'calls':>5s} {'avg us':>8s} {'MFMA busy':>9s} {'GFLOP issued':>12s} "
+          f"{'TFLOP/s issued':>14s}")
+    for key, c in sorted(agg.items(), key=lambda kv: -sum(durs[kv[0]].values())):
+        ops = c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        n = len(durs[key])
+        if not ops or not n:
+            continue
+        t = sum(durs[key].values()) / n
+        gui = c.get("GRBM_GUI_ACTIVE", 0.0) / n
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / n / (1024 * gui / 8) if gui else float("nan")
+        flop = 512 * ops / n
+        print(f"{key[0]:52s} {key[1]:>9s} {n:5d} {t * 1e6:8.1f} {busy:9.3f} {flop / 1e9:12.1f} {flop / t / 1e12:14.1f}")
 
 
 def read_traffic(attn_bytes_now):
@@ -705,12 +770,21 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the attention traffic summary from two rocprofv3 --pmc output folders")
     ap.add_argument("--trace-summary", metavar="DIR", help="print a per-kernel table from a rocprofv3 kernel trace")
+    ap.add_argument("--traffic-table", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print HBM bytes per dispatch of every kernel from two rocprofv3 --pmc output folders")
+    ap.add_argument("--mfma-summary", metavar="DIR", help="print MFMA use per kernel from a rocprofv3 --pmc run")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
         return
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.traffic_table:
+        print("\n".join(traffic_table(*args.traffic_table)))
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "

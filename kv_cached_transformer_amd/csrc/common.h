@@ -229,4 +229,36 @@ __device__ inline void raise_error(uint32_t *err, uint32_t bits) {
   if (err) atomicOr(err, bits);
 }
 
+// A 16-byte-per-lane load from a buffer straight into LDS (lane l's bytes land at lds_addr + 16 l).
+// Issued from asm: the compiler neither counts it nor treats it as a write to LDS, so it adds no waits
+// for it before LDS reads (it would wait for every such load in flight, into any stage, before each
+// read).  The callers wait for these loads themselves and synchronise the block before reading a
+// stage.  The descriptor is built by hand: base address, stride 0, num_records bytes, raw-buffer flags.
+__device__ inline u32x4 buffer_desc(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+// M0 carries the LDS address; nothing else in these kernels uses it, so the compiler's note that a
+// clobbered M0 is not preserved does not apply.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void load_to_lds16(uint32_t voff, u32x4 desc, uint32_t soff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(desc), "s"(soff), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N vector-memory loads of this wave are in flight and all its LDS reads are done,
+// then the block barrier.  The wait is the builtin, so the compiler knows the LDS reads have completed
+// (and adds no waits for them later); the barrier is asm with a memory clobber, so the compiler moves
+// no memory access across it.
+template <int N>
+__device__ inline void wait_loads_barrier() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));  // lgkmcnt field (bits 8-11) 0
+  asm volatile("s_barrier" : : : "memory");
+}
+
 }  // namespace llmdec

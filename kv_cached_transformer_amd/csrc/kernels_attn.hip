@@ -660,11 +660,209 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
       store_out(oacc[db][e] * inv, tok, h * D + db * 16 + g * 4 + e, n_heads * D, out_f32, out_act, out_lo, kpad);
 }
 
+// Head dimension 128: four waves per block, one block per (sequence, head, 64 queries); wave w takes the
+// 16 queries of block 4 x + w.  The block walks the keys its last query sees two pages (32 keys) at a
+// time; each chunk's K and V pages go from the pool straight into LDS (16 loads of 1 KiB, four per
+// wave), through three stages, and every wave reads its operands from there, so a page is fetched once
+// per 64 queries instead of once per 16.  Step: wait for the chunk's loads, barrier, issue the loads of
+// the chunk two ahead (into the stage the previous step read), then the same scores / online softmax /
+// P.V arithmetic as the one-wave kernel; a wave past its own last key only takes part in the loads and
+// barriers.  Every load lands on a 1 KiB boundary of LDS and writes its 1 KiB in lane order, so the
+// bank-conflict-free layouts come from the choice of source bytes per lane: K rows hold their 16-byte
+// units XOR-swizzled by the row (the 16 keys a wave's lanes read at one column land in 16 different bank
+// groups), and odd V quarters hold theirs with bit 3 of the unit index flipped (a 128-byte shift, so the
+// two quarters one half-wave reads use different banks).
+constexpr int kPfKPage = 16 * 128 * 2;         // one page of one K head: 16 keys x 128 dims, bf16
+constexpr int kPfVQuarter = 4 * 128 * 2;       // one quarter of a V page: 128 dims x 4 keys
+constexpr int kPfVPage = 4 * kPfVQuarter;
+constexpr int kPfStage = 2 * kPfKPage + 2 * kPfVPage;
+constexpr int kPfStages = 3;
+
+__global__ __launch_bounds__(256) void prefill_attn4_kernel(const float *__restrict__ q, int ld_q, int n_heads,
+                                                            int n_kv_heads, int n_tokens, int max_q_len,
+                                                            const int32_t *__restrict__ cu,
+                                                            const int32_t *__restrict__ start_pos,
+                                                            const int32_t *__restrict__ block_tables, int max_pages,
+                                                            const uint16_t *__restrict__ pool_k,
+                                                            const uint16_t *__restrict__ pool_v, int num_pages,
+                                                            float *out_f32, uint16_t *out_act, uint16_t *out_lo,
+                                                            int kpad, uint32_t *err) {
+  constexpr int D = 128, KT = D / 32, DB = D / 16;
+  __shared__ uint4 lds[kPfStages * kPfStage / 16];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)lds;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int qg = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int kvh = h / (n_heads / n_kv_heads);
+  const int t0 = cu[s], len = cu[s + 1] - t0;
+  if (t0 < 0 || len < 0 || len > max_q_len || t0 + len > n_tokens || start_pos[s] < 0) {
+    if (threadIdx.x == 0 && qg == 0 && h == 0) raise_error(err, kErrSeq);
+    return;
+  }
+  if (qg * 64 >= len) return;  // block-uniform
+  const int qb = qg * 4 + wave;
+  const int n_q = max(0, min(16, len - qb * 16));
+  const int pos0 = start_pos[s] + qb * 16, my_pos = pos0 + c;
+  const bool q_ok = c < n_q;
+  const float scale = kLog2e * rsqrtf((float)D);
+  uint4 qs[3][KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    float qv[8];
+    if (q_ok) {
+      const float *qp = q + (size_t)(t0 + qb * 16 + c) * ld_q + h * D + kt * 32 + g * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qv[j] = qp[j] * scale;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qv[j] = 0.f;
+    }
+    split3_pack8(qv, qs[0][kt], qs[1][kt], qs[2][kt]);
+  }
+  const int blk_last = start_pos[s] + min(len, qg * 64 + 64) - 1;  // the block's last query position
+  const int n_kpages = (blk_last >> 4) + 1;
+  if (n_kpages > max_pages) {
+    if (threadIdx.x == 0) raise_error(err, kErrPos);
+    return;
+  }
+  const int last_pos = pos0 + n_q - 1;  // this wave's (below pos0 when it has no queries)
+  const int32_t *bt = block_tables + (size_t)s * max_pages;
+  const int n_chunks = (n_kpages + 1) / 2;
+
+  // page pi of the sequence, or -1 (past the block's keys, or a bad entry: its loads read zeros)
+  auto page_of = [&](int pi) -> int {
+    if (pi >= n_kpages) return -1;
+    const int pg = bt[pi];
+    return pg >= 0 && pg < num_pages ? pg : -1;
+  };
+  // wave w loads page u = w / 2 of the chunk: its K (w even) or V (w odd) block, 4 x 1 KiB
+  const int u_ld = wave >> 1;
+  const bool ld_v = wave & 1;
+  auto issue = [&](int st, int ch) {
+    const int pg = page_of(2 * ch + u_ld);
+    const size_t blk = ((size_t)(pg < 0 ? 0 : pg) * n_kv_heads + kvh) * (16 * D);
+    const u32x4 d = buffer_desc((ld_v ? pool_v : pool_k) + blk, pg < 0 ? 0u : (uint32_t)kPfKPage);
+    const uint32_t stage = lds_base + (uint32_t)(st * kPfStage);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (ld_v) {  // quarter j: LDS unit l holds the quarter's unit l ^ (8 (j % 2))
+        load_to_lds16((uint32_t)(j * 1024 + ((lane ^ ((j & 1) * 8)) * 16)), d, 0u,
+                      stage + 2 * kPfKPage + u_ld * kPfVPage + j * 1024);
+      } else {  // rows 4j..4j+3; LDS unit l % 16 of row r holds the row's unit (l % 16) ^ (r % 16)
+        const int r = 4 * j + (lane >> 4), unit = (lane & 15) ^ (r & 15);
+        load_to_lds16((uint32_t)(r * 256 + unit * 16), d, 0u, stage + u_ld * kPfKPage + j * 1024);
+      }
+    }
+  };
+
+  f32x4 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -1e30f, l = 0.f;
+  if (threadIdx.x == 0)
+    for (int pi = 0; pi < n_kpages; ++pi)
+      if (bt[pi] < 0 || bt[pi] >= num_pages) raise_error(err, kErrPage);
+
+  issue(0, 0);
+  issue(1, 1);
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const int st = ch % kPfStages;
+    wait_loads_barrier<4>();  // this wave's loads of chunk ch have landed (chunk ch + 1's may be in flight)
+    issue((ch + 2) % kPfStages, ch + 2);
+    if (ch * 32 > last_pos) continue;  // wave-uniform: no key of this chunk is visible to this wave
+    const char *stg = reinterpret_cast<const char *>(lds) + st * kPfStage;
+    int pgs[2];
+    float sc[2][4];
+    uint2 vt[DB][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int pi = 2 * ch + u;
+      const int pg = page_of(pi);
+      pgs[u] = pg;
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+      const char *kp = stg + u * kPfKPage + c * 256;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const uint4 kk = *reinterpret_cast<const uint4 *>(kp + (((kt * 4 + g) ^ c) * 16));
+        sacc = mfma16(kk, qs[2][kt], sacc);  // smallest parts first
+        sacc = mfma16(kk, qs[1][kt], sacc);
+        sacc = mfma16(kk, qs[0][kt], sacc);
+      }
+      // V quarter g (keys 4g..4g+3 of the page), dim db * 16 + c; keys after this wave's last query are
+      // not written yet (possibly NaN): clear them
+      const char *vp = stg + 2 * kPfKPage + u * kPfVPage + g * 1024;
+      const int n_valid = last_pos + 1 - (pi * 16 + g * 4);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int unit = ((db * 16 + c) >> 1) ^ ((g & 1) * 8);  // 8 bytes: half c % 2 of a 16-byte unit
+        uint2 w = *reinterpret_cast<const uint2 *>(vp + unit * 16 + (c & 1) * 8);
+        w.x = mask_pair(w.x, 0, n_valid);
+        w.y = mask_pair(w.y, 2, n_valid);
+        vt[db][u] = w;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kpos = pi * 16 + g * 4 + e;
+        sc[u][e] = (pg >= 0 && q_ok && kpos <= my_pos) ? sacc[e] : -INFINITY;
+      }
+    }
+    (void)pgs;
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = exp2f(m - m_new);
+    m = m_new;
+    float pr[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pr[u * 4 + e] = exp2f(sc[u][e] - m_new);
+        psum += pr[u * 4 + e];
+      }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) oacc[i][e] *= alpha;
+    uint4 ps[3];
+    split3_pack8(pr, ps[0], ps[1], ps[2]);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint4 va = make_uint4(vt[db][0].x, vt[db][0].y, vt[db][1].x, vt[db][1].y);
+      oacc[db] = mfma16(va, ps[2], oacc[db]);
+      oacc[db] = mfma16(va, ps[1], oacc[db]);
+      oacc[db] = mfma16(va, ps[0], oacc[db]);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // the loads issued past the last chunk land before exit
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (!q_ok) return;
+  const float inv = 1.f / l;
+  const int tok = t0 + qb * 16 + c;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      store_out(oacc[db][e] * inv, tok, h * D + db * 16 + g * 4 + e, n_heads * D, out_f32, out_act, out_lo, kpad);
+}
+
 void launch_prefill_attention(const llmdec_config &cfg, const float *q, int ld_q, int n_seqs, int n_tokens, int max_q_len,
                               const int32_t *cu, const int32_t *start_pos, const int32_t *block_tables, int max_pages,
                               const uint16_t *pk, const uint16_t *pv, int num_pages, float *out_f32, uint16_t *out_act,
                               uint16_t *out_lo, int kpad, uint32_t *err, hipStream_t s) {
   if (n_seqs <= 0 || max_q_len <= 0) return;
+  if (cfg.head_dim == 128) {
+    dim3 grid4((max_q_len + 63) / 64, cfg.n_heads, n_seqs);
+    prefill_attn4_kernel<<<grid4, 256, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, n_tokens, max_q_len, cu, start_pos,
+                                               block_tables, max_pages, pk, pv, num_pages, out_f32, out_act, out_lo,
+                                               kpad, err);
+    return;
+  }
   dim3 grid((max_q_len + 15) / 16, cfg.n_heads, n_seqs);
   if (cfg.head_dim == 128)
     prefill_attn_kernel<128><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, n_tokens, max_q_len, cu, start_pos, block_tables, max_pages, pk, pv,

@@ -179,6 +179,12 @@ __device__ inline float weight_unscale(const void *w_end) {
   return __uint_as_float((uint32_t)(127 - weight_shift(bits)) << 23);
 }
 
+// Two fp32 values rounded to bf16 (nearest-even) in one packed conversion: a in the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
 // x = hi + mid + lo with hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid):
 // the differences are exact in fp32 and the three parts carry fp32's precision.
 // Packs 8 values into the three operand registers of a 16x16x32 bf16 MFMA.
@@ -186,18 +192,10 @@ __device__ inline void split3_pack8(const float *x, uint4 &hi, uint4 &mid, uint4
   uint32_t h[4], m[4], l[4];
 #pragma unroll
   for (int j = 0; j < 8; j += 2) {
-    uint16_t hb[2], mb[2], lb[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const float v = x[j + u];
-      hb[u] = f32_to_bf16(v);
-      const float r1 = v - bf16_to_f32(hb[u]);
-      mb[u] = f32_to_bf16(r1);
-      lb[u] = f32_to_bf16(r1 - bf16_to_f32(mb[u]));
-    }
-    h[j / 2] = hb[0] | ((uint32_t)hb[1] << 16);
-    m[j / 2] = mb[0] | ((uint32_t)mb[1] << 16);
-    l[j / 2] = lb[0] | ((uint32_t)lb[1] << 16);
+    h[j / 2] = pack_bf16x2(x[j], x[j + 1]);
+    const float r0 = x[j] - bf16lo(h[j / 2]), r1 = x[j + 1] - bf16hi(h[j / 2]);
+    m[j / 2] = pack_bf16x2(r0, r1);
+    l[j / 2] = pack_bf16x2(r0 - bf16lo(m[j / 2]), r1 - bf16hi(m[j / 2]));
   }
   hi = make_uint4(h[0], h[1], h[2], h[3]);
   mid = make_uint4(m[0], m[1], m[2], m[3]);

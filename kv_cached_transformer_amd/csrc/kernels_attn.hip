@@ -779,31 +779,43 @@ __global__ __launch_bounds__(256) void prefill_attn4_kernel(const float *__restr
       const int pi = 2 * ch + u;
       const int pg = page_of(pi);
       pgs[u] = pg;
-      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+      // one accumulator per 32 dims (independent MFMA chains), added up afterwards
+      f32x4 sk[KT];
       const char *kp = stg + u * kPfKPage + c * 256;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         const uint4 kk = *reinterpret_cast<const uint4 *>(kp + (((kt * 4 + g) ^ c) * 16));
-        sacc = mfma16(kk, qs[2][kt], sacc);  // smallest parts first
-        sacc = mfma16(kk, qs[1][kt], sacc);
-        sacc = mfma16(kk, qs[0][kt], sacc);
+        sk[kt] = mfma16(kk, qs[2][kt], f32x4{0.f, 0.f, 0.f, 0.f});  // smallest parts first
+        sk[kt] = mfma16(kk, qs[1][kt], sk[kt]);
+        sk[kt] = mfma16(kk, qs[0][kt], sk[kt]);
       }
+      f32x4 sacc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sacc[e] = (sk[0][e] + sk[1][e]) + (sk[2][e] + sk[3][e]);
       // V quarter g (keys 4g..4g+3 of the page), dim db * 16 + c; keys after this wave's last query are
       // not written yet (possibly NaN): clear them
       const char *vp = stg + 2 * kPfKPage + u * kPfVPage + g * 1024;
+      const bool tail = pi * 16 + 15 > last_pos;  // wave-uniform: the page holds keys past this wave's queries
       const int n_valid = last_pos + 1 - (pi * 16 + g * 4);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int unit = ((db * 16 + c) >> 1) ^ ((g & 1) * 8);  // 8 bytes: half c % 2 of a 16-byte unit
         uint2 w = *reinterpret_cast<const uint2 *>(vp + unit * 16 + (c & 1) * 8);
-        w.x = mask_pair(w.x, 0, n_valid);
-        w.y = mask_pair(w.y, 2, n_valid);
+        if (tail) {
+          w.x = mask_pair(w.x, 0, n_valid);
+          w.y = mask_pair(w.y, 2, n_valid);
+        }
         vt[db][u] = w;
       }
+      if (pg >= 0 && pi * 16 + 15 <= pos0) {  // every key of the page is visible to every query of the wave
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kpos = pi * 16 + g * 4 + e;
-        sc[u][e] = (pg >= 0 && q_ok && kpos <= my_pos) ? sacc[e] : -INFINITY;
+        for (int e = 0; e < 4; ++e) sc[u][e] = sacc[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kpos = pi * 16 + g * 4 + e;
+          sc[u][e] = (pg >= 0 && q_ok && kpos <= my_pos) ? sacc[e] : -INFINITY;
+        }
       }
     }
     (void)pgs;
@@ -812,6 +824,8 @@ __global__ __launch_bounds__(256) void prefill_attn4_kernel(const float *__restr
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m, mx);
+    // the accumulators are rescaled only when some query's maximum grew (otherwise the factor is 1)
+    const bool grow = __any(m_new > m);
     const float alpha = exp2f(m - m_new);
     m = m_new;
     float pr[8];
@@ -823,11 +837,15 @@ __global__ __launch_bounds__(256) void prefill_attn4_kernel(const float *__restr
         pr[u * 4 + e] = exp2f(sc[u][e] - m_new);
         psum += pr[u * 4 + e];
       }
-    l = l * alpha + psum;
+    if (grow) {
+      l = l * alpha + psum;
 #pragma unroll
-    for (int i = 0; i < DB; ++i)
+      for (int i = 0; i < DB; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) oacc[i][e] *= alpha;
+        for (int e = 0; e < 4; ++e) oacc[i][e] *= alpha;
+    } else {
+      l += psum;
+    }
     uint4 ps[3];
     split3_pack8(pr, ps[0], ps[1], ps[2]);
 #pragma unroll

@@ -658,7 +658,7 @@ def pmc_summary(fetch_dir, write_dir):
     out.append(f"traffic_bytes_per_call: {total:.0f}  (x{total / alg:.3f} the algorithmic bytes)")
     out.append("# Every kernel of the run with at least 1% of its traffic, bytes per dispatch (the run holds the")
     out.append("# 13 model steps, the standalone attention calls, the 13 graph-replayed steps and the weight setup):")
-    out += traffic_table(fetch_dir, write_dir)
+    out += traffic_table(fetch_dir, write_dir)[2:]  # without the calibration lines, printed above
     print("\n".join(out))
 
 

@@ -434,13 +434,13 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(int n_heads, const in
 }
 
 void decode_partition(const llmdec_config &cfg, int n_seqs, int max_pages, int *pages_per_part, int *n_parts) {
-  // Aim for ~8 waves per CU over 256 CUs counting every (sequence, wave of heads) row at full width,
+  // Aim for ~16 waves per CU over 256 CUs counting every (sequence, wave of heads) row at full width,
   // QH times that where a wave serves QH query heads (its pages cost QH times the arithmetic, so shorter
   // partitions keep the waves' lengths even); never split finer than one page, never coarser than
   // kMaxPartPages.
   const int qh = decode_heads_per_wave(cfg);
   const long rows = (long)n_seqs * (cfg.n_heads / qh);
-  const long target = 2048L * qh;
+  const long target = 4096L * qh;
   int parts = (int)((target + rows - 1) / rows);
   parts = parts < 1 ? 1 : parts;
   int ppp = (max_pages + parts - 1) / parts;

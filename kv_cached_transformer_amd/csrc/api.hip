@@ -54,6 +54,7 @@ WsLayout ws_layout(const llmdec_config &c, int max_tokens, int max_seqs, int max
   L.err = take(kWsHeader);
   L.tok_seq = take(sizeof(int32_t) * T);
   L.tok_pos = take(sizeof(int32_t) * T);
+  L.rope_cs = take(T > 64 ? sizeof(float2) * T * (c.head_dim / 2) : 0);  // prefill rotations
   L.x = take(sizeof(float) * (size_t)rows * h);
   L.act_h = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_h);
   L.act_hl = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_h);
@@ -173,10 +174,11 @@ static Splits run_layer(const LayerArgs &a) {
   uint16_t *act_h = at<uint16_t>(a.ws, L.act_h), *act_hl = at<uint16_t>(a.ws, L.act_hl);
   uint16_t *act_i = at<uint16_t>(a.ws, L.act_i), *act_il = at<uint16_t>(a.ws, L.act_il);
   float *qkv = at<float>(a.ws, L.qkv), *part = at<float>(a.ws, L.part);
-  // The q|k|v product reads its input as an fp16 pair (k and v are rounded to bf16 for the cache, so
-  // their error must stay far below a bf16 step).  The others read the pair in a decode step (at most
-  // 64 rows: the products stream the weights, a second activation plane costs little, and single fp16
-  // inputs would compound over a model's layers) and one fp16 plane in a prefill (matrix-core bound).
+  // The k|v columns of the q|k|v product read their input as an fp16 pair (k and v are rounded to bf16
+  // for the cache, so their error must stay far below a bf16 step).  The other products read the pair in
+  // a decode step (at most 64 rows: the products stream the weights, a second activation plane costs
+  // little, and single fp16 inputs would compound over a model's layers) and one fp16 plane in a prefill
+  // (matrix-core bound), the q columns included.
   const bool pairs = M <= 64;
   uint16_t *lo_h = pairs ? act_hl : nullptr, *lo_i = pairs ? act_il : nullptr;
   const Act ah2{act_h, act_hl, M, L.kpad_h, L.row_blocks}, ah{act_h, lo_h, M, L.kpad_h, L.row_blocks};
@@ -192,8 +194,34 @@ static Splits run_layer(const LayerArgs &a) {
   o_qkv.f32 = qkv;
   const int nqkv = qkv_cols(c);
   o_qkv.ld = nqkv;
-  // a split q|k|v product leaves partial sums that the rotary/append kernel adds up
-  const Splits sp_qkv = launch_linear(ah2, (const uint16_t *)a.w->w_qkv, nqkv, h, o_qkv, part, L.part_floats, kSplitBalanced, a.s);
+  int32_t *ts = at<int32_t>(a.ws, L.tok_seq), *tp = at<int32_t>(a.ws, L.tok_pos);
+  if (!a.decode) launch_token_map(a.cu, a.start, a.n_seqs, M, err, ts, tp, a.s);
+  // A split q|k|v product leaves partial sums that the rotary/append kernel adds up.  A tiled prefill
+  // product applies RoPE and the K/V append in its own epilogue (kRope), from a table of the tokens'
+  // rotations, so no rotary/append pass follows it.
+  const bool fused_rope = !pairs && !a.decode;
+  Splits sp_qkv;
+  if (pairs) {
+    sp_qkv = launch_linear(ah2, (const uint16_t *)a.w->w_qkv, nqkv, h, o_qkv, part, L.part_floats, kSplitBalanced, a.s);
+  } else {
+    const int nq = c.n_heads * c.head_dim;
+    LinearOut o_q = o_qkv, o_kv = o_qkv;
+    o_kv.f32 = qkv + nq;
+    if (fused_rope) {
+      float2 *cs = at<float2>(a.ws, L.rope_cs);
+      launch_rope_table(c, tp, M, cs, a.s);
+      RopeRows rr;
+      rr.cs = cs, rr.tok_seq = ts, rr.tok_pos = tp, rr.block_tables = a.bt;
+      rr.pool_k = pk, rr.pool_v = pv, rr.err = err;
+      rr.n_seqs = a.n_seqs, rr.max_pages = a.max_pages, rr.num_pages = a.pool->num_pages;
+      rr.n_heads = c.n_heads, rr.n_kv_heads = c.n_kv_heads, rr.head_dim = c.head_dim;
+      o_q.kind = o_kv.kind = kRope;
+      o_q.rope = o_kv.rope = rr;
+      o_kv.rope.col0 = nq;
+    }
+    launch_linear_cols(ah, (const uint16_t *)a.w->w_qkv, nqkv, 0, nq, h, o_q, a.s);
+    launch_linear_cols(ah2, (const uint16_t *)a.w->w_qkv, nqkv, nq, nqkv - nq, h, o_kv, a.s);
+  }
   const float *qkv_part = sp_qkv.any() ? part : nullptr;
   if (a.decode) {
     launch_rope_append(c, qkv, qkv_part, sp_qkv, nqkv, M, a.n_seqs, nullptr, a.ctx, a.bt, a.max_pages, pk, pv,
@@ -201,10 +229,9 @@ static Splits run_layer(const LayerArgs &a) {
     launch_decode_attention(c, qkv, nqkv, M, a.ctx, a.bt, a.max_pages, pk, pv, a.pool->num_pages,
                             at<float>(a.ws, L.attn_part), nullptr, act_h, lo_h, L.kpad_h, err, a.s);
   } else {
-    int32_t *ts = at<int32_t>(a.ws, L.tok_seq), *tp = at<int32_t>(a.ws, L.tok_pos);
-    launch_token_map(a.cu, a.start, a.n_seqs, M, err, ts, tp, a.s);
-    launch_rope_append(c, qkv, qkv_part, sp_qkv, nqkv, M, a.n_seqs, ts, tp, a.bt, a.max_pages, pk, pv,
-                       a.pool->num_pages, err, a.s);
+    if (!fused_rope)
+      launch_rope_append(c, qkv, qkv_part, sp_qkv, nqkv, M, a.n_seqs, ts, tp, a.bt, a.max_pages, pk, pv,
+                         a.pool->num_pages, err, a.s);
     launch_prefill_attention(c, qkv, nqkv, a.n_seqs, M, a.max_q_len, a.cu, a.start, a.bt, a.max_pages, pk, pv,
                              a.pool->num_pages, nullptr, act_h, lo_h, L.kpad_h, err, a.s);
   }

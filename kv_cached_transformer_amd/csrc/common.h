@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "host.h"
@@ -212,6 +213,24 @@ __device__ inline float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1 in order: indices that are constants whatever
+// the size of the body (a loop the unroller finds too large keeps a variable index, and an array such
+// as a tile's accumulators indexed by it moves to scratch memory).
+template <int I, int N>
+struct StaticFor {
+  template <class F>
+  __device__ __forceinline__ static void run(F &&f) {
+    if constexpr (I < N) {
+      f(std::integral_constant<int, I>{});
+      StaticFor<I + 1, N>::run(f);
+    }
+  }
+};
+
+// The value of lane l ^ 1 (DPP quad permutation 1, 0, 3, 2); every lane of the wave must be active.
+__device__ inline float swap_pair_lanes(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
 
 // Rotation of pair i at position pos ("为什么要自己动手写一个LLM推理引擎" §4.3 rotates q and k by position):
 // the angle pos * inv_freq (inv_freq = theta^(-2i/D), computed in double on the host) is formed and
@@ -240,10 +259,13 @@ __device__ inline u32x4 buffer_desc(const void *base, uint32_t bytes) {
 // clobbered M0 is not preserved does not apply.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// soff and lds_addr are wave-uniform; readfirstlane hands them to the asm in scalar registers even where
+// the compiler keeps them in vector ones.
 __device__ inline void load_to_lds16(uint32_t voff, u32x4 desc, uint32_t soff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "v"(voff), "s"(desc), "s"(soff), "s"(lds_addr)
+               : "v"(voff), "s"(desc), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory", "m0");
 }
 #pragma clang diagnostic pop

@@ -882,12 +882,9 @@ void launch_prefill_attention(const llmdec_config &cfg, const float *q, int ld_q
     return;
   }
   dim3 grid((max_q_len + 15) / 16, cfg.n_heads, n_seqs);
-  if (cfg.head_dim == 128)
-    prefill_attn_kernel<128><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, n_tokens, max_q_len, cu, start_pos, block_tables, max_pages, pk, pv,
-                                                 num_pages, out_f32, out_act, out_lo, kpad, err);
-  else
-    prefill_attn_kernel<64><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, n_tokens, max_q_len, cu, start_pos, block_tables, max_pages, pk, pv,
-                                                num_pages, out_f32, out_act, out_lo, kpad, err);
+  prefill_attn_kernel<64><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, n_tokens, max_q_len, cu, start_pos,
+                                              block_tables, max_pages, pk, pv, num_pages, out_f32, out_act, out_lo,
+                                              kpad, err);
 }
 
 }  // namespace llmdec

@@ -114,13 +114,15 @@ template <int MB, int WN, int NP> struct SgShape {
 // ring over its k-tiles and leaves either the finished result (no split) or
 // one plane of partial sums.
 //
-// The body takes the block index and the LDS (S::LDS_U4 entries) as arguments, so that the fused decode
-// programs can run it as one of their stages.
+// w points at the first of the n_blocks column blocks the product covers; w_end at the packed matrix's
+// trailer (its scale), which follows the matrix's last column block, so that a product can cover a
+// range of a matrix's columns.
 template <int MB, int WN, int NP>
 __device__ __forceinline__ void stream_gemm_body(uint4 *lds, int bid, const uint4 *__restrict__ a_act,
                                                  const uint4 *__restrict__ a_lo, int a_kt, int rows,
-                                                 const uint4 *__restrict__ w, int kt_count, int n_blocks,
-                                                 const LinearOut &o, float *__restrict__ partials, const Splits &sp) {
+                                                 const uint4 *__restrict__ w, const uint4 *__restrict__ w_end,
+                                                 int kt_count, int n_blocks, const LinearOut &o,
+                                                 float *__restrict__ partials, const Splits &sp) {
   using S = SgShape<MB, WN, NP>;
   constexpr int WK = S::WK, NA = S::NA, APW = S::APW, D = S::D, R = S::R;
   constexpr bool SHARE = WN > 1;
@@ -250,7 +252,7 @@ __device__ __forceinline__ void stream_gemm_body(uint4 *lds, int bid, const uint
       }
     }
     if (kw == 0 && nbs > 0) {
-      const float wunscale = weight_unscale(w + (size_t)n_blocks * kt_count * 64);
+      const float wunscale = weight_unscale(w_end);
       if (sp.any()) {  // plane = this block's place among the blocks covering group g
         float *plane = partials + (size_t)(bid - sp.first_block((long)g * kt_count)) * rows * n;
 #pragma unroll
@@ -286,10 +288,13 @@ __device__ __forceinline__ void stream_gemm_body(uint4 *lds, int bid, const uint
 template <int MB, int WN, int NP>
 __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(const uint4 *__restrict__ a_act,
                                                              const uint4 *__restrict__ a_lo, int a_kt, int rows,
-                                                             const uint4 *__restrict__ w, int kt_count, int n_blocks,
-                                                             LinearOut o, float *__restrict__ partials, Splits sp) {
+                                                             const uint4 *__restrict__ w,
+                                                             const uint4 *__restrict__ w_end, int kt_count,
+                                                             int n_blocks, LinearOut o, float *__restrict__ partials,
+                                                             Splits sp) {
   __shared__ uint4 lds[SgShape<MB, WN, NP>::LDS_U4];
-  stream_gemm_body<MB, WN, NP>(lds, blockIdx.x, a_act, a_lo, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
+  stream_gemm_body<MB, WN, NP>(lds, blockIdx.x, a_act, a_lo, a_kt, rows, w, w_end, kt_count, n_blocks, o, partials,
+                               sp);
 }
 
 // ---------------------------------------------------------------- split-k reduction
@@ -387,10 +392,107 @@ template <int WM, int WNT, int NP> struct TgShape {
   static_assert(R >= 3 && (R - 1) * G <= 63, "at least one k-tile of lookahead; the loads fit vmcnt");
 };
 
-template <int WM, int WNT, int NP>
+// The kRope epilogue (see RopeRows).  Each wave passes its results through its own quarter of the LDS
+// (free once the k-loop has ended), one 16-row block at a time: its accumulators go to a row-major
+// staging area and the block's rows of the rotation table beside them; the wave then walks the staged
+// rows pair by pair, lane l taking pair l of a row (two rows a step when a row holds 32 pairs), so a q
+// row leaves as contiguous fp32 pairs and a k row as contiguous bf16 pairs.  The walk is a short loop,
+// not one unrolled copy per accumulator (an epilogue that large runs from outside the instruction
+// cache).  The rows' page slots are looked up once, lane l holding rows l and l + 64 of the wave.
+template <int WM, int WNT>
+__device__ __forceinline__ void tile_rope_epilogue(uint4 *lds, const f32x4 (&acc)[WM][WNT], float wunscale,
+                                                   const LinearOut &o, int rows, int n_blocks, int mw, int nw,
+                                                   int wave, int lane) {
+  constexpr int P = WNT * 8;            // pairs per row of the wave's columns
+  constexpr int PITCH = WNT * 16 + 4;   // floats per staged row (the 4-float skew spreads the rows' banks)
+  constexpr int STEPS = 16 * P / 64;    // walk steps per 16-row block
+  static_assert(WM * 16 <= 128, "two page slots per lane");
+  const RopeRows &rp = o.rope;
+  const int D = rp.head_dim, half = D >> 1;
+  const int hid = rp.n_heads * D, kvc = rp.n_kv_heads * D;
+  const bool kv = rp.col0 > 0;
+  const int c0 = nw * 16;                                  // the wave's first column of the product
+  const int ncols = min(WNT * 16, (n_blocks - nw) * 16);  // its real columns (none past the matrix)
+  const int rq = (lane >> 4) * 4, cq = lane & 15;
+  float *st = reinterpret_cast<float *>(lds) + wave * (16 * PITCH + 16 * 64 * 2);
+  float2 *cs = reinterpret_cast<float2 *>(st + 16 * PITCH);  // [16 rows][half]
+
+  // page slots of rows mw*16 + lane and + 64 (K/V products): page -1 = no store (flagged)
+  int2 slot[2] = {make_int2(-1, 0), make_int2(-1, 0)};
+  if (kv) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = mw * 16 + lane + 64 * h;
+      if (lane + 64 * h >= WM * 16 || r >= rows) continue;
+      const int seq = rp.tok_seq[r], pos = rp.tok_pos[r];
+      if (seq < 0 || seq >= rp.n_seqs) {
+        raise_error(rp.err, kErrSeq);
+      } else if (pos < 0 || (pos >> 4) >= rp.max_pages) {
+        raise_error(rp.err, kErrPos);
+      } else {
+        const int page = rp.block_tables[(size_t)seq * rp.max_pages + (pos >> 4)];
+        if (page < 0 || page >= rp.num_pages) raise_error(rp.err, kErrPage);
+        else slot[h] = make_int2(page, pos & 15);
+      }
+    }
+  }
+  __syncthreads();  // every wave's k-loop reads of the LDS are done
+
+  StaticFor<0, WM>::run([&](auto mc) __attribute__((always_inline)) {
+    constexpr int m = decltype(mc)::value;
+    const int r0 = (mw + m) * 16;  // the block's first row
+    {  // its 16 table rows (16 * half pairs, as float4), all loads first (a row past the product re-reads
+       // the last row; it is not used)
+      const int n4 = 8 * half;
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = min(u * 64 + lane, n4 - 1), rr = (2 * q) / half;
+        v[u] = *reinterpret_cast<const float4 *>(rp.cs + (size_t)min(r0 + rr, rows - 1) * half + (2 * q - rr * half));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (u * 64 + lane < n4) reinterpret_cast<float4 *>(cs)[u * 64 + lane] = v[u];
+    }
+#pragma unroll
+    for (int j = 0; j < WNT; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st[(rq + e) * PITCH + j * 16 + cq] = acc[m][j][e] * wunscale;
+    for (int it = 0; it < STEPS; ++it) {
+      const int idx = it * 64 + lane, rl = idx / P, p = idx - rl * P;
+      const int r = r0 + rl, rw = m * 16 + rl;  // row of the product, of the wave
+      const int2 ps = make_int2(__shfl(slot[rw >> 6].x, rw & 63, 64), __shfl(slot[rw >> 6].y, rw & 63, 64));
+      if (r >= rows || 2 * p >= ncols) continue;
+      const float2 xv = *reinterpret_cast<const float2 *>(st + rl * PITCH + 2 * p);
+      const int col = rp.col0 + c0 + 2 * p;
+      if (col < hid + kvc) {  // q or k: rotate the pair
+        const int d = col < hid ? col : col - hid;
+        const float2 t = cs[rl * half + ((d % D) >> 1)];
+        const float re = xv.x * t.x - xv.y * t.y, ro = xv.x * t.y + xv.y * t.x;
+        if (col < hid) {
+          *reinterpret_cast<float2 *>(o.f32 + (size_t)r * o.ld + c0 + 2 * p) = make_float2(re, ro);
+        } else if (ps.x >= 0) {  // K [h][o][d]
+          const size_t head = (size_t)ps.x * rp.n_kv_heads + d / D;
+          *reinterpret_cast<uint32_t *>(rp.pool_k + (head * 16 + ps.y) * D + (d % D)) =
+              f32_to_bf16(re) | ((uint32_t)f32_to_bf16(ro) << 16);
+        }
+      } else if (ps.x >= 0) {  // V [h][o/4][d][o%4]
+        const int d = col - hid - kvc;
+        const size_t head = (size_t)ps.x * rp.n_kv_heads + d / D;
+        uint16_t *vp = rp.pool_v + (head * 4 + (ps.y >> 2)) * D * 4 + (size_t)(d % D) * 4 + (ps.y & 3);
+        vp[0] = f32_to_bf16(xv.x);
+        vp[4] = f32_to_bf16(xv.y);
+      }
+    }
+  });
+}
+
+// ROPE: the kRope epilogue (its own instantiation, so that the others carry none of its registers).
+template <int WM, int WNT, int NP, bool ROPE>
 __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(const uint4 *__restrict__ a_act,
                                                            const uint4 *__restrict__ a_lo, int a_kt, int a_blocks,
-                                                           int rows, const uint4 *__restrict__ w, int kt_count,
+                                                           int rows, const uint4 *__restrict__ w,
+                                                           const uint4 *__restrict__ w_end, int kt_count,
                                                            int n_blocks, int tiles_m, int n_tiles, LinearOut o) {
   using S = TgShape<WM, WNT, NP>;
   constexpr int BM = S::BM, BN = S::BN, AT = S::AT, TILES = S::TILES, G = S::G, R = S::R;
@@ -495,10 +597,13 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(const uint4 *__restri
 
   // epilogue, one fully unrolled loop per kind (the accumulators stay in registers only if every index
   // is a constant)
-  const float wunscale = weight_unscale(w + (size_t)n_blocks * kt_count * 64);
+  const float wunscale = weight_unscale(w_end);
   const int rq = (lane >> 4) * 4, cq = lane & 15;
   const int mw = mb0 + wr * WM, nw = nb0 + wc * WNT;
-  if (o.kind == kSiluMul) {
+  if constexpr (ROPE) {
+    static_assert(4 * (16 * (WNT * 16 + 4) + 16 * 64 * 2) * 4 <= R * TILES * 1024, "four waves' staging fits the LDS");
+    tile_rope_epilogue<WM, WNT>(lds, acc, wunscale, o, rows, n_blocks, mw, nw, wave, lane);
+  } else if (o.kind == kSiluMul) {
 #pragma unroll
     for (int m = 0; m < WM; ++m)
 #pragma unroll
@@ -611,42 +716,52 @@ static TileChoice choose_tiles(int rows, int n_blocks, int planes) {
 
 template <int WM, int WNT, int NP>
 static void launch_tile(hipStream_t s, const TileChoice &tc, const uint4 *act, const uint4 *lo, int a_kt,
-                        int a_blocks, int rows, const uint4 *w, int kt_count, int n_blocks, const LinearOut &o) {
+                        int a_blocks, int rows, const uint4 *w, const uint4 *w_end, int kt_count, int n_blocks, const LinearOut &o) {
   const int n_tiles = tc.tiles_m * tc.tiles_n;
   const int grid = (n_tiles + 7) / 8 * 8;
-  tile_gemm_kernel<WM, WNT, NP><<<grid, 256, 0, s>>>(act, lo, a_kt, a_blocks, rows, w,
-                                                                              kt_count, n_blocks, tc.tiles_m, n_tiles,
-                                                                              o);
+  if (o.kind == kRope)
+    tile_gemm_kernel<WM, WNT, NP, true><<<grid, 256, 0, s>>>(act, lo, a_kt, a_blocks, rows, w, w_end, kt_count,
+                                                             n_blocks, tc.tiles_m, n_tiles, o);
+  else
+    tile_gemm_kernel<WM, WNT, NP, false><<<grid, 256, 0, s>>>(act, lo, a_kt, a_blocks, rows, w, w_end, kt_count,
+                                                              n_blocks, tc.tiles_m, n_tiles, o);
 }
 
 template <int NP>
 static void launch_tiles(const TileChoice &tc, hipStream_t s, const uint4 *act, const uint4 *lo, int a_kt,
-                         int a_blocks, int rows, const uint4 *w, int kt_count, int n_blocks, const LinearOut &o) {
-  if (tc.wm == 8 && tc.wnt == 8) launch_tile<8, 8, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, kt_count, n_blocks, o);
-  else if (tc.wm == 8 && tc.wnt == 6) launch_tile<8, 6, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, kt_count, n_blocks, o);
-  else if (tc.wm == 4 && tc.wnt == 8) launch_tile<4, 8, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, kt_count, n_blocks, o);
-  else if (tc.wm == 8 && tc.wnt == 4) launch_tile<8, 4, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, kt_count, n_blocks, o);
-  else launch_tile<4, 4, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, kt_count, n_blocks, o);
+                         int a_blocks, int rows, const uint4 *w, const uint4 *w_end, int kt_count, int n_blocks, const LinearOut &o) {
+  if (tc.wm == 8 && tc.wnt == 8) launch_tile<8, 8, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
+  else if (tc.wm == 8 && tc.wnt == 6) launch_tile<8, 6, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
+  else if (tc.wm == 4 && tc.wnt == 8) launch_tile<4, 8, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
+  else if (tc.wm == 8 && tc.wnt == 4) launch_tile<8, 4, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
+  else launch_tile<4, 4, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
 }
 
 template <int MB, int NP>
 static void launch_stream(int wn, int grid, hipStream_t s, const uint4 *act, const uint4 *lo, int a_kt, int rows,
-                          const uint4 *w, int kt_count, int n_blocks, const LinearOut &o, float *partials,
+                          const uint4 *w, const uint4 *w_end, int kt_count, int n_blocks, const LinearOut &o,
+                          float *partials,
                           const Splits &sp) {
   if (wn == 4)
-    stream_gemm_kernel<MB, 4, NP><<<grid, 256, 0, s>>>(act, lo, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
+    stream_gemm_kernel<MB, 4, NP><<<grid, 256, 0, s>>>(act, lo, a_kt, rows, w, w_end, kt_count, n_blocks, o, partials,
+                                                       sp);
   else if (wn == 2)
-    stream_gemm_kernel<MB, 2, NP><<<grid, 256, 0, s>>>(act, lo, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
+    stream_gemm_kernel<MB, 2, NP><<<grid, 256, 0, s>>>(act, lo, a_kt, rows, w, w_end, kt_count, n_blocks, o, partials,
+                                                       sp);
   else
-    stream_gemm_kernel<MB, 1, NP><<<grid, 256, 0, s>>>(act, lo, a_kt, rows, w, kt_count, n_blocks, o, partials, sp);
+    stream_gemm_kernel<MB, 1, NP><<<grid, 256, 0, s>>>(act, lo, a_kt, rows, w, w_end, kt_count, n_blocks, o, partials,
+                                                       sp);
 }
 
+// The product over n columns of the packed matrix (n_total columns) that start at column block nb0.
 template <int NP>
-static Splits launch_linear_np(const Act &a, const uint16_t *w_packed, int n, int k, const LinearOut &o,
-                               float *partials, size_t partial_floats, SplitPolicy policy, hipStream_t s) {
+static Splits launch_linear_np(const Act &a, const uint16_t *w_packed, int n_total, int nb0, int n, int k,
+                               const LinearOut &o, float *partials, size_t partial_floats, SplitPolicy policy,
+                               hipStream_t s) {
   const int kt_count = round_up(k, kTileK) / kTileK;
   const int n_blocks = n / 16;
-  const uint4 *w = reinterpret_cast<const uint4 *>(w_packed);
+  const uint4 *w = reinterpret_cast<const uint4 *>(w_packed) + (size_t)nb0 * kt_count * 64;
+  const uint4 *w_end = reinterpret_cast<const uint4 *>(w_packed) + (size_t)(n_total / 16) * kt_count * 64;
   const uint4 *act = reinterpret_cast<const uint4 *>(a.a), *lo = reinterpret_cast<const uint4 *>(a.lo);
   const int a_kt = a.kpad / kTileK;
   if (a.rows <= 64) {
@@ -654,23 +769,29 @@ static Splits launch_linear_np(const Act &a, const uint16_t *w_packed, int n, in
     if (p.sp.any() && (!partials || partial_floats < linear_partial_floats(a.rows, n, k, policy)))
       p = stream_plan(a.rows, n, k, kSplitNone);
     switch ((a.rows + 15) / 16) {
-      case 1: launch_stream<1, NP>(p.wn, p.grid, s, act, lo, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
-      case 2: launch_stream<2, NP>(p.wn, p.grid, s, act, lo, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
-      case 3: launch_stream<3, NP>(p.wn, p.grid, s, act, lo, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
-      default: launch_stream<4, NP>(p.wn, p.grid, s, act, lo, a_kt, a.rows, w, kt_count, n_blocks, o, partials, p.sp); break;
+      case 1: launch_stream<1, NP>(p.wn, p.grid, s, act, lo, a_kt, a.rows, w, w_end, kt_count, n_blocks, o, partials, p.sp); break;
+      case 2: launch_stream<2, NP>(p.wn, p.grid, s, act, lo, a_kt, a.rows, w, w_end, kt_count, n_blocks, o, partials, p.sp); break;
+      case 3: launch_stream<3, NP>(p.wn, p.grid, s, act, lo, a_kt, a.rows, w, w_end, kt_count, n_blocks, o, partials, p.sp); break;
+      default: launch_stream<4, NP>(p.wn, p.grid, s, act, lo, a_kt, a.rows, w, w_end, kt_count, n_blocks, o, partials, p.sp); break;
     }
     return p.sp;
   }
   // tile shape: the largest tiles that still give every CU work in whole rounds where possible
   const TileChoice tc = choose_tiles(a.rows, n_blocks, NP);
-  launch_tiles<NP>(tc, s, act, lo, a_kt, a.row_blocks, a.rows, w, kt_count, n_blocks, o);
+  launch_tiles<NP>(tc, s, act, lo, a_kt, a.row_blocks, a.rows, w, w_end, kt_count, n_blocks, o);
   return Splits{};
 }
 
 Splits launch_linear(const Act &a, const uint16_t *w_packed, int n, int k, const LinearOut &o, float *partials,
                      size_t partial_floats, SplitPolicy policy, hipStream_t s) {
-  if (a.lo) return launch_linear_np<2>(a, w_packed, n, k, o, partials, partial_floats, policy, s);
-  return launch_linear_np<1>(a, w_packed, n, k, o, partials, partial_floats, policy, s);
+  if (a.lo) return launch_linear_np<2>(a, w_packed, n, 0, n, k, o, partials, partial_floats, policy, s);
+  return launch_linear_np<1>(a, w_packed, n, 0, n, k, o, partials, partial_floats, policy, s);
+}
+
+void launch_linear_cols(const Act &a, const uint16_t *w_packed, int n_total, int col0, int n, int k,
+                        const LinearOut &o, hipStream_t s) {
+  if (a.lo) launch_linear_np<2>(a, w_packed, n_total, col0 / 16, n, k, o, nullptr, 0, kSplitNone, s);
+  else launch_linear_np<1>(a, w_packed, n_total, col0 / 16, n, k, o, nullptr, 0, kSplitNone, s);
 }
 
 

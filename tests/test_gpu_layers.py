@@ -173,3 +173,28 @@ def test_decode_bad_page_and_position_set_error_bits(L, R, n):
         assert ws.error_bits() & bit, f"error bit {bit} not set (bits {ws.error_bits()})"
         kblk, vblk = case.pool_blocks()
         assert np.array_equal(kblk, case.kblk0) and np.array_equal(vblk, case.vblk0), "a K/V slot was written"
+
+
+@pytest.mark.parametrize("n_tok", [40, 80])
+def test_prefill_bad_page_and_position_set_error_bits(L, R, n_tok):
+    """The same checks in a prefill: new tokens whose block-table entries name pages that do not exist, and
+    new tokens past the block-table row, set the sticky error bits and write no K/V slot.  40 tokens run
+    the RoPE/append kernel after a batched product; 80 run the tiled q|k|v products, which apply RoPE and
+    the append in their epilogue."""
+    banner(f"prefill of {n_tok} tokens with a bad page / position")
+    ctx = 37
+    case = LayerCase(L, R, TINY1, 99, [ctx], [n_tok], build_oracle=False)
+    x_in = synth.hidden_input(99, n_tok, 256)
+    bad = case.bt.copy()
+    bad[0, ctx // 16:(ctx + n_tok - 1) // 16 + 1] = case.num_pages + 3  # every new token's page
+    cu_d = R.dev_i32(np.array([0, n_tok], np.int32))
+    for bt, start, bit in [(bad, ctx, L.ERR_PAGE), (case.bt, case.max_pages * 16, L.ERR_POS)]:
+        ws = case.workspace(n_tok)
+        xd, bt_d, st_d = R.dev_f32(x_in), R.dev_i32(bt), R.dev_i32(np.array([start], np.int32))
+        L.llmdec_layer_prefill(case.cfg, case.packed.struct, 0, xd.data_ptr(), 1, n_tok, n_tok, cu_d.data_ptr(),
+                               st_d.data_ptr(), bt_d.data_ptr(), case.max_pages, case.pool.handle, ws.ptr,
+                               ws.nbytes, R.stream())
+        torch.cuda.synchronize()
+        assert ws.error_bits() & bit, f"error bit {bit} not set (bits {ws.error_bits()})"
+        kblk, vblk = case.pool_blocks()
+        assert np.array_equal(kblk, case.kblk0) and np.array_equal(vblk, case.vblk0), "a K/V slot was written"

@@ -110,12 +110,93 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(float *__restrict
                                     out_act, out_lo, kpad, add, sp, rows);
 }
 
+// Many-row form (a prefill's rows, packed output only): a block of 4 waves takes 8 rows, so that its
+// stores fill whole 128-byte runs of the packed tiles (a tile holds 16 rows, each row 16 bytes of every
+// 256-byte quarter) instead of one 16-byte piece per row.  Lane l holds row l % 8 and, of each 64-column
+// group, columns 8 (l / 8) .. + 7; wave w takes groups w*CG .. w*CG + CG - 1.  The 8 lanes of a row add
+// their squares with shuffles, the 4 waves through LDS.
+template <int CG>
+__global__ __launch_bounds__(256) void rmsnorm_rows8_kernel(const float *__restrict__ x, int ld_x,
+                                                            const uint16_t *__restrict__ gamma, int n, float eps,
+                                                            uint16_t *out_act, uint16_t *out_lo, int kpad, int rows) {
+  __shared__ float red[4][8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rl = lane & 7, piece = lane >> 3;
+  const int r = blockIdx.x * 8 + rl;
+  const bool row_ok = r < rows;
+  const float *xr = x + (size_t)(row_ok ? r : 0) * ld_x;
+  float v[CG][8];
+  uint4 gw[CG];
+  float ss = 0.f;
+#pragma unroll
+  for (int g = 0; g < CG; ++g) {
+    const int c0 = (wave * CG + g) * 64 + piece * 8;
+    if (row_ok && c0 < n) {
+      const float4 a = *reinterpret_cast<const float4 *>(xr + c0), b = *reinterpret_cast<const float4 *>(xr + c0 + 4);
+      gw[g] = *reinterpret_cast<const uint4 *>(gamma + c0);
+      v[g][0] = a.x, v[g][1] = a.y, v[g][2] = a.z, v[g][3] = a.w;
+      v[g][4] = b.x, v[g][5] = b.y, v[g][6] = b.z, v[g][7] = b.w;
+    } else {
+      gw[g] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[g][j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = fmaf(v[g][j], v[g][j], ss);
+  }
+  ss += __shfl_xor(ss, 8, 64);
+  ss += __shfl_xor(ss, 16, 64);
+  ss += __shfl_xor(ss, 32, 64);
+  if (lane < 8) red[wave][lane] = ss;
+  __syncthreads();
+  const float total = red[0][rl] + red[1][rl] + red[2][rl] + red[3][rl];
+  const float inv = 1.0f / sqrtf(total / (float)n + eps);
+  if (!row_ok) return;
+  const int kt = kpad >> 5;
+#pragma unroll
+  for (int g = 0; g < CG; ++g) {
+    const int c0 = (wave * CG + g) * 64 + piece * 8;
+    if (c0 >= kpad) continue;
+    const uint32_t gg[4] = {gw[g].x, gw[g].y, gw[g].z, gw[g].w};
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // past n: zeros (x and gamma were read as zeros)
+      y[2 * j] = v[g][2 * j] * inv * bf16lo(gg[j]);
+      y[2 * j + 1] = v[g][2 * j + 1] * inv * bf16hi(gg[j]);
+    }
+    const size_t off = packed_offset(r, c0, kt);
+    if (out_lo) {
+      uint4 h, l;
+      pack8_f16x2(y, h, l);
+      *reinterpret_cast<uint4 *>(out_act + off) = h;
+      *reinterpret_cast<uint4 *>(out_lo + off) = l;
+    } else {
+      *reinterpret_cast<uint4 *>(out_act + off) = pack8_f16(y);
+    }
+  }
+}
+
+template <int CG>
+static void launch_rows8(const float *x, int ld_x, const uint16_t *gamma, int rows, int n, float eps,
+                         uint16_t *out_act, uint16_t *out_lo, int kpad, hipStream_t s) {
+  rmsnorm_rows8_kernel<CG><<<(rows + 7) / 8, 256, 0, s>>>(x, ld_x, gamma, n, eps, out_act, out_lo, kpad, rows);
+}
+
 void launch_rmsnorm(float *x, int ld_x, const int32_t *cu_last, int n_src_rows, const uint16_t *gamma, int rows, int n,
                     float eps, uint32_t *err, float *out_f32, uint16_t *out_act, uint16_t *out_lo, int kpad,
                     const float *add_partials, const Splits &sp, hipStream_t s) {
-  if (rows > 0)
-    rmsnorm_kernel<<<rows, kNormThreads, 0, s>>>(x, ld_x, cu_last, n_src_rows, gamma, n, eps, err, out_f32, out_act,
-                                                 out_lo, kpad, add_partials, sp, rows);
+  if (rows <= 0) return;
+  const int groups = (kpad + 63) / 64;  // 64-column groups, 4 waves share them
+  if (rows > 64 && out_act && !out_f32 && !add_partials && !cu_last && groups <= 4 * 16) {
+    if (groups <= 4) launch_rows8<1>(x, ld_x, gamma, rows, n, eps, out_act, out_lo, kpad, s);
+    else if (groups <= 8) launch_rows8<2>(x, ld_x, gamma, rows, n, eps, out_act, out_lo, kpad, s);
+    else if (groups <= 16) launch_rows8<4>(x, ld_x, gamma, rows, n, eps, out_act, out_lo, kpad, s);
+    else if (groups <= 32) launch_rows8<8>(x, ld_x, gamma, rows, n, eps, out_act, out_lo, kpad, s);
+    else launch_rows8<16>(x, ld_x, gamma, rows, n, eps, out_act, out_lo, kpad, s);
+    return;
+  }
+  rmsnorm_kernel<<<rows, kNormThreads, 0, s>>>(x, ld_x, cu_last, n_src_rows, gamma, n, eps, err, out_f32, out_act,
+                                               out_lo, kpad, add_partials, sp, rows);
 }
 
 // ---------------------------------------------------------------- fp32 -> packed fp16 activation

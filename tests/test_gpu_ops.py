@@ -42,7 +42,7 @@ def bf16_normal(rng, shape, std=1.0):
 
 
 # ----------------------------------------------------------------------------- RMSNorm
-@pytest.mark.parametrize("rows,n", [(1, 4096), (3, 256), (70, 4096)])
+@pytest.mark.parametrize("rows,n", [(1, 4096), (3, 256), (70, 4096), (133, 1024), (200, 4064)])
 def test_rmsnorm(L, R, rows, n):
     """fp32 output against the oracle; the packed fp16 output is the nearest-even fp16 of the device's own
     fp32 value, bit for bit (both roundings taken in the same precision), and the fp16 pair's lo part is
@@ -68,11 +68,23 @@ def test_rmsnorm(L, R, rows, n):
     assert np.array_equal(h, od.round_to_f16(y))
     assert np.array_equal(l_, od.round_to_f16(y - h))
     assert_close("rmsnorm hi+lo", h + l_, ref, max_abs=1e-5, rel_l2=1e-6)
+    # packed output only, as the layers ask for it (above 64 rows a kernel that normalises 8 rows per block
+    # takes it; its sums of squares add in another order, so its last bits may differ from the above)
+    hi2, lo2 = torch.full_like(hi, -1), torch.full_like(hi, -1)
+    L.llmdec_op_rmsnorm(xd.data_ptr(), gd.data_ptr(), rows, n, 1e-6, None, hi2.data_ptr(), lo2.data_ptr(), kpad,
+                        R.stream())
+    torch.cuda.synchronize()
+    h2_full, l2_full = unpack_tiled(R.host_u16(hi2), rows, kpad, kpad), unpack_tiled(R.host_u16(lo2), rows, kpad, kpad)
+    assert np.all(h2_full[:, n:] == 0) and np.all(l2_full[:, n:] == 0)
+    h2, l2 = f64_from_f16(h2_full[:, :n]), f64_from_f16(l2_full[:, :n])
+    assert_close("rmsnorm packed-only hi+lo", h2 + l2, ref, max_abs=1e-5, rel_l2=1e-6)
+    if rows <= 64:
+        assert torch.equal(hi2, hi) and torch.equal(lo2, lo)
     # the single-plane output (as the MLP norm writes it) is the same hi plane
     one = torch.full_like(hi, -1)
     L.llmdec_op_rmsnorm(xd.data_ptr(), gd.data_ptr(), rows, n, 1e-6, None, one.data_ptr(), None, kpad, R.stream())
     torch.cuda.synchronize()
-    assert torch.equal(one, hi)
+    assert torch.equal(one, hi2)
 
 
 def test_rmsnorm_eps_inside_root(L, R):

@@ -381,12 +381,13 @@ void launch_reduce(const float *partials, const Splits &sp, int rows, int n, con
 // 8, spare blocks exit), with tiles numbered column-major (row tiles innermost): the blocks one XCD runs
 // together cover every row tile of a few column groups, so each weight tile is fetched into that
 // XCD's L2 once and each activation k-slab serves all of them.
-template <int WM, int WNT, int NP> struct TgShape {
+// PCU: blocks per CU (1, or 2 with half the LDS each; the registers are then also halved).
+template <int WM, int WNT, int NP, int PCU = 1> struct TgShape {
   static constexpr int BM = 2 * WM, BN = 2 * WNT;  // row / column blocks of the block tile
   static constexpr int AT = NP * BM;               // activation tiles per k-tile (all planes)
   static constexpr int TILES = AT + BN;            // 1 KiB tiles per stage
   static constexpr int G = TILES / 4;              // loads per wave per k-tile
-  static constexpr int R = 160 / TILES < 4 ? 160 / TILES : 4;  // stages (160 KiB of LDS per CU)
+  static constexpr int R = 160 / PCU / TILES < 4 ? 160 / PCU / TILES : 4;  // stages (160 KiB of LDS per CU)
   static_assert(AT % 4 == 0 && BN % 4 == 0, "load i of wave w is tile 4 i + w: a whole number per kind");
   static_assert(WNT % 2 == 0, "gate/up column pairs");
   static_assert(R >= 3 && (R - 1) * G <= 63, "at least one k-tile of lookahead; the loads fit vmcnt");
@@ -488,13 +489,13 @@ __device__ __forceinline__ void tile_rope_epilogue(uint4 *lds, const f32x4 (&acc
 }
 
 // ROPE: the kRope epilogue (its own instantiation, so that the others carry none of its registers).
-template <int WM, int WNT, int NP, bool ROPE>
-__global__ __launch_bounds__(256, 1) void tile_gemm_kernel(const uint4 *__restrict__ a_act,
+template <int WM, int WNT, int NP, int PCU, bool ROPE>
+__global__ __launch_bounds__(256, PCU) void tile_gemm_kernel(const uint4 *__restrict__ a_act,
                                                            const uint4 *__restrict__ a_lo, int a_kt, int a_blocks,
                                                            int rows, const uint4 *__restrict__ w,
                                                            const uint4 *__restrict__ w_end, int kt_count,
                                                            int n_blocks, int tiles_m, int n_tiles, LinearOut o) {
-  using S = TgShape<WM, WNT, NP>;
+  using S = TgShape<WM, WNT, NP, PCU>;
   constexpr int BM = S::BM, BN = S::BN, AT = S::AT, TILES = S::TILES, G = S::G, R = S::R;
   __shared__ uint4 lds[R * TILES * 64];  // [R stages][TILES tiles][64 lanes]
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)lds;
@@ -689,52 +690,73 @@ size_t linear_partial_floats(int rows, int n, int k, SplitPolicy policy) {
 // Prefill tile shape (WM row blocks x WNT column blocks per wave, four waves per block).  Blocks with more
 // than 80 KiB of LDS stages run one per CU, smaller ones two, so a launch runs in rounds of 256 or 512
 // blocks; a round's time scales with the MFMAs a SIMD runs in it, and smaller tiles load more bytes per
-// MFMA (relative speeds below are estimates).  The shape with the least estimated time wins, larger
-// tiles on ties.
+// MFMA (relative speeds below are estimates, but for the measured two-per-CU 4 x 8).  Two blocks per CU
+// also let one block's matrix cores run while the other waits at its barrier, and their rounds of 512
+// cut the idle tail of a launch whose tile count is not a multiple of 256.  The shape with the least
+// estimated time wins, larger tiles on ties.
 struct TileChoice {
-  int wm, wnt, tiles_m, tiles_n;
+  int wm, wnt, pcu, tiles_m, tiles_n;
 };
 static TileChoice choose_tiles(int rows, int n_blocks, int planes) {
+  // pcu 2: two blocks per CU, each with half the LDS (3 stages of 24 KiB); measured on the 7B gate/up
+  // product (2048 rows, 1376 tiles of 4 x 8) at 0.95 of the 8 x 8 tiles' time for the same MFMAs per SIMD
   static const struct {
-    int wm, wnt;
+    int wm, wnt, pcu;
     double speed;
-  } shapes[] = {{8, 8, 1.0}, {8, 6, 0.95}, {4, 8, 0.85}, {8, 4, 0.85}, {4, 4, 0.7}};
+  } shapes[] = {{8, 8, 1, 1.0}, {8, 6, 1, 0.95}, {4, 8, 1, 0.85}, {8, 4, 1, 0.85}, {4, 4, 1, 0.7}, {4, 8, 2, 1.05}};
   const int row_blocks = (rows + 15) / 16;
-  TileChoice best{0, 0, 0, 0};
+  TileChoice best{0, 0, 1, 0, 0};
   double best_cost = 1e300;
   for (const auto &sh : shapes) {
     const int tiles_kib = planes * 2 * sh.wm + 2 * sh.wnt;
-    const int stages = std::min(4, 160 / tiles_kib);
-    const int per_cu = stages * tiles_kib > 80 ? 1 : 2;
+    const int stages = std::min(4, 160 / sh.pcu / tiles_kib);
+    if (sh.pcu > 1 && stages < 3) continue;
+    // blocks of at most 80 KiB run two per CU whatever their bounds say (4 x 4)
+    const int per_cu = sh.pcu > 1 || stages * tiles_kib <= 80 ? 2 : 1;
     const int tm = (row_blocks + 2 * sh.wm - 1) / (2 * sh.wm), tn = (n_blocks + 2 * sh.wnt - 1) / (2 * sh.wnt);
     const long tiles = (long)tm * tn;
+    // two blocks per CU only pay when the launch fills the second slots
+    if (sh.pcu > 1 && tiles <= (long)kCUs) continue;
     const double cost = (double)((tiles + per_cu * kCUs - 1) / (per_cu * kCUs)) * per_cu * sh.wm * sh.wnt / sh.speed;
-    if (cost < best_cost * 0.999) best_cost = cost, best = TileChoice{sh.wm, sh.wnt, tm, tn};
+    if (cost < best_cost * 0.999) best_cost = cost, best = TileChoice{sh.wm, sh.wnt, sh.pcu, tm, tn};
   }
   return best;
 }
 
-template <int WM, int WNT, int NP>
+template <int WM, int WNT, int NP, int PCU>
 static void launch_tile(hipStream_t s, const TileChoice &tc, const uint4 *act, const uint4 *lo, int a_kt,
-                        int a_blocks, int rows, const uint4 *w, const uint4 *w_end, int kt_count, int n_blocks, const LinearOut &o) {
+                        int a_blocks, int rows, const uint4 *w, const uint4 *w_end, int kt_count, int n_blocks,
+                        const LinearOut &o) {
   const int n_tiles = tc.tiles_m * tc.tiles_n;
   const int grid = (n_tiles + 7) / 8 * 8;
   if (o.kind == kRope)
-    tile_gemm_kernel<WM, WNT, NP, true><<<grid, 256, 0, s>>>(act, lo, a_kt, a_blocks, rows, w, w_end, kt_count,
-                                                             n_blocks, tc.tiles_m, n_tiles, o);
+    tile_gemm_kernel<WM, WNT, NP, PCU, true><<<grid, 256, 0, s>>>(act, lo, a_kt, a_blocks, rows, w, w_end, kt_count,
+                                                                  n_blocks, tc.tiles_m, n_tiles, o);
   else
-    tile_gemm_kernel<WM, WNT, NP, false><<<grid, 256, 0, s>>>(act, lo, a_kt, a_blocks, rows, w, w_end, kt_count,
-                                                              n_blocks, tc.tiles_m, n_tiles, o);
+    tile_gemm_kernel<WM, WNT, NP, PCU, false><<<grid, 256, 0, s>>>(act, lo, a_kt, a_blocks, rows, w, w_end, kt_count,
+                                                                   n_blocks, tc.tiles_m, n_tiles, o);
 }
 
 template <int NP>
 static void launch_tiles(const TileChoice &tc, hipStream_t s, const uint4 *act, const uint4 *lo, int a_kt,
-                         int a_blocks, int rows, const uint4 *w, const uint4 *w_end, int kt_count, int n_blocks, const LinearOut &o) {
-  if (tc.wm == 8 && tc.wnt == 8) launch_tile<8, 8, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
-  else if (tc.wm == 8 && tc.wnt == 6) launch_tile<8, 6, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
-  else if (tc.wm == 4 && tc.wnt == 8) launch_tile<4, 8, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
-  else if (tc.wm == 8 && tc.wnt == 4) launch_tile<8, 4, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
-  else launch_tile<4, 4, NP>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
+                         int a_blocks, int rows, const uint4 *w, const uint4 *w_end, int kt_count, int n_blocks,
+                         const LinearOut &o) {
+#define LLMDEC_TILE(WM_, WNT_, PCU_) \
+  launch_tile<WM_, WNT_, NP, PCU_>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o)
+  if (tc.pcu == 2) {
+    if constexpr (NP == 1) LLMDEC_TILE(4, 8, 2);  // the only two-per-CU shape (3 stages fit one plane only)
+  } else if (tc.wm == 8 && tc.wnt == 8) {
+    LLMDEC_TILE(8, 8, 1);
+  } else if (tc.wm == 8 && tc.wnt == 6) {
+    LLMDEC_TILE(8, 6, 1);
+  } else if (tc.wm == 4 && tc.wnt == 8) {
+    LLMDEC_TILE(4, 8, 1);
+  } else if (tc.wm == 8 && tc.wnt == 4) {
+    LLMDEC_TILE(8, 4, 1);
+  } else {
+    LLMDEC_TILE(4, 4, 1);
+  }
+#undef LLMDEC_TILE
 }
 
 template <int MB, int NP>

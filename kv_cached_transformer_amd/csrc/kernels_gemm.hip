@@ -655,9 +655,11 @@ static StreamPlan stream_plan(int rows, int n, int k, SplitPolicy policy) {
   const double w_bytes = 2.0 * n * k;
   // Wide column groups first (fewer activation requests per weight byte).  With 16 rows or fewer the
   // activations are a small share of the bytes, and narrow groups mean fewer partial planes per column
-  // for the consumers to add up (measured on the batch-1 7B layer: 124.7 -> 120.1 us).
-  const int order[2][3] = {{4, 2, 1}, {1, 2, 4}};
-  for (int wn : order[rows <= 16 ? 1 : 0]) {
+  // for the consumers to add up (measured on the batch-1 7B layer: 124.7 -> 120.1 us).  At 32 rows the
+  // middle width balances the two (7B layer at 32 sequences: 328 -> 317 us); at 64, 4 column waves win
+  // (64-sequence 32-layer step: 11.06 ms against 11.23 with 2 and 12.40 with 1).
+  const int order[3][3] = {{4, 2, 1}, {2, 4, 1}, {1, 2, 4}};
+  for (int wn : order[rows <= 16 ? 2 : (rows <= 32 ? 1 : 0)]) {
     if (policy == kSplitNone) break;
     const int wk = 4 / wn, cols = SG_NB * 16 * wn;
     const int groups = (nb + SG_NB * wn - 1) / (SG_NB * wn);

@@ -358,12 +358,13 @@ void launch_reduce(const float *partials, const Splits &sp, int rows, int n, con
 }
 
 // ---------------------------------------------------------------- tile_gemm (rows > 64)
-// A block is four waves in a 2 x 2 grid; wave (wr, wc) computes WM row blocks by WNT column blocks of
-// the output, so the block tile is BM = 2 WM row blocks by BN = 2 WNT column blocks (16 x 16 each).
-// Per k-tile (32 deep) the block needs NP * BM activation tiles (each used by the two waves of its row
-// half) and BN weight tiles (each used by the two waves of its column half).  All of them go from
-// memory straight into LDS (buffer_load ... lds: lane l's 16 bytes land at l * 16 of the tile's 1 KiB
-// slot, which is the packed tile itself), the four waves issuing a quarter each, through R stages.
+// A block is WR x WC waves (2 x 2, or 2 x 4 with two waves per SIMD); wave (wr, wc) computes WM row
+// blocks by WNT column blocks of the output, so the block tile is BM = WR WM row blocks by BN = WC WNT
+// column blocks (16 x 16 each).  Per k-tile (32 deep) the block needs NP * BM activation tiles (each
+// used by the WC waves of its row group) and BN weight tiles (each used by the WR waves of its column
+// group).  All of them go from memory straight into LDS (buffer_load ... lds: lane l's 16 bytes land at
+// l * 16 of the tile's 1 KiB slot, which is the packed tile itself), every wave issuing an equal share,
+// through R stages.
 // Step t:
 //   * wait until k-tile t + 1 has landed (the loads of R - 2 later k-tiles may still be in flight) and
 //     for this wave's LDS reads of stage t, then a barrier: every wave's share of k-tile t + 1 is in
@@ -381,19 +382,22 @@ void launch_reduce(const float *partials, const Splits &sp, int rows, int n, con
 // 8, spare blocks exit), with tiles numbered column-major (row tiles innermost): the blocks one XCD runs
 // together cover every row tile of a few column groups, so each weight tile is fetched into that
 // XCD's L2 once and each activation k-slab serves all of them.
-// PCU: blocks per CU (1, or 2 with half the LDS each; the registers are then also halved).
-template <int WM, int WNT, int NP, int PCU = 1> struct TgShape {
-  static constexpr int BM = 2 * WM, BN = 2 * WNT;  // row / column blocks of the block tile
-  static constexpr int AT = NP * BM;               // activation tiles per k-tile (all planes)
-  static constexpr int TILES = AT + BN;            // 1 KiB tiles per stage
-  static constexpr int G = TILES / 4;              // loads per wave per k-tile
+// PCU: blocks per CU (1, or 2 with half the LDS each; the registers are then also halved).  WR x WC
+// waves per block (2 x 2, or 2 x 4: two waves per SIMD sharing one block tile).
+template <int WM, int WNT, int NP, int PCU = 1, int WR = 2, int WC = 2> struct TgShape {
+  static constexpr int NW = WR * WC;                 // waves per block
+  static constexpr int BM = WR * WM, BN = WC * WNT;  // row / column blocks of the block tile
+  static constexpr int AT = NP * BM;                 // activation tiles per k-tile (all planes)
+  static constexpr int TILES = AT + BN;              // 1 KiB tiles per stage
+  static constexpr int G = TILES / NW;               // loads per wave per k-tile
   static constexpr int R = 160 / PCU / TILES < 4 ? 160 / PCU / TILES : 4;  // stages (160 KiB of LDS per CU)
-  static_assert(AT % 4 == 0 && BN % 4 == 0, "load i of wave w is tile 4 i + w: a whole number per kind");
+  static_assert(AT % NW == 0 && BN % NW == 0, "load i of wave w is tile NW i + w: a whole number per kind");
+  static_assert(NP == 1 || BM % NW == 0, "a load's plane is the same for every wave");
   static_assert(WNT % 2 == 0, "gate/up column pairs");
   static_assert(R >= 3 && (R - 1) * G <= 63, "at least one k-tile of lookahead; the loads fit vmcnt");
 };
 
-// The kRope epilogue (see RopeRows).  Each wave passes its results through its own quarter of the LDS
+// The kRope epilogue (see RopeRows).  Each wave passes its results through its own share of the LDS
 // (free once the k-loop has ended), one 16-row block at a time: its accumulators go to a row-major
 // staging area and the block's rows of the rotation table beside them; the wave then walks the staged
 // rows pair by pair, lane l taking pair l of a row (two rows a step when a row holds 32 pairs), so a q
@@ -489,26 +493,26 @@ __device__ __forceinline__ void tile_rope_epilogue(uint4 *lds, const f32x4 (&acc
 }
 
 // ROPE: the kRope epilogue (its own instantiation, so that the others carry none of its registers).
-template <int WM, int WNT, int NP, int PCU, bool ROPE>
-__global__ __launch_bounds__(256, PCU) void tile_gemm_kernel(const uint4 *__restrict__ a_act,
+template <int WM, int WNT, int NP, int PCU, bool ROPE, int WR = 2, int WC = 2>
+__global__ __launch_bounds__(64 * WR * WC, PCU) void tile_gemm_kernel(const uint4 *__restrict__ a_act,
                                                            const uint4 *__restrict__ a_lo, int a_kt, int a_blocks,
                                                            int rows, const uint4 *__restrict__ w,
                                                            const uint4 *__restrict__ w_end, int kt_count,
                                                            int n_blocks, int tiles_m, int n_tiles, LinearOut o) {
-  using S = TgShape<WM, WNT, NP, PCU>;
-  constexpr int BM = S::BM, BN = S::BN, AT = S::AT, TILES = S::TILES, G = S::G, R = S::R;
+  using S = TgShape<WM, WNT, NP, PCU, WR, WC>;
+  constexpr int BM = S::BM, BN = S::BN, AT = S::AT, TILES = S::TILES, G = S::G, R = S::R, NW = S::NW;
   __shared__ uint4 lds[R * TILES * 64];  // [R stages][TILES tiles][64 lanes]
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)lds;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wr = wave & 1, wc = wave >> 1;
+  const int wr = wave % WR, wc = wave / WR;
   const int per_xcd = (int)(gridDim.x >> 3);
   const int t = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (t >= n_tiles) return;  // block-uniform: a spare block of the rounded-up grid
   const int tm = t % tiles_m, tn = t / tiles_m;
   const int mb0 = tm * BM, nb0 = tn * BN;
 
-  // Load i of this wave is stage tile q = 4 i + wave: activation tiles first (plane q / BM, row block
+  // Load i of this wave is stage tile q = NW i + wave: activation tiles first (plane q / BM, row block
   // mb0 + q % BM), then weight tiles (column block nb0 + q - AT).  A row block past the operand reads
   // zeros (its lane offsets leave the resource); a column block past the matrix re-reads the last one
   // (its columns are not stored).  Offsets are bytes from the operand's base, without the k-tile.
@@ -518,8 +522,8 @@ __global__ __launch_bounds__(256, PCU) void tile_gemm_kernel(const uint4 *__rest
   uint32_t base[G], oob[G];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    const int q = 4 * i + wave;
-    if (4 * i < AT) {
+    const int q = NW * i + wave;
+    if (NW * i < AT) {
       const int rb = mb0 + q % BM;
       base[i] = (uint32_t)min(rb, a_blocks - 1) * (uint32_t)a_kt * 1024u;
       oob[i] = rb < a_blocks ? 0u : 0x80000000u;
@@ -533,9 +537,9 @@ __global__ __launch_bounds__(256, PCU) void tile_gemm_kernel(const uint4 *__rest
   auto issue = [&](int st, int kt, int i) {
     const uint32_t kflag = kt < kt_count ? 0u : 0x80000000u;
     const uint32_t koff = (uint32_t)min(kt, kt_count - 1) * 1024u;
-    const u32x4 d = 4 * i < AT ? ((4 * i) / BM == 0 ? dhi : dlo) : dw;
+    const u32x4 d = NW * i < AT ? ((NW * i) / BM == 0 ? dhi : dlo) : dw;
     load_to_lds16(lane_bytes | oob[i] | kflag, d, base[i] + koff,
-                  lds_base + (uint32_t)(st * TILES * 1024) + (uint32_t)((4 * i + wave) * 1024));
+                  lds_base + (uint32_t)(st * TILES * 1024) + (uint32_t)((NW * i + wave) * 1024));
   };
 
   // Register set b holds this wave's fragments of one k-tile: its row half's activation tiles of each
@@ -602,7 +606,7 @@ __global__ __launch_bounds__(256, PCU) void tile_gemm_kernel(const uint4 *__rest
   const int rq = (lane >> 4) * 4, cq = lane & 15;
   const int mw = mb0 + wr * WM, nw = nb0 + wc * WNT;
   if constexpr (ROPE) {
-    static_assert(4 * (16 * (WNT * 16 + 4) + 16 * 64 * 2) * 4 <= R * TILES * 1024, "four waves' staging fits the LDS");
+    static_assert(NW * (16 * (WNT * 16 + 4) + 16 * 64 * 2) * 4 <= R * TILES * 1024, "the waves' staging fits the LDS");
     tile_rope_epilogue<WM, WNT>(lds, acc, wunscale, o, rows, n_blocks, mw, nw, wave, lane);
   } else if (o.kind == kSiluMul) {
 #pragma unroll
@@ -689,7 +693,7 @@ size_t linear_partial_floats(int rows, int n, int k, SplitPolicy policy) {
   return (size_t)max_slots * rows * n;
 }
 
-// Prefill tile shape (WM row blocks x WNT column blocks per wave, four waves per block).  Blocks with more
+// Prefill tile shape (WM row blocks x WNT column blocks per wave, 2 x WC waves per block).  Blocks with more
 // than 80 KiB of LDS stages run one per CU, smaller ones two, so a launch runs in rounds of 256 or 512
 // blocks; a round's time scales with the MFMAs a SIMD runs in it, and smaller tiles load more bytes per
 // MFMA (relative speeds below are estimates, but for the measured two-per-CU 4 x 8).  Two blocks per CU
@@ -697,46 +701,56 @@ size_t linear_partial_floats(int rows, int n, int k, SplitPolicy policy) {
 // cut the idle tail of a launch whose tile count is not a multiple of 256.  The shape with the least
 // estimated time wins, larger tiles on ties.
 struct TileChoice {
-  int wm, wnt, pcu, tiles_m, tiles_n;
+  int wm, wnt, pcu, tiles_m, tiles_n, wc = 2;  // wc: column waves (2, or 4: eight waves per block)
 };
-static TileChoice choose_tiles(int rows, int n_blocks, int planes) {
+static TileChoice choose_tiles(int rows, int n_blocks, int planes, bool waves8_ok) {
   // pcu 2: two blocks per CU, each with half the LDS (3 stages of 24 KiB); measured on the 7B gate/up
-  // product (2048 rows, 1376 tiles of 4 x 8) at 0.95 of the 8 x 8 tiles' time for the same MFMAs per SIMD
+  // product (2048 rows, 1376 tiles of 4 x 8) at 0.95 of the 8 x 8 tiles' time for the same MFMAs per SIMD.
+  // wc 4: eight waves of 4 x 4 on a 128 x 256 tile, two per SIMD, so one wave's MFMAs run while the
+  // other waits; measured on the 7B o and down products (256 tiles at 2048 rows) at 0.9 of the four-wave
+  // 4 x 8 tile's time.  (The RoPE epilogue's staging is sized for four waves.)
   static const struct {
-    int wm, wnt, pcu;
+    int wm, wnt, pcu, wc;
     double speed;
-  } shapes[] = {{8, 8, 1, 1.0}, {8, 6, 1, 0.95}, {4, 8, 1, 0.85}, {8, 4, 1, 0.85}, {4, 4, 1, 0.7}, {4, 8, 2, 1.05}};
+  } shapes[] = {{8, 8, 1, 2, 1.0},  {8, 6, 1, 2, 0.95}, {4, 8, 1, 2, 0.85}, {8, 4, 1, 2, 0.85},
+                {4, 4, 1, 2, 0.7},  {4, 8, 2, 2, 1.05}, {4, 4, 1, 4, 0.95}};
   const int row_blocks = (rows + 15) / 16;
   TileChoice best{0, 0, 1, 0, 0};
   double best_cost = 1e300;
   for (const auto &sh : shapes) {
-    const int tiles_kib = planes * 2 * sh.wm + 2 * sh.wnt;
+    if (sh.wc > 2 && (!waves8_ok || planes > 1)) continue;
+    const int bm = 2 * sh.wm, bn = sh.wc * sh.wnt;  // the block tile in 16-row / 16-column blocks
+    const int tiles_kib = planes * bm + bn;
     const int stages = std::min(4, 160 / sh.pcu / tiles_kib);
     if (sh.pcu > 1 && stages < 3) continue;
     // blocks of at most 80 KiB run two per CU whatever their bounds say (4 x 4)
     const int per_cu = sh.pcu > 1 || stages * tiles_kib <= 80 ? 2 : 1;
-    const int tm = (row_blocks + 2 * sh.wm - 1) / (2 * sh.wm), tn = (n_blocks + 2 * sh.wnt - 1) / (2 * sh.wnt);
+    const int tm = (row_blocks + bm - 1) / bm, tn = (n_blocks + bn - 1) / bn;
     const long tiles = (long)tm * tn;
     // two blocks per CU only pay when the launch fills the second slots
     if (sh.pcu > 1 && tiles <= (long)kCUs) continue;
-    const double cost = (double)((tiles + per_cu * kCUs - 1) / (per_cu * kCUs)) * per_cu * sh.wm * sh.wnt / sh.speed;
-    if (cost < best_cost * 0.999) best_cost = cost, best = TileChoice{sh.wm, sh.wnt, sh.pcu, tm, tn};
+    // a round's time: the MFMAs of the waves a SIMD runs in it
+    const double cost = (double)((tiles + per_cu * kCUs - 1) / (per_cu * kCUs)) * per_cu * (sh.wc / 2) * sh.wm *
+                        sh.wnt / sh.speed;
+    if (cost < best_cost * 0.999) best_cost = cost, best = TileChoice{sh.wm, sh.wnt, sh.pcu, tm, tn, sh.wc};
   }
   return best;
 }
 
-template <int WM, int WNT, int NP, int PCU>
+template <int WM, int WNT, int NP, int PCU, int WC = 2>
 static void launch_tile(hipStream_t s, const TileChoice &tc, const uint4 *act, const uint4 *lo, int a_kt,
                         int a_blocks, int rows, const uint4 *w, const uint4 *w_end, int kt_count, int n_blocks,
                         const LinearOut &o) {
   const int n_tiles = tc.tiles_m * tc.tiles_n;
   const int grid = (n_tiles + 7) / 8 * 8;
-  if (o.kind == kRope)
-    tile_gemm_kernel<WM, WNT, NP, PCU, true><<<grid, 256, 0, s>>>(act, lo, a_kt, a_blocks, rows, w, w_end, kt_count,
-                                                                  n_blocks, tc.tiles_m, n_tiles, o);
-  else
-    tile_gemm_kernel<WM, WNT, NP, PCU, false><<<grid, 256, 0, s>>>(act, lo, a_kt, a_blocks, rows, w, w_end, kt_count,
-                                                                   n_blocks, tc.tiles_m, n_tiles, o);
+  constexpr int threads = 64 * 2 * WC;
+  if (o.kind == kRope) {
+    if constexpr (WC == 2)  // the RoPE epilogue's staging is sized for four waves
+      tile_gemm_kernel<WM, WNT, NP, PCU, true, 2, WC><<<grid, threads, 0, s>>>(
+          act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, tc.tiles_m, n_tiles, o);
+  } else
+    tile_gemm_kernel<WM, WNT, NP, PCU, false, 2, WC><<<grid, threads, 0, s>>>(
+        act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, tc.tiles_m, n_tiles, o);
 }
 
 template <int NP>
@@ -745,7 +759,9 @@ static void launch_tiles(const TileChoice &tc, hipStream_t s, const uint4 *act, 
                          const LinearOut &o) {
 #define LLMDEC_TILE(WM_, WNT_, PCU_) \
   launch_tile<WM_, WNT_, NP, PCU_>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o)
-  if (tc.pcu == 2) {
+  if (tc.wc == 4) {
+    if constexpr (NP == 1) launch_tile<4, 4, 1, 1, 4>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
+  } else if (tc.pcu == 2) {
     if constexpr (NP == 1) LLMDEC_TILE(4, 8, 2);  // the only two-per-CU shape (3 stages fit one plane only)
   } else if (tc.wm == 8 && tc.wnt == 8) {
     LLMDEC_TILE(8, 8, 1);
@@ -801,7 +817,7 @@ static Splits launch_linear_np(const Act &a, const uint16_t *w_packed, int n_tot
     return p.sp;
   }
   // tile shape: the largest tiles that still give every CU work in whole rounds where possible
-  const TileChoice tc = choose_tiles(a.rows, n_blocks, NP);
+  const TileChoice tc = choose_tiles(a.rows, n_blocks, NP, o.kind != kRope);
   launch_tiles<NP>(tc, s, act, lo, a_kt, a.row_blocks, a.rows, w, w_end, kt_count, n_blocks, o);
   return Splits{};
 }

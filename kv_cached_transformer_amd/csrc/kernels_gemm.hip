@@ -399,9 +399,10 @@ template <int WM, int WNT, int NP, int PCU = 1, int WR = 2, int WC = 2> struct T
 
 // The kRope epilogue (see RopeRows).  Each wave passes its results through its own share of the LDS
 // (free once the k-loop has ended), one 16-row block at a time: its accumulators go to a row-major
-// staging area and the block's rows of the rotation table beside them; the wave then walks the staged
-// rows pair by pair, lane l taking pair l of a row (two rows a step when a row holds 32 pairs), so a q
-// row leaves as contiguous fp32 pairs and a k row as contiguous bf16 pairs.  The walk is a short loop,
+// staging area, and for each 8-row half of the block that half's rows of the rotation table go beside
+// them; the wave then walks the staged rows pair by pair, lane l taking pair l of a row (two rows a step
+// when a row holds 32 pairs), so a q row leaves as contiguous fp32 pairs and a k row as contiguous bf16
+// pairs.  The walk is a short loop,
 // not one unrolled copy per accumulator (an epilogue that large runs from outside the instruction
 // cache).  The rows' page slots are looked up once, lane l holding rows l and l + 64 of the wave.
 template <int WM, int WNT>
@@ -410,7 +411,7 @@ __device__ __forceinline__ void tile_rope_epilogue(uint4 *lds, const f32x4 (&acc
                                                    int wave, int lane) {
   constexpr int P = WNT * 8;            // pairs per row of the wave's columns
   constexpr int PITCH = WNT * 16 + 4;   // floats per staged row (the 4-float skew spreads the rows' banks)
-  constexpr int STEPS = 16 * P / 64;    // walk steps per 16-row block
+  constexpr int STEPS = 8 * P / 64;     // walk steps per 8-row half
   static_assert(WM * 16 <= 128, "two page slots per lane");
   const RopeRows &rp = o.rope;
   const int D = rp.head_dim, half = D >> 1;
@@ -419,8 +420,8 @@ __device__ __forceinline__ void tile_rope_epilogue(uint4 *lds, const f32x4 (&acc
   const int c0 = nw * 16;                                  // the wave's first column of the product
   const int ncols = min(WNT * 16, (n_blocks - nw) * 16);  // its real columns (none past the matrix)
   const int rq = (lane >> 4) * 4, cq = lane & 15;
-  float *st = reinterpret_cast<float *>(lds) + wave * (16 * PITCH + 16 * 64 * 2);
-  float2 *cs = reinterpret_cast<float2 *>(st + 16 * PITCH);  // [16 rows][half]
+  float *st = reinterpret_cast<float *>(lds) + wave * (16 * PITCH + 8 * 64 * 2);
+  float2 *cs = reinterpret_cast<float2 *>(st + 16 * PITCH);  // [8 rows][half]
 
   // page slots of rows mw*16 + lane and + 64 (K/V products): page -1 = no store (flagged)
   int2 slot[2] = {make_int2(-1, 0), make_int2(-1, 0)};
@@ -446,47 +447,52 @@ __device__ __forceinline__ void tile_rope_epilogue(uint4 *lds, const f32x4 (&acc
   StaticFor<0, WM>::run([&](auto mc) __attribute__((always_inline)) {
     constexpr int m = decltype(mc)::value;
     const int r0 = (mw + m) * 16;  // the block's first row
-    {  // its 16 table rows (16 * half pairs, as float4), all loads first (a row past the product re-reads
-       // the last row; it is not used)
-      const int n4 = 8 * half;
-      float4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int q = min(u * 64 + lane, n4 - 1), rr = (2 * q) / half;
-        v[u] = *reinterpret_cast<const float4 *>(rp.cs + (size_t)min(r0 + rr, rows - 1) * half + (2 * q - rr * half));
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (u * 64 + lane < n4) reinterpret_cast<float4 *>(cs)[u * 64 + lane] = v[u];
-    }
 #pragma unroll
     for (int j = 0; j < WNT; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) st[(rq + e) * PITCH + j * 16 + cq] = acc[m][j][e] * wunscale;
-    for (int it = 0; it < STEPS; ++it) {
-      const int idx = it * 64 + lane, rl = idx / P, p = idx - rl * P;
-      const int r = r0 + rl, rw = m * 16 + rl;  // row of the product, of the wave
-      const int2 ps = make_int2(__shfl(slot[rw >> 6].x, rw & 63, 64), __shfl(slot[rw >> 6].y, rw & 63, 64));
-      if (r >= rows || 2 * p >= ncols) continue;
-      const float2 xv = *reinterpret_cast<const float2 *>(st + rl * PITCH + 2 * p);
-      const int col = rp.col0 + c0 + 2 * p;
-      if (col < hid + kvc) {  // q or k: rotate the pair
-        const int d = col < hid ? col : col - hid;
-        const float2 t = cs[rl * half + ((d % D) >> 1)];
-        const float re = xv.x * t.x - xv.y * t.y, ro = xv.x * t.y + xv.y * t.x;
-        if (col < hid) {
-          *reinterpret_cast<float2 *>(o.f32 + (size_t)r * o.ld + c0 + 2 * p) = make_float2(re, ro);
-        } else if (ps.x >= 0) {  // K [h][o][d]
-          const size_t head = (size_t)ps.x * rp.n_kv_heads + d / D;
-          *reinterpret_cast<uint32_t *>(rp.pool_k + (head * 16 + ps.y) * D + (d % D)) =
-              f32_to_bf16(re) | ((uint32_t)f32_to_bf16(ro) << 16);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      {  // the half's 8 table rows (8 * half pairs, as float4), all loads first (a row past the product
+         // re-reads the last row; it is not used)
+        const int n4 = 4 * half;
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = min(u * 64 + lane, n4 - 1), rr = (2 * q) / half;
+          v[u] = *reinterpret_cast<const float4 *>(rp.cs + (size_t)min(r0 + 8 * hh + rr, rows - 1) * half +
+                                                   (2 * q - rr * half));
         }
-      } else if (ps.x >= 0) {  // V [h][o/4][d][o%4]
-        const int d = col - hid - kvc;
-        const size_t head = (size_t)ps.x * rp.n_kv_heads + d / D;
-        uint16_t *vp = rp.pool_v + (head * 4 + (ps.y >> 2)) * D * 4 + (size_t)(d % D) * 4 + (ps.y & 3);
-        vp[0] = f32_to_bf16(xv.x);
-        vp[4] = f32_to_bf16(xv.y);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (u * 64 + lane < n4) reinterpret_cast<float4 *>(cs)[u * 64 + lane] = v[u];
+      }
+      for (int it = 0; it < STEPS; ++it) {
+        const int idx = it * 64 + lane, rh = idx / P, p = idx - rh * P;
+        const int rl = 8 * hh + rh;               // row within the block
+        const int r = r0 + rl, rw = m * 16 + rl;  // row of the product, of the wave
+        const int2 ps = make_int2(__shfl(slot[rw >> 6].x, rw & 63, 64), __shfl(slot[rw >> 6].y, rw & 63, 64));
+        if (r >= rows || 2 * p >= ncols) continue;
+        const float2 xv = *reinterpret_cast<const float2 *>(st + rl * PITCH + 2 * p);
+        const int col = rp.col0 + c0 + 2 * p;
+        if (col < hid + kvc) {  // q or k: rotate the pair
+          const int d = col < hid ? col : col - hid;
+          const float2 t = cs[rh * half + ((d % D) >> 1)];
+          const float re = xv.x * t.x - xv.y * t.y, ro = xv.x * t.y + xv.y * t.x;
+          if (col < hid) {
+            *reinterpret_cast<float2 *>(o.f32 + (size_t)r * o.ld + c0 + 2 * p) = make_float2(re, ro);
+          } else if (ps.x >= 0) {  // K [h][o][d]
+            const size_t head = (size_t)ps.x * rp.n_kv_heads + d / D;
+            *reinterpret_cast<uint32_t *>(rp.pool_k + (head * 16 + ps.y) * D + (d % D)) =
+                f32_to_bf16(re) | ((uint32_t)f32_to_bf16(ro) << 16);
+          }
+        } else if (ps.x >= 0) {  // V [h][o/4][d][o%4]
+          const int d = col - hid - kvc;
+          const size_t head = (size_t)ps.x * rp.n_kv_heads + d / D;
+          uint16_t *vp = rp.pool_v + (head * 4 + (ps.y >> 2)) * D * 4 + (size_t)(d % D) * 4 + (ps.y & 3);
+          vp[0] = f32_to_bf16(xv.x);
+          vp[4] = f32_to_bf16(xv.y);
+        }
       }
     }
   });
@@ -606,7 +612,7 @@ __global__ __launch_bounds__(64 * WR * WC, PCU) void tile_gemm_kernel(const uint
   const int rq = (lane >> 4) * 4, cq = lane & 15;
   const int mw = mb0 + wr * WM, nw = nb0 + wc * WNT;
   if constexpr (ROPE) {
-    static_assert(NW * (16 * (WNT * 16 + 4) + 16 * 64 * 2) * 4 <= R * TILES * 1024, "the waves' staging fits the LDS");
+    static_assert(NW * (16 * (WNT * 16 + 4) + 8 * 64 * 2) * 4 <= R * TILES * 1024, "the waves' staging fits the LDS");
     tile_rope_epilogue<WM, WNT>(lds, acc, wunscale, o, rows, n_blocks, mw, nw, wave, lane);
   } else if (o.kind == kSiluMul) {
 #pragma unroll
@@ -703,12 +709,12 @@ size_t linear_partial_floats(int rows, int n, int k, SplitPolicy policy) {
 struct TileChoice {
   int wm, wnt, pcu, tiles_m, tiles_n, wc = 2;  // wc: column waves (2, or 4: eight waves per block)
 };
-static TileChoice choose_tiles(int rows, int n_blocks, int planes, bool waves8_ok) {
+static TileChoice choose_tiles(int rows, int n_blocks, int planes) {
   // pcu 2: two blocks per CU, each with half the LDS (3 stages of 24 KiB); measured on the 7B gate/up
   // product (2048 rows, 1376 tiles of 4 x 8) at 0.95 of the 8 x 8 tiles' time for the same MFMAs per SIMD.
   // wc 4: eight waves of 4 x 4 on a 128 x 256 tile, two per SIMD, so one wave's MFMAs run while the
   // other waits; measured on the 7B o and down products (256 tiles at 2048 rows) at 0.9 of the four-wave
-  // 4 x 8 tile's time.  (The RoPE epilogue's staging is sized for four waves.)
+  // 4 x 8 tile's time.
   static const struct {
     int wm, wnt, pcu, wc;
     double speed;
@@ -718,7 +724,9 @@ static TileChoice choose_tiles(int rows, int n_blocks, int planes, bool waves8_o
   TileChoice best{0, 0, 1, 0, 0};
   double best_cost = 1e300;
   for (const auto &sh : shapes) {
-    if (sh.wc > 2 && (!waves8_ok || planes > 1)) continue;
+    // (as 512 tiles of 4 x 4 on the pair, the 7B k|v product measured 234 against 229 us for 256 of 8 x 8)
+    if (sh.wc > 2 && planes > 1) continue;
+    const double speed = sh.speed;
     const int bm = 2 * sh.wm, bn = sh.wc * sh.wnt;  // the block tile in 16-row / 16-column blocks
     const int tiles_kib = planes * bm + bn;
     const int stages = std::min(4, 160 / sh.pcu / tiles_kib);
@@ -731,7 +739,7 @@ static TileChoice choose_tiles(int rows, int n_blocks, int planes, bool waves8_o
     if (sh.pcu > 1 && tiles <= (long)kCUs) continue;
     // a round's time: the MFMAs of the waves a SIMD runs in it
     const double cost = (double)((tiles + per_cu * kCUs - 1) / (per_cu * kCUs)) * per_cu * (sh.wc / 2) * sh.wm *
-                        sh.wnt / sh.speed;
+                        sh.wnt / speed;
     if (cost < best_cost * 0.999) best_cost = cost, best = TileChoice{sh.wm, sh.wnt, sh.pcu, tm, tn, sh.wc};
   }
   return best;
@@ -744,11 +752,10 @@ static void launch_tile(hipStream_t s, const TileChoice &tc, const uint4 *act, c
   const int n_tiles = tc.tiles_m * tc.tiles_n;
   const int grid = (n_tiles + 7) / 8 * 8;
   constexpr int threads = 64 * 2 * WC;
-  if (o.kind == kRope) {
-    if constexpr (WC == 2)  // the RoPE epilogue's staging is sized for four waves
-      tile_gemm_kernel<WM, WNT, NP, PCU, true, 2, WC><<<grid, threads, 0, s>>>(
-          act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, tc.tiles_m, n_tiles, o);
-  } else
+  if (o.kind == kRope)
+    tile_gemm_kernel<WM, WNT, NP, PCU, true, 2, WC><<<grid, threads, 0, s>>>(
+        act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, tc.tiles_m, n_tiles, o);
+  else
     tile_gemm_kernel<WM, WNT, NP, PCU, false, 2, WC><<<grid, threads, 0, s>>>(
         act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, tc.tiles_m, n_tiles, o);
 }
@@ -760,7 +767,7 @@ static void launch_tiles(const TileChoice &tc, hipStream_t s, const uint4 *act, 
 #define LLMDEC_TILE(WM_, WNT_, PCU_) \
   launch_tile<WM_, WNT_, NP, PCU_>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o)
   if (tc.wc == 4) {
-    if constexpr (NP == 1) launch_tile<4, 4, 1, 1, 4>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
+    launch_tile<4, 4, NP, 1, 4>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
   } else if (tc.pcu == 2) {
     if constexpr (NP == 1) LLMDEC_TILE(4, 8, 2);  // the only two-per-CU shape (3 stages fit one plane only)
   } else if (tc.wm == 8 && tc.wnt == 8) {
@@ -817,7 +824,7 @@ static Splits launch_linear_np(const Act &a, const uint16_t *w_packed, int n_tot
     return p.sp;
   }
   // tile shape: the largest tiles that still give every CU work in whole rounds where possible
-  const TileChoice tc = choose_tiles(a.rows, n_blocks, NP, o.kind != kRope);
+  const TileChoice tc = choose_tiles(a.rows, n_blocks, NP);
   launch_tiles<NP>(tc, s, act, lo, a_kt, a.row_blocks, a.rows, w, w_end, kt_count, n_blocks, o);
   return Splits{};
 }

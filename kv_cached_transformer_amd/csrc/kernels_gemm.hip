@@ -712,14 +712,15 @@ struct TileChoice {
 static TileChoice choose_tiles(int rows, int n_blocks, int planes) {
   // pcu 2: two blocks per CU, each with half the LDS (3 stages of 24 KiB); measured on the 7B gate/up
   // product (2048 rows, 1376 tiles of 4 x 8) at 0.95 of the 8 x 8 tiles' time for the same MFMAs per SIMD.
-  // wc 4: eight waves of 4 x 4 on a 128 x 256 tile, two per SIMD, so one wave's MFMAs run while the
-  // other waits; measured on the 7B o and down products (256 tiles at 2048 rows) at 0.9 of the four-wave
-  // 4 x 8 tile's time.
+  // wc 4: eight waves of 4 x 4 on a 128 x 256 tile, or of 8 x 4 on a 256 x 256 one, two per SIMD, so one
+  // wave's MFMAs run while the other waits; measured on the 7B o and down products (256 tiles at 2048
+  // rows) at 0.9 of the four-wave 4 x 8 tile's time, and on gate/up (688 tiles of 256 x 256) at 0.96 of
+  // the two-per-CU 4 x 8 tiles' time.
   static const struct {
     int wm, wnt, pcu, wc;
     double speed;
   } shapes[] = {{8, 8, 1, 2, 1.0},  {8, 6, 1, 2, 0.95}, {4, 8, 1, 2, 0.85}, {8, 4, 1, 2, 0.85},
-                {4, 4, 1, 2, 0.7},  {4, 8, 2, 2, 1.05}, {4, 4, 1, 4, 0.95}};
+                {4, 4, 1, 2, 0.7},  {4, 8, 2, 2, 1.05}, {4, 4, 1, 4, 0.95}, {8, 4, 1, 4, 1.1}};
   const int row_blocks = (rows + 15) / 16;
   TileChoice best{0, 0, 1, 0, 0};
   double best_cost = 1e300;
@@ -766,7 +767,9 @@ static void launch_tiles(const TileChoice &tc, hipStream_t s, const uint4 *act, 
                          const LinearOut &o) {
 #define LLMDEC_TILE(WM_, WNT_, PCU_) \
   launch_tile<WM_, WNT_, NP, PCU_>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o)
-  if (tc.wc == 4) {
+  if (tc.wc == 4 && tc.wm == 8) {
+    if constexpr (NP == 1) launch_tile<8, 4, 1, 1, 4>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
+  } else if (tc.wc == 4) {
     launch_tile<4, 4, NP, 1, 4>(s, tc, act, lo, a_kt, a_blocks, rows, w, w_end, kt_count, n_blocks, o);
   } else if (tc.pcu == 2) {
     if constexpr (NP == 1) LLMDEC_TILE(4, 8, 2);  // the only two-per-CU shape (3 stages fit one plane only)

@@ -54,7 +54,6 @@ WsLayout ws_layout(const llmdec_config &c, int max_tokens, int max_seqs, int max
   L.err = take(kWsHeader);
   L.tok_seq = take(sizeof(int32_t) * T);
   L.tok_pos = take(sizeof(int32_t) * T);
-  L.rope_cs = take(T > 64 ? sizeof(float2) * T * (c.head_dim / 2) : 0);  // prefill rotations
   L.x = take(sizeof(float) * (size_t)rows * h);
   L.act_h = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_h);
   L.act_hl = take(sizeof(uint16_t) * (size_t)L.row_blocks * 16 * L.kpad_h);
@@ -197,8 +196,8 @@ static Splits run_layer(const LayerArgs &a) {
   int32_t *ts = at<int32_t>(a.ws, L.tok_seq), *tp = at<int32_t>(a.ws, L.tok_pos);
   if (!a.decode) launch_token_map(a.cu, a.start, a.n_seqs, M, err, ts, tp, a.s);
   // A split q|k|v product leaves partial sums that the rotary/append kernel adds up.  A tiled prefill
-  // product applies RoPE and the K/V append in its own epilogue (kRope), from a table of the tokens'
-  // rotations, so no rotary/append pass follows it.
+  // product applies RoPE and the K/V append in its own epilogue (kRope), so no rotary/append pass
+  // follows it.
   const bool fused_rope = !pairs && !a.decode;
   Splits sp_qkv;
   if (pairs) {
@@ -208,10 +207,9 @@ static Splits run_layer(const LayerArgs &a) {
     LinearOut o_q = o_qkv, o_kv = o_qkv;
     o_kv.f32 = qkv + nq;
     if (fused_rope) {
-      float2 *cs = at<float2>(a.ws, L.rope_cs);
-      launch_rope_table(c, tp, M, cs, a.s);
       RopeRows rr;
-      rr.cs = cs, rr.tok_seq = ts, rr.tok_pos = tp, rr.block_tables = a.bt;
+      rr.fr = rope_freq(c);
+      rr.tok_seq = ts, rr.tok_pos = tp, rr.block_tables = a.bt;
       rr.pool_k = pk, rr.pool_v = pv, rr.err = err;
       rr.n_seqs = a.n_seqs, rr.max_pages = a.max_pages, rr.num_pages = a.pool->num_pages;
       rr.n_heads = c.n_heads, rr.n_kv_heads = c.n_kv_heads, rr.head_dim = c.head_dim;

@@ -28,15 +28,20 @@ struct Act {
 
 enum Epilogue { kStore = 0, kAccumulate = 1, kSiluMul = 2, kRope = 3 };
 
+struct RopeFreq {
+  double inv_freq[64];
+};
+RopeFreq rope_freq(const llmdec_config &cfg);
+
 // The kRope epilogue of a prefill q|k|v product (tiled products only, more than 64 rows).  Row r is
-// token r: its sequence and position come from tok_seq / tok_pos, the rotation of its pair i from cs
-// [token][head_dim / 2] (cos, sin).  The product's column c is column col0 + c of the q|k|v row: q
+// token r: its sequence and position come from tok_seq / tok_pos; pair i turns by pos * fr.inv_freq[i],
+// as in the RoPE/append kernel.  The product's column c is column col0 + c of the q|k|v row: q
 // columns are rotated and stored to f32[r*ld + c]; k columns are rotated, v columns left as they are,
 // and both rounded to bf16 and written to the page slot block_tables[seq][pos / 16], offset pos % 16,
 // as the RoPE/append kernel stores them (a bad sequence, position or page sets err, and that row's K/V
 // are not written).
 struct RopeRows {
-  const float2 *cs = nullptr;
+  RopeFreq fr;
   const int32_t *tok_seq = nullptr, *tok_pos = nullptr, *block_tables = nullptr;
   uint16_t *pool_k = nullptr, *pool_v = nullptr;
   uint32_t *err = nullptr;
@@ -88,7 +93,7 @@ inline int kv_cols(const llmdec_config &c) { return c.n_kv_heads * c.head_dim; }
 
 // Workspace layout for steps of up to max_tokens tokens and max_seqs sequences.
 struct WsLayout {
-  size_t err, tok_seq, tok_pos, rope_cs, x, act_h, act_hl, act_i, act_il, qkv, part, attn_part, logits, total;
+  size_t err, tok_seq, tok_pos, x, act_h, act_hl, act_i, act_il, qkv, part, attn_part, logits, total;
   size_t part_floats;
   int max_tokens, max_seqs, max_pages, row_blocks, kpad_h, kpad_i, attn_slots;
 };
@@ -140,17 +145,10 @@ void launch_linear_cols(const Act &a, const uint16_t *w_packed, int n_total, int
 // Sum the partial products of a split product and apply the epilogue o.
 void launch_reduce(const float *partials, const Splits &sp, int rows, int n, const LinearOut &o, hipStream_t s);
 
-struct RopeFreq {
-  double inv_freq[64];
-};
-RopeFreq rope_freq(const llmdec_config &cfg);
 
 size_t linear_partial_floats(int rows, int n, int k, SplitPolicy policy = kSplitBalanced);
 void launch_token_map(const int32_t *cu_seqlens, const int32_t *start_pos, int n_seqs, int n_tokens, uint32_t *err, int32_t *tok_seq,
                       int32_t *tok_pos, hipStream_t s);
-// The rotation table of a prefill: cs[t][i] = (cos, sin) of tok_pos[t] * inv_freq[i], i < head_dim / 2,
-// computed as the RoPE/append kernel computes them.
-void launch_rope_table(const llmdec_config &cfg, const int32_t *tok_pos, int n_tokens, float2 *cs, hipStream_t s);
 // qkv_partials / sp: when the q|k|v product was split, its partial sums [plane][n_tokens][3*hidden] are
 // added first (and the sum written to qkv); NULL otherwise.
 void launch_rope_append(const llmdec_config &cfg, float *qkv, const float *qkv_partials, const Splits &sp, int ld_qkv,

@@ -399,50 +399,55 @@ template <int WM, int WNT, int NP, int PCU = 1, int WR = 2, int WC = 2> struct T
 
 // The kRope epilogue (see RopeRows).  Each wave passes its results through its own share of the LDS
 // (free once the k-loop has ended), one 16-row block at a time: its accumulators go to a row-major
-// staging area, and for each 8-row half of the block that half's rows of the rotation table go beside
-// them; the wave then walks the staged rows pair by pair, lane l taking pair l of a row (two rows a step
-// when a row holds 32 pairs), so a q row leaves as contiguous fp32 pairs and a k row as contiguous bf16
-// pairs.  The walk is a short loop,
-// not one unrolled copy per accumulator (an epilogue that large runs from outside the instruction
-// cache).  The rows' page slots are looked up once, lane l holding rows l and l + 64 of the wave.
+// staging area, and the wave then walks the staged rows pair by pair, lane l taking pair l of a row (two
+// rows a step when a row holds 32 pairs), so a q row leaves as contiguous fp32 pairs and a k row as
+// contiguous bf16 pairs.  The walk is a short loop, not one unrolled copy per accumulator (an epilogue
+// that large runs from outside the instruction cache).  Each pair's rotation is formed where it is used
+// (the angle reduced in double, then sine and cosine in fp32, as the RoPE/append kernel does): a load
+// from memory in the walk would make the wave wait for its earlier stores too.  The rows' positions
+// and page slots are looked up once, lane l holding rows l and l + 64 of the wave.
 template <int WM, int WNT>
 __device__ __forceinline__ void tile_rope_epilogue(uint4 *lds, const f32x4 (&acc)[WM][WNT], float wunscale,
                                                    const LinearOut &o, int rows, int n_blocks, int mw, int nw,
                                                    int wave, int lane) {
   constexpr int P = WNT * 8;            // pairs per row of the wave's columns
   constexpr int PITCH = WNT * 16 + 4;   // floats per staged row (the 4-float skew spreads the rows' banks)
-  constexpr int STEPS = 8 * P / 64;     // walk steps per 8-row half
-  static_assert(WM * 16 <= 128, "two page slots per lane");
+  constexpr int STEPS = 16 * P / 64;    // walk steps per 16-row block
+  static_assert(WM * 16 <= 128, "two rows per lane");
   const RopeRows &rp = o.rope;
-  const int D = rp.head_dim, half = D >> 1;
+  const int D = rp.head_dim;
   const int hid = rp.n_heads * D, kvc = rp.n_kv_heads * D;
   const bool kv = rp.col0 > 0;
   const int c0 = nw * 16;                                  // the wave's first column of the product
   const int ncols = min(WNT * 16, (n_blocks - nw) * 16);  // its real columns (none past the matrix)
   const int rq = (lane >> 4) * 4, cq = lane & 15;
-  float *st = reinterpret_cast<float *>(lds) + wave * (16 * PITCH + 8 * 64 * 2);
-  float2 *cs = reinterpret_cast<float2 *>(st + 16 * PITCH);  // [8 rows][half]
+  float *st = reinterpret_cast<float *>(lds) + wave * (16 * PITCH + 2 * 64);
+  double *fq = reinterpret_cast<double *>(st + 16 * PITCH);  // [64] rotation frequencies
 
-  // page slots of rows mw*16 + lane and + 64 (K/V products): page -1 = no store (flagged)
+  // positions and page slots (K/V products; page -1 = no store, flagged) of rows mw*16 + lane and + 64
+  int pos_r[2] = {0, 0};
   int2 slot[2] = {make_int2(-1, 0), make_int2(-1, 0)};
-  if (kv) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = mw * 16 + lane + 64 * h;
-      if (lane + 64 * h >= WM * 16 || r >= rows) continue;
-      const int seq = rp.tok_seq[r], pos = rp.tok_pos[r];
-      if (seq < 0 || seq >= rp.n_seqs) {
-        raise_error(rp.err, kErrSeq);
-      } else if (pos < 0 || (pos >> 4) >= rp.max_pages) {
-        raise_error(rp.err, kErrPos);
-      } else {
-        const int page = rp.block_tables[(size_t)seq * rp.max_pages + (pos >> 4)];
-        if (page < 0 || page >= rp.num_pages) raise_error(rp.err, kErrPage);
-        else slot[h] = make_int2(page, pos & 15);
-      }
+  for (int h = 0; h < 2; ++h) {
+    const int r = mw * 16 + lane + 64 * h;
+    if (lane + 64 * h >= WM * 16 || r >= rows) continue;
+    const int pos = rp.tok_pos[r];
+    pos_r[h] = pos;
+    if (!kv) continue;
+    const int seq = rp.tok_seq[r];
+    if (seq < 0 || seq >= rp.n_seqs) {
+      raise_error(rp.err, kErrSeq);
+    } else if (pos < 0 || (pos >> 4) >= rp.max_pages) {
+      raise_error(rp.err, kErrPos);
+    } else {
+      const int page = rp.block_tables[(size_t)seq * rp.max_pages + (pos >> 4)];
+      if (page < 0 || page >= rp.num_pages) raise_error(rp.err, kErrPage);
+      else slot[h] = make_int2(page, pos & 15);
     }
   }
+  const double f_lane = rp.fr.inv_freq[lane];
   __syncthreads();  // every wave's k-loop reads of the LDS are done
+  fq[lane] = f_lane;
 
   StaticFor<0, WM>::run([&](auto mc) __attribute__((always_inline)) {
     constexpr int m = decltype(mc)::value;
@@ -451,48 +456,32 @@ __device__ __forceinline__ void tile_rope_epilogue(uint4 *lds, const f32x4 (&acc
     for (int j = 0; j < WNT; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) st[(rq + e) * PITCH + j * 16 + cq] = acc[m][j][e] * wunscale;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      {  // the half's 8 table rows (8 * half pairs, as float4), all loads first (a row past the product
-         // re-reads the last row; it is not used)
-        const int n4 = 4 * half;
-        float4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int q = min(u * 64 + lane, n4 - 1), rr = (2 * q) / half;
-          v[u] = *reinterpret_cast<const float4 *>(rp.cs + (size_t)min(r0 + 8 * hh + rr, rows - 1) * half +
-                                                   (2 * q - rr * half));
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (u * 64 + lane < n4) reinterpret_cast<float4 *>(cs)[u * 64 + lane] = v[u];
-      }
-      for (int it = 0; it < STEPS; ++it) {
-        const int idx = it * 64 + lane, rh = idx / P, p = idx - rh * P;
-        const int rl = 8 * hh + rh;               // row within the block
-        const int r = r0 + rl, rw = m * 16 + rl;  // row of the product, of the wave
-        const int2 ps = make_int2(__shfl(slot[rw >> 6].x, rw & 63, 64), __shfl(slot[rw >> 6].y, rw & 63, 64));
-        if (r >= rows || 2 * p >= ncols) continue;
-        const float2 xv = *reinterpret_cast<const float2 *>(st + rl * PITCH + 2 * p);
-        const int col = rp.col0 + c0 + 2 * p;
-        if (col < hid + kvc) {  // q or k: rotate the pair
-          const int d = col < hid ? col : col - hid;
-          const float2 t = cs[rh * half + ((d % D) >> 1)];
-          const float re = xv.x * t.x - xv.y * t.y, ro = xv.x * t.y + xv.y * t.x;
-          if (col < hid) {
-            *reinterpret_cast<float2 *>(o.f32 + (size_t)r * o.ld + c0 + 2 * p) = make_float2(re, ro);
-          } else if (ps.x >= 0) {  // K [h][o][d]
-            const size_t head = (size_t)ps.x * rp.n_kv_heads + d / D;
-            *reinterpret_cast<uint32_t *>(rp.pool_k + (head * 16 + ps.y) * D + (d % D)) =
-                f32_to_bf16(re) | ((uint32_t)f32_to_bf16(ro) << 16);
-          }
-        } else if (ps.x >= 0) {  // V [h][o/4][d][o%4]
-          const int d = col - hid - kvc;
+    for (int it = 0; it < STEPS; ++it) {
+      const int idx = it * 64 + lane, rl = idx / P, p = idx - rl * P;
+      const int r = r0 + rl, rw = m * 16 + rl;  // row of the product, of the wave
+      const int2 ps = make_int2(__shfl(slot[rw >> 6].x, rw & 63, 64), __shfl(slot[rw >> 6].y, rw & 63, 64));
+      const int pos = __shfl(pos_r[rw >> 6], rw & 63, 64);
+      if (r >= rows || 2 * p >= ncols) continue;
+      const float2 xv = *reinterpret_cast<const float2 *>(st + rl * PITCH + 2 * p);
+      const int col = rp.col0 + c0 + 2 * p;
+      if (col < hid + kvc) {  // q or k: rotate the pair
+        const int d = col < hid ? col : col - hid;
+        float c, sn;
+        rope_cos_sin(pos, fq[(d % D) >> 1], c, sn);
+        const float re = xv.x * c - xv.y * sn, ro = xv.x * sn + xv.y * c;
+        if (col < hid) {
+          *reinterpret_cast<float2 *>(o.f32 + (size_t)r * o.ld + c0 + 2 * p) = make_float2(re, ro);
+        } else if (ps.x >= 0) {  // K [h][o][d]
           const size_t head = (size_t)ps.x * rp.n_kv_heads + d / D;
-          uint16_t *vp = rp.pool_v + (head * 4 + (ps.y >> 2)) * D * 4 + (size_t)(d % D) * 4 + (ps.y & 3);
-          vp[0] = f32_to_bf16(xv.x);
-          vp[4] = f32_to_bf16(xv.y);
+          *reinterpret_cast<uint32_t *>(rp.pool_k + (head * 16 + ps.y) * D + (d % D)) =
+              f32_to_bf16(re) | ((uint32_t)f32_to_bf16(ro) << 16);
         }
+      } else if (ps.x >= 0) {  // V [h][o/4][d][o%4]
+        const int d = col - hid - kvc;
+        const size_t head = (size_t)ps.x * rp.n_kv_heads + d / D;
+        uint16_t *vp = rp.pool_v + (head * 4 + (ps.y >> 2)) * D * 4 + (size_t)(d % D) * 4 + (ps.y & 3);
+        vp[0] = f32_to_bf16(xv.x);
+        vp[4] = f32_to_bf16(xv.y);
       }
     }
   });
@@ -612,7 +601,7 @@ __global__ __launch_bounds__(64 * WR * WC, PCU) void tile_gemm_kernel(const uint
   const int rq = (lane >> 4) * 4, cq = lane & 15;
   const int mw = mb0 + wr * WM, nw = nb0 + wc * WNT;
   if constexpr (ROPE) {
-    static_assert(NW * (16 * (WNT * 16 + 4) + 8 * 64 * 2) * 4 <= R * TILES * 1024, "the waves' staging fits the LDS");
+    static_assert(NW * (16 * (WNT * 16 + 4) + 2 * 64) * 4 <= R * TILES * 1024, "the waves' staging fits the LDS");
     tile_rope_epilogue<WM, WNT>(lds, acc, wunscale, o, rows, n_blocks, mw, nw, wave, lane);
   } else if (o.kind == kSiluMul) {
 #pragma unroll

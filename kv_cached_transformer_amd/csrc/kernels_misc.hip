@@ -290,21 +290,6 @@ void launch_rope_append(const llmdec_config &cfg, float *qkv, const float *qkv_p
                                               pool_k, pool_v, num_pages, err);
 }
 
-// The rotations of a prefill's tokens, for the q|k|v product's RoPE epilogue: one block per token, one
-// thread per pair, the same angle reduction and fp32 sine and cosine as above.
-__global__ void rope_table_kernel(const int32_t *__restrict__ tok_pos, int half, RopeFreq fr, float2 *cs) {
-  const int t = blockIdx.x, i = threadIdx.x;
-  if (i >= half) return;
-  float c, sn;
-  rope_cos_sin(tok_pos[t], fr.inv_freq[i], c, sn);
-  cs[(size_t)t * half + i] = make_float2(c, sn);
-}
-
-void launch_rope_table(const llmdec_config &cfg, const int32_t *tok_pos, int n_tokens, float2 *cs, hipStream_t s) {
-  if (n_tokens <= 0) return;
-  rope_table_kernel<<<n_tokens, 64, 0, s>>>(tok_pos, cfg.head_dim / 2, rope_freq(cfg), cs);
-}
-
 // ---------------------------------------------------------------- SwiGLU gate ([W] §1.2, [E] §4.2)
 // Stand-alone form: u = silu(g) * up, silu(z) = z / (1 + e^-z).
 __global__ void silu_mul_kernel(const float *__restrict__ g, const float *__restrict__ u, size_t n,

@@ -405,7 +405,8 @@ template <int WM, int WNT, int NP, int PCU = 1, int WR = 2, int WC = 2> struct T
 // that large runs from outside the instruction cache).  Each pair's rotation is formed where it is used
 // (the angle reduced in double, then sine and cosine in fp32, as the RoPE/append kernel does): a load
 // from memory in the walk would make the wave wait for its earlier stores too.  The rows' positions
-// and page slots are looked up once, lane l holding rows l and l + 64 of the wave.
+// and page slots are looked up once, lane l holding rows l and l + 64 of the wave, and read in the walk
+// with scalar lane reads.
 template <int WM, int WNT>
 __device__ __forceinline__ void tile_rope_epilogue(uint4 *lds, const f32x4 (&acc)[WM][WNT], float wunscale,
                                                    const LinearOut &o, int rows, int n_blocks, int mw, int nw,
@@ -448,6 +449,12 @@ __device__ __forceinline__ void tile_rope_epilogue(uint4 *lds, const f32x4 (&acc
   const double f_lane = rp.fr.inv_freq[lane];
   __syncthreads();  // every wave's k-loop reads of the LDS are done
   fq[lane] = f_lane;
+  double f_pair = 0.0;  // 64 % P == 0: the frequency of this lane's pair (q or k columns)
+  if constexpr (64 % P == 0) {
+    const int col = rp.col0 + c0 + 2 * (lane % P);
+    const int d = col < hid ? col : col - hid;
+    f_pair = fq[(d % D) >> 1];
+  }
 
   StaticFor<0, WM>::run([&](auto mc) __attribute__((always_inline)) {
     constexpr int m = decltype(mc)::value;
@@ -456,18 +463,31 @@ __device__ __forceinline__ void tile_rope_epilogue(uint4 *lds, const f32x4 (&acc
     for (int j = 0; j < WNT; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) st[(rq + e) * PITCH + j * 16 + cq] = acc[m][j][e] * wunscale;
+    // A step covers at most two rows (P >= 32); their positions and slots are read from the lanes that
+    // hold them with scalar reads.  With 64 % P == 0 a lane keeps the same pair in every step, so its
+    // frequency is read once.
+#pragma unroll 4
     for (int it = 0; it < STEPS; ++it) {
       const int idx = it * 64 + lane, rl = idx / P, p = idx - rl * P;
-      const int r = r0 + rl, rw = m * 16 + rl;  // row of the product, of the wave
-      const int2 ps = make_int2(__shfl(slot[rw >> 6].x, rw & 63, 64), __shfl(slot[rw >> 6].y, rw & 63, 64));
-      const int pos = __shfl(pos_r[rw >> 6], rw & 63, 64);
+      const int rla = (it * 64) / P, rlb = min(rla + 1, 15);  // the step's rows (wave-uniform)
+      const int rwa = m * 16 + rla, rwb = m * 16 + rlb;
+      const int pos_a = __builtin_amdgcn_readlane(pos_r[rwa >> 6], rwa & 63);
+      const int pos_b = __builtin_amdgcn_readlane(pos_r[rwb >> 6], rwb & 63);
+      const int pg_a = __builtin_amdgcn_readlane(slot[rwa >> 6].x, rwa & 63);
+      const int pg_b = __builtin_amdgcn_readlane(slot[rwb >> 6].x, rwb & 63);
+      const int of_a = __builtin_amdgcn_readlane(slot[rwa >> 6].y, rwa & 63);
+      const int of_b = __builtin_amdgcn_readlane(slot[rwb >> 6].y, rwb & 63);
+      const bool on_a = rl == rla;
+      const int pos = on_a ? pos_a : pos_b;
+      const int2 ps = make_int2(on_a ? pg_a : pg_b, on_a ? of_a : of_b);
+      const int r = r0 + rl;  // row of the product
       if (r >= rows || 2 * p >= ncols) continue;
       const float2 xv = *reinterpret_cast<const float2 *>(st + rl * PITCH + 2 * p);
       const int col = rp.col0 + c0 + 2 * p;
       if (col < hid + kvc) {  // q or k: rotate the pair
         const int d = col < hid ? col : col - hid;
         float c, sn;
-        rope_cos_sin(pos, fq[(d % D) >> 1], c, sn);
+        rope_cos_sin(pos, 64 % P == 0 ? f_pair : fq[(d % D) >> 1], c, sn);
         const float re = xv.x * c - xv.y * sn, ro = xv.x * sn + xv.y * c;
         if (col < hid) {
           *reinterpret_cast<float2 *>(o.f32 + (size_t)r * o.ld + c0 + 2 * p) = make_float2(re, ro);

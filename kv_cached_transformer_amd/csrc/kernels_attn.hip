@@ -525,7 +525,8 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
                                                           uint32_t *err) {
   constexpr int KT = D / 32;  // k-tiles of the head dimension
   constexpr int DB = D / 16;  // 16-dim blocks of the output
-  const int qb = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  // the query block is the slowest index, counted down: the blocks with the most keys start first
+  const int qb = (int)gridDim.z - 1 - (int)blockIdx.z, h = blockIdx.x, s = blockIdx.y;
   const int kvh = h / (n_heads / n_kv_heads);  // the K/V head this query head reads
   const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
   const int t0 = cu[s], len = cu[s + 1] - t0;
@@ -692,7 +693,9 @@ __global__ __launch_bounds__(256) void prefill_attn4_kernel(const float *__restr
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)lds;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  const int qg = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  // Blocks start roughly in index order and the query group is the slowest index, counted down: every
+  // (head, sequence)'s group with the most keys starts first, and the short ones fill in at the end.
+  const int qg = (int)gridDim.z - 1 - (int)blockIdx.z, h = blockIdx.x, s = blockIdx.y;
   const int kvh = h / (n_heads / n_kv_heads);
   const int t0 = cu[s], len = cu[s + 1] - t0;
   if (t0 < 0 || len < 0 || len > max_q_len || t0 + len > n_tokens || start_pos[s] < 0) {
@@ -875,13 +878,13 @@ void launch_prefill_attention(const llmdec_config &cfg, const float *q, int ld_q
                               uint16_t *out_lo, int kpad, uint32_t *err, hipStream_t s) {
   if (n_seqs <= 0 || max_q_len <= 0) return;
   if (cfg.head_dim == 128) {
-    dim3 grid4((max_q_len + 63) / 64, cfg.n_heads, n_seqs);
+    dim3 grid4(cfg.n_heads, n_seqs, (max_q_len + 63) / 64);
     prefill_attn4_kernel<<<grid4, 256, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, n_tokens, max_q_len, cu, start_pos,
                                                block_tables, max_pages, pk, pv, num_pages, out_f32, out_act, out_lo,
                                                kpad, err);
     return;
   }
-  dim3 grid((max_q_len + 15) / 16, cfg.n_heads, n_seqs);
+  dim3 grid(cfg.n_heads, n_seqs, (max_q_len + 15) / 16);
   prefill_attn_kernel<64><<<grid, 64, 0, s>>>(q, ld_q, cfg.n_heads, cfg.n_kv_heads, n_tokens, max_q_len, cu, start_pos,
                                               block_tables, max_pages, pk, pv, num_pages, out_f32, out_act, out_lo,
                                               kpad, err);

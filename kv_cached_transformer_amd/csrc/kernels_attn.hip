@@ -74,7 +74,8 @@ __device__ inline void store_out(float v, int r, int c, int ld, float *out_f32, 
 // last ones, which fill in the tail.
 constexpr int DA_RING = 3;
 constexpr int DA_WAVES = 8;        // decode waves per block: consecutive partitions of one (sequence, heads)
-constexpr int kMaxPartPages = 16;  // pages per decode partition, at most (one page id per lane)
+constexpr int kMaxPartPages = 18;  // pages per decode partition, at most
+static_assert(DA_WAVES * kMaxPartPages <= 192, "a block's page ids fit three per lane");
 
 __device__ inline uint32_t vword(const uint4 &v, int k) { return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w; }
 __device__ inline uint32_t vword(const uint2 &v, int k) { return k == 0 ? v.x : v.y; }
@@ -127,12 +128,20 @@ __global__ __launch_bounds__(64 * DA_WAVES) void decode_attn_kernel(const float 
   const int kvh = blockIdx.x % n_kv_heads, h0 = kvh * group + (blockIdx.x / n_kv_heads) * QH;
   const int s = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int part = blockIdx.z * DA_WAVES + wave;  // this wave's partition
-  const int p0 = part * ppp;
-  // Three independent reads leave together: the context length, this partition's block-table
-  // entries (one per lane, validated once the length is known) and q.
+  // Block z covers pages [z DA_WAVES ppp, (z + 1) DA_WAVES ppp) of its sequence (ppp pages per wave);
+  // a block holding fewer pages (a sequence's last or only block) spreads them evenly over its waves,
+  // so it lasts as long as its share, not as long as a full partition.
+  const int blk0 = blockIdx.z * DA_WAVES * ppp;
+  // Three independent reads leave together: the context length, the block's block-table entries
+  // (every wave reads all of them, up to three per lane; each picks its own once the length is known)
+  // and q.
   const int32_t *bt = block_tables + (size_t)s * max_pages;
-  const int raw_pg = (lane < ppp && p0 + lane < max_pages) ? bt[p0 + lane] : -1;
+  int ent[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int i = 64 * j + lane;
+    ent[j] = (64 * j < DA_WAVES * ppp && i < DA_WAVES * ppp && blk0 + i < max_pages) ? bt[blk0 + i] : -1;
+  }
   float4 qv0[QH], qv1[QH];
 #pragma unroll
   for (int j = 0; j < QH; ++j) {
@@ -148,12 +157,21 @@ __global__ __launch_bounds__(64 * DA_WAVES) void decode_attn_kernel(const float 
     if (threadIdx.x == 0 && blockIdx.z == 0) raise_error(err, kErrPos);
     return;
   }
-  if (blockIdx.z * DA_WAVES * ppp >= n_pages) return;
+  if (blk0 >= n_pages) return;
   if (n_pages > max_pages) {
     if (threadIdx.x == 0) raise_error(err, kErrPos);
     return;
   }
-  const int p1 = max(p0, min(n_pages, p0 + ppp));
+  const int nb = min(DA_WAVES * ppp, n_pages - blk0);  // the block's pages
+  const int per = (nb + DA_WAVES - 1) / DA_WAVES;       // pages per wave (at most ppp)
+  const int p0 = blk0 + wave * per;
+  const int p1 = max(p0, min(blk0 + nb, p0 + per));
+  // lane i's entry: block page wave * per + i, held by lane (that & 63) in ent[that >> 6]
+  const int bi = wave * per + lane;
+  const int from = (bi & 63) * 4;
+  const int e0 = __builtin_amdgcn_ds_bpermute(from, ent[0]), e1 = __builtin_amdgcn_ds_bpermute(from, ent[1]),
+            e2 = __builtin_amdgcn_ds_bpermute(from, ent[2]);
+  const int raw_pg = bi < 64 ? e0 : (bi < 128 ? e1 : e2);
   int my_pg = -1;  // lane i: page id of page p0 + i
   if (lane < p1 - p0) {
     my_pg = raw_pg;
@@ -436,15 +454,21 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(int n_heads, const in
 void decode_partition(const llmdec_config &cfg, int n_seqs, int max_pages, int *pages_per_part, int *n_parts) {
   // Aim for ~16 waves per CU over 256 CUs counting every (sequence, wave of heads) row at full width,
   // QH times that where a wave serves QH query heads (its pages cost QH times the arithmetic, so shorter
-  // partitions keep the waves' lengths even); never split finer than one page, never coarser than
-  // kMaxPartPages.
+  // partitions keep the waves' lengths even); never split finer than one page.  Where that asks for
+  // partitions longer than kMaxPartPages, a sequence takes as few blocks as hold its pages at up to
+  // kMaxPartPages a wave, the pages spread evenly over the blocks' waves: at 2049 tokens (129 pages) one
+  // block of eight 17-page partitions instead of two blocks of 16-page ones, so no combine launch follows.
   const int qh = decode_heads_per_wave(cfg);
   const long rows = (long)n_seqs * (cfg.n_heads / qh);
   const long target = 4096L * qh;
   int parts = (int)((target + rows - 1) / rows);
   parts = parts < 1 ? 1 : parts;
   int ppp = (max_pages + parts - 1) / parts;
-  ppp = ppp < 1 ? 1 : (ppp > kMaxPartPages ? kMaxPartPages : ppp);
+  ppp = ppp < 1 ? 1 : ppp;
+  if (ppp > kMaxPartPages) {
+    const int blocks = (max_pages + DA_WAVES * kMaxPartPages - 1) / (DA_WAVES * kMaxPartPages);
+    ppp = (max_pages + blocks * DA_WAVES - 1) / (blocks * DA_WAVES);
+  }
   *pages_per_part = ppp;
   *n_parts = (max_pages + ppp - 1) / ppp;
 }

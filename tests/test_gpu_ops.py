@@ -338,11 +338,17 @@ def _gather(kblk, vblk, row, n, Hk, D):
                                          (8, 128, 8, [4096, 33, 511, 512, 1000, 7]),
                                          (32, 128, 8, [0, 15, 16, 2048, 300]),
                                          (4, 64, 1, [0, 1, 17, 100, 513]),
-                                         (4, 64, 4, [2000, 2100, 3])])
+                                         (4, 64, 4, [2000, 2100, 3]),
+                                         (32, 128, 32, [2048, 0, 15, 16, 17, 100, 1, 31, 32, 33, 200, 5, 64,
+                                                        65, 127, 128]),
+                                         (32, 128, 32, [4000, 2048, 0, 15, 16, 17, 100, 1, 31, 32, 33, 200, 5,
+                                                        64, 65, 127])])
 def test_decode_attention(L, R, H, D, Hk, ctxs):
-    """Query head h attends over K/V head h // (H / Hk) (grouped-query when Hk < H).  The last case
-    leaves 16 and 17 block results per head to the combine (one-page partitions, 8 per block): the
-    largest count it reads in one pass and one past it."""
+    """Query head h attends over K/V head h // (H / Hk) (grouped-query when Hk < H).  The [2000, 2100,
+    3] case leaves 16 and 17 block results per head to the combine (one-page partitions, 8 per block):
+    the largest count it reads in one pass and one past it.  The last two ask for partitions longer
+    than a wave takes: at 2049 tokens one block of eight 17-page partitions (no combine), at 4001 tokens
+    two blocks of 16-page ones."""
     banner(f"decode_attention H={H} D={D} Hk={Hk} ctxs={ctxs}")
     shape = Shape(H, D, Hk=Hk)
     g = H // Hk

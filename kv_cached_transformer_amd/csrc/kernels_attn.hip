@@ -685,6 +685,23 @@ __global__ __launch_bounds__(64) void prefill_attn_kernel(const float *__restric
       store_out(oacc[db][e] * inv, tok, h * D + db * 16 + g * 4 + e, n_heads * D, out_f32, out_act, out_lo, kpad);
 }
 
+// Maximum and sum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (in an MFMA accumulator: the four key groups of
+// one query column), with gfx950's row swaps (no trip through the LDS crossbar).  A swap returns the
+// operand with rows exchanged in both orders, so op(r[0], r[1]) pairs every lane with its partner; the
+// sums associate as (x_l + x_l^16) + (x_l^32 + x_l^48) in every lane, so all four get the same bits.
+__device__ inline float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Head dimension 128: four waves per block, one block per (sequence, head, 64 queries); wave w takes the
 // 16 queries of block 4 x + w.  The block walks the keys its last query sees two pages (32 keys) at a
 // time; each chunk's K and V pages go from the pool straight into LDS (16 loads of 1 KiB, four per
@@ -703,7 +720,8 @@ constexpr int kPfVPage = 4 * kPfVQuarter;
 constexpr int kPfStage = 2 * kPfKPage + 2 * kPfVPage;
 constexpr int kPfStages = 3;
 
-__global__ __launch_bounds__(256) void prefill_attn4_kernel(const float *__restrict__ q, int ld_q, int n_heads,
+// Three blocks per CU (one wave per SIMD each, 48 KiB of LDS each): at most 168 registers a lane.
+__global__ __launch_bounds__(256, 3) void prefill_attn4_kernel(const float *__restrict__ q, int ld_q, int n_heads,
                                                             int n_kv_heads, int n_tokens, int max_q_len,
                                                             const int32_t *__restrict__ cu,
                                                             const int32_t *__restrict__ start_pos,
@@ -848,12 +866,11 @@ __global__ __launch_bounds__(256) void prefill_attn4_kernel(const float *__restr
     (void)pgs;
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = rows4_max(mx);
     const float m_new = fmaxf(m, mx);
     // the accumulators are rescaled only when some query's maximum grew (otherwise the factor is 1)
     const bool grow = __any(m_new > m);
-    const float alpha = exp2f(m - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
     m = m_new;
     float pr[8];
     float psum = 0.f;
@@ -861,7 +878,7 @@ __global__ __launch_bounds__(256) void prefill_attn4_kernel(const float *__restr
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pr[u * 4 + e] = exp2f(sc[u][e] - m_new);
+        pr[u * 4 + e] = __builtin_amdgcn_exp2f(sc[u][e] - m_new);  // 0 for masked keys
         psum += pr[u * 4 + e];
       }
     if (grow) {
@@ -884,8 +901,7 @@ __global__ __launch_bounds__(256) void prefill_attn4_kernel(const float *__restr
     }
   }
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // the loads issued past the last chunk land before exit
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = rows4_sum(l);
   if (!q_ok) return;
   const float inv = 1.f / l;
   const int tok = t0 + qb * 16 + c;

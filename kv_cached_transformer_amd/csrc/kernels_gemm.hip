@@ -407,6 +407,54 @@ template <int WM, int WNT, int NP, int PCU = 1, int WR = 2, int WC = 2> struct T
 // from memory in the walk would make the wave wait for its earlier stores too.  The rows' positions
 // and page slots are looked up once, lane l holding rows l and l + 64 of the wave, and read in the walk
 // with scalar lane reads.
+// A wave whose columns are all v columns skips the walk: it works on the accumulators' own layout (lane
+// l of a 16 x 16 block holds column l % 16 of rows 4 (l / 16) .. + 3), and where a lane's four rows are
+// the token slots 4i..4i+3 of one page (consecutive positions of one sequence), its four values are
+// the four adjacent bf16 of the V layout and leave as one 8-byte store (else one value at a time).  It
+// parks its blocks of one 16-row band in its LDS share and takes them in a short loop (one copy of the
+// per-block code), each lane reading back its own 16 bytes.
+template <int WM, int WNT>
+__device__ __forceinline__ void tile_v_epilogue(f32x4 *fr, const f32x4 (&acc)[WM][WNT], float wunscale,
+                                                const RopeRows &rp, int rows, int n_blocks, int mw, int nw,
+                                                const int (&slot_r)[2], int lane) {
+  const int D = rp.head_dim;
+  const int v0 = rp.n_heads * D + rp.n_kv_heads * D;  // the first v column of the q|k|v row
+  const int g = lane >> 4, cq = lane & 15;
+  StaticFor<0, WM>::run([&](auto mc) __attribute__((always_inline)) {
+    constexpr int m = decltype(mc)::value;
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) fr[j * 64 + lane] = acc[m][j] * wunscale;
+    int slt[4];  // page * 16 + offset of this lane's rows m*16 + 4g + e (-1: none)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      slt[e] = __builtin_amdgcn_ds_bpermute(((m * 16 + 4 * g + e) & 63) * 4, slot_r[(m * 16) >> 6]);
+    const int r0 = (mw + m) * 16 + 4 * g;
+    const bool quad = r0 + 3 < rows && slt[0] >= 0 && (slt[0] & 3) == 0 && slt[1] == slt[0] + 1 &&
+                      slt[2] == slt[0] + 2 && slt[3] == slt[0] + 3;
+#pragma unroll 2
+    for (int j = 0; j < WNT; ++j) {
+      if (nw + j >= n_blocks) break;  // no columns past the matrix (wave-uniform)
+      const f32x4 v = fr[j * 64 + lane];
+      const int d = rp.col0 + (nw + j) * 16 + cq - v0;
+      const size_t head_d = (size_t)(d / D);
+      if (quad) {  // V [h][o/4][d][o%4]
+        const size_t head = (size_t)(slt[0] >> 4) * rp.n_kv_heads + head_d;
+        const uint2 w = make_uint2(f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                                   f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+        *reinterpret_cast<uint2 *>(rp.pool_v + (head * 4 + ((slt[0] & 15) >> 2)) * D * 4 + (size_t)(d % D) * 4) = w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (r0 + e < rows && slt[e] >= 0) {
+            const size_t head = (size_t)(slt[e] >> 4) * rp.n_kv_heads + head_d;
+            const int of = slt[e] & 15;
+            rp.pool_v[(head * 4 + (of >> 2)) * D * 4 + (size_t)(d % D) * 4 + (of & 3)] = f32_to_bf16(v[e]);
+          }
+      }
+    }
+  });
+}
+
 template <int WM, int WNT>
 __device__ __forceinline__ void tile_rope_epilogue(uint4 *lds, const f32x4 (&acc)[WM][WNT], float wunscale,
                                                    const LinearOut &o, int rows, int n_blocks, int mw, int nw,
@@ -448,6 +496,12 @@ __device__ __forceinline__ void tile_rope_epilogue(uint4 *lds, const f32x4 (&acc
   }
   const double f_lane = rp.fr.inv_freq[lane];
   __syncthreads();  // every wave's k-loop reads of the LDS are done
+  if (kv && rp.col0 + c0 >= hid + kvc) {  // every column of the wave is a v column (wave-uniform)
+    const int slot_r[2] = {slot[0].x >= 0 ? slot[0].x * 16 + slot[0].y : -1,
+                           slot[1].x >= 0 ? slot[1].x * 16 + slot[1].y : -1};
+    tile_v_epilogue<WM, WNT>(reinterpret_cast<f32x4 *>(st), acc, wunscale, rp, rows, n_blocks, mw, nw, slot_r, lane);
+    return;
+  }
   fq[lane] = f_lane;
   double f_pair = 0.0;  // 64 % P == 0: the frequency of this lane's pair (q or k columns)
   if constexpr (64 % P == 0) {
@@ -622,6 +676,7 @@ __global__ __launch_bounds__(64 * WR * WC, PCU) void tile_gemm_kernel(const uint
   const int mw = mb0 + wr * WM, nw = nb0 + wc * WNT;
   if constexpr (ROPE) {
     static_assert(NW * (16 * (WNT * 16 + 4) + 2 * 64) * 4 <= R * TILES * 1024, "the waves' staging fits the LDS");
+    static_assert(16 * (WNT * 16 + 4) + 2 * 64 >= WNT * 64 * 4, "a wave's share holds its blocks of one band");
     tile_rope_epilogue<WM, WNT>(lds, acc, wunscale, o, rows, n_blocks, mw, nw, wave, lane);
   } else if (o.kind == kSiluMul) {
 #pragma unroll

@@ -620,10 +620,10 @@ def _pmc_rows(d, counter):
 
 def _per_dispatch(rows, name_part, last=64):
     """Mean counter value (KiB) over the last `last` dispatches of the named kernel (the standalone
-    attention calls, which follow the model steps)."""
+    attention calls, which follow the model steps); None where the run has no dispatch of it."""
     sel = sorted((r for r in rows if name_part in r["Kernel_Name"]), key=lambda r: int(r["Dispatch_Id"]))[-last:]
     if not sel:
-        raise SystemExit(f"no dispatch of {name_part}")
+        return None
     vals = [float(r["Counter_Value"]) for r in sel]
     return sum(vals) / len(vals), len(vals), sel[-1]["Grid_Size"]
 
@@ -636,7 +636,8 @@ def pmc_summary(fetch_dir, write_dir):
     copy_w = max(float(r["Counter_Value"]) for r in wr if "copy" in r["Kernel_Name"].lower())
     kf, kw = COPY_BYTES / (copy_f * 1024), COPY_BYTES / (copy_w * 1024)
     out = ["# HBM traffic per call of llmdec_op_decode_attention on the 64-sequence decode cache (7B shapes,",
-           "# contexts 256..2048 after the default 3 + 10 steps): partition kernel + combine kernel.",
+           "# contexts 256..2048 after the default 3 + 10 steps): the partition kernel, plus the combine kernel",
+           "# where some sequence spans several blocks (none does at these contexts: it is not launched).",
            "# Counters are KiB per dispatch; each is scaled by what it reads for a 1 GiB device copy.",
            "# Commands (from /tmp, committed files only), then the summary:",
            "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <F> -o p -- python3 <repo>/bench.py --only c5,copy --no-cpu",
@@ -647,8 +648,13 @@ def pmc_summary(fetch_dir, write_dir):
            f"copy_write_kib: {copy_w:.1f}  write_scale: {kw:.4f}"]
     total = 0.0
     for name in ("decode_attn_kernel<128,", "decode_combine_kernel<128>"):
-        f, nf, grid = _per_dispatch(fr, name)
-        w, nw, _ = _per_dispatch(wr, name)
+        pf, pw = _per_dispatch(fr, name), _per_dispatch(wr, name)
+        if pf is None or pw is None:
+            if name.startswith("decode_attn"):
+                raise SystemExit(f"no dispatch of {name}")
+            out.append(f"{name}: not launched")
+            continue
+        (f, nf, grid), (w, nw, _) = pf, pw
         b = f * 1024 * kf + w * 1024 * kw
         total += b
         out.append(f"{name.rstrip(',')}: grid {grid}: FETCH_SIZE {f:.1f} KiB ({nf} dispatches), WRITE_SIZE {w:.1f} KiB "
@@ -856,7 +862,8 @@ def main():
         a = head["attn"]
         line["hbm_frac_step"] = head["hbm_frac"]
         line["roofline"] = {"bound": "hbm",
-                            "kernel": "paged decode attention, one layer, 64 sequences (partition + combine kernels)",
+                            "kernel": "paged decode attention, one layer, 64 sequences (partition kernel; the combine "
+                                      "kernel only where a sequence spans several blocks)",
                             "achieved": a["gbps"], "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                             "frac": a["gbps"] * 1e9 / HBM_PEAK, "traffic": read_traffic(a["bytes"]),
                             "algorithmic_bytes": a["bytes"], "us_per_call": a["ms"] * 1e3}

@@ -204,8 +204,10 @@ llmdec_status llmdec_workspace_error(const void *ws, llmdec_stream stream, uint3
 /* ------------------------------------------------------------------ layer steps */
 /* Prefill (or chunked prefill) of one layer.  hidden: dev fp32 [n_tokens][hidden],
  * the residual stream, updated in place.  Sequence s owns tokens
- * cu_seqlens[s]..cu_seqlens[s+1]-1 (dev int32 [n_seqs+1]); its first new token
- * sits at position start_pos[s] (dev int32 [n_seqs]).  block_tables: dev int32
+ * cu_seqlens[s]..cu_seqlens[s+1]-1 (dev int32 [n_seqs+1], starting at 0 and
+ * strictly increasing: every sequence carries at least one new token; a
+ * segment with none sets error bit 8); its first new token sits at position
+ * start_pos[s] (dev int32 [n_seqs]).  block_tables: dev int32
  * [n_seqs][max_pages], rows already covering start_pos+len tokens.  n_tokens
  * (= cu_seqlens[n_seqs]) and max_q_len (>= every sequence's new-token count)
  * are host copies used to size the launch.  Computes ([W] §1.1, [E] §4.2-4.3):

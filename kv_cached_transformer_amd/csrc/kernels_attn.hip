@@ -6,8 +6,9 @@
 //
 // Decode: one wave per (sequence, head, partition of pages), every load a
 // contiguous 1 KiB of a K or V block (details at the kernel); the running max
-// is wave-uniform per page (one rescale per page).  Partitions are merged by
-// a log-sum-exp combine kernel.
+// is wave-uniform per page (one rescale per page).  The eight waves of a block
+// merge their partitions in LDS; where a sequence spans several blocks, a
+// log-sum-exp combine kernel merges the blocks' results.
 //
 // Prefill: MFMA.  Scores are formed transposed, S^T = K Q^T (keys as rows),
 // so a lane's accumulator holds 4 keys of one query: exactly the operand

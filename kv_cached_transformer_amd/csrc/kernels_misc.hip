@@ -254,8 +254,8 @@ void launch_token_map(const int32_t *cu, const int32_t *start, int n_seqs, int n
 // One block per (new token, chunk of heads holding 256 rotation pairs).  Pair i
 // of every head turns by pos * inv_freq[i],
 // inv_freq[i] = theta^(-2i/D) computed in double on the host; the angle is
-// formed and reduced to [-pi, pi] in double, then its sine and cosine taken
-// in fp32, so positions in the thousands lose no accuracy.  q is rotated in
+// formed and reduced to a fraction of a turn in double, then its sine and
+// cosine taken in fp32, so positions in the thousands lose no accuracy.  q is rotated in
 // place; rotated k and plain v are rounded to bf16 and written to the page
 // slot bt[seq][pos/16], offset pos%16 (K as [h][o][d], V as [h][o/4][d][o%4]).
 __global__ __launch_bounds__(256) void rope_append_kernel(float *__restrict__ qkv, const float *__restrict__ part,

@@ -452,3 +452,34 @@ def test_tiny_model_continuous_batching(L, R):
         eps, flips = kv_bounds(layer)
         assert_stored_bf16(f"continuous batching layer {layer} cached K/V", np.stack(got_kv), np.stack(ref_kv),
                            eps, flips)
+
+
+def test_model_step_empty_segment_sets_error_bit(L, R):
+    """Every sequence of a step carries at least one new token: a cu_seqlens segment with none (the
+    middle sequence here) sets error bit 8 rather than handing that sequence the previous sequence's
+    last token, and the step still completes.  A step whose segments all hold tokens, on the same
+    pool and rows, raises nothing."""
+    banner("tiny model: empty cu_seqlens segment")
+    shape = synth.TINY
+    W = 43
+    mw = synth.model_weights(W, shape)
+    dm = DeviceModel(L, R, mw)
+    num_pages, max_pages = 8, 2
+    order = synth.free_order(W, num_pages)
+    pool = R.Pool(dm.cfg, num_pages, order, fill_bits=0xFFFF)
+    rows = np.full((3, max_pages), -1, np.int32)
+    for s in range(3):
+        pool.alloc(5, rows[s], 0, max_pages)
+    ws = R.Workspace(L.llmdec_workspace_bytes(dm.cfg, 16, 3, max_pages))
+    bt_d, st_d = R.dev_i32(rows), R.dev_i32(np.zeros(3, np.int32))
+    nxt = torch.empty(3, dtype=torch.int32, device="cuda")
+    for lens, bits in (([5, 0, 4], 8), ([5, 1, 4], 0)):
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        toks = synth.prompt_ids(W, int(cu[-1]), shape.vocab).astype(np.int32)
+        toks_d, cu_d = R.dev_i32(toks), R.dev_i32(cu)
+        L.llmdec_workspace_reset(ws.ptr, ws.nbytes, R.stream())
+        L.llmdec_model_step_greedy(dm.cfg, dm.struct, 3, int(cu[-1]), max(lens), toks_d.data_ptr(), cu_d.data_ptr(),
+                                   st_d.data_ptr(), bt_d.data_ptr(), max_pages, pool.handle, nxt.data_ptr(), None,
+                                   ws.ptr, ws.nbytes, R.stream())
+        torch.cuda.synchronize()
+        assert ws.error_bits() == bits, f"segments {lens}: error bits {ws.error_bits()} (expected {bits})"

@@ -458,22 +458,23 @@ def test_model_step_empty_segment_sets_error_bit(L, R):
     """Every sequence of a step carries at least one new token: a cu_seqlens segment with none (the
     middle sequence here) sets error bit 8 rather than handing that sequence the previous sequence's
     last token, and the step still completes.  A step whose segments all hold tokens, on the same
-    pool and rows, raises nothing."""
+    pool and rows, raises nothing.  Steps of 9-10 rows (the single-row RMSNorm) and of 80-81 rows
+    (the many-row RMSNorm)."""
     banner("tiny model: empty cu_seqlens segment")
     shape = synth.TINY
     W = 43
     mw = synth.model_weights(W, shape)
     dm = DeviceModel(L, R, mw)
-    num_pages, max_pages = 8, 2
+    num_pages, max_pages = 12, 4
     order = synth.free_order(W, num_pages)
     pool = R.Pool(dm.cfg, num_pages, order, fill_bits=0xFFFF)
     rows = np.full((3, max_pages), -1, np.int32)
     for s in range(3):
-        pool.alloc(5, rows[s], 0, max_pages)
-    ws = R.Workspace(L.llmdec_workspace_bytes(dm.cfg, 16, 3, max_pages))
+        pool.alloc(48, rows[s], 0, max_pages)
+    ws = R.Workspace(L.llmdec_workspace_bytes(dm.cfg, 96, 3, max_pages))
     bt_d, st_d = R.dev_i32(rows), R.dev_i32(np.zeros(3, np.int32))
     nxt = torch.empty(3, dtype=torch.int32, device="cuda")
-    for lens, bits in (([5, 0, 4], 8), ([5, 1, 4], 0)):
+    for lens, bits in (([5, 0, 4], 8), ([5, 1, 4], 0), ([40, 0, 40], 8), ([40, 1, 40], 0)):
         cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
         toks = synth.prompt_ids(W, int(cu[-1]), shape.vocab).astype(np.int32)
         toks_d, cu_d = R.dev_i32(toks), R.dev_i32(cu)

@@ -260,8 +260,9 @@ llmdec_status llmdec_model_step_greedy(const llmdec_config *cfg, const llmdec_mo
  * [rows][n], n a multiple of 32 and at most 8192; gamma: dev bf16 [n].
  * out_f32 (fp32 [rows][n]) and out_act (fp16(y), rounded to nearest-even and
  * clipped to +-65504, in the packed tile layout of a
- * [round_up(rows,16)][ld_packed] matrix: see "Packed activations" above;
- * columns n..ld_packed-1 zeroed) may each be NULL but not both.  out_lo
+ * [round_up(rows,16)][ld_packed] matrix, ld_packed a multiple of 32 from n
+ * to 8192: see "Packed activations" above; columns n..ld_packed-1 zeroed)
+ * may each be NULL but not both.  out_lo
  * (NULL, or the same layout as out_act, which must then be given) receives
  * fp16(y - out_act): the pair the q|k|v product reads. */
 llmdec_status llmdec_op_rmsnorm(const float *x, const void *gamma, int32_t rows, int32_t n, float eps,

@@ -620,9 +620,11 @@ extern "C" llmdec_status llmdec_op_rmsnorm(const float *x, const void *gamma, in
                                           llmdec_stream stream) {
   if (!x || !gamma || (!out_f32 && !out_act) || (out_lo && !out_act))
     return set_error(LLMDEC_E_INVALID, "op_rmsnorm: NULL pointer");
-  if (rows <= 0 || n <= 0 || n % 32 || n > 8192 || (out_act && (ld_packed < n || ld_packed % 32)))
-    return set_error(LLMDEC_E_INVALID, "op_rmsnorm: rows=%d n=%d (a multiple of 32, <= 8192) ld_packed=%d out of range",
-                     rows, n, ld_packed);
+  // the row kernel writes (and zero-pads) at most 8192 columns of a row
+  if (rows <= 0 || n <= 0 || n % 32 || n > 8192 || (out_act && (ld_packed < n || ld_packed % 32 || ld_packed > 8192)))
+    return set_error(LLMDEC_E_INVALID,
+                     "op_rmsnorm: rows=%d n=%d (a multiple of 32, <= 8192) ld_packed=%d (a multiple of 32, n..8192) "
+                     "out of range", rows, n, ld_packed);
   launch_rmsnorm(const_cast<float *>(x), n, nullptr, rows, (const uint16_t *)gamma, rows, n, eps, nullptr, out_f32,
                  (uint16_t *)out_act, (uint16_t *)out_lo, ld_packed, nullptr, Splits{}, (hipStream_t)stream);
   return check_launch("op_rmsnorm");

@@ -42,7 +42,9 @@ def bf16_normal(rng, shape, std=1.0):
 
 
 # ----------------------------------------------------------------------------- RMSNorm
-@pytest.mark.parametrize("rows,n", [(1, 4096), (3, 256), (70, 4096), (133, 1024), (200, 4064)])
+# above 64 rows: 64-column groups of kpad = n + 32 at each block shape of the many-row kernel (5, 17, 64, 65
+# and 128 groups, the last at the widest packed stride, 8192)
+@pytest.mark.parametrize("rows,n", [(1, 4096), (3, 256), (80, 256), (70, 4096), (133, 1024), (200, 4064), (72, 8160)])
 def test_rmsnorm(L, R, rows, n):
     """fp32 output against the oracle; the packed fp16 output is the nearest-even fp16 of the device's own
     fp32 value, bit for bit (both roundings taken in the same precision), and the fp16 pair's lo part is

@@ -199,3 +199,14 @@ def test_q4_sizes_and_validation(L):
     with pytest.raises(L.LlmdecError) as e:
         L.llmdec_q4_pack_matrix(8, 256, src, 1 << 23, 100)
     assert e.value.status == L.LLMDEC_E_INVALID and "q4_pack_matrix" in str(e.value)
+
+
+def test_rmsnorm_op_shape_validation_before_launch(L):
+    """llmdec_op_rmsnorm refuses shapes its kernels would not cover before anything is launched: n past
+    8192 or not a multiple of 32, and a packed stride (ld_packed) below n, not a multiple of 32 or past
+    8192 columns (the padding columns n..ld_packed-1 are zeroed only up to there)."""
+    p = 1 << 20
+    for n, ld in ((8192, 8224), (256, 240), (256, 272), (8224, 8224), (250, 256)):
+        with pytest.raises(L.LlmdecError) as e:
+            L.llmdec_op_rmsnorm(p, p, 4, n, 1e-6, None, p, None, ld)
+        assert e.value.status == L.LLMDEC_E_INVALID, (n, ld)

@@ -112,6 +112,14 @@ def test_prefill_tiny_chunked(L, R):
     run_prefill(L, R, TINY1, 93, starts, lens, synth.hidden_input(93, sum(lens), 256), "tiny prefill chunked")
 
 
+@pytest.mark.parametrize("starts,lens", [([0], [64]), ([0, 7], [33, 32]), ([3, 0, 16], [1, 63, 15])])
+def test_prefill_tiny_at_the_row_boundary(L, R, starts, lens):
+    """64 rows take the streaming products with the fp16 pair and the RoPE/append kernel; 65 and 79 rows
+    the tiled products with RoPE and the append in their epilogues (one row past a 16-row block)."""
+    n = sum(lens)
+    run_prefill(L, R, TINY1, 99 + n, starts, lens, synth.hidden_input(99 + n, n, 256), f"tiny prefill {n} rows")
+
+
 def test_prefill_tiny_single_token(L, R):
     run_prefill(L, R, TINY1, 94, [20], [1], synth.hidden_input(94, 1, 256), "tiny prefill 1 token")
 
